@@ -1,0 +1,135 @@
+"""Independent implementation of the library's device weight layout
+("layout 1"), used only to check the repack kernel byte for byte.
+
+The pages say the weights, scales and zero points are first brought into one
+common representation and then padded and re-ordered for the device and the
+kernel (ywsung.com note "How vLLM Humming computes 4 bits", section on layout;
+aihaber.org article, Architecture).  The re-ordered layout itself is this
+library's own design; it is specified here in words and built element by
+element from that specification:
+
+E experts, N columns (output features), K (multiple of 128), NB = ceil(N/16)
+blocks of 16 columns, KG = K/128 steps of 128 along K.
+
+Region A, codes: E*NB*KG tiles of 1024 bytes, tile index (e*NB + nb)*KG + g.
+  A tile is 64 slots of 16 bytes.  Slot L covers column n = 16*nb + L%16 and
+  quarter h = L//16.
+  * int4 formats: byte 4*j + b of slot L (j, b in 0..3) holds
+    k = 128*g + 32*j + 8*h + 2*b in its low nibble and k+1 in its high nibble.
+    Stored value: uint4_zp -> u; int4_sym -> q + 8 (offset binary).
+  * mxfp4: byte b (0..15) of slot L holds k = 128*g + 32*h + 2*b (low nibble)
+    and k+1 (high nibble), E2M1 bits as given.
+  Columns n >= N hold the value-zero code (int4_sym 8, others 0).
+Region B, scales (starts at the next 256-byte boundary):
+  * int4 formats: bf16 entry ((e*NB + nb)*KG + g)*16 + c = scale of column
+    16*nb + c, group g.
+  * mxfp4: KG4 = ceil(KG/4); byte (((e*NB + nb)*KG4 + g//4)*64 + L)*4 + g%4 =
+    E8M0 of column 16*nb + L%16 and 32-block 4*g + L//16.
+  Padding entries are 0.
+Region C, zero points (uint4_zp only, next 256-byte boundary): 8 bytes per
+  ((e*NB + nb)*KG + g); byte c//2, nibble c%2 (low nibble for even c) = zero
+  point of column 16*nb + c, group g.  Padding 0.
+Total size: end of the last region rounded up to 256 bytes.
+"""
+import numpy as np
+
+from .quant import FMT_INT4_SYM, FMT_UINT4_ZP, FMT_MXFP4, unpack_nibbles
+
+
+def _align(x, a=256):
+    return (x + a - 1) // a * a
+
+
+def sizes(fmt, E, N, K):
+    """(offset_B, offset_C, total) in bytes."""
+    NB = (N + 15) // 16
+    KG = K // 128
+    a = E * NB * KG * 1024
+    if fmt == FMT_MXFP4:
+        b = E * NB * ((KG + 3) // 4) * 256
+    else:
+        b = E * NB * KG * 16 * 2
+    c = E * NB * KG * 8 if fmt == FMT_UINT4_ZP else 0
+    ob = _align(a)
+    oc = _align(ob + b)
+    return ob, oc, _align(oc + c)
+
+
+def transform_ref(fmt, codes, scales, zeros=None):
+    """Build the device bytes from the standard format.
+
+    codes  uint8 [E,N,K/2]  (packed nibbles, even k low)
+    scales int4: uint16 bf16 bits [E,N,K/128]; mxfp4: uint8 [E,N,K/32]
+    zeros  uint8 [E,N,K/128] (uint4_zp only)
+    Returns a uint8 array of the total size."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    E, N, K2 = codes.shape
+    K = 2 * K2
+    NB = (N + 15) // 16
+    KG = K // 128
+    ob, oc, total = sizes(fmt, E, N, K)
+    out = np.zeros(total, dtype=np.uint8)
+
+    # unsigned nibble values [E, NB*16, K], padded columns at the value-zero code
+    u = np.zeros((E, NB * 16, K), dtype=np.uint8)
+    if fmt == FMT_INT4_SYM:
+        u[:] = 8
+    for e in range(E):
+        v = unpack_nibbles(codes[e])
+        if fmt == FMT_INT4_SYM:
+            v = v ^ 8
+        u[e, :N] = v
+
+    # Region A: element by element from the slot rule
+    tiles = np.zeros((E, NB, KG, 64, 16), dtype=np.uint8)
+    L = np.arange(64)
+    c = L % 16
+    h = L // 16
+    for b in range(16):
+        if fmt == FMT_MXFP4:
+            k_lo = 32 * h + 2 * b                         # [64]
+        else:
+            j, bb = b // 4, b % 4
+            k_lo = 32 * j + 8 * h + 2 * bb
+        for g in range(KG):
+            klo = 128 * g + k_lo
+            for nb in range(NB):
+                col = 16 * nb + c
+                lo = u[:, col, klo]                        # [E, 64]
+                hi = u[:, col, klo + 1]
+                tiles[:, nb, g, :, b] = lo | (hi << 4)
+    out[:tiles.size] = tiles.ravel()
+
+    # Region B
+    if fmt == FMT_MXFP4:
+        KG4 = (KG + 3) // 4
+        sb = np.zeros((E, NB, KG4, 64, 4), dtype=np.uint8)
+        sc = np.asarray(scales, dtype=np.uint8)            # [E, N, K/32]
+        for g in range(KG):
+            for nb in range(NB):
+                for l in range(64):
+                    n = 16 * nb + l % 16
+                    if n < N:
+                        sb[:, nb, g // 4, l, g % 4] = sc[:, n, 4 * g + l // 16]
+        out[ob:ob + sb.size] = sb.ravel()
+    else:
+        sb = np.zeros((E, NB, KG, 16), dtype=np.uint16)
+        sc = np.asarray(scales, dtype=np.uint16)           # [E, N, KG]
+        for nb in range(NB):
+            for cc in range(16):
+                n = 16 * nb + cc
+                if n < N:
+                    sb[:, nb, :, cc] = sc[:, n, :]
+        out[ob:ob + sb.size * 2] = sb.view(np.uint8).ravel()
+
+    # Region C
+    if fmt == FMT_UINT4_ZP:
+        zb = np.zeros((E, NB, KG, 8), dtype=np.uint8)
+        zz = np.asarray(zeros, dtype=np.uint8) & 0xF       # [E, N, KG]
+        for nb in range(NB):
+            for cc in range(16):
+                n = 16 * nb + cc
+                if n < N:
+                    zb[:, nb, :, cc // 2] |= (zz[:, n, :] << (4 * (cc % 2))).astype(np.uint8)
+        out[oc:oc + zb.size] = zb.ravel()
+    return out

@@ -1,0 +1,52 @@
+"""MoE expert sort and grouped GEMM reference (oracle side).
+
+Tokens are split by expert, so each expert's GEMM has its own M that depends on
+the routing load (ywsung.com note "How vLLM Humming computes 4 bits", section on
+one token vs many tokens; aihaber.org article, "what problem does it solve"),
+and a grouped path runs all experts' GEMMs (aihaber.org, Performance).
+
+Pairs: with T tokens and top-k routing, pair p = t*topk + j is token t's j-th
+expert choice ids[t, j].  Rows of the grouped GEMM are in pair order.
+"""
+import numpy as np
+
+from .gemm import gemm_ref
+
+
+def moe_sort_ref(ids, num_experts):
+    """counts[e] = number of pairs routed to e; offsets = [0, cumsum(counts)];
+    sorted_pairs = pair ids grouped by expert, ascending within each expert."""
+    flat = np.asarray(ids, dtype=np.int64).ravel()
+    counts = np.bincount(flat, minlength=num_experts).astype(np.int32)
+    offsets = np.zeros(num_experts + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    sorted_pairs = np.argsort(flat, kind="stable").astype(np.int32)
+    return counts, offsets, sorted_pairs
+
+
+def moe_gemm_ref(a_hat, a_rows_are_pairs, topk, ids, w_hat_of, n, bound=True,
+                 bound_dtype=np.float64, pairs=None):
+    """Y_ref[p] = A_row(p) . W_hat_{ids[p]}^T for every pair p (or only for the
+    pairs listed in `pairs`).
+
+    a_hat: float64 [T,K] (gate_up: row of pair p is t = p // topk) or [P,K]
+           (down: row of pair p is p).
+    w_hat_of(e) -> float64 [N,K] exact dequantized weights of expert e.
+    Returns (Y_ref [len(pairs), N], B or None, pairs)."""
+    flat = np.asarray(ids, dtype=np.int64).ravel()
+    P = flat.size
+    if pairs is None:
+        pairs = np.arange(P)
+    pairs = np.asarray(pairs, dtype=np.int64)
+    y = np.zeros((pairs.size, n), dtype=np.float64)
+    b = np.zeros((pairs.size, n), dtype=np.float64) if bound else None
+    experts = flat[pairs]
+    for e in np.unique(experts):
+        sel = np.nonzero(experts == e)[0]
+        p = pairs[sel]
+        rows = p if a_rows_are_pairs else p // topk
+        ye, be = gemm_ref(a_hat[rows], w_hat_of(int(e)), bound=bound, bound_dtype=bound_dtype)
+        y[sel] = ye
+        if bound:
+            b[sel] = be
+    return y, b, pairs

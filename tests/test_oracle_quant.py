@@ -1,0 +1,205 @@
+"""Pins for the oracle's quantizers, packing, dequantization and FP8 rows:
+the pages' worked examples, brute-force nearest-code searches on small inputs,
+and invariants."""
+import numpy as np
+import pytest
+import torch
+
+from conftest import read_golden
+from oracle import codecs, quant
+
+G = read_golden("worked_examples.txt")
+
+
+def test_worked_example_int4():
+    ex = G["int4_example"]
+    q = quant.quant_int4_sym_fixed_scale(np.array([ex["w"]]), ex["s"])
+    assert q[0] == ex["q"]
+    assert abs(q[0] * ex["s"] - ex["restored"]) < 1e-15
+    lo, hi = G["int4_range"]["lo"], G["int4_range"]["hi"]
+    # out-of-range values are limited (clamped) to the signed 4-bit range
+    q2 = quant.quant_int4_sym_fixed_scale(np.array([0.9, -0.9, 100.0, -100.0]), 0.1)
+    assert list(q2) == [hi, lo, hi, lo]
+
+
+def test_worked_example_dot():
+    ex = G["dot_example"]
+    w = np.array(ex["w"])
+    x = np.array(ex["x"])
+    assert abs(w @ x - ex["exact"]) < 1e-15
+    q = quant.quant_int4_sym_fixed_scale(w, 0.1)
+    assert list(q) == [3, -1]
+    wq = q * 0.1
+    assert np.allclose(wq, ex["wq"], atol=1e-15)
+    assert abs(wq @ x - ex["quantized"]) < 1e-15
+
+
+def test_worked_example_storage():
+    ex = G["storage_example"]
+    g = int(ex["group"])
+    assert quant.storage_bytes(1, g, quant.FMT_INT4_SYM) == ex["bytes"]
+    assert quant.bits_per_value(quant.FMT_INT4_SYM) == ex["bits_per_value"]
+    # same formula, extended: packed 4-bit zero point, and MX (8-bit scale per 32)
+    assert quant.bits_per_value(quant.FMT_UINT4_ZP) == 4.15625
+    assert quant.bits_per_value(quant.FMT_MXFP4) == 4.25
+    # the dense FFN up-projection weight in the asymmetric format
+    assert quant.storage_bytes(14336, 4096, quant.FMT_UINT4_ZP) == 30507008
+
+
+def _brute_nearest(t, cands):
+    """nearest candidate value to t; ties to the even candidate value"""
+    d = np.abs(cands - t)
+    best = cands[d == d.min()]
+    if len(best) == 1:
+        return best[0]
+    ev = [b for b in best if int(b) % 2 == 0]
+    return ev[0]
+
+
+def test_int4_sym_brute_force():
+    r = np.random.default_rng(10)
+    w = r.normal(0, 0.02, size=(6, 256)).astype(np.float32)
+    w[0, :128] = 0.0                      # an all-zero group
+    w[1, :128] = 0.003                    # a constant group
+    q, sbits = quant.quant_int4_sym(w)
+    s = codecs.bf16_value(sbits).astype(np.float64)
+    cands = np.arange(-8, 8, dtype=np.float64)
+    for n in range(w.shape[0]):
+        for g in range(2):
+            amax = np.abs(w[n, g * 128:(g + 1) * 128]).max()
+            # scale: bf16 of the fp32 quotient amax/7 (torch conversions as the reference)
+            s32 = torch.tensor(float(amax), dtype=torch.float32) / 7.0
+            assert sbits[n, g] == s32.to(torch.bfloat16).view(torch.int16).item() & 0xFFFF
+            for k in range(g * 128, (g + 1) * 128):
+                if s[n, g] == 0:
+                    assert q[n, k] == 0
+                else:
+                    assert q[n, k] == _brute_nearest(float(w[n, k]) / s[n, g], cands)
+    assert q.min() >= -8 and q.max() <= 7
+    assert (q[0, :128] == 0).all() and s[0, 0] == 0
+
+
+def test_int4_sym_error_bound():
+    w = np.random.default_rng(11).normal(0, 0.02, size=(64, 1024)).astype(np.float32)
+    q, sbits = quant.quant_int4_sym(w)
+    wq = quant.dequant(quant.FMT_INT4_SYM, quant.pack_nibbles(q), sbits).astype(np.float64)
+    s = np.repeat(codecs.bf16_value(sbits).astype(np.float64), 128, axis=1)
+    # with the scale from amax/7 the clamp never binds, so |w - w_hat| <= s/2
+    assert (np.abs(w - wq) <= s / 2 + 1e-12).all()
+
+
+def test_uint4_zp_brute_force_and_invariants():
+    r = np.random.default_rng(12)
+    w = r.normal(0, 0.02, size=(5, 256)).astype(np.float32)
+    w[2, 128:] = 0.01                     # constant group -> s = 0
+    w[3, :128] = np.abs(w[3, :128]) + 0.05  # all positive -> z clamps at 0
+    u, sbits, z = quant.quant_uint4_zp(w)
+    s = codecs.bf16_value(sbits).astype(np.float64)
+    assert u.max() <= 15 and z.max() <= 15
+    for n in range(w.shape[0]):
+        for g in range(2):
+            blk = w[n, g * 128:(g + 1) * 128].astype(np.float64)
+            if s[n, g] == 0:
+                assert z[n, g] == 0 and (u[n, g * 128:(g + 1) * 128] == 0).all()
+                continue
+            zz = min(max(_brute_nearest(-blk.min() / s[n, g], np.arange(-64, 64.0)), 0), 15)
+            assert z[n, g] == zz
+            for i, wk in enumerate(blk):
+                t = wk / s[n, g]
+                v = _brute_nearest(t, np.arange(-64, 64.0)) + zz
+                assert u[n, g * 128 + i] == min(max(v, 0), 15)
+    wq = quant.dequant(quant.FMT_UINT4_ZP, quant.pack_nibbles(u), sbits, z).astype(np.float64)
+    sf = np.repeat(s, 128, axis=1)
+    # where the group range contains 0 the restore error is at most one step s;
+    # a one-signed group (row 3) is where the min-max zero point clamps at 0
+    wg = w.reshape(5, 2, 128)
+    spans0 = np.repeat((wg.min(axis=2) <= 0) & (wg.max(axis=2) >= 0), 128, axis=1)
+    ok = (sf > 0) & spans0
+    assert (np.abs(w - wq)[ok] <= sf[ok] + 1e-12).all()
+    assert not spans0[3, 0]
+
+
+def test_mxfp4_rule_brute_force():
+    r = np.random.default_rng(13)
+    w = r.normal(0, 0.02, size=(4, 128)).astype(np.float32)
+    w[0, :32] = 0.0
+    w[1, 32:64] *= 1e-30                  # tiny block
+    codes, e = quant.quant_mxfp4(w)
+    assert e[0, 0] == 0 and (codes[0, :32] == 0).all()
+    vals = np.concatenate([codecs.E2M1_MAG, -codecs.E2M1_MAG])
+    for n in range(4):
+        for b in range(4):
+            blk = w[n, 32 * b:32 * (b + 1)].astype(np.float64)
+            amax = np.abs(blk).max()
+            if amax == 0:
+                continue
+            X = int(e[n, b]) - 127
+            # the shared exponent puts amax in [4, 8) times the scale
+            assert 4.0 <= amax / 2.0 ** X < 8.0
+            for i, wk in enumerate(blk):
+                t = min(max(wk / 2.0 ** X, -6.0), 6.0)
+                d = np.abs(codecs.E2M1_MAG - abs(t))
+                cand = np.nonzero(d == d.min())[0]
+                mag = cand[0] if len(cand) == 1 else [c for c in cand if c % 2 == 0][0]
+                assert codes[n, 32 * b + i] & 7 == mag
+                assert bool(codes[n, 32 * b + i] & 8) == bool(wk < 0)
+
+
+def test_pack_unpack_all_bytes():
+    p = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    u = quant.unpack_nibbles(p)
+    assert (u[0, 0::2] == np.arange(256) % 16).all() and (u[0, 1::2] == np.arange(256) // 16).all()
+    assert np.array_equal(quant.pack_nibbles(u), p)
+    r = np.random.default_rng(14)
+    for n in (1, 7, 40):
+        for k in (128, 256):
+            c = r.integers(0, 16, size=(n, k))
+            assert np.array_equal(quant.unpack_nibbles(quant.pack_nibbles(c)), c)
+    # two's complement packing of signed codes
+    q = np.array([[-8, -1, 0, 7]])
+    assert list(quant.pack_nibbles(q)[0]) == [0xF8, 0x70]
+    assert list(quant.nibble_to_int4(quant.unpack_nibbles(quant.pack_nibbles(q)))[0]) == [-8, -1, 0, 7]
+
+
+def test_dequant_exact_and_negative_zero():
+    r = np.random.default_rng(15)
+    for fmt in quant.FORMATS:
+        w = r.normal(0, 0.02, size=(8, 256)).astype(np.float32)
+        st = quant.quantize(fmt, w)
+        d32 = quant.dequant(fmt, st["codes"], st["scales"], st["zeros"])
+        # recompute in fp64 from the parts: the fp32 result must equal it exactly
+        u = quant.unpack_nibbles(st["codes"]).astype(np.float64)
+        if fmt == quant.FMT_MXFP4:
+            ref = codecs.e2m1_value(u.astype(np.uint8)) * np.repeat(codecs.e8m0_value(st["scales"]), 32, 1)
+        else:
+            s = np.repeat(codecs.bf16_value(st["scales"]).astype(np.float64), 128, 1)
+            if fmt == quant.FMT_INT4_SYM:
+                ref = np.where(u >= 8, u - 16, u) * s
+            else:
+                ref = (u - np.repeat(st["zeros"].astype(np.float64), 128, 1)) * s
+        assert np.array_equal(d32.astype(np.float64), ref)
+    p = np.full((1, 16), 0x88, dtype=np.uint8)          # every code 8 = E2M1 -0
+    d = quant.dequant(quant.FMT_MXFP4, p, np.full((1, 1), 127, np.uint8))
+    assert (d == 0).all() and np.signbit(d).all()
+
+
+def test_fp8_rows_brute_force_and_torch():
+    r = np.random.default_rng(16)
+    x32 = r.normal(0, 1, size=(6, 256)).astype(np.float32)
+    x32[1] *= 20.0
+    x32[2] = 0.0
+    x32[3, 5] = -300.0
+    from synthetic import to_bf16_bits
+    xb = to_bf16_bits(x32)
+    codes, s = quant.quant_fp8_rows(xb)
+    x = codecs.bf16_value(xb)
+    assert s[2] == 0 and (codes[2] == 0).all()
+    for m in range(6):
+        amax = np.float32(np.abs(x[m]).max())
+        assert s[m] == np.float32(amax) / np.float32(448.0)
+        if s[m] == 0:
+            continue
+        qf = (torch.from_numpy(x[m]) / torch.tensor(s[m])).to(torch.float8_e4m3fn)
+        assert np.array_equal(codes[m], qf.view(torch.uint8).numpy())
+        # the row maximum lands on (or next to) the largest code
+        assert codecs.e4m3_value(codes[m]).__abs__().max() == 448.0
