@@ -1,0 +1,195 @@
+/*
+ * hm.h -- C ABI of the MI355X (gfx950) low-bit GEMM library.
+ *
+ * The library computes a linear layer Y[M,N] = X[M,K] . W_hat[N,K]^T whose
+ * weights are stored in 4-bit form and dequantized inside the kernel, and the
+ * grouped (MoE) variant in which every routed (token, expert) pair runs against
+ * its expert's weights.  Sources, cited by page and section:
+ *   - linear layer as X times W transposed, weights read once and reused over
+ *     the M rows, about 2*M*N*K flops: ywsung.com note "How vLLM Humming
+ *     computes 4 bits", section on one token vs many tokens;
+ *   - 4-bit codes with a scale, q = round(w/s), restored as s*q, signed range
+ *     -8..7, one 16-bit scale per 128 weights: same note, section on scales;
+ *   - one common representation of weights, scales and zero points, then
+ *     padding and re-ordering for the device, done once before inference
+ *     (transform, then call the layer): same note, section on layout, and the
+ *     aihaber.org article, Architecture;
+ *   - the formats (INT4, MXFP4) and activation widths (16-bit, 8-bit):
+ *     cocoloop.cn news item, format list; aihaber.org, hardware and format
+ *     support; per-token FP8 activations: ywsung.com note, section on weight
+ *     format / activation / backend;
+ *   - tokens split per expert so that every expert's GEMM has its own M, and a
+ *     grouped path over all experts: ywsung.com note, section on one token vs
+ *     many tokens; aihaber.org, Performance.
+ *
+ * Conventions (every entry point):
+ *   - Tensor pointers are DEVICE pointers unless stated; descriptors are host
+ *     pointers.  The caller owns every buffer (weights, inputs, outputs,
+ *     workspaces); the library allocates no device memory and keeps no state
+ *     between calls.
+ *   - Calls are asynchronous on `stream` (NULL = the default stream), never
+ *     synchronize, and are safe to call from several host threads.
+ *   - All argument checks happen before any launch.  On any error the call
+ *     returns a non-zero hm_status and no kernel has been launched; outputs are
+ *     untouched.  HM_ERR_HIP reports a failed launch.
+ *   - Matrices are row-major and contiguous.  bf16 values are passed as their
+ *     16-bit patterns (uint16_t).  Outputs are bf16, rounded to nearest even
+ *     from an fp32 accumulator.
+ *   - K must be a multiple of 128 for every format.  N is arbitrary.
+ *   - Alignment: w_dev and workspaces 256 bytes, every other pointer 16 bytes
+ *     (HM_ERR_ALIGN otherwise).
+ *   - Inputs are finite; NaN or Inf in X, scales or weights gives unspecified
+ *     (but memory-safe) results.
+ */
+#ifndef HM_H
+#define HM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HM_ABI_VERSION 1
+
+typedef enum hm_status {
+  HM_OK = 0,
+  HM_ERR_NULL = 1,        /* a required pointer is NULL */
+  HM_ERR_SHAPE = 2,       /* bad size, group or count */
+  HM_ERR_ALIGN = 3,       /* pointer not aligned as required */
+  HM_ERR_UNSUPPORTED = 4, /* unknown weight format or format/activation pair */
+  HM_ERR_WORKSPACE = 5,   /* buffer smaller than its size query */
+  HM_ERR_HIP = 6,         /* a HIP launch failed */
+  HM_ERR_ABI = 7          /* descriptor abi field != HM_ABI_VERSION */
+} hm_status;
+
+/* Weight number format (the "number format / scale unit / zero point" of the
+ * quantization description, ywsung.com note, section on layout, figure on the
+ * quantization description). */
+typedef enum hm_wfmt {
+  HM_W_INT4_SYM = 0, /* signed 4-bit two's complement q, bf16 scale per 128 along K: w = s*q */
+  HM_W_UINT4_ZP = 1, /* unsigned 4-bit u, bf16 scale + 4-bit zero point per 128: w = s*(u-z) */
+  HM_W_MXFP4 = 2     /* E2M1 codes, E8M0 scale per 32 along K: w = e2m1(c) * 2^(b-127) */
+} hm_wfmt;
+
+/* Activation format (the compute option choosing A16 or A8). */
+typedef enum hm_afmt {
+  HM_A_BF16 = 0,        /* X is bf16 [M,K]; x_row_scale unused (may be NULL) */
+  HM_A_FP8_ROWSCALE = 1 /* X is OCP E4M3 bytes [M,K] with one fp32 scale per row: x = e4m3(c)*s[m] */
+} hm_afmt;
+
+/* Supported pairs: INT4_SYM and UINT4_ZP with HM_A_BF16 (W4A16);
+ *                  MXFP4 with HM_A_FP8_ROWSCALE (W4A8-MXFP4). */
+
+/* Layer description (shapes, number format, group).  num_experts is 1 for a
+ * dense layer.  group must be 128 for the INT4 formats and 32 for MXFP4. */
+typedef struct hm_wdesc {
+  int32_t abi;         /* HM_ABI_VERSION */
+  int32_t wfmt;        /* hm_wfmt */
+  int32_t group;       /* elements per scale along K */
+  int32_t num_experts; /* >= 1 */
+  int64_t n;           /* output features (rows of W), >= 1 */
+  int64_t k;           /* input features, multiple of 128, >= 128 */
+} hm_wdesc;
+
+/* ---------------------------------------------------------------- weights */
+
+/* Bytes of the device weight buffer for `d` (all experts). */
+hm_status hm_transform_size(const hm_wdesc* d, size_t* bytes);
+
+/* Repack the standard format into the device layout (padding N to 16 and
+ * re-ordering codes, scales and zero points so that each 64-lane wave reads
+ * one 1 KiB tile of 16 columns x 128 K per 16-byte-per-lane load).  Run once
+ * per weight, before inference.
+ *   codes  [E][N][K/2] bytes, element k=2j in the low nibble of byte j,
+ *          k=2j+1 in the high nibble (two's complement for INT4_SYM, unsigned
+ *          for UINT4_ZP, E2M1 bits for MXFP4).
+ *   scales INT4 formats: bf16 [E][N][K/128]; MXFP4: E8M0 bytes [E][N][K/32].
+ *   zeros  UINT4_ZP only: bytes [E][N][K/128], low nibble used; else NULL.
+ *   w_dev  output, w_bytes >= hm_transform_size.  Opaque; valid only for the
+ *          same descriptor. */
+hm_status hm_transform(const hm_wdesc* d, const uint8_t* codes, const void* scales,
+                       const uint8_t* zeros, void* w_dev, size_t w_bytes, hipStream_t stream);
+
+/* Exact dequantization of one expert of a transformed buffer into fp32
+ * out[N][K] (every restored weight is exactly representable in fp32). */
+hm_status hm_dequant(const hm_wdesc* d, const void* w_dev, size_t w_bytes, int32_t expert,
+                     float* out, hipStream_t stream);
+
+/* -------------------------------------------------------------- activations */
+
+/* Per-token FP8: for each row m, s[m] = amax_k |x[m,k]| / 448 (fp32 division),
+ * x8[m,k] = E4M3(x[m,k] / s[m]) with the division in fp32, round to nearest
+ * even, saturating at +-448; a row of zeros gives s = 0 and zero codes.
+ *   x bf16 [m][k]; x8 bytes [m][k]; row_scale fp32 [m].  k >= 1 (any k). */
+hm_status hm_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* x8,
+                            float* row_scale, hipStream_t stream);
+
+/* ---------------------------------------------------------------- dense GEMM */
+
+/* Workspace bytes hm_gemm needs for this shape (may be 0). */
+hm_status hm_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t m, size_t* bytes);
+
+/* y[m][n] = bf16( sum_k x_hat[m,k] * w_hat[n,k] ), fp32 accumulation.
+ *   w_dev      transformed weights (num_experts must be 1).
+ *   x          bf16 [m][k] (HM_A_BF16) or E4M3 bytes [m][k] (HM_A_FP8_ROWSCALE).
+ *   x_row_scale fp32 [m] for HM_A_FP8_ROWSCALE, else ignored.
+ *   y          bf16 [m][n].
+ *   ws         workspace of at least hm_gemm_workspace_size bytes (NULL if 0).
+ * m = 0 is a no-op. */
+hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* x,
+                  const float* x_row_scale, int64_t m, uint16_t* y, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/* A short text naming the kernel path and tile configuration hm_gemm selects
+ * for this shape (so a caller can confirm what actually runs). */
+hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* buf, size_t buf_len);
+
+/* ------------------------------------------------------------------- MoE */
+
+/* Workspace bytes hm_moe_sort needs (0 in this version; kept for the ABI). */
+hm_status hm_moe_sort_workspace_size(int64_t t, int32_t topk, int32_t num_experts, size_t* bytes);
+
+/* Expert sort: pairs p = t*topk + j with ids topk_ids[t][j].
+ *   counts[e]        number of pairs routed to expert e        (int32 [E])
+ *   offsets[e]       exclusive prefix sum, offsets[E] = pairs  (int32 [E+1])
+ *   sorted_pairs[i]  pair ids grouped by expert, ascending within each
+ *                    expert (stable)                           (int32 [t*topk])
+ * Ids outside [0, E) are dropped (not counted, not placed); offsets[E] then
+ * falls short of t*topk.  1 <= num_experts <= 512, topk <= num_experts,
+ * t*topk < 2^31.  t = 0 is a no-op. */
+hm_status hm_moe_sort(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t num_experts,
+                      int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes hm_moe_gemm needs for t tokens and topk. */
+hm_status hm_moe_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
+                                     size_t* bytes);
+
+/* Grouped GEMM over all experts in one call:
+ *   y[p][:] = bf16( A_row(p) . W_hat_{e(p)}^T ) for every routed pair p,
+ * where e(p) is the expert whose segment of sorted_pairs holds p.
+ *   a            a_rows_are_pairs = 0: activations [t][k] and pair p uses row
+ *                p / topk (gate/up projection);  = 1: [t*topk][k] and pair p
+ *                uses row p (down projection).  bf16, or E4M3 bytes with
+ *                a_row_scale (one fp32 per row of a) for HM_A_FP8_ROWSCALE.
+ *   offsets, sorted_pairs  as produced by hm_moe_sort (device).
+ *   y            bf16 [t*topk][n], rows in pair order; rows of dropped pairs
+ *                are not written.
+ *   ws           at least hm_moe_gemm_workspace_size bytes.
+ * t = 0 is a no-op. */
+hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* a,
+                      const float* a_row_scale, int32_t a_rows_are_pairs, int64_t t,
+                      int32_t topk, const int32_t* offsets, const int32_t* sorted_pairs,
+                      uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* hm_status_string(hm_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HM_H */

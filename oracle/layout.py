@@ -29,7 +29,8 @@ Region B, scales (starts at the next 256-byte boundary):
 Region C, zero points (uint4_zp only, next 256-byte boundary): 8 bytes per
   ((e*NB + nb)*KG + g); byte c//2, nibble c%2 (low nibble for even c) = zero
   point of column 16*nb + c, group g.  Padding 0.
-Total size: end of the last region rounded up to 256 bytes.
+Total size: end of the last region rounded up to 256 bytes.  Every byte not
+named above (the alignment gaps between regions) is zero.
 """
 import numpy as np
 

@@ -1,0 +1,225 @@
+"""Python binding of the MI355X low-bit GEMM library (libhm.so).
+
+Thin argument marshalling only: every function takes torch tensors (device
+memory), passes their data pointers, sizes and the current HIP stream to the C
+entry point of the same name, and raises HmError on a non-zero status.  All
+work runs in the library's HIP kernels.  Importing this package fails loudly if
+libhm.so has not been built (python -m quantized_gemm_int4_amd.build).
+
+The C functions are declared and documented in include/hm.h.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhm.so")
+
+HM_ABI_VERSION = 1
+HM_W_INT4_SYM, HM_W_UINT4_ZP, HM_W_MXFP4 = 0, 1, 2
+HM_A_BF16, HM_A_FP8_ROWSCALE = 0, 1
+WFMT = {"int4_sym": HM_W_INT4_SYM, "uint4_zp": HM_W_UINT4_ZP, "mxfp4": HM_W_MXFP4}
+STATUS = {0: "HM_OK", 1: "HM_ERR_NULL", 2: "HM_ERR_SHAPE", 3: "HM_ERR_ALIGN",
+          4: "HM_ERR_UNSUPPORTED", 5: "HM_ERR_WORKSPACE", 6: "HM_ERR_HIP", 7: "HM_ERR_ABI"}
+
+
+class HmError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({lib.hm_status_string(code).decode()})")
+
+
+class hm_wdesc(ctypes.Structure):
+    _fields_ = [("abi", ctypes.c_int32), ("wfmt", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
+
+
+def wdesc(wfmt, n, k, num_experts=1):
+    """Layer description; wfmt is an HM_W_* value or 'int4_sym' / 'uint4_zp' / 'mxfp4'."""
+    f = WFMT.get(wfmt, wfmt)
+    return hm_wdesc(HM_ABI_VERSION, int(f), 32 if f == HM_W_MXFP4 else 128, int(num_experts),
+                    int(n), int(k))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m quantized_gemm_int4_amd.build` (needs hipcc)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D = ctypes.POINTER(hm_wdesc)
+    sig = {
+        "hm_transform_size": [D, ctypes.POINTER(SZ)],
+        "hm_transform": [D, P, P, P, P, SZ, P],
+        "hm_dequant": [D, P, SZ, I32, P, P],
+        "hm_quant_fp8_rows": [P, I64, I64, P, P, P],
+        "hm_gemm_workspace_size": [D, I32, I64, ctypes.POINTER(SZ)],
+        "hm_gemm": [D, P, I32, P, P, I64, P, P, SZ, P],
+        "hm_gemm_plan": [D, I32, I64, ctypes.c_char_p, SZ],
+        "hm_moe_sort_workspace_size": [I64, I32, I32, ctypes.POINTER(SZ)],
+        "hm_moe_sort": [P, I64, I32, I32, P, P, P, P, SZ, P],
+        "hm_moe_gemm_workspace_size": [D, I32, I64, I32, ctypes.POINTER(SZ)],
+        "hm_moe_gemm": [D, P, I32, P, P, I32, I64, I32, P, P, P, P, SZ, P],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.hm_status_string.argtypes = [ctypes.c_int]
+    L.hm_status_string.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ok(fn, code):
+    if code != 0:
+        raise HmError(fn, code)
+
+
+def _need(t, dtype, numel, name):
+    if t is None:
+        return
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype or t.numel() < numel:
+        raise ValueError(f"{name}: need a contiguous CUDA {dtype} tensor with >= {numel} elements")
+
+
+# --------------------------------------------------------------------- weights
+
+def hm_transform_size(desc):
+    out = ctypes.c_size_t()
+    _ok("hm_transform_size", lib.hm_transform_size(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
+
+
+def hm_transform(desc, codes, scales, zeros=None, w_dev=None, stream=None):
+    """codes uint8 [E,N,K/2]; scales int16/uint16 bits [E,N,K/128] (INT4) or uint8
+    [E,N,K/32] (MXFP4); zeros uint8 [E,N,K/128] (UINT4_ZP).  Returns w_dev (uint8)."""
+    nbytes = hm_transform_size(desc)
+    if w_dev is None:
+        w_dev = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    E, n, k = desc.num_experts, desc.n, desc.k
+    _need(codes, torch.uint8, E * n * k // 2, "codes")
+    _need(w_dev, torch.uint8, nbytes, "w_dev")
+    _ok("hm_transform", lib.hm_transform(ctypes.byref(desc), _ptr(codes), _ptr(scales), _ptr(zeros),
+                                         _ptr(w_dev), w_dev.numel(), _stream(stream)))
+    return w_dev
+
+
+def hm_dequant(desc, w_dev, expert=0, out=None, stream=None):
+    if out is None:
+        out = torch.empty(desc.n, desc.k, dtype=torch.float32, device=w_dev.device)
+    _need(out, torch.float32, desc.n * desc.k, "out")
+    _ok("hm_dequant", lib.hm_dequant(ctypes.byref(desc), _ptr(w_dev), w_dev.numel(), int(expert),
+                                     _ptr(out), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------ activations
+
+def hm_quant_fp8_rows(x, x8=None, row_scale=None, stream=None):
+    """x bf16 [m,k] -> (E4M3 bytes uint8 [m,k], fp32 row scales [m])."""
+    m, k = x.shape
+    _need(x, torch.bfloat16, m * k, "x")
+    if x8 is None:
+        x8 = torch.empty(m, k, dtype=torch.uint8, device=x.device)
+    if row_scale is None:
+        row_scale = torch.empty(m, dtype=torch.float32, device=x.device)
+    _ok("hm_quant_fp8_rows", lib.hm_quant_fp8_rows(_ptr(x), m, k, _ptr(x8), _ptr(row_scale),
+                                                   _stream(stream)))
+    return x8, row_scale
+
+
+# -------------------------------------------------------------------- dense GEMM
+
+def _afmt(desc):
+    return HM_A_FP8_ROWSCALE if desc.wfmt == HM_W_MXFP4 else HM_A_BF16
+
+
+def hm_gemm_workspace_size(desc, afmt, m):
+    out = ctypes.c_size_t()
+    _ok("hm_gemm_workspace_size", lib.hm_gemm_workspace_size(ctypes.byref(desc), int(afmt), int(m),
+                                                             ctypes.byref(out)))
+    return out.value
+
+
+def hm_gemm_plan(desc, afmt, m):
+    buf = ctypes.create_string_buffer(256)
+    _ok("hm_gemm_plan", lib.hm_gemm_plan(ctypes.byref(desc), int(afmt), int(m), buf, 256))
+    return buf.value.decode()
+
+
+def hm_gemm(desc, w_dev, x, x_row_scale=None, y=None, ws=None, afmt=None, stream=None):
+    """y[m,n] = x_hat . w_hat^T in bf16.  x: bf16 [m,k] (W4A16) or uint8 E4M3
+    [m,k] with fp32 x_row_scale [m] (W4A8-MXFP4)."""
+    afmt = _afmt(desc) if afmt is None else afmt
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty(m, desc.n, dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, m * desc.n, "y")
+    need = hm_gemm_workspace_size(desc, afmt, m)
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _ok("hm_gemm", lib.hm_gemm(ctypes.byref(desc), _ptr(w_dev), int(afmt), _ptr(x), _ptr(x_row_scale),
+                               m, _ptr(y), _ptr(ws) if need else None,
+                               ws.numel() if (need and ws is not None) else 0, _stream(stream)))
+    return y
+
+
+# -------------------------------------------------------------------------- MoE
+
+def hm_moe_sort_workspace_size(t, topk, num_experts):
+    out = ctypes.c_size_t()
+    _ok("hm_moe_sort_workspace_size", lib.hm_moe_sort_workspace_size(int(t), int(topk),
+                                                                     int(num_experts), ctypes.byref(out)))
+    return out.value
+
+
+def hm_moe_sort(topk_ids, num_experts, counts=None, offsets=None, sorted_pairs=None, stream=None):
+    """topk_ids int32 [t, topk] -> (counts [E], offsets [E+1], sorted_pairs [t*topk])."""
+    t, topk = topk_ids.shape
+    dev = topk_ids.device
+    _need(topk_ids, torch.int32, t * topk, "topk_ids")
+    counts = torch.empty(num_experts, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    sorted_pairs = (torch.empty(t * topk, dtype=torch.int32, device=dev)
+                    if sorted_pairs is None else sorted_pairs)
+    _ok("hm_moe_sort", lib.hm_moe_sort(_ptr(topk_ids), t, topk, int(num_experts), _ptr(counts),
+                                       _ptr(offsets), _ptr(sorted_pairs), None, 0, _stream(stream)))
+    return counts, offsets, sorted_pairs
+
+
+def hm_moe_gemm_workspace_size(desc, afmt, t, topk):
+    out = ctypes.c_size_t()
+    _ok("hm_moe_gemm_workspace_size", lib.hm_moe_gemm_workspace_size(ctypes.byref(desc), int(afmt),
+                                                                     int(t), int(topk), ctypes.byref(out)))
+    return out.value
+
+
+def hm_moe_gemm(desc, w_dev, a, offsets, sorted_pairs, t, topk, a_rows_are_pairs, a_row_scale=None,
+                y=None, ws=None, afmt=None, stream=None):
+    """Grouped GEMM; returns y bf16 [t*topk, n] in pair order."""
+    afmt = _afmt(desc) if afmt is None else afmt
+    P = t * topk
+    if y is None:
+        y = torch.empty(P, desc.n, dtype=torch.bfloat16, device=a.device)
+    _need(y, torch.bfloat16, P * desc.n, "y")
+    need = hm_moe_gemm_workspace_size(desc, afmt, t, topk)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=a.device)
+    _ok("hm_moe_gemm", lib.hm_moe_gemm(ctypes.byref(desc), _ptr(w_dev), int(afmt), _ptr(a),
+                                       _ptr(a_row_scale), int(a_rows_are_pairs), int(t), int(topk),
+                                       _ptr(offsets), _ptr(sorted_pairs), _ptr(y), _ptr(ws),
+                                       ws.numel(), _stream(stream)))
+    return y

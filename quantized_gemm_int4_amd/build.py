@@ -1,0 +1,70 @@
+"""Build of the HIP library libhm.so (gfx950) in-tree.
+
+    python -m quantized_gemm_int4_amd.build
+
+compiles every source under csrc/ with hipcc into _build/ at the repository
+root and links quantized_gemm_int4_amd/libhm.so.  It always recompiles.
+"""
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libhm.so")
+SOURCES = ["k_weights.hip", "k_fp8.hip", "k_moe.hip", "k_gemm_stream.hip", "k_gemm_tile.hip",
+           "hm_api.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc():
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (set HIPCC)")
+
+
+def compile_flags():
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",
+            # keep the compiler from emitting packed-fp32 VALU instructions
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def _compile(src, obj, extra):
+    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + compile_flags() + extra
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns about the device-only feature flag; drop those lines
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {src}\n{' '.join(cmd)}\n{err}")
+    return err
+
+
+def build(verbose=False, jobs=None, extra=None):
+    """Compile all sources and link libhm.so; returns the library path."""
+    extra = list(extra or [])
+    bdir = os.path.join(ROOT, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2) - 1), 8)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = [ex.submit(_compile, s, o, extra) for s, o in zip(SOURCES, objs)]
+        for s, f in zip(SOURCES, futs):
+            w = f.result()
+            if verbose and w.strip():
+                print(f"[{s}]\n{w}", file=sys.stderr)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,110 @@
+// Shared device helpers and the device weight-layout geometry.
+//
+// Device layout ("layout 1") for E experts, N columns, K (multiple of 128):
+//   NB = ceil(N/16) column blocks, KG = K/128 steps along K.
+//   Region A (codes): tile (e, nb, g) of 1024 bytes at ((e*NB + nb)*KG + g)*1024;
+//     64 slots of 16 bytes, slot L = column 16*nb + L%16, quarter h = L/16.
+//     int4:  byte 4*j+b of slot L holds k = 128g + 32j + 8h + 2b (low nibble), k+1 (high);
+//            the u32 j of a slot is the 8 K-values one lane feeds to the j-th
+//            16x16x32 bf16 MFMA of the step.  INT4_SYM is stored offset-binary (q+8).
+//     mxfp4: byte b of slot L holds k = 128g + 32h + 2b (low), k+1 (high); the
+//            16 bytes are the 32 E2M1 values one lane feeds to a 16x16x128
+//            scaled MFMA.
+//     Columns >= N hold the value-zero code.
+//   Region B (scales, 256-aligned): int4: bf16 [E][NB][KG][16];
+//     mxfp4: bytes [E][NB][ceil(KG/4)][64 lanes][4], byte g%4 of lane L's u32
+//     = E8M0 of (column 16nb + L%16, 32-block 4g + L/16).
+//   Region C (zero points, UINT4_ZP only, 256-aligned): [E][NB][KG] u64,
+//     nibble c = zero point of column 16nb + c.
+//   Total = end of the last region rounded up to 256 bytes; gap bytes are zero.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace hm {
+
+enum WFmt : int { W_INT4_SYM = 0, W_UINT4_ZP = 1, W_MXFP4 = 2 };
+
+struct Geom {
+  int64_t E, N, K, NB, KG, KG4;
+  size_t off_scales, off_zeros, total;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline Geom make_geom(int wfmt, int64_t E, int64_t N, int64_t K) {
+  Geom g;
+  g.E = E; g.N = N; g.K = K;
+  g.NB = (N + 15) / 16;
+  g.KG = K / 128;
+  g.KG4 = (g.KG + 3) / 4;
+  size_t a = (size_t)E * g.NB * g.KG * 1024;
+  size_t b = (wfmt == W_MXFP4) ? (size_t)E * g.NB * g.KG4 * 256 : (size_t)E * g.NB * g.KG * 32;
+  size_t c = (wfmt == W_UINT4_ZP) ? (size_t)E * g.NB * g.KG * 8 : 0;
+  g.off_scales = align256(a);
+  g.off_zeros = align256(g.off_scales + b);
+  g.total = align256(g.off_zeros + c);
+  return g;
+}
+
+// ------------------------------------------------------------------ vector types
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+
+// Two fp32 -> packed bf16 pair (round to nearest even), low half = a.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  f32x2_t v = {a, b};
+  bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Eight 4-bit unsigned codes (element i at bits 4i) -> eight bf16 of s*u + zs,
+// in element order, as four packed pairs.  The fp32 value s*u + zs = s*(u-z)
+// is exact (at most 12 significant bits), then rounded once to bf16.
+__device__ __forceinline__ u32x4_t dq8_u4(uint32_t w, float s, float zs) {
+  uint32_t lo = w & 0x0F0F0F0Fu;         // bytes: elements 0,2,4,6
+  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: elements 1,3,5,7
+  u32x4_t r;
+  r[0] = pack_bf16(__builtin_fmaf((float)(lo & 0xFF), s, zs), __builtin_fmaf((float)(hi & 0xFF), s, zs));
+  r[1] = pack_bf16(__builtin_fmaf((float)((lo >> 8) & 0xFF), s, zs), __builtin_fmaf((float)((hi >> 8) & 0xFF), s, zs));
+  r[2] = pack_bf16(__builtin_fmaf((float)((lo >> 16) & 0xFF), s, zs), __builtin_fmaf((float)((hi >> 16) & 0xFF), s, zs));
+  r[3] = pack_bf16(__builtin_fmaf((float)(lo >> 24), s, zs), __builtin_fmaf((float)(hi >> 24), s, zs));
+  return r;
+}
+
+// 16x16x32 bf16 MFMA: C[i][j] += sum_k A[i][k] B[k][j]; lane L supplies A row
+// L%16 and B column L%16 for K-quarter L/16 (8 values each); C: lane L holds
+// column L%16, rows 4*(L/16) + 0..3.
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 16x16x128 scaled MFMA, A = E2M1, B = E4M3 (measured operand layout on gfx950):
+//   A: lane L supplies row L%16, K = 32*(L/16) + 0..31 (16 bytes, even K in the
+//      low nibble);
+//   B: lane L supplies column L%16 with two 16-byte halves: b0 = K 16*(L/16) +
+//      0..15 and b1 = K 64 + 16*(L/16) + 0..15;
+//   scales: lane r + 16*b supplies the E8M0 byte of row/column r, K-block
+//      32b..32b+31, for each operand (sa for A, sb for B).
+//   C: same layout as the bf16 MFMA above.
+__device__ __forceinline__ f32x4_t mfma_fp4_fp8(u32x4_t a, u32x4_t b0, u32x4_t b1, f32x4_t c,
+                                                int sa, int sb) {
+  i32x8_t av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  i32x8_t bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, 0, sa, 0, sb);
+}
+
+}  // namespace hm

@@ -1,0 +1,330 @@
+// C ABI entry points: argument checks, tile-configuration choice and launches.
+// Every check runs before any launch; the library allocates nothing.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/hm.h"
+#include "common.h"
+#include "launch.h"
+
+#define HM_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace hm;
+
+constexpr int kStreamMaxRows = 32;   // rows handled by the streaming kernel (two 16-row blocks)
+constexpr int kGroupedGridStream = 2048;
+constexpr int kGroupedGridTile = 1024;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+hm_status check_desc(const hm_wdesc* d) {
+  if (!d) return HM_ERR_NULL;
+  if (d->abi != HM_ABI_VERSION) return HM_ERR_ABI;
+  if (d->wfmt != HM_W_INT4_SYM && d->wfmt != HM_W_UINT4_ZP && d->wfmt != HM_W_MXFP4)
+    return HM_ERR_UNSUPPORTED;
+  const int want_group = (d->wfmt == HM_W_MXFP4) ? 32 : 128;
+  if (d->group != want_group) return HM_ERR_SHAPE;
+  if (d->num_experts < 1 || d->n < 1 || d->k < 128 || (d->k % 128) != 0) return HM_ERR_SHAPE;
+  if (d->n > (1ll << 24) || d->k > (1ll << 24)) return HM_ERR_SHAPE;
+  return HM_OK;
+}
+
+hm_status check_pair(const hm_wdesc* d, int32_t afmt) {
+  if (afmt != HM_A_BF16 && afmt != HM_A_FP8_ROWSCALE) return HM_ERR_UNSUPPORTED;
+  const bool mx = (d->wfmt == HM_W_MXFP4);
+  if (mx != (afmt == HM_A_FP8_ROWSCALE)) return HM_ERR_UNSUPPORTED;
+  return HM_OK;
+}
+
+Geom geom_of(const hm_wdesc* d) { return make_geom(d->wfmt, d->num_experts, d->n, d->k); }
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return (s && *s) ? atoi(s) : dflt;
+}
+
+// ---------------------------------------------------------------- dense plan
+struct DensePlan {
+  bool stream;
+  StreamCfg sc;
+  int ksg;
+  size_t ws_bytes;
+};
+
+DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
+  DensePlan p{};
+  const Geom G = geom_of(d);
+  const int force = env_int("HM_FORCE_PATH", 0);  // 1 = streaming, 2 = tile
+  p.stream = (force == 1) || (force == 0 && m <= kStreamMaxRows);
+  if (force == 1 && m > kStreamMaxRows) p.stream = false;  // streaming handles <= 32 rows per block
+  if (!p.stream) return p;
+  p.sc.mb = (m <= 16) ? 1 : 2;
+  p.sc.nbw = env_int("HM_STREAM_NBW", G.NB >= 512 ? 2 : 1);
+  if (p.sc.nbw != 1 && p.sc.nbw != 2 && p.sc.nbw != 4) p.sc.nbw = 1;
+  const int64_t n_tiles = (G.NB + 4 * p.sc.nbw - 1) / (4 * p.sc.nbw);
+  const int64_t m_chunks = (m + 16 * p.sc.mb - 1) / (16 * p.sc.mb);
+  int64_t splits = env_int("HM_STREAM_SPLITS", 0);
+  if (splits <= 0) {
+    const int64_t target = 1024;
+    splits = (target + n_tiles * m_chunks - 1) / (n_tiles * m_chunks);
+  }
+  if (splits > G.KG) splits = G.KG;
+  if (splits < 1) splits = 1;
+  p.ksg = (int)((G.KG + splits - 1) / splits);
+  p.sc.splits = (int)((G.KG + p.ksg - 1) / p.ksg);
+  p.ws_bytes = (p.sc.splits > 1) ? (size_t)p.sc.splits * m * G.NB * 16 * sizeof(float) : 0;
+  return p;
+}
+
+// ---------------------------------------------------------------- MoE plan
+struct MoePlan {
+  int64_t P, max_s, max_t;
+  size_t off_su, off_tu, ws_bytes;
+  int nbw;
+};
+
+MoePlan plan_moe(const hm_wdesc* d, int64_t t, int32_t topk) {
+  MoePlan p{};
+  p.P = t * topk;
+  const int64_t act = (p.P < d->num_experts) ? p.P : d->num_experts;
+  p.max_s = act;
+  p.max_t = (p.P + kTileM - 1) / kTileM + act;
+  p.off_su = 256;
+  p.off_tu = align256(p.off_su + (size_t)p.max_s * 16);
+  p.ws_bytes = align256(p.off_tu + (size_t)p.max_t * 16);
+  p.nbw = 1;
+  return p;
+}
+
+}  // namespace
+
+// =====================================================================================
+
+HM_API const char* hm_status_string(hm_status s) {
+  switch (s) {
+    case HM_OK: return "ok";
+    case HM_ERR_NULL: return "null pointer";
+    case HM_ERR_SHAPE: return "bad shape, group or count";
+    case HM_ERR_ALIGN: return "misaligned pointer";
+    case HM_ERR_UNSUPPORTED: return "unsupported format or format/activation pair";
+    case HM_ERR_WORKSPACE: return "workspace too small";
+    case HM_ERR_HIP: return "HIP launch failed";
+    case HM_ERR_ABI: return "descriptor ABI version mismatch";
+  }
+  return "unknown status";
+}
+
+HM_API hm_status hm_transform_size(const hm_wdesc* d, size_t* bytes) {
+  hm_status s = check_desc(d);
+  if (s) return s;
+  if (!bytes) return HM_ERR_NULL;
+  *bytes = geom_of(d).total;
+  return HM_OK;
+}
+
+HM_API hm_status hm_transform(const hm_wdesc* d, const uint8_t* codes, const void* scales,
+                              const uint8_t* zeros, void* w_dev, size_t w_bytes,
+                              hipStream_t stream) {
+  hm_status s = check_desc(d);
+  if (s) return s;
+  if (!codes || !scales || !w_dev) return HM_ERR_NULL;
+  if (d->wfmt == HM_W_UINT4_ZP && !zeros) return HM_ERR_NULL;
+  if (!aligned(codes, 16) || !aligned(w_dev, 256)) return HM_ERR_ALIGN;
+  if (!aligned(scales, d->wfmt == HM_W_MXFP4 ? 1 : 2)) return HM_ERR_ALIGN;
+  const Geom G = geom_of(d);
+  if (w_bytes < G.total) return HM_ERR_WORKSPACE;
+  if (launch_transform(d->wfmt, G, codes, scales, zeros, (uint8_t*)w_dev, stream) != hipSuccess)
+    return HM_ERR_HIP;
+  return HM_OK;
+}
+
+HM_API hm_status hm_dequant(const hm_wdesc* d, const void* w_dev, size_t w_bytes, int32_t expert,
+                            float* out, hipStream_t stream) {
+  hm_status s = check_desc(d);
+  if (s) return s;
+  if (!w_dev || !out) return HM_ERR_NULL;
+  if (!aligned(w_dev, 256) || !aligned(out, 16)) return HM_ERR_ALIGN;
+  if (expert < 0 || expert >= d->num_experts) return HM_ERR_SHAPE;
+  const Geom G = geom_of(d);
+  if (w_bytes < G.total) return HM_ERR_WORKSPACE;
+  if (launch_dequant(d->wfmt, G, (const uint8_t*)w_dev, expert, out, stream) != hipSuccess)
+    return HM_ERR_HIP;
+  return HM_OK;
+}
+
+HM_API hm_status hm_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* x8,
+                                   float* row_scale, hipStream_t stream) {
+  if (m < 0 || k < 1) return HM_ERR_SHAPE;
+  if (m == 0) return HM_OK;
+  if (!x || !x8 || !row_scale) return HM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(row_scale, 16)) return HM_ERR_ALIGN;
+  if (launch_quant_fp8_rows(x, m, k, x8, row_scale, stream) != hipSuccess) return HM_ERR_HIP;
+  return HM_OK;
+}
+
+HM_API hm_status hm_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t m, size_t* bytes) {
+  hm_status s = check_desc(d);
+  if (s) return s;
+  if ((s = check_pair(d, afmt))) return s;
+  if (!bytes) return HM_ERR_NULL;
+  if (m < 0) return HM_ERR_SHAPE;
+  *bytes = (m == 0) ? 0 : plan_dense(d, m).ws_bytes;
+  return HM_OK;
+}
+
+HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* buf,
+                              size_t buf_len) {
+  hm_status s = check_desc(d);
+  if (s) return s;
+  if ((s = check_pair(d, afmt))) return s;
+  if (!buf || buf_len == 0) return HM_ERR_NULL;
+  if (m < 0) return HM_ERR_SHAPE;
+  const DensePlan p = plan_dense(d, m);
+  const char* w = d->wfmt == HM_W_MXFP4 ? "w4a8-mxfp4" : (d->wfmt == HM_W_UINT4_ZP ? "w4a16-uint4zp" : "w4a16-int4sym");
+  if (p.stream)
+    snprintf(buf, buf_len, "%s stream mb=%d nbw=%d splits=%d ksg=%d mfma=%s", w, p.sc.mb, p.sc.nbw,
+             p.sc.splits, p.ksg, d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
+  else
+    snprintf(buf, buf_len, "%s tile %dx%d waves=2x2 mfma=%s", w, kTileM, kTileN,
+             d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
+  return HM_OK;
+}
+
+HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* x,
+                         const float* x_row_scale, int64_t m, uint16_t* y, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  hm_status s = check_desc(d);
+  if (s) return s;
+  if ((s = check_pair(d, afmt))) return s;
+  if (d->num_experts != 1) return HM_ERR_SHAPE;
+  if (m < 0 || m > 65535ll * kTileM) return HM_ERR_SHAPE;
+  if (m == 0) return HM_OK;
+  if (!w_dev || !x || !y) return HM_ERR_NULL;
+  if (afmt == HM_A_FP8_ROWSCALE && !x_row_scale) return HM_ERR_NULL;
+  if (!aligned(w_dev, 256) || !aligned(x, 16) || !aligned(y, 16)) return HM_ERR_ALIGN;
+  if (x_row_scale && !aligned(x_row_scale, 4)) return HM_ERR_ALIGN;
+  const DensePlan p = plan_dense(d, m);
+  if (p.ws_bytes) {
+    if (!ws) return HM_ERR_NULL;
+    if (ws_bytes < p.ws_bytes) return HM_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return HM_ERR_ALIGN;
+  }
+  GemmArgs a{};
+  a.w = (const uint8_t*)w_dev;
+  a.G = geom_of(d);
+  a.wfmt = d->wfmt;
+  a.x = x;
+  a.xs = (afmt == HM_A_FP8_ROWSCALE) ? x_row_scale : nullptr;
+  a.M = m;
+  a.y = y;
+  hipError_t e;
+  if (p.stream) {
+    a.part = (p.sc.splits > 1) ? (float*)ws : nullptr;
+    a.ksg = p.ksg;
+    e = launch_gemm_stream(a, p.sc, false, 0, stream);
+    if (e == hipSuccess && p.sc.splits > 1) e = launch_splitk_reduce(a, p.sc.splits, stream);
+  } else {
+    e = launch_gemm_tile(a, false, 0, stream);
+  }
+  return (e == hipSuccess) ? HM_OK : HM_ERR_HIP;
+}
+
+HM_API hm_status hm_moe_sort_workspace_size(int64_t t, int32_t topk, int32_t num_experts,
+                                            size_t* bytes) {
+  if (!bytes) return HM_ERR_NULL;
+  if (t < 0 || topk < 1 || num_experts < 1 || num_experts > 512 || topk > num_experts)
+    return HM_ERR_SHAPE;
+  *bytes = 0;
+  return HM_OK;
+}
+
+HM_API hm_status hm_moe_sort(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t num_experts,
+                             int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (t < 0 || topk < 1 || num_experts < 1 || num_experts > 512 || topk > num_experts)
+    return HM_ERR_SHAPE;
+  if (t * (int64_t)topk >= (1ll << 31)) return HM_ERR_SHAPE;
+  if (t == 0) return HM_OK;
+  if (!topk_ids || !counts || !offsets || !sorted_pairs) return HM_ERR_NULL;
+  if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_pairs, 4))
+    return HM_ERR_ALIGN;
+  if (launch_moe_sort(topk_ids, t * topk, num_experts, counts, offsets, sorted_pairs, stream) !=
+      hipSuccess)
+    return HM_ERR_HIP;
+  return HM_OK;
+}
+
+HM_API hm_status hm_moe_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
+                                            size_t* bytes) {
+  hm_status s = check_desc(d);
+  if (s) return s;
+  if ((s = check_pair(d, afmt))) return s;
+  if (!bytes) return HM_ERR_NULL;
+  if (t < 0 || topk < 1 || topk > d->num_experts || d->num_experts > 512) return HM_ERR_SHAPE;
+  *bytes = plan_moe(d, t, topk).ws_bytes;
+  return HM_OK;
+}
+
+HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* a_in,
+                             const float* a_row_scale, int32_t a_rows_are_pairs, int64_t t,
+                             int32_t topk, const int32_t* offsets, const int32_t* sorted_pairs,
+                             uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hm_status s = check_desc(d);
+  if (s) return s;
+  if ((s = check_pair(d, afmt))) return s;
+  if (t < 0 || topk < 1 || topk > d->num_experts || d->num_experts > 512) return HM_ERR_SHAPE;
+  if (t * (int64_t)topk >= (1ll << 31)) return HM_ERR_SHAPE;
+  if (a_rows_are_pairs != 0 && a_rows_are_pairs != 1) return HM_ERR_SHAPE;
+  if (t == 0) return HM_OK;
+  if (!w_dev || !a_in || !offsets || !sorted_pairs || !y || !ws) return HM_ERR_NULL;
+  if (afmt == HM_A_FP8_ROWSCALE && !a_row_scale) return HM_ERR_NULL;
+  if (!aligned(w_dev, 256) || !aligned(a_in, 16) || !aligned(y, 16) || !aligned(ws, 256) ||
+      !aligned(offsets, 4) || !aligned(sorted_pairs, 4))
+    return HM_ERR_ALIGN;
+  if (a_row_scale && !aligned(a_row_scale, 4)) return HM_ERR_ALIGN;
+  const MoePlan p = plan_moe(d, t, topk);
+  if (ws_bytes < p.ws_bytes) return HM_ERR_WORKSPACE;
+
+  uint8_t* w8 = (uint8_t*)ws;
+  int32_t* hdr = (int32_t*)w8;
+  int32_t* su = (int32_t*)(w8 + p.off_su);
+  int32_t* tu = (int32_t*)(w8 + p.off_tu);
+  GemmArgs a{};
+  a.w = (const uint8_t*)w_dev;
+  a.G = geom_of(d);
+  a.wfmt = d->wfmt;
+  a.x = a_in;
+  a.xs = (afmt == HM_A_FP8_ROWSCALE) ? a_row_scale : nullptr;
+  a.M = 0;
+  a.y = y;
+  a.hdr = hdr;
+  a.sorted_pairs = sorted_pairs;
+  a.topk = topk;
+  a.rows_are_pairs = a_rows_are_pairs;
+
+  a.P = p.P;
+  hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, kStreamMaxRows, kTileM, p.max_s,
+                                     p.max_t, hdr, su, tu, stream);
+  if (e == hipSuccess) {
+    StreamCfg sc{2, p.nbw, 1};
+    const int64_t nts = (a.G.NB + 4 * sc.nbw - 1) / (4 * sc.nbw);
+    int64_t gi = p.max_s * nts;
+    if (gi > kGroupedGridStream) gi = kGroupedGridStream;
+    a.units = su;
+    if (gi > 0) e = launch_gemm_stream(a, sc, true, (int)gi, stream);
+  }
+  if (e == hipSuccess) {
+    const int64_t ntt = (a.G.NB + 7) / 8;
+    int64_t gi = p.max_t * ntt;
+    if (gi > kGroupedGridTile) gi = kGroupedGridTile;
+    a.units = tu;
+    if (gi > 0) e = launch_gemm_tile(a, true, (int)gi, stream);
+  }
+  return (e == hipSuccess) ? HM_OK : HM_ERR_HIP;
+}

@@ -1,0 +1,86 @@
+// Per-token FP8 activation quantization (the BF16 -> per-token FP8 switch the
+// ywsung.com note "How vLLM Humming computes 4 bits" describes in its section
+// on weight format / activation / backend):
+//   s[m] = amax_k |x[m,k]| / 448  (fp32 division),
+//   x8[m,k] = E4M3(x[m,k] / s[m]) (fp32 division, round to nearest even,
+//   saturating at 448);  a zero row gives s = 0 and zero codes.
+// E4M3 is the OCP "FN" layout: bias 7, no infinities, largest finite 448,
+// subnormal step 2^-9.
+#include "common.h"
+#include "launch.h"
+
+namespace hm {
+
+// fp32 -> E4M3 bits, round to nearest even, saturating; sign kept on zero.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;           // |x| >= 448: saturate
+  if (a < 0x3C800000u) {                                // |x| < 2^-6: subnormal range
+    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);  // units of 2^-9, 0..8
+    return sign | (uint32_t)m;                          // 8 -> 0x08 = 2^-6 (exact carry)
+  }
+  // normal: keep 3 mantissa bits with round-to-nearest-even, then rebias 127 -> 7
+  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+  return sign | ((r >> 20) - (120u << 3));
+}
+
+// One 256-thread block per row; rows of any length k.
+__global__ void __launch_bounds__(256)
+k_quant_fp8_rows(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint8_t* __restrict__ x8,
+                 float* __restrict__ row_scale) {
+  __shared__ float red[4];
+  for (int64_t row = blockIdx.x; row < m; row += gridDim.x) {
+    const uint16_t* xr = x + row * k;
+    uint8_t* qr = x8 + row * k;
+    const bool vec = ((k & 7) == 0);
+    float amax = 0.0f;
+    if (vec) {
+      for (int64_t i = threadIdx.x * 8; i < k; i += 256 * 8) {
+        const u32x4_t v = ld16(xr + i);
+        for (int j = 0; j < 4; ++j) {
+          amax = fmaxf(amax, fabsf(bf16_to_f32(v[j] & 0xFFFF)));
+          amax = fmaxf(amax, fabsf(bf16_to_f32(v[j] >> 16)));
+        }
+      }
+    } else {
+      for (int64_t i = threadIdx.x; i < k; i += 256) amax = fmaxf(amax, fabsf(bf16_to_f32(xr[i])));
+    }
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    const float s = __fdiv_rn(amax, 448.0f);
+    if (threadIdx.x == 0) row_scale[row] = s;
+    if (vec) {
+      for (int64_t i = threadIdx.x * 8; i < k; i += 256 * 8) {
+        const u32x4_t v = ld16(xr + i);
+        uint32_t lo = 0, hi = 0;
+        for (int j = 0; j < 4; ++j) {
+          uint32_t c0 = 0, c1 = 0;
+          if (s != 0.0f) {
+            c0 = f32_to_e4m3(__fdiv_rn(bf16_to_f32(v[j] & 0xFFFF), s));
+            c1 = f32_to_e4m3(__fdiv_rn(bf16_to_f32(v[j] >> 16), s));
+          }
+          const uint32_t pair = c0 | (c1 << 8);
+          if (j < 2) lo |= pair << (16 * j); else hi |= pair << (16 * (j - 2));
+        }
+        *reinterpret_cast<u32x2_t*>(qr + i) = (u32x2_t){lo, hi};
+      }
+    } else {
+      for (int64_t i = threadIdx.x; i < k; i += 256)
+        qr[i] = (s != 0.0f) ? (uint8_t)f32_to_e4m3(__fdiv_rn(bf16_to_f32(xr[i]), s)) : (uint8_t)0;
+    }
+  }
+}
+
+hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* x8, float* s,
+                                 hipStream_t st) {
+  int64_t blocks = m < 65536 ? m : 65536;
+  hipLaunchKernelGGL(k_quant_fp8_rows, dim3((unsigned)blocks), dim3(256), 0, st, x, m, k, x8, s);
+  return hipGetLastError();
+}
+
+}  // namespace hm

@@ -1,0 +1,241 @@
+// MFMA tile GEMM for many rows (prefill-sized M, and large experts of a
+// grouped GEMM), where the ~2*M*N*K matrix multiply dominates (ywsung.com note
+// "How vLLM Humming computes 4 bits", section on one token vs many tokens).
+//
+// One 256-thread block computes a 128 x 128 output tile; its four waves each
+// own 64 x 64 (4 x 4 MFMA blocks of 16 x 16).  Per 128-K step:
+//   * the activation tile (128 rows) is staged in LDS with a padded row stride
+//     (conflict-free 16-byte fragment reads);
+//   * W4A16: the eight 1 KiB weight tiles are read once per block, unpacked and
+//     scaled to bf16 by the block's threads (once per block, not per wave) and
+//     written to LDS already in MFMA fragment order;
+//   * W4A8-MXFP4: each wave loads its E2M1 fragments straight into registers
+//     and feeds them with their E8M0 scales to the 16x16x128 scaled MFMA; the
+//     per-token FP8 scale is applied in the epilogue.
+// Global loads for step g+1 are issued before the MFMAs of step g.
+#include "common.h"
+#include "launch.h"
+
+namespace hm {
+
+template <bool MX, bool GROUPED>
+__global__ void __launch_bounds__(256)
+k_gemm_tile(GemmArgs a, int n_tiles) {
+  constexpr int XB = MX ? (128 + 16) : (256 + 16);     // LDS activation row stride (bytes)
+  constexpr int XPR = MX ? 8 : 16;                     // 16-byte pieces per activation row
+  constexpr int XLD = kTileM * XPR / 256;              // pieces per thread
+  constexpr int WLDS = MX ? 16 : 8 * 4 * 1024;         // dequantized weight fragments
+  __shared__ __attribute__((aligned(16))) uint8_t xs_lds[kTileM * XB];
+  __shared__ __attribute__((aligned(16))) uint8_t ws_lds[WLDS];
+  __shared__ int64_t arow_s[kTileM];
+  __shared__ int64_t orow_s[kTileM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n_l = lane & 15, q_l = lane >> 4;
+  const Geom G = a.G;
+  const int64_t K = G.K;
+  const uint8_t* xbase = reinterpret_cast<const uint8_t*>(a.x);
+  const int64_t xrow_bytes = MX ? K : 2 * K;
+
+  const int64_t n_items = GROUPED ? (int64_t)a.hdr[1] * n_tiles : 1;
+  for (int64_t item = GROUPED ? blockIdx.x : 0; item < n_items;
+       item += GROUPED ? gridDim.x : 1) {
+    int64_t e = 0;
+    int nt, rcount;
+    if (GROUPED) {
+      const int64_t unit = item / n_tiles;
+      nt = (int)(item % n_tiles);
+      const int32_t* u = a.units + 4 * unit;
+      e = u[0];
+      rcount = u[2];
+      if (tid < kTileM) {
+        int64_t ar = -1, orr = -1;
+        if (tid < rcount) {
+          const int64_t pair = a.sorted_pairs[u[1] + tid];
+          if (pair >= 0 && pair < a.P) {
+            orr = pair;
+            ar = a.rows_are_pairs ? pair : pair / a.topk;
+          }
+        }
+        arow_s[tid] = ar;
+        orow_s[tid] = orr;
+      }
+    } else {
+      nt = blockIdx.x;
+      const int64_t m0 = (int64_t)blockIdx.y * kTileM;
+      rcount = (int)((a.M - m0) < kTileM ? (a.M - m0) : kTileM);
+      if (tid < kTileM) {
+        arow_s[tid] = (tid < rcount) ? m0 + tid : -1;
+        orow_s[tid] = arow_s[tid];
+      }
+    }
+    __syncthreads();
+
+    const int64_t nbt = (int64_t)nt * 8;  // first 16-column block of this tile
+
+    // ---- register staging of one K step
+    u32x4_t xr[XLD];
+    u32x4_t wq[2];               // W4A16: two code slots per thread
+    float wsv[2], wzs[2];
+    u32x4_t mq[4];               // W4A8: this wave's four fragments
+    int msc[4];
+
+    auto load_step = [&](int64_t g) {
+#pragma unroll
+      for (int i = 0; i < XLD; ++i) {
+        const int q = tid + 256 * i;
+        const int row = q / XPR, pc = q % XPR;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (row < rcount && arow_s[row] >= 0)
+          v = ld16(xbase + arow_s[row] * xrow_bytes + g * (MX ? 128 : 256) + pc * 16);
+        xr[i] = v;
+      }
+      if (MX) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t nb = nbt + wn * 4 + j;
+          mq[j] = (u32x4_t){0u, 0u, 0u, 0u};
+          msc[j] = 0;
+          if (nb < G.NB) {
+            const int64_t tile = (e * G.NB + nb) * G.KG + g;
+            mq[j] = ld16(a.w + tile * 1024 + lane * 16);
+            const uint32_t* scm = reinterpret_cast<const uint32_t*>(a.w + G.off_scales);
+            msc[j] = (int)((scm[((e * G.NB + nb) * G.KG4 + g / 4) * 64 + lane] >> (8 * (g % 4))) & 0xFF);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int q = tid + 256 * i;
+          const int64_t nb = nbt + (q >> 6);
+          const int L = q & 63;
+          wq[i] = (u32x4_t){0u, 0u, 0u, 0u};
+          wsv[i] = 0.0f;
+          wzs[i] = 0.0f;
+          if (nb < G.NB) {
+            const int64_t tile = (e * G.NB + nb) * G.KG + g;
+            wq[i] = ld16(a.w + tile * 1024 + L * 16);
+            const uint16_t* s16 = reinterpret_cast<const uint16_t*>(a.w + G.off_scales);
+            const float sv = bf16_to_f32(s16[tile * 16 + (L & 15)]);
+            float z = 8.0f;
+            if (a.wfmt == W_UINT4_ZP) {
+              const uint64_t* zz = reinterpret_cast<const uint64_t*>(a.w + G.off_zeros);
+              z = (float)((zz[tile] >> (4 * (L & 15))) & 0xF);
+            }
+            wsv[i] = sv;
+            wzs[i] = -z * sv;
+          }
+        }
+      }
+    };
+    auto store_step = [&]() {
+#pragma unroll
+      for (int i = 0; i < XLD; ++i) {
+        const int q = tid + 256 * i;
+        const int row = q / XPR, pc = q % XPR;
+        st16(&xs_lds[row * XB + pc * 16], xr[i]);
+      }
+      if (!MX) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int q = tid + 256 * i;
+          const int nbl = q >> 6, L = q & 63;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            st16(&ws_lds[((nbl * 4 + j) * 64 + L) * 16], dq8_u4(wq[i][j], wsv[i], wzs[i]));
+        }
+      }
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    load_step(0);
+    store_step();
+    __syncthreads();
+    u32x4_t cq[4];
+    int csc[4];
+    for (int64_t g = 0; g < G.KG; ++g) {
+      if (MX) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { cq[j] = mq[j]; csc[j] = msc[j]; }
+      }
+      const bool more = (g + 1 < G.KG);
+      if (more) load_step(g + 1);
+      if (MX) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const uint8_t* p = xs_lds + (wm * 64 + mb * 16 + n_l) * XB + 16 * q_l;
+          const u32x4_t a0 = ld16(p), a1 = ld16(p + 64);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j][mb] = mfma_fp4_fp8(cq[j], a0, a1, acc[j][mb], csc[j], 127);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          u32x4_t xf[4], wf[4];
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+            xf[mb] = ld16(xs_lds + (wm * 64 + mb * 16 + n_l) * XB + (32 * ks + 8 * q_l) * 2);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) wf[j] = ld16(ws_lds + (((wn * 4 + j) * 4 + ks) * 64 + lane) * 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) acc[j][mb] = mfma_bf16(wf[j], xf[mb], acc[j][mb]);
+        }
+      }
+      __syncthreads();
+      if (more) {
+        store_step();
+        __syncthreads();
+      }
+    }
+
+    // ---- epilogue: lane holds C[n = 16nb + 4*q_l + r][row = 16mb + n_l]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t nb = nbt + wn * 4 + j;
+      if (nb >= G.NB) continue;
+      const int64_t n = nb * 16 + 4 * q_l;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int rl = wm * 64 + mb * 16 + n_l;
+        if (rl >= rcount || orow_s[rl] < 0) continue;
+        f32x4_t v = acc[j][mb];
+        if (MX) v = v * a.xs[arow_s[rl]];
+        uint16_t* dst = a.y + orow_s[rl] * G.N + n;
+        if ((G.N & 3) == 0 && n + 3 < G.N) {
+          *reinterpret_cast<u32x2_t*>(dst) = (u32x2_t){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < G.N) dst[r] = (uint16_t)(pack_bf16(v[r], 0.0f) & 0xFFFF);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <bool MX, bool GROUPED>
+static hipError_t go_tile(const GemmArgs& a, int grid_items, hipStream_t st) {
+  const int n_tiles = (int)((a.G.NB + 7) / 8);
+  dim3 grid;
+  if (GROUPED) grid = dim3((unsigned)(grid_items > 0 ? grid_items : 1));
+  else grid = dim3((unsigned)n_tiles, (unsigned)((a.M + kTileM - 1) / kTileM));
+  hipLaunchKernelGGL((k_gemm_tile<MX, GROUPED>), grid, dim3(256), 0, st, a, n_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
+  const bool mx = (a.wfmt == W_MXFP4);
+  if (mx) return grouped ? go_tile<true, true>(a, grid_items, st) : go_tile<true, false>(a, grid_items, st);
+  return grouped ? go_tile<false, true>(a, grid_items, st) : go_tile<false, false>(a, grid_items, st);
+}
+
+}  // namespace hm

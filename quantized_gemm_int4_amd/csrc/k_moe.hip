@@ -1,0 +1,153 @@
+// MoE expert sort and grouped-GEMM scheduling.
+//
+// Tokens are split per expert, so every expert's GEMM has its own M that
+// depends on the routing load (ywsung.com note "How vLLM Humming computes 4
+// bits", section on one token vs many tokens).  The sort groups the
+// (token, expert) pairs by expert; the scheduler cuts every expert's segment
+// into row units for the two GEMM kernels (short segments to the streaming
+// kernel, long ones to the MFMA tile kernel).
+#include "common.h"
+#include "launch.h"
+
+namespace hm {
+
+constexpr int kSortThreads = 1024;
+constexpr int kSortWaves = kSortThreads / 64;
+
+// Inclusive scan of one value per thread over the first 512 threads of a
+// block (8 waves).  `wsum` is 8 ints of shared scratch.  Must be reached by
+// every thread of the block.
+__device__ int block_scan512(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63 && wave < 8) wsum[wave] = v;
+  __syncthreads();
+  int pre = 0;
+  for (int w = 0; w < wave && w < 8; ++w) pre += wsum[w];
+  __syncthreads();
+  return v + pre;
+}
+
+// Deterministic, stable counting sort of pair ids by expert in one block.
+// Wave w owns the contiguous pair range [w*chunk, (w+1)*chunk); its per-expert
+// base positions come from the exclusive prefix over earlier waves, and inside
+// a wave each batch of 64 pairs is ranked in lane order with ballot matching.
+__global__ void __launch_bounds__(kSortThreads)
+k_moe_sort(const int32_t* __restrict__ ids, int64_t P, int E, int32_t* __restrict__ counts,
+           int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs) {
+  __shared__ int hist[kSortWaves][512];
+  __shared__ int wsum[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kSortWaves * 512; i += kSortThreads) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t chunk = (P + kSortWaves - 1) / kSortWaves;
+  const int64_t beg = wave * chunk;
+  const int64_t end = (beg + chunk < P) ? beg + chunk : P;
+  for (int64_t b = beg; b < end; b += 64) {
+    const int64_t p = b + lane;
+    if (p < end) {
+      const int e = ids[p];
+      if (e >= 0 && e < E) atomicAdd(&hist[wave][e], 1);
+    }
+  }
+  __syncthreads();
+  // per-expert totals and per-wave exclusive bases
+  int total = 0;
+  if (tid < E) {
+    for (int w = 0; w < kSortWaves; ++w) {
+      const int c = hist[w][tid];
+      hist[w][tid] = total;
+      total += c;
+    }
+  }
+  const int incl = block_scan512(tid < 512 ? total : 0, wsum);
+  const int excl = incl - total;
+  if (tid < E) {
+    counts[tid] = total;
+    offsets[tid] = excl;
+    if (tid == E - 1) offsets[E] = incl;
+    for (int w = 0; w < kSortWaves; ++w) hist[w][tid] += excl;
+  }
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t b = beg; b < end; b += 64) {
+    const int64_t p = b + lane;
+    int e = -1;
+    if (p < end) e = ids[p];
+    const bool valid = (e >= 0 && e < E);
+    uint64_t m = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t x = __ballot(valid && ((e >> bit) & 1));
+      m &= ((e >> bit) & 1) ? x : ~x;
+    }
+    if (valid) {
+      const int rank = __popcll(m & lt);
+      const int pos = hist[wave][e] + rank;
+      sorted_pairs[pos] = (int32_t)p;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (valid && __popcll(m & lt) == 0) hist[wave][e] += __popcll(m);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Cut every expert's segment into units: segments of 1..s_max rows become one
+// streaming unit; longer ones become ceil(count/bm) tile units of <= bm rows.
+// Unit = {expert, first index into sorted_pairs, row count, 0}.
+// hdr[0] = number of streaming units, hdr[1] = number of tile units.
+__global__ void __launch_bounds__(512)
+k_moe_schedule(const int32_t* __restrict__ offsets, int E, int64_t P, int s_max, int bm,
+               int64_t max_s, int64_t max_t, int32_t* __restrict__ hdr, int32_t* __restrict__ su,
+               int32_t* __restrict__ tu) {
+  __shared__ int wsum[8];
+  const int e = threadIdx.x;
+  int c = 0, beg = 0;
+  if (e < E) {
+    // clamp to [0, P] so that malformed offsets can never address outside the pairs
+    int64_t b = offsets[e], f = offsets[e + 1];
+    b = b < 0 ? 0 : (b > P ? P : b);
+    f = f < b ? b : (f > P ? P : f);
+    beg = (int)b;
+    c = (int)(f - b);
+  }
+  const int ns = (c > 0 && c <= s_max) ? 1 : 0;
+  const int nt = (c > s_max) ? (c + bm - 1) / bm : 0;
+  const int is = block_scan512(ns, wsum);
+  const int it = block_scan512(nt, wsum);
+  if (ns && is - 1 < max_s) {
+    int32_t* u = su + 4 * (is - 1);
+    u[0] = e; u[1] = beg; u[2] = c; u[3] = 0;
+  }
+  for (int i = 0; i < nt; ++i) {
+    if (it - nt + i >= max_t) break;
+    int32_t* u = tu + 4 * (it - nt + i);
+    const int r0 = i * bm;
+    u[0] = e; u[1] = beg + r0; u[2] = (c - r0 < bm) ? c - r0 : bm; u[3] = 0;
+  }
+  if (e == 511) {
+    hdr[0] = (int32_t)(is < max_s ? is : max_s);
+    hdr[1] = (int32_t)(it < max_t ? it : max_t);
+  }
+}
+
+hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int E, int32_t* counts, int32_t* offsets,
+                           int32_t* sorted_pairs, hipStream_t st) {
+  hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(kSortThreads), 0, st, ids, P, E, counts, offsets,
+                     sorted_pairs);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_max, int bm,
+                               int64_t max_s, int64_t max_t, int32_t* hdr, int32_t* su,
+                               int32_t* tu, hipStream_t st) {
+  hipLaunchKernelGGL(k_moe_schedule, dim3(1), dim3(512), 0, st, offsets, E, P, s_max, bm, max_s,
+                     max_t, hdr, su, tu);
+  return hipGetLastError();
+}
+
+}  // namespace hm

@@ -1,0 +1,58 @@
+// Internal launchers (host side) for the kernels of the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "common.h"
+
+namespace hm {
+
+// Arguments shared by the GEMM kernels.
+struct GemmArgs {
+  const uint8_t* w;        // device weight layout (all experts)
+  Geom G;
+  int wfmt;                // W_INT4_SYM / W_UINT4_ZP / W_MXFP4
+  const void* x;           // activations: bf16 [rows][K] or E4M3 bytes [rows][K]
+  const float* xs;         // fp32 row scales (A8) or null
+  int64_t M;               // dense: rows of x and y
+  uint16_t* y;             // bf16 output [rows][N]
+  float* part;             // split-K partials [splits][M][NB*16] (dense streaming only)
+  int ksg;                 // K groups per split (dense streaming)
+  // grouped (MoE) mode
+  const int32_t* units;    // {expert, first, count, 0} per unit
+  const int32_t* hdr;      // hdr[0] streaming units, hdr[1] tile units
+  const int32_t* sorted_pairs;
+  int topk;
+  int rows_are_pairs;
+  int64_t P;               // routed pairs (row ids outside [0, P) are skipped)
+};
+
+hipError_t launch_transform(int wfmt, const Geom& G, const uint8_t* codes, const void* scales,
+                            const uint8_t* zeros, uint8_t* out, hipStream_t st);
+hipError_t launch_dequant(int wfmt, const Geom& G, const uint8_t* w, int64_t e, float* out,
+                          hipStream_t st);
+hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* x8, float* s,
+                                 hipStream_t st);
+hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int E, int32_t* counts, int32_t* offsets,
+                           int32_t* sorted_pairs, hipStream_t st);
+hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_max, int bm,
+                               int64_t max_s, int64_t max_t, int32_t* hdr, int32_t* su,
+                               int32_t* tu, hipStream_t st);
+
+// Streaming (small-M) kernel.  Dense: grid (n_tiles, splits, m_chunks).
+// Grouped: persistent over (streaming unit x n tile) items.
+struct StreamCfg {
+  int mb;      // 16-row blocks per unit: 1 or 2
+  int nbw;     // 16-column blocks per wave
+  int splits;  // dense split-K factor
+};
+hipError_t launch_gemm_stream(const GemmArgs& a, const StreamCfg& c, bool grouped, int grid_items,
+                              hipStream_t st);
+hipError_t launch_splitk_reduce(const GemmArgs& a, int splits, hipStream_t st);
+
+// MFMA tile kernel, 128x128 output tiles.  Dense: grid (n_tiles, m_tiles).
+// Grouped: persistent over (tile unit x n tile) items.
+constexpr int kTileM = 128;
+constexpr int kTileN = 128;
+hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
+
+}  // namespace hm

@@ -1,0 +1,116 @@
+"""The C library loads, exports every entry point include/hm.h declares, and
+rejects bad arguments before any launch (no GPU needed: these calls return
+before touching HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_gemm_int4_amd as hm
+from oracle import layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(hm.lib, n), n
+    out = os.popen(f"nm -D --defined-only {hm.LIB_PATH}").read()
+    exported = set(re.findall(r" T (hm_[a-z0-9_]+)", out))
+    assert set(names) <= exported
+    # nothing else leaks out of the library's namespace
+    assert all(s.startswith("hm_") for s in exported)
+
+
+def test_status_strings():
+    for code in range(8):
+        s = hm.lib.hm_status_string(code)
+        assert s and s.decode() != "unknown status"
+    assert hm.lib.hm_status_string(99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("fmt", ["int4_sym", "uint4_zp", "mxfp4"])
+@pytest.mark.parametrize("E,N,K", [(1, 256, 512), (1, 14336, 4096), (3, 37, 640), (256, 4096, 7168)])
+def test_transform_size_matches_layout_spec(fmt, E, N, K):
+    d = hm.wdesc(fmt, N, K, E)
+    assert hm.hm_transform_size(d) == layout.sizes(fmt, E, N, K)[2]
+
+
+def _err(fn, *args):
+    return getattr(hm.lib, fn)(*args)
+
+
+def test_descriptor_checks():
+    sz = ctypes.c_size_t()
+    d = hm.wdesc("int4_sym", 256, 512)
+    assert _err("hm_transform_size", None, ctypes.byref(sz)) == 1
+    bad = hm.wdesc("int4_sym", 256, 512); bad.abi = 99
+    assert _err("hm_transform_size", ctypes.byref(bad), ctypes.byref(sz)) == 7
+    bad = hm.wdesc("int4_sym", 256, 500)                       # K not a multiple of 128
+    assert _err("hm_transform_size", ctypes.byref(bad), ctypes.byref(sz)) == 2
+    bad = hm.wdesc("int4_sym", 256, 512); bad.group = 64
+    assert _err("hm_transform_size", ctypes.byref(bad), ctypes.byref(sz)) == 2
+    bad = hm.wdesc("int4_sym", 0, 512)
+    assert _err("hm_transform_size", ctypes.byref(bad), ctypes.byref(sz)) == 2
+    bad = hm.wdesc("int4_sym", 256, 512); bad.wfmt = 9
+    assert _err("hm_transform_size", ctypes.byref(bad), ctypes.byref(sz)) == 4
+    assert _err("hm_transform_size", ctypes.byref(d), None) == 1
+
+
+def test_gemm_argument_checks():
+    d = hm.wdesc("uint4_zp", 256, 512)
+    P = ctypes.c_void_p
+    good = P(0x100000)          # aligned fake addresses: never dereferenced, calls return first
+    odd = P(0x100008)
+    # wrong activation format for the weight format
+    assert _err("hm_gemm", ctypes.byref(d), good, 1, good, good, 4, good, None, 0, None) == 4
+    # m = 0 is a no-op even with null pointers
+    assert _err("hm_gemm", ctypes.byref(d), None, 0, None, None, 0, None, None, 0, None) == 0
+    assert _err("hm_gemm", ctypes.byref(d), None, 0, good, None, 4, good, None, 0, None) == 1
+    assert _err("hm_gemm", ctypes.byref(d), good, 0, good, None, -1, good, None, 0, None) == 2
+    assert _err("hm_gemm", ctypes.byref(d), odd, 0, good, None, 4, good, None, 0, None) == 3
+    # the streaming path at M=1 needs a split-K workspace
+    need = hm.hm_gemm_workspace_size(d, 0, 1)
+    assert need > 0
+    assert _err("hm_gemm", ctypes.byref(d), good, 0, good, None, 1, good, None, 0, None) == 1
+    assert _err("hm_gemm", ctypes.byref(d), good, 0, good, None, 1, good, good, need - 1, None) == 5
+    mx = hm.wdesc("mxfp4", 256, 512)
+    assert _err("hm_gemm", ctypes.byref(mx), good, 1, good, None, 4, good, None, 0, None) == 1
+    moe = hm.wdesc("int4_sym", 256, 512, 4)
+    assert _err("hm_gemm", ctypes.byref(moe), good, 0, good, None, 4, good, None, 0, None) == 2
+
+
+def test_plan_strings():
+    d = hm.wdesc("uint4_zp", 14336, 4096)
+    assert "stream" in hm.hm_gemm_plan(d, 0, 1)
+    assert "stream" in hm.hm_gemm_plan(d, 0, 16)
+    assert "tile" in hm.hm_gemm_plan(d, 0, 4096)
+    assert hm.hm_gemm_workspace_size(d, 0, 4096) == 0
+
+
+def test_moe_argument_checks():
+    P = ctypes.c_void_p
+    good = P(0x100000)
+    assert _err("hm_moe_sort", good, 4, 9, 8, good, good, good, None, 0, None) == 2      # topk > E
+    assert _err("hm_moe_sort", good, 4, 2, 600, good, good, good, None, 0, None) == 2    # E > 512
+    assert _err("hm_moe_sort", None, 0, 2, 8, None, None, None, None, 0, None) == 0      # t = 0
+    assert _err("hm_moe_sort", None, 4, 2, 8, good, good, good, None, 0, None) == 1
+    assert _err("hm_moe_sort", P(0x100002), 4, 2, 8, good, good, good, None, 0, None) == 3
+    d = hm.wdesc("int4_sym", 4096, 7168, 256)
+    need = hm.hm_moe_gemm_workspace_size(d, 0, 64, 8)
+    assert need > 0
+    args = (ctypes.byref(d), good, 0, good, None, 0, 64, 8, good, good, good, good)
+    assert _err("hm_moe_gemm", *args, need - 1, None) == 5
+    assert _err("hm_moe_gemm", ctypes.byref(d), good, 0, good, None, 2, 64, 8, good, good, good,
+                good, need, None) == 2
+    assert _err("hm_moe_gemm", ctypes.byref(d), good, 0, good, None, 0, 64, 8, None, good, good,
+                good, need, None) == 1

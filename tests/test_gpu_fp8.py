@@ -1,0 +1,44 @@
+"""GPU parity: per-token FP8 quantization is bit-exact (codes and fp32 scales)
+against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import quant
+from gpu_util import bf16_to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(m, k, seed):
+    r = np.random.default_rng(seed)
+    x = r.normal(0, 1, size=(m, k)).astype(np.float32)
+    # spread magnitudes over many binades so subnormal E4M3 codes appear
+    x *= np.exp2(r.integers(-12, 4, size=(m, 1))).astype(np.float32)
+    x *= np.exp2(r.integers(-10, 1, size=(m, k))).astype(np.float32)
+    x[0] = 0.0                                     # zero row
+    if m > 2:
+        x[1, :] = -0.0
+        x[2, min(3, k - 1)] = 1e4                    # one dominant outlier
+    return synthetic.to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("m,k", [(1, 128), (7, 2048), (33, 100), (300, 7168), (5, 1)])
+def test_fp8_rows_bit_exact(m, k):
+    import quantized_gemm_int4_amd as hm
+    xb = _rows(m, k, m * 1000 + k)
+    x8, s = hm.hm_quant_fp8_rows(bf16_to_dev(xb))
+    torch.cuda.synchronize()
+    rc, rs = quant.quant_fp8_rows(xb)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(x8.cpu().numpy(), rc)
+
+
+def test_fp8_rows_workload_outliers():
+    import quantized_gemm_int4_amd as hm
+    xb = synthetic.activations(3, 256, 2048, outliers=0.01)
+    x8, s = hm.hm_quant_fp8_rows(bf16_to_dev(xb))
+    rc, rs = quant.quant_fp8_rows(xb)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(x8.cpu().numpy(), rc)

@@ -1,0 +1,185 @@
+"""GPU parity for the dense GEMM against the oracle (fp64 GEMM of the exact
+dequantized weights): the five acceptance shapes of the workloads at full
+size (large M on sampled rows), ragged shapes on both kernel paths, closed
+forms, degenerate inputs and run-to-run determinism."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import codecs, gemm, quant
+from gpu_util import bf16_to_dev, bits_of, quantize_experts, std_to_dev, xhat_of
+
+pytestmark = pytest.mark.gpu
+
+
+class Layer:
+    """One dense layer prepared on both sides from the same fp32 weights."""
+
+    def __init__(self, fmt, n, k, cfg=2, wseed=0):
+        import quantized_gemm_int4_amd as hm
+        self.fmt, self.n, self.k = fmt, n, k
+        wf = synthetic.weights(cfg, n, k, index=wseed)
+        codes, scales, zeros, what = quantize_experts(fmt, [wf])
+        self.what = what[0].astype(np.float64)
+        self.desc = hm.wdesc(fmt, n, k)
+        self.w = hm.hm_transform(self.desc, *std_to_dev(fmt, codes, scales, zeros))
+
+    def run(self, x_bits):
+        import quantized_gemm_int4_amd as hm
+        x = bf16_to_dev(x_bits)
+        if self.fmt == quant.FMT_MXFP4:
+            x8, s = hm.hm_quant_fp8_rows(x)
+            y = hm.hm_gemm(self.desc, self.w, x8, s)
+        else:
+            y = hm.hm_gemm(self.desc, self.w, x)
+        torch.cuda.synchronize()
+        return bits_of(y)
+
+    def check(self, x_bits, rows=None):
+        yb = self.run(x_bits)
+        xh = xhat_of(self.fmt, x_bits)
+        if rows is not None:
+            xh, yb = xh[rows], yb[rows]
+        yref, b = gemm.gemm_ref(xh, self.what, bound_dtype=np.float32 if xh.shape[0] > 512 else np.float64)
+        res = gemm.check(yb, yref, b)
+        assert res["ok"], res
+        return res
+
+
+def _force(path):
+    if path is None:
+        os.environ.pop("HM_FORCE_PATH", None)
+    else:
+        os.environ["HM_FORCE_PATH"] = str(path)
+
+
+@pytest.fixture(autouse=True)
+def _no_force():
+    yield
+    _force(None)
+
+
+def test_config1_symmetric_decode():
+    L = Layer(quant.FMT_INT4_SYM, 256, 512, cfg=1)
+    L.check(synthetic.activations(1, 1, 512))
+
+
+@pytest.fixture(scope="module")
+def config2():
+    return Layer(quant.FMT_UINT4_ZP, 14336, 4096, cfg=2)
+
+
+@pytest.mark.parametrize("m", [1, 16, 128, 1024])
+def test_config2_asym_full(config2, m):
+    config2.check(synthetic.activations(2, m, 4096, index=m))
+
+
+def test_config2_m4096_sampled_rows(config2):
+    rows = np.random.default_rng(0).choice(4096, 96, replace=False)
+    rows = np.concatenate([rows, [0, 127, 128, 4095]])
+    config2.check(synthetic.activations(2, 4096, 4096, index=4096), rows=rows)
+
+
+@pytest.fixture(scope="module")
+def config3():
+    return Layer(quant.FMT_MXFP4, 7168, 2048, cfg=3)
+
+
+@pytest.mark.parametrize("m", [16, 256])
+def test_config3_mxfp4_full(config3, m):
+    config3.check(synthetic.activations(3, m, 2048, index=m, outliers=0.01))
+
+
+def test_config3_m4096_sampled_rows(config3):
+    rows = np.random.default_rng(1).choice(4096, 96, replace=False)
+    config3.check(synthetic.activations(3, 4096, 2048, index=4096, outliers=0.01), rows=rows)
+
+
+@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("n,k", [(200, 384), (37, 128), (1000, 1152)])
+@pytest.mark.parametrize("m", [1, 7, 16, 17, 32, 33, 100, 129, 257])
+def test_ragged_default_path(fmt, n, k, m):
+    L = Layer(fmt, n, k, cfg=7, wseed=n + k)
+    L.check(synthetic.activations(7, m, k, index=m))
+
+
+@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("m", [1, 17, 32])
+@pytest.mark.parametrize("path", [1, 2])
+def test_forced_paths_agree_with_oracle(fmt, m, path):
+    L = Layer(fmt, 328, 640, cfg=8)
+    _force(path)
+    L.check(synthetic.activations(8, m, 640, index=m))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 5])
+def test_stream_split_counts(splits):
+    L = Layer(quant.FMT_UINT4_ZP, 512, 640, cfg=9)
+    os.environ["HM_STREAM_SPLITS"] = str(splits)
+    try:
+        L.check(synthetic.activations(9, 5, 640))
+    finally:
+        os.environ.pop("HM_STREAM_SPLITS", None)
+
+
+def test_one_hot_weights_exact():
+    """Closed form: one nonzero code per row with a power-of-two scale makes Y a
+    scaled column gather of X, exact in bf16, on both kernel paths."""
+    import quantized_gemm_int4_amd as hm
+    n, k = 96, 512
+    ks = np.random.default_rng(3).integers(0, k, size=n)
+    q = np.zeros((n, k), dtype=np.int64)
+    q[np.arange(n), ks] = 3
+    codes = quant.pack_nibbles(q)[None]
+    scales = np.full((1, n, k // 128), 0x3E00, dtype=np.uint16)     # bf16 0.125
+    d = hm.wdesc("int4_sym", n, k)
+    w = hm.hm_transform(d, *std_to_dev(quant.FMT_INT4_SYM, codes, scales, None))
+    for m, path in [(3, 1), (40, 2)]:
+        _force(path)
+        xb = synthetic.activations(10, m, k, index=m)
+        y = bits_of(hm.hm_gemm(d, w, bf16_to_dev(xb)))
+        x = codecs.bf16_value(xb).astype(np.float64)
+        want = codecs.bf16_rne_bits((x[:, ks] * 0.375).astype(np.float32))
+        assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("fmt", quant.FORMATS)
+def test_zero_weights_give_exact_zeros(fmt):
+    import quantized_gemm_int4_amd as hm
+    n, k = 64, 256
+    zcode = {quant.FMT_INT4_SYM: 0, quant.FMT_UINT4_ZP: 5, quant.FMT_MXFP4: 0}[fmt]
+    codes = quant.pack_nibbles(np.full((n, k), zcode))[None]
+    if fmt == quant.FMT_MXFP4:
+        scales = np.full((1, n, k // 32), 130, dtype=np.uint8)
+        zeros = None
+    else:
+        scales = np.full((1, n, k // 128), 0x3F80, dtype=np.uint16)
+        zeros = np.full((1, n, k // 128), 5, dtype=np.uint8) if fmt == quant.FMT_UINT4_ZP else None
+    d = hm.wdesc(fmt, n, k)
+    w = hm.hm_transform(d, *std_to_dev(fmt, codes, scales, zeros))
+    for m in (2, 50):
+        xb = synthetic.activations(11, m, k, index=m)
+        x = bf16_to_dev(xb)
+        if fmt == quant.FMT_MXFP4:
+            x8, s = hm.hm_quant_fp8_rows(x)
+            y = hm.hm_gemm(d, w, x8, s)
+        else:
+            y = hm.hm_gemm(d, w, x)
+        assert (bits_of(y) & 0x7FFF == 0).all()
+
+
+def test_deterministic_repeat(config2):
+    xb = synthetic.activations(2, 16, 4096, index=99)
+    a = config2.run(xb)
+    b = config2.run(xb)
+    assert np.array_equal(a, b)
+
+
+def test_m_zero_is_noop(config2):
+    import quantized_gemm_int4_amd as hm
+    x = torch.empty(0, 4096, dtype=torch.bfloat16, device="cuda")
+    y = hm.hm_gemm(config2.desc, config2.w, x)
+    assert y.shape == (0, 14336)
