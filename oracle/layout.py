@@ -14,8 +14,10 @@ blocks of 16 columns, KG = K/128 steps of 128 along K.
 Region A, codes: E*NB*KG tiles of 1024 bytes, tile index (e*NB + nb)*KG + g.
   A tile is 64 slots of 16 bytes.  Slot L covers column n = 16*nb + L%16 and
   quarter h = L//16.
-  * int4 formats: byte 4*j + b of slot L (j, b in 0..3) holds
-    k = 128*g + 32*j + 8*h + 2*b in its low nibble and k+1 in its high nibble.
+  * int4 formats: 32-bit word j of slot L (j in 0..3, little endian) holds
+    the 8 values k = 128*g + 32*j + 8*h + i, i in 0..7, with value i in nibble
+    position i/2 for even i and 4 + (i-1)/2 for odd i (so nibbles p and p+4
+    are the consecutive pair 2p, 2p+1).
     Stored value: uint4_zp -> u; int4_sym -> q + 8 (offset binary).
   * mxfp4: byte b (0..15) of slot L holds k = 128*g + 32*h + 2*b (low nibble)
     and k+1 (high nibble), E2M1 bits as given.
@@ -86,19 +88,25 @@ def transform_ref(fmt, codes, scales, zeros=None):
     L = np.arange(64)
     c = L % 16
     h = L // 16
-    for b in range(16):
-        if fmt == FMT_MXFP4:
-            k_lo = 32 * h + 2 * b                         # [64]
-        else:
-            j, bb = b // 4, b % 4
-            k_lo = 32 * j + 8 * h + 2 * bb
-        for g in range(KG):
-            klo = 128 * g + k_lo
-            for nb in range(NB):
-                col = 16 * nb + c
-                lo = u[:, col, klo]                        # [E, 64]
-                hi = u[:, col, klo + 1]
-                tiles[:, nb, g, :, b] = lo | (hi << 4)
+    if fmt == FMT_MXFP4:
+        for b in range(16):
+            k_lo = 32 * h + 2 * b                          # [64]
+            for g in range(KG):
+                klo = 128 * g + k_lo
+                for nb in range(NB):
+                    col = 16 * nb + c
+                    tiles[:, nb, g, :, b] = u[:, col, klo] | (u[:, col, klo + 1] << 4)
+    else:
+        words = np.zeros((E, NB, KG, 64, 4), dtype=np.uint32)
+        for j in range(4):
+            for i in range(8):
+                pos = i // 2 if i % 2 == 0 else 4 + (i - 1) // 2
+                for g in range(KG):
+                    kk = 128 * g + 32 * j + 8 * h + i        # [64]
+                    for nb in range(NB):
+                        col = 16 * nb + c
+                        words[:, nb, g, :, j] |= u[:, col, kk].astype(np.uint32) << (4 * pos)
+        tiles = words.view(np.uint8).reshape(E, NB, KG, 64, 16)
     out[:tiles.size] = tiles.ravel()
 
     # Region B

@@ -33,11 +33,17 @@ def test_layout_addresses(fmt, E, N, K):
                 if fmt == quant.FMT_MXFP4:
                     slot = c + 16 * (kk // 32)
                     byte = (kk % 32) // 2
+                    shift = 4 * (k % 2)
                 else:
+                    # word j = kk // 32 of the slot; value i = kk % 8 sits in nibble
+                    # position i/2 (even i) or 4 + (i-1)/2 (odd i) of that word
                     slot = c + 16 * ((kk % 32) // 8)
-                    byte = 4 * (kk // 32) + (kk % 8) // 2
+                    i = kk % 8
+                    pos = i // 2 if i % 2 == 0 else 4 + (i - 1) // 2
+                    byte = 4 * (kk // 32) + pos // 2
+                    shift = 4 * (pos % 2)
                 addr = ((e * NB + nb) * KG + g) * 1024 + slot * 16 + byte
-                nib = (out[addr] >> (4 * (k % 2))) & 0xF
+                nib = (out[addr] >> shift) & 0xF
                 if n < N:
                     src = (codes[e, n, k // 2] >> (4 * (k % 2))) & 0xF
                     want = src ^ 8 if fmt == quant.FMT_INT4_SYM else src
