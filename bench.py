@@ -67,6 +67,23 @@ def traffic_for(kernel_key):
     return e.get("bytes_per_launch")
 
 
+def capture(torch, fn):
+    """Run fn once eagerly on a side stream (warm-up, lazy init), then capture
+    it into a HIP graph (torch.cuda.CUDAGraph).  The library launches on the
+    current stream, so every kernel of fn is recorded; fn allocates nothing."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 class Timer:
     """HIP events on the current stream (the stream the library launches on)."""
 
@@ -145,36 +162,51 @@ def run_dense(args, fmt):
     alg_w = oq.storage_bytes(n, k, fmt)          # algorithmic weight bytes (standard format)
     tm = Timer(torch)
 
-    # ---- the contract's timed region: K steps, each one pass of the M sweep
-    it = 0
-    for _ in range(args.warmup):
-        for m in ms:
-            dense_call(hm, S, m, it, fmt)
-            it += 1
+    ctr = [0]
+
+    def steps(nsteps):
+        def fn():
+            for _ in range(nsteps):
+                for m in ms:
+                    dense_call(hm, S, m, ctr[0], fmt)
+                    ctr[0] += 1
+        return fn
+
+    # ---- eager launches (host launch overhead included), for reference
+    steps(args.warmup)()
     torch.cuda.synchronize()
     tm.start()
-    for _ in range(args.steps):
-        for m in ms:
-            dense_call(hm, S, m, it, fmt)
-            it += 1
+    steps(args.steps)()
+    eager_ms_step = tm.stop_ms() / args.steps
+
+    # ---- the contract's timed region: K steps (one pass of the M sweep each),
+    # launched as one HIP graph replay after W warm-up steps (also a replay)
+    g_warm = capture(torch, steps(max(args.warmup, 1)))
+    g_steps = capture(torch, steps(args.steps))
+    g_warm.replay()
+    torch.cuda.synchronize()
+    tm.start()
+    g_steps.replay()
     ms_total = tm.stop_ms()
     torch.cuda.synchronize()
     ms_step = ms_total / args.steps
     flops_step = sum(2.0 * m * n * k for m in ms)
     value = flops_step / (ms_step * 1e-3) / 1e12
 
-    # ---- per-M timing (back-to-back launches of the same call, rotating weights)
+    # ---- per-M timing: a graph of `reps` back-to-back calls, rotating weights
     sweep = []
     for m in ms:
-        for _ in range(3):
-            dense_call(hm, S, m, it, fmt)
-            it += 1
+        def reps_fn(m=m):
+            for _ in range(args.reps):
+                dense_call(hm, S, m, ctr[0], fmt)
+                ctr[0] += 1
+        g = capture(torch, reps_fn)
+        g.replay()
         torch.cuda.synchronize()
         tm.start()
-        for _ in range(args.reps):
-            dense_call(hm, S, m, it, fmt)
-            it += 1
+        g.replay()
         us = tm.stop_ms() * 1e3 / args.reps
+        del g
         fl = 2.0 * m * n * k
         xbytes = m * k * (1 if fmt == "mxfp4" else 2) + (4 * m if fmt == "mxfp4" else 0)
         ybytes = m * n * 2
@@ -208,7 +240,8 @@ def run_dense(args, fmt):
     out = dict(metric=METRIC, value=round(value, 3), unit="TFLOP/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms_step, 4), higher_is_better=True,
                scaling="weak", vs_baseline=None, dtype="fp8" if fmt == "mxfp4" else "bf16",
-               data="synthetic",
+               data="synthetic", timing="HIP graph replay of the K steps (eager launch: "
+               f"{eager_ms_step:.4f} ms/step)",
                config=dict(workload=wl, weight_copies=S["copies"],
                            weight_bytes_per_copy=S["wbytes"], algorithmic_weight_bytes=alg_w),
                sweep=sweep, roofline=roof, cpu_baseline=cpu)
@@ -317,13 +350,19 @@ def run_moe(args, fmt):
                 hm.hm_moe_gemm(d_gu, w_gu, x, off, sp, t, topk, 0, y=y1, ws=ws1)
                 hm.hm_moe_gemm(d_dn, w_dn, a2, off, sp, t, topk, 1, y=y2, ws=ws2)
 
-        for _ in range(args.warmup):
-            step()
+        def nsteps(k):
+            def fn():
+                for _ in range(k):
+                    step()
+            return fn
+        g_warm = capture(torch, nsteps(max(args.warmup, 1)))
+        g_steps = capture(torch, nsteps(args.steps))
+        g_warm.replay()
         torch.cuda.synchronize()
         tm.start()
-        for _ in range(args.steps):
-            step()
+        g_steps.replay()
         ms_t = tm.stop_ms() / args.steps
+        del g_warm, g_steps
         counts = np.bincount(ids.ravel(), minlength=E)
         act = int((counts > 0).sum())
         fl = 2.0 * P * (2 * I) * H + 2.0 * P * H * I

@@ -168,12 +168,14 @@ def hm_gemm(desc, w_dev, x, x_row_scale=None, y=None, ws=None, afmt=None, stream
     if y is None:
         y = torch.empty(m, desc.n, dtype=torch.bfloat16, device=x.device)
     _need(y, torch.bfloat16, m * desc.n, "y")
-    need = hm_gemm_workspace_size(desc, afmt, m)
-    if need and (ws is None or ws.numel() < need):
-        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if ws is None:
+        # a caller-provided workspace is passed through as is (the library checks its size)
+        need = hm_gemm_workspace_size(desc, afmt, m)
+        if need:
+            ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     _ok("hm_gemm", lib.hm_gemm(ctypes.byref(desc), _ptr(w_dev), int(afmt), _ptr(x), _ptr(x_row_scale),
-                               m, _ptr(y), _ptr(ws) if need else None,
-                               ws.numel() if (need and ws is not None) else 0, _stream(stream)))
+                               m, _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0,
+                               _stream(stream)))
     return y
 
 
@@ -215,8 +217,8 @@ def hm_moe_gemm(desc, w_dev, a, offsets, sorted_pairs, t, topk, a_rows_are_pairs
     if y is None:
         y = torch.empty(P, desc.n, dtype=torch.bfloat16, device=a.device)
     _need(y, torch.bfloat16, P * desc.n, "y")
-    need = hm_moe_gemm_workspace_size(desc, afmt, t, topk)
-    if ws is None or ws.numel() < need:
+    if ws is None:
+        need = hm_moe_gemm_workspace_size(desc, afmt, t, topk)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=a.device)
     _ok("hm_moe_gemm", lib.hm_moe_gemm(ctypes.byref(desc), _ptr(w_dev), int(afmt), _ptr(a),
                                        _ptr(a_row_scale), int(a_rows_are_pairs), int(t), int(topk),

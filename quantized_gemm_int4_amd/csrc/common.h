@@ -4,9 +4,11 @@
 //   NB = ceil(N/16) column blocks, KG = K/128 steps along K.
 //   Region A (codes): tile (e, nb, g) of 1024 bytes at ((e*NB + nb)*KG + g)*1024;
 //     64 slots of 16 bytes, slot L = column 16*nb + L%16, quarter h = L/16.
-//     int4:  byte 4*j+b of slot L holds k = 128g + 32j + 8h + 2b (low nibble), k+1 (high);
-//            the u32 j of a slot is the 8 K-values one lane feeds to the j-th
-//            16x16x32 bf16 MFMA of the step.  INT4_SYM is stored offset-binary (q+8).
+//     int4:  u32 j of slot L holds k = 128g + 32j + 8h + i (i = 0..7), value i in
+//            nibble i/2 (even i) or 4 + i/2 (odd i), so that the pair (2p, 2p+1)
+//            sits in nibbles p and p+4, one per 16-bit half; the u32 j of a slot
+//            is the 8 K-values one lane feeds to the j-th 16x16x32 bf16 MFMA of
+//            the step.  INT4_SYM is stored offset-binary (q+8).
 //     mxfp4: byte b of slot L holds k = 128g + 32h + 2b (low), k+1 (high); the
 //            16 bytes are the 32 E2M1 values one lane feeds to a 16x16x128
 //            scaled MFMA.
@@ -69,19 +71,35 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// Eight 4-bit unsigned codes (element i at bits 4i) -> eight bf16 of s*u + zs,
-// in element order, as four packed pairs.  The fp32 value s*u + zs = s*(u-z)
-// is exact (at most 12 significant bits), then rounded once to bf16.
+// Eight 4-bit unsigned codes in device order (value 2j in nibble j, value
+// 2j+1 in nibble j+4) -> eight bf16 of s*u + zs, in value order, as four packed
+// pairs.  The fp32 value s*u + zs = s*(u-z) is exact (at most 12 significant
+// bits), then rounded once to bf16.
 __device__ __forceinline__ u32x4_t dq8_u4(uint32_t w, float s, float zs) {
-  uint32_t lo = w & 0x0F0F0F0Fu;         // bytes: elements 0,2,4,6
-  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: elements 1,3,5,7
   u32x4_t r;
-  r[0] = pack_bf16(__builtin_fmaf((float)(lo & 0xFF), s, zs), __builtin_fmaf((float)(hi & 0xFF), s, zs));
-  r[1] = pack_bf16(__builtin_fmaf((float)((lo >> 8) & 0xFF), s, zs), __builtin_fmaf((float)((hi >> 8) & 0xFF), s, zs));
-  r[2] = pack_bf16(__builtin_fmaf((float)((lo >> 16) & 0xFF), s, zs), __builtin_fmaf((float)((hi >> 16) & 0xFF), s, zs));
-  r[3] = pack_bf16(__builtin_fmaf((float)(lo >> 24), s, zs), __builtin_fmaf((float)(hi >> 24), s, zs));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = (w >> (4 * j)) & 0x000F000Fu;   // values 2j (bits 0-3) and 2j+1 (bits 16-19)
+    r[j] = pack_bf16(__builtin_fmaf((float)(t & 0xFFu), s, zs), __builtin_fmaf((float)(t >> 16), s, zs));
+  }
   return r;
 }
+
+// The same eight codes as bf16 values 1 + u/16, exact, in value order: each
+// code is OR-ed into the top four mantissa bits of bf16(1.0), so the constant
+// part of every value (1) is only 16 code steps, which keeps the cancellation
+// in a later subtraction of the zero-point product small.  Two instructions
+// per pair, no conversions.
+__device__ __forceinline__ u32x4_t raw8_u4(uint32_t w) {
+  u32x4_t r;
+  r[0] = ((w << 3) & 0x00780078u) | 0x3F803F80u;
+#pragma unroll
+  for (int j = 1; j < 4; ++j) r[j] = ((w >> (4 * j - 3)) & 0x00780078u) | 0x3F803F80u;
+  return r;
+}
+
+// bf16 bits of 1 + z/16 for a 4-bit zero point z, matching raw8_u4.
+__device__ __forceinline__ uint32_t raw_u4_bits(uint32_t z) { return 0x3F80u | (z << 3); }
 
 // 16x16x32 bf16 MFMA: C[i][j] += sum_k A[i][k] B[k][j]; lane L supplies A row
 // L%16 and B column L%16 for K-quarter L/16 (8 values each); C: lane L holds

@@ -15,7 +15,8 @@ namespace {
 
 using namespace hm;
 
-constexpr int kStreamMaxRows = 32;   // rows handled by the streaming kernel (two 16-row blocks)
+constexpr int kStreamMaxRows = 32;   // dense rows handled by the streaming kernel (two 16-row blocks)
+constexpr int kMoeStreamRows = 16;   // expert segments of at most this many rows use the streaming kernel
 constexpr int kGroupedGridStream = 2048;
 constexpr int kGroupedGridTile = 1024;
 
@@ -63,14 +64,16 @@ DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
   if (force == 1 && m > kStreamMaxRows) p.stream = false;  // streaming handles <= 32 rows per block
   if (!p.stream) return p;
   p.sc.mb = (m <= 16) ? 1 : 2;
-  p.sc.nbw = env_int("HM_STREAM_NBW", G.NB >= 512 ? 2 : 1);
+  p.sc.nbw = env_int("HM_STREAM_NBW", 1);
   if (p.sc.nbw != 1 && p.sc.nbw != 2 && p.sc.nbw != 4) p.sc.nbw = 1;
   const int64_t n_tiles = (G.NB + 4 * p.sc.nbw - 1) / (4 * p.sc.nbw);
   const int64_t m_chunks = (m + 16 * p.sc.mb - 1) / (16 * p.sc.mb);
   int64_t splits = env_int("HM_STREAM_SPLITS", 0);
   if (splits <= 0) {
-    const int64_t target = 1024;
-    splits = (target + n_tiles * m_chunks - 1) / (n_tiles * m_chunks);
+    // enough waves to keep every SIMD streaming (1024 SIMDs); split K only below that
+    const int64_t target_waves = 800;
+    const int64_t waves = n_tiles * 4 * m_chunks;
+    splits = (target_waves + waves - 1) / waves;
   }
   if (splits > G.KG) splits = G.KG;
   if (splits < 1) splits = 1;
@@ -309,10 +312,10 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   a.rows_are_pairs = a_rows_are_pairs;
 
   a.P = p.P;
-  hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, kStreamMaxRows, kTileM, p.max_s,
+  hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, kMoeStreamRows, kTileM, p.max_s,
                                      p.max_t, hdr, su, tu, stream);
   if (e == hipSuccess) {
-    StreamCfg sc{2, p.nbw, 1};
+    StreamCfg sc{kMoeStreamRows / 16, p.nbw, 1};
     const int64_t nts = (a.G.NB + 4 * sc.nbw - 1) / (4 * sc.nbw);
     int64_t gi = p.max_s * nts;
     if (gi > kGroupedGridStream) gi = kGroupedGridStream;

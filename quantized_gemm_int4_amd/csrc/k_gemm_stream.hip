@@ -15,25 +15,43 @@
 
 namespace hm {
 
-constexpr int kChunkG = 2;  // 128-K groups per staged activation chunk
+// activation bytes staged per block: 159 KiB of dynamic LDS, leaving room for the
+// row tables within the 160 KiB of a gfx950 compute unit
+constexpr int64_t kStreamLdsBudget = 159 * 1024;
 
-template <bool MX, int MB, int NBW, bool GROUPED>
+// LDS-only barrier: waits for this wave's LDS operations, then meets the other
+// waves.  Unlike __syncthreads() it does not wait for outstanding global loads
+// (on CDNA one counter covers loads and stores), so the weight prefetch ring
+// stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Template parameters: MX (W4A8-MXFP4 vs W4A16), ZP (zero points), MB (16-row
+// blocks per unit), NBW (16-column blocks per wave), DW (weight prefetch ring:
+// K groups of 128 held in registers ahead of use), GROUPED.
+// Runtime: pg = K groups per activation piece staged in LDS (a multiple of DW);
+// dynamic LDS = staged rows x (pg * bytes per group + 16).
+template <bool MX, bool ZP, int MB, int NBW, int DW, bool GROUPED>
 __global__ void __launch_bounds__(256)
-k_gemm_stream(GemmArgs a, int n_tiles) {
+k_gemm_stream(GemmArgs a, int n_tiles, int pg) {
   constexpr int ROWS = MB * 16;
-  constexpr int XB = MX ? (kChunkG * 128 + 16) : (kChunkG * 256 + 16);  // LDS row stride (bytes)
-  constexpr int PIECES_PER_ROW = MX ? kChunkG * 8 : kChunkG * 16;       // 16-byte pieces per row
-  constexpr int XLD = (ROWS * PIECES_PER_ROW + 255) / 256;               // pieces per thread
-  __shared__ __attribute__((aligned(16))) uint8_t xs_lds[2][ROWS * XB];
+  constexpr int GB = MX ? 128 : 256;                    // activation bytes per row per K group
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs_lds[];
   __shared__ int64_t arow_s[ROWS];
   __shared__ int64_t orow_s[ROWS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const Geom G = a.G;
   const int64_t K = G.K;
   const int n_l = lane & 15, q_l = lane >> 4;
   const uint8_t* xbase = reinterpret_cast<const uint8_t*>(a.x);
   const int64_t xrow_bytes = MX ? K : 2 * K;
+  const uint16_t* s16 = reinterpret_cast<const uint16_t*>(a.w + G.off_scales);
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(a.w + G.off_scales);
+  const uint32_t* z32 = reinterpret_cast<const uint32_t*>(a.w + G.off_zeros);
+  const int XB = pg * GB + 16;                          // LDS row stride (bytes), padded
 
   const int64_t n_items = GROUPED ? (int64_t)a.hdr[0] * n_tiles : 1;
   for (int64_t item = GROUPED ? blockIdx.x : 0; item < n_items;
@@ -46,11 +64,11 @@ k_gemm_stream(GemmArgs a, int n_tiles) {
       nt = (int)(item % n_tiles);
       const int32_t* u = a.units + 4 * unit;
       e = u[0];
-      rcount = u[2];
+      rcount = u[2] < ROWS ? u[2] : ROWS;
       g_begin = 0;
       g_end = G.KG;
       if (tid < ROWS) {
-        int64_t ar = -1, orr = -1;
+        int64_t ar = 0, orr = -1;   // invalid rows read row 0 (always present) and are not stored
         if (tid < rcount) {
           const int64_t pair = a.sorted_pairs[u[1] + tid];
           if (pair >= 0 && pair < a.P) {
@@ -69,76 +87,65 @@ k_gemm_stream(GemmArgs a, int n_tiles) {
       g_begin = (int64_t)split * a.ksg;
       g_end = (g_begin + a.ksg < G.KG) ? g_begin + a.ksg : G.KG;
       if (tid < ROWS) {
-        arow_s[tid] = (tid < rcount) ? m0 + tid : -1;
-        orow_s[tid] = arow_s[tid];
+        const bool ok = tid < rcount;
+        arow_s[tid] = ok ? m0 + tid : m0;
+        orow_s[tid] = ok ? m0 + tid : -1;
       }
     }
     __syncthreads();
 
     const int64_t nb0 = ((int64_t)nt * 4 + wave) * NBW;
-    const int64_t n_chunks = (g_end - g_begin + kChunkG - 1) / kChunkG;
-
-    // ---- activation chunk: global -> registers -> LDS
-    u32x4_t xr[XLD];
-    auto load_x = [&](int64_t c) {
-      const int64_t gc0 = g_begin + c * kChunkG;
-      const int cg = (int)((g_end - gc0) < kChunkG ? (g_end - gc0) : kChunkG);
+    const int ng = (int)(g_end - g_begin);
+    int64_t nbc[NBW];  // clamped column blocks: loads stay in bounds, results of
+                       // blocks >= NB are never stored
 #pragma unroll
-      for (int i = 0; i < XLD; ++i) {
-        const int q = tid + 256 * i;
-        const int row = q / PIECES_PER_ROW, pc = q % PIECES_PER_ROW;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (row < ROWS && row < rcount && pc < cg * (PIECES_PER_ROW / kChunkG)) {
-          const int64_t ar = arow_s[row];
-          if (ar >= 0) v = ld16(xbase + ar * xrow_bytes + gc0 * (MX ? 128 : 256) + pc * 16);
+    for (int j = 0; j < NBW; ++j) nbc[j] = (nb0 + j < G.NB) ? nb0 + j : G.NB - 1;
+    // LDS row of each MFMA row block: rows past the staged ones reuse the last
+    // staged row (their outputs are never stored)
+    int lrow[MB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) lrow[rb] = (rb * 16 + n_l < rcount) ? rb * 16 + n_l : rcount - 1;
+
+    // stage activation rows [0, rcount) x groups [gp, gp + plen) into LDS
+    auto stage_x = [&](int gp, int plen) {
+      const int per_row = plen * (GB / 16);
+      const int total = rcount * per_row;
+      const int64_t off0 = (g_begin + gp) * GB;
+#pragma nounroll
+      for (int base = 0; base < total; base += 256 * 4) {
+        u32x4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = base + u * 256 + tid;
+          if (i < total)
+            v[u] = ld16(xbase + arow_s[i / per_row] * xrow_bytes + off0 + (i % per_row) * 16);
         }
-        xr[i] = v;
-      }
-    };
-    auto store_x = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < XLD; ++i) {
-        const int q = tid + 256 * i;
-        const int row = q / PIECES_PER_ROW, pc = q % PIECES_PER_ROW;
-        if (row < ROWS) st16(&xs_lds[buf][row * XB + pc * 16], xr[i]);
+        for (int u = 0; u < 4; ++u) {
+          const int i = base + u * 256 + tid;
+          if (i < total) st16(xs_lds + (i / per_row) * XB + (i % per_row) * 16, v[u]);
+        }
       }
     };
 
-    // ---- weight registers for one chunk
-    u32x4_t bq[NBW][kChunkG];
-    float bs[NBW][kChunkG], bz[NBW][kChunkG];
-    int bsc[NBW][kChunkG];
-    auto load_w = [&](int64_t c, u32x4_t (&q)[NBW][kChunkG], float (&s)[NBW][kChunkG],
-                      float (&zs)[NBW][kChunkG], int (&sc)[NBW][kChunkG]) {
-      const int64_t gc0 = g_begin + c * kChunkG;
+    // ---- weight ring: DW groups ahead, raw scale / zero words kept until use
+    u32x4_t wq[DW][NBW];
+    // INT4: wsr / wsh hold the bf16 scales of the four output rows 4*q_l + 0..3
+    // that this lane accumulates (the MFMA result is scaled, not the operand).
+    uint32_t wsr[DW][NBW], wsh[MX ? 1 : DW][MX ? 1 : NBW], wzr[DW][NBW];
+    auto load_w = [&](int d, int gl) {                  // gl: group index within [0, ng)
+      const int64_t g = g_begin + gl;
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        const int64_t nb = nb0 + j;
-#pragma unroll
-        for (int gl = 0; gl < kChunkG; ++gl) {
-          const int64_t g = gc0 + gl;
-          q[j][gl] = (u32x4_t){0u, 0u, 0u, 0u};
-          s[j][gl] = 0.0f;
-          zs[j][gl] = 0.0f;
-          sc[j][gl] = 0;
-          if (nb < G.NB && g < g_end) {
-            const int64_t tile = (e * G.NB + nb) * G.KG + g;
-            q[j][gl] = ld16(a.w + tile * 1024 + lane * 16);
-            if (MX) {
-              const uint32_t* scm = reinterpret_cast<const uint32_t*>(a.w + G.off_scales);
-              sc[j][gl] = (int)((scm[((e * G.NB + nb) * G.KG4 + g / 4) * 64 + lane] >> (8 * (g % 4))) & 0xFF);
-            } else {
-              const uint16_t* s16 = reinterpret_cast<const uint16_t*>(a.w + G.off_scales);
-              const float sv = bf16_to_f32(s16[tile * 16 + n_l]);
-              float z = 8.0f;
-              if (a.wfmt == W_UINT4_ZP) {
-                const uint64_t* zz = reinterpret_cast<const uint64_t*>(a.w + G.off_zeros);
-                z = (float)((zz[tile] >> (4 * n_l)) & 0xF);
-              }
-              s[j][gl] = sv;
-              zs[j][gl] = -z * sv;
-            }
-          }
+        const int64_t tile = (e * G.NB + nbc[j]) * G.KG + g;
+        wq[d][j] = ld16(a.w + tile * 1024 + lane * 16);
+        if (MX) {
+          wsr[d][j] = s32[((e * G.NB + nbc[j]) * G.KG4 + g / 4) * 64 + lane];
+        } else {
+          const u32x2_t sp = *reinterpret_cast<const u32x2_t*>(s16 + tile * 16 + 4 * q_l);
+          wsr[d][j] = sp[0];
+          wsh[d][j] = sp[1];
+          if (ZP) wzr[d][j] = z32[tile * 2 + (n_l >> 3)];
         }
       }
     };
@@ -149,67 +156,98 @@ k_gemm_stream(GemmArgs a, int n_tiles) {
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb) acc[j][rb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    u32x4_t nq[NBW][kChunkG];
-    float ns[NBW][kChunkG], nz[NBW][kChunkG];
-    int nsc[NBW][kChunkG];
-    if (n_chunks > 0) {
-      load_x(0);
-      load_w(0, nq, ns, nz, nsc);
-      store_x(0);
-    }
-    __syncthreads();
-
-    for (int64_t c = 0; c < n_chunks; ++c) {
+    // K is walked in pieces of pg groups whose activations fit in LDS.  Each
+    // piece restarts its weight ring (one memory latency per piece; a single
+    // piece covers the whole K range whenever the rows fit), which keeps the
+    // ring's load order identical on every entry to the round loop so that
+    // each slot waits only for its own loads.
+    const int n_pieces = (ng + pg - 1) / pg;
+#pragma nounroll
+    for (int p = 0; p < n_pieces; ++p) {
+      const int gp = p * pg;
+      const int plen = (ng - gp) < pg ? (ng - gp) : pg;
+      if (p > 0) lds_barrier();               // everyone is done with the previous piece
+      stage_x(gp, plen);
 #pragma unroll
-      for (int j = 0; j < NBW; ++j)
+      for (int d = 0; d < DW; ++d) load_w(d, gp + (d < plen ? d : plen - 1));
+      lds_barrier();
+      const int rounds = (plen + DW - 1) / DW;
+#pragma nounroll
+      for (int r = 0; r < rounds; ++r) {
 #pragma unroll
-        for (int gl = 0; gl < kChunkG; ++gl) {
-          bq[j][gl] = nq[j][gl]; bs[j][gl] = ns[j][gl]; bz[j][gl] = nz[j][gl]; bsc[j][gl] = nsc[j][gl];
-        }
-      const bool more = (c + 1 < n_chunks);
-      if (more) {
-        load_w(c + 1, nq, ns, nz, nsc);
-        load_x(c + 1);
-      }
-      const uint8_t* xl = xs_lds[c & 1];
-      const int64_t gc0 = g_begin + c * kChunkG;
+        for (int d = 0; d < DW; ++d) {
+          const int lg = r * DW + d;          // group within the piece
+          if (lg < plen) {
+            const int64_t g = g_begin + gp + lg;
+            if (MX) {
+              u32x4_t a0[MB], a1[MB];
 #pragma unroll
-      for (int gl = 0; gl < kChunkG; ++gl) {
-        if (gc0 + gl >= g_end) break;
-        if (MX) {
-          u32x4_t a0[MB], a1[MB];
+              for (int rb = 0; rb < MB; ++rb) {
+                const uint8_t* xp = xs_lds + lrow[rb] * XB + lg * 128 + 16 * q_l;
+                a0[rb] = ld16(xp);
+                a1[rb] = ld16(xp + 64);
+              }
 #pragma unroll
-          for (int rb = 0; rb < MB; ++rb) {
-            const uint8_t* p = xl + (rb * 16 + n_l) * XB + gl * 128 + 16 * q_l;
-            a0[rb] = ld16(p);
-            a1[rb] = ld16(p + 64);
-          }
+              for (int j = 0; j < NBW; ++j) {
+                const int sc = (int)((wsr[d][j] >> (8 * (g & 3))) & 0xFF);
 #pragma unroll
-          for (int j = 0; j < NBW; ++j) {
-            if (nb0 + j >= G.NB) continue;
+                for (int rb = 0; rb < MB; ++rb)
+                  acc[j][rb] = mfma_fp4_fp8(wq[d][j], a0[rb], a1[rb], acc[j][rb], sc, 127);
+              }
+            } else {
+              // Raw codes: the MFMA sees bf16(1 + u/16) (exact), a second MFMA sees
+              // bf16(1 + z/16); their difference is sum_k x_k (u_k - z)/16 for this
+              // group, exactly 0 where every code equals the zero point, and 16
+              // times the group scale is applied once to the difference.
+              f32x4_t raw[NBW][MB], zc[ZP ? NBW : 1][MB];
+              u32x4_t bz[ZP ? NBW : 1];
 #pragma unroll
-            for (int rb = 0; rb < MB; ++rb)
-              acc[j][rb] = mfma_fp4_fp8(bq[j][gl], a0[rb], a1[rb], acc[j][rb], bsc[j][gl], 127);
-          }
-        } else {
+              for (int j = 0; j < (ZP ? NBW : 1); ++j) {
+                const uint32_t z = ZP ? ((wzr[d][j] >> (4 * (n_l & 7))) & 0xF) : 8u;
+                const uint32_t pz = raw_u4_bits(z) * 0x00010001u;
+                bz[j] = (u32x4_t){pz, pz, pz, pz};
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            u32x4_t af[MB];
+                for (int rb = 0; rb < MB; ++rb) zc[j][rb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+              }
 #pragma unroll
-            for (int rb = 0; rb < MB; ++rb)
-              af[rb] = ld16(xl + (rb * 16 + n_l) * XB + (gl * 128 + 32 * kk + 8 * q_l) * 2);
+              for (int j = 0; j < NBW; ++j)
 #pragma unroll
-            for (int j = 0; j < NBW; ++j) {
-              if (nb0 + j >= G.NB) continue;
-              const u32x4_t bw = dq8_u4(bq[j][gl][kk], bs[j][gl], bz[j][gl]);
+                for (int rb = 0; rb < MB; ++rb) raw[j][rb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int rb = 0; rb < MB; ++rb) acc[j][rb] = mfma_bf16(bw, af[rb], acc[j][rb]);
+              for (int kk = 0; kk < 4; ++kk) {
+                u32x4_t af[MB];
+#pragma unroll
+                for (int rb = 0; rb < MB; ++rb)
+                  af[rb] = ld16(xs_lds + lrow[rb] * XB + (lg * 128 + 32 * kk + 8 * q_l) * 2);
+#pragma unroll
+                for (int j = 0; j < NBW; ++j) {
+                  const u32x4_t bw = raw8_u4(wq[d][j][kk]);
+#pragma unroll
+                  for (int rb = 0; rb < MB; ++rb) raw[j][rb] = mfma_bf16(bw, af[rb], raw[j][rb]);
+                }
+#pragma unroll
+                for (int j = 0; j < (ZP ? NBW : 1); ++j)
+#pragma unroll
+                  for (int rb = 0; rb < MB; ++rb) zc[j][rb] = mfma_bf16(bz[j], af[rb], zc[j][rb]);
+              }
+#pragma unroll
+              for (int j = 0; j < NBW; ++j) {
+                const float s0 = bf16_to_f32(wsr[d][j] & 0xFFFFu), s1 = __uint_as_float(wsr[d][j] & 0xFFFF0000u);
+                const float s2 = bf16_to_f32(wsh[d][j] & 0xFFFFu), s3 = __uint_as_float(wsh[d][j] & 0xFFFF0000u);
+#pragma unroll
+                for (int rb = 0; rb < MB; ++rb) {
+                  const f32x4_t dl = (raw[j][rb] - zc[ZP ? j : 0][rb]) * 16.f;   // exact scaling
+                  acc[j][rb][0] = fmaf(s0, dl[0], acc[j][rb][0]);
+                  acc[j][rb][1] = fmaf(s1, dl[1], acc[j][rb][1]);
+                  acc[j][rb][2] = fmaf(s2, dl[2], acc[j][rb][2]);
+                  acc[j][rb][3] = fmaf(s3, dl[3], acc[j][rb][3]);
+                }
+              }
             }
           }
+          load_w(d, gp + (lg + DW < plen ? lg + DW : plen - 1));
         }
       }
-      if (more) store_x((int)((c + 1) & 1));
-      __syncthreads();
     }
 
     // ---- epilogue: lane holds C[n = 16nb + 4*q_l + r][row = 16rb + n_l]
@@ -273,9 +311,27 @@ k_splitk_reduce(GemmArgs a, int splits) {
   }
 }
 
-template <bool MX, int MB, int NBW, bool GROUPED>
+template <bool MX, bool ZP, int MB, int NBW, bool GROUPED>
 static hipError_t go_stream(const GemmArgs& a, const StreamCfg& c, int grid_items, hipStream_t st) {
+  // ring depth: up to 16 groups per 16-column block, within the 63 outstanding
+  // vector-memory operations one wave can track (three loads per group)
+  constexpr int DW = (NBW == 1) ? (MB == 1 ? 16 : 8) : (NBW == 2 ? 8 : 4);
   const int n_tiles = (int)((a.G.NB + 4 * NBW - 1) / (4 * NBW));
+  const int gb = (a.wfmt == W_MXFP4) ? 128 : 256;
+  // activation piece: as many K groups as fit the LDS budget, a multiple of DW
+  const int64_t rows = GROUPED ? 16 * MB : (a.M < 16 * MB ? a.M : 16 * MB);
+  const int64_t ksl = GROUPED ? a.G.KG : a.ksg;
+  int64_t pg = (kStreamLdsBudget / rows - 16) / gb;
+  pg = pg / DW * DW;
+  if (pg < DW) pg = DW;
+  const int64_t need = (ksl + DW - 1) / DW * DW;
+  if (pg > need) pg = need;
+  const size_t lds = (size_t)rows * (pg * gb + 16);
+  // allow more than the default dynamic LDS (set once per instance; thread-safe static init)
+  static const hipError_t attr_err = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_gemm_stream<MX, ZP, MB, NBW, DW, GROUPED>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsBudget);
+  if (attr_err != hipSuccess) return attr_err;
   dim3 grid;
   if (GROUPED) {
     grid = dim3((unsigned)(grid_items > 0 ? grid_items : 1));
@@ -283,32 +339,36 @@ static hipError_t go_stream(const GemmArgs& a, const StreamCfg& c, int grid_item
     const int64_t m_chunks = (a.M + MB * 16 - 1) / (MB * 16);
     grid = dim3((unsigned)n_tiles, (unsigned)c.splits, (unsigned)m_chunks);
   }
-  hipLaunchKernelGGL((k_gemm_stream<MX, MB, NBW, GROUPED>), grid, dim3(256), 0, st, a, n_tiles);
+  hipLaunchKernelGGL((k_gemm_stream<MX, ZP, MB, NBW, DW, GROUPED>), grid, dim3(256), lds, st, a,
+                     n_tiles, (int)pg);
   return hipGetLastError();
 }
 
-template <bool MX, int MB, bool GROUPED>
+template <bool MX, bool ZP, int MB, bool GROUPED>
 static hipError_t go_stream_nbw(const GemmArgs& a, const StreamCfg& c, int gi, hipStream_t st) {
   switch (c.nbw) {
-    case 1: return go_stream<MX, MB, 1, GROUPED>(a, c, gi, st);
-    case 2: return go_stream<MX, MB, 2, GROUPED>(a, c, gi, st);
-    default: return go_stream<MX, MB, 4, GROUPED>(a, c, gi, st);
+    case 1: return go_stream<MX, ZP, MB, 1, GROUPED>(a, c, gi, st);
+    case 2: return go_stream<MX, ZP, MB, 2, GROUPED>(a, c, gi, st);
+    default: return go_stream<MX, ZP, MB, 4, GROUPED>(a, c, gi, st);
   }
 }
 
-template <bool MX, bool GROUPED>
+template <bool MX, bool ZP, bool GROUPED>
 static hipError_t go_stream_mb(const GemmArgs& a, const StreamCfg& c, int gi, hipStream_t st) {
-  return (c.mb == 1) ? go_stream_nbw<MX, 1, GROUPED>(a, c, gi, st)
-                     : go_stream_nbw<MX, 2, GROUPED>(a, c, gi, st);
+  return (c.mb == 1) ? go_stream_nbw<MX, ZP, 1, GROUPED>(a, c, gi, st)
+                     : go_stream_nbw<MX, ZP, 2, GROUPED>(a, c, gi, st);
 }
 
 hipError_t launch_gemm_stream(const GemmArgs& a, const StreamCfg& c, bool grouped, int grid_items,
                               hipStream_t st) {
-  const bool mx = (a.wfmt == W_MXFP4);
-  if (mx) return grouped ? go_stream_mb<true, true>(a, c, grid_items, st)
-                         : go_stream_mb<true, false>(a, c, grid_items, st);
-  return grouped ? go_stream_mb<false, true>(a, c, grid_items, st)
-                 : go_stream_mb<false, false>(a, c, grid_items, st);
+  if (a.wfmt == W_MXFP4)
+    return grouped ? go_stream_mb<true, false, true>(a, c, grid_items, st)
+                   : go_stream_mb<true, false, false>(a, c, grid_items, st);
+  if (a.wfmt == W_UINT4_ZP)
+    return grouped ? go_stream_mb<false, true, true>(a, c, grid_items, st)
+                   : go_stream_mb<false, true, false>(a, c, grid_items, st);
+  return grouped ? go_stream_mb<false, false, true>(a, c, grid_items, st)
+                 : go_stream_mb<false, false, false>(a, c, grid_items, st);
 }
 
 hipError_t launch_splitk_reduce(const GemmArgs& a, int splits, hipStream_t st) {

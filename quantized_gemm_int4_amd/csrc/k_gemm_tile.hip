@@ -30,7 +30,8 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
   __shared__ int64_t arow_s[kTileM];
   __shared__ int64_t orow_s[kTileM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int wm = wave >> 1, wn = wave & 1;
   const int n_l = lane & 15, q_l = lane >> 4;
   const Geom G = a.G;
@@ -50,7 +51,7 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
       e = u[0];
       rcount = u[2];
       if (tid < kTileM) {
-        int64_t ar = -1, orr = -1;
+        int64_t ar = 0, orr = -1;   // invalid rows read row 0 (always present) and are not stored
         if (tid < rcount) {
           const int64_t pair = a.sorted_pairs[u[1] + tid];
           if (pair >= 0 && pair < a.P) {
@@ -66,66 +67,55 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
       const int64_t m0 = (int64_t)blockIdx.y * kTileM;
       rcount = (int)((a.M - m0) < kTileM ? (a.M - m0) : kTileM);
       if (tid < kTileM) {
-        arow_s[tid] = (tid < rcount) ? m0 + tid : -1;
-        orow_s[tid] = arow_s[tid];
+        const bool ok = tid < rcount;
+        arow_s[tid] = ok ? m0 + tid : m0;
+        orow_s[tid] = ok ? m0 + tid : -1;
       }
     }
     __syncthreads();
 
     const int64_t nbt = (int64_t)nt * 8;  // first 16-column block of this tile
 
-    // ---- register staging of one K step
+    // ---- register staging of one K step.  Loads are unconditional (column
+    // blocks clamped into range, invalid rows read a valid row) so that the
+    // compiler issues them back to back; scale and zero words stay raw until use.
+    const uint16_t* s16 = reinterpret_cast<const uint16_t*>(a.w + G.off_scales);
+    const uint32_t* s32 = reinterpret_cast<const uint32_t*>(a.w + G.off_scales);
+    const uint32_t* z32 = reinterpret_cast<const uint32_t*>(a.w + G.off_zeros);
+    const bool zp = (a.wfmt == W_UINT4_ZP);
     u32x4_t xr[XLD];
     u32x4_t wq[2];               // W4A16: two code slots per thread
-    float wsv[2], wzs[2];
+    uint32_t wsr[2], wzr[2];
     u32x4_t mq[4];               // W4A8: this wave's four fragments
-    int msc[4];
+    uint32_t msr[4];
 
     auto load_step = [&](int64_t g) {
 #pragma unroll
       for (int i = 0; i < XLD; ++i) {
         const int q = tid + 256 * i;
         const int row = q / XPR, pc = q % XPR;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (row < rcount && arow_s[row] >= 0)
-          v = ld16(xbase + arow_s[row] * xrow_bytes + g * (MX ? 128 : 256) + pc * 16);
-        xr[i] = v;
+        xr[i] = ld16(xbase + arow_s[row] * xrow_bytes + g * (MX ? 128 : 256) + pc * 16);
       }
       if (MX) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int64_t nb = nbt + wn * 4 + j;
-          mq[j] = (u32x4_t){0u, 0u, 0u, 0u};
-          msc[j] = 0;
-          if (nb < G.NB) {
-            const int64_t tile = (e * G.NB + nb) * G.KG + g;
-            mq[j] = ld16(a.w + tile * 1024 + lane * 16);
-            const uint32_t* scm = reinterpret_cast<const uint32_t*>(a.w + G.off_scales);
-            msc[j] = (int)((scm[((e * G.NB + nb) * G.KG4 + g / 4) * 64 + lane] >> (8 * (g % 4))) & 0xFF);
-          }
+          int64_t nb = nbt + wn * 4 + j;
+          if (nb >= G.NB) nb = G.NB - 1;
+          const int64_t tile = (e * G.NB + nb) * G.KG + g;
+          mq[j] = ld16(a.w + tile * 1024 + lane * 16);
+          msr[j] = s32[((e * G.NB + nb) * G.KG4 + g / 4) * 64 + lane];
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int q = tid + 256 * i;
-          const int64_t nb = nbt + (q >> 6);
+          int64_t nb = nbt + (q >> 6);
+          if (nb >= G.NB) nb = G.NB - 1;
           const int L = q & 63;
-          wq[i] = (u32x4_t){0u, 0u, 0u, 0u};
-          wsv[i] = 0.0f;
-          wzs[i] = 0.0f;
-          if (nb < G.NB) {
-            const int64_t tile = (e * G.NB + nb) * G.KG + g;
-            wq[i] = ld16(a.w + tile * 1024 + L * 16);
-            const uint16_t* s16 = reinterpret_cast<const uint16_t*>(a.w + G.off_scales);
-            const float sv = bf16_to_f32(s16[tile * 16 + (L & 15)]);
-            float z = 8.0f;
-            if (a.wfmt == W_UINT4_ZP) {
-              const uint64_t* zz = reinterpret_cast<const uint64_t*>(a.w + G.off_zeros);
-              z = (float)((zz[tile] >> (4 * (L & 15))) & 0xF);
-            }
-            wsv[i] = sv;
-            wzs[i] = -z * sv;
-          }
+          const int64_t tile = (e * G.NB + nb) * G.KG + g;
+          wq[i] = ld16(a.w + tile * 1024 + L * 16);
+          wsr[i] = s16[tile * 16 + (L & 15)];
+          wzr[i] = zp ? z32[tile * 2 + ((L & 15) >> 3)] : 0u;
         }
       }
     };
@@ -141,9 +131,12 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
         for (int i = 0; i < 2; ++i) {
           const int q = tid + 256 * i;
           const int nbl = q >> 6, L = q & 63;
+          const float sv = bf16_to_f32(wsr[i] & 0xFFFF);
+          const float z = zp ? (float)((wzr[i] >> (4 * (L & 7))) & 0xF) : 8.0f;
+          const float zs = -z * sv;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            st16(&ws_lds[((nbl * 4 + j) * 64 + L) * 16], dq8_u4(wq[i][j], wsv[i], wzs[i]));
+            st16(&ws_lds[((nbl * 4 + j) * 64 + L) * 16], dq8_u4(wq[i][j], sv, zs));
         }
       }
     };
@@ -162,7 +155,7 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
     for (int64_t g = 0; g < G.KG; ++g) {
       if (MX) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { cq[j] = mq[j]; csc[j] = msc[j]; }
+        for (int j = 0; j < 4; ++j) { cq[j] = mq[j]; csc[j] = (int)((msr[j] >> (8 * (g & 3))) & 0xFF); }
       }
       const bool more = (g + 1 < G.KG);
       if (more) load_step(g + 1);

@@ -8,6 +8,12 @@
 
 namespace hm {
 
+// Four nibbles held in the low nibbles of the four bytes of x -> 16 bits.
+__device__ __forceinline__ uint32_t compact_nibbles(uint32_t x) {
+  x = (x | (x >> 4)) & 0x00FF00FFu;
+  return (x | (x >> 8)) & 0x0000FFFFu;
+}
+
 // One thread per 16-byte code slot (e, nb, g, L).
 __global__ void __launch_bounds__(256)
 k_transform_codes(int wfmt, Geom G, const uint8_t* __restrict__ codes, uint8_t* __restrict__ out) {
@@ -29,7 +35,12 @@ k_transform_codes(int wfmt, Geom G, const uint8_t* __restrict__ codes, uint8_t* 
         v = ld16(row + 64 * g + 16 * h);
       } else {
         const uint8_t* p = row + 64 * g + 4 * h;
-        for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const uint32_t*>(p + 16 * j);
+        for (int j = 0; j < 4; ++j) {
+          // standard order (value i in nibble i) -> device order (value 2p in nibble p,
+          // value 2p+1 in nibble p+4): even values to the low half-word, odd to the high
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(p + 16 * j);
+          v[j] = compact_nibbles(w & 0x0F0F0F0Fu) | (compact_nibbles((w >> 4) & 0x0F0F0F0Fu) << 16);
+        }
         if (wfmt == W_INT4_SYM) v ^= 0x88888888u;  // two's complement -> offset binary
       }
     } else {
@@ -151,7 +162,10 @@ k_dequant(int wfmt, Geom G, const uint8_t* __restrict__ w, int64_t e, float* __r
         z = (uint32_t)((zz[tile] >> (4 * c)) & 0xF);
       }
       // (u - z) * s: exact, and the sign of a zero result follows the IEEE product rule
-      for (int q = 0; q < 8; ++q) r[q] = (float)((int)((word >> (4 * q)) & 0xF) - (int)z) * s;
+      for (int q = 0; q < 8; ++q) {
+        const int pos = (q & 1) ? 4 + (q >> 1) : (q >> 1);   // device nibble order
+        r[q] = (float)((int)((word >> (4 * pos)) & 0xF) - (int)z) * s;
+      }
     }
     float* o = out + n * G.K + k;
     st16(o, __builtin_bit_cast(u32x4_t, (f32x4_t){r[0], r[1], r[2], r[3]}));
