@@ -88,18 +88,32 @@ __device__ __forceinline__ u32x4_t dq8_u4(uint32_t w, float s, float zs) {
 // The same eight codes as bf16 values 1 + u/16, exact, in value order: each
 // code is OR-ed into the top four mantissa bits of bf16(1.0), so the constant
 // part of every value (1) is only 16 code steps, which keeps the cancellation
-// in a later subtraction of the zero-point product small.  Two instructions
-// per pair, no conversions.
-__device__ __forceinline__ u32x4_t raw8_u4(uint32_t w) {
+// in a later subtraction of the zero-point product small.  mask must hold
+// 0x00780078 and bias 0x3F803F80; passing them in registers (not literals)
+// lets each pair compile to a shift and one v_and_or_b32.
+__device__ __forceinline__ u32x4_t raw8_u4(uint32_t w, uint32_t mask, uint32_t bias) {
   u32x4_t r;
-  r[0] = ((w << 3) & 0x00780078u) | 0x3F803F80u;
+  r[0] = ((w << 3) & mask) | bias;
 #pragma unroll
-  for (int j = 1; j < 4; ++j) r[j] = ((w >> (4 * j - 3)) & 0x00780078u) | 0x3F803F80u;
+  for (int j = 1; j < 4; ++j) r[j] = ((w >> (4 * j - 3)) & mask) | bias;
   return r;
 }
 
-// bf16 bits of 1 + z/16 for a 4-bit zero point z, matching raw8_u4.
-__device__ __forceinline__ uint32_t raw_u4_bits(uint32_t z) { return 0x3F80u | (z << 3); }
+// bf16 pair of -(1 + z/16) for a 4-bit zero point z: the A operand that
+// subtracts the zero-point product inside the same MFMA accumulation.
+__device__ __forceinline__ uint32_t neg_raw_u4_pair(uint32_t z) {
+  return (z * 0x00080008u) | 0xBF80BF80u;
+}
+
+// Opaque copies of constants, so the compiler keeps them in registers.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  __asm__ volatile("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t in_sgpr(uint32_t v) {
+  __asm__ volatile("" : "+s"(v));
+  return v;
+}
 
 // 16x16x32 bf16 MFMA: C[i][j] += sum_k A[i][k] B[k][j]; lane L supplies A row
 // L%16 and B column L%16 for K-quarter L/16 (8 values each); C: lane L holds

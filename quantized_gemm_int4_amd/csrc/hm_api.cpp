@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/hm.h"
 #include "common.h"
 #include "launch.h"
@@ -16,6 +18,7 @@ namespace {
 using namespace hm;
 
 constexpr int kStreamMaxRows = 32;   // dense rows handled by the streaming kernel (two 16-row blocks)
+constexpr int64_t kStreamLdsBytes = 159 * 1024;  // dynamic LDS one streaming block may use
 constexpr int kMoeStreamRows = 16;   // expert segments of at most this many rows use the streaming kernel
 constexpr int kGroupedGridStream = 2048;
 constexpr int kGroupedGridTile = 1024;
@@ -64,13 +67,44 @@ DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
   if (force == 1 && m > kStreamMaxRows) p.stream = false;  // streaming handles <= 32 rows per block
   if (!p.stream) return p;
   p.sc.mb = (m <= 16) ? 1 : 2;
-  p.sc.nbw = env_int("HM_STREAM_NBW", 1);
-  if (p.sc.nbw != 1 && p.sc.nbw != 2 && p.sc.nbw != 4) p.sc.nbw = 1;
-  const int64_t n_tiles = (G.NB + 4 * p.sc.nbw - 1) / (4 * p.sc.nbw);
+  const int64_t rows = (m < 16 * p.sc.mb) ? m : 16 * p.sc.mb;
   const int64_t m_chunks = (m + 16 * p.sc.mb - 1) / (16 * p.sc.mb);
+  const int64_t gb = (d->wfmt == HM_W_MXFP4) ? 128 : 256;   // activation bytes per row per group
+  // Launch shape: (ks, nbw) from the narrowest block (most waves, least work
+  // per wave) to the widest, take the first whose blocks all fit on the chip
+  // at once.  A block keeps its activation rows in LDS, so the LDS footprint
+  // decides how many blocks share a compute unit (at most 5: the register
+  // budget allows 5 waves per SIMD).
+  int ks = env_int("HM_STREAM_KS", 0), nbw = env_int("HM_STREAM_NBW", 0);
+  static const int kShapes[6][2] = {{4, 1}, {2, 1}, {4, 2}, {2, 2}, {1, 1}, {1, 2}};
+  if (ks != 1 && ks != 2 && ks != 4) ks = 0;
+  if (nbw != 1 && nbw != 2) nbw = 0;
+  if (!ks || !nbw) {
+    const int64_t row_bytes = std::min<int64_t>(G.KG * gb + 16, kStreamLdsBytes / rows);
+    int pick = 5;
+    for (int i = 0; i < 6; ++i) {
+      const int cks = kShapes[i][0], cnbw = kShapes[i][1];
+      if ((ks && cks != ks) || (nbw && cnbw != nbw)) continue;
+      if (G.KG < 2 * cks && cks > 1) continue;                  // >= 2 groups per wave
+      StreamCfg t = p.sc;
+      t.ks = cks;
+      t.nbw = cnbw;
+      const int64_t lds = rows * row_bytes + (cks > 1 ? 4 * cnbw * p.sc.mb * 1024 : 0);
+      const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(5, kStreamLdsBytes / lds));
+      const int64_t blocks = stream_n_tiles(G, t) * m_chunks;
+      pick = i;
+      if (blocks <= 256 * per_cu) break;
+    }
+    ks = kShapes[pick][0];
+    nbw = kShapes[pick][1];
+  }
+  p.sc.ks = ks;
+  p.sc.nbw = nbw;
+  const int64_t n_tiles = stream_n_tiles(G, p.sc);
   int64_t splits = env_int("HM_STREAM_SPLITS", 0);
   if (splits <= 0) {
-    // enough waves to keep every SIMD streaming (1024 SIMDs); split K only below that
+    // enough waves to keep every SIMD streaming (1024 SIMDs); split K over
+    // blocks only below that
     const int64_t target_waves = 800;
     const int64_t waves = n_tiles * 4 * m_chunks;
     splits = (target_waves + waves - 1) / waves;
@@ -87,7 +121,7 @@ DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
 struct MoePlan {
   int64_t P, max_s, max_t;
   size_t off_su, off_tu, ws_bytes;
-  int nbw;
+  int nbw, ks, lds_kb;
 };
 
 MoePlan plan_moe(const hm_wdesc* d, int64_t t, int32_t topk) {
@@ -100,6 +134,13 @@ MoePlan plan_moe(const hm_wdesc* d, int64_t t, int32_t topk) {
   p.off_tu = align256(p.off_su + (size_t)p.max_s * 16);
   p.ws_bytes = align256(p.off_tu + (size_t)p.max_t * 16);
   p.nbw = 1;
+  p.ks = env_int("HM_MOE_STREAM_KS", 1);
+  if (p.ks != 1 && p.ks != 2 && p.ks != 4) p.ks = 1;
+  // LDS per streaming block: a unit stages up to 16 rows, so K is walked in
+  // pieces that fit this budget; a smaller budget lets more blocks share a
+  // compute unit
+  p.lds_kb = env_int("HM_MOE_STREAM_LDS_KB", 79);
+  if (p.lds_kb < 20 || p.lds_kb > 159) p.lds_kb = 79;
   return p;
 }
 
@@ -189,8 +230,8 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* 
   const DensePlan p = plan_dense(d, m);
   const char* w = d->wfmt == HM_W_MXFP4 ? "w4a8-mxfp4" : (d->wfmt == HM_W_UINT4_ZP ? "w4a16-uint4zp" : "w4a16-int4sym");
   if (p.stream)
-    snprintf(buf, buf_len, "%s stream mb=%d nbw=%d splits=%d ksg=%d mfma=%s", w, p.sc.mb, p.sc.nbw,
-             p.sc.splits, p.ksg, d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
+    snprintf(buf, buf_len, "%s stream mb=%d nbw=%d ks=%d splits=%d ksg=%d mfma=%s", w, p.sc.mb,
+             p.sc.nbw, p.sc.ks, p.sc.splits, p.ksg, d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
   else
     snprintf(buf, buf_len, "%s tile %dx%d waves=2x2 mfma=%s", w, kTileM, kTileN,
              d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
@@ -315,8 +356,8 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, kMoeStreamRows, kTileM, p.max_s,
                                      p.max_t, hdr, su, tu, stream);
   if (e == hipSuccess) {
-    StreamCfg sc{kMoeStreamRows / 16, p.nbw, 1};
-    const int64_t nts = (a.G.NB + 4 * sc.nbw - 1) / (4 * sc.nbw);
+    StreamCfg sc{kMoeStreamRows / 16, p.nbw, 1, p.ks, p.lds_kb};
+    const int64_t nts = stream_n_tiles(a.G, sc);
     int64_t gi = p.max_s * nts;
     if (gi > kGroupedGridStream) gi = kGroupedGridStream;
     a.units = su;

@@ -5,18 +5,23 @@
 // registers: one 16-byte load per lane fetches one 1 KiB tile (16 columns x
 // 128 K) of the device layout, which is exactly the operand of four
 // 16x16x32 bf16 MFMAs (or of one 16x16x128 scaled fp4 x fp8 MFMA for MXFP4).
-// The few activation rows are staged in LDS per chunk of 256 K and shared by
-// the block's four waves.  The weights are the MFMA "A" operand (rows = output
-// columns n) and the activations the "B" operand, so each lane ends with four
-// consecutive n of one row and stores them as one 8-byte write.
-// Dense calls split K over blocks and reduce fp32 partials in a second kernel.
+// The few activation rows are copied into LDS with direct global-to-LDS loads
+// (issued before the weight loads, so both latencies overlap) and shared by
+// the block's four waves.  The weights are the MFMA "A" operand (rows =
+// output columns n) and the activations the "B" operand, so each lane ends
+// with four consecutive n of one row and stores them as one 8-byte write.
+//
+// Work split: a block has four waves; KS of them share one set of NBW
+// 16-column blocks and split its K range, adding their sums through LDS at
+// the end; 4/KS such sets make one block.  Dense calls may also split K over
+// blocks and reduce fp32 partials in a second kernel.
 #include "common.h"
 #include "launch.h"
 
 namespace hm {
 
-// activation bytes staged per block: 159 KiB of dynamic LDS, leaving room for the
-// row tables within the 160 KiB of a gfx950 compute unit
+// dynamic LDS per block: 159 KiB, leaving room for the row tables within the
+// 160 KiB of a gfx950 compute unit
 constexpr int64_t kStreamLdsBudget = 159 * 1024;
 
 // LDS-only barrier: waits for this wave's LDS operations, then meets the other
@@ -27,31 +32,50 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 16-byte direct global-to-LDS load per lane: lane L's bytes land at
+// lds_base + 16 * L (lds_base wave-uniform, 16-byte aligned).
+__device__ __forceinline__ void g2lds16(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+template <int KS, int NBW, int MB>
+struct StreamShape {
+  static constexpr int kRedBytes = KS > 1 ? 4 * NBW * MB * 1024 : 0;  // K-split sums
+};
+
 // Template parameters: MX (W4A8-MXFP4 vs W4A16), ZP (zero points), MB (16-row
-// blocks per unit), NBW (16-column blocks per wave), DW (weight prefetch ring:
-// K groups of 128 held in registers ahead of use), GROUPED.
-// Runtime: pg = K groups per activation piece staged in LDS (a multiple of DW);
-// dynamic LDS = staged rows x (pg * bytes per group + 16).
-template <bool MX, bool ZP, int MB, int NBW, int DW, bool GROUPED>
+// blocks per unit), NBW (16-column blocks per wave), KS (waves splitting one
+// column set's K range), DW (weight prefetch ring: K groups of 128 held in
+// registers ahead of use), GROUPED.
+// Runtime: pg = K groups per activation piece staged in LDS, xb = LDS row
+// stride in bytes (a multiple of 1 KiB plus 16).
+template <bool MX, bool ZP, int MB, int NBW, int KS, int DW, bool GROUPED>
 __global__ void __launch_bounds__(256)
-k_gemm_stream(GemmArgs a, int n_tiles, int pg) {
+k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
   constexpr int ROWS = MB * 16;
   constexpr int GB = MX ? 128 : 256;                    // activation bytes per row per K group
-  extern __shared__ __attribute__((aligned(16))) uint8_t xs_lds[];
+  constexpr int CS = 4 / KS;                            // column sets per block
+  constexpr int RED = StreamShape<KS, NBW, MB>::kRedBytes;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  uint8_t* const xs_lds = lds + RED;                    // activations: [rows][xb]
   __shared__ int64_t arow_s[ROWS];
   __shared__ int64_t orow_s[ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int cset = wave / KS, kq = wave % KS;
   const Geom G = a.G;
   const int64_t K = G.K;
   const int n_l = lane & 15, q_l = lane >> 4;
   const uint8_t* xbase = reinterpret_cast<const uint8_t*>(a.x);
   const int64_t xrow_bytes = MX ? K : 2 * K;
-  const uint16_t* s16 = reinterpret_cast<const uint16_t*>(a.w + G.off_scales);
-  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(a.w + G.off_scales);
-  const uint32_t* z32 = reinterpret_cast<const uint32_t*>(a.w + G.off_zeros);
-  const int XB = pg * GB + 16;                          // LDS row stride (bytes), padded
+  const uint8_t* sbase = a.w + G.off_scales;
+  const uint8_t* zbase = a.w + G.off_zeros;
+  // register-held constants of the raw-code conversion (see raw8_u4)
+  const uint32_t cmask = in_vgpr(0x00780078u), cbias = in_sgpr(0x3F803F80u);
+  const uint32_t zshift = 4u * (uint32_t)(n_l & 7);
 
   const int64_t n_items = GROUPED ? (int64_t)a.hdr[0] * n_tiles : 1;
   for (int64_t item = GROUPED ? blockIdx.x : 0; item < n_items;
@@ -94,58 +118,67 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg) {
     }
     __syncthreads();
 
-    const int64_t nb0 = ((int64_t)nt * 4 + wave) * NBW;
+    const int64_t nb0 = ((int64_t)nt * CS + cset) * NBW;
     const int ng = (int)(g_end - g_begin);
-    int64_t nbc[NBW];  // clamped column blocks: loads stay in bounds, results of
-                       // blocks >= NB are never stored
+    // clamped column blocks (scalar): loads stay in bounds, results of blocks
+    // >= NB are never stored
+    int64_t wtile0[NBW], stile0[NBW];
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) nbc[j] = (nb0 + j < G.NB) ? nb0 + j : G.NB - 1;
+    for (int j = 0; j < NBW; ++j) {
+      const int64_t nbc = (nb0 + j < G.NB) ? nb0 + j : G.NB - 1;
+      wtile0[j] = (e * G.NB + nbc) * G.KG;            // tile index of group 0
+      stile0[j] = (e * G.NB + nbc) * G.KG4;           // MXFP4 scale word row
+    }
     // LDS row of each MFMA row block: rows past the staged ones reuse the last
     // staged row (their outputs are never stored)
     int lrow[MB];
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) lrow[rb] = (rb * 16 + n_l < rcount) ? rb * 16 + n_l : rcount - 1;
 
-    // stage activation rows [0, rcount) x groups [gp, gp + plen) into LDS
+    // Byte offset of activation row r (r < ROWS) held by lane r: the copy loop
+    // below takes it with readlane, because an LDS read there would have to
+    // wait for the copies already in flight (they write LDS too).
+    const int64_t xrow_off = arow_s[lane & (ROWS - 1)] * xrow_bytes;
+    const uint32_t xro_lo = (uint32_t)xrow_off, xro_hi = (uint32_t)((uint64_t)xrow_off >> 32);
+
+    // Copy activation rows [0, rcount) x groups [gp, gp + plen) into LDS: one
+    // wave instruction moves 1 KiB of one row; lanes past the row's end re-read
+    // its first chunk and land in the row's padding.
     auto stage_x = [&](int gp, int plen) {
-      const int per_row = plen * (GB / 16);
-      const int total = rcount * per_row;
+      const int per_row = plen * (GB / 16);             // 16-byte chunks per row
+      const int cpr = (per_row + 63) / 64;              // 1 KiB pieces per row
+      const int total = rcount * cpr;
       const int64_t off0 = (g_begin + gp) * GB;
 #pragma nounroll
-      for (int base = 0; base < total; base += 256 * 4) {
-        u32x4_t v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = base + u * 256 + tid;
-          if (i < total)
-            v[u] = ld16(xbase + arow_s[i / per_row] * xrow_bytes + off0 + (i % per_row) * 16);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = base + u * 256 + tid;
-          if (i < total) st16(xs_lds + (i / per_row) * XB + (i % per_row) * 16, v[u]);
-        }
+      for (int i = wave; i < total; i += 4) {
+        const int r = i / cpr, blk = i - (i / cpr) * cpr;
+        const int c = blk * 64 + lane;
+        const int cc = c < per_row ? c : 0;
+        const uint64_t ro = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xro_hi, r) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)xro_lo, r);
+        g2lds16(xbase + ro + off0 + (int64_t)cc * 16, xs_lds + r * xb + blk * 1024);
       }
     };
 
     // ---- weight ring: DW groups ahead, raw scale / zero words kept until use
     u32x4_t wq[DW][NBW];
-    // INT4: wsr / wsh hold the bf16 scales of the four output rows 4*q_l + 0..3
-    // that this lane accumulates (the MFMA result is scaled, not the operand).
-    uint32_t wsr[DW][NBW], wsh[MX ? 1 : DW][MX ? 1 : NBW], wzr[DW][NBW];
-    auto load_w = [&](int d, int gl) {                  // gl: group index within [0, ng)
-      const int64_t g = g_begin + gl;
+    uint32_t wsr[DW][NBW], wsh[MX ? 1 : DW][MX ? 1 : NBW], wzr[ZP ? DW : 1][ZP ? NBW : 1];
+    auto load_w = [&](int d, int64_t g) {               // g: group index in [0, KG)
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        const int64_t tile = (e * G.NB + nbc[j]) * G.KG + g;
+        const int64_t tile = wtile0[j] + g;
         wq[d][j] = ld16(a.w + tile * 1024 + lane * 16);
         if (MX) {
-          wsr[d][j] = s32[((e * G.NB + nbc[j]) * G.KG4 + g / 4) * 64 + lane];
+          // four groups' E8M0 scales per lane word: [e][nb][g/4][64 lanes]
+          wsr[d][j] = *reinterpret_cast<const uint32_t*>(sbase + ((stile0[j] + g / 4) * 64 + lane) * 4);
         } else {
-          const u32x2_t sp = *reinterpret_cast<const u32x2_t*>(s16 + tile * 16 + 4 * q_l);
+          // bf16 scales of the four output rows 4*q_l + 0..3 this lane accumulates
+          const u32x2_t sp = *reinterpret_cast<const u32x2_t*>(sbase + tile * 32 + q_l * 8);
           wsr[d][j] = sp[0];
-          wsh[d][j] = sp[1];
-          if (ZP) wzr[d][j] = z32[tile * 2 + (n_l >> 3)];
+          wsh[MX ? 0 : d][MX ? 0 : j] = sp[1];
+          if (ZP)
+            wzr[ZP ? d : 0][ZP ? j : 0] =
+                *reinterpret_cast<const uint32_t*>(zbase + tile * 8 + (n_l >> 3) * 4);
         }
       }
     };
@@ -156,9 +189,9 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg) {
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb) acc[j][rb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    // K is walked in pieces of pg groups whose activations fit in LDS.  Each
-    // piece restarts its weight ring (one memory latency per piece; a single
-    // piece covers the whole K range whenever the rows fit), which keeps the
+    // K is walked in pieces of pg groups whose activations fit in LDS (a single
+    // piece whenever the rows fit).  Inside a piece, wave kq takes the kq-th of
+    // KS equal slices.  Each piece restarts the weight ring, which keeps the
     // ring's load order identical on every entry to the round loop so that
     // each slot waits only for its own loads.
     const int n_pieces = (ng + pg - 1) / pg;
@@ -166,24 +199,31 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg) {
     for (int p = 0; p < n_pieces; ++p) {
       const int gp = p * pg;
       const int plen = (ng - gp) < pg ? (ng - gp) : pg;
+      const int sub = (plen + KS - 1) / KS;
+      const int lo = kq * sub;                              // this wave's slice [lo, lo + sl)
+      const int sl = (plen - lo) < sub ? (plen - lo) : sub; // may be <= 0
+      const int64_t gw = g_begin + gp + lo;                 // first group of the slice
+      const int last = sl > 0 ? sl - 1 : 0;
+      const int64_t gsafe = sl > 0 ? gw : g_begin + gp;     // loads of empty slices stay in range
       if (p > 0) lds_barrier();               // everyone is done with the previous piece
       stage_x(gp, plen);
 #pragma unroll
-      for (int d = 0; d < DW; ++d) load_w(d, gp + (d < plen ? d : plen - 1));
-      lds_barrier();
-      const int rounds = (plen + DW - 1) / DW;
+      for (int d = 0; d < DW; ++d) load_w(d, gsafe + (d < last ? d : last));
+      __syncthreads();                        // activations (and the ring's first loads) landed
+      const int rounds = sl > 0 ? (sl + DW - 1) / DW : 0;
 #pragma nounroll
       for (int r = 0; r < rounds; ++r) {
 #pragma unroll
         for (int d = 0; d < DW; ++d) {
-          const int lg = r * DW + d;          // group within the piece
-          if (lg < plen) {
-            const int64_t g = g_begin + gp + lg;
+          const int lg = r * DW + d;          // group within the slice
+          if (lg < sl) {
+            const int64_t g = gw + lg;
+            const uint8_t* xg = xs_lds + (lo + lg) * GB;
             if (MX) {
               u32x4_t a0[MB], a1[MB];
 #pragma unroll
               for (int rb = 0; rb < MB; ++rb) {
-                const uint8_t* xp = xs_lds + lrow[rb] * XB + lg * 128 + 16 * q_l;
+                const uint8_t* xp = xg + lrow[rb] * xb + 16 * q_l;
                 a0[rb] = ld16(xp);
                 a1[rb] = ld16(xp + 64);
               }
@@ -195,90 +235,105 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg) {
                   acc[j][rb] = mfma_fp4_fp8(wq[d][j], a0[rb], a1[rb], acc[j][rb], sc, 127);
               }
             } else {
-              // Raw codes: the MFMA sees bf16(1 + u/16) (exact), a second MFMA sees
-              // bf16(1 + z/16); their difference is sum_k x_k (u_k - z)/16 for this
-              // group, exactly 0 where every code equals the zero point, and 16
-              // times the group scale is applied once to the difference.
-              f32x4_t raw[NBW][MB], zc[ZP ? NBW : 1][MB];
+              // Raw codes: one MFMA chain adds x * (1 + u/16) and x * -(1 + z/16)
+              // per K step, i.e. x * (u - z) / 16, exactly 0 where every code
+              // equals the zero point; the group scale of each output row is
+              // applied once to the chain's result, the factor 16 at the end.
               u32x4_t bz[ZP ? NBW : 1];
 #pragma unroll
               for (int j = 0; j < (ZP ? NBW : 1); ++j) {
-                const uint32_t z = ZP ? ((wzr[d][j] >> (4 * (n_l & 7))) & 0xF) : 8u;
-                const uint32_t pz = raw_u4_bits(z) * 0x00010001u;
+                const uint32_t z = ZP ? ((wzr[ZP ? d : 0][ZP ? j : 0] >> zshift) & 0xFu) : 8u;
+                const uint32_t pz = neg_raw_u4_pair(z);
                 bz[j] = (u32x4_t){pz, pz, pz, pz};
-#pragma unroll
-                for (int rb = 0; rb < MB; ++rb) zc[j][rb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
               }
-#pragma unroll
-              for (int j = 0; j < NBW; ++j)
-#pragma unroll
-                for (int rb = 0; rb < MB; ++rb) raw[j][rb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+              f32x4_t t[NBW][MB];
 #pragma unroll
               for (int kk = 0; kk < 4; ++kk) {
                 u32x4_t af[MB];
 #pragma unroll
-                for (int rb = 0; rb < MB; ++rb)
-                  af[rb] = ld16(xs_lds + lrow[rb] * XB + (lg * 128 + 32 * kk + 8 * q_l) * 2);
+                for (int rb = 0; rb < MB; ++rb) af[rb] = ld16(xg + lrow[rb] * xb + (32 * kk + 8 * q_l) * 2);
 #pragma unroll
                 for (int j = 0; j < NBW; ++j) {
-                  const u32x4_t bw = raw8_u4(wq[d][j][kk]);
+                  const u32x4_t bw = raw8_u4(wq[d][j][kk], cmask, cbias);
 #pragma unroll
-                  for (int rb = 0; rb < MB; ++rb) raw[j][rb] = mfma_bf16(bw, af[rb], raw[j][rb]);
+                  for (int rb = 0; rb < MB; ++rb) {
+                    t[j][rb] = mfma_bf16(bw, af[rb], kk == 0 ? (f32x4_t){0.f, 0.f, 0.f, 0.f} : t[j][rb]);
+                    t[j][rb] = mfma_bf16(bz[ZP ? j : 0], af[rb], t[j][rb]);
+                  }
                 }
-#pragma unroll
-                for (int j = 0; j < (ZP ? NBW : 1); ++j)
-#pragma unroll
-                  for (int rb = 0; rb < MB; ++rb) zc[j][rb] = mfma_bf16(bz[j], af[rb], zc[j][rb]);
               }
 #pragma unroll
               for (int j = 0; j < NBW; ++j) {
-                const float s0 = bf16_to_f32(wsr[d][j] & 0xFFFFu), s1 = __uint_as_float(wsr[d][j] & 0xFFFF0000u);
-                const float s2 = bf16_to_f32(wsh[d][j] & 0xFFFFu), s3 = __uint_as_float(wsh[d][j] & 0xFFFF0000u);
+                const uint32_t lo2 = wsr[d][j], hi2 = wsh[MX ? 0 : d][MX ? 0 : j];
+                const float s0 = bf16_to_f32(lo2 & 0xFFFFu), s1 = __uint_as_float(lo2 & 0xFFFF0000u);
+                const float s2 = bf16_to_f32(hi2 & 0xFFFFu), s3 = __uint_as_float(hi2 & 0xFFFF0000u);
 #pragma unroll
                 for (int rb = 0; rb < MB; ++rb) {
-                  const f32x4_t dl = (raw[j][rb] - zc[ZP ? j : 0][rb]) * 16.f;   // exact scaling
-                  acc[j][rb][0] = fmaf(s0, dl[0], acc[j][rb][0]);
-                  acc[j][rb][1] = fmaf(s1, dl[1], acc[j][rb][1]);
-                  acc[j][rb][2] = fmaf(s2, dl[2], acc[j][rb][2]);
-                  acc[j][rb][3] = fmaf(s3, dl[3], acc[j][rb][3]);
+                  acc[j][rb][0] = fmaf(s0, t[j][rb][0], acc[j][rb][0]);
+                  acc[j][rb][1] = fmaf(s1, t[j][rb][1], acc[j][rb][1]);
+                  acc[j][rb][2] = fmaf(s2, t[j][rb][2], acc[j][rb][2]);
+                  acc[j][rb][3] = fmaf(s3, t[j][rb][3], acc[j][rb][3]);
                 }
               }
             }
           }
-          load_w(d, gp + (lg + DW < plen ? lg + DW : plen - 1));
+          load_w(d, gsafe + (lg + DW < last ? lg + DW : last));
         }
       }
     }
 
+    // ---- K-split sum: waves kq > 0 park their sums in LDS, wave kq == 0 adds them
+    if (KS > 1) {
+      f32x4_t* red = reinterpret_cast<f32x4_t*>(lds);
+      if (kq > 0) {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+          for (int rb = 0; rb < MB; ++rb) red[((wave * NBW + j) * MB + rb) * 64 + lane] = acc[j][rb];
+      }
+      lds_barrier();
+      if (kq == 0) {
+#pragma unroll
+        for (int k2 = 1; k2 < KS; ++k2)
+#pragma unroll
+          for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) acc[j][rb] += red[(((wave + k2) * NBW + j) * MB + rb) * 64 + lane];
+      }
+    }
+
     // ---- epilogue: lane holds C[n = 16nb + 4*q_l + r][row = 16rb + n_l]
-    const bool partial = (!GROUPED) && (a.part != nullptr);
-    const int64_t Np = G.NB * 16;
+    if (kq == 0) {
+      const bool partial = (!GROUPED) && (a.part != nullptr);
+      const int64_t Np = G.NB * 16;
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      const int64_t nb = nb0 + j;
-      if (nb >= G.NB) continue;
-      const int64_t n = nb * 16 + 4 * q_l;
+      for (int j = 0; j < NBW; ++j) {
+        const int64_t nb = nb0 + j;
+        if (nb >= G.NB) continue;
+        const int64_t n = nb * 16 + 4 * q_l;
 #pragma unroll
-      for (int rb = 0; rb < MB; ++rb) {
-        const int rl = rb * 16 + n_l;
-        if (rl >= rcount || orow_s[rl] < 0) continue;
-        f32x4_t v = acc[j][rb];
-        if (partial) {
-          float* dst = a.part + ((int64_t)split * a.M + m0 + rl) * Np + n;
-          st16(dst, __builtin_bit_cast(u32x4_t, v));
-          continue;
-        }
-        if (MX) {
-          const float rs = a.xs[arow_s[rl]];
-          v = v * rs;
-        }
-        uint16_t* dst = a.y + orow_s[rl] * G.N + n;
-        if ((G.N & 3) == 0 && n + 3 < G.N) {
-          *reinterpret_cast<u32x2_t*>(dst) = (u32x2_t){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-        } else {
+        for (int rb = 0; rb < MB; ++rb) {
+          const int rl = rb * 16 + n_l;
+          if (rl >= rcount || orow_s[rl] < 0) continue;
+          f32x4_t v = acc[j][rb];
+          if (!MX) v = v * 16.f;                // raw-code sums carry a factor 1/16 (exact)
+          if (partial) {
+            float* dst = a.part + ((int64_t)split * a.M + m0 + rl) * Np + n;
+            st16(dst, __builtin_bit_cast(u32x4_t, v));
+            continue;
+          }
+          if (MX) {
+            const float rs = a.xs[arow_s[rl]];
+            v = v * rs;
+          }
+          uint16_t* dst = a.y + orow_s[rl] * G.N + n;
+          if ((G.N & 3) == 0 && n + 3 < G.N) {
+            *reinterpret_cast<u32x2_t*>(dst) = (u32x2_t){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+          } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < G.N) dst[r] = (uint16_t)(pack_bf16(v[r], 0.0f) & 0xFFFF);
+            for (int r = 0; r < 4; ++r)
+              if (n + r < G.N) dst[r] = (uint16_t)(pack_bf16(v[r], 0.0f) & 0xFFFF);
+          }
         }
       }
     }
@@ -311,27 +366,48 @@ k_splitk_reduce(GemmArgs a, int splits) {
   }
 }
 
-template <bool MX, bool ZP, int MB, int NBW, bool GROUPED>
-static hipError_t go_stream(const GemmArgs& a, const StreamCfg& c, int grid_items, hipStream_t st) {
-  // ring depth: up to 16 groups per 16-column block, within the 63 outstanding
-  // vector-memory operations one wave can track (three loads per group)
-  constexpr int DW = (NBW == 1) ? (MB == 1 ? 16 : 8) : (NBW == 2 ? 8 : 4);
-  const int n_tiles = (int)((a.G.NB + 4 * NBW - 1) / (4 * NBW));
-  const int gb = (a.wfmt == W_MXFP4) ? 128 : 256;
-  // activation piece: as many K groups as fit the LDS budget, a multiple of DW
-  const int64_t rows = GROUPED ? 16 * MB : (a.M < 16 * MB ? a.M : 16 * MB);
-  const int64_t ksl = GROUPED ? a.G.KG : a.ksg;
-  int64_t pg = (kStreamLdsBudget / rows - 16) / gb;
-  pg = pg / DW * DW;
-  if (pg < DW) pg = DW;
-  const int64_t need = (ksl + DW - 1) / DW * DW;
+int64_t stream_n_tiles(const Geom& G, const StreamCfg& c) {
+  const int64_t cols = (int64_t)(4 / c.ks) * c.nbw;   // 16-column blocks per block
+  return (G.NB + cols - 1) / cols;
+}
+
+// LDS plan of one launch: K groups per activation piece and the row stride.
+static void stream_lds_plan(const GemmArgs& a, const StreamCfg& c, bool grouped, int red_bytes,
+                            int* pg_out, int* xb_out, size_t* bytes_out) {
+  const int64_t gb = (a.wfmt == W_MXFP4) ? 128 : 256;
+  const int64_t rows = grouped ? 16 * c.mb : (a.M < 16 * c.mb ? a.M : 16 * c.mb);
+  const int64_t ksl = grouped ? a.G.KG : a.ksg;         // groups one block walks
+  const int64_t gq = 1024 / gb;                         // groups per 1 KiB of a row
+  // largest piece (a multiple of gq groups) whose rows fit the budget
+  const int64_t budget = (c.lds_kb > 0 && c.lds_kb * 1024 < kStreamLdsBudget) ? c.lds_kb * 1024 : kStreamLdsBudget;
+  const int64_t avail = budget - red_bytes;
+  int64_t pg = ((avail / rows - 16) / 1024) * gq;
+  if (pg < gq) pg = gq;
+  const int64_t need = (ksl + gq - 1) / gq * gq;
   if (pg > need) pg = need;
-  const size_t lds = (size_t)rows * (pg * gb + 16);
+  const int64_t xb = (pg * gb + 1023) / 1024 * 1024 + 16;
+  *pg_out = (int)pg;
+  *xb_out = (int)xb;
+  *bytes_out = (size_t)(red_bytes + rows * xb);
+}
+
+template <bool MX, bool ZP, int MB, int NBW, int KS, bool GROUPED>
+static hipError_t go_stream(const GemmArgs& a, const StreamCfg& c, int grid_items, hipStream_t st) {
+  // ring depth in K groups, within the 63 outstanding vector-memory operations
+  // one wave can track (up to three loads per group and column block) and a
+  // register budget that leaves room for four waves per SIMD at small M
+  constexpr int DW = (NBW == 1 && MB == 1 && KS < 4) ? 16 : 8;
+  constexpr int RED = StreamShape<KS, NBW, MB>::kRedBytes;
+  auto kern = &k_gemm_stream<MX, ZP, MB, NBW, KS, DW, GROUPED>;
+  int pg, xb;
+  size_t lds;
+  stream_lds_plan(a, c, GROUPED, RED, &pg, &xb, &lds);
   // allow more than the default dynamic LDS (set once per instance; thread-safe static init)
   static const hipError_t attr_err = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm_stream<MX, ZP, MB, NBW, DW, GROUPED>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsBudget);
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)kStreamLdsBudget);
   if (attr_err != hipSuccess) return attr_err;
+  const int64_t n_tiles = stream_n_tiles(a.G, c);
   dim3 grid;
   if (GROUPED) {
     grid = dim3((unsigned)(grid_items > 0 ? grid_items : 1));
@@ -339,18 +415,23 @@ static hipError_t go_stream(const GemmArgs& a, const StreamCfg& c, int grid_item
     const int64_t m_chunks = (a.M + MB * 16 - 1) / (MB * 16);
     grid = dim3((unsigned)n_tiles, (unsigned)c.splits, (unsigned)m_chunks);
   }
-  hipLaunchKernelGGL((k_gemm_stream<MX, ZP, MB, NBW, DW, GROUPED>), grid, dim3(256), lds, st, a,
-                     n_tiles, (int)pg);
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, a, (int)n_tiles, pg, xb);
   return hipGetLastError();
+}
+
+template <bool MX, bool ZP, int MB, int NBW, bool GROUPED>
+static hipError_t go_stream_ks(const GemmArgs& a, const StreamCfg& c, int gi, hipStream_t st) {
+  switch (c.ks) {
+    case 4: return go_stream<MX, ZP, MB, NBW, 4, GROUPED>(a, c, gi, st);
+    case 2: return go_stream<MX, ZP, MB, NBW, 2, GROUPED>(a, c, gi, st);
+    default: return go_stream<MX, ZP, MB, NBW, 1, GROUPED>(a, c, gi, st);
+  }
 }
 
 template <bool MX, bool ZP, int MB, bool GROUPED>
 static hipError_t go_stream_nbw(const GemmArgs& a, const StreamCfg& c, int gi, hipStream_t st) {
-  switch (c.nbw) {
-    case 1: return go_stream<MX, ZP, MB, 1, GROUPED>(a, c, gi, st);
-    case 2: return go_stream<MX, ZP, MB, 2, GROUPED>(a, c, gi, st);
-    default: return go_stream<MX, ZP, MB, 4, GROUPED>(a, c, gi, st);
-  }
+  return (c.nbw == 2) ? go_stream_ks<MX, ZP, MB, 2, GROUPED>(a, c, gi, st)
+                      : go_stream_ks<MX, ZP, MB, 1, GROUPED>(a, c, gi, st);
 }
 
 template <bool MX, bool ZP, bool GROUPED>

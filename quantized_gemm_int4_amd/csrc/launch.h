@@ -42,9 +42,13 @@ hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_m
 // Grouped: persistent over (streaming unit x n tile) items.
 struct StreamCfg {
   int mb;      // 16-row blocks per unit: 1 or 2
-  int nbw;     // 16-column blocks per wave
-  int splits;  // dense split-K factor
+  int nbw;     // 16-column blocks per wave: 1 or 2
+  int splits;  // dense split-K factor (over blocks, fp32 partials)
+  int ks;      // waves of a block splitting one column set's K range: 1, 2 or 4
+  int lds_kb;  // dynamic LDS budget per block in KiB (0: the 159 KiB maximum)
 };
+// blocks along N (dense) or n tiles per unit (grouped) of a streaming launch
+int64_t stream_n_tiles(const Geom& G, const StreamCfg& c);
 hipError_t launch_gemm_stream(const GemmArgs& a, const StreamCfg& c, bool grouped, int grid_items,
                               hipStream_t st);
 hipError_t launch_splitk_reduce(const GemmArgs& a, int splits, hipStream_t st);

@@ -193,3 +193,43 @@ def test_m_zero_is_noop(config2):
     x = torch.empty(0, 4096, dtype=torch.bfloat16, device="cuda")
     y = hm.hm_gemm(config2.desc, config2.w, x)
     assert y.shape == (0, 14336)
+
+
+def _with_env(env, fn):
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update({k: str(v) for k, v in env.items()})
+    try:
+        return fn()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("ks", [1, 2, 4])
+@pytest.mark.parametrize("nbw", [1, 2])
+@pytest.mark.parametrize("m", [1, 13, 32])
+def test_stream_wave_splits(fmt, ks, nbw, m):
+    """Every streaming launch shape: K split over 1, 2 or 4 waves of a block
+    (7 groups: uneven slices, one wave with a single group), one or two column
+    blocks per wave, N ragged against the block's column sets."""
+    L = Layer(fmt, 200, 896, cfg=10, wseed=ks + 3 * nbw)
+    x = synthetic.activations(10, m, 896, index=m)
+    _with_env({"HM_FORCE_PATH": 1, "HM_STREAM_KS": ks, "HM_STREAM_NBW": nbw}, lambda: L.check(x))
+
+
+@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("ks", [1, 4])
+@pytest.mark.parametrize("m", [17, 32])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_stream_multi_piece(fmt, ks, m, splits):
+    """Activation rows larger than LDS: K is walked in several staged pieces
+    (32 rows x 3072 bf16 or 6144 fp8 bytes exceed the 159 KiB budget)."""
+    k = 6144 if fmt == quant.FMT_MXFP4 else 3072
+    L = Layer(fmt, 96, k, cfg=11, wseed=ks)
+    x = synthetic.activations(11, m, k, index=m + splits)
+    env = {"HM_FORCE_PATH": 1, "HM_STREAM_KS": ks, "HM_STREAM_SPLITS": splits}
+    _with_env(env, lambda: L.check(x))

@@ -155,3 +155,18 @@ def test_moe_workload_size_sampled(fmt, t, proj):
     yref, b, _ = moe.moe_gemm_ref(xh, bool(rows_are_pairs), topk, ids, what, n, pairs=pairs)
     res = gemm.check(bits_of(y)[pairs], yref, b)
     assert res["ok"], res
+
+
+@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("ks", [2, 4])
+def test_moe_stream_wave_splits(fmt, ks):
+    """Streaming units with K split over 2 or 4 waves of a block (K = 5 groups:
+    uneven slices, and with 4 waves one wave holds a single group)."""
+    import os
+    t, topk, E, n, k = 150, 2, 8, 208, 640
+    ids = _skewed_ids(t, topk, E, 3)
+    os.environ["HM_MOE_STREAM_KS"] = str(ks)
+    try:
+        _run_moe(fmt, E, n, k, t, topk, ids, 0, 3)
+    finally:
+        os.environ.pop("HM_MOE_STREAM_KS", None)
