@@ -54,6 +54,7 @@ __host__ __device__ inline Geom make_geom(int wfmt, int64_t E, int64_t N, int64_
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -113,6 +114,14 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
 __device__ __forceinline__ uint32_t in_sgpr(uint32_t v) {
   __asm__ volatile("" : "+s"(v));
   return v;
+}
+
+// 32x32x16 bf16 MFMA: lane L supplies A row L%32 and B column L%32 for K
+// = 8*(L/32) + 0..7; C: lane L holds column L%32, rows 8*j + 4*(L/32) + r in
+// register 4*j + r (j, r = 0..3).
+__device__ __forceinline__ f32x16_t mfma32_bf16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
 // 16x16x32 bf16 MFMA: C[i][j] += sum_k A[i][k] B[k][j]; lane L supplies A row

@@ -19,7 +19,8 @@ using namespace hm;
 
 constexpr int kStreamMaxRows = 32;   // dense rows handled by the streaming kernel (two 16-row blocks)
 constexpr int64_t kStreamLdsBytes = 159 * 1024;  // dynamic LDS one streaming block may use
-constexpr int kMoeStreamRows = 16;   // expert segments of at most this many rows use the streaming kernel
+constexpr int kMoeStreamRows = 16;
+constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles are used   // expert segments of at most this many rows use the streaming kernel
 constexpr int kGroupedGridStream = 2048;
 constexpr int kGroupedGridTile = 1024;
 
@@ -54,6 +55,7 @@ int env_int(const char* name, int dflt) {
 // ---------------------------------------------------------------- dense plan
 struct DensePlan {
   bool stream;
+  bool big;          // 256 x 256 tiles (large M), else 128 x 128 tiles
   StreamCfg sc;
   int ksg;
   size_t ws_bytes;
@@ -62,10 +64,13 @@ struct DensePlan {
 DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
   DensePlan p{};
   const Geom G = geom_of(d);
-  const int force = env_int("HM_FORCE_PATH", 0);  // 1 = streaming, 2 = tile
+  const int force = env_int("HM_FORCE_PATH", 0);  // 1 = streaming, 2 = 128-row tiles, 3 = 256-row tiles
   p.stream = (force == 1) || (force == 0 && m <= kStreamMaxRows);
   if (force == 1 && m > kStreamMaxRows) p.stream = false;  // streaming handles <= 32 rows per block
-  if (!p.stream) return p;
+  if (!p.stream) {
+    p.big = (force == 3) || (force == 0 && m >= kBigMinRows);
+    return p;
+  }
   p.sc.mb = (m <= 16) ? 1 : 2;
   const int64_t rows = (m < 16 * p.sc.mb) ? m : 16 * p.sc.mb;
   const int64_t m_chunks = (m + 16 * p.sc.mb - 1) / (16 * p.sc.mb);
@@ -233,7 +238,7 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* 
     snprintf(buf, buf_len, "%s stream mb=%d nbw=%d ks=%d splits=%d ksg=%d mfma=%s", w, p.sc.mb,
              p.sc.nbw, p.sc.ks, p.sc.splits, p.ksg, d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
   else
-    snprintf(buf, buf_len, "%s tile %dx%d waves=2x2 mfma=%s", w, kTileM, kTileN,
+    snprintf(buf, buf_len, "%s tile %dx%d waves=2x2 mfma=%s", w, p.big ? 256 : kTileM, p.big ? 256 : kTileN,
              d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
   return HM_OK;
 }
@@ -272,7 +277,7 @@ HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, con
     e = launch_gemm_stream(a, p.sc, false, 0, stream);
     if (e == hipSuccess && p.sc.splits > 1) e = launch_splitk_reduce(a, p.sc.splits, stream);
   } else {
-    e = launch_gemm_tile(a, false, 0, stream);
+    e = p.big ? launch_gemm_big(a, stream) : launch_gemm_tile(a, false, 0, stream);
   }
   return (e == hipSuccess) ? HM_OK : HM_ERR_HIP;
 }

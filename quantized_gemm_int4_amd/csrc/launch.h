@@ -59,4 +59,7 @@ constexpr int kTileM = 128;
 constexpr int kTileN = 128;
 hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
 
+// MFMA kernel with 256 x 256 output tiles for large dense M: one block per tile.
+hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t st);
+
 }  // namespace hm

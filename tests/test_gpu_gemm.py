@@ -233,3 +233,14 @@ def test_stream_multi_piece(fmt, ks, m, splits):
     x = synthetic.activations(11, m, k, index=m + splits)
     env = {"HM_FORCE_PATH": 1, "HM_STREAM_KS": ks, "HM_STREAM_SPLITS": splits}
     _with_env(env, lambda: L.check(x))
+
+
+@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("m,n,k", [(1, 200, 384), (300, 1000, 1152), (513, 528, 640), (256, 256, 128),
+                                   (700, 96, 256)])
+def test_big_tiles_ragged(fmt, m, n, k):
+    """The 256 x 256 tile kernel on ragged shapes: M and N not multiples of
+    256, one or an odd number of K groups, a single row, a single tile."""
+    L = Layer(fmt, n, k, cfg=13, wseed=m)
+    x = synthetic.activations(13, m, k, index=m, outliers=0.01 if fmt == quant.FMT_MXFP4 else 0)
+    _with_env({"HM_FORCE_PATH": 3}, lambda: L.check(x))
