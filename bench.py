@@ -41,7 +41,20 @@ def parse():
                    choices=["dense_w4a16", "dense_w4a8", "moe_w4a16", "moe_w4a8"])
     p.add_argument("--reps", type=int, default=30, help="launches per M for per-kernel timing")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle (cpu_baseline) leg")
+    p.add_argument("--counters-run", action="store_true",
+                   help="launches only, for rocprofv3 --pmc: each M of the dense sweep 3 times "
+                        "between marker kernels, then a 512 MiB copy for calibration")
+    p.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn the FETCH_SIZE and WRITE_SIZE csv output of two --counters-run "
+                        "passes into profiles/traffic.json (no GPU needed)")
     return p.parse_args()
+
+
+def kernel_of(plan):
+    """Kernel that carries a dense launch, from its plan string."""
+    if " stream " in plan:
+        return "k_gemm_stream"
+    return "k_gemm_big" if "256x256" in plan else "k_gemm_tile"
 
 
 def src_hash():
@@ -53,18 +66,22 @@ def src_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel_key):
-    """HBM bytes per launch measured with rocprofv3 counters for this exact
+def traffic_for(workload, ms):
+    """Mean HBM bytes (read + written) per launch over the given M values, as
+    measured with rocprofv3 FETCH_SIZE / WRITE_SIZE counters for this exact
     kernel source (profiles/traffic.json), or None if absent or stale."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    e = t.get(kernel_key)
+    e = t.get(workload)
     if not e or e.get("src_hash") != src_hash():
         return None
-    return e.get("bytes_per_launch")
+    per_m = e.get("bytes_per_launch_by_M", {})
+    if not all(str(m) in per_m for m in ms):
+        return None
+    return round(float(np.mean([per_m[str(m)] for m in ms])), 1)
 
 
 def capture(torch, fn):
@@ -217,24 +234,28 @@ def run_dense(args, fmt):
                           roofline_frac=round(t_roof / (us * 1e-6), 4),
                           plan=hm.hm_gemm_plan(S["desc"], afmt, m)))
 
-    # ---- roofline of the dominant kernel (the one with most time per step)
-    tile_ms = [s for s in sweep if "tile" in s["plan"]]
-    stream_ms = [s for s in sweep if "stream" in s["plan"]]
-    if sum(s["us"] for s in tile_ms) >= sum(s["us"] for s in stream_ms):
-        fl_avg = np.mean([2.0 * s["M"] * n * k for s in tile_ms])
-        us_avg = np.mean([s["us"] for s in tile_ms])
-        achieved = fl_avg / (us_avg * 1e-6) / 1e12
-        roof = dict(bound="mfma", kernel="k_gemm_tile", achieved=round(achieved, 2), peak=peak,
-                    unit="TFLOP/s", frac=round(achieved / peak, 4),
-                    per_launch=f"mean over M={[s['M'] for s in tile_ms]} of 2*M*N*K flops",
-                    traffic=traffic_for(f"tile_{fmt}"))
+    # ---- roofline of the dominant kernel: the one with most launch time per
+    # step.  achieved = its algorithmic flops (MFMA-bound, 2*M*N*K per launch)
+    # or weight bytes (HBM-bound) summed over its launches, divided by their
+    # summed launch times measured above.
+    by_kernel = {}
+    for s_ in sweep:
+        by_kernel.setdefault(kernel_of(s_["plan"]), []).append(s_)
+    dom = max(by_kernel, key=lambda kn: sum(s_["us"] for s_ in by_kernel[kn]))
+    runs = by_kernel[dom]
+    us_sum = sum(s_["us"] for s_ in runs)
+    if dom == "k_gemm_stream":
+        achieved = alg_w * len(runs) / (us_sum * 1e-6) / 1e9
+        roof = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4),
+                    per_launch=f"{alg_w} algorithmic weight bytes per launch, M={[s_['M'] for s_ in runs]}")
     else:
-        by_avg = np.mean([alg_w for _ in stream_ms])
-        us_avg = np.mean([s["us"] for s in stream_ms])
-        achieved = by_avg / (us_avg * 1e-6) / 1e9
-        roof = dict(bound="hbm", kernel="k_gemm_stream", achieved=round(achieved, 1),
-                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=traffic_for(f"stream_{fmt}"))
+        achieved = sum(2.0 * s_["M"] * n * k for s_ in runs) / (us_sum * 1e-6) / 1e12
+        roof = dict(bound="mfma", kernel=dom, achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4),
+                    per_launch=f"2*M*N*K flops per launch, M={[s_['M'] for s_ in runs]}")
+    roof["traffic"] = traffic_for(f"dense_{fmt}", [s_["M"] for s_ in runs])
+    roof["traffic_unit"] = "bytes per launch (HBM read + write)"
 
     cpu = None if args.no_cpu else cpu_dense(S, fmt, n, k, ms, hm, torch)
     out = dict(metric=METRIC, value=round(value, 3), unit="TFLOP/s", n_gpus=1, steps=args.steps,
@@ -371,7 +392,9 @@ def run_moe(args, fmt):
         t_roof = max(wb / (HBM_PEAK_GBS * 1e9), fl / (peak * 1e12))
         per_t.append(dict(T=t, ms=round(ms_t, 4), tflops=round(fl / ms_t / 1e9, 3),
                           weight_GBps=round(wb / ms_t / 1e6, 1), active_experts=act,
-                          max_rows=int(counts.max()), roofline_frac=round(t_roof / (ms_t * 1e-3), 4)))
+                          max_rows=int(counts.max()), roofline_frac=round(t_roof / (ms_t * 1e-3), 4),
+                          bound="mfma" if fl / (peak * 1e12) >= wb / (HBM_PEAK_GBS * 1e9) else "hbm",
+                          flops=fl, weight_bytes=wb))
         step_ms += ms_t
         step_fl += fl
     wl = (f"MoE {'W4A8-MXFP4' if fmt == 'mxfp4' else 'W4A16 int4-sym G128'} 256 experts top-8 "
@@ -380,11 +403,125 @@ def run_moe(args, fmt):
                 n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=round(step_ms, 4),
                 higher_is_better=True, scaling="weak", vs_baseline=None,
                 dtype="fp8" if fmt == "mxfp4" else "bf16", data="synthetic",
-                config=dict(workload=wl), per_T=per_t, roofline=None, cpu_baseline=None)
+                config=dict(workload=wl), per_T=per_t, roofline=moe_roofline(per_t, fmt),
+                cpu_baseline=None)
+
+
+def moe_roofline(per_t, fmt):
+    """Roofline of the dominant part of the MoE step: the token count with the
+    most time; one launch = one step (expert sort, gate_up and down grouped
+    GEMMs), its bound the binding one at that token count."""
+    r = max(per_t, key=lambda e: e["ms"])
+    peak = FP8_PEAK_TFLOPS if fmt == "mxfp4" else BF16_PEAK_TFLOPS
+    if r["bound"] == "mfma":
+        a = r["flops"] / (r["ms"] * 1e-3) / 1e12
+        return dict(bound="mfma", kernel="hm_moe_gemm (grouped k_gemm_tile + k_gemm_stream)",
+                    achieved=round(a, 2), peak=peak, unit="TFLOP/s", frac=round(a / peak, 4),
+                    per_launch=f"2*P*N*K flops of gate_up + down at T={r['T']}", traffic=None)
+    a = r["weight_bytes"] / (r["ms"] * 1e-3) / 1e9
+    return dict(bound="hbm", kernel="hm_moe_gemm (grouped k_gemm_stream + k_gemm_tile)",
+                achieved=round(a, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(a / HBM_PEAK_GBS, 4),
+                per_launch=f"weight bytes of the active experts at T={r['T']}", traffic=None)
+
+
+def counters_run(fmt):
+    """Launches only (no timing), for two rocprofv3 --pmc passes (FETCH_SIZE,
+    then WRITE_SIZE): each M of the dense sweep 3 times on rotating weight
+    copies, a marker fill kernel after each M, then a 512 MiB device copy
+    whose known traffic calibrates the counters."""
+    import torch
+    import quantized_gemm_int4_amd as hm
+    import synthetic
+    n, k, ms = (7168, 2048, [16, 256, 4096]) if fmt == "mxfp4" else (14336, 4096, [1, 16, 128, 1024, 4096])
+    S = dense_setup(torch, hm, synthetic, fmt, n, k, ms)
+    marker = torch.empty(64, dtype=torch.int32, device="cuda:0")
+    i = 0
+    # warm-up sweep (lazy initialization, write-back of the weight copies just
+    # made), closed by a marker; the ingest step skips this first group
+    for m in ms:
+        dense_call(hm, S, m, i, fmt)
+        i += 1
+    torch.cuda.synchronize()
+    marker.fill_(0)
+    for m in ms:
+        for _ in range(3):
+            dense_call(hm, S, m, i, fmt)
+            i += 1
+        marker.fill_(m)
+    torch.cuda.synchronize()
+    src = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(counters_run=fmt, M=ms, plans=[hm.hm_gemm_plan(S["desc"], 1 if fmt == "mxfp4" else 0, m)
+                                                        for m in ms])), flush=True)
+
+
+def ingest_counters(fetch_dir, write_dir):
+    """Per-launch HBM bytes of the dense sweep from two counters-run passes.
+    Dispatches between consecutive marker fills belong to one M (3 launches;
+    the W4A8 launches include the FP8 activation quantization); the group
+    before the first marker is the warm-up sweep and is skipped.  The counters
+    are scaled by the factor that makes the 512 MiB copy read (FETCH_SIZE) and
+    write (WRITE_SIZE) exactly 512 MiB."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        rows = [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return rows
+
+    out = {}
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        rows = load(d, counter)
+        marks = [i for i, r in enumerate(rows) if "FillFunctor<int>" in r["Kernel_Name"]]
+        # the calibration copies are the copy dispatches after the last marker
+        copy = [float(r["Counter_Value"]) for r in rows[marks[-1] + 1:] if "copy" in r["Kernel_Name"].lower()]
+        calib = (512 * 2 ** 20 / 1024) / float(np.median(copy))       # counters are KiB
+        groups, cur = [], []
+        for r in rows[:marks[-1] + 1]:
+            name = r["Kernel_Name"]
+            if "FillFunctor<int>" in name:
+                groups.append(cur)
+                cur = []
+            elif "hm::" in name:
+                cur.append(float(r["Counter_Value"]) * 1024 * calib)
+        out[counter] = dict(calib=calib, per_group=[sum(g) / 3.0 for g in groups[1:]],
+                            copy_kib=float(np.median(copy)))
+    return out
 
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        fmt = "mxfp4" if args.workload == "dense_w4a8" else "uint4_zp"
+        ms = [16, 256, 4096] if fmt == "mxfp4" else [1, 16, 128, 1024, 4096]
+        res = ingest_counters(*args.ingest_counters)
+        fetch, write = res["FETCH_SIZE"]["per_group"], res["WRITE_SIZE"]["per_group"]
+        if len(fetch) != len(ms) or len(write) != len(ms):
+            sys.exit(f"expected {len(ms)} marker-separated groups, got {len(fetch)} / {len(write)}")
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        t = json.load(open(path)) if os.path.exists(path) else {}
+        t[f"dense_{fmt}"] = dict(
+            src_hash=src_hash(),
+            bytes_per_launch_by_M={str(m): round(f + w, 1) for m, f, w in zip(ms, fetch, write)},
+            fetch_bytes_by_M={str(m): round(f, 1) for m, f in zip(ms, fetch)},
+            write_bytes_by_M={str(m): round(w, 1) for m, w in zip(ms, write)},
+            calibration=dict(fetch=round(res["FETCH_SIZE"]["calib"], 4), write=round(res["WRITE_SIZE"]["calib"], 4),
+                             reference="512 MiB device copy, known read and write bytes"),
+            command=f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
+                    f"python3 bench.py --workload {args.workload} --counters-run")
+        with open(path, "w") as f:
+            json.dump(t, f, indent=1, sort_keys=True)
+        print(json.dumps(t[f"dense_{fmt}"]))
+        return
+    if args.counters_run:
+        counters_run("mxfp4" if args.workload == "dense_w4a8" else "uint4_zp")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
