@@ -20,9 +20,11 @@ using namespace hm;
 constexpr int kStreamMaxRows = 32;   // dense rows handled by the streaming kernel (two 16-row blocks)
 constexpr int64_t kStreamLdsBytes = 159 * 1024;  // dynamic LDS one streaming block may use
 constexpr int kMoeStreamRows = 16;
-constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles are used   // expert segments of at most this many rows use the streaming kernel
+constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles are used
+constexpr int kMoeBigMinRows = 192;   // an expert remainder of this many rows gets a 256-row unit   // expert segments of at most this many rows use the streaming kernel
 constexpr int kGroupedGridStream = 2048;
 constexpr int kGroupedGridTile = 1024;
+constexpr int kGroupedGridBig = 256;     // one 256-tile block per compute unit (LDS-bound)
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -124,8 +126,8 @@ DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
 
 // ---------------------------------------------------------------- MoE plan
 struct MoePlan {
-  int64_t P, max_s, max_t;
-  size_t off_su, off_tu, ws_bytes;
+  int64_t P, max_s, max_t, max_b;
+  size_t off_su, off_tu, off_bu, ws_bytes;
   int nbw, ks, lds_kb;
 };
 
@@ -135,9 +137,11 @@ MoePlan plan_moe(const hm_wdesc* d, int64_t t, int32_t topk) {
   const int64_t act = (p.P < d->num_experts) ? p.P : d->num_experts;
   p.max_s = act;
   p.max_t = (p.P + kTileM - 1) / kTileM + act;
+  p.max_b = p.P / kMoeBigMinRows + 1;         // every 256-row unit holds >= kMoeBigMinRows rows
   p.off_su = 256;
   p.off_tu = align256(p.off_su + (size_t)p.max_s * 16);
-  p.ws_bytes = align256(p.off_tu + (size_t)p.max_t * 16);
+  p.off_bu = align256(p.off_tu + (size_t)p.max_t * 16);
+  p.ws_bytes = align256(p.off_bu + (size_t)p.max_b * 16);
   p.nbw = 1;
   p.ks = env_int("HM_MOE_STREAM_KS", 1);
   if (p.ks != 1 && p.ks != 2 && p.ks != 4) p.ks = 1;
@@ -277,7 +281,7 @@ HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, con
     e = launch_gemm_stream(a, p.sc, false, 0, stream);
     if (e == hipSuccess && p.sc.splits > 1) e = launch_splitk_reduce(a, p.sc.splits, stream);
   } else {
-    e = p.big ? launch_gemm_big(a, stream) : launch_gemm_tile(a, false, 0, stream);
+    e = p.big ? launch_gemm_big(a, false, 0, stream) : launch_gemm_tile(a, false, 0, stream);
   }
   return (e == hipSuccess) ? HM_OK : HM_ERR_HIP;
 }
@@ -344,6 +348,7 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   int32_t* hdr = (int32_t*)w8;
   int32_t* su = (int32_t*)(w8 + p.off_su);
   int32_t* tu = (int32_t*)(w8 + p.off_tu);
+  int32_t* bu = (int32_t*)(w8 + p.off_bu);
   GemmArgs a{};
   a.w = (const uint8_t*)w_dev;
   a.G = geom_of(d);
@@ -358,8 +363,11 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   a.rows_are_pairs = a_rows_are_pairs;
 
   a.P = p.P;
-  hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, kMoeStreamRows, kTileM, p.max_s,
-                                     p.max_t, hdr, su, tu, stream);
+  // 256-row units address activation rows with 32-bit byte offsets
+  const int64_t a_bytes = (a_rows_are_pairs ? p.P : t) * d->k * (afmt == HM_A_FP8_ROWSCALE ? 1 : 2);
+  const int big_min = (a_bytes < (1ll << 32) && env_int("HM_MOE_BIG", 1)) ? kMoeBigMinRows : 0;
+  hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, kMoeStreamRows, kTileM, big_min,
+                                     p.max_s, p.max_t, p.max_b, hdr, su, tu, bu, stream);
   if (e == hipSuccess) {
     StreamCfg sc{kMoeStreamRows / 16, p.nbw, 1, p.ks, p.lds_kb};
     const int64_t nts = stream_n_tiles(a.G, sc);
@@ -374,6 +382,12 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
     if (gi > kGroupedGridTile) gi = kGroupedGridTile;
     a.units = tu;
     if (gi > 0) e = launch_gemm_tile(a, true, (int)gi, stream);
+  }
+  if (e == hipSuccess && big_min > 0) {
+    int64_t gi = p.max_b * big_n_tiles(a.G);
+    if (gi > kGroupedGridBig) gi = kGroupedGridBig;
+    a.units = bu;
+    if (gi > 0) e = launch_gemm_big(a, true, (int)gi, stream);
   }
   return (e == hipSuccess) ? HM_OK : HM_ERR_HIP;
 }

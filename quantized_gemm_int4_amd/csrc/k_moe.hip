@@ -100,10 +100,17 @@ k_moe_sort(const int32_t* __restrict__ ids, int64_t P, int E, int32_t* __restric
 // streaming unit; longer ones become ceil(count/bm) tile units of <= bm rows.
 // Unit = {expert, first index into sorted_pairs, row count, 0}.
 // hdr[0] = number of streaming units, hdr[1] = number of tile units.
+// Work units of a grouped GEMM from the expert offsets (one thread per
+// expert, E <= 512).  An expert with at most s_max rows is one streaming unit.
+// A larger one is cut into 256-row units while big_min > 0 (a remainder of at
+// least big_min rows is one more 256-row unit) and what is left into units of
+// at most bm rows for the 128-row tile kernel.  Units are {expert, first row,
+// rows, 0}; hdr = {streaming units, tile units, 256-row units}, each capped
+// at its array size.
 __global__ void __launch_bounds__(512)
-k_moe_schedule(const int32_t* __restrict__ offsets, int E, int64_t P, int s_max, int bm,
-               int64_t max_s, int64_t max_t, int32_t* __restrict__ hdr, int32_t* __restrict__ su,
-               int32_t* __restrict__ tu) {
+k_moe_schedule(const int32_t* __restrict__ offsets, int E, int64_t P, int s_max, int bm, int big_min,
+               int64_t max_s, int64_t max_t, int64_t max_b, int32_t* __restrict__ hdr,
+               int32_t* __restrict__ su, int32_t* __restrict__ tu, int32_t* __restrict__ bu) {
   __shared__ int wsum[8];
   const int e = threadIdx.x;
   int c = 0, beg = 0;
@@ -116,22 +123,41 @@ k_moe_schedule(const int32_t* __restrict__ offsets, int E, int64_t P, int s_max,
     c = (int)(f - b);
   }
   const int ns = (c > 0 && c <= s_max) ? 1 : 0;
-  const int nt = (c > s_max) ? (c + bm - 1) / bm : 0;
+  int nb = 0, rest = 0;
+  if (c > s_max) {
+    if (big_min > 0) {
+      nb = c / kBigRows;
+      rest = c - nb * kBigRows;
+      if (rest >= big_min) { ++nb; rest = 0; }
+    } else {
+      rest = c;
+    }
+  }
+  const int nt = (rest + bm - 1) / bm;
   const int is = block_scan512(ns, wsum);
   const int it = block_scan512(nt, wsum);
+  const int ib = block_scan512(nb, wsum);
   if (ns && is - 1 < max_s) {
     int32_t* u = su + 4 * (is - 1);
     u[0] = e; u[1] = beg; u[2] = c; u[3] = 0;
   }
+  for (int i = 0; i < nb; ++i) {
+    if (ib - nb + i >= max_b) break;
+    int32_t* u = bu + 4 * (ib - nb + i);
+    const int r0 = i * kBigRows;
+    u[0] = e; u[1] = beg + r0; u[2] = (c - r0 < kBigRows) ? c - r0 : kBigRows; u[3] = 0;
+  }
+  const int t0 = c - rest;                        // first row left for the tile units
   for (int i = 0; i < nt; ++i) {
     if (it - nt + i >= max_t) break;
     int32_t* u = tu + 4 * (it - nt + i);
-    const int r0 = i * bm;
+    const int r0 = t0 + i * bm;
     u[0] = e; u[1] = beg + r0; u[2] = (c - r0 < bm) ? c - r0 : bm; u[3] = 0;
   }
   if (e == 511) {
     hdr[0] = (int32_t)(is < max_s ? is : max_s);
     hdr[1] = (int32_t)(it < max_t ? it : max_t);
+    hdr[2] = (int32_t)(ib < max_b ? ib : max_b);
   }
 }
 
@@ -142,11 +168,11 @@ hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int E, int32_t* counts
   return hipGetLastError();
 }
 
-hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_max, int bm,
-                               int64_t max_s, int64_t max_t, int32_t* hdr, int32_t* su,
-                               int32_t* tu, hipStream_t st) {
-  hipLaunchKernelGGL(k_moe_schedule, dim3(1), dim3(512), 0, st, offsets, E, P, s_max, bm, max_s,
-                     max_t, hdr, su, tu);
+hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_max, int bm, int big_min,
+                               int64_t max_s, int64_t max_t, int64_t max_b, int32_t* hdr, int32_t* su,
+                               int32_t* tu, int32_t* bu, hipStream_t st) {
+  hipLaunchKernelGGL(k_moe_schedule, dim3(1), dim3(512), 0, st, offsets, E, P, s_max, bm, big_min, max_s,
+                     max_t, max_b, hdr, su, tu, bu);
   return hipGetLastError();
 }
 

@@ -6,6 +6,8 @@
 
 namespace hm {
 
+constexpr int kBigRows = 256;   // rows of a 256 x 256 tile (and of a grouped 256-row unit)
+
 // Arguments shared by the GEMM kernels.
 struct GemmArgs {
   const uint8_t* w;        // device weight layout (all experts)
@@ -19,7 +21,7 @@ struct GemmArgs {
   int ksg;                 // K groups per split (dense streaming)
   // grouped (MoE) mode
   const int32_t* units;    // {expert, first, count, 0} per unit
-  const int32_t* hdr;      // hdr[0] streaming units, hdr[1] tile units
+  const int32_t* hdr;      // hdr[0] streaming units, hdr[1] tile units, hdr[2] 256-row units
   const int32_t* sorted_pairs;
   int topk;
   int rows_are_pairs;
@@ -34,9 +36,9 @@ hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_
                                  hipStream_t st);
 hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int E, int32_t* counts, int32_t* offsets,
                            int32_t* sorted_pairs, hipStream_t st);
-hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_max, int bm,
-                               int64_t max_s, int64_t max_t, int32_t* hdr, int32_t* su,
-                               int32_t* tu, hipStream_t st);
+hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_max, int bm, int big_min,
+                               int64_t max_s, int64_t max_t, int64_t max_b, int32_t* hdr, int32_t* su,
+                               int32_t* tu, int32_t* bu, hipStream_t st);
 
 // Streaming (small-M) kernel.  Dense: grid (n_tiles, splits, m_chunks).
 // Grouped: persistent over (streaming unit x n tile) items.
@@ -59,7 +61,9 @@ constexpr int kTileM = 128;
 constexpr int kTileN = 128;
 hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
 
-// MFMA kernel with 256 x 256 output tiles for large dense M: one block per tile.
-hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t st);
+// MFMA kernel with 256 x 256 output tiles.  Dense: one block per tile.
+// Grouped: persistent over (256-row unit x 256-column tile) items, hdr[2] units.
+hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
+int64_t big_n_tiles(const Geom& G);
 
 }  // namespace hm

@@ -170,3 +170,27 @@ def test_moe_stream_wave_splits(fmt, ks):
         _run_moe(fmt, E, n, k, t, topk, ids, 0, 3)
     finally:
         os.environ.pop("HM_MOE_STREAM_KS", None)
+
+
+@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("rows_are_pairs", [0, 1])
+@pytest.mark.parametrize("big", [1, 0])
+def test_moe_big_units(fmt, rows_are_pairs, big):
+    """Experts large enough for 256-row units: 600 rows (two units of 256 and
+    an 88-row tile unit), 450 rows (256 + a 194-row remainder, which takes a
+    second 256-row unit), 100 rows (tile unit) and a few rows (streaming), on
+    K = 5 groups and ragged N; with HM_MOE_BIG=0 the same call uses tile
+    units only."""
+    import os
+    t, topk, E, n, k = 600, 2, 6, 288, 640
+    r = np.random.default_rng(7)
+    ids = np.zeros((t, topk), dtype=np.int32)
+    ids[:, 0] = 0                                   # expert 0: 600 rows
+    second = np.concatenate([np.full(450, 1), np.full(100, 2), np.full(30, 3), np.full(12, 4),
+                             np.full(8, 5)])
+    ids[:, 1] = r.permutation(second)
+    os.environ["HM_MOE_BIG"] = str(big)
+    try:
+        _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, 9)
+    finally:
+        os.environ.pop("HM_MOE_BIG", None)
