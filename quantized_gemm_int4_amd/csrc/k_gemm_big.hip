@@ -1,26 +1,24 @@
-// MFMA GEMM for many rows (prefill-sized M), where the ~2*M*N*K matrix
-// multiply dominates (ywsung.com note "How vLLM Humming computes 4 bits",
-// section on one token vs many tokens).
+// MFMA GEMM for many rows (prefill-sized M, and 256-row units of a grouped
+// GEMM), where the ~2*M*N*K matrix multiply dominates (ywsung.com note "How
+// vLLM Humming computes 4 bits", section on one token vs many tokens).
 //
-// One 256-thread block computes a 256 x 256 output tile; each of its four
-// waves owns 128 x 128 (8 x 8 MFMA blocks of 16 x 16, 256 fp32 accumulators
-// per lane), which halves the LDS operand traffic per MFMA compared with
-// 64 x 64 wave tiles.  Activations reach LDS through 16-byte direct
-// global-to-LDS loads laid out in MFMA fragment order (lane L of a 1 KiB
-// fragment at byte 16 L), so every operand read is one conflict-free 1 KiB
-// sweep.  Two LDS stages: the loads of step s+1 fly while step s multiplies.
-//   * W4A16 (K step 64): the block's threads unpack the next step's weights
-//     to bf16 s * (u - z) between the MFMAs of the current step and write them
-//     to LDS in fragment order.  Codes, scales and zero points of a K group are
-//     fetched one step before their first use.
-//   * W4A8-MXFP4 (K step 128): each wave loads its E2M1 weight tiles straight
-//     into registers (they are already the A operand of the 16x16x128 scaled
-//     MFMA) and passes their E8M0 scales; the per-token FP8 scale is applied
-//     in the epilogue.
-// Tiles are assigned XCD by XCD: blocks are dispatched round-robin over the
-// eight XCDs, so block b runs on XCD b % 8; each XCD gets a contiguous range
-// of tiles, visited in groups of four tile rows, so the blocks that share an
-// XCD's L2 also share activation and weight slices.
+// One block computes a 256 x 256 output tile.  Activations reach LDS through
+// 16-byte direct global-to-LDS loads laid out in MFMA fragment order (lane L
+// of a 1 KiB fragment at byte 16 L), so every operand read is one
+// conflict-free 1 KiB sweep.  Three LDS stages: copies run two K steps ahead.
+//   * W4A16 (K step 64, eight waves, two per SIMD): each wave owns 128 rows x
+//     64 columns as 32x32x16 bf16 MFMA blocks (128 accumulators per lane) and
+//     unpacks its columns' weights, copied into LDS one step ahead of the
+//     activations, to bf16 s * (u - z) after its MFMAs of the step, while the
+//     other wave of the SIMD multiplies.
+//   * W4A8-MXFP4 (K step 128, four waves of 128 x 128): E2M1 weight tiles and
+//     their E8M0 scale words are copied to LDS too and fed as stored to the
+//     16x16x128 scaled MFMA; the per-token FP8 scale is applied in the
+//     epilogue.
+// Dense tiles are assigned XCD by XCD: blocks are dispatched round-robin over
+// the eight XCDs, so block b runs on XCD b % 8; each XCD gets a contiguous
+// range of tiles, visited in groups of four tile rows, so the blocks that
+// share an XCD's L2 also share activation and weight slices.
 #include <algorithm>
 #include <type_traits>
 
@@ -81,7 +79,7 @@ __host__ __device__ constexpr int big_lds_bytes(bool mx) { return kBigStages * b
 // expert, whose activation rows are gathered through the sorted pair list
 // and whose outputs are written in pair order.
 template <bool MX, bool ZP, bool GROUPED>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(MX ? 256 : 512, 1)
 k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   constexpr int SB = big_stage_bytes(MX);
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -104,7 +102,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
       e = u[0];
       rows_left = u[2] < kBigM ? u[2] : kBigM;
       nb0 = (item % tiles_n) * kBigCB;
-      {
+      if (tid < kBigM) {
         int64_t ar = 0, orr = -1;   // invalid rows read row 0 (always present) and are not stored
         if (tid < rows_left) {
           const int64_t pair = a.sorted_pairs[u[1] + tid];
@@ -257,85 +255,88 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
       }
     } else {
       // ================================ W4A16: K step 64 = half a K group;
-      // wave w owns columns 64w..64w+63 for all 256 rows as 2 x 8 blocks of
-      // 32 x 32 (v_mfma_f32_32x32x16_bf16: unlike the 16x16x32 form, one wave
-      // per SIMD keeps the matrix core busy), and unpacks its own weights into
-      // MFMA operands.  32x32x16 operands: A row / B column = lane % 32, K =
-      // 8 (lane / 32) + 0..7; result: column lane % 32, rows 8 j + 4 (lane / 32) + r
-      // in register 4 j + r.
-      f32x16_t acc[2][8];
-  #pragma unroll
+      // eight waves, two per SIMD: wave w owns rows 128 (w & 1) + 0..127 and
+      // columns 64 (w >> 1) + 0..63 as 2 x 4 blocks of 32 x 32
+      // (v_mfma_f32_32x32x16_bf16; unlike the 16x16x32 form it keeps the
+      // matrix core busy).  Each wave unpacks the weights of its 64 columns
+      // into MFMA operands after its MFMAs of the step; the other wave on the
+      // SIMD multiplies meanwhile.  32x32x16 operands: A row / B column =
+      // lane % 32, K = 8 (lane / 32) + 0..7; result: column lane % 32, rows
+      // 8 j + 4 (lane / 32) + r in register 4 j + r.
+      const int wm = wave & 1, wn = wave >> 1;
+      f32x16_t acc[2][4];
+#pragma unroll
       for (int nb2 = 0; nb2 < 2; ++nb2)
-  #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-  #pragma unroll
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
           for (int r = 0; r < 16; ++r) acc[nb2][mb][r] = 0.f;
       const int l32 = lane & 31, hi = lane >> 5;
-      // activation fragments: fragment f = 4 mb + kq (row block of 32, K part of
-      // 16); wave w copies kq = w for mb = 0..7
-      uint32_t xoff[8];
-  #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        xoff[mb] = xrow(mb * 32 + l32) + 2 * (16 * wave + 8 * hi);
+      // activation fragments: fragment f = 4 mb + kq (row block of 32, K part
+      // of 16); wave w copies K part w & 3 of row blocks 4 (w >> 2) + 0..3
+      uint32_t xoff[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int mb = 4 * (wave >> 2) + i;
+        xoff[i] = xrow(mb * 32 + l32) + 2 * (16 * (wave & 3) + 8 * hi);
       }
       auto copy_x = [&](int64_t step, uint8_t* stg) {
         const uint8_t* src = xblk + step * 128;     // 64 bf16 per K step
-  #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) g2lds(src + xoff[mb], stg + (mb * 4 + wave) * 1024);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          g2lds(src + xoff[i], stg + ((4 * (wave >> 2) + i) * 4 + (wave & 3)) * 1024);
       };
-      // This wave's four weight tiles per K group, copied to LDS with their
-      // scales and zero points: one 1 KiB tile per copy; one 4-byte-per-lane
-      // copy for the 4 x 32 B of bf16 scales (lane L: tile L / 8, bytes 4 (L % 8));
-      // one for the 4 x 8 B of zero-point words (lane L: tile (L / 2) % 4, word L % 2).
+      // Weight tiles of the block's 16 column blocks: wave w copies tiles
+      // 4 wn + 2 wm + {0, 1}; wave wm = 0 also copies its column quarter's
+      // bf16 scales (lane L: tile L / 8 of the quarter, bytes 4 (L % 8)), wave
+      // wm = 1 the zero-point words (lane L: tile (L / 2) % 4, word L % 2).
       // Lanes past the useful ones repeat in-range addresses into unused bytes.
-      const uint8_t* wsrc[4];
-  #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        int64_t nb = nb0 + wave * 4 + c;
+      const uint8_t* wsrc[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        int64_t nb = nb0 + 4 * wn + 2 * wm + c;
         if (nb >= G.NB) nb = G.NB - 1;
         wsrc[c] = a.w + (wbase + nb) * G.KG * 1024 + lane * 16;
       }
-      const int sc_c = (lane >> 3) & 3, zc_c = (lane >> 1) & 3;
-      int64_t nbs = nb0 + wave * 4 + sc_c, nbz = nb0 + wave * 4 + zc_c;
-      if (nbs >= G.NB) nbs = G.NB - 1;
-      if (nbz >= G.NB) nbz = G.NB - 1;
-      const uint8_t* ssrc = a.w + G.off_scales + (wbase + nbs) * G.KG * 32 + (lane & 7) * 4;
-      const uint8_t* zsrc = a.w + G.off_zeros + (wbase + nbz) * G.KG * 8 + (lane & 1) * 4;
+      const int sz_c = wm == 0 ? ((lane >> 3) & 3) : ((lane >> 1) & 3);
+      int64_t nbq = nb0 + 4 * wn + sz_c;
+      if (nbq >= G.NB) nbq = G.NB - 1;
+      const uint8_t* szsrc = wm == 0 ? a.w + G.off_scales + (wbase + nbq) * G.KG * 32 + (lane & 7) * 4
+                                     : a.w + G.off_zeros + (wbase + nbq) * G.KG * 8 + (lane & 1) * 4;
+      const int64_t szstride = wm == 0 ? 32 : 8;
       constexpr int kWOff = 32 * 1024, kSOff = 48 * 1024, kZOff = 49 * 1024;
       // weights of K step s (group s / 2) into the weight part of stage s % 3
       auto copy_w = [&](int64_t s, uint8_t* stg) {
         const int64_t g = s >> 1;
-  #pragma unroll
-        for (int c = 0; c < 4; ++c) g2lds(wsrc[c] + g * 1024, stg + kWOff + (wave * 4 + c) * 1024);
-        __builtin_amdgcn_global_load_lds(ssrc + g * 32, (lds_void_t*)(stg + kSOff + wave * 256), 4, 0, 0);
-        if (ZP) __builtin_amdgcn_global_load_lds(zsrc + g * 8, (lds_void_t*)(stg + kZOff + wave * 256), 4, 0, 0);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) g2lds(wsrc[c] + g * 1024, stg + kWOff + (4 * wn + 2 * wm + c) * 1024);
+        if (wm == 0 || ZP)
+          __builtin_amdgcn_global_load_lds(szsrc + g * szstride,
+                                           (lds_void_t*)(stg + (wm == 0 ? kSOff : kZOff) + wn * 256), 4, 0, 0);
       };
-      constexpr int kPer = 8 + 4 + 1 + (ZP ? 1 : 0);    // copies per wave per step
-      // A operands of the current step (af) and the next (an): 32-column block
-      // nb2, K part kq.  Lane row n = 32 nb2 + l32 lies in tile 2 nb2 + l32 / 16
-      // at column l32 % 16; K = 64 h + 16 kq + 8 hi is word 2 h + kq / 2 of slot
+      // copies per wave per step: 4 + 2 + 1, except the zero-point copy is
+      // missing for symmetric weights on waves wm = 1; the wait below uses the
+      // smaller count (waiting for one more copy than needed is harmless)
+      constexpr int kPer = 4 + 2 + (ZP ? 1 : 0);
+      // A operands of one step: 32-column block nb2, K part kq.  Lane row n =
+      // 32 nb2 + l32 of the quarter lies in tile 4 wn + 2 nb2 + l32 / 16 at
+      // column l32 % 16; K = 64 h + 16 kq + 8 hi is word 2 h + kq / 2 of slot
       // (l32 % 16) + 16 ((2 kq + hi) % 4) of that tile.
-      u32x4_t af[2][4], an[2][4];
-      auto unpack_from = [&](const uint8_t* stg, int h, auto out_c, int part) {
-        constexpr int o = decltype(out_c)::value;
-        // part = -1: all operands; part = 0..3: column block part >> 1, K parts
-        // 2 (part & 1) and 2 (part & 1) + 1
-  #pragma unroll
+      u32x4_t af[2][4];
+      auto unpack_from = [&](const uint8_t* stg, int h) {
+#pragma unroll
         for (int nb2 = 0; nb2 < 2; ++nb2) {
-          if (part >= 0 && nb2 != (part >> 1)) continue;
           const int c = 2 * nb2 + (l32 >> 4), c16 = l32 & 15;
-          const uint8_t* tile = stg + kWOff + (wave * 4 + c) * 1024;
-          const float sv = bf16_to_f32(*reinterpret_cast<const uint16_t*>(stg + kSOff + wave * 256 + c * 32 + c16 * 2));
-          const uint32_t zw = ZP ? *reinterpret_cast<const uint32_t*>(stg + kZOff + wave * 256 + c * 8 + (c16 >> 3) * 4) : 0u;
+          const uint8_t* tile = stg + kWOff + (4 * wn + c) * 1024;
+          const float sv = bf16_to_f32(*reinterpret_cast<const uint16_t*>(stg + kSOff + wn * 256 + c * 32 + c16 * 2));
+          const uint32_t zw = ZP ? *reinterpret_cast<const uint32_t*>(stg + kZOff + wn * 256 + c * 8 + (c16 >> 3) * 4) : 0u;
           const float z = ZP ? (float)((zw >> (4 * (c16 & 7))) & 0xFu) : 8.0f;
           const float zs = -z * sv;
-  #pragma unroll
+#pragma unroll
           for (int kq = 0; kq < 4; ++kq) {
-            if (part >= 0 && (kq >> 1) != (part & 1)) continue;
             const int slot = c16 + 16 * ((2 * kq + hi) & 3);
             const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + slot * 16 + 4 * (2 * h + (kq >> 1)));
-            if (o == 0) af[nb2][kq] = dq8_bytes(w, sv, zs);
-            else an[nb2][kq] = dq8_bytes(w, sv, zs);
+            af[nb2][kq] = dq8_bytes(w, sv, zs);
           }
         }
       };
@@ -349,64 +350,48 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
       copy_x(0, stage(0));
       copy_x(std::min<int64_t>(1, S - 1), stage(1));
       __syncthreads();
-      unpack_from(stage(0), 0, std::integral_constant<int, 0>(), -1);
-      // Step s multiplies stage s % 3 with operands af.  It first issues the
-      // activations of step s + 2 and the weights of step s + 3 (weights run one
-      // step further ahead: the operands of step s + 1 are unpacked from stage
-      // s + 1 during step s, between the MFMAs).  No branches: near the end the
-      // copies repeat the last step into parts no longer read, so every step
-      // issues the same copies and the wait count is exact.
-  #pragma nounroll
+      unpack_from(stage(0), 0);
+      // Step s multiplies stage s % 3 with operands af, then unpacks the
+      // operands of step s + 1 from stage s + 1.  It first issues the
+      // activations of step s + 2 and the weights of step s + 3.  No branches:
+      // near the end the copies repeat the last step into parts no longer read,
+      // so every step issues the same copies and the wait count is exact.
+#pragma nounroll
       for (int64_t s = 0; s < S; ++s) {
+        copy_x(std::min<int64_t>(s + 2, S - 1), stage(s + 2));
+        copy_w(std::min<int64_t>(s + 3, S - 1), stage(s + 3));
         const uint8_t* stg = stage(s);
-        const uint8_t* nxt = stage(s + 1);
-        const int hn = (int)((s + 1) & 1);
-        // row blocks in pairs; the four K parts of a pair's accumulators run back
-        // to back (clustered updates keep them in place), B fragments one K part ahead
-  #pragma unroll
-        for (int mp = 0; mp < 4; ++mp) {
-          u32x4_t b0 = ld16(stg + ((2 * mp) * 4 + 0) * 1024 + lane * 16);
-          u32x4_t b1 = ld16(stg + ((2 * mp + 1) * 4 + 0) * 1024 + lane * 16);
-  #pragma unroll
-          for (int kq = 0; kq < 4; ++kq) {
-            u32x4_t n0 = b0, n1 = b1;
-            if (kq + 1 < 4) {
-              n0 = ld16(stg + ((2 * mp) * 4 + kq + 1) * 1024 + lane * 16);
-              n1 = ld16(stg + ((2 * mp + 1) * 4 + kq + 1) * 1024 + lane * 16);
-            }
-  #pragma unroll
-            for (int nb2 = 0; nb2 < 2; ++nb2) {
-              acc[nb2][2 * mp] = mfma32_bf16(af[nb2][kq], b0, acc[nb2][2 * mp]);
-              acc[nb2][2 * mp + 1] = mfma32_bf16(af[nb2][kq], b1, acc[nb2][2 * mp + 1]);
-            }
-            b0 = n0;
-            b1 = n1;
-          }
-          if (mp == 0) copy_x(std::min<int64_t>(s + 2, S - 1), stage(s + 2));
-          if (mp == 2) copy_w(std::min<int64_t>(s + 3, S - 1), stage(s + 3));
-          unpack_from(nxt, hn, std::integral_constant<int, 1>(), mp);
+        // each accumulator takes its four K parts back to back (clustered
+        // updates keep the register allocation in place)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const uint8_t* fr = stg + ((4 * wm + mb) * 4) * 1024 + lane * 16;
+          u32x4_t b[4];
+#pragma unroll
+          for (int kq = 0; kq < 4; ++kq) b[kq] = ld16(fr + kq * 1024);
+#pragma unroll
+          for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+            for (int nb2 = 0; nb2 < 2; ++nb2) acc[nb2][mb] = mfma32_bf16(af[nb2][kq], b[kq], acc[nb2][mb]);
         }
-  #pragma unroll
-        for (int nb2 = 0; nb2 < 2; ++nb2)
-  #pragma unroll
-          for (int kq = 0; kq < 4; ++kq) af[nb2][kq] = an[nb2][kq];
+        unpack_from(stage(s + 1), (int)((s + 1) & 1));
         // stage s + 1 (activations) came one step earlier, weights two; after
         // them only this step's copies
         __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPer) : "memory");
       }
 
-      // ---- epilogue: lane holds C[n = 64 w + 32 nb2 + 8 j + 4 hi + r][row = 32 mb + l32]
+      // ---- epilogue: lane holds C[n = 64 wn + 32 nb2 + 8 j + 4 hi + r][row = 128 wm + 32 mb + l32]
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the stages are reused
-  #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const int64_t row = out_row(mb * 32 + l32);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int64_t row = out_row(128 * wm + mb * 32 + l32);
         if (row < 0) continue;
-  #pragma unroll
+#pragma unroll
         for (int nb2 = 0; nb2 < 2; ++nb2)
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 4; ++j) {
             const f32x4_t v = {acc[nb2][mb][4 * j], acc[nb2][mb][4 * j + 1], acc[nb2][mb][4 * j + 2], acc[nb2][mb][4 * j + 3]};
-            store_bf16x4(a.y + row * G.N, G.N, nb0 * 16 + wave * 64 + nb2 * 32 + 8 * j + 4 * hi, v);
+            store_bf16x4(a.y + row * G.N, G.N, nb0 * 16 + wn * 64 + nb2 * 32 + 8 * j + 4 * hi, v);
           }
       }
     }
@@ -423,7 +408,7 @@ static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
   const int tiles_n = (int)((a.G.NB + kBigCB - 1) / kBigCB);
   const int tiles_m = GROUPED ? 0 : (int)((a.M + kBigM - 1) / kBigM);
   const unsigned grid = GROUPED ? (unsigned)(grid_items > 0 ? grid_items : 1) : (unsigned)(tiles_n * tiles_m);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), big_lds_bytes(MX), st, a, tiles_n, tiles_m);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(MX ? 256 : 512), big_lds_bytes(MX), st, a, tiles_n, tiles_m);
   return hipGetLastError();
 }
 
