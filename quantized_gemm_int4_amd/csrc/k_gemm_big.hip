@@ -11,7 +11,7 @@
 //     unpacks its columns' weights, copied into LDS one step ahead of the
 //     activations, to bf16 s * (u - z) after its MFMAs of the step, while the
 //     other wave of the SIMD multiplies.
-//   * W4A8-MXFP4 (K step 128, four waves of 128 x 128): E2M1 weight tiles and
+//   * W4A8-MXFP4 (K step 128, eight waves of 64 x 128): E2M1 weight tiles and
 //     their E8M0 scale words are copied to LDS too and fed as stored to the
 //     16x16x128 scaled MFMA; the per-token FP8 scale is applied in the
 //     epilogue.
@@ -79,7 +79,7 @@ __host__ __device__ constexpr int big_lds_bytes(bool mx) { return kBigStages * b
 // expert, whose activation rows are gathered through the sorted pair list
 // and whose outputs are written in pair order.
 template <bool MX, bool ZP, bool GROUPED>
-__global__ void __launch_bounds__(MX ? 256 : 512, 1)
+__global__ void __launch_bounds__(512, 1)
 k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   constexpr int SB = big_stage_bytes(MX);
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -158,53 +158,54 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
 
     if constexpr (MX) {
       // ================================ W4A8-MXFP4: K step 128 = one K group;
-      // waves 2 x 2, each 128 rows x 128 columns (8 x 8 MFMA blocks)
-      f32x4_t acc[8][8];
-  #pragma unroll
+      // eight waves, two per SIMD: wave w owns rows 64 (w & 3) + 0..63 and
+      // columns 128 (w >> 2) + 0..127 (4 x 8 blocks of 16 x 16, 128
+      // accumulators per lane)
+      const int wm = wave & 3, wn = wave >> 2;
+      f32x4_t acc[8][4];
+#pragma unroll
       for (int j = 0; j < 8; ++j)
-  #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[j][i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      // activation fragments this thread copies: fragment f = w + 4 i (i = 0..7)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      // activation fragments this thread copies: fragment f = w + 8 i (i = 0..3)
       // covers row block f >> 1 and the 16-byte halves at 16 q_l (f even) or
-      // 64 + 16 q_l (f odd) of a 128-K step.  Offsets are 32-bit from the block's
-      // first row (256 rows of at most K bytes each).
-      uint32_t xoff[8];
-  #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int f = wave + 4 * i;
+      // 64 + 16 q_l (f odd) of a 128-K step
+      uint32_t xoff[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = wave + 8 * i;
         xoff[i] = xrow((f >> 1) * 16 + n_l) + 16 * q_l + 64 * (f & 1);
       }
       auto copy_x = [&](int64_t step, uint8_t* stage) {
         const uint8_t* src = xblk + step * 128;   // 128 fp8 per K step
-  #pragma unroll
-        for (int i = 0; i < 8; ++i) g2lds(src + xoff[i], stage + (wave + 4 * i) * 1024);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g2lds(src + xoff[i], stage + (wave + 8 * i) * 1024);
       };
-      const int wm = wave >> 1, wn = wave & 1;
-      // weight tiles and scale words this wave copies per stage: column blocks wave + 4 c
-      const uint8_t* wsrc[4];
-      const uint8_t* ssrc[4];
-  #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        int64_t nb = nb0 + wave + 4 * c;
+      // weight tiles and scale words this wave copies per stage: column blocks w and w + 8
+      const uint8_t* wsrc[2];
+      const uint8_t* ssrc[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        int64_t nb = nb0 + wave + 8 * c;
         if (nb >= G.NB) nb = G.NB - 1;
         wsrc[c] = a.w + (wbase + nb) * G.KG * 1024 + lane * 16;
         ssrc[c] = a.w + G.off_scales + (wbase + nb) * G.KG4 * 256 + lane * 4;
       }
       auto copy_stage = [&](int64_t s, uint8_t* st) {
         copy_x(s, st);
-  #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int cb = wave + 4 * c;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int cb = wave + 8 * c;
           g2lds(wsrc[c] + s * 1024, st + 32 * 1024 + cb * 1024);
           __builtin_amdgcn_global_load_lds(ssrc[c] + (s / 4) * 256, (lds_void_t*)(st + 48 * 1024 + cb * 256), 4, 0, 0);
         }
       };
-      constexpr int kPer = 16;                        // copies per wave per stage
+      constexpr int kPer = 8;                         // copies per wave per stage
       const int64_t S = G.KG;
       copy_stage(0, lds);
       if (S > 1) copy_stage(1, lds + SB);
       barrier_after(S > 1, std::integral_constant<int, kPer>());
-  #pragma nounroll
+#pragma nounroll
       for (int64_t s = 0; s < S; ++s) {
         const uint8_t* st = lds + (s % kBigStages) * SB;
         const bool issue = s + 2 < S;
@@ -212,41 +213,36 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
         const int sh = 8 * (int)(s & 3);
         u32x4_t wq[8];
         int wsc[8];
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int cb = wn * 8 + j;
           wq[j] = ld16(st + 32 * 1024 + cb * 1024 + lane * 16);
           wsc[j] = (int)((*reinterpret_cast<const uint32_t*>(st + 48 * 1024 + cb * 256 + lane * 4) >> sh) & 0xFF);
         }
-        // B fragments of row block i, read one row block ahead
-        u32x4_t b0 = ld16(st + (wm * 8 * 2 + 0) * 1024 + lane * 16);
-        u32x4_t b1 = ld16(st + (wm * 8 * 2 + 1) * 1024 + lane * 16);
-  #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          u32x4_t n0 = b0, n1 = b1;
-          if (i + 1 < 8) {
-            const int rb = wm * 8 + i + 1;
-            n0 = ld16(st + (rb * 2 + 0) * 1024 + lane * 16);
-            n1 = ld16(st + (rb * 2 + 1) * 1024 + lane * 16);
-          }
-  #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[j][i] = mfma_fp4_fp8(wq[j], b0, b1, acc[j][i], wsc[j], 127);
-          b0 = n0;
-          b1 = n1;
+        u32x4_t b0[4], b1[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rb = wm * 4 + i;
+          b0[i] = ld16(st + (rb * 2 + 0) * 1024 + lane * 16);
+          b1[i] = ld16(st + (rb * 2 + 1) * 1024 + lane * 16);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j][i] = mfma_fp4_fp8(wq[j], b0[i], b1[i], acc[j][i], wsc[j], 127);
         // the next stage was issued one step ago, this step's copies after it
         barrier_after(issue, std::integral_constant<int, kPer>());
       }
 
       // ---- epilogue: lane holds C[n = 16 nb + 4 q_l + r][row = 16 rb + n_l]
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the stages are reused
-  #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t lr = (wm * 8 + i) * 16 + n_l;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t lr = (wm * 4 + i) * 16 + n_l;
         const int64_t row = out_row(lr);
         if (row < 0) continue;
         const float rs = a.xs[in_row(lr)];
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int64_t nb = nb0 + wn * 8 + j;
           if (nb >= G.NB) continue;
@@ -408,7 +404,7 @@ static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
   const int tiles_n = (int)((a.G.NB + kBigCB - 1) / kBigCB);
   const int tiles_m = GROUPED ? 0 : (int)((a.M + kBigM - 1) / kBigM);
   const unsigned grid = GROUPED ? (unsigned)(grid_items > 0 ? grid_items : 1) : (unsigned)(tiles_n * tiles_m);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(MX ? 256 : 512), big_lds_bytes(MX), st, a, tiles_n, tiles_m);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), big_lds_bytes(MX), st, a, tiles_n, tiles_m);
   return hipGetLastError();
 }
 
