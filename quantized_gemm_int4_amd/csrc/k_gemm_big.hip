@@ -2,15 +2,18 @@
 // GEMM), where the ~2*M*N*K matrix multiply dominates (ywsung.com note "How
 // vLLM Humming computes 4 bits", section on one token vs many tokens).
 //
-// One block computes a 256 x 256 output tile.  Activations reach LDS through
-// 16-byte direct global-to-LDS loads laid out in MFMA fragment order (lane L
-// of a 1 KiB fragment at byte 16 L), so every operand read is one
-// conflict-free 1 KiB sweep.  Three LDS stages: copies run two K steps ahead.
-//   * W4A16 (K step 64, eight waves, two per SIMD): each wave owns 128 rows x
-//     64 columns as 32x32x16 bf16 MFMA blocks (128 accumulators per lane) and
-//     unpacks its columns' weights, copied into LDS one step ahead of the
-//     activations, to bf16 s * (u - z) after its MFMAs of the step, while the
-//     other wave of the SIMD multiplies.
+// One block computes a 256 x 256 output tile.  Activations and weights reach
+// LDS through 16-byte direct buffer-to-LDS loads; each activation copy reads
+// whole 128-byte lines (eight rows of one K step), which the L1 path moves
+// about three times faster than copies that gather 32 bytes from each of 32
+// rows.  The row-major activation stage is XOR-swizzled so that the MFMA
+// operand reads stay free of bank conflicts.  Three LDS stages: copies run
+// two K steps ahead.
+//   * W4A16 (K step 64, eight waves, two per SIMD): each wave owns all 256
+//     rows x 32 columns as 32x32x16 bf16 MFMA blocks (128 accumulators per
+//     lane) and unpacks its columns' weights, copied into LDS one step ahead
+//     of the activations, to bf16 s * (u - z) in between its MFMAs of the
+//     previous step.
 //   * W4A8-MXFP4 (K step 128, eight waves of 64 x 128): E2M1 weight tiles and
 //     their E8M0 scale words are copied to LDS too and fed as stored to the
 //     16x16x128 scaled MFMA; the per-token FP8 scale is applied in the
@@ -31,8 +34,23 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ void g2lds(const void* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_base, 16, 0, 0);
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over `bytes` bytes from `base` (reads at or past the end return
+// zero; larger extents are capped at the 32-bit maximum).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(uint32_t)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull), 0x00020000);
+}
+
+// Direct buffer-to-LDS copies: lane L's `n` bytes at base + voff + soff land at
+// lds_base + n L.  The buffer form (unlike the global one) leaves the
+// compiler's LDS wait counts exact for the reads that follow.
+__device__ __forceinline__ void b2lds16(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void b2lds4(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 4, voff, soff, 0, 0);
 }
 
 // Four consecutive outputs y[n..n+3] of one row as bf16 (one 8-byte store when aligned).
@@ -46,14 +64,35 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* yrow, int64_t N, int64_t 
   }
 }
 
+// Eight consecutive outputs y[n..n+7] of one row (one 16-byte store when aligned).
+__device__ __forceinline__ void store_bf16x8(uint16_t* yrow, int64_t N, int64_t n, u32x4_t v) {
+  if ((N & 7) == 0 && n + 7 < N) {
+    *reinterpret_cast<u32x4_t*>(yrow + n) = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (n + e < N) yrow[n + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
 __device__ __forceinline__ float ubyte_f(uint32_t x, int b) { return (float)((x >> (8 * b)) & 0xFFu); }
 
 // Eight codes of one device-layout word (value 2p in nibble p, 2p+1 in nibble
 // p+4) -> eight bf16 of s*u + zs (= s*(u - z), exact before the bf16 rounding)
 // in value order.
+// Word r of the result below from the masked bytes lo = w & 0x0F0F0F0F and
+// hi = (w >> 4) & 0x0F0F0F0F.
+__device__ __forceinline__ uint32_t dq8_word(uint32_t lo, uint32_t hi, int r, float s, float zs) {
+  const uint32_t x = (r & 1) ? hi : lo;
+  const int b0 = r >> 1;                         // bytes b0 and b0 + 2 of x
+  return pack_bf16(fmaf(ubyte_f(x, b0), s, zs), fmaf(ubyte_f(x, b0 + 2), s, zs));
+}
+
 __device__ __forceinline__ u32x4_t dq8_bytes(uint32_t w, float s, float zs) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;          // bytes: v0 v4 v1 v5
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // bytes: v2 v6 v3 v7
+  // opaque masks: otherwise the compiler folds mask and byte select into one
+  // bit-field extract per value instead of converting the masked bytes
+  const uint32_t lo = in_vgpr(w & 0x0F0F0F0Fu);          // bytes: v0 v4 v1 v5
+  const uint32_t hi = in_vgpr((w >> 4) & 0x0F0F0F0Fu);   // bytes: v2 v6 v3 v7
   u32x4_t r;
   r[0] = pack_bf16(fmaf(ubyte_f(lo, 0), s, zs), fmaf(ubyte_f(lo, 2), s, zs));
   r[1] = pack_bf16(fmaf(ubyte_f(hi, 0), s, zs), fmaf(ubyte_f(hi, 2), s, zs));
@@ -64,9 +103,13 @@ __device__ __forceinline__ u32x4_t dq8_bytes(uint32_t w, float s, float zs) {
 
 }  // namespace
 
+// first column block of expert e
+__device__ __forceinline__ int64_t wbase_of(int64_t e, const Geom& G) { return e * G.NB; }
+
 constexpr int kBigM = 256;        // rows per block
 constexpr int kBigCB = 16;        // 16-column blocks per block (256 columns)
 constexpr int kBigStages = 3;     // LDS stages: loads run two K steps ahead
+constexpr int kBigGrid = 256;     // persistent dense grid: one block per CU
 
 // LDS bytes of one stage: activation fragments (32 x 1 KiB) and the block's
 // 16 weight tiles (16 KiB), plus MXFP4: their E8M0 scale words (16 x 256 B);
@@ -74,142 +117,269 @@ constexpr int kBigStages = 3;     // LDS stages: loads run two K steps ahead
 __host__ __device__ constexpr int big_stage_bytes(bool mx) { return mx ? (32 + 16 + 4) * 1024 : (32 + 16 + 2) * 1024; }
 __host__ __device__ constexpr int big_lds_bytes(bool mx) { return kBigStages * big_stage_bytes(mx); }
 
-// Dense: one block per 256 x 256 tile.  Grouped (MoE): a persistent grid
-// walks (unit, 256-column tile) items; a unit is up to 256 rows of one
-// expert, whose activation rows are gathered through the sorted pair list
-// and whose outputs are written in pair order.
+// Unit swizzles of the epilogue slabs (8-byte units, 64 per 512-byte row),
+// chosen so that the accumulator writes of 32 lanes hit distinct banks:
+// W4A16 lanes write 32 rows of one unit, MXFP4 lanes 16 rows x 2 units.
+struct Swz16 {
+  __device__ static int swz(int r) { return r & 31; }
+};
+struct SwzMx {
+  __device__ static int swz(int r) { return 2 * (r & 15); }
+};
+
+// One 256 x 256 output tile: expert, first row (dense), first 16-column
+// block, valid rows (1..256) and, grouped, its first index into the sorted
+// pair list.
+struct BigTile {
+  int64_t e, m0, nb0, rows, first;
+};
+
+// What one thread's copies of a tile need: buffers over the tile's
+// activation rows and its 16 weight column blocks, and per-lane byte offsets.
+struct BigCopy {
+  rsrc_t rx, rw;
+  uint32_t xoff[4];   // activation copies (row offset + swizzled chunk)
+  uint32_t wvo[2];    // weight tile copies
+  uint32_t svo[2];    // MXFP4: scale words of the two tiles; INT4: scale / zero gather
+};
+
+// A persistent grid: block b takes tiles b, b + grid, b + 2 grid, ...  Dense
+// tiles are visited XCD by XCD: blocks are dispatched round-robin over the
+// eight XCDs, so item i runs on XCD i % 8 (the grid is a multiple of 8 or a
+// single round); each XCD walks a contiguous range of tiles in groups of four
+// tile rows, so the blocks sharing an XCD's L2 also share activation and
+// weight slices.  Grouped (MoE) items are (unit, 256-column tile) pairs; a
+// unit is up to 256 rows of one expert, whose activation rows are gathered
+// through the sorted pair list and whose outputs are written in pair order.
+//
+// With three or more K steps per tile the copies run on across tiles: the
+// last steps of a tile copy the first steps of the block's next tile, whose
+// MFMAs then start right after this tile's epilogue, and the output stores
+// drain while the next tile computes.
 template <bool MX, bool ZP, bool GROUPED>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   constexpr int SB = big_stage_bytes(MX);
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
-  __shared__ int64_t arow_s[GROUPED ? kBigM : 1];
-  __shared__ int64_t orow_s[GROUPED ? kBigM : 1];
+  __shared__ int32_t arow_s[GROUPED ? kBigM : 1];   // activation row of each local row
+  __shared__ int32_t orow_s[GROUPED ? kBigM : 1];   // output row, or -1 (not stored)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n_l = lane & 15, q_l = lane >> 4;
+  const int n_l = lane & 15, q_l = lane >> 4, l32 = lane & 31, hi = lane >> 5;
   const Geom G = a.G;
-  const int64_t K = G.K;
-  const int64_t row_bytes = MX ? K : 2 * K;
+  const int64_t row_bytes = MX ? G.K : 2 * G.K;
+  const int S = (int)(MX ? G.KG : 2 * G.KG);      // K steps per tile
+  const bool chained = S >= 3;
+  const int64_t n_items = GROUPED ? (int64_t)a.hdr[2] * tiles_n : (int64_t)tiles_n * tiles_m;
+  int64_t item = blockIdx.x;
+  if (item >= n_items) return;
 
-  const int64_t n_items = GROUPED ? (int64_t)a.hdr[2] * tiles_n : 1;
-  for (int64_t item = GROUPED ? blockIdx.x : 0; item < n_items; item += GROUPED ? gridDim.x : 1) {
-    int64_t e = 0, m0 = 0, nb0;
-    int64_t rows_left;                               // valid rows of this tile (>= 1)
+  auto decode = [&](int64_t it) -> BigTile {
+    BigTile t;
     if (GROUPED) {
-      const int32_t* u = a.units + 4 * (item / tiles_n);
-      e = u[0];
-      rows_left = u[2] < kBigM ? u[2] : kBigM;
-      nb0 = (item % tiles_n) * kBigCB;
-      if (tid < kBigM) {
-        int64_t ar = 0, orr = -1;   // invalid rows read row 0 (always present) and are not stored
-        if (tid < rows_left) {
-          const int64_t pair = a.sorted_pairs[u[1] + tid];
-          if (pair >= 0 && pair < a.P) {
-            orr = pair;
-            ar = a.rows_are_pairs ? pair : pair / a.topk;
-          }
-        }
-        arow_s[tid] = ar;
-        orow_s[tid] = orr;
-      }
-      __syncthreads();
+      const int32_t* u = a.units + 4 * (it / tiles_n);
+      t.e = u[0];
+      t.first = u[1];
+      t.rows = u[2] < kBigM ? u[2] : kBigM;
+      t.m0 = 0;
+      t.nb0 = (it % tiles_n) * kBigCB;
     } else {
-      // tile of this block (XCD-aware order, see the file comment)
       const int total = tiles_n * tiles_m;
-      const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+      const int xcd = (int)(it % 8), idx = (int)(it / 8);
       const int base = total / 8, extra = total % 8;
-      const int t = xcd * base + (xcd < extra ? xcd : extra) + idx;
+      const int tt = xcd * base + (xcd < extra ? xcd : extra) + idx;
       constexpr int GM = 4;
-      const int grp = t / (GM * tiles_n);
+      const int grp = tt / (GM * tiles_n);
       const int first_m = grp * GM;
       const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-      const int tin = t - grp * GM * tiles_n;
+      const int tin = tt - grp * GM * tiles_n;
       const int tm = first_m + tin % gm, tn = tin / gm;
-      m0 = (int64_t)tm * kBigM;
-      nb0 = (int64_t)tn * kBigCB;
-      rows_left = a.M - m0;
+      t.e = 0;
+      t.first = 0;
+      t.m0 = (int64_t)tm * kBigM;
+      t.nb0 = (int64_t)tn * kBigCB;
+      t.rows = (a.M - t.m0) < kBigM ? (a.M - t.m0) : kBigM;
     }
-    // activation bytes: dense offsets are relative to the tile's first row,
-    // grouped offsets to the start of A (the launcher checks they fit 32 bits)
-    const uint8_t* xblk = reinterpret_cast<const uint8_t*>(a.x) + m0 * row_bytes;
-    auto xrow = [&](int64_t r) -> uint32_t {         // local row -> byte offset from xblk
-      if (r >= rows_left) r = rows_left - 1;         // rows past the tile's end load a valid row, never stored
-      return (uint32_t)((GROUPED ? arow_s[r] : r) * row_bytes);
-    };
-    auto out_row = [&](int64_t r) -> int64_t {       // local row -> output row, or -1
-      if (r >= rows_left) return -1;
-      return GROUPED ? orow_s[r] : m0 + r;
-    };
-    auto in_row = [&](int64_t r) -> int64_t {        // local row -> activation row (for the A8 scale)
-      return GROUPED ? arow_s[r] : m0 + r;
-    };
-    const int64_t wbase = e * G.NB;                  // first column block of this expert
-    auto barrier_after = [&](bool exact, auto n_c) {
-      // wait for this wave's copies into the next stage (all but the n most
-      // recent vector-memory operations) and its LDS operations, then meet the
-      // other waves; the memory clobber keeps the compiler from moving LDS
-      // accesses across
-      constexpr int n = decltype(n_c)::value;
-      if (exact) __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
-      else __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    };
+    return t;
+  };
+  // grouped: activation row of a sorted pair (invalid pairs read row 0 and are not stored)
+  auto act_row = [&](int32_t pair) -> int64_t {
+    if (pair < 0 || pair >= a.P) return 0;
+    return a.rows_are_pairs ? pair : pair / a.topk;
+  };
+  // grouped: sorted pair of local row r, clamped to the tile
+  auto pair_of = [&](const BigTile& t, int r) -> int32_t {
+    return a.sorted_pairs[t.first + (r < t.rows ? r : t.rows - 1)];
+  };
 
-    if constexpr (MX) {
-      // ================================ W4A8-MXFP4: K step 128 = one K group;
-      // eight waves, two per SIMD: wave w owns rows 64 (w & 3) + 0..63 and
-      // columns 128 (w >> 2) + 0..127 (4 x 8 blocks of 16 x 16, 128
-      // accumulators per lane)
-      const int wm = wave & 3, wn = wave >> 2;
+  // Activations of one K step (128 bytes per row: 64 bf16 or 128 fp8) are
+  // staged row-major, 256 rows x 128 bytes, with 16-byte chunk c of row r in
+  // slot c ^ ((r >> 1) & 7), so that the 16 lanes of an operand read (16
+  // rows, one chunk each) hit all 64 banks once.  Copy j = 4 w + i (i =
+  // 0..3) of wave w covers rows 8 j .. 8 j + 7: lane L row 8 j + L / 8, slot
+  // L % 8, so every copy reads eight whole 128-byte lines.
+  const rsrc_t rsz = make_rsrc(a.w + G.off_scales, G.total - G.off_scales);
+  // INT4: lanes 0..15 gather bf16 scales (tile (L / 8) % 2, bytes 4 (L % 8)),
+  // lanes 16..19 zero-point words (tile (L / 2) % 2, word L % 2)
+  const bool zlane = !MX && ZP && lane >= 16 && lane < 20;
+  const uint32_t szstride = zlane ? 8 : 32;
+  auto make_copy = [&](const BigTile& t, const int32_t (&pr)[4]) -> BigCopy {
+    BigCopy c;
+    c.rx = make_rsrc(reinterpret_cast<const uint8_t*>(a.x) + t.m0 * row_bytes,
+                     GROUPED ? 0xFFFFFFFFull : (uint64_t)t.rows * row_bytes);
+    const int64_t wb = wbase_of(t.e, G);
+    c.rw = make_rsrc(a.w + (wb + t.nb0) * G.KG * 1024, (uint64_t)kBigCB * G.KG * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * (4 * wave + i) + (lane >> 3);
+      const int64_t src = GROUPED ? act_row(pr[i]) : (r < t.rows ? r : t.rows - 1);
+      c.xoff[i] = (uint32_t)(src * row_bytes) + 16 * ((lane & 7) ^ ((r >> 1) & 7));
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      int64_t nb = MX ? t.nb0 + wave + 8 * cc : t.nb0 + 2 * wave + cc;
+      if (nb >= G.NB) nb = G.NB - 1;
+      c.wvo[cc] = (uint32_t)((nb - t.nb0) * G.KG * 1024 + lane * 16);
+      c.svo[cc] = MX ? (uint32_t)((wb + nb) * G.KG4 * 256 + lane * 4) : 0u;
+    }
+    if (!MX) {
+      int64_t nbq = t.nb0 + 2 * wave + (zlane ? ((lane >> 1) & 1) : ((lane >> 3) & 1));
+      if (nbq >= G.NB) nbq = G.NB - 1;
+      c.svo[0] = (uint32_t)(zlane ? (G.off_zeros - G.off_scales) + (wb + nbq) * G.KG * 8 + (lane & 1) * 4
+                                  : (wb + nbq) * G.KG * 32 + (lane & 7) * 4);
+    }
+    return c;
+  };
+  // grouped: this thread's four copy rows of tile t, and its row of the tables
+  auto load_rows = [&](const BigTile& t, int32_t (&pr)[4], int32_t& tp) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = pair_of(t, 8 * (4 * wave + i) + (lane >> 3));
+    tp = (tid < t.rows) ? a.sorted_pairs[t.first + tid] : -1;
+  };
+  auto write_table = [&](int32_t tp) {
+    if (GROUPED && tid < kBigM) {
+      const bool ok = tp >= 0 && tp < a.P;
+      arow_s[tid] = (int32_t)act_row(tp);
+      orow_s[tid] = ok ? tp : -1;
+    }
+  };
+  // LDS offsets of the stages of the current step and the next two (the one
+  // after those is the current one again), rotated after every step
+  uint32_t so[3] = {0u, (uint32_t)SB, 2u * SB};
+  auto rotate = [&]() {
+    const uint32_t t = so[0];
+    so[0] = so[1];
+    so[1] = so[2];
+    so[2] = t;
+  };
+  auto copy_x = [&](const BigCopy& c, int ls, uint8_t* stg) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b2lds16(c.rx, c.xoff[i], (uint32_t)(ls * 128), stg + (4 * wave + i) * 1024);
+  };
+  auto wait_barrier = [&](auto n_c) {
+    // wait for this wave's copies except the n most recent vector-memory
+    // operations and for its LDS operations, then meet the other waves; the
+    // memory clobber keeps the compiler from moving LDS accesses across
+    __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(decltype(n_c)::value) : "memory");
+  };
+  auto local_row = [&](const BigTile& t, int64_t r, int64_t& out, int64_t& in) {
+    if (r >= t.rows) { out = -1; in = 0; return; }
+    out = GROUPED ? (int64_t)orow_s[r] : t.m0 + r;
+    in = GROUPED ? (int64_t)arow_s[r] : t.m0 + r;
+  };
+
+  // Epilogue through LDS: the tile leaves in four slabs of 64 rows, staged
+  // as bf16 in the activation part of the last step's stage (free until the
+  // next tile's first step), 512 bytes per row with 8-byte unit u of row r
+  // at unit u ^ g(r); each thread then stores 16-byte chunks, 32 lanes per
+  // row, so every store writes whole 128-byte lines.
+  auto store_slab = [&](const BigTile& t, const uint8_t* ost, int p, auto gfun) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 16 * k + (tid >> 5), c = tid & 31;
+      const int g = decltype(gfun)::swz(r);
+      const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(ost + r * 512 + ((2 * c) ^ g) * 8);
+      const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(ost + r * 512 + ((2 * c + 1) ^ g) * 8);
+      int64_t row, arow;
+      local_row(t, 64 * p + r, row, arow);
+      if (row >= 0) store_bf16x8(a.y + row * G.N, G.N, t.nb0 * 16 + 8 * c, (u32x4_t){v0[0], v0[1], v1[0], v1[1]});
+    }
+  };
+
+  BigTile cur = decode(item);
+  int32_t pr[4] = {0, 0, 0, 0}, tp = -1;
+  if (GROUPED) load_rows(cur, pr, tp);
+  BigCopy cc = make_copy(cur, pr);
+  bool first = true;
+
+  if constexpr (MX) {
+    // ================================ W4A8-MXFP4: K step 128 = one K group;
+    // eight waves, two per SIMD: wave w owns rows 64 (w & 3) + 0..63 and
+    // columns 128 (w >> 2) + 0..127 (4 x 8 blocks of 16 x 16, 128
+    // accumulators per lane)
+    const int wm = wave & 3, wn = wave >> 2;
+    // operand rows 16 rb + n_l: K chunks q_l and 4 + q_l (16 fp8 each)
+    const int xsw = (n_l >> 1) & 7;
+    const uint32_t xo0 = n_l * 128 + 16 * (q_l ^ xsw), xo1 = n_l * 128 + 16 * ((4 + q_l) ^ xsw);
+    // copies of one stage: activations, weight tiles (column blocks w and
+    // w + 8) and their scale words
+    auto copy_stage = [&](const BigCopy& c, int ls, uint8_t* st) {
+      copy_x(c, ls, st);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int cb = wave + 8 * k;
+        b2lds16(c.rw, c.wvo[k], (uint32_t)(ls * 1024), st + 32 * 1024 + cb * 1024);
+        b2lds4(rsz, c.svo[k], (uint32_t)((ls / 4) * 256), st + 48 * 1024 + cb * 256);
+      }
+    };
+    constexpr int kPer = 8;                         // copies per wave per stage
+    while (true) {
+      const int64_t nitem = item + gridDim.x;
+      const bool has_next = nitem < n_items;
+      const BigTile nxt = has_next ? decode(nitem) : cur;
+      int32_t prn[4] = {0, 0, 0, 0}, tpn = -1;
+      if (!chained || first) {
+        // stand-alone start: earlier copies and stores done, all waves past
+        // the previous epilogue
+        if (!first) {
+          __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          if (GROUPED) load_rows(cur, pr, tp);
+          cc = make_copy(cur, pr);
+        }
+        write_table(tp);
+        copy_stage(cc, 0, lds + so[0]);
+        if (S > 1) {
+          copy_stage(cc, 1, lds + so[1]);
+          wait_barrier(std::integral_constant<int, kPer>());
+        } else {
+          wait_barrier(std::integral_constant<int, 0>());
+        }
+      }
+      // the next tile's rows load before this tile's copies (done by the end of step 0)
+      if (GROUPED && chained && has_next) load_rows(nxt, prn, tpn);
+      BigCopy nc = cc;
+      if (!GROUPED && chained && has_next) nc = make_copy(nxt, prn);
+
       f32x4_t acc[8][4];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[j][i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      // activation fragments this thread copies: fragment f = w + 8 i (i = 0..3)
-      // covers row block f >> 1 and the 16-byte halves at 16 q_l (f even) or
-      // 64 + 16 q_l (f odd) of a 128-K step
-      uint32_t xoff[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = wave + 8 * i;
-        xoff[i] = xrow((f >> 1) * 16 + n_l) + 16 * q_l + 64 * (f & 1);
-      }
-      auto copy_x = [&](int64_t step, uint8_t* stage) {
-        const uint8_t* src = xblk + step * 128;   // 128 fp8 per K step
-#pragma unroll
-        for (int i = 0; i < 4; ++i) g2lds(src + xoff[i], stage + (wave + 8 * i) * 1024);
-      };
-      // weight tiles and scale words this wave copies per stage: column blocks w and w + 8
-      const uint8_t* wsrc[2];
-      const uint8_t* ssrc[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        int64_t nb = nb0 + wave + 8 * c;
-        if (nb >= G.NB) nb = G.NB - 1;
-        wsrc[c] = a.w + (wbase + nb) * G.KG * 1024 + lane * 16;
-        ssrc[c] = a.w + G.off_scales + (wbase + nb) * G.KG4 * 256 + lane * 4;
-      }
-      auto copy_stage = [&](int64_t s, uint8_t* st) {
-        copy_x(s, st);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int cb = wave + 8 * c;
-          g2lds(wsrc[c] + s * 1024, st + 32 * 1024 + cb * 1024);
-          __builtin_amdgcn_global_load_lds(ssrc[c] + (s / 4) * 256, (lds_void_t*)(st + 48 * 1024 + cb * 256), 4, 0, 0);
-        }
-      };
-      constexpr int kPer = 8;                         // copies per wave per stage
-      const int64_t S = G.KG;
-      copy_stage(0, lds);
-      if (S > 1) copy_stage(1, lds + SB);
-      barrier_after(S > 1, std::integral_constant<int, kPer>());
 #pragma nounroll
-      for (int64_t s = 0; s < S; ++s) {
-        const uint8_t* st = lds + (s % kBigStages) * SB;
-        const bool issue = s + 2 < S;
-        if (issue) copy_stage(s + 2, lds + ((s + 2) % kBigStages) * SB);
+      for (int s = 0; s < S; ++s) {
+        if (GROUPED && chained && s == 1) {
+          write_table(tp);
+          if (has_next) nc = make_copy(nxt, prn);
+        }
+        const uint8_t* st = lds + so[0];
+        // copies for step s + 2: this tile's, the next tile's, or (none left)
+        // a repeat of the last one into a stage no longer read
+        const int t2 = s + 2;
+        uint8_t* d2 = lds + so[2];
+        if (t2 < S) copy_stage(cc, t2, d2);
+        else if (chained && has_next) copy_stage(nc, t2 - S, d2);
+        else copy_stage(cc, S - 1, d2);
         const int sh = 8 * (int)(s & 3);
         u32x4_t wq[8];
         int wsc[8];
@@ -223,176 +393,232 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rb = wm * 4 + i;
-          b0[i] = ld16(st + (rb * 2 + 0) * 1024 + lane * 16);
-          b1[i] = ld16(st + (rb * 2 + 1) * 1024 + lane * 16);
+          b0[i] = ld16(st + rb * 2048 + xo0);
+          b1[i] = ld16(st + rb * 2048 + xo1);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 8; ++j) acc[j][i] = mfma_fp4_fp8(wq[j], b0[i], b1[i], acc[j][i], wsc[j], 127);
         // the next stage was issued one step ago, this step's copies after it
-        barrier_after(issue, std::integral_constant<int, kPer>());
+        wait_barrier(std::integral_constant<int, kPer>());
+        rotate();
       }
 
-      // ---- epilogue: lane holds C[n = 16 nb + 4 q_l + r][row = 16 rb + n_l]
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the stages are reused
+      // ---- epilogue: lane holds C[n = 16 nb + 4 q_l + r][row = 16 rb + n_l];
+      // slab p holds the rows of the two waves with wm = p; the copies still
+      // in flight finish first (the stores then never overtake a copy)
+      float rs[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t lr = (wm * 4 + i) * 16 + n_l;
-        const int64_t row = out_row(lr);
-        if (row < 0) continue;
-        const float rs = a.xs[in_row(lr)];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int64_t nb = nb0 + wn * 8 + j;
-          if (nb >= G.NB) continue;
-          store_bf16x4(a.y + row * G.N, G.N, nb * 16 + 4 * q_l, acc[j][i] * rs);
-        }
+        int64_t row, arow;
+        local_row(cur, (wm * 4 + i) * 16 + n_l, row, arow);
+        rs[i] = a.xs[arow];
       }
-    } else {
-      // ================================ W4A16: K step 64 = half a K group;
-      // eight waves, two per SIMD: wave w owns rows 128 (w & 1) + 0..127 and
-      // columns 64 (w >> 1) + 0..63 as 2 x 4 blocks of 32 x 32
-      // (v_mfma_f32_32x32x16_bf16; unlike the 16x16x32 form it keeps the
-      // matrix core busy).  Each wave unpacks the weights of its 64 columns
-      // into MFMA operands after its MFMAs of the step; the other wave on the
-      // SIMD multiplies meanwhile.  32x32x16 operands: A row / B column =
-      // lane % 32, K = 8 (lane / 32) + 0..7; result: column lane % 32, rows
-      // 8 j + 4 (lane / 32) + r in register 4 j + r.
-      const int wm = wave & 1, wn = wave >> 1;
-      f32x16_t acc[2][4];
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      uint8_t* ost = lds + so[2];                    // the last step's stage
+      for (int p = 0; p < 4; ++p) {
+        if (wm == p) {
 #pragma unroll
-      for (int nb2 = 0; nb2 < 2; ++nb2)
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * i + n_l;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[nb2][mb][r] = 0.f;
-      const int l32 = lane & 31, hi = lane >> 5;
-      // activation fragments: fragment f = 4 mb + kq (row block of 32, K part
-      // of 16); wave w copies K part w & 3 of row blocks 4 (w >> 2) + 0..3
-      uint32_t xoff[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int mb = 4 * (wave >> 2) + i;
-        xoff[i] = xrow(mb * 32 + l32) + 2 * (16 * (wave & 3) + 8 * hi);
-      }
-      auto copy_x = [&](int64_t step, uint8_t* stg) {
-        const uint8_t* src = xblk + step * 128;     // 64 bf16 per K step
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          g2lds(src + xoff[i], stg + ((4 * (wave >> 2) + i) * 4 + (wave & 3)) * 1024);
-      };
-      // Weight tiles of the block's 16 column blocks: wave w copies tiles
-      // 4 wn + 2 wm + {0, 1}; wave wm = 0 also copies its column quarter's
-      // bf16 scales (lane L: tile L / 8 of the quarter, bytes 4 (L % 8)), wave
-      // wm = 1 the zero-point words (lane L: tile (L / 2) % 4, word L % 2).
-      // Lanes past the useful ones repeat in-range addresses into unused bytes.
-      const uint8_t* wsrc[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        int64_t nb = nb0 + 4 * wn + 2 * wm + c;
-        if (nb >= G.NB) nb = G.NB - 1;
-        wsrc[c] = a.w + (wbase + nb) * G.KG * 1024 + lane * 16;
-      }
-      const int sz_c = wm == 0 ? ((lane >> 3) & 3) : ((lane >> 1) & 3);
-      int64_t nbq = nb0 + 4 * wn + sz_c;
-      if (nbq >= G.NB) nbq = G.NB - 1;
-      const uint8_t* szsrc = wm == 0 ? a.w + G.off_scales + (wbase + nbq) * G.KG * 32 + (lane & 7) * 4
-                                     : a.w + G.off_zeros + (wbase + nbq) * G.KG * 8 + (lane & 1) * 4;
-      const int64_t szstride = wm == 0 ? 32 : 8;
-      constexpr int kWOff = 32 * 1024, kSOff = 48 * 1024, kZOff = 49 * 1024;
-      // weights of K step s (group s / 2) into the weight part of stage s % 3
-      auto copy_w = [&](int64_t s, uint8_t* stg) {
-        const int64_t g = s >> 1;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) g2lds(wsrc[c] + g * 1024, stg + kWOff + (4 * wn + 2 * wm + c) * 1024);
-        if (wm == 0 || ZP)
-          __builtin_amdgcn_global_load_lds(szsrc + g * szstride,
-                                           (lds_void_t*)(stg + (wm == 0 ? kSOff : kZOff) + wn * 256), 4, 0, 0);
-      };
-      // copies per wave per step: 4 + 2 + 1, except the zero-point copy is
-      // missing for symmetric weights on waves wm = 1; the wait below uses the
-      // smaller count (waiting for one more copy than needed is harmless)
-      constexpr int kPer = 4 + 2 + (ZP ? 1 : 0);
-      // A operands of one step: 32-column block nb2, K part kq.  Lane row n =
-      // 32 nb2 + l32 of the quarter lies in tile 4 wn + 2 nb2 + l32 / 16 at
-      // column l32 % 16; K = 64 h + 16 kq + 8 hi is word 2 h + kq / 2 of slot
-      // (l32 % 16) + 16 ((2 kq + hi) % 4) of that tile.
-      u32x4_t af[2][4];
-      auto unpack_from = [&](const uint8_t* stg, int h) {
-#pragma unroll
-        for (int nb2 = 0; nb2 < 2; ++nb2) {
-          const int c = 2 * nb2 + (l32 >> 4), c16 = l32 & 15;
-          const uint8_t* tile = stg + kWOff + (4 * wn + c) * 1024;
-          const float sv = bf16_to_f32(*reinterpret_cast<const uint16_t*>(stg + kSOff + wn * 256 + c * 32 + c16 * 2));
-          const uint32_t zw = ZP ? *reinterpret_cast<const uint32_t*>(stg + kZOff + wn * 256 + c * 8 + (c16 >> 3) * 4) : 0u;
-          const float z = ZP ? (float)((zw >> (4 * (c16 & 7))) & 0xFu) : 8.0f;
-          const float zs = -z * sv;
-#pragma unroll
-          for (int kq = 0; kq < 4; ++kq) {
-            const int slot = c16 + 16 * ((2 * kq + hi) & 3);
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + slot * 16 + 4 * (2 * h + (kq >> 1)));
-            af[nb2][kq] = dq8_bytes(w, sv, zs);
+            for (int j = 0; j < 8; ++j) {
+              const f32x4_t v = acc[j][i] * rs[i];
+              const int u = 32 * wn + 4 * j + q_l;
+              *reinterpret_cast<u32x2_t*>(ost + r * 512 + (u ^ SwzMx::swz(r)) * 8) =
+                  (u32x2_t){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+            }
           }
         }
-      };
-      const int64_t S = 2 * G.KG;
-      auto stage = [&](int64_t s) { return lds + (s % kBigStages) * SB; };
-      // prologue: weights of steps 0, 1, 2 and activations of steps 0, 1 (their
-      // stages), operands of step 0
-      copy_w(0, stage(0));
-      copy_w(std::min<int64_t>(1, S - 1), stage(1));
-      copy_w(std::min<int64_t>(2, S - 1), stage(2));
-      copy_x(0, stage(0));
-      copy_x(std::min<int64_t>(1, S - 1), stage(1));
-      __syncthreads();
-      unpack_from(stage(0), 0);
-      // Step s multiplies stage s % 3 with operands af, then unpacks the
-      // operands of step s + 1 from stage s + 1.  It first issues the
-      // activations of step s + 2 and the weights of step s + 3.  No branches:
-      // near the end the copies repeat the last step into parts no longer read,
-      // so every step issues the same copies and the wait count is exact.
-#pragma nounroll
-      for (int64_t s = 0; s < S; ++s) {
-        copy_x(std::min<int64_t>(s + 2, S - 1), stage(s + 2));
-        copy_w(std::min<int64_t>(s + 3, S - 1), stage(s + 3));
-        const uint8_t* stg = stage(s);
-        // each accumulator takes its four K parts back to back (clustered
-        // updates keep the register allocation in place)
+        wait_barrier(std::integral_constant<int, 0>());
+        store_slab(cur, ost, p, SwzMx());
+        wait_barrier(std::integral_constant<int, 0>());
+      }
+      if (!has_next) break;
+      cur = nxt;
+      cc = nc;
+      tp = tpn;
+      item = nitem;
+      first = false;
+    }
+  } else {
+    // ================================ W4A16: K step 64 = half a K group;
+    // eight waves, two per SIMD: wave w owns columns 32 w + 0..31 and all
+    // 256 rows as eight 32 x 32 blocks (v_mfma_f32_32x32x16_bf16, 128
+    // accumulators per lane), so every weight is unpacked by one wave only.
+    // 32x32x16 operands: A row / B column = lane % 32, K = 8 (lane / 32) +
+    // 0..7; result: column lane % 32, rows 8 j + 4 (lane / 32) + r in
+    // register 4 j + r.  The unpacking of the next step's operands is
+    // interleaved with this step's MFMAs, so it runs on the vector ALU while
+    // the matrix core works.
+    // operand rows 32 mb + l32, K part kq: chunk 2 kq + hi (8 bf16)
+    const int xsw = (l32 >> 1) & 7;
+    uint32_t xo[4];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const uint8_t* fr = stg + ((4 * wm + mb) * 4) * 1024 + lane * 16;
-          u32x4_t b[4];
+    for (int kq = 0; kq < 4; ++kq) xo[kq] = l32 * 128 + 16 * ((2 * kq + hi) ^ xsw);
+    // Wave w copies its own two weight tiles (column blocks 2 w, 2 w + 1) and
+    // one 4-byte-per-lane gather of their scales and zero points into its
+    // 256-byte slot at kSOff + 256 w.
+    constexpr int kWOff = 32 * 1024, kSOff = 48 * 1024;
+    // weights of K step ls (group ls / 2) into the weight part of a stage
+    auto copy_w = [&](const BigCopy& c, int ls, uint8_t* stg) {
+      const int g = ls >> 1;
 #pragma unroll
-          for (int kq = 0; kq < 4; ++kq) b[kq] = ld16(fr + kq * 1024);
+      for (int k = 0; k < 2; ++k) b2lds16(c.rw, c.wvo[k], (uint32_t)(g * 1024), stg + kWOff + (2 * wave + k) * 1024);
+      b2lds4(rsz, c.svo[0] + (uint32_t)g * szstride, 0u, stg + kSOff + wave * 256);
+    };
+    constexpr int kPer = 4 + 2 + 1;                 // copies per wave per step
+    // A operands of one step: K part kq.  Lane row n = 32 w + l32 lies in
+    // tile 2 w + l32 / 16 at column l32 % 16; K = 64 h + 16 kq + 8 hi is
+    // word 2 h + kq / 2 of slot (l32 % 16) + 16 ((2 kq + hi) % 4).
+    const int c_l = l32 >> 4, c16 = l32 & 15;
+    auto fetch = [&](const uint8_t* stg, int h, uint32_t (&wv)[4], float& sv, float& zs) {
+      const uint8_t* tile = stg + kWOff + (2 * wave + c_l) * 1024;
 #pragma unroll
-          for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-            for (int nb2 = 0; nb2 < 2; ++nb2) acc[nb2][mb] = mfma32_bf16(af[nb2][kq], b[kq], acc[nb2][mb]);
+      for (int kq = 0; kq < 4; ++kq)
+        wv[kq] = *reinterpret_cast<const uint32_t*>(tile + (c16 + 16 * ((2 * kq + hi) & 3)) * 16 + 4 * (2 * h + (kq >> 1)));
+      const uint8_t* sz = stg + kSOff + wave * 256;
+      sv = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sz + c_l * 32 + c16 * 2));
+      const uint32_t zw = ZP ? *reinterpret_cast<const uint32_t*>(sz + 64 + c_l * 8 + (c16 >> 3) * 4) : 0u;
+      const float z = ZP ? (float)((zw >> (4 * (c16 & 7))) & 0xFu) : 8.0f;
+      zs = -z * sv;
+    };
+    u32x4_t af[4];
+    uint32_t w3c = 0;                               // code word of operand 3, its scale and offset
+    float sv3c = 0.f, zs3c = 0.f;
+    while (true) {
+      const int64_t nitem = item + gridDim.x;
+      const bool has_next = nitem < n_items;
+      const BigTile nxt = has_next ? decode(nitem) : cur;
+      int32_t prn[4] = {0, 0, 0, 0}, tpn = -1;
+      if (!chained || first) {
+        // stand-alone start: weights of steps 0, 1, 2 and activations of
+        // steps 0, 1, then operands 0..2 of step 0
+        if (!first) {
+          __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          if (GROUPED) load_rows(cur, pr, tp);
+          cc = make_copy(cur, pr);
         }
-        unpack_from(stage(s + 1), (int)((s + 1) & 1));
+        write_table(tp);
+        copy_w(cc, 0, lds + so[0]);
+        copy_w(cc, std::min(1, S - 1), lds + so[1]);
+        copy_w(cc, std::min(2, S - 1), lds + so[2]);
+        copy_x(cc, 0, lds + so[0]);
+        copy_x(cc, std::min(1, S - 1), lds + so[1]);
+        wait_barrier(std::integral_constant<int, 0>());
+        uint32_t wv[4];
+        fetch(lds + so[0], 0, wv, sv3c, zs3c);
+#pragma unroll
+        for (int kq = 0; kq < 3; ++kq) af[kq] = dq8_bytes(wv[kq], sv3c, zs3c);
+        af[3] = (u32x4_t){0u, 0u, 0u, 0u};
+        w3c = wv[3];
+      }
+      if (GROUPED && chained && has_next) load_rows(nxt, prn, tpn);
+      BigCopy nc = cc;
+      if (!GROUPED && chained && has_next) nc = make_copy(nxt, prn);
+
+      f32x16_t acc[8];
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+      // Step s runs its 32 MFMAs K part by K part (kq = 0..3, row blocks
+      // 0..7 each, so no accumulator is updated twice in a row) with the
+      // activation fragments read kD MFMAs ahead.  Operand kq is free once
+      // its eight MFMAs are issued, so the unpacking follows behind: during
+      // K part 0 operand 3 of this step (from the word carried over), during
+      // K part kq = 1..3 operand kq - 1 of the next step (this tile's or, at
+      // the last step, the next tile's first), one result word per two MFMAs.
+      // The scheduling barriers keep this interleaving as written.  Each step
+      // first issues the activations of step s + 2 and the weights of step
+      // s + 3 (of this tile or the next, else repeats of this tile's last
+      // step into parts no longer read), so the wait count is exact.
+      constexpr int kD = 4;
+#pragma nounroll
+      for (int s = 0; s < S; ++s) {
+        if (GROUPED && chained && s == 1) {
+          write_table(tp);
+          if (has_next) nc = make_copy(nxt, prn);
+        }
+        // activations of step s + 2 into stage so[2], weights of step s + 3
+        // into the weight part of this step's stage so[0] (read one step ago)
+        const int t2 = s + 2, t3 = s + 3;
+        uint8_t* d2 = lds + so[2];
+        uint8_t* d3 = lds + so[0];
+        if (t2 < S) copy_x(cc, t2, d2);
+        else if (chained && has_next) copy_x(nc, t2 - S, d2);
+        else copy_x(cc, S - 1, d2);
+        if (t3 < S) copy_w(cc, t3, d3);
+        else if (chained && has_next) copy_w(nc, t3 - S, d3);
+        else copy_w(cc, S - 1, d3);
+        const uint8_t* xs = lds + so[0];
+        uint32_t wv[4];
+        float svn, zsn;
+        fetch(lds + so[1], (s + 1) & 1, wv, svn, zsn);
+        u32x4_t b[32];
+#pragma unroll
+        for (int i = 0; i < kD; ++i) b[i] = ld16(xs + (i & 7) * 4096 + xo[i >> 3]);
+        uint32_t lo = 0, hi4 = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int kq = i >> 3, mb = i & 7;
+          acc[mb] = mfma32_bf16(af[kq], b[i], acc[mb]);
+          if (i + kD < 32) {
+            const int j = i + kD;
+            b[j] = ld16(xs + (j & 7) * 4096 + xo[j >> 3]);
+          }
+          if (i & 1) {
+            const int u = (i & 7) >> 1;               // result word of the operand being unpacked
+            const uint32_t w = kq == 0 ? w3c : wv[kq - 1];
+            const float sv = kq == 0 ? sv3c : svn, zs = kq == 0 ? zs3c : zsn;
+            if (u == 0) {
+              lo = in_vgpr(w & 0x0F0F0F0Fu);
+              hi4 = in_vgpr((w >> 4) & 0x0F0F0F0Fu);
+            }
+            af[(kq + 3) & 3][u] = dq8_word(lo, hi4, u, sv, zs);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        w3c = wv[3];
+        sv3c = svn;
+        zs3c = zsn;
         // stage s + 1 (activations) came one step earlier, weights two; after
         // them only this step's copies
-        __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPer) : "memory");
+        wait_barrier(std::integral_constant<int, kPer>());
+        rotate();
       }
 
-      // ---- epilogue: lane holds C[n = 64 wn + 32 nb2 + 8 j + 4 hi + r][row = 128 wm + 32 mb + l32]
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the stages are reused
+      // ---- epilogue: lane holds C[n = 32 w + 8 j + 4 hi + r][row = 32 mb + l32];
+      // slab p holds row blocks 2 p and 2 p + 1 of every wave; the copies still
+      // in flight finish first (the stores then never overtake a copy)
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      uint8_t* ost = lds + so[2];                    // the last step's stage
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int64_t row = out_row(128 * wm + mb * 32 + l32);
-        if (row < 0) continue;
+      for (int p = 0; p < 4; ++p) {
 #pragma unroll
-        for (int nb2 = 0; nb2 < 2; ++nb2)
+        for (int mm = 0; mm < 2; ++mm) {
+          const int mb = 2 * p + mm, r = 32 * mm + l32;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const f32x4_t v = {acc[nb2][mb][4 * j], acc[nb2][mb][4 * j + 1], acc[nb2][mb][4 * j + 2], acc[nb2][mb][4 * j + 3]};
-            store_bf16x4(a.y + row * G.N, G.N, nb0 * 16 + wn * 64 + nb2 * 32 + 8 * j + 4 * hi, v);
+            const int u = 8 * wave + 2 * j + hi;
+            *reinterpret_cast<u32x2_t*>(ost + r * 512 + (u ^ Swz16::swz(r)) * 8) =
+                (u32x2_t){pack_bf16(acc[mb][4 * j], acc[mb][4 * j + 1]), pack_bf16(acc[mb][4 * j + 2], acc[mb][4 * j + 3])};
           }
+        }
+        wait_barrier(std::integral_constant<int, 0>());
+        store_slab(cur, ost, p, Swz16());
+        wait_barrier(std::integral_constant<int, 0>());
       }
+      if (!has_next) break;
+      cur = nxt;
+      cc = nc;
+      tp = tpn;
+      item = nitem;
+      first = false;
     }
-    __syncthreads();  // row tables and LDS stages are reused by the next item
   }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the block ends
 }
 
 template <bool MX, bool ZP, bool GROUPED>
@@ -403,7 +629,11 @@ static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
   if (attr_err != hipSuccess) return attr_err;
   const int tiles_n = (int)((a.G.NB + kBigCB - 1) / kBigCB);
   const int tiles_m = GROUPED ? 0 : (int)((a.M + kBigM - 1) / kBigM);
-  const unsigned grid = GROUPED ? (unsigned)(grid_items > 0 ? grid_items : 1) : (unsigned)(tiles_n * tiles_m);
+  // dense: one round of tiles, or a persistent grid of one block per CU
+  // (a multiple of 8, so a block's items stay on its XCD)
+  const int64_t tiles = (int64_t)tiles_n * tiles_m;
+  const unsigned grid = GROUPED ? (unsigned)(grid_items > 0 ? grid_items : 1)
+                                : (unsigned)(tiles <= kBigGrid ? tiles : kBigGrid);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(512), big_lds_bytes(MX), st, a, tiles_n, tiles_m);
   return hipGetLastError();
 }
@@ -411,6 +641,8 @@ static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
 int64_t big_n_tiles(const Geom& G) { return (G.NB + kBigCB - 1) / kBigCB; }
 
 hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
+  // scale and zero-point copies use 32-bit offsets from the scale region
+  if (a.G.total - a.G.off_scales > 0xFFFFFFFFull) return hipErrorInvalidValue;
   if (a.wfmt == W_MXFP4)
     return grouped ? go_big<true, false, true>(a, grid_items, st) : go_big<true, false, false>(a, 0, st);
   if (a.wfmt == W_UINT4_ZP)
