@@ -116,6 +116,8 @@ constexpr int kBigGrid = 256;     // persistent dense grid: one block per CU
 // INT4: per wave 256 B of bf16 scales and 256 B of zero-point words.
 __host__ __device__ constexpr int big_stage_bytes(bool mx) { return mx ? (32 + 16 + 4) * 1024 : (32 + 16 + 2) * 1024; }
 __host__ __device__ constexpr int big_lds_bytes(bool mx) { return kBigStages * big_stage_bytes(mx); }
+// MXFP4: eight waves (two per SIMD); W4A16: four (one per SIMD, 256 accumulators each)
+__host__ __device__ constexpr int big_threads(bool mx) { return mx ? 512 : 256; }
 
 // Unit swizzles of the epilogue slabs (8-byte units, 64 per 512-byte row),
 // chosen so that the accumulator writes of 32 lanes hit distinct banks:
@@ -136,10 +138,11 @@ struct BigTile {
 
 // What one thread's copies of a tile need: buffers over the tile's
 // activation rows and its 16 weight column blocks, and per-lane byte offsets.
+template <int NX, int NWT>
 struct BigCopy {
   rsrc_t rx, rw;
-  uint32_t xoff[4];   // activation copies (row offset + swizzled chunk)
-  uint32_t wvo[2];    // weight tile copies
+  uint32_t xoff[NX];  // activation copies (row offset + swizzled chunk)
+  uint32_t wvo[NWT];  // weight tile copies
   uint32_t svo[2];    // MXFP4: scale words of the two tiles; INT4: scale / zero gather
 };
 
@@ -157,9 +160,13 @@ struct BigCopy {
 // MFMAs then start right after this tile's epilogue, and the output stores
 // drain while the next tile computes.
 template <bool MX, bool ZP, bool GROUPED>
-__global__ void __launch_bounds__(512, 1)
+__global__ void __launch_bounds__(big_threads(MX), 1)
 k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   constexpr int SB = big_stage_bytes(MX);
+  constexpr int NW = big_threads(MX) / 64;         // waves
+  constexpr int NX = 32 / NW;                      // activation copies per lane per step
+  constexpr int NWT = 16 / NW;                     // weight tiles copied per wave per step
+  typedef BigCopy<NX, NWT> Copy;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   __shared__ int32_t arow_s[GROUPED ? kBigM : 1];   // activation row of each local row
   __shared__ int32_t orow_s[GROUPED ? kBigM : 1];   // output row, or -1 (not stored)
@@ -216,45 +223,47 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   // Activations of one K step (128 bytes per row: 64 bf16 or 128 fp8) are
   // staged row-major, 256 rows x 128 bytes, with 16-byte chunk c of row r in
   // slot c ^ ((r >> 1) & 7), so that the 16 lanes of an operand read (16
-  // rows, one chunk each) hit all 64 banks once.  Copy j = 4 w + i (i =
-  // 0..3) of wave w covers rows 8 j .. 8 j + 7: lane L row 8 j + L / 8, slot
+  // rows, one chunk each) hit all 64 banks once.  Copy j = NX w + i (i <
+  // NX) of wave w covers rows 8 j .. 8 j + 7: lane L row 8 j + L / 8, slot
   // L % 8, so every copy reads eight whole 128-byte lines.
   const rsrc_t rsz = make_rsrc(a.w + G.off_scales, G.total - G.off_scales);
-  // INT4: lanes 0..15 gather bf16 scales (tile (L / 8) % 2, bytes 4 (L % 8)),
-  // lanes 16..19 zero-point words (tile (L / 2) % 2, word L % 2)
-  const bool zlane = !MX && ZP && lane >= 16 && lane < 20;
+  // INT4: lanes 0..31 gather the bf16 scales of the wave's four column blocks
+  // (tile (L / 8) % 4, bytes 4 (L % 8)), lanes 32..39 their zero-point words
+  // (tile (L / 2) % 4, word L % 2)
+  const bool zlane = !MX && ZP && lane >= 32 && lane < 40;
   const uint32_t szstride = zlane ? 8 : 32;
-  auto make_copy = [&](const BigTile& t, const int32_t (&pr)[4]) -> BigCopy {
-    BigCopy c;
+  auto make_copy = [&](const BigTile& t, const int32_t (&pr)[NX]) -> Copy {
+    Copy c;
     c.rx = make_rsrc(reinterpret_cast<const uint8_t*>(a.x) + t.m0 * row_bytes,
                      GROUPED ? 0xFFFFFFFFull : (uint64_t)t.rows * row_bytes);
     const int64_t wb = wbase_of(t.e, G);
     c.rw = make_rsrc(a.w + (wb + t.nb0) * G.KG * 1024, (uint64_t)kBigCB * G.KG * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 8 * (4 * wave + i) + (lane >> 3);
+    for (int i = 0; i < NX; ++i) {
+      const int r = 8 * (NX * wave + i) + (lane >> 3);
       const int64_t src = GROUPED ? act_row(pr[i]) : (r < t.rows ? r : t.rows - 1);
       c.xoff[i] = (uint32_t)(src * row_bytes) + 16 * ((lane & 7) ^ ((r >> 1) & 7));
     }
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      int64_t nb = MX ? t.nb0 + wave + 8 * cc : t.nb0 + 2 * wave + cc;
+    for (int k = 0; k < NWT; ++k) {
+      int64_t nb = MX ? t.nb0 + wave + 8 * k : t.nb0 + NWT * wave + k;
       if (nb >= G.NB) nb = G.NB - 1;
-      c.wvo[cc] = (uint32_t)((nb - t.nb0) * G.KG * 1024 + lane * 16);
-      c.svo[cc] = MX ? (uint32_t)((wb + nb) * G.KG4 * 256 + lane * 4) : 0u;
+      c.wvo[k] = (uint32_t)((nb - t.nb0) * G.KG * 1024 + lane * 16);
+      if (MX) c.svo[k & 1] = (uint32_t)((wb + nb) * G.KG4 * 256 + lane * 4);
     }
     if (!MX) {
-      int64_t nbq = t.nb0 + 2 * wave + (zlane ? ((lane >> 1) & 1) : ((lane >> 3) & 1));
+      c.svo[1] = 0u;
+      int64_t nbq = t.nb0 + NWT * wave + (zlane ? ((lane >> 1) & 3) : ((lane >> 3) & 3));
       if (nbq >= G.NB) nbq = G.NB - 1;
       c.svo[0] = (uint32_t)(zlane ? (G.off_zeros - G.off_scales) + (wb + nbq) * G.KG * 8 + (lane & 1) * 4
                                   : (wb + nbq) * G.KG * 32 + (lane & 7) * 4);
     }
     return c;
   };
-  // grouped: this thread's four copy rows of tile t, and its row of the tables
-  auto load_rows = [&](const BigTile& t, int32_t (&pr)[4], int32_t& tp) {
+  // grouped: this thread's copy rows of tile t, and its row of the tables
+  auto load_rows = [&](const BigTile& t, int32_t (&pr)[NX], int32_t& tp) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = pair_of(t, 8 * (4 * wave + i) + (lane >> 3));
+    for (int i = 0; i < NX; ++i) pr[i] = pair_of(t, 8 * (NX * wave + i) + (lane >> 3));
     tp = (tid < t.rows) ? a.sorted_pairs[t.first + tid] : -1;
   };
   auto write_table = [&](int32_t tp) {
@@ -273,9 +282,9 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
     so[1] = so[2];
     so[2] = t;
   };
-  auto copy_x = [&](const BigCopy& c, int ls, uint8_t* stg) {
+  auto copy_x = [&](const Copy& c, int ls, uint8_t* stg) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b2lds16(c.rx, c.xoff[i], (uint32_t)(ls * 128), stg + (4 * wave + i) * 1024);
+    for (int i = 0; i < NX; ++i) b2lds16(c.rx, c.xoff[i], (uint32_t)(ls * 128), stg + (NX * wave + i) * 1024);
   };
   auto wait_barrier = [&](auto n_c) {
     // wait for this wave's copies except the n most recent vector-memory
@@ -295,9 +304,10 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   // at unit u ^ g(r); each thread then stores 16-byte chunks, 32 lanes per
   // row, so every store writes whole 128-byte lines.
   auto store_slab = [&](const BigTile& t, const uint8_t* ost, int p, auto gfun) {
+    constexpr int RS = 2 * NW;                     // rows per sweep of the block
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r = 16 * k + (tid >> 5), c = tid & 31;
+    for (int k = 0; k < 64 / RS; ++k) {
+      const int r = RS * k + (tid >> 5), c = tid & 31;
       const int g = decltype(gfun)::swz(r);
       const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(ost + r * 512 + ((2 * c) ^ g) * 8);
       const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(ost + r * 512 + ((2 * c + 1) ^ g) * 8);
@@ -308,9 +318,9 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   };
 
   BigTile cur = decode(item);
-  int32_t pr[4] = {0, 0, 0, 0}, tp = -1;
+  int32_t pr[NX] = {}, tp = -1;
   if (GROUPED) load_rows(cur, pr, tp);
-  BigCopy cc = make_copy(cur, pr);
+  Copy cc = make_copy(cur, pr);
   bool first = true;
 
   if constexpr (MX) {
@@ -324,7 +334,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
     const uint32_t xo0 = n_l * 128 + 16 * (q_l ^ xsw), xo1 = n_l * 128 + 16 * ((4 + q_l) ^ xsw);
     // copies of one stage: activations, weight tiles (column blocks w and
     // w + 8) and their scale words
-    auto copy_stage = [&](const BigCopy& c, int ls, uint8_t* st) {
+    auto copy_stage = [&](const Copy& c, int ls, uint8_t* st) {
       copy_x(c, ls, st);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -338,7 +348,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
       const int64_t nitem = item + gridDim.x;
       const bool has_next = nitem < n_items;
       const BigTile nxt = has_next ? decode(nitem) : cur;
-      int32_t prn[4] = {0, 0, 0, 0}, tpn = -1;
+      int32_t prn[NX] = {}, tpn = -1;
       if (!chained || first) {
         // stand-alone start: earlier copies and stores done, all waves past
         // the previous epilogue
@@ -358,7 +368,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
       }
       // the next tile's rows load before this tile's copies (done by the end of step 0)
       if (GROUPED && chained && has_next) load_rows(nxt, prn, tpn);
-      BigCopy nc = cc;
+      Copy nc = cc;
       if (!GROUPED && chained && has_next) nc = make_copy(nxt, prn);
 
       f32x4_t acc[8][4];
@@ -375,31 +385,56 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
         const uint8_t* st = lds + so[0];
         // copies for step s + 2: this tile's, the next tile's, or (none left)
         // a repeat of the last one into a stage no longer read
+        // copies for step s + 2 (this tile's, the next tile's, or, none
+        // left, repeats of this tile's last step into a stage no longer
+        // read), one after every four MFMAs: activations q < 4, then per
+        // weight tile its 1 KiB and its scale words
         const int t2 = s + 2;
+        const bool xnext = chained && has_next && t2 >= S;
+        const int ls = t2 < S ? t2 : (xnext ? t2 - S : S - 1);
         uint8_t* d2 = lds + so[2];
-        if (t2 < S) copy_stage(cc, t2, d2);
-        else if (chained && has_next) copy_stage(nc, t2 - S, d2);
-        else copy_stage(cc, S - 1, d2);
-        const int sh = 8 * (int)(s & 3);
+        auto dma = [&](int q) {
+          const Copy& c = xnext ? nc : cc;
+          if (q < 4) {
+            b2lds16(c.rx, c.xoff[q], (uint32_t)(ls * 128), d2 + (4 * wave + q) * 1024);
+          } else {
+            const int k = (q - 4) >> 1, cb = wave + 8 * k;
+            if ((q & 1) == 0) b2lds16(c.rw, c.wvo[k], (uint32_t)(ls * 1024), d2 + 32 * 1024 + cb * 1024);
+            else b2lds4(rsz, c.svo[k], (uint32_t)((ls / 4) * 256), d2 + 48 * 1024 + cb * 256);
+          }
+        };
+        // operands: the wave's eight weight tiles and their scales (kept for
+        // the step), activation halves of one row block at a time, read one
+        // row block ahead
+        const int sh = 8 * (s & 3);
+        const uint8_t* wbase = st + 32 * 1024 + wn * 8 * 1024 + lane * 16;
+        const uint8_t* sbase = st + 48 * 1024 + wn * 8 * 256 + lane * 4;
+        const uint8_t* xbase = st + wm * 4 * 2048;
         u32x4_t wq[8];
         int wsc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int cb = wn * 8 + j;
-          wq[j] = ld16(st + 32 * 1024 + cb * 1024 + lane * 16);
-          wsc[j] = (int)((*reinterpret_cast<const uint32_t*>(st + 48 * 1024 + cb * 256 + lane * 4) >> sh) & 0xFF);
+          wq[j] = ld16(wbase + j * 1024);
+          wsc[j] = (int)((*reinterpret_cast<const uint32_t*>(sbase + j * 256) >> sh) & 0xFF);
         }
-        u32x4_t b0[4], b1[4];
+        u32x4_t b0[2], b1[2];
+        b0[0] = ld16(xbase + xo0);
+        b1[0] = ld16(xbase + xo1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rb = wm * 4 + i;
-          b0[i] = ld16(st + rb * 2048 + xo0);
-          b1[i] = ld16(st + rb * 2048 + xo1);
+          if (i + 1 < 4) {
+            b0[(i + 1) & 1] = ld16(xbase + (i + 1) * 2048 + xo0);
+            b1[(i + 1) & 1] = ld16(xbase + (i + 1) * 2048 + xo1);
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            acc[j][i] = mfma_fp4_fp8(wq[j], b0[i & 1], b1[i & 1], acc[j][i], wsc[j], 127);
+            if ((j & 3) == 3) {
+              dma(2 * i + (j >> 2));
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[j][i] = mfma_fp4_fp8(wq[j], b0[i], b1[i], acc[j][i], wsc[j], 127);
         // the next stage was issued one step ago, this step's copies after it
         wait_barrier(std::integral_constant<int, kPer>());
         rotate();
@@ -444,54 +479,60 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
     }
   } else {
     // ================================ W4A16: K step 64 = half a K group;
-    // eight waves, two per SIMD: wave w owns columns 32 w + 0..31 and all
-    // 256 rows as eight 32 x 32 blocks (v_mfma_f32_32x32x16_bf16, 128
-    // accumulators per lane), so every weight is unpacked by one wave only.
-    // 32x32x16 operands: A row / B column = lane % 32, K = 8 (lane / 32) +
-    // 0..7; result: column lane % 32, rows 8 j + 4 (lane / 32) + r in
-    // register 4 j + r.  The unpacking of the next step's operands is
-    // interleaved with this step's MFMAs, so it runs on the vector ALU while
-    // the matrix core works.
+    // four waves, one per SIMD: wave w owns columns 64 w + 0..63 and all 256
+    // rows as 2 x 8 blocks of 32 x 32 (v_mfma_f32_32x32x16_bf16, 256
+    // accumulators per lane), so every weight is unpacked by one wave and
+    // every activation fragment read from LDS feeds two MFMAs.  32x32x16
+    // operands: A row / B column = lane % 32, K = 8 (lane / 32) + 0..7;
+    // result: column lane % 32, rows 8 j + 4 (lane / 32) + r in register
+    // 4 j + r.  The unpacking of the next step's operands is interleaved with
+    // this step's MFMAs, so it runs on the vector ALU while the matrix core
+    // works.
     // operand rows 32 mb + l32, K part kq: chunk 2 kq + hi (8 bf16)
     const int xsw = (l32 >> 1) & 7;
     uint32_t xo[4];
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) xo[kq] = l32 * 128 + 16 * ((2 * kq + hi) ^ xsw);
-    // Wave w copies its own two weight tiles (column blocks 2 w, 2 w + 1) and
-    // one 4-byte-per-lane gather of their scales and zero points into its
-    // 256-byte slot at kSOff + 256 w.
+    // Wave w copies its own four weight tiles (column blocks 4 w .. 4 w + 3)
+    // and one 4-byte-per-lane gather of their scales and zero points into its
+    // 256-byte slot at kSOff + 256 w (scales at 0, zero-point words at 128).
     constexpr int kWOff = 32 * 1024, kSOff = 48 * 1024;
     // weights of K step ls (group ls / 2) into the weight part of a stage
-    auto copy_w = [&](const BigCopy& c, int ls, uint8_t* stg) {
+    auto copy_w = [&](const Copy& c, int ls, uint8_t* stg) {
       const int g = ls >> 1;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) b2lds16(c.rw, c.wvo[k], (uint32_t)(g * 1024), stg + kWOff + (2 * wave + k) * 1024);
+      for (int k = 0; k < NWT; ++k) b2lds16(c.rw, c.wvo[k], (uint32_t)(g * 1024), stg + kWOff + (NWT * wave + k) * 1024);
       b2lds4(rsz, c.svo[0] + (uint32_t)g * szstride, 0u, stg + kSOff + wave * 256);
     };
-    constexpr int kPer = 4 + 2 + 1;                 // copies per wave per step
-    // A operands of one step: K part kq.  Lane row n = 32 w + l32 lies in
-    // tile 2 w + l32 / 16 at column l32 % 16; K = 64 h + 16 kq + 8 hi is
-    // word 2 h + kq / 2 of slot (l32 % 16) + 16 ((2 kq + hi) % 4).
+    constexpr int kPer = NX + NWT + 1;              // copies per wave per step
+    // A operands of one step: column half nb2, K part kq.  Lane row n =
+    // 64 w + 32 nb2 + l32 lies in tile 4 w + 2 nb2 + l32 / 16 at column
+    // l32 % 16; K = 64 h + 16 kq + 8 hi is word 2 h + kq / 2 of slot
+    // (l32 % 16) + 16 ((2 kq + hi) % 4).
     const int c_l = l32 >> 4, c16 = l32 & 15;
-    auto fetch = [&](const uint8_t* stg, int h, uint32_t (&wv)[4], float& sv, float& zs) {
-      const uint8_t* tile = stg + kWOff + (2 * wave + c_l) * 1024;
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq)
-        wv[kq] = *reinterpret_cast<const uint32_t*>(tile + (c16 + 16 * ((2 * kq + hi) & 3)) * 16 + 4 * (2 * h + (kq >> 1)));
+    auto fetch = [&](const uint8_t* stg, int h, uint32_t (&wv)[2][4], float (&sv)[2], float (&zs)[2]) {
       const uint8_t* sz = stg + kSOff + wave * 256;
-      sv = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sz + c_l * 32 + c16 * 2));
-      const uint32_t zw = ZP ? *reinterpret_cast<const uint32_t*>(sz + 64 + c_l * 8 + (c16 >> 3) * 4) : 0u;
-      const float z = ZP ? (float)((zw >> (4 * (c16 & 7))) & 0xFu) : 8.0f;
-      zs = -z * sv;
+#pragma unroll
+      for (int nb2 = 0; nb2 < 2; ++nb2) {
+        const uint8_t* tile = stg + kWOff + (NWT * wave + 2 * nb2 + c_l) * 1024;
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+          wv[nb2][kq] = *reinterpret_cast<const uint32_t*>(tile + (c16 + 16 * ((2 * kq + hi) & 3)) * 16 + 4 * (2 * h + (kq >> 1)));
+        const int t4 = 2 * nb2 + c_l;
+        sv[nb2] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sz + t4 * 32 + c16 * 2));
+        const uint32_t zw = ZP ? *reinterpret_cast<const uint32_t*>(sz + 128 + t4 * 8 + (c16 >> 3) * 4) : 0u;
+        const float z = ZP ? (float)((zw >> (4 * (c16 & 7))) & 0xFu) : 8.0f;
+        zs[nb2] = -z * sv[nb2];
+      }
     };
-    u32x4_t af[4];
-    uint32_t w3c = 0;                               // code word of operand 3, its scale and offset
-    float sv3c = 0.f, zs3c = 0.f;
+    u32x4_t af[2][4];
+    uint32_t w3c[2] = {0u, 0u};                     // code words of operands (nb2, 3), their scales and offsets
+    float sv3c[2] = {0.f, 0.f}, zs3c[2] = {0.f, 0.f};
     while (true) {
       const int64_t nitem = item + gridDim.x;
       const bool has_next = nitem < n_items;
       const BigTile nxt = has_next ? decode(nitem) : cur;
-      int32_t prn[4] = {0, 0, 0, 0}, tpn = -1;
+      int32_t prn[NX] = {}, tpn = -1;
       if (!chained || first) {
         // stand-alone start: weights of steps 0, 1, 2 and activations of
         // steps 0, 1, then operands 0..2 of step 0
@@ -507,33 +548,39 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
         copy_x(cc, 0, lds + so[0]);
         copy_x(cc, std::min(1, S - 1), lds + so[1]);
         wait_barrier(std::integral_constant<int, 0>());
-        uint32_t wv[4];
+        uint32_t wv[2][4];
         fetch(lds + so[0], 0, wv, sv3c, zs3c);
 #pragma unroll
-        for (int kq = 0; kq < 3; ++kq) af[kq] = dq8_bytes(wv[kq], sv3c, zs3c);
-        af[3] = (u32x4_t){0u, 0u, 0u, 0u};
-        w3c = wv[3];
+        for (int nb2 = 0; nb2 < 2; ++nb2) {
+#pragma unroll
+          for (int kq = 0; kq < 3; ++kq) af[nb2][kq] = dq8_bytes(wv[nb2][kq], sv3c[nb2], zs3c[nb2]);
+          af[nb2][3] = (u32x4_t){0u, 0u, 0u, 0u};
+          w3c[nb2] = wv[nb2][3];
+        }
       }
       if (GROUPED && chained && has_next) load_rows(nxt, prn, tpn);
-      BigCopy nc = cc;
+      Copy nc = cc;
       if (!GROUPED && chained && has_next) nc = make_copy(nxt, prn);
 
-      f32x16_t acc[8];
+      f32x16_t acc[2][8];
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
+      for (int nb2 = 0; nb2 < 2; ++nb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
-      // Step s runs its 32 MFMAs K part by K part (kq = 0..3, row blocks
-      // 0..7 each, so no accumulator is updated twice in a row) with the
-      // activation fragments read kD MFMAs ahead.  Operand kq is free once
-      // its eight MFMAs are issued, so the unpacking follows behind: during
-      // K part 0 operand 3 of this step (from the word carried over), during
-      // K part kq = 1..3 operand kq - 1 of the next step (this tile's or, at
-      // the last step, the next tile's first), one result word per two MFMAs.
-      // The scheduling barriers keep this interleaving as written.  Each step
-      // first issues the activations of step s + 2 and the weights of step
-      // s + 3 (of this tile or the next, else repeats of this tile's last
-      // step into parts no longer read), so the wait count is exact.
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[nb2][mb][r] = 0.f;
+      // Step s runs its 64 MFMAs K part by K part (kq = 0..3; row blocks
+      // 0..7, each activation fragment feeding both column halves, so no
+      // accumulator is updated twice in a row) with the fragments read kD
+      // fragments ahead.  Operands (nb2, kq) are free once their MFMAs are
+      // issued, so the unpacking follows behind: during K part 0 operands
+      // (nb2, 3) of this step (from the words carried over), during K part
+      // kq = 1..3 operands (nb2, kq - 1) of the next step (this tile's or, at
+      // the last step, the next tile's first), one result word per two
+      // MFMAs.  The scheduling barriers keep this interleaving as written.
+      // Each step first issues the activations of step s + 2 and the weights
+      // of step s + 3 (of this tile or the next, else repeats of this tile's
+      // last step into parts no longer read), so the wait count is exact.
       constexpr int kD = 4;
 #pragma nounroll
       for (int s = 0; s < S; ++s) {
@@ -542,19 +589,33 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
           if (has_next) nc = make_copy(nxt, prn);
         }
         // activations of step s + 2 into stage so[2], weights of step s + 3
-        // into the weight part of this step's stage so[0] (read one step ago)
+        // into the weight part of this step's stage so[0] (read one step
+        // ago): this tile's, the next tile's, or (none left) repeats of this
+        // tile's last step into parts no longer read.  Copy q of the step is
+        // issued after MFMA pair 2 q + 1, so the in-order issue never holds
+        // the matrix core up behind a burst of copies.
         const int t2 = s + 2, t3 = s + 3;
+        const bool xnext = chained && has_next && t2 >= S, wnext = chained && has_next && t3 >= S;
+        const int xls = t2 < S ? t2 : (xnext ? t2 - S : S - 1);
+        const int wls = t3 < S ? t3 : (wnext ? t3 - S : S - 1);
         uint8_t* d2 = lds + so[2];
         uint8_t* d3 = lds + so[0];
-        if (t2 < S) copy_x(cc, t2, d2);
-        else if (chained && has_next) copy_x(nc, t2 - S, d2);
-        else copy_x(cc, S - 1, d2);
-        if (t3 < S) copy_w(cc, t3, d3);
-        else if (chained && has_next) copy_w(nc, t3 - S, d3);
-        else copy_w(cc, S - 1, d3);
+        auto dma = [&](int q) {
+          if (q < NX) {
+            const Copy& c = xnext ? nc : cc;
+            b2lds16(c.rx, c.xoff[q], (uint32_t)(xls * 128), d2 + (NX * wave + q) * 1024);
+          } else if (q < NX + NWT) {
+            const Copy& c = wnext ? nc : cc;
+            const int k = q - NX;
+            b2lds16(c.rw, c.wvo[k], (uint32_t)((wls >> 1) * 1024), d3 + kWOff + (NWT * wave + k) * 1024);
+          } else {
+            const Copy& c = wnext ? nc : cc;
+            b2lds4(rsz, c.svo[0] + (uint32_t)(wls >> 1) * szstride, 0u, d3 + kSOff + wave * 256);
+          }
+        };
         const uint8_t* xs = lds + so[0];
-        uint32_t wv[4];
-        float svn, zsn;
+        uint32_t wv[2][4];
+        float svn[2], zsn[2];
         fetch(lds + so[1], (s + 1) & 1, wv, svn, zsn);
         u32x4_t b[32];
 #pragma unroll
@@ -563,33 +624,38 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
           const int kq = i >> 3, mb = i & 7;
-          acc[mb] = mfma32_bf16(af[kq], b[i], acc[mb]);
+#pragma unroll
+          for (int nb2 = 0; nb2 < 2; ++nb2) acc[nb2][mb] = mfma32_bf16(af[nb2][kq], b[i], acc[nb2][mb]);
           if (i + kD < 32) {
             const int j = i + kD;
             b[j] = ld16(xs + (j & 7) * 4096 + xo[j >> 3]);
           }
-          if (i & 1) {
-            const int u = (i & 7) >> 1;               // result word of the operand being unpacked
-            const uint32_t w = kq == 0 ? w3c : wv[kq - 1];
-            const float sv = kq == 0 ? sv3c : svn, zs = kq == 0 ? zs3c : zsn;
+          {
+            const int nb2 = (i & 7) >> 2, u = i & 3;   // result word u of operand (nb2, (kq + 3) % 4)
+            const uint32_t w = kq == 0 ? w3c[nb2] : wv[nb2][kq - 1];
+            const float sv = kq == 0 ? sv3c[nb2] : svn[nb2], zs = kq == 0 ? zs3c[nb2] : zsn[nb2];
             if (u == 0) {
               lo = in_vgpr(w & 0x0F0F0F0Fu);
               hi4 = in_vgpr((w >> 4) & 0x0F0F0F0Fu);
             }
-            af[(kq + 3) & 3][u] = dq8_word(lo, hi4, u, sv, zs);
+            af[nb2][(kq + 3) & 3][u] = dq8_word(lo, hi4, u, sv, zs);
           }
+          if ((i & 1) && (i >> 1) < kPer) dma(i >> 1);
           __builtin_amdgcn_sched_barrier(0);
         }
-        w3c = wv[3];
-        sv3c = svn;
-        zs3c = zsn;
+#pragma unroll
+        for (int nb2 = 0; nb2 < 2; ++nb2) {
+          w3c[nb2] = wv[nb2][3];
+          sv3c[nb2] = svn[nb2];
+          zs3c[nb2] = zsn[nb2];
+        }
         // stage s + 1 (activations) came one step earlier, weights two; after
         // them only this step's copies
         wait_barrier(std::integral_constant<int, kPer>());
         rotate();
       }
 
-      // ---- epilogue: lane holds C[n = 32 w + 8 j + 4 hi + r][row = 32 mb + l32];
+      // ---- epilogue: lane holds C[n = 64 w + 32 nb2 + 8 j + 4 hi + r][row = 32 mb + l32];
       // slab p holds row blocks 2 p and 2 p + 1 of every wave; the copies still
       // in flight finish first (the stores then never overtake a copy)
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -600,11 +666,14 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
         for (int mm = 0; mm < 2; ++mm) {
           const int mb = 2 * p + mm, r = 32 * mm + l32;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int u = 8 * wave + 2 * j + hi;
-            *reinterpret_cast<u32x2_t*>(ost + r * 512 + (u ^ Swz16::swz(r)) * 8) =
-                (u32x2_t){pack_bf16(acc[mb][4 * j], acc[mb][4 * j + 1]), pack_bf16(acc[mb][4 * j + 2], acc[mb][4 * j + 3])};
-          }
+          for (int nb2 = 0; nb2 < 2; ++nb2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int u = 16 * wave + 8 * nb2 + 2 * j + hi;
+              *reinterpret_cast<u32x2_t*>(ost + r * 512 + (u ^ Swz16::swz(r)) * 8) =
+                  (u32x2_t){pack_bf16(acc[nb2][mb][4 * j], acc[nb2][mb][4 * j + 1]),
+                            pack_bf16(acc[nb2][mb][4 * j + 2], acc[nb2][mb][4 * j + 3])};
+            }
         }
         wait_barrier(std::integral_constant<int, 0>());
         store_slab(cur, ost, p, Swz16());
@@ -634,7 +703,7 @@ static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
   const int64_t tiles = (int64_t)tiles_n * tiles_m;
   const unsigned grid = GROUPED ? (unsigned)(grid_items > 0 ? grid_items : 1)
                                 : (unsigned)(tiles <= kBigGrid ? tiles : kBigGrid);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), big_lds_bytes(MX), st, a, tiles_n, tiles_m);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(big_threads(MX)), big_lds_bytes(MX), st, a, tiles_n, tiles_m);
   return hipGetLastError();
 }
 
