@@ -242,7 +242,7 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* 
     snprintf(buf, buf_len, "%s stream mb=%d nbw=%d ks=%d splits=%d ksg=%d mfma=%s", w, p.sc.mb,
              p.sc.nbw, p.sc.ks, p.sc.splits, p.ksg, d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
   else if (p.big)
-    snprintf(buf, buf_len, "%s tile 256x256 waves=%s mfma=%s", w, d->wfmt == HM_W_MXFP4 ? "4x2" : "2x4",
+    snprintf(buf, buf_len, "%s tile 256x256 waves=%s mfma=%s", w, d->wfmt == HM_W_MXFP4 ? "4x2" : "1x4",
              d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "32x32x16_bf16");
   else
     snprintf(buf, buf_len, "%s tile %dx%d waves=2x2 mfma=%s", w, kTileM, kTileN,

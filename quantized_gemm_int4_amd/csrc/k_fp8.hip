@@ -26,7 +26,7 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | ((r >> 20) - (120u << 3));
 }
 
-// One 256-thread block per row; rows of any length k.
+// One 256-thread block per row; rows of any length k (two passes over the row).
 __global__ void __launch_bounds__(256)
 k_quant_fp8_rows(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint8_t* __restrict__ x8,
                  float* __restrict__ row_scale) {
@@ -76,10 +76,67 @@ k_quant_fp8_rows(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint8_t* 
   }
 }
 
+// Rows with k % 8 == 0 and k <= 2048 CH: each thread keeps its CH 16-byte
+// chunks of the row (thread t: values 8 (256 c + t) .. + 7) in registers, so
+// the row is read once and the amax pass and the quantizing pass share it.
+template <int CH>
+__global__ void __launch_bounds__(256)
+k_quant_fp8_rows_reg(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint8_t* __restrict__ x8,
+                     float* __restrict__ row_scale) {
+  __shared__ float red[4];
+  for (int64_t row = blockIdx.x; row < m; row += gridDim.x) {
+    const uint16_t* xr = x + row * k;
+    uint8_t* qr = x8 + row * k;
+    u32x4_t v[CH];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t i = ((int64_t)c * 256 + threadIdx.x) * 8;
+      v[c] = i < k ? ld16(xr + i) : (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        amax = fmaxf(amax, fabsf(bf16_to_f32(v[c][j] & 0xFFFF)));
+        amax = fmaxf(amax, fabsf(bf16_to_f32(v[c][j] >> 16)));
+      }
+    }
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    const float s = __fdiv_rn(amax, 448.0f);
+    if (threadIdx.x == 0) row_scale[row] = s;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t i = ((int64_t)c * 256 + threadIdx.x) * 8;
+      if (i >= k) continue;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t c0 = 0, c1 = 0;
+        if (s != 0.0f) {
+          c0 = f32_to_e4m3(__fdiv_rn(bf16_to_f32(v[c][j] & 0xFFFF), s));
+          c1 = f32_to_e4m3(__fdiv_rn(bf16_to_f32(v[c][j] >> 16), s));
+        }
+        const uint32_t pair = c0 | (c1 << 8);
+        if (j < 2) lo |= pair << (16 * j); else hi |= pair << (16 * (j - 2));
+      }
+      *reinterpret_cast<u32x2_t*>(qr + i) = (u32x2_t){lo, hi};
+    }
+  }
+}
+
 hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* x8, float* s,
                                  hipStream_t st) {
-  int64_t blocks = m < 65536 ? m : 65536;
-  hipLaunchKernelGGL(k_quant_fp8_rows, dim3((unsigned)blocks), dim3(256), 0, st, x, m, k, x8, s);
+  const int64_t blocks = m < 65536 ? m : 65536;
+  if ((k & 7) == 0 && k <= 2048 * 4) {
+    // one row per block, held in registers
+    if (k <= 2048) hipLaunchKernelGGL(k_quant_fp8_rows_reg<1>, dim3((unsigned)blocks), dim3(256), 0, st, x, m, k, x8, s);
+    else if (k <= 4096) hipLaunchKernelGGL(k_quant_fp8_rows_reg<2>, dim3((unsigned)blocks), dim3(256), 0, st, x, m, k, x8, s);
+    else hipLaunchKernelGGL(k_quant_fp8_rows_reg<4>, dim3((unsigned)blocks), dim3(256), 0, st, x, m, k, x8, s);
+  } else {
+    hipLaunchKernelGGL(k_quant_fp8_rows, dim3((unsigned)blocks), dim3(256), 0, st, x, m, k, x8, s);
+  }
   return hipGetLastError();
 }
 
