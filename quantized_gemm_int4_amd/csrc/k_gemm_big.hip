@@ -32,27 +32,6 @@ namespace hm {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw buffer over `bytes` bytes from `base` (reads at or past the end return
-// zero; larger extents are capped at the 32-bit maximum).
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           (int)(uint32_t)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull), 0x00020000);
-}
-
-// Direct buffer-to-LDS copies: lane L's `n` bytes at base + voff + soff land at
-// lds_base + n L.  The buffer form (unlike the global one) leaves the
-// compiler's LDS wait counts exact for the reads that follow.
-__device__ __forceinline__ void b2lds16(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void b2lds4(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 4, voff, soff, 0, 0);
-}
-
 // Four consecutive outputs y[n..n+3] of one row as bf16 (one 8-byte store when aligned).
 __device__ __forceinline__ void store_bf16x4(uint16_t* yrow, int64_t N, int64_t n, f32x4_t v) {
   if ((N & 3) == 0 && n + 3 < N) {

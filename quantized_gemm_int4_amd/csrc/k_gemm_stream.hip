@@ -32,13 +32,6 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// One 16-byte direct global-to-LDS load per lane: lane L's bytes land at
-// lds_base + 16 * L (lds_base wave-uniform, 16-byte aligned).
-__device__ __forceinline__ void g2lds16(const void* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_base, 16, 0, 0);
-}
 
 template <int KS, int NBW, int MB>
 struct StreamShape {
@@ -58,6 +51,9 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
   constexpr int GB = MX ? 128 : 256;                    // activation bytes per row per K group
   constexpr int CS = 4 / KS;                            // column sets per block
   constexpr int RED = StreamShape<KS, NBW, MB>::kRedBytes;
+  // vector-memory loads per ring slot: per column block the 1 KiB tile and
+  // its scale word(s), plus the zero-point word
+  constexpr int kRingLoads = NBW * (MX ? 2 : (ZP ? 3 : 2));
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   uint8_t* const xs_lds = lds + RED;                    // activations: [rows][xb]
   __shared__ int64_t arow_s[ROWS];
@@ -142,8 +138,11 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
     const uint32_t xro_lo = (uint32_t)xrow_off, xro_hi = (uint32_t)((uint64_t)xrow_off >> 32);
 
     // Copy activation rows [0, rcount) x groups [gp, gp + plen) into LDS: one
-    // wave instruction moves 1 KiB of one row; lanes past the row's end re-read
-    // its first chunk and land in the row's padding.
+    // wave instruction moves 1 KiB of one row (buffer over the row's piece,
+    // lane L at byte 16 L of the instruction's 1 KiB); lanes past the row's
+    // end fall outside the buffer, read zeros and land in the row's padding.
+    // The per-lane offset never changes, so no copy waits for an earlier one.
+    const uint32_t lane16 = (uint32_t)lane * 16;
     auto stage_x = [&](int gp, int plen) {
       const int per_row = plen * (GB / 16);             // 16-byte chunks per row
       const int cpr = (per_row + 63) / 64;              // 1 KiB pieces per row
@@ -152,11 +151,10 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
 #pragma nounroll
       for (int i = wave; i < total; i += 4) {
         const int r = i / cpr, blk = i - (i / cpr) * cpr;
-        const int c = blk * 64 + lane;
-        const int cc = c < per_row ? c : 0;
         const uint64_t ro = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xro_hi, r) << 32) |
                             (uint32_t)__builtin_amdgcn_readlane((int)xro_lo, r);
-        g2lds16(xbase + ro + off0 + (int64_t)cc * 16, xs_lds + r * xb + blk * 1024);
+        b2lds16(make_rsrc(xbase + ro + off0, (uint64_t)per_row * 16), lane16, (uint32_t)blk * 1024,
+                xs_lds + r * xb + blk * 1024);
       }
     };
 
@@ -207,79 +205,102 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
       const int64_t gsafe = sl > 0 ? gw : g_begin + gp;     // loads of empty slices stay in range
       if (p > 0) lds_barrier();               // everyone is done with the previous piece
       stage_x(gp, plen);
+      // the ring's first loads go out after the activation copies (the
+      // memory clobber keeps the compiler from hoisting them), so waiting
+      // until only those loads are outstanding means the copies landed; the
+      // ring slots themselves are waited for one by one where they are used
+      __asm__ volatile("" ::: "memory");
 #pragma unroll
       for (int d = 0; d < DW; ++d) load_w(d, gsafe + (d < last ? d : last));
-      __syncthreads();                        // activations (and the ring's first loads) landed
+      __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(DW * kRingLoads) : "memory");
       const int rounds = sl > 0 ? (sl + DW - 1) / DW : 0;
-#pragma nounroll
-      for (int r = 0; r < rounds; ++r) {
+      // group lg of the slice from ring slot d
+      auto process = [&](int d, int lg) {
+        const int64_t g = gw + lg;
+        const uint8_t* xg = xs_lds + (lo + lg) * GB;
+        if (MX) {
+          u32x4_t a0[MB], a1[MB];
 #pragma unroll
-        for (int d = 0; d < DW; ++d) {
-          const int lg = r * DW + d;          // group within the slice
-          if (lg < sl) {
-            const int64_t g = gw + lg;
-            const uint8_t* xg = xs_lds + (lo + lg) * GB;
-            if (MX) {
-              u32x4_t a0[MB], a1[MB];
+          for (int rb = 0; rb < MB; ++rb) {
+            const uint8_t* xp = xg + lrow[rb] * xb + 16 * q_l;
+            a0[rb] = ld16(xp);
+            a1[rb] = ld16(xp + 64);
+          }
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            const int sc = (int)((wsr[d][j] >> (8 * (g & 3))) & 0xFF);
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb)
+              acc[j][rb] = mfma_fp4_fp8(wq[d][j], a0[rb], a1[rb], acc[j][rb], sc, 127);
+          }
+        } else {
+          // Raw codes: one MFMA chain adds x * (1 + u/16) and x * -(1 + z/16)
+          // per K step, i.e. x * (u - z) / 16, exactly 0 where every code
+          // equals the zero point; the group scale of each output row is
+          // applied once to the chain's result, the factor 16 at the end.
+          u32x4_t bz[ZP ? NBW : 1];
+#pragma unroll
+          for (int j = 0; j < (ZP ? NBW : 1); ++j) {
+            const uint32_t z = ZP ? ((wzr[ZP ? d : 0][ZP ? j : 0] >> zshift) & 0xFu) : 8u;
+            const uint32_t pz = neg_raw_u4_pair(z);
+            bz[j] = (u32x4_t){pz, pz, pz, pz};
+          }
+          f32x4_t t[NBW][MB];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            u32x4_t af[MB];
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) af[rb] = ld16(xg + lrow[rb] * xb + (32 * kk + 8 * q_l) * 2);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+              const u32x4_t bw = raw8_u4(wq[d][j][kk], cmask, cbias);
 #pragma unroll
               for (int rb = 0; rb < MB; ++rb) {
-                const uint8_t* xp = xg + lrow[rb] * xb + 16 * q_l;
-                a0[rb] = ld16(xp);
-                a1[rb] = ld16(xp + 64);
-              }
-#pragma unroll
-              for (int j = 0; j < NBW; ++j) {
-                const int sc = (int)((wsr[d][j] >> (8 * (g & 3))) & 0xFF);
-#pragma unroll
-                for (int rb = 0; rb < MB; ++rb)
-                  acc[j][rb] = mfma_fp4_fp8(wq[d][j], a0[rb], a1[rb], acc[j][rb], sc, 127);
-              }
-            } else {
-              // Raw codes: one MFMA chain adds x * (1 + u/16) and x * -(1 + z/16)
-              // per K step, i.e. x * (u - z) / 16, exactly 0 where every code
-              // equals the zero point; the group scale of each output row is
-              // applied once to the chain's result, the factor 16 at the end.
-              u32x4_t bz[ZP ? NBW : 1];
-#pragma unroll
-              for (int j = 0; j < (ZP ? NBW : 1); ++j) {
-                const uint32_t z = ZP ? ((wzr[ZP ? d : 0][ZP ? j : 0] >> zshift) & 0xFu) : 8u;
-                const uint32_t pz = neg_raw_u4_pair(z);
-                bz[j] = (u32x4_t){pz, pz, pz, pz};
-              }
-              f32x4_t t[NBW][MB];
-#pragma unroll
-              for (int kk = 0; kk < 4; ++kk) {
-                u32x4_t af[MB];
-#pragma unroll
-                for (int rb = 0; rb < MB; ++rb) af[rb] = ld16(xg + lrow[rb] * xb + (32 * kk + 8 * q_l) * 2);
-#pragma unroll
-                for (int j = 0; j < NBW; ++j) {
-                  const u32x4_t bw = raw8_u4(wq[d][j][kk], cmask, cbias);
-#pragma unroll
-                  for (int rb = 0; rb < MB; ++rb) {
-                    t[j][rb] = mfma_bf16(bw, af[rb], kk == 0 ? (f32x4_t){0.f, 0.f, 0.f, 0.f} : t[j][rb]);
-                    t[j][rb] = mfma_bf16(bz[ZP ? j : 0], af[rb], t[j][rb]);
-                  }
-                }
-              }
-#pragma unroll
-              for (int j = 0; j < NBW; ++j) {
-                const uint32_t lo2 = wsr[d][j], hi2 = wsh[MX ? 0 : d][MX ? 0 : j];
-                const float s0 = bf16_to_f32(lo2 & 0xFFFFu), s1 = __uint_as_float(lo2 & 0xFFFF0000u);
-                const float s2 = bf16_to_f32(hi2 & 0xFFFFu), s3 = __uint_as_float(hi2 & 0xFFFF0000u);
-#pragma unroll
-                for (int rb = 0; rb < MB; ++rb) {
-                  acc[j][rb][0] = fmaf(s0, t[j][rb][0], acc[j][rb][0]);
-                  acc[j][rb][1] = fmaf(s1, t[j][rb][1], acc[j][rb][1]);
-                  acc[j][rb][2] = fmaf(s2, t[j][rb][2], acc[j][rb][2]);
-                  acc[j][rb][3] = fmaf(s3, t[j][rb][3], acc[j][rb][3]);
-                }
+                t[j][rb] = mfma_bf16(bw, af[rb], kk == 0 ? (f32x4_t){0.f, 0.f, 0.f, 0.f} : t[j][rb]);
+                t[j][rb] = mfma_bf16(bz[ZP ? j : 0], af[rb], t[j][rb]);
               }
             }
           }
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            const uint32_t lo2 = wsr[d][j], hi2 = wsh[MX ? 0 : d][MX ? 0 : j];
+            const float s0 = bf16_to_f32(lo2 & 0xFFFFu), s1 = __uint_as_float(lo2 & 0xFFFF0000u);
+            const float s2 = bf16_to_f32(hi2 & 0xFFFFu), s3 = __uint_as_float(hi2 & 0xFFFF0000u);
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) {
+              acc[j][rb][0] = fmaf(s0, t[j][rb][0], acc[j][rb][0]);
+              acc[j][rb][1] = fmaf(s1, t[j][rb][1], acc[j][rb][1]);
+              acc[j][rb][2] = fmaf(s2, t[j][rb][2], acc[j][rb][2]);
+              acc[j][rb][3] = fmaf(s3, t[j][rb][3], acc[j][rb][3]);
+            }
+          }
+        }
+      };
+      // Every round but the last refills each slot right after its use (with
+      // a repeat of the last group when the slice runs out), so each round
+      // issues the same loads and the waits for the slots stay exact; the
+      // last round refills nothing.
+      int r = 0;
+#pragma nounroll
+      for (; r + 1 < rounds; ++r) {
+#pragma unroll
+        for (int d = 0; d < DW; ++d) {
+          const int lg = r * DW + d;
+          process(d, lg);
           load_w(d, gsafe + (lg + DW < last ? lg + DW : last));
         }
       }
+      if (rounds > 0) {
+#pragma unroll
+        for (int d = 0; d < DW; ++d) {
+          const int lg = r * DW + d;
+          if (lg < sl) process(d, lg);
+        }
+      }
+      // slots past a short slice were loaded but never used: let them land
+      // here (a wait the compiler sees), so that the next piece's ring loads
+      // do not wait behind its activation copies for them
+      __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
     }
 
     // ---- K-split sum: waves kq > 0 park their sums in LDS, wave kq == 0 adds them
