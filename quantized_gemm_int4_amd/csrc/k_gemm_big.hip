@@ -271,6 +271,9 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
     // memory clobber keeps the compiler from moving LDS accesses across
     __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(decltype(n_c)::value) : "memory");
   };
+  // LDS-only barrier for the epilogue's staging: the output stores drain on
+  // their own (the next step's wait covers them, vector memory completes in order)
+  auto lds_barrier = [&]() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   auto local_row = [&](const BigTile& t, int64_t r, int64_t& out, int64_t& in) {
     if (r >= t.rows) { out = -1; in = 0; return; }
     out = GROUPED ? (int64_t)orow_s[r] : t.m0 + r;
@@ -445,9 +448,9 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
             }
           }
         }
-        wait_barrier(std::integral_constant<int, 0>());
+        lds_barrier();
         store_slab(cur, ost, p, SwzMx());
-        wait_barrier(std::integral_constant<int, 0>());
+        lds_barrier();
       }
       if (!has_next) break;
       cur = nxt;
@@ -654,9 +657,9 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
                             pack_bf16(acc[nb2][mb][4 * j + 2], acc[nb2][mb][4 * j + 3])};
             }
         }
-        wait_barrier(std::integral_constant<int, 0>());
+        lds_barrier();
         store_slab(cur, ost, p, Swz16());
-        wait_barrier(std::integral_constant<int, 0>());
+        lds_barrier();
       }
       if (!has_next) break;
       cur = nxt;
