@@ -475,18 +475,29 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
     uint32_t xo[4];
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) xo[kq] = l32 * 128 + 16 * ((2 * kq + hi) ^ xsw);
-    // Wave w copies its own four weight tiles (column blocks 4 w .. 4 w + 3)
-    // and one 4-byte-per-lane gather of their scales and zero points into its
-    // 256-byte slot at kSOff + 256 w (scales at 0, zero-point words at 128).
+    // Weights travel per K group (two steps): the weight parts of the three
+    // stages form a ring of group slots (group slot offsets wso, rotated
+    // every second step), and group g + 2 is copied during the two steps of
+    // group g, half of the wave's four tiles per step.  Wave w copies its own
+    // tiles (column blocks 4 w .. 4 w + 3) and one 4-byte-per-lane gather of
+    // their scales and zero points into its 256-byte slot at kSOff + 256 w
+    // (scales at 0, zero-point words at 128), repeated in both steps.
     constexpr int kWOff = 32 * 1024, kSOff = 48 * 1024;
-    // weights of K step ls (group ls / 2) into the weight part of a stage
-    auto copy_w = [&](const Copy& c, int ls, uint8_t* stg) {
-      const int g = ls >> 1;
-#pragma unroll
-      for (int k = 0; k < NWT; ++k) b2lds16(c.rw, c.wvo[k], (uint32_t)(g * 1024), stg + kWOff + (NWT * wave + k) * 1024);
-      b2lds4(rsz, c.svo[0] + (uint32_t)g * szstride, 0u, stg + kSOff + wave * 256);
+    uint32_t wso[3] = {0u, (uint32_t)SB, 2u * SB};
+    auto rotate_w = [&]() {
+      const uint32_t t = wso[0];
+      wso[0] = wso[1];
+      wso[1] = wso[2];
+      wso[2] = t;
     };
-    constexpr int kPer = NX + NWT + 1;              // copies per wave per step
+    // all four tiles of group g and the gather
+    auto copy_w = [&](const Copy& c, int g, uint8_t* slot) {
+#pragma unroll
+      for (int k = 0; k < NWT; ++k)
+        b2lds16(c.rw, c.wvo[k], (uint32_t)(g * 1024), slot + kWOff + (NWT * wave + k) * 1024);
+      b2lds4(rsz, c.svo[0] + (uint32_t)g * szstride, 0u, slot + kSOff + wave * 256);
+    };
+    constexpr int kPer = NX + 2 + 1;                // copies per wave per step
     // A operands of one step: column half nb2, K part kq.  Lane row n =
     // 64 w + 32 nb2 + l32 lies in tile 4 w + 2 nb2 + l32 / 16 at column
     // l32 % 16; K = 64 h + 16 kq + 8 hi is word 2 h + kq / 2 of slot
@@ -524,14 +535,14 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
           cc = make_copy(cur, pr);
         }
         write_table(tp);
-        copy_w(cc, 0, lds + so[0]);
-        copy_w(cc, std::min(1, S - 1), lds + so[1]);
-        copy_w(cc, std::min(2, S - 1), lds + so[2]);
+        const int KGt = S >> 1;
+        copy_w(cc, 0, lds + wso[0]);
+        copy_w(cc, std::min(1, KGt - 1), lds + wso[1]);
         copy_x(cc, 0, lds + so[0]);
         copy_x(cc, std::min(1, S - 1), lds + so[1]);
         wait_barrier(std::integral_constant<int, 0>());
         uint32_t wv[2][4];
-        fetch(lds + so[0], 0, wv, sv3c, zs3c);
+        fetch(lds + wso[0], 0, wv, sv3c, zs3c);
 #pragma unroll
         for (int nb2 = 0; nb2 < 2; ++nb2) {
 #pragma unroll
@@ -570,35 +581,38 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
           write_table(tp);
           if (has_next) nc = make_copy(nxt, prn);
         }
-        // activations of step s + 2 into stage so[2], weights of step s + 3
-        // into the weight part of this step's stage so[0] (read one step
-        // ago): this tile's, the next tile's, or (none left) repeats of this
-        // tile's last step into parts no longer read.  Copy q of the step is
-        // issued after MFMA pair 2 q + 1, so the in-order issue never holds
-        // the matrix core up behind a burst of copies.
-        const int t2 = s + 2, t3 = s + 3;
-        const bool xnext = chained && has_next && t2 >= S, wnext = chained && has_next && t3 >= S;
+        // activations of step s + 2 into stage so[2], half of the weights of
+        // group s / 2 + 2 into group slot wso[2]: this tile's, the next
+        // tile's, or (none left) repeats of this tile's last into parts no
+        // longer read.  Copy q of the step is issued after MFMA pair 2 q + 1,
+        // so the in-order issue never holds the matrix core up behind a
+        // burst of copies.
+        const int KGt = S >> 1;
+        const int t2 = s + 2, tg = (s >> 1) + 2, wh = s & 1;
+        const bool xnext = chained && has_next && t2 >= S, wnext = chained && has_next && tg >= KGt;
         const int xls = t2 < S ? t2 : (xnext ? t2 - S : S - 1);
-        const int wls = t3 < S ? t3 : (wnext ? t3 - S : S - 1);
+        const int wg = tg < KGt ? tg : (wnext ? tg - KGt : KGt - 1);
         uint8_t* d2 = lds + so[2];
-        uint8_t* d3 = lds + so[0];
+        uint8_t* dw = lds + wso[2];
         auto dma = [&](int q) {
           if (q < NX) {
             const Copy& c = xnext ? nc : cc;
             b2lds16(c.rx, c.xoff[q], (uint32_t)(xls * 128), d2 + (NX * wave + q) * 1024);
-          } else if (q < NX + NWT) {
+          } else if (q < NX + 2) {
+            // tile 2 wh + (q - NX): a branch per half keeps the index constant
             const Copy& c = wnext ? nc : cc;
-            const int k = q - NX;
-            b2lds16(c.rw, c.wvo[k], (uint32_t)((wls >> 1) * 1024), d3 + kWOff + (NWT * wave + k) * 1024);
+            const int k0 = q - NX;
+            if (wh == 0) b2lds16(c.rw, c.wvo[k0], (uint32_t)(wg * 1024), dw + kWOff + (NWT * wave + k0) * 1024);
+            else b2lds16(c.rw, c.wvo[2 + k0], (uint32_t)(wg * 1024), dw + kWOff + (NWT * wave + 2 + k0) * 1024);
           } else {
             const Copy& c = wnext ? nc : cc;
-            b2lds4(rsz, c.svo[0] + (uint32_t)(wls >> 1) * szstride, 0u, d3 + kSOff + wave * 256);
+            b2lds4(rsz, c.svo[0] + (uint32_t)wg * szstride, 0u, dw + kSOff + wave * 256);
           }
         };
         const uint8_t* xs = lds + so[0];
         uint32_t wv[2][4];
         float svn[2], zsn[2];
-        fetch(lds + so[1], (s + 1) & 1, wv, svn, zsn);
+        fetch(lds + ((s & 1) ? wso[1] : wso[0]), (s + 1) & 1, wv, svn, zsn);
         u32x4_t b[32];
 #pragma unroll
         for (int i = 0; i < kD; ++i) b[i] = ld16(xs + (i & 7) * 4096 + xo[i >> 3]);
@@ -631,10 +645,11 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
           sv3c[nb2] = svn[nb2];
           zs3c[nb2] = zsn[nb2];
         }
-        // stage s + 1 (activations) came one step earlier, weights two; after
-        // them only this step's copies
+        // stage s + 1 (activations) came one step earlier, the weights of its
+        // group at least two; after them only this step's copies
         wait_barrier(std::integral_constant<int, kPer>());
         rotate();
+        if (s & 1) rotate_w();
       }
 
       // ---- epilogue: lane holds C[n = 64 w + 32 nb2 + 8 j + 4 hi + r][row = 32 mb + l32];
