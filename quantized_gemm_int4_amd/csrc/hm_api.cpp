@@ -24,6 +24,7 @@ constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles a
 constexpr int kMoeBigMinRows = 192;   // an expert remainder of this many rows gets a 256-row unit   // expert segments of at most this many rows use the streaming kernel
 constexpr int kGroupedGridStream = 2048;
 constexpr int kGroupedGridTile = 1024;
+constexpr int kGroupedGridMid = 256;     // one 128 x 64 tile block per compute unit (LDS-bound)
 constexpr int kGroupedGridBig = 256;     // one 256-tile block per compute unit (LDS-bound)
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -57,7 +58,8 @@ int env_int(const char* name, int dflt) {
 // ---------------------------------------------------------------- dense plan
 struct DensePlan {
   bool stream;
-  bool big;          // 256 x 256 tiles (large M), else 128 x 128 tiles
+  bool big;          // 256 x 256 tiles (large M)
+  bool mid;          // W4A16 128 x 64 tiles with the K groups split over the waves
   StreamCfg sc;
   int ksg;
   size_t ws_bytes;
@@ -66,11 +68,13 @@ struct DensePlan {
 DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
   DensePlan p{};
   const Geom G = geom_of(d);
-  const int force = env_int("HM_FORCE_PATH", 0);  // 1 = streaming, 2 = 128-row tiles, 3 = 256-row tiles
+  // 1 = streaming, 2 = 128-row tiles, 3 = 256-row tiles, 4 = W4A16 128 x 128 tiles
+  const int force = env_int("HM_FORCE_PATH", 0);
   p.stream = (force == 1) || (force == 0 && m <= kStreamMaxRows);
   if (force == 1 && m > kStreamMaxRows) p.stream = false;  // streaming handles <= 32 rows per block
   if (!p.stream) {
     p.big = (force == 3) || (force == 0 && m >= kBigMinRows);
+    p.mid = !p.big && d->wfmt != HM_W_MXFP4 && force != 4;
     return p;
   }
   p.sc.mb = (m <= 16) ? 1 : 2;
@@ -244,6 +248,8 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* 
   else if (p.big)
     snprintf(buf, buf_len, "%s tile 256x256 waves=%s mfma=%s", w, d->wfmt == HM_W_MXFP4 ? "4x2" : "1x4",
              d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "32x32x16_bf16");
+  else if (p.mid)
+    snprintf(buf, buf_len, "%s tile 128x64 waves=4 (K split) mfma=32x32x16_bf16", w);
   else
     snprintf(buf, buf_len, "%s tile %dx%d waves=2x2 mfma=%s", w, kTileM, kTileN,
              d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
@@ -284,7 +290,8 @@ HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, con
     e = launch_gemm_stream(a, p.sc, false, 0, stream);
     if (e == hipSuccess && p.sc.splits > 1) e = launch_splitk_reduce(a, p.sc.splits, stream);
   } else {
-    e = p.big ? launch_gemm_big(a, false, 0, stream) : launch_gemm_tile(a, false, 0, stream);
+    e = p.big ? launch_gemm_big(a, false, 0, stream)
+              : (p.mid ? launch_gemm_mid(a, false, 0, stream) : launch_gemm_tile(a, false, 0, stream));
   }
   return (e == hipSuccess) ? HM_OK : HM_ERR_HIP;
 }
@@ -380,11 +387,15 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
     if (gi > 0) e = launch_gemm_stream(a, sc, true, (int)gi, stream);
   }
   if (e == hipSuccess) {
-    const int64_t ntt = (a.G.NB + 7) / 8;
+    // units of up to 128 rows: W4A16 on 128 x 64 tiles (one block per
+    // compute unit, LDS-bound), W4A8 on 128 x 128 tiles
+    const bool mid = d->wfmt != HM_W_MXFP4 && env_int("HM_MOE_MID", 1);
+    const int64_t ntt = mid ? mid_n_tiles(a.G) : (a.G.NB + 7) / 8;
     int64_t gi = p.max_t * ntt;
-    if (gi > kGroupedGridTile) gi = kGroupedGridTile;
+    const int64_t cap = mid ? kGroupedGridMid : kGroupedGridTile;
+    if (gi > cap) gi = cap;
     a.units = tu;
-    if (gi > 0) e = launch_gemm_tile(a, true, (int)gi, stream);
+    if (gi > 0) e = mid ? launch_gemm_mid(a, true, (int)gi, stream) : launch_gemm_tile(a, true, (int)gi, stream);
   }
   if (e == hipSuccess && big_min > 0) {
     int64_t gi = p.max_b * big_n_tiles(a.G);

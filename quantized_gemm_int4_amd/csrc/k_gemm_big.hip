@@ -43,43 +43,6 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* yrow, int64_t N, int64_t 
   }
 }
 
-// Eight consecutive outputs y[n..n+7] of one row (one 16-byte store when aligned).
-__device__ __forceinline__ void store_bf16x8(uint16_t* yrow, int64_t N, int64_t n, u32x4_t v) {
-  if ((N & 7) == 0 && n + 7 < N) {
-    *reinterpret_cast<u32x4_t*>(yrow + n) = v;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (n + e < N) yrow[n + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-  }
-}
-
-__device__ __forceinline__ float ubyte_f(uint32_t x, int b) { return (float)((x >> (8 * b)) & 0xFFu); }
-
-// Eight codes of one device-layout word (value 2p in nibble p, 2p+1 in nibble
-// p+4) -> eight bf16 of s*u + zs (= s*(u - z), exact before the bf16 rounding)
-// in value order.
-// Word r of the result below from the masked bytes lo = w & 0x0F0F0F0F and
-// hi = (w >> 4) & 0x0F0F0F0F.
-__device__ __forceinline__ uint32_t dq8_word(uint32_t lo, uint32_t hi, int r, float s, float zs) {
-  const uint32_t x = (r & 1) ? hi : lo;
-  const int b0 = r >> 1;                         // bytes b0 and b0 + 2 of x
-  return pack_bf16(fmaf(ubyte_f(x, b0), s, zs), fmaf(ubyte_f(x, b0 + 2), s, zs));
-}
-
-__device__ __forceinline__ u32x4_t dq8_bytes(uint32_t w, float s, float zs) {
-  // opaque masks: otherwise the compiler folds mask and byte select into one
-  // bit-field extract per value instead of converting the masked bytes
-  const uint32_t lo = in_vgpr(w & 0x0F0F0F0Fu);          // bytes: v0 v4 v1 v5
-  const uint32_t hi = in_vgpr((w >> 4) & 0x0F0F0F0Fu);   // bytes: v2 v6 v3 v7
-  u32x4_t r;
-  r[0] = pack_bf16(fmaf(ubyte_f(lo, 0), s, zs), fmaf(ubyte_f(lo, 2), s, zs));
-  r[1] = pack_bf16(fmaf(ubyte_f(hi, 0), s, zs), fmaf(ubyte_f(hi, 2), s, zs));
-  r[2] = pack_bf16(fmaf(ubyte_f(lo, 1), s, zs), fmaf(ubyte_f(lo, 3), s, zs));
-  r[3] = pack_bf16(fmaf(ubyte_f(hi, 1), s, zs), fmaf(ubyte_f(hi, 3), s, zs));
-  return r;
-}
-
 }  // namespace
 
 // first column block of expert e

@@ -108,7 +108,7 @@ def test_ragged_default_path(fmt, n, k, m):
 
 @pytest.mark.parametrize("fmt", quant.FORMATS)
 @pytest.mark.parametrize("m", [1, 17, 32])
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 4])
 def test_forced_paths_agree_with_oracle(fmt, m, path):
     L = Layer(fmt, 328, 640, cfg=8)
     _force(path)
@@ -244,3 +244,16 @@ def test_big_tiles_ragged(fmt, m, n, k):
     L = Layer(fmt, n, k, cfg=13, wseed=m)
     x = synthetic.activations(13, m, k, index=m, outliers=0.01 if fmt == quant.FMT_MXFP4 else 0)
     _with_env({"HM_FORCE_PATH": 3}, lambda: L.check(x))
+
+
+@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("m,n,k", [(1, 200, 384), (300, 1000, 1152), (128, 72, 128), (129, 64, 256),
+                                   (77, 520, 640), (256, 136, 768), (200, 48, 896), (40, 2000, 1024)])
+def test_mid_tiles_ragged(fmt, m, n, k):
+    """The 128-row tile path (W4A16: 128 x 64 tiles with the K groups split
+    over the waves) on ragged shapes: M and N not multiples of the tile, one
+    to eight K groups (fewer than, equal to and more than the copy-ahead
+    depths), a single row."""
+    L = Layer(fmt, n, k, cfg=14, wseed=m + n)
+    x = synthetic.activations(14, m, k, index=m, outliers=0.01 if fmt == quant.FMT_MXFP4 else 0)
+    _with_env({"HM_FORCE_PATH": 2}, lambda: L.check(x))

@@ -2,6 +2,8 @@
 the stable pair order), and the grouped GEMM matches the oracle's per-expert
 fp64 GEMM for every pair, on small shapes that mix streaming units (<= 32
 rows) and tile units (> 32 rows), and at the workload sizes on sampled pairs."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -74,12 +76,19 @@ def _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, seed):
 
 @pytest.mark.parametrize("fmt", quant.FORMATS)
 @pytest.mark.parametrize("rows_are_pairs", [0, 1])
-def test_moe_mixed_units(fmt, rows_are_pairs):
+@pytest.mark.parametrize("mid", [1, 0])
+def test_moe_mixed_units(fmt, rows_are_pairs, mid):
+    """Streaming, 128-row and 256-row units in one call; W4A16 128-row units
+    on the 128 x 64 tile kernel (mid=1, the default) or the 128 x 128 one."""
     t, topk, E, n, k = 150, 2, 8, 208, 384
     ids = _skewed_ids(t, topk, E, 1)
     counts = np.bincount(ids.ravel(), minlength=E)
     assert counts.max() > 128 and (counts[counts > 0] <= 32).any()   # both kernels used, multi-unit
-    _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, 1)
+    os.environ["HM_MOE_MID"] = str(mid)
+    try:
+        _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, 1)
+    finally:
+        os.environ.pop("HM_MOE_MID", None)
 
 
 @pytest.mark.parametrize("fmt", [quant.FMT_INT4_SYM, quant.FMT_MXFP4])
