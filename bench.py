@@ -54,7 +54,9 @@ def kernel_of(plan):
     """Kernel that carries a dense launch, from its plan string."""
     if " stream " in plan:
         return "k_gemm_stream"
-    return "k_gemm_big" if "256x256" in plan else "k_gemm_tile"
+    if "256x256" in plan:
+        return "k_gemm_big"
+    return "k_gemm_mid" if "128x64" in plan else "k_gemm_tile"
 
 
 def src_hash():
@@ -415,11 +417,11 @@ def moe_roofline(per_t, fmt):
     peak = FP8_PEAK_TFLOPS if fmt == "mxfp4" else BF16_PEAK_TFLOPS
     if r["bound"] == "mfma":
         a = r["flops"] / (r["ms"] * 1e-3) / 1e12
-        return dict(bound="mfma", kernel="hm_moe_gemm (grouped k_gemm_tile + k_gemm_stream)",
+        return dict(bound="mfma", kernel="hm_moe_gemm (grouped k_gemm_big + k_gemm_mid/tile + k_gemm_stream)",
                     achieved=round(a, 2), peak=peak, unit="TFLOP/s", frac=round(a / peak, 4),
                     per_launch=f"2*P*N*K flops of gate_up + down at T={r['T']}", traffic=None)
     a = r["weight_bytes"] / (r["ms"] * 1e-3) / 1e9
-    return dict(bound="hbm", kernel="hm_moe_gemm (grouped k_gemm_stream + k_gemm_tile)",
+    return dict(bound="hbm", kernel="hm_moe_gemm (grouped k_gemm_stream + k_gemm_mid/tile + k_gemm_big)",
                 achieved=round(a, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(a / HBM_PEAK_GBS, 4),
                 per_launch=f"weight bytes of the active experts at T={r['T']}", traffic=None)
 
