@@ -74,7 +74,7 @@ DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
   if (force == 1 && m > kStreamMaxRows) p.stream = false;  // streaming handles <= 32 rows per block
   if (!p.stream) {
     p.big = (force == 3) || (force == 0 && m >= kBigMinRows);
-    p.mid = !p.big && d->wfmt != HM_W_MXFP4 && force != 4;
+    p.mid = !p.big && force != 4;
     return p;
   }
   p.sc.mb = (m <= 16) ? 1 : 2;
@@ -248,6 +248,8 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* 
   else if (p.big)
     snprintf(buf, buf_len, "%s tile 256x256 waves=%s mfma=%s", w, d->wfmt == HM_W_MXFP4 ? "4x2" : "1x4",
              d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "32x32x16_bf16");
+  else if (p.mid && d->wfmt == HM_W_MXFP4)
+    snprintf(buf, buf_len, "%s tile 64x128 waves=2x2 mfma=scale_16x16x128_f8f6f4", w);
   else if (p.mid)
     snprintf(buf, buf_len, "%s tile 128x64 waves=4 (K split) mfma=32x32x16_bf16", w);
   else
@@ -387,10 +389,11 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
     if (gi > 0) e = launch_gemm_stream(a, sc, true, (int)gi, stream);
   }
   if (e == hipSuccess) {
-    // units of up to 128 rows: W4A16 on 128 x 64 tiles (one block per
-    // compute unit, LDS-bound), W4A8 on 128 x 128 tiles
-    const bool mid = d->wfmt != HM_W_MXFP4 && env_int("HM_MOE_MID", 1);
-    const int64_t ntt = mid ? mid_n_tiles(a.G) : (a.G.NB + 7) / 8;
+    // units of up to 128 rows: W4A16 on 128 x 64 tiles, W4A8 on 64 x 128
+    // tiles (one block per compute unit, LDS-bound); HM_MOE_MID=0 keeps
+    // them on the 128 x 128 kernel
+    const bool mid = env_int("HM_MOE_MID", 1) != 0;
+    const int64_t ntt = mid ? mid_n_tiles(a.G, d->wfmt == HM_W_MXFP4) : (a.G.NB + 7) / 8;
     int64_t gi = p.max_t * ntt;
     const int64_t cap = mid ? kGroupedGridMid : kGroupedGridTile;
     if (gi > cap) gi = cap;

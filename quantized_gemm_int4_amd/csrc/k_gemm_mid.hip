@@ -24,6 +24,15 @@
 //     ahead (they come from HBM, the activations mostly from L2).
 // Operands of the next group's first K part are unpacked during the second
 // K part of the current one, so each group starts with ready operands.
+//
+// W4A8-MXFP4 (k_gemm_mid_mx): one K group (128 values) is a single scaled
+// 16x16x128 fp4 x fp8 MFMA, so the waves split the tile instead: 64 rows x
+// 128 columns per 256-thread block (224 blocks for M = 256, N = 7168), each
+// wave 32 rows x 64 columns (2 x 4 MFMA blocks).  E2M1 code tiles and their
+// E8M0 scale words are fed to the MFMA as stored; the per-token FP8 scale is
+// applied in the epilogue.  Six LDS stages of one group each (activations,
+// the eight code tiles, their scale words), copied five groups ahead; the
+// fragments of the next group are read during the current one.
 #include <algorithm>
 
 #include "common.h"
@@ -46,6 +55,21 @@ constexpr int kMidCopies = 8 + 2;                // copies per wave per group
 
 struct MidTile {
   int64_t e, m0, nb0, rows, first;
+};
+
+constexpr int kMxM = 64;                         // rows per W4A8 tile
+constexpr int kMxCB = 8;                         // 16-column blocks per W4A8 tile (128 columns)
+constexpr int kMxStages = 6;                     // one K group each, copied five ahead
+constexpr int kMxSB = 8 * 1024 + kMxCB * 1024 + kMxCB * 256;   // activations, code tiles, scale words
+constexpr int kMxLds = kMxStages * kMxSB;        // 108 KiB
+constexpr int kMxCopies = 6;                     // copies per wave per group
+
+// One group's operands of a wave: its four code tiles and their scale words,
+// and both 16-byte halves of its two row blocks' activation fragments.
+struct MxFrag {
+  u32x4_t wq[4];
+  uint32_t ws[4];
+  u32x4_t b0[2], b1[2];
 };
 
 }  // namespace
@@ -361,6 +385,210 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
   }
 }
 
+template <bool GROUPED>
+__global__ void __launch_bounds__(256, 1)
+k_gemm_mid_mx(GemmArgs a, int tiles_n, int tiles_m) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  __shared__ int32_t orow_s[GROUPED ? kMxM : 1];   // output row of each local row, or -1
+  __shared__ int32_t arow_s[GROUPED ? kMxM : 1];   // activation row of each local row
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_l = lane & 15, q_l = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;         // rows 32 wm .. + 31, column blocks 4 wn .. 4 wn + 3
+  const Geom G = a.G;
+  const int64_t row_bytes = G.K;                   // fp8 activations
+  const int KG = (int)G.KG;
+  // grouped items: (128-row unit, 64-row half, 128-column tile)
+  const int64_t n_items = GROUPED ? (int64_t)a.hdr[1] * 2 * tiles_n : (int64_t)tiles_n * tiles_m;
+
+  auto act_row = [&](int32_t pair) -> int64_t {
+    if (pair < 0 || pair >= a.P) return 0;
+    return a.rows_are_pairs ? pair : pair / a.topk;
+  };
+  const rsrc_t rsz = make_rsrc(a.w + G.off_scales, G.total - G.off_scales);
+  // operand rows 16 rb + n_l: 16-byte K chunks q_l and 4 + q_l, at slot
+  // c ^ ((r >> 1) & 7) of the row (the copies place them so)
+  const int xsw = (n_l >> 1) & 7;
+  const uint32_t xo0 = n_l * 128 + 16 * (q_l ^ xsw), xo1 = n_l * 128 + 16 * ((4 + q_l) ^ xsw);
+
+  int64_t item = blockIdx.x;
+  for (; item < n_items; item += gridDim.x) {
+    MidTile t;
+    if (GROUPED) {
+      const int64_t unit = item / (2 * tiles_n);
+      const int half = (int)((item / tiles_n) & 1);
+      const int32_t* u = a.units + 4 * unit;
+      t.e = u[0];
+      t.first = (int64_t)u[1] + kMxM * half;
+      t.rows = std::min<int64_t>((int64_t)u[2] - kMxM * half, kMxM);
+      t.m0 = 0;
+      t.nb0 = (item % tiles_n) * kMxCB;
+      if (t.rows <= 0) continue;                   // block-uniform: a unit of <= 64 rows
+    } else {
+      const int total = tiles_n * tiles_m;
+      const int xcd = (int)(item % 8), idx = (int)(item / 8);
+      const int base = total / 8, extra = total % 8;
+      const int tt = (total >= 8) ? xcd * base + (xcd < extra ? xcd : extra) + idx : (int)item;
+      t.e = 0;
+      t.first = 0;
+      t.m0 = (int64_t)(tt % tiles_m) * kMxM;
+      t.nb0 = (int64_t)(tt / tiles_m) * kMxCB;
+      t.rows = (a.M - t.m0) < kMxM ? (a.M - t.m0) : kMxM;
+    }
+    // ---- copy descriptors: activation copy j = 2 w + q covers rows 8 j ..
+    // 8 j + 7 (lane L: row 8 j + L / 8, slot L % 8); weight copies k = 0, 1
+    // the code tile and scale words of column block 2 w + k
+    const rsrc_t rx = make_rsrc(reinterpret_cast<const uint8_t*>(a.x) + t.m0 * row_bytes,
+                                GROUPED ? 0xFFFFFFFFull : (uint64_t)t.rows * row_bytes);
+    uint32_t xoff[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = 8 * (2 * wave + q) + (lane >> 3);
+      const int rc = r < t.rows ? r : (int)t.rows - 1;
+      const int64_t src = GROUPED ? act_row(a.sorted_pairs[t.first + rc]) : rc;
+      xoff[q] = (uint32_t)(src * row_bytes) + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+    }
+    const int64_t wb = t.e * G.NB;
+    const rsrc_t rw = make_rsrc(a.w + (wb + t.nb0) * G.KG * 1024, (uint64_t)kMxCB * G.KG * 1024);
+    uint32_t wvo[2], svo[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      int64_t nb = t.nb0 + 2 * wave + k;
+      if (nb >= G.NB) nb = G.NB - 1;
+      wvo[k] = (uint32_t)((nb - t.nb0) * G.KG * 1024 + lane * 16);
+      svo[k] = (uint32_t)((wb + nb) * G.KG4 * 256 + lane * 4);
+    }
+    if (GROUPED && tid < kMxM) {
+      const int32_t p = tid < t.rows ? a.sorted_pairs[t.first + tid] : -1;
+      orow_s[tid] = (p >= 0 && p < a.P) ? p : -1;
+      arow_s[tid] = (int32_t)act_row(p);
+    }
+    uint32_t so[kMxStages];
+#pragma unroll
+    for (int i = 0; i < kMxStages; ++i) so[i] = (uint32_t)(i * kMxSB);
+    // the six copies of group g into the stage at offset st (q = 0, 1
+    // activations, 2, 3 code tiles, 4, 5 scale words)
+    auto dma = [&](int q, int g, uint32_t st) {
+      uint8_t* d = lds + st;
+      if (q < 2) b2lds16(rx, xoff[q], (uint32_t)(g * 128), d + (2 * wave + q) * 1024);
+      else if (q < 4) b2lds16(rw, wvo[q - 2], (uint32_t)(g * 1024), d + 8 * 1024 + (2 * wave + q - 2) * 1024);
+      else b2lds4(rsz, svo[q - 4], (uint32_t)((g / 4) * 256), d + 16 * 1024 + (2 * wave + q - 4) * 256);
+    };
+    // ---- prologue: groups 0 .. 4 (past the end: repeats of the last), then
+    // wait for groups 0 and 1
+#pragma unroll
+    for (int i = 0; i < kMxStages - 1; ++i)
+#pragma unroll
+      for (int q = 0; q < kMxCopies; ++q) dma(q, std::min(i, KG - 1), so[i]);
+    __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(3 * kMxCopies) : "memory");
+
+    auto load = [&](MxFrag& f, uint32_t st) {
+      const uint8_t* wbase = lds + st + 8 * 1024 + 4 * wn * 1024 + lane * 16;
+      const uint8_t* sbase = lds + st + 16 * 1024 + 4 * wn * 256 + lane * 4;
+      const uint8_t* xbase = lds + st + wm * 2 * 2048;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        f.wq[c] = ld16(wbase + c * 1024);
+        f.ws[c] = *reinterpret_cast<const uint32_t*>(sbase + c * 256);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f.b0[rb] = ld16(xbase + rb * 2048 + xo0);
+        f.b1[rb] = ld16(xbase + rb * 2048 + xo1);
+      }
+    };
+    f32x4_t acc[4][2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) acc[c][rb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    // Group g: eight MFMAs from fragments read during group g - 1, while the
+    // fragments of group g + 1 (landed two groups ago) are read and the
+    // copies of group g + 5 go out, one after each MFMA from the second.
+    auto group = [&](int g, const MxFrag& cur, MxFrag& nxt) {
+      load(nxt, so[1]);
+      const int dg = std::min(g + kMxStages - 1, KG - 1);
+      const uint32_t dst = so[kMxStages - 1];
+      const int sh = 8 * (g & 3);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = i & 3, rb = i >> 2;
+        acc[c][rb] = mfma_fp4_fp8(cur.wq[c], cur.b0[rb], cur.b1[rb], acc[c][rb], (int)((cur.ws[c] >> sh) & 0xFFu), 127);
+        if (i >= 1 && i <= kMxCopies) dma(i - 1, dg, dst);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const uint32_t s0 = so[0];
+#pragma unroll
+      for (int i = 0; i + 1 < kMxStages; ++i) so[i] = so[i + 1];
+      so[kMxStages - 1] = s0;
+      // all but the last three groups' copies: group g + 2 has landed
+      __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(3 * kMxCopies) : "memory");
+    };
+    MxFrag f0, f1;
+    load(f0, so[0]);
+    int g = 0;
+#pragma nounroll
+    for (; g + 1 < KG; g += 2) {
+      group(g, f0, f1);
+      group(g + 1, f1, f0);
+    }
+    if (g < KG) group(g, f0, f1);
+
+    // ---- epilogue: lane holds C[n = 16 (4 wn + c) + 4 q_l + r][row = 32 wm +
+    // 16 rb + n_l]; rows scaled by their token scale, staged as bf16 (8-byte
+    // unit u of row r at u ^ 2 (r % 16), 256 bytes per row), then stored as
+    // 16-byte chunks, 16 lanes per row
+    float rs[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int lr = 32 * wm + 16 * rb + n_l;
+      const int lc = lr < t.rows ? lr : 0;
+      rs[rb] = a.xs[GROUPED ? (int64_t)arow_s[lc] : t.m0 + lc];
+    }
+    __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = 32 * wm + 16 * rb + n_l;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4_t v = acc[c][rb] * rs[rb];
+        const int u = 4 * (4 * wn + c) + q_l;
+        *reinterpret_cast<u32x2_t*>(lds + r * 256 + (u ^ (2 * (r & 15))) * 8) =
+            (u32x2_t){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      }
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 16 * k + (tid >> 4), c16 = tid & 15;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + r * 256 + ((2 * c16) ^ (2 * (r & 15))) * 8);
+      if (r < t.rows) {
+        const int64_t row = GROUPED ? (int64_t)orow_s[r] : t.m0 + r;
+        if (row >= 0) store_bf16x8(a.y + row * G.N, G.N, t.nb0 * 16 + 8 * c16, v);
+      }
+    }
+    // the next tile's copies overwrite the staging and the row tables
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
+template <bool GROUPED>
+static hipError_t go_mid_mx(const GemmArgs& a, int grid_items, hipStream_t st) {
+  auto kern = &k_gemm_mid_mx<GROUPED>;
+  static const hipError_t attr_err = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+  if (attr_err != hipSuccess) return attr_err;
+  const int tiles_n = (int)((a.G.NB + kMxCB - 1) / kMxCB);
+  const int tiles_m = GROUPED ? 0 : (int)((a.M + kMxM - 1) / kMxM);
+  const int64_t tiles = (int64_t)tiles_n * tiles_m;
+  if (!GROUPED && tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const unsigned grid = GROUPED ? (unsigned)(grid_items > 0 ? grid_items : 1) : (unsigned)tiles;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), kMxLds, st, a, tiles_n, tiles_m);
+  return hipGetLastError();
+}
+
 template <bool ZP, bool GROUPED>
 static hipError_t go_mid(const GemmArgs& a, int grid_items, hipStream_t st) {
   auto kern = &k_gemm_mid<ZP, GROUPED>;
@@ -376,17 +604,19 @@ static hipError_t go_mid(const GemmArgs& a, int grid_items, hipStream_t st) {
   return hipGetLastError();
 }
 
-int64_t mid_n_tiles(const Geom& G) { return (G.NB + kMidCB - 1) / kMidCB; }
+int64_t mid_n_tiles(const Geom& G, bool mx) {
+  return mx ? 2 * ((G.NB + kMxCB - 1) / kMxCB) : (G.NB + kMidCB - 1) / kMidCB;
+}
 
 hipError_t launch_gemm_mid(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
-  if (a.wfmt == W_MXFP4) return hipErrorInvalidValue;
   // scale and zero-point copies use 32-bit offsets from the scale region
   if (a.G.total - a.G.off_scales > 0xFFFFFFFFull) return hipErrorInvalidValue;
   // grouped activation rows are addressed by 32-bit offsets from x
   if (grouped) {
     const int64_t xrows = a.rows_are_pairs ? a.P : (a.P + a.topk - 1) / a.topk;
-    if (xrows * 2 * a.G.K > 0xFFFFFFFFll) return hipErrorInvalidValue;
+    if (xrows * (a.wfmt == W_MXFP4 ? 1 : 2) * a.G.K > 0xFFFFFFFFll) return hipErrorInvalidValue;
   }
+  if (a.wfmt == W_MXFP4) return grouped ? go_mid_mx<true>(a, grid_items, st) : go_mid_mx<false>(a, 0, st);
   if (a.wfmt == W_UINT4_ZP)
     return grouped ? go_mid<true, true>(a, grid_items, st) : go_mid<true, false>(a, 0, st);
   return grouped ? go_mid<false, true>(a, grid_items, st) : go_mid<false, false>(a, 0, st);

@@ -61,11 +61,12 @@ constexpr int kTileM = 128;
 constexpr int kTileN = 128;
 hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
 
-// W4A16 MFMA kernel with 128 x 64 output tiles (K groups split over the four
-// waves).  Dense: one block per tile.  Grouped: persistent over (tile unit x
-// 64-column tile) items, hdr[1] units of up to 128 rows.
+// Mid-M MFMA kernels: W4A16 128 x 64 output tiles (K groups split over the
+// four waves), W4A8-MXFP4 64 x 128 tiles.  Dense: one block per tile.
+// Grouped: persistent over items of hdr[1] units of up to 128 rows; items
+// per unit from mid_n_tiles (MXFP4: two 64-row halves per column tile).
 hipError_t launch_gemm_mid(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
-int64_t mid_n_tiles(const Geom& G);
+int64_t mid_n_tiles(const Geom& G, bool mx);
 
 // MFMA kernel with 256 x 256 output tiles.  Dense: one block per tile.
 // Grouped: persistent over (256-row unit x 256-column tile) items, hdr[2] units.
