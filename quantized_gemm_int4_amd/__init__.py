@@ -4,7 +4,7 @@ Thin argument marshalling only: every function takes torch tensors (device
 memory), passes their data pointers, sizes and the current HIP stream to the C
 entry point of the same name, and raises HmError on a non-zero status.  All
 work runs in the library's HIP kernels.  Importing this package fails loudly if
-libhm.so has not been built (python -m quantized_gemm_int4_amd.build).
+libhm.so has not been built (python quantized_gemm_int4_amd/build.py).
 
 The C functions are declared and documented in include/hm.h.
 """
@@ -45,7 +45,7 @@ def wdesc(wfmt, n, k, num_experts=1):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m quantized_gemm_int4_amd.build` (needs hipcc)")
+                          "`python quantized_gemm_int4_amd/build.py` (needs hipcc)")
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     D = ctypes.POINTER(hm_wdesc)

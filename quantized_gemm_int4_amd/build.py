@@ -1,6 +1,6 @@
 """Build of the HIP library libhm.so (gfx950) in-tree.
 
-    python -m quantized_gemm_int4_amd.build
+    python quantized_gemm_int4_amd/build.py
 
 compiles every source under csrc/ with hipcc into _build/ at the repository
 root and links quantized_gemm_int4_amd/libhm.so.  It always recompiles.
