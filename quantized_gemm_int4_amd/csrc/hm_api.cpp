@@ -245,9 +245,14 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* 
   if (p.stream)
     snprintf(buf, buf_len, "%s stream mb=%d nbw=%d ks=%d splits=%d ksg=%d mfma=%s", w, p.sc.mb,
              p.sc.nbw, p.sc.ks, p.sc.splits, p.ksg, d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
-  else if (p.big)
-    snprintf(buf, buf_len, "%s tile 256x256 waves=%s mfma=%s", w, d->wfmt == HM_W_MXFP4 ? "4x2" : "1x4",
-             d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "32x32x16_bf16");
+  else if (p.big) {
+    const Geom G = make_geom(d->wfmt, 1, d->n, d->k);
+    const int64_t tiles = big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows);
+    const int64_t halves = 2 * (tiles - big_full_tiles(G, m, d->wfmt == HM_W_MXFP4));
+    snprintf(buf, buf_len, "%s tile 256x256 waves=%s mfma=%s half_tiles=%lld", w,
+             d->wfmt == HM_W_MXFP4 ? "4x2" : "1x4", d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "32x32x16_bf16",
+             (long long)halves);
+  }
   else if (p.mid && d->wfmt == HM_W_MXFP4)
     snprintf(buf, buf_len, "%s tile 64x128 waves=2x2 mfma=scale_16x16x128_f8f6f4", w);
   else if (p.mid)

@@ -101,9 +101,95 @@ struct BigCopy {
 // last steps of a tile copy the first steps of the block's next tile, whose
 // MFMAs then start right after this tile's epilogue, and the output stores
 // drain while the next tile computes.
+// W4A16 K-step loop of one tile (the body of k_gemm_big below, written once
+// and expanded there for MB_ = 8 or 4 32-row blocks; it uses the kernel's
+// locals).  A function or lambda here would make the compiler keep the two
+// copy-descriptor sets in scratch memory.
+#define HM_BIG_W4A16_STEPS(MB_)                                                                                     \
+  do {                                                                                                              \
+        constexpr int MB = MB_;                                                                                     \
+        constexpr int NI = 4 * MB;                                                                                  \
+        constexpr int WPI = 32 / NI;                                                                                \
+_Pragma("nounroll")                                                                                                 \
+        for (int s = 0; s < S; ++s) {                                                                               \
+          if (GROUPED && chained && s == 1) {                                                                       \
+            write_table(tp);                                                                                        \
+            if (has_next) nc = make_copy(nxt, prn);                                                                 \
+          }                                                                                                         \
+          const int KGt = S >> 1;                                                                                   \
+          const int t2 = s + 2, tg = (s >> 1) + 2, wh = s & 1;                                                      \
+          const bool xnext = chained && has_next && t2 >= S, wnext = chained && has_next && tg >= KGt;              \
+          const int xls = t2 < S ? t2 : (xnext ? t2 - S : S - 1);                                                   \
+          const int wg = tg < KGt ? tg : (wnext ? tg - KGt : KGt - 1);                                              \
+          uint8_t* d2 = lds + so[2];                                                                                \
+          uint8_t* dw = lds + wso[2];                                                                               \
+          auto dma = [&](int q) __attribute__((always_inline)) {                                                    \
+            if (q < NX) {                                                                                           \
+              const rsrc_t r = xnext ? nc.rx : cc.rx;                                                               \
+              b2lds16(r, xnext ? nc.xoff[q] : cc.xoff[q], (uint32_t)(xls * 128), d2 + (NX * wave + q) * 1024);      \
+            } else if (q < NX + 2) {                                                                                \
+              const rsrc_t r = wnext ? nc.rw : cc.rw;                                                               \
+              const int k0 = q - NX;                                                                                \
+              if (wh == 0)                                                                                          \
+                b2lds16(r, wnext ? nc.wvo[k0] : cc.wvo[k0], (uint32_t)(wg * 1024),                                  \
+                        dw + kWOff + (NWT * wave + k0) * 1024);                                                     \
+              else                                                                                                  \
+                b2lds16(r, wnext ? nc.wvo[2 + k0] : cc.wvo[2 + k0], (uint32_t)(wg * 1024),                          \
+                        dw + kWOff + (NWT * wave + 2 + k0) * 1024);                                                 \
+            } else {                                                                                                \
+              b2lds4(rsz, (wnext ? nc.svo[0] : cc.svo[0]) + (uint32_t)wg * szstride, 0u, dw + kSOff + wave * 256);  \
+            }                                                                                                       \
+          };                                                                                                        \
+          const uint8_t* xs = lds + so[0];                                                                          \
+          uint32_t wv[2][4];                                                                                        \
+          float svn[2], zsn[2];                                                                                     \
+          fetch(lds + ((s & 1) ? wso[1] : wso[0]), (s + 1) & 1, wv, svn, zsn);                                      \
+          u32x4_t b[NI];                                                                                            \
+_Pragma("unroll")                                                                                                   \
+          for (int i = 0; i < kD; ++i) b[i] = ld16(xs + (i % MB) * 4096 + xo[i / MB]);                              \
+          uint32_t lo = 0, hi4 = 0;                                                                                 \
+_Pragma("unroll")                                                                                                   \
+          for (int i = 0; i < NI; ++i) {                                                                            \
+            const int kq = i / MB, mb = i % MB;                                                                     \
+_Pragma("unroll")                                                                                                   \
+            for (int nb2 = 0; nb2 < 2; ++nb2) acc[nb2][mb] = mfma32_bf16(af[nb2][kq], b[i], acc[nb2][mb]);          \
+            if (i + kD < NI) {                                                                                      \
+              const int j = i + kD;                                                                                 \
+              b[j] = ld16(xs + (j % MB) * 4096 + xo[j / MB]);                                                       \
+            }                                                                                                       \
+_Pragma("unroll")                                                                                                   \
+            for (int e = 0; e < WPI; ++e) {                                                                         \
+              const int wi = WPI * i + e, nb2 = (wi >> 2) & 1, u = wi & 3;                                          \
+              const uint32_t w = kq == 0 ? w3c[nb2] : wv[nb2][kq - 1];                                              \
+              const float sv = kq == 0 ? sv3c[nb2] : svn[nb2], zs = kq == 0 ? zs3c[nb2] : zsn[nb2];                 \
+              if (u == 0) {                                                                                         \
+                lo = in_vgpr(w & 0x0F0F0F0Fu);                                                                      \
+                hi4 = in_vgpr((w >> 4) & 0x0F0F0F0Fu);                                                              \
+              }                                                                                                     \
+              af[nb2][(kq + 3) & 3][u] = dq8_word(lo, hi4, u, sv, zs);                                              \
+            }                                                                                                       \
+            if (MB == 8) {                                                                                          \
+              if ((i & 1) && (i >> 1) < kPer) dma(i >> 1);                                                          \
+            } else {                                                                                                \
+              if (i >= 1 && i - 1 < kPer) dma(i - 1);                                                               \
+            }                                                                                                       \
+            __builtin_amdgcn_sched_barrier(0);                                                                      \
+          }                                                                                                         \
+_Pragma("unroll")                                                                                                   \
+          for (int nb2 = 0; nb2 < 2; ++nb2) {                                                                       \
+            w3c[nb2] = wv[nb2][3];                                                                                  \
+            sv3c[nb2] = svn[nb2];                                                                                   \
+            zs3c[nb2] = zsn[nb2];                                                                                   \
+          }                                                                                                         \
+          wait_barrier(std::integral_constant<int, kPer>());                                                        \
+          rotate();                                                                                                 \
+          if (s & 1) rotate_w();                                                                                    \
+        }                                                                                                           \
+  } while (0)
+
 template <bool MX, bool ZP, bool GROUPED>
 __global__ void __launch_bounds__(big_threads(MX), 1)
-k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
+k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
   constexpr int SB = big_stage_bytes(MX);
   constexpr int NW = big_threads(MX) / 64;         // waves
   constexpr int NX = 32 / NW;                      // activation copies per lane per step
@@ -120,11 +206,13 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   const int64_t row_bytes = MX ? G.K : 2 * G.K;
   const int S = (int)(MX ? G.KG : 2 * G.KG);      // K steps per tile
   const bool chained = S >= 3;
-  const int64_t n_items = GROUPED ? (int64_t)a.hdr[2] * tiles_n : (int64_t)tiles_n * tiles_m;
+  // dense: tiles n_full.. of the visiting order run as two 128-row halves
+  const int64_t n_items = GROUPED ? (int64_t)a.hdr[2] * tiles_n
+                                  : (int64_t)n_full + 2 * ((int64_t)tiles_n * tiles_m - n_full);
   int64_t item = blockIdx.x;
   if (item >= n_items) return;
 
-  auto decode = [&](int64_t it) -> BigTile {
+  auto decode = [&](int64_t it) __attribute__((always_inline)) -> BigTile {
     BigTile t;
     if (GROUPED) {
       const int32_t* u = a.units + 4 * (it / tiles_n);
@@ -135,9 +223,20 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
       t.nb0 = (it % tiles_n) * kBigCB;
     } else {
       const int total = tiles_n * tiles_m;
-      const int xcd = (int)(it % 8), idx = (int)(it / 8);
-      const int base = total / 8, extra = total % 8;
-      const int tt = xcd * base + (xcd < extra ? xcd : extra) + idx;
+      // item j of a range of cnt items -> its position in the range: the
+      // items of one XCD (j % 8) take a contiguous part
+      auto spread = [](int j, int cnt) __attribute__((always_inline)) {
+        const int xcd = j % 8, idx = j / 8, base = cnt / 8, extra = cnt % 8;
+        return xcd * base + (xcd < extra ? xcd : extra) + idx;
+      };
+      int tt, half = -1;
+      if (it < n_full) {
+        tt = spread((int)it, n_full);
+      } else {
+        const int h = spread((int)(it - n_full), 2 * (total - n_full));
+        tt = n_full + (h >> 1);
+        half = h & 1;
+      }
       constexpr int GM = 4;
       const int grp = tt / (GM * tiles_n);
       const int first_m = grp * GM;
@@ -146,19 +245,20 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
       const int tm = first_m + tin % gm, tn = tin / gm;
       t.e = 0;
       t.first = 0;
-      t.m0 = (int64_t)tm * kBigM;
+      t.m0 = (int64_t)tm * kBigM + (half > 0 ? kBigM / 2 : 0);
       t.nb0 = (int64_t)tn * kBigCB;
-      t.rows = (a.M - t.m0) < kBigM ? (a.M - t.m0) : kBigM;
+      const int64_t cap = half >= 0 ? kBigM / 2 : kBigM;
+      t.rows = (a.M - t.m0) < cap ? (a.M - t.m0) : cap;
     }
     return t;
   };
   // grouped: activation row of a sorted pair (invalid pairs read row 0 and are not stored)
-  auto act_row = [&](int32_t pair) -> int64_t {
+  auto act_row = [&](int32_t pair) __attribute__((always_inline)) -> int64_t {
     if (pair < 0 || pair >= a.P) return 0;
     return a.rows_are_pairs ? pair : pair / a.topk;
   };
   // grouped: sorted pair of local row r, clamped to the tile
-  auto pair_of = [&](const BigTile& t, int r) -> int32_t {
+  auto pair_of = [&](const BigTile& t, int r) __attribute__((always_inline)) -> int32_t {
     return a.sorted_pairs[t.first + (r < t.rows ? r : t.rows - 1)];
   };
 
@@ -174,7 +274,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   // (tile (L / 2) % 4, word L % 2)
   const bool zlane = !MX && ZP && lane >= 32 && lane < 40;
   const uint32_t szstride = zlane ? 8 : 32;
-  auto make_copy = [&](const BigTile& t, const int32_t (&pr)[NX]) -> Copy {
+  auto make_copy = [&](const BigTile& t, const int32_t (&pr)[NX]) __attribute__((always_inline)) -> Copy {
     Copy c;
     c.rx = make_rsrc(reinterpret_cast<const uint8_t*>(a.x) + t.m0 * row_bytes,
                      GROUPED ? 0xFFFFFFFFull : (uint64_t)t.rows * row_bytes);
@@ -183,7 +283,8 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int r = 8 * (NX * wave + i) + (lane >> 3);
-      const int64_t src = GROUPED ? act_row(pr[i]) : (r < t.rows ? r : t.rows - 1);
+      // dense rows past the tile's end lie outside the buffer: zeros, no memory traffic
+      const int64_t src = GROUPED ? act_row(pr[i]) : (r < t.rows ? r : t.rows);
       c.xoff[i] = (uint32_t)(src * row_bytes) + 16 * ((lane & 7) ^ ((r >> 1) & 7));
     }
 #pragma unroll
@@ -203,12 +304,12 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
     return c;
   };
   // grouped: this thread's copy rows of tile t, and its row of the tables
-  auto load_rows = [&](const BigTile& t, int32_t (&pr)[NX], int32_t& tp) {
+  auto load_rows = [&](const BigTile& t, int32_t (&pr)[NX], int32_t& tp) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NX; ++i) pr[i] = pair_of(t, 8 * (NX * wave + i) + (lane >> 3));
     tp = (tid < t.rows) ? a.sorted_pairs[t.first + tid] : -1;
   };
-  auto write_table = [&](int32_t tp) {
+  auto write_table = [&](int32_t tp) __attribute__((always_inline)) {
     if (GROUPED && tid < kBigM) {
       const bool ok = tp >= 0 && tp < a.P;
       arow_s[tid] = (int32_t)act_row(tp);
@@ -218,17 +319,17 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   // LDS offsets of the stages of the current step and the next two (the one
   // after those is the current one again), rotated after every step
   uint32_t so[3] = {0u, (uint32_t)SB, 2u * SB};
-  auto rotate = [&]() {
+  auto rotate = [&]() __attribute__((always_inline)) {
     const uint32_t t = so[0];
     so[0] = so[1];
     so[1] = so[2];
     so[2] = t;
   };
-  auto copy_x = [&](const Copy& c, int ls, uint8_t* stg) {
+  auto copy_x = [&](const Copy& c, int ls, uint8_t* stg) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NX; ++i) b2lds16(c.rx, c.xoff[i], (uint32_t)(ls * 128), stg + (NX * wave + i) * 1024);
   };
-  auto wait_barrier = [&](auto n_c) {
+  auto wait_barrier = [&](auto n_c) __attribute__((always_inline)) {
     // wait for this wave's copies except the n most recent vector-memory
     // operations and for its LDS operations, then meet the other waves; the
     // memory clobber keeps the compiler from moving LDS accesses across
@@ -236,8 +337,8 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   };
   // LDS-only barrier for the epilogue's staging: the output stores drain on
   // their own (the next step's wait covers them, vector memory completes in order)
-  auto lds_barrier = [&]() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-  auto local_row = [&](const BigTile& t, int64_t r, int64_t& out, int64_t& in) {
+  auto lds_barrier = [&]() __attribute__((always_inline)) { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  auto local_row = [&](const BigTile& t, int64_t r, int64_t& out, int64_t& in) __attribute__((always_inline)) {
     if (r >= t.rows) { out = -1; in = 0; return; }
     out = GROUPED ? (int64_t)orow_s[r] : t.m0 + r;
     in = GROUPED ? (int64_t)arow_s[r] : t.m0 + r;
@@ -248,7 +349,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
   // next tile's first step), 512 bytes per row with 8-byte unit u of row r
   // at unit u ^ g(r); each thread then stores 16-byte chunks, 32 lanes per
   // row, so every store writes whole 128-byte lines.
-  auto store_slab = [&](const BigTile& t, const uint8_t* ost, int p, auto gfun) {
+  auto store_slab = [&](const BigTile& t, const uint8_t* ost, int p, auto gfun) __attribute__((always_inline)) {
     constexpr int RS = 2 * NW;                     // rows per sweep of the block
 #pragma unroll
     for (int k = 0; k < 64 / RS; ++k) {
@@ -279,7 +380,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
     const uint32_t xo0 = n_l * 128 + 16 * (q_l ^ xsw), xo1 = n_l * 128 + 16 * ((4 + q_l) ^ xsw);
     // copies of one stage: activations, weight tiles (column blocks w and
     // w + 8) and their scale words
-    auto copy_stage = [&](const Copy& c, int ls, uint8_t* st) {
+    auto copy_stage = [&](const Copy& c, int ls, uint8_t* st) __attribute__((always_inline)) {
       copy_x(c, ls, st);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -338,7 +439,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
         const bool xnext = chained && has_next && t2 >= S;
         const int ls = t2 < S ? t2 : (xnext ? t2 - S : S - 1);
         uint8_t* d2 = lds + so[2];
-        auto dma = [&](int q) {
+        auto dma = [&](int q) __attribute__((always_inline)) {
           const Copy& c = xnext ? nc : cc;
           if (q < 4) {
             b2lds16(c.rx, c.xoff[q], (uint32_t)(ls * 128), d2 + (4 * wave + q) * 1024);
@@ -447,14 +548,14 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
     // (scales at 0, zero-point words at 128), repeated in both steps.
     constexpr int kWOff = 32 * 1024, kSOff = 48 * 1024;
     uint32_t wso[3] = {0u, (uint32_t)SB, 2u * SB};
-    auto rotate_w = [&]() {
+    auto rotate_w = [&]() __attribute__((always_inline)) {
       const uint32_t t = wso[0];
       wso[0] = wso[1];
       wso[1] = wso[2];
       wso[2] = t;
     };
     // all four tiles of group g and the gather
-    auto copy_w = [&](const Copy& c, int g, uint8_t* slot) {
+    auto copy_w = [&](const Copy& c, int g, uint8_t* slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < NWT; ++k)
         b2lds16(c.rw, c.wvo[k], (uint32_t)(g * 1024), slot + kWOff + (NWT * wave + k) * 1024);
@@ -466,7 +567,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
     // l32 % 16; K = 64 h + 16 kq + 8 hi is word 2 h + kq / 2 of slot
     // (l32 % 16) + 16 ((2 kq + hi) % 4).
     const int c_l = l32 >> 4, c16 = l32 & 15;
-    auto fetch = [&](const uint8_t* stg, int h, uint32_t (&wv)[2][4], float (&sv)[2], float (&zs)[2]) {
+    auto fetch = [&](const uint8_t* stg, int h, uint32_t (&wv)[2][4], float (&sv)[2], float (&zs)[2]) __attribute__((always_inline)) {
       const uint8_t* sz = stg + kSOff + wave * 256;
 #pragma unroll
       for (int nb2 = 0; nb2 < 2; ++nb2) {
@@ -525,119 +626,50 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[nb2][mb][r] = 0.f;
-      // Step s runs its 64 MFMAs K part by K part (kq = 0..3; row blocks
-      // 0..7, each activation fragment feeding both column halves, so no
+      // Step s runs its MFMAs K part by K part (kq = 0..3; row blocks 0..MB-1,
+      // each activation fragment feeding both column halves, so no
       // accumulator is updated twice in a row) with the fragments read kD
       // fragments ahead.  Operands (nb2, kq) are free once their MFMAs are
       // issued, so the unpacking follows behind: during K part 0 operands
       // (nb2, 3) of this step (from the words carried over), during K part
       // kq = 1..3 operands (nb2, kq - 1) of the next step (this tile's or, at
-      // the last step, the next tile's first), one result word per two
-      // MFMAs.  The scheduling barriers keep this interleaving as written.
-      // Each step first issues the activations of step s + 2 and the weights
-      // of step s + 3 (of this tile or the next, else repeats of this tile's
-      // last step into parts no longer read), so the wait count is exact.
+      // the last step, the next tile's first), 32 result words spread evenly
+      // over the step's MFMA pairs.  The scheduling barriers keep this
+      // interleaving as written.  Each step first issues the activations of
+      // step s + 2 and the weights of step s + 3 (of this tile or the next,
+      // else repeats of this tile's last step into parts no longer read), so
+      // the wait count is exact.  A tile of at most 128 rows (a half tile, or
+      // the last rows of M) runs only row blocks 0..3.
       constexpr int kD = 4;
-#pragma nounroll
-      for (int s = 0; s < S; ++s) {
-        if (GROUPED && chained && s == 1) {
-          write_table(tp);
-          if (has_next) nc = make_copy(nxt, prn);
-        }
-        // activations of step s + 2 into stage so[2], half of the weights of
-        // group s / 2 + 2 into group slot wso[2]: this tile's, the next
-        // tile's, or (none left) repeats of this tile's last into parts no
-        // longer read.  Copy q of the step is issued after MFMA pair 2 q + 1,
-        // so the in-order issue never holds the matrix core up behind a
-        // burst of copies.
-        const int KGt = S >> 1;
-        const int t2 = s + 2, tg = (s >> 1) + 2, wh = s & 1;
-        const bool xnext = chained && has_next && t2 >= S, wnext = chained && has_next && tg >= KGt;
-        const int xls = t2 < S ? t2 : (xnext ? t2 - S : S - 1);
-        const int wg = tg < KGt ? tg : (wnext ? tg - KGt : KGt - 1);
-        uint8_t* d2 = lds + so[2];
-        uint8_t* dw = lds + wso[2];
-        auto dma = [&](int q) {
-          if (q < NX) {
-            const Copy& c = xnext ? nc : cc;
-            b2lds16(c.rx, c.xoff[q], (uint32_t)(xls * 128), d2 + (NX * wave + q) * 1024);
-          } else if (q < NX + 2) {
-            // tile 2 wh + (q - NX): a branch per half keeps the index constant
-            const Copy& c = wnext ? nc : cc;
-            const int k0 = q - NX;
-            if (wh == 0) b2lds16(c.rw, c.wvo[k0], (uint32_t)(wg * 1024), dw + kWOff + (NWT * wave + k0) * 1024);
-            else b2lds16(c.rw, c.wvo[2 + k0], (uint32_t)(wg * 1024), dw + kWOff + (NWT * wave + 2 + k0) * 1024);
-          } else {
-            const Copy& c = wnext ? nc : cc;
-            b2lds4(rsz, c.svo[0] + (uint32_t)wg * szstride, 0u, dw + kSOff + wave * 256);
-          }
-        };
-        const uint8_t* xs = lds + so[0];
-        uint32_t wv[2][4];
-        float svn[2], zsn[2];
-        fetch(lds + ((s & 1) ? wso[1] : wso[0]), (s + 1) & 1, wv, svn, zsn);
-        u32x4_t b[32];
-#pragma unroll
-        for (int i = 0; i < kD; ++i) b[i] = ld16(xs + (i & 7) * 4096 + xo[i >> 3]);
-        uint32_t lo = 0, hi4 = 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int kq = i >> 3, mb = i & 7;
-#pragma unroll
-          for (int nb2 = 0; nb2 < 2; ++nb2) acc[nb2][mb] = mfma32_bf16(af[nb2][kq], b[i], acc[nb2][mb]);
-          if (i + kD < 32) {
-            const int j = i + kD;
-            b[j] = ld16(xs + (j & 7) * 4096 + xo[j >> 3]);
-          }
-          {
-            const int nb2 = (i & 7) >> 2, u = i & 3;   // result word u of operand (nb2, (kq + 3) % 4)
-            const uint32_t w = kq == 0 ? w3c[nb2] : wv[nb2][kq - 1];
-            const float sv = kq == 0 ? sv3c[nb2] : svn[nb2], zs = kq == 0 ? zs3c[nb2] : zsn[nb2];
-            if (u == 0) {
-              lo = in_vgpr(w & 0x0F0F0F0Fu);
-              hi4 = in_vgpr((w >> 4) & 0x0F0F0F0Fu);
-            }
-            af[nb2][(kq + 3) & 3][u] = dq8_word(lo, hi4, u, sv, zs);
-          }
-          if ((i & 1) && (i >> 1) < kPer) dma(i >> 1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int nb2 = 0; nb2 < 2; ++nb2) {
-          w3c[nb2] = wv[nb2][3];
-          sv3c[nb2] = svn[nb2];
-          zs3c[nb2] = zsn[nb2];
-        }
-        // stage s + 1 (activations) came one step earlier, the weights of its
-        // group at least two; after them only this step's copies
-        wait_barrier(std::integral_constant<int, kPer>());
-        rotate();
-        if (s & 1) rotate_w();
-      }
+      if (cur.rows > kBigM / 2) HM_BIG_W4A16_STEPS(8);
+      else HM_BIG_W4A16_STEPS(4);
 
       // ---- epilogue: lane holds C[n = 64 w + 32 nb2 + 8 j + 4 hi + r][row = 32 mb + l32];
       // slab p holds row blocks 2 p and 2 p + 1 of every wave; the copies still
       // in flight finish first (the stores then never overtake a copy)
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       uint8_t* ost = lds + so[2];                    // the last step's stage
+      const int n_slabs = cur.rows > kBigM / 2 ? 4 : 2;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const int mb = 2 * p + mm, r = 32 * mm + l32;
-#pragma unroll
-          for (int nb2 = 0; nb2 < 2; ++nb2)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int u = 16 * wave + 8 * nb2 + 2 * j + hi;
-              *reinterpret_cast<u32x2_t*>(ost + r * 512 + (u ^ Swz16::swz(r)) * 8) =
-                  (u32x2_t){pack_bf16(acc[nb2][mb][4 * j], acc[nb2][mb][4 * j + 1]),
-                            pack_bf16(acc[nb2][mb][4 * j + 2], acc[nb2][mb][4 * j + 3])};
-            }
+        if (p < n_slabs) {
+  #pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            const int mb = 2 * p + mm, r = 32 * mm + l32;
+  #pragma unroll
+            for (int nb2 = 0; nb2 < 2; ++nb2)
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int u = 16 * wave + 8 * nb2 + 2 * j + hi;
+                *reinterpret_cast<u32x2_t*>(ost + r * 512 + (u ^ Swz16::swz(r)) * 8) =
+                    (u32x2_t){pack_bf16(acc[nb2][mb][4 * j], acc[nb2][mb][4 * j + 1]),
+                              pack_bf16(acc[nb2][mb][4 * j + 2], acc[nb2][mb][4 * j + 3])};
+              }
+          }
+          lds_barrier();
+          store_slab(cur, ost, p, Swz16());
+          lds_barrier();
         }
-        lds_barrier();
-        store_slab(cur, ost, p, Swz16());
-        lds_barrier();
       }
       if (!has_next) break;
       cur = nxt;
@@ -648,6 +680,20 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m) {
     }
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the block ends
+}
+
+// Dense tiles that run whole; the rest of the visiting order runs as two
+// 128-row halves.  When the tiles fill the persistent grid a whole number of
+// rounds plus at most half a round (896 tiles of M = 4096, N = 14336 on 256
+// CUs: 3.5), the last round's tiles are split so that every CU takes part in
+// it; W4A16 only (the half tiles compute four of the eight row blocks), and
+// not where the second half of a last tile row would be empty.
+int64_t big_full_tiles(const Geom& G, int64_t M, bool mx) {
+  const int64_t tiles_n = (G.NB + kBigCB - 1) / kBigCB, tiles_m = (M + kBigM - 1) / kBigM;
+  const int64_t tiles = tiles_n * tiles_m, rest = tiles % kBigGrid;
+  const bool tail_ok = (M % kBigM) == 0 || (M % kBigM) > kBigM / 2;
+  if (mx || tiles <= kBigGrid || rest == 0 || 2 * rest > kBigGrid || !tail_ok) return tiles;
+  return tiles - rest;
 }
 
 template <bool MX, bool ZP, bool GROUPED>
@@ -661,9 +707,12 @@ static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
   // dense: one round of tiles, or a persistent grid of one block per CU
   // (a multiple of 8, so a block's items stay on its XCD)
   const int64_t tiles = (int64_t)tiles_n * tiles_m;
+  const int n_full = GROUPED ? 0 : (int)big_full_tiles(a.G, a.M, MX);
+  const int64_t items = GROUPED ? 0 : 2 * tiles - n_full;
   const unsigned grid = GROUPED ? (unsigned)(grid_items > 0 ? grid_items : 1)
-                                : (unsigned)(tiles <= kBigGrid ? tiles : kBigGrid);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(big_threads(MX)), big_lds_bytes(MX), st, a, tiles_n, tiles_m);
+                                : (unsigned)(items <= kBigGrid ? items : kBigGrid);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(big_threads(MX)), big_lds_bytes(MX), st, a, tiles_n, tiles_m,
+                     n_full);
   return hipGetLastError();
 }
 

@@ -72,5 +72,7 @@ int64_t mid_n_tiles(const Geom& G, bool mx);
 // Grouped: persistent over (256-row unit x 256-column tile) items, hdr[2] units.
 hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
 int64_t big_n_tiles(const Geom& G);
+// dense: tiles of the visiting order that run whole (the rest as 128-row halves)
+int64_t big_full_tiles(const Geom& G, int64_t M, bool mx);
 
 }  // namespace hm

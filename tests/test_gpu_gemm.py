@@ -257,3 +257,19 @@ def test_mid_tiles_ragged(fmt, m, n, k):
     L = Layer(fmt, n, k, cfg=14, wseed=m + n)
     x = synthetic.activations(14, m, k, index=m, outliers=0.01 if fmt == quant.FMT_MXFP4 else 0)
     _with_env({"HM_FORCE_PATH": 2}, lambda: L.check(x))
+
+
+@pytest.mark.parametrize("fmt", [quant.FMT_UINT4_ZP, quant.FMT_INT4_SYM])
+@pytest.mark.parametrize("m,halves", [(4352, 32), (4288, 32), (4160, 0)])
+def test_big_half_tiles(fmt, m, halves):
+    """Dense W4A16 with more 256 x 256 tiles than the persistent grid and at
+    most half a round left over (N = 4096: 16 column tiles, 17 tile rows =
+    272 tiles on 256 blocks): the last 16 tiles run as 32 halves of 128
+    rows, the last of them holding 64 rows when M = 4288; with 64 rows in
+    the last tile row (M = 4160) nothing is split.  Every output is checked."""
+    import quantized_gemm_int4_amd as hm
+    n, k = 4096, 256
+    L = Layer(fmt, n, k, cfg=15, wseed=m)
+    plan = hm.hm_gemm_plan(L.desc, hm.HM_A_BF16, m)
+    assert "256x256" in plan and f"half_tiles={halves}" in plan, plan
+    L.check(synthetic.activations(15, m, k, index=m))
