@@ -19,9 +19,9 @@ using namespace hm;
 
 constexpr int kStreamMaxRows = 32;   // dense rows handled by the streaming kernel (two 16-row blocks)
 constexpr int64_t kStreamLdsBytes = 159 * 1024;  // dynamic LDS one streaming block may use
-constexpr int kMoeStreamRows = 16;
+constexpr int kMoeStreamRows = 16;   // expert segments of at most this many rows use the streaming kernel
 constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles are used
-constexpr int kMoeBigMinRows = 192;   // an expert remainder of this many rows gets a 256-row unit   // expert segments of at most this many rows use the streaming kernel
+constexpr int kMoeBigMinRows = 192;   // an expert remainder of this many rows gets a 256-row unit
 constexpr int kGroupedGridStream = 2048;
 constexpr int kGroupedGridTile = 1024;
 constexpr int kGroupedGridMid = 256;     // one 128 x 64 tile block per compute unit (LDS-bound)
@@ -132,7 +132,7 @@ DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
 struct MoePlan {
   int64_t P, max_s, max_t, max_b;
   size_t off_su, off_tu, off_bu, ws_bytes;
-  int nbw, ks, lds_kb;
+  int nbw, ks, lds_kb, s_rows;
 };
 
 MoePlan plan_moe(const hm_wdesc* d, int64_t t, int32_t topk) {
@@ -147,6 +147,8 @@ MoePlan plan_moe(const hm_wdesc* d, int64_t t, int32_t topk) {
   p.off_bu = align256(p.off_tu + (size_t)p.max_t * 16);
   p.ws_bytes = align256(p.off_bu + (size_t)p.max_b * 16);
   p.nbw = 1;
+  p.s_rows = env_int("HM_MOE_STREAM_ROWS", kMoeStreamRows);
+  if (p.s_rows != 16 && p.s_rows != 32) p.s_rows = kMoeStreamRows;
   p.ks = env_int("HM_MOE_STREAM_KS", 1);
   if (p.ks != 1 && p.ks != 2 && p.ks != 4) p.ks = 1;
   // LDS per streaming block: a unit stages up to 16 rows, so K is walked in
@@ -383,10 +385,10 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   // 256-row units address activation rows with 32-bit byte offsets
   const int64_t a_bytes = (a_rows_are_pairs ? p.P : t) * d->k * (afmt == HM_A_FP8_ROWSCALE ? 1 : 2);
   const int big_min = (a_bytes < (1ll << 32) && env_int("HM_MOE_BIG", 1)) ? kMoeBigMinRows : 0;
-  hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, kMoeStreamRows, kTileM, big_min,
+  hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, p.s_rows, kTileM, big_min,
                                      p.max_s, p.max_t, p.max_b, hdr, su, tu, bu, stream);
   if (e == hipSuccess) {
-    StreamCfg sc{kMoeStreamRows / 16, p.nbw, 1, p.ks, p.lds_kb};
+    StreamCfg sc{p.s_rows / 16, p.nbw, 1, p.ks, p.lds_kb};
     const int64_t nts = stream_n_tiles(a.G, sc);
     int64_t gi = p.max_s * nts;
     if (gi > kGroupedGridStream) gi = kGroupedGridStream;

@@ -572,9 +572,13 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
 #pragma unroll
       for (int nb2 = 0; nb2 < 2; ++nb2) {
         const uint8_t* tile = stg + kWOff + (NWT * wave + 2 * nb2 + c_l) * 1024;
+        // K parts kq and kq + 2 are words 2 h and 2 h + 1 of one slot: one 8-byte read
 #pragma unroll
-        for (int kq = 0; kq < 4; ++kq)
-          wv[nb2][kq] = *reinterpret_cast<const uint32_t*>(tile + (c16 + 16 * ((2 * kq + hi) & 3)) * 16 + 4 * (2 * h + (kq >> 1)));
+        for (int kq = 0; kq < 2; ++kq) {
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(tile + (c16 + 16 * (2 * kq + hi)) * 16 + 8 * h);
+          wv[nb2][kq] = v[0];
+          wv[nb2][kq + 2] = v[1];
+        }
         const int t4 = 2 * nb2 + c_l;
         sv[nb2] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sz + t4 * 32 + c16 * 2));
         const uint32_t zw = ZP ? *reinterpret_cast<const uint32_t*>(sz + 128 + t4 * 8 + (c16 >> 3) * 4) : 0u;
