@@ -19,7 +19,14 @@ using namespace hm;
 
 constexpr int kStreamMaxRows = 32;   // dense rows handled by the streaming kernel (two 16-row blocks)
 constexpr int64_t kStreamLdsBytes = 159 * 1024;  // dynamic LDS one streaming block may use
-constexpr int kMoeStreamRows = 16;   // expert segments of at most this many rows use the streaming kernel
+constexpr int kMoeStreamRows = 16;   // rows per grouped streaming unit
+// Experts with at most this many rows use the streaming kernel (as units of
+// kMoeStreamRows rows that share the expert's weights through the L2), with
+// this many 16-column blocks per wave.  Measured on the 256-expert top-8
+// workloads: W4A16 64 rows and two blocks per wave (T = 64 / 1024 / 8192:
+// -19% / -5% / -5% against 16 rows and one block); MXFP4 keeps 16 and one.
+constexpr int kMoeStreamMaxA16 = 64, kMoeStreamNbwA16 = 2;
+constexpr int kMoeStreamMaxMx = 16, kMoeStreamNbwMx = 1;
 constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles are used
 constexpr int kMoeBigMinRows = 192;   // an expert remainder of this many rows gets a 256-row unit
 constexpr int kGroupedGridStream = 2048;
@@ -132,23 +139,28 @@ DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
 struct MoePlan {
   int64_t P, max_s, max_t, max_b;
   size_t off_su, off_tu, off_bu, ws_bytes;
-  int nbw, ks, lds_kb, s_rows;
+  int nbw, ks, lds_kb, s_rows, s_max;
 };
 
 MoePlan plan_moe(const hm_wdesc* d, int64_t t, int32_t topk) {
   MoePlan p{};
   p.P = t * topk;
   const int64_t act = (p.P < d->num_experts) ? p.P : d->num_experts;
-  p.max_s = act;
+  p.s_rows = env_int("HM_MOE_STREAM_ROWS", kMoeStreamRows);
+  if (p.s_rows != 16 && p.s_rows != 32) p.s_rows = kMoeStreamRows;
+  // experts with up to s_max rows stream, as ceil(rows / s_rows) units
+  const bool mx = d->wfmt == HM_W_MXFP4;
+  p.s_max = env_int("HM_MOE_STREAM_MAX", mx ? kMoeStreamMaxMx : kMoeStreamMaxA16);
+  if (p.s_max < p.s_rows) p.s_max = p.s_rows;
+  p.max_s = p.P / p.s_rows + act;
   p.max_t = (p.P + kTileM - 1) / kTileM + act;
   p.max_b = p.P / kMoeBigMinRows + 1;         // every 256-row unit holds >= kMoeBigMinRows rows
   p.off_su = 256;
   p.off_tu = align256(p.off_su + (size_t)p.max_s * 16);
   p.off_bu = align256(p.off_tu + (size_t)p.max_t * 16);
   p.ws_bytes = align256(p.off_bu + (size_t)p.max_b * 16);
-  p.nbw = 1;
-  p.s_rows = env_int("HM_MOE_STREAM_ROWS", kMoeStreamRows);
-  if (p.s_rows != 16 && p.s_rows != 32) p.s_rows = kMoeStreamRows;
+  p.nbw = env_int("HM_MOE_STREAM_NBW", mx ? kMoeStreamNbwMx : kMoeStreamNbwA16);
+  if (p.nbw != 1 && p.nbw != 2) p.nbw = mx ? kMoeStreamNbwMx : kMoeStreamNbwA16;
   p.ks = env_int("HM_MOE_STREAM_KS", 1);
   if (p.ks != 1 && p.ks != 2 && p.ks != 4) p.ks = 1;
   // LDS per streaming block: a unit stages up to 16 rows, so K is walked in
@@ -385,7 +397,7 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   // 256-row units address activation rows with 32-bit byte offsets
   const int64_t a_bytes = (a_rows_are_pairs ? p.P : t) * d->k * (afmt == HM_A_FP8_ROWSCALE ? 1 : 2);
   const int big_min = (a_bytes < (1ll << 32) && env_int("HM_MOE_BIG", 1)) ? kMoeBigMinRows : 0;
-  hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, p.s_rows, kTileM, big_min,
+  hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, p.s_rows, p.s_max, kTileM, big_min,
                                      p.max_s, p.max_t, p.max_b, hdr, su, tu, bu, stream);
   if (e == hipSuccess) {
     StreamCfg sc{p.s_rows / 16, p.nbw, 1, p.ks, p.lds_kb};

@@ -96,19 +96,18 @@ k_moe_sort(const int32_t* __restrict__ ids, int64_t P, int E, int32_t* __restric
   }
 }
 
-// Cut every expert's segment into units: segments of 1..s_max rows become one
-// streaming unit; longer ones become ceil(count/bm) tile units of <= bm rows.
-// Unit = {expert, first index into sorted_pairs, row count, 0}.
-// hdr[0] = number of streaming units, hdr[1] = number of tile units.
 // Work units of a grouped GEMM from the expert offsets (one thread per
-// expert, E <= 512).  An expert with at most s_max rows is one streaming unit.
-// A larger one is cut into 256-row units while big_min > 0 (a remainder of at
-// least big_min rows is one more 256-row unit) and what is left into units of
-// at most bm rows for the 128-row tile kernel.  Units are {expert, first row,
-// rows, 0}; hdr = {streaming units, tile units, 256-row units}, each capped
-// at its array size.
+// expert, E <= 512).  An expert with 1..s_max rows becomes ceil(rows/s_rows)
+// consecutive streaming units of at most s_rows rows (the streaming kernel
+// takes s_rows rows per unit; consecutive units of one expert run side by
+// side and share its weights through the L2).  A larger one is cut into
+// 256-row units while big_min > 0 (a remainder of at least big_min rows is
+// one more 256-row unit) and what is left into units of at most bm rows for
+// the 128-row tile kernel.  Units are {expert, first index into
+// sorted_pairs, rows, 0}; hdr = {streaming units, tile units, 256-row
+// units}, each capped at its array size.
 __global__ void __launch_bounds__(512)
-k_moe_schedule(const int32_t* __restrict__ offsets, int E, int64_t P, int s_max, int bm, int big_min,
+k_moe_schedule(const int32_t* __restrict__ offsets, int E, int64_t P, int s_rows, int s_max, int bm, int big_min,
                int64_t max_s, int64_t max_t, int64_t max_b, int32_t* __restrict__ hdr,
                int32_t* __restrict__ su, int32_t* __restrict__ tu, int32_t* __restrict__ bu) {
   __shared__ int wsum[8];
@@ -122,7 +121,7 @@ k_moe_schedule(const int32_t* __restrict__ offsets, int E, int64_t P, int s_max,
     beg = (int)b;
     c = (int)(f - b);
   }
-  const int ns = (c > 0 && c <= s_max) ? 1 : 0;
+  const int ns = (c > 0 && c <= s_max) ? (c + s_rows - 1) / s_rows : 0;
   int nb = 0, rest = 0;
   if (c > s_max) {
     if (big_min > 0) {
@@ -137,9 +136,11 @@ k_moe_schedule(const int32_t* __restrict__ offsets, int E, int64_t P, int s_max,
   const int is = block_scan512(ns, wsum);
   const int it = block_scan512(nt, wsum);
   const int ib = block_scan512(nb, wsum);
-  if (ns && is - 1 < max_s) {
-    int32_t* u = su + 4 * (is - 1);
-    u[0] = e; u[1] = beg; u[2] = c; u[3] = 0;
+  for (int i = 0; i < ns; ++i) {
+    if (is - ns + i >= max_s) break;
+    int32_t* u = su + 4 * (is - ns + i);
+    const int r0 = i * s_rows;
+    u[0] = e; u[1] = beg + r0; u[2] = (c - r0 < s_rows) ? c - r0 : s_rows; u[3] = 0;
   }
   for (int i = 0; i < nb; ++i) {
     if (ib - nb + i >= max_b) break;
@@ -168,11 +169,11 @@ hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int E, int32_t* counts
   return hipGetLastError();
 }
 
-hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_max, int bm, int big_min,
-                               int64_t max_s, int64_t max_t, int64_t max_b, int32_t* hdr, int32_t* su,
-                               int32_t* tu, int32_t* bu, hipStream_t st) {
-  hipLaunchKernelGGL(k_moe_schedule, dim3(1), dim3(512), 0, st, offsets, E, P, s_max, bm, big_min, max_s,
-                     max_t, max_b, hdr, su, tu, bu);
+hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_rows, int s_max, int bm,
+                               int big_min, int64_t max_s, int64_t max_t, int64_t max_b, int32_t* hdr,
+                               int32_t* su, int32_t* tu, int32_t* bu, hipStream_t st) {
+  hipLaunchKernelGGL(k_moe_schedule, dim3(1), dim3(512), 0, st, offsets, E, P, s_rows, s_max, bm, big_min,
+                     max_s, max_t, max_b, hdr, su, tu, bu);
   return hipGetLastError();
 }
 

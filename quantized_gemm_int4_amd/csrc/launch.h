@@ -36,9 +36,9 @@ hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_
                                  hipStream_t st);
 hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int E, int32_t* counts, int32_t* offsets,
                            int32_t* sorted_pairs, hipStream_t st);
-hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_max, int bm, int big_min,
-                               int64_t max_s, int64_t max_t, int64_t max_b, int32_t* hdr, int32_t* su,
-                               int32_t* tu, int32_t* bu, hipStream_t st);
+hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_rows, int s_max, int bm,
+                               int big_min, int64_t max_s, int64_t max_t, int64_t max_b, int32_t* hdr,
+                               int32_t* su, int32_t* tu, int32_t* bu, hipStream_t st);
 
 // Streaming (small-M) kernel.  Dense: grid (n_tiles, splits, m_chunks).
 // Grouped: persistent over (streaming unit x n tile) items.

@@ -203,3 +203,23 @@ def test_moe_big_units(fmt, rows_are_pairs, big):
         _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, 9)
     finally:
         os.environ.pop("HM_MOE_BIG", None)
+
+
+@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("s_max,nbw,s_rows", [(64, 2, 16), (128, 1, 16), (128, 2, 32), (16, 2, 16)])
+def test_moe_stream_multi_unit(fmt, s_max, nbw, s_rows):
+    """Experts of 120, 64, 33, 17, 16 and 5 rows: those with at most s_max
+    rows stream as several consecutive units of s_rows rows (the others take
+    tile units), with one or two 16-column blocks per wave on a ragged N (13
+    column blocks) and K = 5 groups."""
+    t, topk, E, n, k = 255, 1, 6, 208, 640
+    r = np.random.default_rng(11)
+    ids = r.permutation(np.concatenate([np.full(c, e) for e, c in enumerate([120, 64, 33, 17, 16, 5])]))
+    ids = ids.reshape(t, topk).astype(np.int32)
+    env = {"HM_MOE_STREAM_MAX": s_max, "HM_MOE_STREAM_NBW": nbw, "HM_MOE_STREAM_ROWS": s_rows}
+    os.environ.update({kk: str(v) for kk, v in env.items()})
+    try:
+        _run_moe(fmt, E, n, k, t, topk, ids, 0, 13)
+    finally:
+        for kk in env:
+            os.environ.pop(kk, None)
