@@ -57,3 +57,17 @@ def check(y_bf16_bits, y_ref, b, norm_tol=NORM_TOL, elem_tol=ELEM_TOL):
     bad = int((ratio > 1.0).sum())
     return dict(ok=ok, norm_err=float(norm_err), worst_ratio=worst, n_bad=bad,
                 finite=finite)
+
+
+def check_elementwise(y_bf16_bits, y_ref, extra=0.0):
+    """Element-wise acceptance of a bf16 result of an elementwise step (SiLU
+    product, weighted combine): |Y - Y_ref| <= ulp_bf16(Y_ref) + extra, where
+    extra covers the fp32 accumulation of a sum (0 for a single product)."""
+    y = codecs.bf16_value(np.asarray(y_bf16_bits, dtype=np.uint16)).astype(np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    lim = codecs.ulp_bf16(y_ref) + np.asarray(extra, dtype=np.float64)
+    ratio = np.abs(y - y_ref) / lim
+    finite = bool(np.all(np.isfinite(y)))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    return dict(ok=finite and worst <= 1.0, worst_ratio=worst, n_bad=int((ratio > 1.0).sum()),
+                finite=finite)

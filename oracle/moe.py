@@ -7,6 +7,16 @@ and a grouped path runs all experts' GEMMs (aihaber.org, Performance).
 
 Pairs: with T tokens and top-k routing, pair p = t*topk + j is token t's j-th
 expert choice ids[t, j].  Rows of the grouped GEMM are in pair order.
+
+Around the two grouped GEMMs of an MoE feed-forward block (tokens split per
+expert, each token activating only some experts: aihaber.org article, "what
+problem does it solve"; ywsung.com note, section on one token vs many
+tokens) sit a gated activation between gate_up and down and the weighted
+combine of each token's expert outputs.  The pages name neither formula; the
+readings here are the plainest ones:
+  h[p, i]   = silu(gu[p, i]) * gu[p, d + i],  silu(x) = x / (1 + exp(-x))
+              (gate in columns 0..d-1 of the gate_up output, up in d..2d-1);
+  out[t, n] = sum_j w[t, j] * y[t*topk + j, n]   (w: the routing weights).
 """
 import numpy as np
 
@@ -50,3 +60,24 @@ def moe_gemm_ref(a_hat, a_rows_are_pairs, topk, ids, w_hat_of, n, bound=True,
         if bound:
             b[sel] = be
     return y, b, pairs
+
+
+def silu_mul_ref(gu_hat, d):
+    """h = silu(gate) * up in float64 from the [rows, 2d] gate_up output
+    (gate = columns 0..d-1, up = columns d..2d-1)."""
+    x = np.asarray(gu_hat, dtype=np.float64)
+    g, u = x[:, :d], x[:, d:2 * d]
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))          # exp overflow -> sigmoid 0
+    return g * sig * u
+
+
+def combine_ref(y_hat, weights, topk):
+    """out[t] = sum_j w[t, j] * y[t*topk + j] in float64 over pair-order rows
+    y_hat [T*topk, N], and the bound sum_j |w[t, j] * y[t*topk + j]|."""
+    w = np.asarray(weights, dtype=np.float64)
+    t = w.shape[0]
+    y = np.asarray(y_hat, dtype=np.float64).reshape(t, topk, -1)
+    out = np.einsum("tj,tjn->tn", w, y)
+    bnd = np.einsum("tj,tjn->tn", np.abs(w), np.abs(y))
+    return out, bnd

@@ -54,3 +54,69 @@ def test_moe_rows_follow_pairs():
     y2, _, _ = moe.moe_gemm_ref(a, True, topk, ids, lambda e: ws[e], n)
     for p in range(t * topk):
         assert np.allclose(y2[p], ws[ids.ravel()[p]] @ a[p], atol=1e-12)
+
+
+def test_silu_mul_closed_forms():
+    """silu(x) = x * sigmoid(x): silu(0) = 0; sigmoid(1) = 1 / (1 + 1/e), the
+    logistic function's value at 1, 0.7310585786300049, and sigmoid(2) =
+    0.8807970779778823 (a sign error in the exponent gives sigmoid(-1)
+    instead); silu(x) - silu(-x) = x for every x (sigmoid(x) + sigmoid(-x) =
+    1), which a dropped factor x breaks; gate and up are not interchangeable
+    (gate 2, up 3 gives 3 silu(2), not 2 silu(3))."""
+    gu = np.array([[0.0, 1.0, 2.0, 5.0, 1.0, 3.0]])
+    h = moe.silu_mul_ref(gu, 3)
+    assert h[0, 0] == 0.0
+    assert abs(h[0, 1] - 0.7310585786300049) < 1e-15                   # silu(1) * 1
+    assert abs(h[0, 2] - 3.0 * 2.0 * 0.8807970779778823) < 1e-14     # sigmoid(2)
+    r = np.random.default_rng(3)
+    x = r.normal(0, 4, 1000)
+    ones = np.ones_like(x)
+    hp = moe.silu_mul_ref(np.stack([x, ones], 1), 1)[:, 0]
+    hm_ = moe.silu_mul_ref(np.stack([-x, ones], 1), 1)[:, 0]
+    assert np.allclose(hp - hm_, x, rtol=0, atol=1e-12)
+    big = moe.silu_mul_ref(np.array([[60.0, -800.0, 1.0, 1.0]]), 2)
+    assert abs(big[0, 0] - 60.0) < 1e-12 and big[0, 1] == 0.0          # limits, exp overflow handled
+
+
+def test_silu_mul_brute_force():
+    r = np.random.default_rng(4)
+    gu = r.normal(size=(5, 6))
+    h = moe.silu_mul_ref(gu, 3)
+    for i in range(5):
+        for j in range(3):
+            g, u = gu[i, j], gu[i, 3 + j]
+            assert abs(h[i, j] - g / (1.0 + np.exp(-g)) * u) < 1e-14
+
+
+def test_combine_one_hot_and_brute_force():
+    """A one-hot weight row gathers that pair's row exactly; otherwise the
+    result equals the explicit loop over pairs t*topk + j."""
+    r = np.random.default_rng(5)
+    t, topk, n = 4, 3, 7
+    y = r.normal(size=(t * topk, n))
+    w = np.zeros((t, topk))
+    w[np.arange(t), [2, 0, 1, 2]] = 1.0
+    out, b = moe.combine_ref(y, w, topk)
+    for i, j in enumerate([2, 0, 1, 2]):
+        assert np.array_equal(out[i], y[i * topk + j])
+        assert np.array_equal(b[i], np.abs(y[i * topk + j]))
+    w = r.random((t, topk))
+    out, b = moe.combine_ref(y, w, topk)
+    for i in range(t):
+        ref = np.zeros(n)
+        ab = np.zeros(n)
+        for j in range(topk):
+            ref += w[i, j] * y[i * topk + j]
+            ab += abs(w[i, j]) * np.abs(y[i * topk + j])
+        assert np.allclose(out[i], ref, rtol=0, atol=1e-13)
+        assert np.allclose(b[i], ab, rtol=0, atol=1e-13)
+
+
+def test_check_elementwise_rejects_two_ulps():
+    from oracle import codecs
+    ref = np.array([1.0, 3.0, -0.5])
+    bits = codecs.bf16_rne_bits(ref.astype(np.float32))
+    assert gemm.check_elementwise(bits, ref)["ok"]
+    off = bits.copy()
+    off[1] += 2                                    # two bf16 ulps away
+    assert not gemm.check_elementwise(off, ref)["ok"]
