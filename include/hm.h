@@ -185,6 +185,38 @@ hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const 
                       int32_t topk, const int32_t* offsets, const int32_t* sorted_pairs,
                       uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------- MoE block steps */
+
+/* Gated activation between the gate_up and down grouped GEMMs of an MoE
+ * feed-forward block (tokens split per expert, each token activating only
+ * some experts: aihaber.org article on Humming, "what problem does it solve";
+ * ywsung.com note "How vLLM Humming computes 4 bits", section on one token vs
+ * many tokens; the pages give no formula, the reading is the plainest one):
+ *   h[r][i] = bf16( silu(gu[r][i]) * gu[r][d + i] ),  silu(x) = x / (1 + exp(-x)),
+ * computed in fp32 from the bf16 inputs, rounded to nearest even.
+ *   gu   bf16 [rows][2d], row-major: gate in columns 0..d-1, up in d..2d-1
+ *        (hm_moe_gemm's gate_up output with n = 2d, pair order kept);
+ *   h    bf16 [rows][d] (the down projection's input, a_rows_are_pairs = 1).
+ * Device pointers, caller-owned, 16-byte aligned; gu and h must not overlap.
+ * rows = 0 is a no-op.  HM_ERR_NULL for a null pointer when rows > 0,
+ * HM_ERR_SHAPE for rows < 0 or d <= 0, HM_ERR_ALIGN for a misaligned pointer,
+ * HM_ERR_HIP if the launch fails. */
+hm_status hm_silu_mul(const uint16_t* gu, int64_t rows, int64_t d, uint16_t* h, hipStream_t stream);
+
+/* Top-k weighted combine of an MoE block (same pages; the reading: each
+ * token's output is its routing-weighted sum of its experts' outputs):
+ *   out[t][c] = bf16( sum_{j = 0..topk-1} w[t][j] * y[t*topk + j][c] ),
+ * summed in fp32 in ascending j, rounded to nearest even.
+ *   y    bf16 [t*topk][n], pair order (hm_moe_gemm's down output);
+ *   w    fp32 [t][topk] routing weights;
+ *   out  bf16 [t][n].
+ * Device pointers, caller-owned; y and out 16-byte aligned, w 4-byte aligned;
+ * out must not overlap y or w.  t = 0 is a no-op.  HM_ERR_NULL for a null
+ * pointer when t > 0, HM_ERR_SHAPE for t < 0, n <= 0 or topk < 1,
+ * HM_ERR_ALIGN for a misaligned pointer, HM_ERR_HIP if the launch fails. */
+hm_status hm_moe_combine(const uint16_t* y, const float* w, int64_t t, int32_t topk, int64_t n,
+                         uint16_t* out, hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* hm_status_string(hm_status s);
 

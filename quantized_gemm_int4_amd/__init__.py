@@ -61,6 +61,8 @@ def _load():
         "hm_moe_sort": [P, I64, I32, I32, P, P, P, P, SZ, P],
         "hm_moe_gemm_workspace_size": [D, I32, I64, I32, ctypes.POINTER(SZ)],
         "hm_moe_gemm": [D, P, I32, P, P, I32, I64, I32, P, P, P, P, SZ, P],
+        "hm_silu_mul": [P, I64, I64, P, P],
+        "hm_moe_combine": [P, P, I64, I32, I64, P, P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -225,3 +227,33 @@ def hm_moe_gemm(desc, w_dev, a, offsets, sorted_pairs, t, topk, a_rows_are_pairs
                                        _ptr(offsets), _ptr(sorted_pairs), _ptr(y), _ptr(ws),
                                        ws.numel(), _stream(stream)))
     return y
+
+
+# --------------------------------------------------------------- MoE block steps
+
+def hm_silu_mul(gu, h=None, stream=None):
+    """gu bf16 [rows, 2d] (gate | up) -> h bf16 [rows, d] = silu(gate) * up."""
+    rows, two_d = gu.shape
+    if two_d % 2:
+        raise ValueError("gu: the last dimension must be even (gate | up)")
+    d = two_d // 2
+    _need(gu, torch.bfloat16, rows * two_d, "gu")
+    if h is None:
+        h = torch.empty(rows, d, dtype=torch.bfloat16, device=gu.device)
+    _need(h, torch.bfloat16, rows * d, "h")
+    _ok("hm_silu_mul", lib.hm_silu_mul(_ptr(gu), rows, d, _ptr(h), _stream(stream)))
+    return h
+
+
+def hm_moe_combine(y, weights, topk, out=None, stream=None):
+    """y bf16 [t*topk, n] (pair order), weights fp32 [t, topk] -> out bf16 [t, n]."""
+    t = weights.shape[0]
+    n = y.shape[1]
+    _need(y, torch.bfloat16, t * topk * n, "y")
+    _need(weights, torch.float32, t * topk, "weights")
+    if out is None:
+        out = torch.empty(t, n, dtype=torch.bfloat16, device=y.device)
+    _need(out, torch.bfloat16, t * n, "out")
+    _ok("hm_moe_combine", lib.hm_moe_combine(_ptr(y), _ptr(weights), t, int(topk), n, _ptr(out),
+                                             _stream(stream)))
+    return out

@@ -237,6 +237,28 @@ HM_API hm_status hm_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint
   return HM_OK;
 }
 
+HM_API hm_status hm_silu_mul(const uint16_t* gu, int64_t rows, int64_t d, uint16_t* h, hipStream_t stream) {
+  if (rows < 0 || d <= 0) return HM_ERR_SHAPE;
+  if (rows == 0) return HM_OK;
+  if (!gu || !h) return HM_ERR_NULL;
+  if (!aligned(gu, 16) || !aligned(h, 16)) return HM_ERR_ALIGN;
+  // one thread per 16-byte chunk (or per element): the grid's x extent is 32-bit
+  if ((rows * d + 255) / 256 > 0x7FFFFFFFll) return HM_ERR_SHAPE;
+  if (launch_silu_mul(gu, rows, d, h, stream) != hipSuccess) return HM_ERR_HIP;
+  return HM_OK;
+}
+
+HM_API hm_status hm_moe_combine(const uint16_t* y, const float* w, int64_t t, int32_t topk, int64_t n,
+                                uint16_t* out, hipStream_t stream) {
+  if (t < 0 || n <= 0 || topk < 1) return HM_ERR_SHAPE;
+  if (t == 0) return HM_OK;
+  if (!y || !w || !out) return HM_ERR_NULL;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(w, 4)) return HM_ERR_ALIGN;
+  if ((t * n + 255) / 256 > 0x7FFFFFFFll) return HM_ERR_SHAPE;
+  if (launch_combine(y, w, t, topk, n, out, stream) != hipSuccess) return HM_ERR_HIP;
+  return HM_OK;
+}
+
 HM_API hm_status hm_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t m, size_t* bytes) {
   hm_status s = check_desc(d);
   if (s) return s;

@@ -1,0 +1,121 @@
+// The two elementwise steps of an MoE feed-forward block around its grouped
+// GEMMs (tokens split per expert, each token activating only some experts:
+// aihaber.org article on Humming, "what problem does it solve"; ywsung.com
+// note "How vLLM Humming computes 4 bits", section on one token vs many
+// tokens):
+//   gated activation  h[r][i]   = silu(gu[r][i]) * gu[r][d + i]
+//   weighted combine  out[t][c] = sum_j w[t][j] * y[t*topk + j][c]
+// Both only stream bf16 rows through HBM (6 bytes per output of the gated
+// activation; 2 * topk + 2 bytes per output of the combine), so each thread
+// moves whole 16-byte chunks (eight bf16) and the grid holds one thread per
+// chunk: enough waves in flight to cover the memory latency without a loop.
+#include "common.h"
+#include "launch.h"
+
+namespace hm {
+
+namespace {
+
+// silu(g) = g / (1 + e^-g), written so that no intermediate overflows or
+// leaves the normal range: for g < 0 as g e^g / (1 + e^g), and below -80
+// (where 1 + e^g rounds to 1) as (g e^(g + 64 ln 2)) 2^-64.
+__device__ __forceinline__ float silu_f(float g) {
+  if (g >= 0.0f) return g / (1.0f + expf(-g));
+  if (g > -80.0f) {
+    const float e = expf(g);
+    return g * e / (1.0f + e);
+  }
+  return (g * expf(g + 44.3614195558365f)) * 5.421010862427522e-20f;
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+}  // namespace
+
+// d % 8 == 0: thread q handles outputs 8 (q % (d/8)) .. + 7 of row q / (d/8)
+__global__ void __launch_bounds__(256)
+k_silu_mul_v8(const uint16_t* __restrict__ gu, int64_t chunks, int64_t dc, uint16_t* __restrict__ h) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= chunks) return;
+  const int64_t r = q / dc, c = q - r * dc;
+  const uint16_t* g = gu + r * (16 * dc) + 8 * c;      // row stride 2d = 16 dc
+  const u32x4_t gv = ld16(g), uv = ld16(g + 8 * dc);
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = pack_bf16(silu_f(lo_bf16(gv[j])) * lo_bf16(uv[j]), silu_f(hi_bf16(gv[j])) * hi_bf16(uv[j]));
+  st16(h + r * (8 * dc) + 8 * c, o);
+}
+
+// any d: one output per thread
+__global__ void __launch_bounds__(256)
+k_silu_mul_s(const uint16_t* __restrict__ gu, int64_t total, int64_t d, uint16_t* __restrict__ h) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= total) return;
+  const int64_t r = q / d, i = q - r * d;
+  const float g = bf16_to_f32(gu[r * 2 * d + i]), u = bf16_to_f32(gu[r * 2 * d + d + i]);
+  h[q] = (uint16_t)(pack_bf16(silu_f(g) * u, 0.0f) & 0xFFFF);
+}
+
+// n % 8 == 0: thread q handles columns 8 (q % (n/8)) .. + 7 of token q / (n/8)
+__global__ void __launch_bounds__(256)
+k_combine_v8(const uint16_t* __restrict__ y, const float* __restrict__ w, int64_t chunks, int64_t nc,
+             int topk, uint16_t* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= chunks) return;
+  const int64_t t = q / nc, c = q - t * nc;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const uint16_t* yr = y + t * topk * (8 * nc) + 8 * c;
+  for (int j = 0; j < topk; ++j) {
+    const float wj = w[t * topk + j];
+    const u32x4_t v = ld16(yr + (int64_t)j * (8 * nc));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(wj, lo_bf16(v[e]), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(wj, hi_bf16(v[e]), acc[2 * e + 1]);
+    }
+  }
+  st16(out + t * (8 * nc) + 8 * c, (u32x4_t){pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
+                                             pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7])});
+}
+
+// any n: one output per thread
+__global__ void __launch_bounds__(256)
+k_combine_s(const uint16_t* __restrict__ y, const float* __restrict__ w, int64_t total, int64_t n, int topk,
+            uint16_t* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= total) return;
+  const int64_t t = q / n, c = q - t * n;
+  float acc = 0.f;
+  for (int j = 0; j < topk; ++j) acc = fmaf(w[t * topk + j], bf16_to_f32(y[(t * topk + j) * n + c]), acc);
+  out[q] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFF);
+}
+
+hipError_t launch_silu_mul(const uint16_t* gu, int64_t rows, int64_t d, uint16_t* h, hipStream_t st) {
+  if ((d & 7) == 0) {
+    const int64_t chunks = rows * (d / 8);
+    hipLaunchKernelGGL(k_silu_mul_v8, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, gu, chunks,
+                       d / 8, h);
+  } else {
+    const int64_t total = rows * d;
+    hipLaunchKernelGGL(k_silu_mul_s, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, gu, total, d, h);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const uint16_t* y, const float* w, int64_t t, int topk, int64_t n, uint16_t* out,
+                          hipStream_t st) {
+  if ((n & 7) == 0) {
+    const int64_t chunks = t * (n / 8);
+    hipLaunchKernelGGL(k_combine_v8, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, y, w, chunks,
+                       n / 8, topk, out);
+  } else {
+    const int64_t total = t * n;
+    hipLaunchKernelGGL(k_combine_s, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, y, w, total, n,
+                       topk, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hm

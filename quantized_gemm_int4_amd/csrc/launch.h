@@ -40,6 +40,13 @@ hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_r
                                int big_min, int64_t max_s, int64_t max_t, int64_t max_b, int32_t* hdr,
                                int32_t* su, int32_t* tu, int32_t* bu, hipStream_t st);
 
+// MoE block steps around the grouped GEMMs (bf16 rows, 16-byte chunks when
+// d (n) is a multiple of 8).  Grids of one thread per chunk: the caller keeps
+// rows * d (t * n) / 8 under 2^31 * 256.
+hipError_t launch_silu_mul(const uint16_t* gu, int64_t rows, int64_t d, uint16_t* h, hipStream_t st);
+hipError_t launch_combine(const uint16_t* y, const float* w, int64_t t, int topk, int64_t n, uint16_t* out,
+                          hipStream_t st);
+
 // Streaming (small-M) kernel.  Dense: grid (n_tiles, splits, m_chunks).
 // Grouped: persistent over (streaming unit x n tile) items.
 struct StreamCfg {

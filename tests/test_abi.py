@@ -114,3 +114,19 @@ def test_moe_argument_checks():
                 good, need, None) == 2
     assert _err("hm_moe_gemm", ctypes.byref(d), good, 0, good, None, 0, 64, 8, None, good, good,
                 good, need, None) == 1
+
+
+def test_moe_block_argument_checks():
+    """Validation of the MoE block steps happens before any launch."""
+    P = ctypes.c_void_p
+    good = P(0x100000)
+    assert _err("hm_silu_mul", good, 4, 0, good, None) == 2                 # d <= 0
+    assert _err("hm_silu_mul", good, -1, 8, good, None) == 2                # rows < 0
+    assert _err("hm_silu_mul", None, 0, 8, None, None) == 0                 # rows = 0: no-op
+    assert _err("hm_silu_mul", None, 4, 8, good, None) == 1
+    assert _err("hm_silu_mul", good, 4, 8, P(0x100008), None) == 3          # h not 16-byte aligned
+    assert _err("hm_moe_combine", good, good, 4, 0, 8, good, None) == 2     # topk < 1
+    assert _err("hm_moe_combine", good, good, 4, 2, 0, good, None) == 2     # n <= 0
+    assert _err("hm_moe_combine", None, None, 0, 2, 8, None, None) == 0     # t = 0: no-op
+    assert _err("hm_moe_combine", good, None, 4, 2, 8, good, None) == 1
+    assert _err("hm_moe_combine", good, P(0x100002), 4, 2, 8, good, None) == 3   # w not 4-byte aligned

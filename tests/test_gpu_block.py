@@ -1,0 +1,140 @@
+"""GPU parity for the MoE block steps around the grouped GEMMs: the SiLU-gated
+product and the top-k weighted combine against the oracle's fp64 definitions
+(element-wise, one bf16 ulp, plus the fp32 summation bound for the combine),
+on both the 16-byte-chunk and the per-element kernels, special values, the
+workload's shapes, and the whole block chained through the library."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import codecs, gemm, moe, quant
+from gpu_util import bf16_to_dev, bits_of, quantize_experts, std_to_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_bits(x):
+    return codecs.bf16_rne_bits(np.asarray(x, dtype=np.float32))
+
+
+def _combine_extra(w, b, topk):
+    # fp32 fused multiply-adds over topk terms: |error| <= topk 2^-24 sum_j |w y| (first order),
+    # taken twice for the second-order terms
+    return topk * 2.0 ** -23 * b
+
+
+@pytest.mark.parametrize("rows,d", [(1, 8), (37, 2048), (300, 64), (5, 13), (64, 1001)])
+def test_silu_mul_parity(rows, d):
+    import quantized_gemm_int4_amd as hm
+    r = np.random.default_rng(rows * 7 + d)
+    gu = r.normal(0, 3, size=(rows, 2 * d))
+    flat = gu.reshape(-1)
+    special = [0.0, -0.0, 100.0, -100.0, -90.0, 88.5, 1e-30, -1e-38, 6.0, -87.5, -79.9, -150.0, -80.5]
+    flat[: min(flat.size, len(special))] = special[: min(flat.size, len(special))]
+    bits = _bf16_bits(gu)
+    h = hm.hm_silu_mul(bf16_to_dev(bits))
+    torch.cuda.synchronize()
+    ref = moe.silu_mul_ref(codecs.bf16_value(bits).astype(np.float64), d)
+    res = gemm.check_elementwise(bits_of(h), ref)
+    assert res["ok"], res
+
+
+def test_silu_mul_rows_zero_and_workload_rows():
+    """rows = 0 is a no-op; the gate_up output of the T = 1024 workload (8192
+    pairs x 4096 columns) is checked on 256 sampled rows."""
+    import quantized_gemm_int4_amd as hm
+    h = hm.hm_silu_mul(torch.empty(0, 16, dtype=torch.bfloat16, device="cuda"))
+    assert h.shape == (0, 8)
+    P, d = 8192, 2048
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    gu = (torch.randn(P, 2 * d, device="cuda", generator=g) * 2).to(torch.bfloat16)
+    h = hm.hm_silu_mul(gu)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(0).choice(P, 256, replace=False)
+    gb = bits_of(gu)[rows]
+    ref = moe.silu_mul_ref(codecs.bf16_value(gb).astype(np.float64), d)
+    res = gemm.check_elementwise(bits_of(h)[rows], ref)
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("t,topk,n", [(1, 1, 8), (50, 8, 7168), (33, 2, 24), (7, 3, 13), (16, 8, 1001)])
+def test_combine_parity(t, topk, n):
+    import quantized_gemm_int4_amd as hm
+    r = np.random.default_rng(t * 31 + topk * 7 + n)
+    y = r.normal(0, 2, size=(t * topk, n))
+    ybits = _bf16_bits(y)
+    if topk == 8:
+        _, w = synthetic.router_topk(4, t, 256, 8)          # the workload's softmax weights
+    else:
+        w = r.random((t, topk)).astype(np.float32)
+    out = hm.hm_moe_combine(bf16_to_dev(ybits), to_dev(w), topk)
+    torch.cuda.synchronize()
+    ref, b = moe.combine_ref(codecs.bf16_value(ybits).astype(np.float64), w.astype(np.float64), topk)
+    res = gemm.check_elementwise(bits_of(out), ref, _combine_extra(w, b, topk))
+    assert res["ok"], res
+
+
+def test_combine_one_hot_weights_gather_exactly():
+    """One-hot weights pick one pair's row: the output equals it bit for bit."""
+    import quantized_gemm_int4_amd as hm
+    t, topk, n = 40, 8, 264
+    r = np.random.default_rng(9)
+    ybits = _bf16_bits(r.normal(size=(t * topk, n)))
+    pick = r.integers(0, topk, t)
+    w = np.zeros((t, topk), dtype=np.float32)
+    w[np.arange(t), pick] = 1.0
+    out = bits_of(hm.hm_moe_combine(bf16_to_dev(ybits), to_dev(w), topk))
+    assert np.array_equal(out, ybits[np.arange(t) * topk + pick])
+
+
+@pytest.mark.parametrize("fmt", [quant.FMT_INT4_SYM, quant.FMT_MXFP4])
+def test_moe_block_chained(fmt):
+    """Sort, gate_up (n = 2d), SiLU product, [FP8 rows], down, combine, all
+    through the library on a small routed batch; every step is compared with
+    the oracle applied to the previous step's GPU output."""
+    import quantized_gemm_int4_amd as hm
+    t, topk, E, H, d = 48, 2, 6, 256, 128
+    ids, w = synthetic.router_topk(6, t, E, topk)
+    wg = [synthetic.weights(16, 2 * d, H, index=e) for e in range(E)]
+    wd = [synthetic.weights(16, H, d, index=100 + e) for e in range(E)]
+    cg, sg, zg, what_g = quantize_experts(fmt, wg)
+    cd, sd, zd, what_d = quantize_experts(fmt, wd)
+    dg, dd = hm.wdesc(fmt, 2 * d, H, E), hm.wdesc(fmt, H, d, E)
+    w_g = hm.hm_transform(dg, *std_to_dev(fmt, cg, sg, zg))
+    w_d = hm.hm_transform(dd, *std_to_dev(fmt, cd, sd, zd))
+    xb = synthetic.activations(16, t, H, index=1)
+    _, off, sp = hm.hm_moe_sort(to_dev(ids), E)
+    x = bf16_to_dev(xb)
+    a8 = fmt == quant.FMT_MXFP4
+    if a8:
+        x8, xs = hm.hm_quant_fp8_rows(x)
+        y1 = hm.hm_moe_gemm(dg, w_g, x8, off, sp, t, topk, 0, a_row_scale=xs)
+    else:
+        y1 = hm.hm_moe_gemm(dg, w_g, x, off, sp, t, topk, 0)
+    h = hm.hm_silu_mul(y1)
+    if a8:
+        h8, hs = hm.hm_quant_fp8_rows(h)
+        y2 = hm.hm_moe_gemm(dd, w_d, h8, off, sp, t, topk, 1, a_row_scale=hs)
+    else:
+        y2 = hm.hm_moe_gemm(dd, w_d, h, off, sp, t, topk, 1)
+    out = hm.hm_moe_combine(y2, to_dev(w), topk)
+    torch.cuda.synchronize()
+
+    def xhat(bits_dev_bf16):
+        b = bits_of(bits_dev_bf16)
+        if not a8:
+            return codecs.bf16_value(b).astype(np.float64)
+        c, s = quant.quant_fp8_rows(b)
+        return quant.fp8_rows_dequant(c, s)
+
+    yr, bb, _ = moe.moe_gemm_ref(xhat(x), False, topk, ids, lambda e: what_g[e].astype(np.float64), 2 * d)
+    assert gemm.check(bits_of(y1), yr, bb)["ok"]
+    y1v = codecs.bf16_value(bits_of(y1)).astype(np.float64)
+    assert gemm.check_elementwise(bits_of(h), moe.silu_mul_ref(y1v, d))["ok"]
+    yr, bb, _ = moe.moe_gemm_ref(xhat(h), True, topk, ids, lambda e: what_d[e].astype(np.float64), H)
+    assert gemm.check(bits_of(y2), yr, bb)["ok"]
+    y2v = codecs.bf16_value(bits_of(y2)).astype(np.float64)
+    ref, b = moe.combine_ref(y2v, w.astype(np.float64), topk)
+    assert gemm.check_elementwise(bits_of(out), ref, _combine_extra(w, b, topk))["ok"]
