@@ -343,7 +343,7 @@ def run_moe(args, fmt):
     step_ms = 0.0
     step_fl = 0.0
     for t in ts:
-        ids, _ = synthetic.router_topk(4 if fmt != "mxfp4" else 5, t, E, topk)
+        ids, rw = synthetic.router_topk(4 if fmt != "mxfp4" else 5, t, E, topk)
         P = t * topk
         ids_d = torch.from_numpy(ids).to(dev)
         x = torch.from_numpy(synthetic.activations(4, t, H, index=t).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -356,6 +356,9 @@ def run_moe(args, fmt):
         sp = torch.empty(P, dtype=torch.int32, device=dev)
         ws1 = torch.empty(hm.hm_moe_gemm_workspace_size(d_gu, afmt, t, topk), dtype=torch.uint8, device=dev)
         ws2 = torch.empty(hm.hm_moe_gemm_workspace_size(d_dn, afmt, t, topk), dtype=torch.uint8, device=dev)
+        rw_d = torch.from_numpy(rw).to(dev)
+        hbuf = torch.empty(P, I, dtype=torch.bfloat16, device=dev)
+        out = torch.empty(t, H, dtype=torch.bfloat16, device=dev)
         if fmt == "mxfp4":
             x8 = torch.empty(t, H, dtype=torch.uint8, device=dev)
             xs = torch.empty(t, dtype=torch.float32, device=dev)
@@ -373,19 +376,45 @@ def run_moe(args, fmt):
                 hm.hm_moe_gemm(d_gu, w_gu, x, off, sp, t, topk, 0, y=y1, ws=ws1)
                 hm.hm_moe_gemm(d_dn, w_dn, a2, off, sp, t, topk, 1, y=y2, ws=ws2)
 
-        def nsteps(k):
+        def block():
+            # the whole MoE feed-forward block: sort, gate_up, SiLU product,
+            # down on its output, weighted combine back to token order
+            hm.hm_moe_sort(ids_d, E, cnt, off, sp)
+            if fmt == "mxfp4":
+                hm.hm_quant_fp8_rows(x, x8, xs)
+                hm.hm_moe_gemm(d_gu, w_gu, x8, off, sp, t, topk, 0, a_row_scale=xs, y=y1, ws=ws1)
+                hm.hm_silu_mul(y1, hbuf)
+                hm.hm_quant_fp8_rows(hbuf, a8, as_)
+                hm.hm_moe_gemm(d_dn, w_dn, a8, off, sp, t, topk, 1, a_row_scale=as_, y=y2, ws=ws2)
+            else:
+                hm.hm_moe_gemm(d_gu, w_gu, x, off, sp, t, topk, 0, y=y1, ws=ws1)
+                hm.hm_silu_mul(y1, hbuf)
+                hm.hm_moe_gemm(d_dn, w_dn, hbuf, off, sp, t, topk, 1, y=y2, ws=ws2)
+            hm.hm_moe_combine(y2, rw_d, topk, out)
+
+        def nsteps(k, fn1=step):
             def fn():
                 for _ in range(k):
-                    step()
+                    fn1()
             return fn
-        g_warm = capture(torch, nsteps(max(args.warmup, 1)))
-        g_steps = capture(torch, nsteps(args.steps))
-        g_warm.replay()
-        torch.cuda.synchronize()
-        tm.start()
-        g_steps.replay()
-        ms_t = tm.stop_ms() / args.steps
-        del g_warm, g_steps
+
+        def timed(fn1, k):
+            g_warm = capture(torch, nsteps(max(args.warmup, 1), fn1))
+            g_steps = capture(torch, nsteps(k, fn1))
+            g_warm.replay()
+            torch.cuda.synchronize()
+            tm.start()
+            g_steps.replay()
+            ms = tm.stop_ms() / k
+            del g_warm, g_steps
+            return ms
+        ms_t = timed(step, args.steps)
+        block_ms = timed(block, args.steps)
+        reps = max(args.reps, 1)
+        silu_ms = timed(lambda: hm.hm_silu_mul(y1, hbuf), reps)
+        comb_ms = timed(lambda: hm.hm_moe_combine(y2, rw_d, topk, out), reps)
+        silu_b = P * (2 * I) * 2 + P * I * 2               # read gate | up, write h
+        comb_b = P * H * 2 + t * H * 2 + P * 4             # read pair rows and weights, write tokens
         counts = np.bincount(ids.ravel(), minlength=E)
         act = int((counts > 0).sum())
         fl = 2.0 * P * (2 * I) * H + 2.0 * P * H * I
@@ -396,11 +425,17 @@ def run_moe(args, fmt):
                           weight_GBps=round(wb / ms_t / 1e6, 1), active_experts=act,
                           max_rows=int(counts.max()), roofline_frac=round(t_roof / (ms_t * 1e-3), 4),
                           bound="mfma" if fl / (peak * 1e12) >= wb / (HBM_PEAK_GBS * 1e9) else "hbm",
-                          flops=fl, weight_bytes=wb))
+                          flops=fl, weight_bytes=wb,
+                          block_ms=round(block_ms, 4),
+                          silu_mul=dict(us=round(silu_ms * 1e3, 2), GBps=round(silu_b / silu_ms / 1e6, 1),
+                                        hbm_frac=round(silu_b / silu_ms / 1e6 / HBM_PEAK_GBS, 4)),
+                          combine=dict(us=round(comb_ms * 1e3, 2), GBps=round(comb_b / comb_ms / 1e6, 1),
+                                       hbm_frac=round(comb_b / comb_ms / 1e6 / HBM_PEAK_GBS, 4))))
         step_ms += ms_t
         step_fl += fl
     wl = (f"MoE {'W4A8-MXFP4' if fmt == 'mxfp4' else 'W4A16 int4-sym G128'} 256 experts top-8 "
-          f"Zipf(1.1) router, gate_up N=4096 K=7168 + down N=7168 K=2048, T={ts}, sort included")
+          f"Zipf(1.1) router, gate_up N=4096 K=7168 + down N=7168 K=2048, T={ts}, sort included; "
+          f"block_ms adds the SiLU product, the down GEMM on its output and the weighted combine")
     return dict(metric=METRIC, value=round(step_fl / (step_ms * 1e-3) / 1e12, 3), unit="TFLOP/s",
                 n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=round(step_ms, 4),
                 higher_is_better=True, scaling="weak", vs_baseline=None,
