@@ -56,7 +56,9 @@ def kernel_of(plan):
         return "k_gemm_stream"
     if "256x256" in plan:
         return "k_gemm_big"
-    return "k_gemm_mid" if "128x64" in plan else "k_gemm_tile"
+    if "128x64" in plan:
+        return "k_gemm_mid"
+    return "k_gemm_mid_mx" if "64x128" in plan else "k_gemm_tile"
 
 
 def src_hash():
