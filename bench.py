@@ -8,7 +8,7 @@ flops of the step / step time (TFLOP/s).  Weights rotate through enough
 distinct copies (>= 2 x 256 MB) that the 256 MB last-level cache cannot serve
 them; activations are resident in HBM before the timed region starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_w4a16|dense_w4a8|moe_w4a16|moe_w4a8]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_w4a16|dense_w4a8|moe_w4a16|moe_w4a8|shards]
 
 One JSON line is printed (rank 0).  Extra workloads exist for measurement; the
 default line is the dense W4A16 sweep.
@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="dense_w4a16",
-                   choices=["dense_w4a16", "dense_w4a8", "moe_w4a16", "moe_w4a8"])
+                   choices=["dense_w4a16", "dense_w4a8", "moe_w4a16", "moe_w4a8", "shards"])
     p.add_argument("--reps", type=int, default=30, help="launches per M for per-kernel timing")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle (cpu_baseline) leg")
     p.add_argument("--counters-run", action="store_true",
@@ -48,6 +48,17 @@ def parse():
                    help="turn the FETCH_SIZE and WRITE_SIZE csv output of two --counters-run "
                         "passes into profiles/traffic.json (no GPU needed)")
     return p.parse_args()
+
+
+def weight_bytes(n, k, fmt):
+    """Algorithmic bytes of one layer's weights in the standard format: 4-bit
+    codes plus one scale per group (bf16 per 128 for the INT4 formats, one
+    E8M0 byte per 32 for MXFP4) and, for uint4, one 4-bit zero point per
+    group (the pages' 66 bytes per 128 weights, 66.5 with the zero point)."""
+    if fmt == "mxfp4":
+        return n * k / 2 + n * (k // 32)
+    extra = 0.5 if fmt == "uint4_zp" else 0.0
+    return n * k / 2 + n * (k // 128) * (2 + extra)
 
 
 def kernel_of(plan):
@@ -167,7 +178,6 @@ def run_dense(args, fmt):
     import torch
     import quantized_gemm_int4_amd as hm
     import synthetic
-    from oracle import quant as oq  # noqa: F401  (only the cpu_baseline leg below uses the oracle)
 
     if fmt == "mxfp4":
         n, k, ms = 7168, 2048, [16, 256, 4096]
@@ -180,7 +190,7 @@ def run_dense(args, fmt):
         afmt = 0
         wl = "dense W4A16 asym uint4 G128 (bf16 scale + 4-bit zero) N=14336 K=4096 M={1,16,128,1024,4096}"
     S = dense_setup(torch, hm, synthetic, fmt, n, k, ms)
-    alg_w = oq.storage_bytes(n, k, fmt)          # algorithmic weight bytes (standard format)
+    alg_w = weight_bytes(n, k, fmt)              # algorithmic weight bytes (standard format)
     tm = Timer(torch)
 
     ctr = [0]
@@ -314,11 +324,62 @@ def cpu_dense(S, fmt, n, k, ms, hm, torch):
 
 # ============================================================================ MoE
 
+def run_shards(args):
+    """One rank's share of the dense W4A16 layer (N=14336, K=4096) under
+    8-way tensor parallelism, on this one GPU: the column shard N=1792, K=4096
+    (each rank a slice of the outputs; no exchange, or one all-gather) and the
+    row shard N=14336, K=512 (each rank a slice of K; one all-reduce of the
+    output).  The collectives are not run; the figures are the GEMM a rank
+    would launch, per M of the sweep."""
+    import torch
+    import quantized_gemm_int4_amd as hm
+    import synthetic
+
+    ms = [1, 16, 128, 1024, 4096]
+    tm = Timer(torch)
+    ctr = [0]
+    shapes = []
+    tot_fl, tot_ms = 0.0, 0.0
+    for label, n, k in (("tp8 column shard", 1792, 4096), ("tp8 row shard", 14336, 512)):
+        S = dense_setup(torch, hm, synthetic, "uint4_zp", n, k, ms)
+        alg_w = weight_bytes(n, k, "uint4_zp")
+        per_m = []
+        for m in ms:
+            def reps_fn(m=m):
+                for _ in range(args.reps):
+                    dense_call(hm, S, m, ctr[0], "uint4_zp")
+                    ctr[0] += 1
+            g = capture(torch, reps_fn)
+            g.replay()
+            torch.cuda.synchronize()
+            tm.start()
+            g.replay()
+            us = tm.stop_ms() * 1e3 / args.reps
+            del g
+            fl = 2.0 * m * n * k
+            byts = alg_w + m * k * 2 + m * n * 2
+            t_roof = max(byts / (HBM_PEAK_GBS * 1e9), fl / (BF16_PEAK_TFLOPS * 1e12))
+            per_m.append(dict(M=m, us=round(us, 3), tflops=round(fl / us / 1e6, 3),
+                              weight_GBps=round(alg_w / us / 1e3, 1), roofline_frac=round(t_roof / (us * 1e-6), 4),
+                              plan=hm.hm_gemm_plan(S["desc"], 0, m)))
+            tot_fl += fl
+            tot_ms += us * 1e-3
+        shapes.append(dict(shard=label, N=n, K=k, sweep=per_m))
+        del S
+        torch.cuda.empty_cache()
+    return dict(metric=METRIC, value=round(tot_fl / (tot_ms * 1e-3) / 1e12, 3), unit="TFLOP/s", n_gpus=1,
+                steps=args.reps, warmup=args.warmup, ms_per_step=round(tot_ms, 4), higher_is_better=True,
+                scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+                config=dict(workload="one rank's GEMM of the dense W4A16 uint4 layer N=14336 K=4096 under 8-way "
+                                     "tensor parallelism (column shard N=1792 K=4096, row shard N=14336 K=512), "
+                                     "M={1,16,128,1024,4096}; collectives not run"),
+                shards=shapes, roofline=None, cpu_baseline=None)
+
+
 def run_moe(args, fmt):
     import torch
     import quantized_gemm_int4_amd as hm
     import synthetic
-    from oracle import quant as oq
 
     dev = torch.device("cuda:0")
     E, topk, H, I = 256, 8, 7168, 2048
@@ -420,7 +481,7 @@ def run_moe(args, fmt):
         counts = np.bincount(ids.ravel(), minlength=E)
         act = int((counts > 0).sum())
         fl = 2.0 * P * (2 * I) * H + 2.0 * P * H * I
-        wb = act * (oq.storage_bytes(2 * I, H, fmt) + oq.storage_bytes(H, I, fmt))
+        wb = act * (weight_bytes(2 * I, H, fmt) + weight_bytes(H, I, fmt))
         peak = FP8_PEAK_TFLOPS if fmt == "mxfp4" else BF16_PEAK_TFLOPS
         t_roof = max(wb / (HBM_PEAK_GBS * 1e9), fl / (peak * 1e12))
         per_t.append(dict(T=t, ms=round(ms_t, 4), tflops=round(fl / ms_t / 1e9, 3),
@@ -565,7 +626,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
-    if args.workload.startswith("dense"):
+    if args.workload == "shards":
+        out = run_shards(args)
+    elif args.workload.startswith("dense"):
         out = run_dense(args, "mxfp4" if args.workload == "dense_w4a8" else "uint4_zp")
     else:
         out = run_moe(args, "mxfp4" if args.workload == "moe_w4a8" else "int4_sym")

@@ -27,7 +27,7 @@ constexpr int kMoeStreamRows = 16;   // rows per grouped streaming unit
 // -19% / -5% / -5% against 16 rows and one block); MXFP4 keeps 16 and one.
 constexpr int kMoeStreamMaxA16 = 64, kMoeStreamNbwA16 = 2;
 constexpr int kMoeStreamMaxMx = 16, kMoeStreamNbwMx = 1;
-constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles are used
+constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles may be used
 constexpr int kMoeBigMinRows = 192;   // an expert remainder of this many rows gets a 256-row unit
 constexpr int kGroupedGridStream = 2048;
 constexpr int kGroupedGridTile = 1024;
@@ -80,7 +80,15 @@ DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
   p.stream = (force == 1) || (force == 0 && m <= kStreamMaxRows);
   if (force == 1 && m > kStreamMaxRows) p.stream = false;  // streaming handles <= 32 rows per block
   if (!p.stream) {
-    p.big = (force == 3) || (force == 0 && m >= kBigMinRows);
+    // W4A16: 256 x 256 tiles unless 128 x 64 tiles take fewer rounds of the
+    // chip by the measured cost of a round (one of 256 x 256 tiles ~ 3.8 of
+    // 128 x 64 tiles, N = 1792 / 7168 / 14336, K = 4096): a narrow N (one
+    // rank's column shard, N = 1792, M = 1024: 28 large tiles) runs 3.5x
+    // faster on the smaller tiles
+    const int64_t big_rounds = (big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows) + 255) / 256;
+    const int64_t mid_rounds = (mid_n_tiles(G, false) * ((m + kTileM - 1) / kTileM) + 255) / 256;
+    const bool mid_fewer = d->wfmt != HM_W_MXFP4 && mid_rounds * 10 < big_rounds * 38;
+    p.big = (force == 3) || (force == 0 && m >= kBigMinRows && !mid_fewer);
     p.mid = !p.big && force != 4;
     return p;
   }

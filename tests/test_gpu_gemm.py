@@ -273,3 +273,13 @@ def test_big_half_tiles(fmt, m, halves):
     plan = hm.hm_gemm_plan(L.desc, hm.HM_A_BF16, m)
     assert "256x256" in plan and f"half_tiles={halves}" in plan, plan
     L.check(synthetic.activations(15, m, k, index=m))
+
+
+@pytest.mark.parametrize("n,k", [(1792, 4096), (14336, 512)])
+@pytest.mark.parametrize("m", [16, 300, 600])
+def test_tp8_shard_shapes(n, k, m):
+    """One rank's GEMM of the dense uint4 layer under 8-way tensor
+    parallelism: the column shard (N=1792, K=4096) and the row shard
+    (N=14336, K=512), on the streaming, 128-row and 256-row paths."""
+    L = Layer(quant.FMT_UINT4_ZP, n, k, cfg=18, wseed=n + m)
+    L.check(synthetic.activations(18, m, k, index=m))

@@ -203,3 +203,17 @@ def test_fp8_rows_brute_force_and_torch():
         assert np.array_equal(codes[m], qf.view(torch.uint8).numpy())
         # the row maximum lands on (or next to) the largest code
         assert codecs.e4m3_value(codes[m]).__abs__().max() == 448.0
+
+
+def test_bench_weight_bytes_match_storage():
+    """bench.py counts algorithmic weight bytes on its own (the product side
+    does not import the oracle); the count equals the oracle's storage size."""
+    import importlib.util
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("_bench", os.path.join(root, "bench.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    for n, k, name, fmt in [(14336, 4096, "uint4_zp", quant.FMT_UINT4_ZP), (7168, 2048, "mxfp4", quant.FMT_MXFP4),
+                            (4096, 7168, "int4_sym", quant.FMT_INT4_SYM), (1792, 4096, "uint4_zp", quant.FMT_UINT4_ZP)]:
+        assert b.weight_bytes(n, k, name) == quant.storage_bytes(n, k, fmt)
