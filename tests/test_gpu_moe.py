@@ -1,7 +1,8 @@
 """GPU parity for the MoE path: the expert sort is exact (counts, offsets and
 the stable pair order), and the grouped GEMM matches the oracle's per-expert
-fp64 GEMM for every pair, on small shapes that mix streaming units (<= 32
-rows) and tile units (> 32 rows), and at the workload sizes on sampled pairs."""
+fp64 GEMM for every pair, on small shapes that mix streaming units (small
+experts, cut into 16- or 32-row units), 128-row and 256-row tile units, and
+at the workload sizes on sampled pairs."""
 import os
 
 import numpy as np
