@@ -28,7 +28,12 @@ constexpr int kMoeStreamRows = 16;   // rows per grouped streaming unit
 constexpr int kMoeStreamMaxA16 = 64, kMoeStreamNbwA16 = 2;
 constexpr int kMoeStreamMaxMx = 16, kMoeStreamNbwMx = 1;
 constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles may be used
-constexpr int kMoeBigMinRows = 192;   // an expert remainder of this many rows gets a 256-row unit
+// An expert remainder of at least this many rows gets a 256-row unit (a unit
+// of at most 128 rows runs four of the eight 32-row MFMA blocks) instead of
+// 128 x 64 tile units, which copy the unit's activation rows once per 64
+// columns.  Measured against 192: W4A16 T = 1024 -12%, T = 8192 -2%; W4A8
+// T = 16384 -3..4% (65 and 129 rows).
+constexpr int kMoeBigMinRows = 97;
 constexpr int kGroupedGridStream = 2048;
 constexpr int kGroupedGridTile = 1024;
 constexpr int kGroupedGridMid = 256;     // one 128 x 64 tile block per compute unit (LDS-bound)
@@ -147,7 +152,7 @@ DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
 struct MoePlan {
   int64_t P, max_s, max_t, max_b;
   size_t off_su, off_tu, off_bu, ws_bytes;
-  int nbw, ks, lds_kb, s_rows, s_max;
+  int nbw, ks, lds_kb, s_rows, s_max, big_min;
 };
 
 MoePlan plan_moe(const hm_wdesc* d, int64_t t, int32_t topk) {
@@ -162,7 +167,10 @@ MoePlan plan_moe(const hm_wdesc* d, int64_t t, int32_t topk) {
   if (p.s_max < p.s_rows) p.s_max = p.s_rows;
   p.max_s = p.P / p.s_rows + act;
   p.max_t = (p.P + kTileM - 1) / kTileM + act;
-  p.max_b = p.P / kMoeBigMinRows + 1;         // every 256-row unit holds >= kMoeBigMinRows rows
+  // an expert remainder of at least big_min rows takes a 256-row unit
+  p.big_min = env_int("HM_MOE_BIG_MIN", kMoeBigMinRows);
+  if (p.big_min < 1 || p.big_min > kBigRows) p.big_min = kMoeBigMinRows;
+  p.max_b = p.P / p.big_min + 1;              // every 256-row unit holds >= big_min rows
   p.off_su = 256;
   p.off_tu = align256(p.off_su + (size_t)p.max_s * 16);
   p.off_bu = align256(p.off_tu + (size_t)p.max_t * 16);
@@ -426,7 +434,7 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   a.P = p.P;
   // 256-row units address activation rows with 32-bit byte offsets
   const int64_t a_bytes = (a_rows_are_pairs ? p.P : t) * d->k * (afmt == HM_A_FP8_ROWSCALE ? 1 : 2);
-  const int big_min = (a_bytes < (1ll << 32) && env_int("HM_MOE_BIG", 1)) ? kMoeBigMinRows : 0;
+  const int big_min = (a_bytes < (1ll << 32) && env_int("HM_MOE_BIG", 1)) ? p.big_min : 0;
   hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, p.s_rows, p.s_max, kTileM, big_min,
                                      p.max_s, p.max_t, p.max_b, hdr, su, tu, bu, stream);
   if (e == hipSuccess) {
