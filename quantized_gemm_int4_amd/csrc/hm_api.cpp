@@ -179,7 +179,7 @@ MoePlan plan_moe(const hm_wdesc* d, int64_t t, int32_t topk) {
   if (p.nbw != 1 && p.nbw != 2) p.nbw = mx ? kMoeStreamNbwMx : kMoeStreamNbwA16;
   p.ks = env_int("HM_MOE_STREAM_KS", 1);
   if (p.ks != 1 && p.ks != 2 && p.ks != 4) p.ks = 1;
-  // LDS per streaming block: a unit stages up to 16 rows, so K is walked in
+  // LDS per streaming block: a unit stages up to s_rows rows, so K is walked in
   // pieces that fit this budget; a smaller budget lets more blocks share a
   // compute unit
   p.lds_kb = env_int("HM_MOE_STREAM_LDS_KB", 79);

@@ -9,11 +9,13 @@
 // rows.  The row-major activation stage is XOR-swizzled so that the MFMA
 // operand reads stay free of bank conflicts.  Three LDS stages: copies run
 // two K steps ahead.
-//   * W4A16 (K step 64, eight waves, two per SIMD): each wave owns all 256
-//     rows x 32 columns as 32x32x16 bf16 MFMA blocks (128 accumulators per
-//     lane) and unpacks its columns' weights, copied into LDS one step ahead
-//     of the activations, to bf16 s * (u - z) in between its MFMAs of the
-//     previous step.
+//   * W4A16 (K step 64, four waves, one per SIMD): each wave owns all 256
+//     rows x 64 columns as 2 x 8 blocks of 32x32x16 bf16 MFMA (256
+//     accumulators per lane) and unpacks its columns' weights, copied into
+//     LDS per K group through a ring of group slots, to bf16 s * (u - z) in
+//     between its MFMAs of the previous step.  A tile of at most 128 rows
+//     (the last round's half tiles of a dense grid, a short unit) runs only
+//     four of the eight row blocks.
 //   * W4A8-MXFP4 (K step 128, eight waves of 64 x 128): E2M1 weight tiles and
 //     their E8M0 scale words are copied to LDS too and fed as stored to the
 //     16x16x128 scaled MFMA; the per-token FP8 scale is applied in the

@@ -75,8 +75,11 @@ hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hip
 hipError_t launch_gemm_mid(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
 int64_t mid_n_tiles(const Geom& G, bool mx);
 
-// MFMA kernel with 256 x 256 output tiles.  Dense: one block per tile.
-// Grouped: persistent over (256-row unit x 256-column tile) items, hdr[2] units.
+// MFMA kernel with 256 x 256 output tiles.  Dense: one block per tile, or a
+// persistent grid of one block per CU when there are more tiles than CUs (the
+// last round's tiles split into 128-row halves when they fill half the grid
+// or less, W4A16).  Grouped: persistent over (256-row unit x 256-column tile)
+// items, hdr[2] units.
 hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
 int64_t big_n_tiles(const Geom& G);
 // dense: tiles of the visiting order that run whole (the rest as 128-row halves)
