@@ -130,3 +130,21 @@ def test_moe_block_argument_checks():
     assert _err("hm_moe_combine", None, None, 0, 2, 8, None, None) == 0     # t = 0: no-op
     assert _err("hm_moe_combine", good, None, 4, 2, 8, good, None) == 1
     assert _err("hm_moe_combine", good, P(0x100002), 4, 2, 8, good, None) == 3   # w not 4-byte aligned
+
+
+def test_tile_kernel_choice_by_rounds():
+    """The dense planner takes 256 x 256 tiles unless 128 x 64 tiles need
+    fewer rounds of the chip (a round of large tiles costs ~3.8 small ones):
+    the TP8 column shard (N = 1792) runs its M = 512..2048 on the 128-row
+    kernel, the full layer and the row shard keep 256 x 256 from M = 512."""
+    col = hm.wdesc("uint4_zp", 1792, 4096)
+    full = hm.wdesc("uint4_zp", 14336, 4096)
+    row = hm.wdesc("uint4_zp", 14336, 512)
+    for m in (512, 1024, 2048):
+        assert "128x64" in hm.hm_gemm_plan(col, 0, m)
+    assert "256x256" in hm.hm_gemm_plan(col, 0, 4096)
+    for d in (full, row):
+        for m in (512, 1024, 4096):
+            assert "256x256" in hm.hm_gemm_plan(d, 0, m)
+    assert "128x64" in hm.hm_gemm_plan(full, 0, 511)
+    assert "half_tiles=256" in hm.hm_gemm_plan(full, 0, 4096)
