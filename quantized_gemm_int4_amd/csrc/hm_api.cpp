@@ -17,7 +17,9 @@ namespace {
 
 using namespace hm;
 
-constexpr int kStreamMaxRows = 32;   // dense rows handled by the streaming kernel (two 16-row blocks)
+constexpr int kStreamMaxRows = 32;   // dense rows of one streaming block (two 16-row blocks)
+constexpr int64_t kStreamWideRows = 256;      // narrow-N dense calls stream up to this many rows ...
+constexpr int64_t kStreamChunkCols = 16384;   // ... while 32-row chunks x N stays within this
 constexpr int64_t kStreamLdsBytes = 159 * 1024;  // dynamic LDS one streaming block may use
 constexpr int kMoeStreamRows = 16;   // rows per grouped streaming unit
 // Experts with at most this many rows use the streaming kernel (as units of
@@ -82,8 +84,15 @@ DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
   const Geom G = geom_of(d);
   // 1 = streaming, 2 = 128-row tiles, 3 = 256-row tiles, 4 = W4A16 128 x 128 tiles
   const int force = env_int("HM_FORCE_PATH", 0);
-  p.stream = (force == 1) || (force == 0 && m <= kStreamMaxRows);
-  if (force == 1 && m > kStreamMaxRows) p.stream = false;  // streaming handles <= 32 rows per block
+  // W4A16 up to 256 rows also streams (in 32-row chunks, each re-reading the
+  // weights from the L2) when N is narrow: measured at K = 4096, a streaming
+  // launch costs ~8 us + 0.8 ns per (chunk x column) and a round of 128 x 64
+  // tiles 23-25 us, so chunks x N <= 16384 streams (N = 1792, M = 128: 14.9
+  // against 23.4 us; N = 7168, M = 128 stays on tiles: 25.3 against 28.8 us)
+  const bool narrow = d->wfmt != HM_W_MXFP4 && m <= kStreamWideRows &&
+                      ((m + kStreamMaxRows - 1) / kStreamMaxRows) * d->n <= kStreamChunkCols;
+  p.stream = (force == 1) || (force == 0 && (m <= kStreamMaxRows || narrow));
+  if (force == 1 && m > kStreamWideRows) p.stream = false;  // forced streaming: up to 256 rows
   if (!p.stream) {
     // W4A16: 256 x 256 tiles unless 128 x 64 tiles take fewer rounds of the
     // chip by the measured cost of a round (one of 256 x 256 tiles ~ 3.8 of

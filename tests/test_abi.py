@@ -142,6 +142,12 @@ def test_tile_kernel_choice_by_rounds():
     row = hm.wdesc("uint4_zp", 14336, 512)
     for m in (512, 1024, 2048):
         assert "128x64" in hm.hm_gemm_plan(col, 0, m)
+    # narrow N streams up to 256 rows while 32-row chunks x N <= 16384
+    for m in (48, 128, 256):
+        assert " stream " in hm.hm_gemm_plan(col, 0, m)
+    assert "128x64" in hm.hm_gemm_plan(col, 0, 257)
+    for m in (33, 64, 128):
+        assert "128x64" in hm.hm_gemm_plan(full, 0, m)
     assert "256x256" in hm.hm_gemm_plan(col, 0, 4096)
     for d in (full, row):
         for m in (512, 1024, 4096):

@@ -276,10 +276,11 @@ def test_big_half_tiles(fmt, m, halves):
 
 
 @pytest.mark.parametrize("n,k", [(1792, 4096), (14336, 512)])
-@pytest.mark.parametrize("m", [16, 300, 600])
+@pytest.mark.parametrize("m", [16, 128, 256, 300, 600])
 def test_tp8_shard_shapes(n, k, m):
     """One rank's GEMM of the dense uint4 layer under 8-way tensor
-    parallelism: the column shard (N=1792, K=4096) and the row shard
-    (N=14336, K=512), on the streaming, 128-row and 256-row paths."""
+    parallelism: the column shard (N=1792, K=4096: M = 128 and 256 stream in
+    32-row chunks) and the row shard (N=14336, K=512), on the streaming,
+    128-row and 256-row paths."""
     L = Layer(quant.FMT_UINT4_ZP, n, k, cfg=18, wseed=n + m)
     L.check(synthetic.activations(18, m, k, index=m))
