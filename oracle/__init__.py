@@ -13,9 +13,10 @@ title and section; the pages are the only specification):
 * ``quant``   -- the weight quantizers (symmetric INT4, asymmetric uint4 with a
   zero point, MXFP4), nibble packing, exact dequantization, per-token FP8
   activation quantization, storage accounting.
-* ``gemm``    -- Y = X_hat . W_hat^T in fp64, its error bound sum_k |x w|, and the
-  acceptance check.
-* ``moe``     -- expert sort/offsets and the per-expert (grouped) GEMM.
+* ``gemm``    -- Y = X_hat . W_hat^T in fp64, its error bound sum_k |x w|, the
+  acceptance check, and the element-wise check of the MoE block steps.
+* ``moe``     -- expert sort/offsets, the per-expert (grouped) GEMM, and the
+  MoE block steps around it (SiLU-gated product, top-k weighted combine).
 * ``layout``  -- an independent implementation of the library's documented
   device weight layout, used to check the repack byte for byte.
 
