@@ -8,7 +8,7 @@ flops of the step / step time (TFLOP/s).  Weights rotate through enough
 distinct copies (>= 2 x 256 MB) that the 256 MB last-level cache cannot serve
 them; activations are resident in HBM before the timed region starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_w4a16|dense_w4a8|moe_w4a16|moe_w4a8|shards]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_w4a16|dense_w4a8|moe_w4a16|moe_w4a8|moe_w4a16_mxfp4|shards]
 
 One JSON line is printed (rank 0).  Extra workloads exist for measurement; the
 default line is the dense W4A16 sweep.
@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="dense_w4a16",
-                   choices=["dense_w4a16", "dense_w4a8", "moe_w4a16", "moe_w4a8", "shards"])
+                   choices=["dense_w4a16", "dense_w4a8", "moe_w4a16", "moe_w4a8", "moe_w4a16_mxfp4", "shards"])
     p.add_argument("--reps", type=int, default=30, help="launches per M for per-kernel timing")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle (cpu_baseline) leg")
     p.add_argument("--counters-run", action="store_true",
@@ -376,14 +376,15 @@ def run_shards(args):
                 shards=shapes, roofline=None, cpu_baseline=None)
 
 
-def run_moe(args, fmt):
+def run_moe(args, fmt, a8):
+    """a8: FP8 rows (W4A8-MXFP4); otherwise bf16 rows with any weight format."""
     import torch
     import quantized_gemm_int4_amd as hm
     import synthetic
 
     dev = torch.device("cuda:0")
     E, topk, H, I = 256, 8, 7168, 2048
-    ts = [16384] if fmt == "mxfp4" else [64, 1024, 8192]
+    ts = [16384] if a8 else [64, 1024, 8192]
     g = torch.Generator(device="cuda")
     g.manual_seed(5)
 
@@ -400,13 +401,13 @@ def run_moe(args, fmt):
 
     d_gu, w_gu = weights(2 * I, H)
     d_dn, w_dn = weights(H, I)
-    afmt = 1 if fmt == "mxfp4" else 0
+    afmt = 1 if a8 else 0
     per_t = []
     tm = Timer(torch)
     step_ms = 0.0
     step_fl = 0.0
     for t in ts:
-        ids, rw = synthetic.router_topk(4 if fmt != "mxfp4" else 5, t, E, topk)
+        ids, rw = synthetic.router_topk(5 if a8 else 4, t, E, topk)
         P = t * topk
         ids_d = torch.from_numpy(ids).to(dev)
         x = torch.from_numpy(synthetic.activations(4, t, H, index=t).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -422,19 +423,19 @@ def run_moe(args, fmt):
         rw_d = torch.from_numpy(rw).to(dev)
         hbuf = torch.empty(P, I, dtype=torch.bfloat16, device=dev)
         out = torch.empty(t, H, dtype=torch.bfloat16, device=dev)
-        if fmt == "mxfp4":
+        if a8:
             x8 = torch.empty(t, H, dtype=torch.uint8, device=dev)
             xs = torch.empty(t, dtype=torch.float32, device=dev)
-            a8 = torch.empty(P, I, dtype=torch.uint8, device=dev)
+            a8b = torch.empty(P, I, dtype=torch.uint8, device=dev)
             as_ = torch.empty(P, dtype=torch.float32, device=dev)
 
         def step():
             hm.hm_moe_sort(ids_d, E, cnt, off, sp)
-            if fmt == "mxfp4":
+            if a8:
                 hm.hm_quant_fp8_rows(x, x8, xs)
                 hm.hm_moe_gemm(d_gu, w_gu, x8, off, sp, t, topk, 0, a_row_scale=xs, y=y1, ws=ws1)
-                hm.hm_quant_fp8_rows(a2, a8, as_)
-                hm.hm_moe_gemm(d_dn, w_dn, a8, off, sp, t, topk, 1, a_row_scale=as_, y=y2, ws=ws2)
+                hm.hm_quant_fp8_rows(a2, a8b, as_)
+                hm.hm_moe_gemm(d_dn, w_dn, a8b, off, sp, t, topk, 1, a_row_scale=as_, y=y2, ws=ws2)
             else:
                 hm.hm_moe_gemm(d_gu, w_gu, x, off, sp, t, topk, 0, y=y1, ws=ws1)
                 hm.hm_moe_gemm(d_dn, w_dn, a2, off, sp, t, topk, 1, y=y2, ws=ws2)
@@ -443,12 +444,12 @@ def run_moe(args, fmt):
             # the whole MoE feed-forward block: sort, gate_up, SiLU product,
             # down on its output, weighted combine back to token order
             hm.hm_moe_sort(ids_d, E, cnt, off, sp)
-            if fmt == "mxfp4":
+            if a8:
                 hm.hm_quant_fp8_rows(x, x8, xs)
                 hm.hm_moe_gemm(d_gu, w_gu, x8, off, sp, t, topk, 0, a_row_scale=xs, y=y1, ws=ws1)
                 hm.hm_silu_mul(y1, hbuf)
-                hm.hm_quant_fp8_rows(hbuf, a8, as_)
-                hm.hm_moe_gemm(d_dn, w_dn, a8, off, sp, t, topk, 1, a_row_scale=as_, y=y2, ws=ws2)
+                hm.hm_quant_fp8_rows(hbuf, a8b, as_)
+                hm.hm_moe_gemm(d_dn, w_dn, a8b, off, sp, t, topk, 1, a_row_scale=as_, y=y2, ws=ws2)
             else:
                 hm.hm_moe_gemm(d_gu, w_gu, x, off, sp, t, topk, 0, y=y1, ws=ws1)
                 hm.hm_silu_mul(y1, hbuf)
@@ -482,7 +483,7 @@ def run_moe(args, fmt):
         act = int((counts > 0).sum())
         fl = 2.0 * P * (2 * I) * H + 2.0 * P * H * I
         wb = act * (weight_bytes(2 * I, H, fmt) + weight_bytes(H, I, fmt))
-        peak = FP8_PEAK_TFLOPS if fmt == "mxfp4" else BF16_PEAK_TFLOPS
+        peak = FP8_PEAK_TFLOPS if a8 else BF16_PEAK_TFLOPS
         t_roof = max(wb / (HBM_PEAK_GBS * 1e9), fl / (peak * 1e12))
         per_t.append(dict(T=t, ms=round(ms_t, 4), tflops=round(fl / ms_t / 1e9, 3),
                           weight_GBps=round(wb / ms_t / 1e6, 1), active_experts=act,
@@ -496,30 +497,35 @@ def run_moe(args, fmt):
                                        hbm_frac=round(comb_b / comb_ms / 1e6 / HBM_PEAK_GBS, 4))))
         step_ms += ms_t
         step_fl += fl
-    wl = (f"MoE {'W4A8-MXFP4' if fmt == 'mxfp4' else 'W4A16 int4-sym G128'} 256 experts top-8 "
+    name = "W4A8-MXFP4" if a8 else ("W4A16-MXFP4 (E2M1 + E8M0/32, bf16 rows)" if fmt == "mxfp4"
+                                     else "W4A16 int4-sym G128")
+    wl = (f"MoE {name} 256 experts top-8 "
           f"Zipf(1.1) router, gate_up N=4096 K=7168 + down N=7168 K=2048, T={ts}, sort included; "
           f"block_ms adds the SiLU product, the down GEMM on its output and the weighted combine")
     return dict(metric=METRIC, value=round(step_fl / (step_ms * 1e-3) / 1e12, 3), unit="TFLOP/s",
                 n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=round(step_ms, 4),
                 higher_is_better=True, scaling="weak", vs_baseline=None,
-                dtype="fp8" if fmt == "mxfp4" else "bf16", data="synthetic",
-                config=dict(workload=wl), per_T=per_t, roofline=moe_roofline(per_t, fmt),
+                dtype="fp8" if a8 else "bf16", data="synthetic",
+                config=dict(workload=wl), per_T=per_t, roofline=moe_roofline(per_t, a8, fmt == "mxfp4" and not a8),
                 cpu_baseline=None)
 
 
-def moe_roofline(per_t, fmt):
+def moe_roofline(per_t, a8, f4=False):
     """Roofline of the dominant part of the MoE step: the token count with the
     most time; one launch = one step (expert sort, gate_up and down grouped
     GEMMs), its bound the binding one at that token count."""
     r = max(per_t, key=lambda e: e["ms"])
-    peak = FP8_PEAK_TFLOPS if fmt == "mxfp4" else BF16_PEAK_TFLOPS
+    peak = FP8_PEAK_TFLOPS if a8 else BF16_PEAK_TFLOPS
+    # MXFP4 weights with bf16 rows run grouped streaming and 128 x 128 units only
+    kern = ("hm_moe_gemm (grouped k_gemm_tile + k_gemm_stream)" if f4 else
+            "hm_moe_gemm (grouped k_gemm_big + k_gemm_mid/tile + k_gemm_stream)")
     if r["bound"] == "mfma":
         a = r["flops"] / (r["ms"] * 1e-3) / 1e12
-        return dict(bound="mfma", kernel="hm_moe_gemm (grouped k_gemm_big + k_gemm_mid/tile + k_gemm_stream)",
+        return dict(bound="mfma", kernel=kern,
                     achieved=round(a, 2), peak=peak, unit="TFLOP/s", frac=round(a / peak, 4),
                     per_launch=f"2*P*N*K flops of gate_up + down at T={r['T']}", traffic=None)
     a = r["weight_bytes"] / (r["ms"] * 1e-3) / 1e9
-    return dict(bound="hbm", kernel="hm_moe_gemm (grouped k_gemm_stream + k_gemm_mid/tile + k_gemm_big)",
+    return dict(bound="hbm", kernel=kern,
                 achieved=round(a, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(a / HBM_PEAK_GBS, 4),
                 per_launch=f"weight bytes of the active experts at T={r['T']}", traffic=None)
 
@@ -631,7 +637,8 @@ def main():
     elif args.workload.startswith("dense"):
         out = run_dense(args, "mxfp4" if args.workload == "dense_w4a8" else "uint4_zp")
     else:
-        out = run_moe(args, "mxfp4" if args.workload == "moe_w4a8" else "int4_sym")
+        out = run_moe(args, "int4_sym" if args.workload == "moe_w4a16" else "mxfp4",
+                      args.workload == "moe_w4a8")
     print(json.dumps(out), flush=True)
 
 

@@ -80,8 +80,15 @@ typedef enum hm_afmt {
   HM_A_FP8_ROWSCALE = 1 /* X is OCP E4M3 bytes [M,K] with one fp32 scale per row: x = e4m3(c)*s[m] */
 } hm_afmt;
 
-/* Supported pairs: INT4_SYM and UINT4_ZP with HM_A_BF16 (W4A16);
- *                  MXFP4 with HM_A_FP8_ROWSCALE (W4A8-MXFP4). */
+/* Supported pairs: every weight format with HM_A_BF16 (W4A16: INT4_SYM,
+ *                  UINT4_ZP, and MXFP4, whose E2M1 codes are scaled to bf16
+ *                  in the kernel; the pages list MXFP4 W4A16 among the MoE
+ *                  results, aihaber.org article, performance section);
+ *                  MXFP4 with HM_A_FP8_ROWSCALE (W4A8-MXFP4).
+ * MXFP4 with bf16 rows requires every |w| < 2^128 (E8M0 scale bytes up to
+ * 252 always satisfy it; larger products become inf, and the row's sums NaN):
+ * the dequantized weights enter the bf16 MFMA.  Subnormal products (scale
+ * bytes 0..3) are kept exactly. */
 
 /* Layer description (shapes, number format, group).  num_experts is 1 for a
  * dense layer.  group must be 128 for the INT4 formats and 32 for MXFP4. */

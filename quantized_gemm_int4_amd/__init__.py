@@ -145,8 +145,9 @@ def hm_quant_fp8_rows(x, x8=None, row_scale=None, stream=None):
 
 # -------------------------------------------------------------------- dense GEMM
 
-def _afmt(desc):
-    return HM_A_FP8_ROWSCALE if desc.wfmt == HM_W_MXFP4 else HM_A_BF16
+def _afmt(x):
+    """Activation format from the activation tensor: bf16 rows or E4M3 bytes."""
+    return HM_A_FP8_ROWSCALE if x.dtype == torch.uint8 else HM_A_BF16
 
 
 def hm_gemm_workspace_size(desc, afmt, m):
@@ -163,9 +164,9 @@ def hm_gemm_plan(desc, afmt, m):
 
 
 def hm_gemm(desc, w_dev, x, x_row_scale=None, y=None, ws=None, afmt=None, stream=None):
-    """y[m,n] = x_hat . w_hat^T in bf16.  x: bf16 [m,k] (W4A16) or uint8 E4M3
-    [m,k] with fp32 x_row_scale [m] (W4A8-MXFP4)."""
-    afmt = _afmt(desc) if afmt is None else afmt
+    """y[m,n] = x_hat . w_hat^T in bf16.  x: bf16 [m,k] (W4A16, any weight
+    format) or uint8 E4M3 [m,k] with fp32 x_row_scale [m] (W4A8-MXFP4)."""
+    afmt = _afmt(x) if afmt is None else afmt
     m = x.shape[0]
     if y is None:
         y = torch.empty(m, desc.n, dtype=torch.bfloat16, device=x.device)
@@ -213,8 +214,9 @@ def hm_moe_gemm_workspace_size(desc, afmt, t, topk):
 
 def hm_moe_gemm(desc, w_dev, a, offsets, sorted_pairs, t, topk, a_rows_are_pairs, a_row_scale=None,
                 y=None, ws=None, afmt=None, stream=None):
-    """Grouped GEMM; returns y bf16 [t*topk, n] in pair order."""
-    afmt = _afmt(desc) if afmt is None else afmt
+    """Grouped GEMM; returns y bf16 [t*topk, n] in pair order.  a: bf16 rows,
+    or E4M3 bytes with fp32 a_row_scale (MXFP4 weights only)."""
+    afmt = _afmt(a) if afmt is None else afmt
     P = t * topk
     if y is None:
         y = torch.empty(P, desc.n, dtype=torch.bfloat16, device=a.device)

@@ -174,6 +174,25 @@ __device__ __forceinline__ u32x4_t dq8_bytes(uint32_t w, float s, float zs) {
   return r;
 }
 
+// E8M0 scale byte -> 2^(e - 127) as fp32 (e = 0 is the subnormal 2^-127,
+// e = 255 the format's NaN).
+__device__ __forceinline__ float e8m0_f32(uint32_t e) {
+  return __uint_as_float(e == 0u ? 0x00400000u : (e == 255u ? 0x7FC00000u : e << 23));
+}
+
+// Eight E2M1 codes of one mxfp4 layout word (value 2b in the low nibble of
+// byte b, 2b + 1 in its high nibble) times the power of two s -> eight bf16
+// in value order, by gfx950's scaled fp4 -> bf16 conversion (two values per
+// instruction).  Every product is a bf16 number while |code * s| < 2^128.
+__device__ __forceinline__ u32x4_t fp4x8_bf16(uint32_t w, float s) {
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+  return r;
+}
+
 // 32x32x16 bf16 MFMA: lane L supplies A row L%32 and B column L%32 for K
 // = 8*(L/32) + 0..7; C: lane L holds column L%32, rows 8*j + 4*(L/32) + r in
 // register 4*j + r (j, r = 0..3).

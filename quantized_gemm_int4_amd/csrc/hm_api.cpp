@@ -57,9 +57,17 @@ hm_status check_desc(const hm_wdesc* d) {
 
 hm_status check_pair(const hm_wdesc* d, int32_t afmt) {
   if (afmt != HM_A_BF16 && afmt != HM_A_FP8_ROWSCALE) return HM_ERR_UNSUPPORTED;
-  const bool mx = (d->wfmt == HM_W_MXFP4);
-  if (mx != (afmt == HM_A_FP8_ROWSCALE)) return HM_ERR_UNSUPPORTED;
+  // FP8 rows pair with MXFP4 weights only; bf16 rows with every format
+  if (afmt == HM_A_FP8_ROWSCALE && d->wfmt != HM_W_MXFP4) return HM_ERR_UNSUPPORTED;
   return HM_OK;
+}
+
+// MXFP4 weights with bf16 rows (E2M1 scaled to bf16 inside the kernels)
+bool mx_a16(const hm_wdesc* d, int32_t afmt) { return d->wfmt == HM_W_MXFP4 && afmt == HM_A_BF16; }
+
+const char* pair_name(const hm_wdesc* d, int32_t afmt) {
+  if (d->wfmt == HM_W_MXFP4) return afmt == HM_A_BF16 ? "w4a16-mxfp4" : "w4a8-mxfp4";
+  return d->wfmt == HM_W_UINT4_ZP ? "w4a16-uint4zp" : "w4a16-int4sym";
 }
 
 Geom geom_of(const hm_wdesc* d) { return make_geom(d->wfmt, d->num_experts, d->n, d->k); }
@@ -79,9 +87,10 @@ struct DensePlan {
   size_t ws_bytes;
 };
 
-DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
+DensePlan plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m) {
   DensePlan p{};
   const Geom G = geom_of(d);
+  const bool f4 = mx_a16(d, afmt);
   // 1 = streaming, 2 = 128-row tiles, 3 = 256-row tiles, 4 = W4A16 128 x 128 tiles
   const int force = env_int("HM_FORCE_PATH", 0);
   // W4A16 up to 256 rows also streams (in 32-row chunks, each re-reading the
@@ -104,12 +113,14 @@ DensePlan plan_dense(const hm_wdesc* d, int64_t m) {
     const bool mid_fewer = d->wfmt != HM_W_MXFP4 && mid_rounds * 10 < big_rounds * 38;
     p.big = (force == 3) || (force == 0 && m >= kBigMinRows && !mid_fewer);
     p.mid = !p.big && force != 4;
+    // MXFP4 with bf16 rows: 128 x 128 tiles
+    if (f4) p.big = p.mid = false;
     return p;
   }
   p.sc.mb = (m <= 16) ? 1 : 2;
   const int64_t rows = (m < 16 * p.sc.mb) ? m : 16 * p.sc.mb;
   const int64_t m_chunks = (m + 16 * p.sc.mb - 1) / (16 * p.sc.mb);
-  const int64_t gb = (d->wfmt == HM_W_MXFP4) ? 128 : 256;   // activation bytes per row per group
+  const int64_t gb = (afmt == HM_A_FP8_ROWSCALE) ? 128 : 256;   // activation bytes per row per group
   // Launch shape: (ks, nbw) from the narrowest block (most waves, least work
   // per wave) to the widest, take the first whose blocks all fit on the chip
   // at once.  A block keeps its activation rows in LDS, so the LDS footprint
@@ -164,14 +175,14 @@ struct MoePlan {
   int nbw, ks, lds_kb, s_rows, s_max, big_min;
 };
 
-MoePlan plan_moe(const hm_wdesc* d, int64_t t, int32_t topk) {
+MoePlan plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk) {
   MoePlan p{};
   p.P = t * topk;
   const int64_t act = (p.P < d->num_experts) ? p.P : d->num_experts;
   p.s_rows = env_int("HM_MOE_STREAM_ROWS", kMoeStreamRows);
   if (p.s_rows != 16 && p.s_rows != 32) p.s_rows = kMoeStreamRows;
   // experts with up to s_max rows stream, as ceil(rows / s_rows) units
-  const bool mx = d->wfmt == HM_W_MXFP4;
+  const bool mx = afmt == HM_A_FP8_ROWSCALE;
   p.s_max = env_int("HM_MOE_STREAM_MAX", mx ? kMoeStreamMaxMx : kMoeStreamMaxA16);
   if (p.s_max < p.s_rows) p.s_max = p.s_rows;
   p.max_s = p.P / p.s_rows + act;
@@ -290,7 +301,7 @@ HM_API hm_status hm_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t
   if ((s = check_pair(d, afmt))) return s;
   if (!bytes) return HM_ERR_NULL;
   if (m < 0) return HM_ERR_SHAPE;
-  *bytes = (m == 0) ? 0 : plan_dense(d, m).ws_bytes;
+  *bytes = (m == 0) ? 0 : plan_dense(d, afmt, m).ws_bytes;
   return HM_OK;
 }
 
@@ -301,11 +312,12 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* 
   if ((s = check_pair(d, afmt))) return s;
   if (!buf || buf_len == 0) return HM_ERR_NULL;
   if (m < 0) return HM_ERR_SHAPE;
-  const DensePlan p = plan_dense(d, m);
-  const char* w = d->wfmt == HM_W_MXFP4 ? "w4a8-mxfp4" : (d->wfmt == HM_W_UINT4_ZP ? "w4a16-uint4zp" : "w4a16-int4sym");
+  const DensePlan p = plan_dense(d, afmt, m);
+  const char* w = pair_name(d, afmt);
+  const bool a8 = afmt == HM_A_FP8_ROWSCALE;
   if (p.stream)
     snprintf(buf, buf_len, "%s stream mb=%d nbw=%d ks=%d splits=%d ksg=%d mfma=%s", w, p.sc.mb,
-             p.sc.nbw, p.sc.ks, p.sc.splits, p.ksg, d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
+             p.sc.nbw, p.sc.ks, p.sc.splits, p.ksg, a8 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
   else if (p.big) {
     const Geom G = make_geom(d->wfmt, 1, d->n, d->k);
     const int64_t tiles = big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows);
@@ -320,7 +332,7 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* 
     snprintf(buf, buf_len, "%s tile 128x64 waves=4 (K split) mfma=32x32x16_bf16", w);
   else
     snprintf(buf, buf_len, "%s tile %dx%d waves=2x2 mfma=%s", w, kTileM, kTileN,
-             d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
+             a8 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
   return HM_OK;
 }
 
@@ -337,7 +349,7 @@ HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, con
   if (afmt == HM_A_FP8_ROWSCALE && !x_row_scale) return HM_ERR_NULL;
   if (!aligned(w_dev, 256) || !aligned(x, 16) || !aligned(y, 16)) return HM_ERR_ALIGN;
   if (x_row_scale && !aligned(x_row_scale, 4)) return HM_ERR_ALIGN;
-  const DensePlan p = plan_dense(d, m);
+  const DensePlan p = plan_dense(d, afmt, m);
   if (p.ws_bytes) {
     if (!ws) return HM_ERR_NULL;
     if (ws_bytes < p.ws_bytes) return HM_ERR_WORKSPACE;
@@ -347,6 +359,7 @@ HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, con
   a.w = (const uint8_t*)w_dev;
   a.G = geom_of(d);
   a.wfmt = d->wfmt;
+  a.a8 = afmt == HM_A_FP8_ROWSCALE;
   a.x = x;
   a.xs = (afmt == HM_A_FP8_ROWSCALE) ? x_row_scale : nullptr;
   a.M = m;
@@ -398,7 +411,7 @@ HM_API hm_status hm_moe_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int
   if ((s = check_pair(d, afmt))) return s;
   if (!bytes) return HM_ERR_NULL;
   if (t < 0 || topk < 1 || topk > d->num_experts || d->num_experts > 512) return HM_ERR_SHAPE;
-  *bytes = plan_moe(d, t, topk).ws_bytes;
+  *bytes = plan_moe(d, afmt, t, topk).ws_bytes;
   return HM_OK;
 }
 
@@ -419,7 +432,7 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
       !aligned(offsets, 4) || !aligned(sorted_pairs, 4))
     return HM_ERR_ALIGN;
   if (a_row_scale && !aligned(a_row_scale, 4)) return HM_ERR_ALIGN;
-  const MoePlan p = plan_moe(d, t, topk);
+  const MoePlan p = plan_moe(d, afmt, t, topk);
   if (ws_bytes < p.ws_bytes) return HM_ERR_WORKSPACE;
 
   uint8_t* w8 = (uint8_t*)ws;
@@ -431,6 +444,7 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   a.w = (const uint8_t*)w_dev;
   a.G = geom_of(d);
   a.wfmt = d->wfmt;
+  a.a8 = afmt == HM_A_FP8_ROWSCALE;
   a.x = a_in;
   a.xs = (afmt == HM_A_FP8_ROWSCALE) ? a_row_scale : nullptr;
   a.M = 0;
@@ -443,7 +457,8 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   a.P = p.P;
   // 256-row units address activation rows with 32-bit byte offsets
   const int64_t a_bytes = (a_rows_are_pairs ? p.P : t) * d->k * (afmt == HM_A_FP8_ROWSCALE ? 1 : 2);
-  const int big_min = (a_bytes < (1ll << 32) && env_int("HM_MOE_BIG", 1)) ? p.big_min : 0;
+  const bool f4 = mx_a16(d, afmt);   // MXFP4 with bf16 rows: streaming and 128 x 128 units only
+  const int big_min = (!f4 && a_bytes < (1ll << 32) && env_int("HM_MOE_BIG", 1)) ? p.big_min : 0;
   hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, p.s_rows, p.s_max, kTileM, big_min,
                                      p.max_s, p.max_t, p.max_b, hdr, su, tu, bu, stream);
   if (e == hipSuccess) {
@@ -458,7 +473,7 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
     // units of up to 128 rows: W4A16 on 128 x 64 tiles, W4A8 on 64 x 128
     // tiles (one block per compute unit, LDS-bound); HM_MOE_MID=0 keeps
     // them on the 128 x 128 kernel
-    const bool mid = env_int("HM_MOE_MID", 1) != 0;
+    const bool mid = !f4 && env_int("HM_MOE_MID", 1) != 0;
     const int64_t ntt = mid ? mid_n_tiles(a.G, d->wfmt == HM_W_MXFP4) : (a.G.NB + 7) / 8;
     int64_t gi = p.max_t * ntt;
     const int64_t cap = mid ? kGroupedGridMid : kGroupedGridTile;

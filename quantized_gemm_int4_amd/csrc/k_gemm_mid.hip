@@ -609,6 +609,8 @@ int64_t mid_n_tiles(const Geom& G, bool mx) {
 }
 
 hipError_t launch_gemm_mid(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
+  // MXFP4 weights with bf16 rows run on the streaming and 128 x 128 kernels only
+  if (kmode_of(a) == KM_MX_A16) return hipErrorInvalidValue;
   // scale and zero-point copies use 32-bit offsets from the scale region
   if (a.G.total - a.G.off_scales > 0xFFFFFFFFull) return hipErrorInvalidValue;
   // grouped activation rows are addressed by 32-bit offsets from x

@@ -4,7 +4,10 @@
 // tokens), so every weight byte is read from HBM exactly once, straight into
 // registers: one 16-byte load per lane fetches one 1 KiB tile (16 columns x
 // 128 K) of the device layout, which is exactly the operand of four
-// 16x16x32 bf16 MFMAs (or of one 16x16x128 scaled fp4 x fp8 MFMA for MXFP4).
+// 16x16x32 bf16 MFMAs (or of one 16x16x128 scaled fp4 x fp8 MFMA for MXFP4
+// with FP8 rows; with bf16 rows the E2M1 codes are scaled to bf16 first and fed
+// to four bf16 MFMAs, the lane's 32 K values split into four runs of eight and
+// the activation fragments read in the same order).
 // The few activation rows are copied into LDS with direct global-to-LDS loads
 // (issued before the weight loads, so both latencies overlap) and shared by
 // the block's four waves.  The weights are the MFMA "A" operand (rows =
@@ -38,22 +41,25 @@ struct StreamShape {
   static constexpr int kRedBytes = KS > 1 ? 4 * NBW * MB * 1024 : 0;  // K-split sums
 };
 
-// Template parameters: MX (W4A8-MXFP4 vs W4A16), ZP (zero points), MB (16-row
+// Template parameters: MODE (KMode: INT4 / MXFP4 weights, bf16 / FP8 rows), ZP (zero points), MB (16-row
 // blocks per unit), NBW (16-column blocks per wave), KS (waves splitting one
 // column set's K range), DW (weight prefetch ring: K groups of 128 held in
 // registers ahead of use), GROUPED.
 // Runtime: pg = K groups per activation piece staged in LDS, xb = LDS row
 // stride in bytes (a multiple of 1 KiB plus 16).
-template <bool MX, bool ZP, int MB, int NBW, int KS, int DW, bool GROUPED>
+template <int MODE, bool ZP, int MB, int NBW, int KS, int DW, bool GROUPED>
 __global__ void __launch_bounds__(256)
 k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
+  constexpr bool MX = MODE == KM_MX_A8;                 // FP8 rows, scaled fp4 x fp8 MFMA
+  constexpr bool F4 = MODE == KM_MX_A16;                // MXFP4 codes scaled to bf16
+  constexpr bool MXW = MX || F4;                        // E8M0 scale words
   constexpr int ROWS = MB * 16;
   constexpr int GB = MX ? 128 : 256;                    // activation bytes per row per K group
   constexpr int CS = 4 / KS;                            // column sets per block
   constexpr int RED = StreamShape<KS, NBW, MB>::kRedBytes;
   // vector-memory loads per ring slot: per column block the 1 KiB tile and
   // its scale word(s), plus the zero-point word
-  constexpr int kRingLoads = NBW * (MX ? 2 : (ZP ? 3 : 2));
+  constexpr int kRingLoads = NBW * (MXW ? 2 : (ZP ? 3 : 2));
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   uint8_t* const xs_lds = lds + RED;                    // activations: [rows][xb]
   __shared__ int64_t arow_s[ROWS];
@@ -160,20 +166,20 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
 
     // ---- weight ring: DW groups ahead, raw scale / zero words kept until use
     u32x4_t wq[DW][NBW];
-    uint32_t wsr[DW][NBW], wsh[MX ? 1 : DW][MX ? 1 : NBW], wzr[ZP ? DW : 1][ZP ? NBW : 1];
+    uint32_t wsr[DW][NBW], wsh[MXW ? 1 : DW][MXW ? 1 : NBW], wzr[ZP ? DW : 1][ZP ? NBW : 1];
     auto load_w = [&](int d, int64_t g) {               // g: group index in [0, KG)
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
         const int64_t tile = wtile0[j] + g;
         wq[d][j] = ld16(a.w + tile * 1024 + lane * 16);
-        if (MX) {
+        if (MXW) {
           // four groups' E8M0 scales per lane word: [e][nb][g/4][64 lanes]
           wsr[d][j] = *reinterpret_cast<const uint32_t*>(sbase + ((stile0[j] + g / 4) * 64 + lane) * 4);
         } else {
           // bf16 scales of the four output rows 4*q_l + 0..3 this lane accumulates
           const u32x2_t sp = *reinterpret_cast<const u32x2_t*>(sbase + tile * 32 + q_l * 8);
           wsr[d][j] = sp[0];
-          wsh[MX ? 0 : d][MX ? 0 : j] = sp[1];
+          wsh[MXW ? 0 : d][MXW ? 0 : j] = sp[1];
           if (ZP)
             wzr[ZP ? d : 0][ZP ? j : 0] =
                 *reinterpret_cast<const uint32_t*>(zbase + tile * 8 + (n_l >> 3) * 4);
@@ -233,6 +239,24 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
             for (int rb = 0; rb < MB; ++rb)
               acc[j][rb] = mfma_fp4_fp8(wq[d][j], a0[rb], a1[rb], acc[j][rb], sc, 127);
           }
+        } else if (F4) {
+          // word kk of the lane's slot holds K = 32 q_l + 8 kk + 0..7 of its
+          // column; the activation fragment of MFMA kk covers the same K
+          float sf[NBW];
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) sf[j] = e8m0_f32((wsr[d][j] >> (8 * (g & 3))) & 0xFFu);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            u32x4_t af[MB];
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) af[rb] = ld16(xg + lrow[rb] * xb + (32 * q_l + 8 * kk) * 2);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+              const u32x4_t bw = fp4x8_bf16(wq[d][j][kk], sf[j]);
+#pragma unroll
+              for (int rb = 0; rb < MB; ++rb) acc[j][rb] = mfma_bf16(bw, af[rb], acc[j][rb]);
+            }
+          }
         } else {
           // Raw codes: one MFMA chain adds x * (1 + u/16) and x * -(1 + z/16)
           // per K step, i.e. x * (u - z) / 16, exactly 0 where every code
@@ -263,7 +287,7 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
           }
 #pragma unroll
           for (int j = 0; j < NBW; ++j) {
-            const uint32_t lo2 = wsr[d][j], hi2 = wsh[MX ? 0 : d][MX ? 0 : j];
+            const uint32_t lo2 = wsr[d][j], hi2 = wsh[MXW ? 0 : d][MXW ? 0 : j];
             const float s0 = bf16_to_f32(lo2 & 0xFFFFu), s1 = __uint_as_float(lo2 & 0xFFFF0000u);
             const float s2 = bf16_to_f32(hi2 & 0xFFFFu), s3 = __uint_as_float(hi2 & 0xFFFF0000u);
 #pragma unroll
@@ -337,7 +361,7 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
           const int rl = rb * 16 + n_l;
           if (rl >= rcount || orow_s[rl] < 0) continue;
           f32x4_t v = acc[j][rb];
-          if (!MX) v = v * 16.f;                // raw-code sums carry a factor 1/16 (exact)
+          if (MODE == KM_INT4_A16) v = v * 16.f;   // raw-code sums carry a factor 1/16 (exact)
           if (partial) {
             float* dst = a.part + ((int64_t)split * a.M + m0 + rl) * Np + n;
             st16(dst, __builtin_bit_cast(u32x4_t, v));
@@ -395,7 +419,7 @@ int64_t stream_n_tiles(const Geom& G, const StreamCfg& c) {
 // LDS plan of one launch: K groups per activation piece and the row stride.
 static void stream_lds_plan(const GemmArgs& a, const StreamCfg& c, bool grouped, int red_bytes,
                             int* pg_out, int* xb_out, size_t* bytes_out) {
-  const int64_t gb = (a.wfmt == W_MXFP4) ? 128 : 256;
+  const int64_t gb = (kmode_of(a) == KM_MX_A8) ? 128 : 256;
   const int64_t rows = grouped ? 16 * c.mb : (a.M < 16 * c.mb ? a.M : 16 * c.mb);
   const int64_t ksl = grouped ? a.G.KG : a.ksg;         // groups one block walks
   const int64_t gq = 1024 / gb;                         // groups per 1 KiB of a row
@@ -412,14 +436,14 @@ static void stream_lds_plan(const GemmArgs& a, const StreamCfg& c, bool grouped,
   *bytes_out = (size_t)(red_bytes + rows * xb);
 }
 
-template <bool MX, bool ZP, int MB, int NBW, int KS, bool GROUPED>
+template <int MODE, bool ZP, int MB, int NBW, int KS, bool GROUPED>
 static hipError_t go_stream(const GemmArgs& a, const StreamCfg& c, int grid_items, hipStream_t st) {
   // ring depth in K groups, within the 63 outstanding vector-memory operations
   // one wave can track (up to three loads per group and column block) and a
   // register budget that leaves room for four waves per SIMD at small M
   constexpr int DW = (NBW == 1 && MB == 1 && KS < 4) ? 16 : 8;
   constexpr int RED = StreamShape<KS, NBW, MB>::kRedBytes;
-  auto kern = &k_gemm_stream<MX, ZP, MB, NBW, KS, DW, GROUPED>;
+  auto kern = &k_gemm_stream<MODE, ZP, MB, NBW, KS, DW, GROUPED>;
   int pg, xb;
   size_t lds;
   stream_lds_plan(a, c, GROUPED, RED, &pg, &xb, &lds);
@@ -440,37 +464,41 @@ static hipError_t go_stream(const GemmArgs& a, const StreamCfg& c, int grid_item
   return hipGetLastError();
 }
 
-template <bool MX, bool ZP, int MB, int NBW, bool GROUPED>
+template <int MODE, bool ZP, int MB, int NBW, bool GROUPED>
 static hipError_t go_stream_ks(const GemmArgs& a, const StreamCfg& c, int gi, hipStream_t st) {
   switch (c.ks) {
-    case 4: return go_stream<MX, ZP, MB, NBW, 4, GROUPED>(a, c, gi, st);
-    case 2: return go_stream<MX, ZP, MB, NBW, 2, GROUPED>(a, c, gi, st);
-    default: return go_stream<MX, ZP, MB, NBW, 1, GROUPED>(a, c, gi, st);
+    case 4: return go_stream<MODE, ZP, MB, NBW, 4, GROUPED>(a, c, gi, st);
+    case 2: return go_stream<MODE, ZP, MB, NBW, 2, GROUPED>(a, c, gi, st);
+    default: return go_stream<MODE, ZP, MB, NBW, 1, GROUPED>(a, c, gi, st);
   }
 }
 
-template <bool MX, bool ZP, int MB, bool GROUPED>
+template <int MODE, bool ZP, int MB, bool GROUPED>
 static hipError_t go_stream_nbw(const GemmArgs& a, const StreamCfg& c, int gi, hipStream_t st) {
-  return (c.nbw == 2) ? go_stream_ks<MX, ZP, MB, 2, GROUPED>(a, c, gi, st)
-                      : go_stream_ks<MX, ZP, MB, 1, GROUPED>(a, c, gi, st);
+  return (c.nbw == 2) ? go_stream_ks<MODE, ZP, MB, 2, GROUPED>(a, c, gi, st)
+                      : go_stream_ks<MODE, ZP, MB, 1, GROUPED>(a, c, gi, st);
 }
 
-template <bool MX, bool ZP, bool GROUPED>
+template <int MODE, bool ZP, bool GROUPED>
 static hipError_t go_stream_mb(const GemmArgs& a, const StreamCfg& c, int gi, hipStream_t st) {
-  return (c.mb == 1) ? go_stream_nbw<MX, ZP, 1, GROUPED>(a, c, gi, st)
-                     : go_stream_nbw<MX, ZP, 2, GROUPED>(a, c, gi, st);
+  return (c.mb == 1) ? go_stream_nbw<MODE, ZP, 1, GROUPED>(a, c, gi, st)
+                     : go_stream_nbw<MODE, ZP, 2, GROUPED>(a, c, gi, st);
 }
 
 hipError_t launch_gemm_stream(const GemmArgs& a, const StreamCfg& c, bool grouped, int grid_items,
                               hipStream_t st) {
-  if (a.wfmt == W_MXFP4)
-    return grouped ? go_stream_mb<true, false, true>(a, c, grid_items, st)
-                   : go_stream_mb<true, false, false>(a, c, grid_items, st);
+  const int mode = kmode_of(a);
+  if (mode == KM_MX_A8)
+    return grouped ? go_stream_mb<KM_MX_A8, false, true>(a, c, grid_items, st)
+                   : go_stream_mb<KM_MX_A8, false, false>(a, c, grid_items, st);
+  if (mode == KM_MX_A16)
+    return grouped ? go_stream_mb<KM_MX_A16, false, true>(a, c, grid_items, st)
+                   : go_stream_mb<KM_MX_A16, false, false>(a, c, grid_items, st);
   if (a.wfmt == W_UINT4_ZP)
-    return grouped ? go_stream_mb<false, true, true>(a, c, grid_items, st)
-                   : go_stream_mb<false, true, false>(a, c, grid_items, st);
-  return grouped ? go_stream_mb<false, false, true>(a, c, grid_items, st)
-                 : go_stream_mb<false, false, false>(a, c, grid_items, st);
+    return grouped ? go_stream_mb<KM_INT4_A16, true, true>(a, c, grid_items, st)
+                   : go_stream_mb<KM_INT4_A16, true, false>(a, c, grid_items, st);
+  return grouped ? go_stream_mb<KM_INT4_A16, false, true>(a, c, grid_items, st)
+                 : go_stream_mb<KM_INT4_A16, false, false>(a, c, grid_items, st);
 }
 
 hipError_t launch_splitk_reduce(const GemmArgs& a, int splits, hipStream_t st) {

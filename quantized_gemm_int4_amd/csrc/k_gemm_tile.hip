@@ -9,6 +9,10 @@
 //   * W4A16: the eight 1 KiB weight tiles are read once per block, unpacked and
 //     scaled to bf16 by the block's threads (once per block, not per wave) and
 //     written to LDS already in MFMA fragment order;
+//   * MXFP4 with bf16 rows: the same, each lane's eight E2M1 codes of a
+//     fragment scaled to bf16 with their E8M0 scale (the fragment's K run is
+//     32 (L/16) + 8 ks + 0..7 instead of 32 ks + 8 (L/16) + 0..7, and the
+//     activation fragments follow it);
 //   * W4A8-MXFP4: each wave loads its E2M1 fragments straight into registers
 //     and feeds them with their E8M0 scales to the 16x16x128 scaled MFMA; the
 //     per-token FP8 scale is applied in the epilogue.
@@ -18,9 +22,11 @@
 
 namespace hm {
 
-template <bool MX, bool GROUPED>
+template <int MODE, bool GROUPED>
 __global__ void __launch_bounds__(256)
 k_gemm_tile(GemmArgs a, int n_tiles) {
+  constexpr bool MX = MODE == KM_MX_A8;                // FP8 rows, scaled fp4 x fp8 MFMA
+  constexpr bool F4 = MODE == KM_MX_A16;               // MXFP4 codes scaled to bf16
   constexpr int XB = MX ? (128 + 16) : (256 + 16);     // LDS activation row stride (bytes)
   constexpr int XPR = MX ? 8 : 16;                     // 16-byte pieces per activation row
   constexpr int XLD = kTileM * XPR / 256;              // pieces per thread
@@ -114,8 +120,13 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
           const int L = q & 63;
           const int64_t tile = (e * G.NB + nb) * G.KG + g;
           wq[i] = ld16(a.w + tile * 1024 + L * 16);
-          wsr[i] = s16[tile * 16 + (L & 15)];
-          wzr[i] = zp ? z32[tile * 2 + ((L & 15) >> 3)] : 0u;
+          if (F4) {
+            wsr[i] = (s32[((e * G.NB + nb) * G.KG4 + g / 4) * 64 + L] >> (8 * (g & 3))) & 0xFFu;
+            wzr[i] = 0u;
+          } else {
+            wsr[i] = s16[tile * 16 + (L & 15)];
+            wzr[i] = zp ? z32[tile * 2 + ((L & 15) >> 3)] : 0u;
+          }
         }
       }
     };
@@ -131,6 +142,12 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
         for (int i = 0; i < 2; ++i) {
           const int q = tid + 256 * i;
           const int nbl = q >> 6, L = q & 63;
+          if (F4) {
+            const float sf = e8m0_f32(wsr[i]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st16(&ws_lds[((nbl * 4 + j) * 64 + L) * 16], fp4x8_bf16(wq[i][j], sf));
+            continue;
+          }
           const float sv = bf16_to_f32(wsr[i] & 0xFFFF);
           const float z = zp ? (float)((wzr[i] >> (4 * (L & 7))) & 0xF) : 8.0f;
           const float zs = -z * sv;
@@ -173,7 +190,7 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
           u32x4_t xf[4], wf[4];
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
-            xf[mb] = ld16(xs_lds + (wm * 64 + mb * 16 + n_l) * XB + (32 * ks + 8 * q_l) * 2);
+            xf[mb] = ld16(xs_lds + (wm * 64 + mb * 16 + n_l) * XB + (F4 ? 32 * q_l + 8 * ks : 32 * ks + 8 * q_l) * 2);
 #pragma unroll
           for (int j = 0; j < 4; ++j) wf[j] = ld16(ws_lds + (((wn * 4 + j) * 4 + ks) * 64 + lane) * 16);
 #pragma unroll
@@ -215,20 +232,23 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
   }
 }
 
-template <bool MX, bool GROUPED>
+template <int MODE, bool GROUPED>
 static hipError_t go_tile(const GemmArgs& a, int grid_items, hipStream_t st) {
   const int n_tiles = (int)((a.G.NB + 7) / 8);
   dim3 grid;
   if (GROUPED) grid = dim3((unsigned)(grid_items > 0 ? grid_items : 1));
   else grid = dim3((unsigned)n_tiles, (unsigned)((a.M + kTileM - 1) / kTileM));
-  hipLaunchKernelGGL((k_gemm_tile<MX, GROUPED>), grid, dim3(256), 0, st, a, n_tiles);
+  hipLaunchKernelGGL((k_gemm_tile<MODE, GROUPED>), grid, dim3(256), 0, st, a, n_tiles);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
-  const bool mx = (a.wfmt == W_MXFP4);
-  if (mx) return grouped ? go_tile<true, true>(a, grid_items, st) : go_tile<true, false>(a, grid_items, st);
-  return grouped ? go_tile<false, true>(a, grid_items, st) : go_tile<false, false>(a, grid_items, st);
+  const int mode = kmode_of(a);
+  if (mode == KM_MX_A8)
+    return grouped ? go_tile<KM_MX_A8, true>(a, grid_items, st) : go_tile<KM_MX_A8, false>(a, grid_items, st);
+  if (mode == KM_MX_A16)
+    return grouped ? go_tile<KM_MX_A16, true>(a, grid_items, st) : go_tile<KM_MX_A16, false>(a, grid_items, st);
+  return grouped ? go_tile<KM_INT4_A16, true>(a, grid_items, st) : go_tile<KM_INT4_A16, false>(a, grid_items, st);
 }
 
 }  // namespace hm

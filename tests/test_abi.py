@@ -97,6 +97,27 @@ def test_plan_strings():
     assert hm.hm_gemm_workspace_size(d, 0, 4096) == 0
 
 
+def test_mxfp4_bf16_rows_plans():
+    """MXFP4 weights take bf16 rows too: the streaming kernel for few rows,
+    the 128 x 128 kernel above (bf16 MFMA); FP8 rows keep the W4A8 kernels;
+    INT4 weights reject FP8 rows."""
+    mx = hm.wdesc("mxfp4", 7168, 2048)
+    for m in (1, 16, 32):
+        p = hm.hm_gemm_plan(mx, hm.HM_A_BF16, m)
+        assert p.startswith("w4a16-mxfp4 stream") and p.endswith("mfma=16x16x32_bf16"), p
+    for m in (33, 256, 4096):
+        p = hm.hm_gemm_plan(mx, hm.HM_A_BF16, m)
+        assert p.startswith("w4a16-mxfp4 tile 128x128") and p.endswith("16x16x32_bf16"), p
+    assert hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, 4096).startswith("w4a8-mxfp4 tile 256x256")
+    assert hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, 1).startswith("w4a8-mxfp4 stream")
+    sz = ctypes.c_size_t()
+    i4 = hm.wdesc("int4_sym", 256, 512)
+    assert _err("hm_gemm_workspace_size", ctypes.byref(i4), 1, 4, ctypes.byref(sz)) == 4
+    moe = hm.wdesc("mxfp4", 4096, 7168, 256)
+    assert _err("hm_moe_gemm_workspace_size", ctypes.byref(moe), 0, 64, 8, ctypes.byref(sz)) == 0
+    assert sz.value > 0
+
+
 def test_moe_argument_checks():
     P = ctypes.c_void_p
     good = P(0x100000)
