@@ -193,6 +193,17 @@ __device__ __forceinline__ u32x4_t fp4x8_bf16(uint32_t w, float s) {
   return r;
 }
 
+// Codes 2 sel, 2 sel + 1 of one word (byte sel, sel = 0..3 known at compile
+// time after unrolling) times s -> one bf16 pair.
+__device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t w, float s, int sel) {
+  switch (sel & 3) {
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+  }
+}
+
 // 32x32x16 bf16 MFMA: lane L supplies A row L%32 and B column L%32 for K
 // = 8*(L/32) + 0..7; C: lane L holds column L%32, rows 8*j + 4*(L/32) + r in
 // register 4*j + r (j, r = 0..3).

@@ -87,6 +87,15 @@ struct DensePlan {
   size_t ws_bytes;
 };
 
+// MXFP4 with bf16 rows: rows that take the 128 x 128 kernel instead of the
+// 128 x 64 one (at least 8 rounds of 128 x 64 tiles on the 256 compute units)
+bool f4_wide_tiles(const Geom& G, int64_t rows) {
+  const int64_t mt = (rows + kTileM - 1) / kTileM;
+  const int64_t mid_rounds = (mid_n_tiles(G, false) * mt + 255) / 256;
+  const int64_t tile_rounds = (((G.NB + 7) / 8) * mt + 255) / 256;
+  return mid_rounds >= 8 && tile_rounds < mid_rounds;
+}
+
 DensePlan plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m) {
   DensePlan p{};
   const Geom G = geom_of(d);
@@ -113,8 +122,16 @@ DensePlan plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m) {
     const bool mid_fewer = d->wfmt != HM_W_MXFP4 && mid_rounds * 10 < big_rounds * 38;
     p.big = (force == 3) || (force == 0 && m >= kBigMinRows && !mid_fewer);
     p.mid = !p.big && force != 4;
-    // MXFP4 with bf16 rows: 128 x 128 tiles
-    if (f4) p.big = p.mid = false;
+    // MXFP4 with bf16 rows (no 256 x 256 kernel): 128 x 64 tiles, or 128 x
+    // 128 tiles once the 128 x 64 ones take many rounds of the chip.
+    // Measured at N = 7168 K = 2048 / N = 14336 K = 4096: M = 256 / 128 on
+    // 128 x 64 tiles 14.9 / 23.9 us against 30.1 / 63.2 (one round each),
+    // M = 1024 even (4 / 7 rounds against 2 / 4), M = 4096 147 / 520 us on
+    // 128 x 128 tiles against 273 / 1039 (14 / 28 rounds against 7 / 14)
+    if (f4) {
+      p.big = false;
+      p.mid = (force == 2 || force == 3) || (force == 0 && !f4_wide_tiles(G, m));
+    }
     return p;
   }
   p.sc.mb = (m <= 16) ? 1 : 2;
@@ -326,7 +343,7 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* 
              d->wfmt == HM_W_MXFP4 ? "4x2" : "1x4", d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "32x32x16_bf16",
              (long long)halves);
   }
-  else if (p.mid && d->wfmt == HM_W_MXFP4)
+  else if (p.mid && a8)
     snprintf(buf, buf_len, "%s tile 64x128 waves=2x2 mfma=scale_16x16x128_f8f6f4", w);
   else if (p.mid)
     snprintf(buf, buf_len, "%s tile 128x64 waves=4 (K split) mfma=32x32x16_bf16", w);
@@ -457,7 +474,7 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   a.P = p.P;
   // 256-row units address activation rows with 32-bit byte offsets
   const int64_t a_bytes = (a_rows_are_pairs ? p.P : t) * d->k * (afmt == HM_A_FP8_ROWSCALE ? 1 : 2);
-  const bool f4 = mx_a16(d, afmt);   // MXFP4 with bf16 rows: streaming and 128 x 128 units only
+  const bool f4 = mx_a16(d, afmt);   // MXFP4 with bf16 rows: streaming and 128-row units only
   const int big_min = (!f4 && a_bytes < (1ll << 32) && env_int("HM_MOE_BIG", 1)) ? p.big_min : 0;
   hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, p.s_rows, p.s_max, kTileM, big_min,
                                      p.max_s, p.max_t, p.max_b, hdr, su, tu, bu, stream);
@@ -473,8 +490,11 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
     // units of up to 128 rows: W4A16 on 128 x 64 tiles, W4A8 on 64 x 128
     // tiles (one block per compute unit, LDS-bound); HM_MOE_MID=0 keeps
     // them on the 128 x 128 kernel
-    const bool mid = !f4 && env_int("HM_MOE_MID", 1) != 0;
-    const int64_t ntt = mid ? mid_n_tiles(a.G, d->wfmt == HM_W_MXFP4) : (a.G.NB + 7) / 8;
+    // MXFP4 with bf16 rows: the 128 x 128 kernel when all pairs in 128-row
+    // units would take many rounds of 128 x 64 tiles (T = 8192: 7.92 against
+    // 8.30 ms)
+    const bool mid = env_int("HM_MOE_MID", 1) != 0 && !(f4 && f4_wide_tiles(a.G, p.P));
+    const int64_t ntt = mid ? mid_n_tiles(a.G, afmt == HM_A_FP8_ROWSCALE) : (a.G.NB + 7) / 8;
     int64_t gi = p.max_t * ntt;
     const int64_t cap = mid ? kGroupedGridMid : kGroupedGridTile;
     if (gi > cap) gi = cap;

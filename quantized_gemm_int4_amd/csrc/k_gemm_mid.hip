@@ -25,6 +25,13 @@
 // Operands of the next group's first K part are unpacked during the second
 // K part of the current one, so each group starts with ready operands.
 //
+// MXFP4 weights with bf16 rows (F4) run the same kernel: wave w's K values
+// 32 w .. 32 w + 31 are exactly the E2M1 codes of quarter w of each 16-byte
+// slot, whose words 2 kk' + hi the lanes read, with one E8M0 scale per lane
+// and column half; the gather copies the 256 bytes of scale words of the
+// wave's column block (four groups each) and the codes are scaled to bf16
+// by the hardware conversion instead of the INT4 arithmetic.
+//
 // W4A8-MXFP4 (k_gemm_mid_mx): one K group (128 values) is a single scaled
 // 16x16x128 fp4 x fp8 MFMA, so the waves split the tile instead: 64 rows x
 // 128 columns per 256-thread block (224 blocks for M = 256, N = 7168), each
@@ -74,7 +81,7 @@ struct MxFrag {
 
 }  // namespace
 
-template <bool ZP, bool GROUPED>
+template <bool ZP, bool GROUPED, bool F4>
 __global__ void __launch_bounds__(256, 1)
 k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -130,13 +137,15 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2) xo[k2] = (uint32_t)(l32 * 256 + 16 * ((4 * wave + 2 * k2 + hi) ^ (l32 & 15)));
   // A operand (weights) of column half nb2, K part kk': column 32 nb2 + l32 in
-  // code tile 2 nb2 + c_l, word w of slot c16 + 16 (2 kk' + hi)
+  // code tile 2 nb2 + c_l, word w of slot c16 + 16 (2 kk' + hi) (INT4), word
+  // 2 kk' + hi of slot c16 + 16 w (MXFP4)
   uint32_t wo[2][2];
 #pragma unroll
   for (int nb2 = 0; nb2 < 2; ++nb2)
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
-      wo[nb2][k2] = (uint32_t)((2 * nb2 + c_l) * 1024 + (c16 + 16 * (2 * k2 + hi)) * 16 + 4 * wave);
+      wo[nb2][k2] = F4 ? (uint32_t)((2 * nb2 + c_l) * 1024 + (c16 + 16 * wave) * 16 + 4 * (2 * k2 + hi))
+                       : (uint32_t)((2 * nb2 + c_l) * 1024 + (c16 + 16 * (2 * k2 + hi)) * 16 + 4 * wave);
 
   int64_t item = blockIdx.x;
   while (item < n_items) {
@@ -157,8 +166,9 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
     if (nbw >= G.NB) nbw = G.NB - 1;
     const rsrc_t rw = make_rsrc(a.w + (wb + nbw) * G.KG * 1024, (uint64_t)G.KG * 1024);
     const uint32_t wvo = (uint32_t)lane * 16u;
-    const uint32_t svo = zlane ? (uint32_t)((G.off_zeros - G.off_scales) + (wb + nbw) * G.KG * 8 + (lane - 8) * 4)
-                               : (uint32_t)((wb + nbw) * G.KG * 32 + (lane & 7) * 4);
+    const uint32_t svo = F4 ? (uint32_t)((wb + nbw) * G.KG4 * 256 + lane * 4)
+                         : zlane ? (uint32_t)((G.off_zeros - G.off_scales) + (wb + nbw) * G.KG * 8 + (lane - 8) * 4)
+                                 : (uint32_t)((wb + nbw) * G.KG * 32 + (lane & 7) * 4);
     if (GROUPED && tid < kMidM) {
       const int32_t p = tid < t.rows ? a.sorted_pairs[t.first + tid] : -1;
       orow_s[tid] = (p >= 0 && p < a.P) ? p : -1;
@@ -179,7 +189,9 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
       b2lds16(rw, wvo, (uint32_t)(g * 1024), lds + so + wave * 1024);
     };
     auto copy_sz = [&](int g, uint32_t so) {
-      b2lds4(rsz, svo + (uint32_t)g * szstride, 0u, lds + so + kMidCB * 1024 + wave * 256);
+      // MXFP4: the scale words of groups 4 (g / 4) .. + 3, 256 bytes
+      b2lds4(rsz, F4 ? svo + (uint32_t)(g >> 2) * 256u : svo + (uint32_t)g * szstride, 0u,
+             lds + so + kMidCB * 1024 + wave * 256);
     };
 
     // ---- prologue: weights of groups 0 .. DW - 1 and activations of 0 .. DX
@@ -208,14 +220,21 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
     if (KG >= 5) __asm__ volatile("s_waitcnt vmcnt(14)\n\ts_barrier" ::: "memory");
     else __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // code word, scale and s * (-z) of column half nb2, K part kk' of the group in slot so
-    auto fetch = [&](uint32_t so, uint32_t (&wq)[2][2], float (&sv)[2], float (&zs)[2]) {
+    // code word, scale and s * (-z) of column half nb2, K part kk' of group g in slot so
+    auto fetch = [&](uint32_t so, int g, uint32_t (&wq)[2][2], float (&sv)[2], float (&zs)[2]) {
       const uint8_t* slot = lds + so;
 #pragma unroll
       for (int nb2 = 0; nb2 < 2; ++nb2) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) wq[nb2][k2] = *reinterpret_cast<const uint32_t*>(slot + wo[nb2][k2]);
         const uint8_t* sz = slot + kMidCB * 1024 + (2 * nb2 + c_l) * 256;
+        if (F4) {
+          // E8M0 of (column c16, K block w): byte g % 4 of scale word c16 + 16 w
+          const uint32_t sw = *reinterpret_cast<const uint32_t*>(sz + 4 * (c16 + 16 * wave));
+          sv[nb2] = e8m0_f32((sw >> (8 * (g & 3))) & 0xFFu);
+          zs[nb2] = 0.f;
+          continue;
+        }
         sv[nb2] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sz + 2 * c16));
         const uint32_t zw = ZP ? *reinterpret_cast<const uint32_t*>(sz + 32 + 4 * (c16 >> 3)) : 0u;
         const float z = ZP ? (float)((zw >> (4 * (c16 & 7))) & 0xFu) : 8.0f;
@@ -228,10 +247,10 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
     float csv[2], czs[2];
     {
       uint32_t wq[2][2];
-      fetch(wso[0], wq, csv, czs);
+      fetch(wso[0], 0, wq, csv, czs);
 #pragma unroll
       for (int nb2 = 0; nb2 < 2; ++nb2) {
-        af[nb2][0] = dq8_bytes(wq[nb2][0], csv[nb2], czs[nb2]);
+        af[nb2][0] = F4 ? fp4x8_bf16(wq[nb2][0], csv[nb2]) : dq8_bytes(wq[nb2][0], csv[nb2], czs[nb2]);
         af[nb2][1] = (u32x4_t){0u, 0u, 0u, 0u};
         c1[nb2] = wq[nb2][1];
       }
@@ -261,7 +280,7 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
     for (int g = 0; g < KG; ++g) {
       uint32_t nq[2][2];
       float nsv[2], nzs[2];
-      fetch(wso[1], nq, nsv, nzs);
+      fetch(wso[1], g + 1, nq, nsv, nzs);
       // past the end: repeats of the last group into slots no longer read
       const int xg = std::min(g + kMidDX, KG - 1), wg = std::min(g + kMidDW, KG - 1);
       const uint32_t xd = xso[kMidDX], wd = wso[kMidDW];
@@ -284,6 +303,10 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
           const int nb2 = wi >> 2, u = wi & 3;
           const uint32_t w = k2 == 0 ? c1[nb2] : nq[nb2][0];
           const float sv = k2 == 0 ? csv[nb2] : nsv[nb2], zs = k2 == 0 ? czs[nb2] : nzs[nb2];
+          if (F4) {
+            af[nb2][k2 ^ 1][u] = fp4x2_bf16(w, sv, u);
+            continue;
+          }
           if (u == 0) {
             lo = in_vgpr(w & 0x0F0F0F0Fu);
             hi4 = in_vgpr((w >> 4) & 0x0F0F0F0Fu);
@@ -589,9 +612,9 @@ static hipError_t go_mid_mx(const GemmArgs& a, int grid_items, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool ZP, bool GROUPED>
+template <bool ZP, bool GROUPED, bool F4 = false>
 static hipError_t go_mid(const GemmArgs& a, int grid_items, hipStream_t st) {
-  auto kern = &k_gemm_mid<ZP, GROUPED>;
+  auto kern = &k_gemm_mid<ZP, GROUPED, F4>;
   static const hipError_t attr_err = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kMidLds);
   if (attr_err != hipSuccess) return attr_err;
@@ -609,15 +632,15 @@ int64_t mid_n_tiles(const Geom& G, bool mx) {
 }
 
 hipError_t launch_gemm_mid(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
-  // MXFP4 weights with bf16 rows run on the streaming and 128 x 128 kernels only
-  if (kmode_of(a) == KM_MX_A16) return hipErrorInvalidValue;
   // scale and zero-point copies use 32-bit offsets from the scale region
   if (a.G.total - a.G.off_scales > 0xFFFFFFFFull) return hipErrorInvalidValue;
   // grouped activation rows are addressed by 32-bit offsets from x
   if (grouped) {
     const int64_t xrows = a.rows_are_pairs ? a.P : (a.P + a.topk - 1) / a.topk;
-    if (xrows * (a.wfmt == W_MXFP4 ? 1 : 2) * a.G.K > 0xFFFFFFFFll) return hipErrorInvalidValue;
+    if (xrows * (a.a8 ? 1 : 2) * a.G.K > 0xFFFFFFFFll) return hipErrorInvalidValue;
   }
+  if (kmode_of(a) == KM_MX_A16)
+    return grouped ? go_mid<false, true, true>(a, grid_items, st) : go_mid<false, false, true>(a, 0, st);
   if (a.wfmt == W_MXFP4) return grouped ? go_mid_mx<true>(a, grid_items, st) : go_mid_mx<false>(a, 0, st);
   if (a.wfmt == W_UINT4_ZP)
     return grouped ? go_mid<true, true>(a, grid_items, st) : go_mid<true, false>(a, 0, st);

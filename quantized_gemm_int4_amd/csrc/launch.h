@@ -75,7 +75,7 @@ constexpr int kTileN = 128;
 hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
 
 // Mid-M MFMA kernels: W4A16 128 x 64 output tiles (K groups split over the
-// four waves), W4A8-MXFP4 64 x 128 tiles.  Dense: one block per tile.
+// four waves; INT4, and MXFP4 with bf16 rows), W4A8-MXFP4 64 x 128 tiles.  Dense: one block per tile.
 // Grouped: persistent over items of hdr[1] units of up to 128 rows; items
 // per unit from mid_n_tiles (MXFP4: two 64-row halves per column tile).
 hipError_t launch_gemm_mid(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);

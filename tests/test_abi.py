@@ -99,15 +99,27 @@ def test_plan_strings():
 
 def test_mxfp4_bf16_rows_plans():
     """MXFP4 weights take bf16 rows too: the streaming kernel for few rows,
-    the 128 x 128 kernel above (bf16 MFMA); FP8 rows keep the W4A8 kernels;
-    INT4 weights reject FP8 rows."""
+    the 128 x 64 kernel above (128 x 128 when forced; bf16 MFMA); FP8 rows
+    keep the W4A8 kernels; INT4 weights reject FP8 rows."""
+    import os
     mx = hm.wdesc("mxfp4", 7168, 2048)
     for m in (1, 16, 32):
         p = hm.hm_gemm_plan(mx, hm.HM_A_BF16, m)
         assert p.startswith("w4a16-mxfp4 stream") and p.endswith("mfma=16x16x32_bf16"), p
-    for m in (33, 256, 4096):
+    for m in (33, 256, 1024):
         p = hm.hm_gemm_plan(mx, hm.HM_A_BF16, m)
+        assert p.startswith("w4a16-mxfp4 tile 128x64") and p.endswith("32x32x16_bf16"), p
+    # 14 rounds of 128 x 64 tiles against 7 of 128 x 128
+    p = hm.hm_gemm_plan(mx, hm.HM_A_BF16, 4096)
+    assert p.startswith("w4a16-mxfp4 tile 128x128") and p.endswith("16x16x32_bf16"), p
+    os.environ["HM_FORCE_PATH"] = "4"
+    try:
+        p = hm.hm_gemm_plan(mx, hm.HM_A_BF16, 256)
         assert p.startswith("w4a16-mxfp4 tile 128x128") and p.endswith("16x16x32_bf16"), p
+        os.environ["HM_FORCE_PATH"] = "3"      # no 256 x 256 kernel for this pair
+        assert "128x64" in hm.hm_gemm_plan(mx, hm.HM_A_BF16, 4096)
+    finally:
+        os.environ.pop("HM_FORCE_PATH", None)
     assert hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, 4096).startswith("w4a8-mxfp4 tile 256x256")
     assert hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, 1).startswith("w4a8-mxfp4 stream")
     sz = ctypes.c_size_t()

@@ -34,12 +34,13 @@ def _bf16_one_rows(k, cols):
     return x
 
 
-@pytest.mark.parametrize("m,force", [(32, None), (7, None), (256, None), (200, 1)])
+@pytest.mark.parametrize("m,force", [(32, None), (7, None), (256, None), (256, 4), (200, 1)])
 def test_dequant_through_unit_rows(m, force):
     """y[i, n] = w_hat[n, c_i] exactly: all 16 E2M1 codes under scale bytes
     from 0 (products down to 2^-128, subnormal in fp32 and bf16) to 252
     (largest 6 * 2^125, the last byte whose products stay below 2^128), on the
-    streaming (m <= 32, or forced) and 128 x 128 kernels."""
+    streaming (m <= 32, or forced), 128 x 64 (default above 32 rows) and
+    128 x 128 (forced) kernels."""
     import quantized_gemm_int4_amd as hm
     n, k = 40, 256
     r = np.random.default_rng(11)
@@ -89,7 +90,7 @@ def test_ragged_default_path(n, k, m):
     MxLayer(n, k, cfg=7, wseed=n + k).check(synthetic.activations(7, m, k, index=m, outliers=0.01))
 
 
-@pytest.mark.parametrize("m,force", [(64, 1), (256, 1), (1, 4), (17, 4)])
+@pytest.mark.parametrize("m,force", [(64, 1), (256, 1), (1, 4), (17, 4), (100, 4), (300, 4), (300, 3)])
 def test_forced_paths(m, force):
     os.environ["HM_FORCE_PATH"] = str(force)
     MxLayer(264, 640, cfg=7, wseed=5).check(synthetic.activations(7, m, 640, index=m, outliers=0.01))
@@ -120,9 +121,20 @@ def _skewed_ids(t, topk, E, seed):
 
 
 @pytest.mark.parametrize("rows_are_pairs", [0, 1])
-def test_moe_mixed_units(rows_are_pairs):
-    """Streaming units (small experts) and 128-row tile units in one grouped call."""
+@pytest.mark.parametrize("mid", [1, 0])
+def test_moe_mixed_units(rows_are_pairs, mid):
+    """Streaming units (small experts) and 128-row tile units in one grouped
+    call; the tile units on the 128 x 64 kernel (mid=1, the default) or the
+    128 x 128 one."""
     import quantized_gemm_int4_amd as hm
+    os.environ["HM_MOE_MID"] = str(mid)
+    try:
+        _moe_mixed(hm, rows_are_pairs)
+    finally:
+        os.environ.pop("HM_MOE_MID", None)
+
+
+def _moe_mixed(hm, rows_are_pairs):
     t, topk, E, n, k = 150, 2, 8, 208, 384
     ids = _skewed_ids(t, topk, E, 1)
     counts = np.bincount(ids.ravel(), minlength=E)
