@@ -19,13 +19,13 @@ Region A, codes: E*NB*KG tiles of 1024 bytes, tile index (e*NB + nb)*KG + g.
     position i/2 for even i and 4 + (i-1)/2 for odd i (so nibbles p and p+4
     are the consecutive pair 2p, 2p+1).
     Stored value: uint4_zp -> u; int4_sym -> q + 8 (offset binary).
-  * mxfp4: byte b (0..15) of slot L holds k = 128*g + 32*h + 2*b (low nibble)
-    and k+1 (high nibble), E2M1 bits as given.
+  * mxfp4, mxint4: byte b (0..15) of slot L holds k = 128*g + 32*h + 2*b (low
+    nibble) and k+1 (high nibble), the E2M1 / two's complement bits as given.
   Columns n >= N hold the value-zero code (int4_sym 8, others 0).
 Region B, scales (starts at the next 256-byte boundary):
   * int4 formats: bf16 entry ((e*NB + nb)*KG + g)*16 + c = scale of column
     16*nb + c, group g.
-  * mxfp4: KG4 = ceil(KG/4); byte (((e*NB + nb)*KG4 + g//4)*64 + L)*4 + g%4 =
+  * mxfp4, mxint4: KG4 = ceil(KG/4); byte (((e*NB + nb)*KG4 + g//4)*64 + L)*4 + g%4 =
     E8M0 of column 16*nb + L%16 and 32-block 4*g + L//16.
   Padding entries are 0.
 Region C, zero points (uint4_zp only, next 256-byte boundary): 8 bytes per
@@ -36,7 +36,7 @@ named above (the alignment gaps between regions) is zero.
 """
 import numpy as np
 
-from .quant import FMT_INT4_SYM, FMT_UINT4_ZP, FMT_MXFP4, unpack_nibbles
+from .quant import FMT_INT4_SYM, FMT_UINT4_ZP, FMT_MXFP4, MX_FORMATS, unpack_nibbles
 
 
 def _align(x, a=256):
@@ -48,7 +48,7 @@ def sizes(fmt, E, N, K):
     NB = (N + 15) // 16
     KG = K // 128
     a = E * NB * KG * 1024
-    if fmt == FMT_MXFP4:
+    if fmt in MX_FORMATS:
         b = E * NB * ((KG + 3) // 4) * 256
     else:
         b = E * NB * KG * 16 * 2
@@ -88,7 +88,7 @@ def transform_ref(fmt, codes, scales, zeros=None):
     L = np.arange(64)
     c = L % 16
     h = L // 16
-    if fmt == FMT_MXFP4:
+    if fmt in MX_FORMATS:
         for b in range(16):
             k_lo = 32 * h + 2 * b                          # [64]
             for g in range(KG):
@@ -110,7 +110,7 @@ def transform_ref(fmt, codes, scales, zeros=None):
     out[:tiles.size] = tiles.ravel()
 
     # Region B
-    if fmt == FMT_MXFP4:
+    if fmt in MX_FORMATS:
         KG4 = (KG + 3) // 4
         sb = np.zeros((E, NB, KG4, 64, 4), dtype=np.uint8)
         sc = np.asarray(scales, dtype=np.uint8)            # [E, N, K/32]

@@ -40,7 +40,10 @@ GROUP_MX = 32
 FMT_INT4_SYM = "int4_sym"
 FMT_UINT4_ZP = "uint4_zp"
 FMT_MXFP4 = "mxfp4"
+FMT_MXINT4 = "mxint4"
 FORMATS = (FMT_INT4_SYM, FMT_UINT4_ZP, FMT_MXFP4)
+# formats with one E8M0 scale per 32 values (the MX family)
+MX_FORMATS = (FMT_MXFP4, FMT_MXINT4)
 
 
 def _groups(w, g):
@@ -130,6 +133,31 @@ def quant_mxfp4(w):
     return codes.reshape(n, k), (x + 127).astype(np.uint8)
 
 
+# ----------------------------------------------------------------------------- MXINT4
+
+def quant_mxint4(w):
+    """MXINT4 (named in the pages' format lists, cocoloop.cn item and aihaber.org
+    article, hardware and format support, without a definition).  Reading
+    taken: the MX scheme with 4-bit two's complement elements read as 1.2
+    fixed point, value q/4 with q in -8..7 (range [-2, 1.75], the INT4
+    analogue of the MX INT8 element), one E8M0 scale per 32 values along K.
+    The shared exponent is X = floor(log2 amax) (the largest element
+    magnitude is below 2, so its power-of-two exponent is 0), and
+    q = clamp(round-half-even(4 w / 2^X), -8, 7), so w_hat = 2^X q / 4.
+    An all-zero block takes X = -127 and zero codes.
+    Returns (codes uint8 [N,K] in 0..15 = q & 0xF, e8m0 bytes uint8 [N,K/32])."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    wg = _groups(w, GROUP_MX).astype(np.float64)
+    amax = np.abs(wg).max(axis=2)
+    _, e = np.frexp(amax)                       # amax = m * 2^e, m in [0.5, 1)
+    x = np.clip(np.where(amax > 0, e - 1, -127), -127, 127).astype(np.int64)
+    scaled = wg / np.ldexp(1.0, x - 2)[:, :, None]      # exact: power of two
+    q = np.clip(np.rint(scaled), -8, 7)
+    q = np.where((amax > 0)[:, :, None], q, 0).astype(np.int64)
+    return (q & 0xF).reshape(n, k).astype(np.uint8), (x + 127).astype(np.uint8)
+
+
 # ----------------------------------------------------------------------------- packing
 
 def pack_nibbles(codes):
@@ -165,8 +193,9 @@ def dequant(fmt, packed, scales, zeros=None):
     int4_sym:  s * q           (q two's complement nibble, s bf16)
     uint4_zp:  s * (u - z)     (z one byte per group, low nibble used)
     mxfp4:     E2M1(code) * 2^(b-127)
+    mxint4:    (q / 4) * 2^(b-127)   (q two's complement nibble)
     Every product is exact in fp32 (at most 12 significant bits, and the MX
-    products stay at or above 2^-128)."""
+    products stay at or above 2^-129) while it stays below 2^128."""
     u = unpack_nibbles(packed)
     n, k = u.shape
     if fmt == FMT_INT4_SYM:
@@ -180,6 +209,9 @@ def dequant(fmt, packed, scales, zeros=None):
         out = d * s[:, :, None]
     elif fmt == FMT_MXFP4:
         v = codecs.e2m1_value(u).reshape(n, k // GROUP_MX, GROUP_MX)
+        out = v * codecs.e8m0_value(scales)[:, :, None]
+    elif fmt == FMT_MXINT4:
+        v = nibble_to_int4(u).astype(np.float64).reshape(n, k // GROUP_MX, GROUP_MX) / 4.0
         out = v * codecs.e8m0_value(scales)[:, :, None]
     else:
         raise ValueError(fmt)
@@ -197,6 +229,9 @@ def quantize(fmt, w):
         return dict(codes=pack_nibbles(u), scales=s, zeros=z)
     if fmt == FMT_MXFP4:
         c, e = quant_mxfp4(w)
+        return dict(codes=pack_nibbles(c), scales=e, zeros=None)
+    if fmt == FMT_MXINT4:
+        c, e = quant_mxint4(w)
         return dict(codes=pack_nibbles(c), scales=e, zeros=None)
     raise ValueError(fmt)
 
@@ -232,7 +267,7 @@ def fp8_rows_dequant(codes, scales):
 def storage_bytes(n, k, fmt, group=None, scale_bits=16, zero_bits=4):
     """Bytes of the standard format excluding padding and alignment:
     n*k 4-bit codes + one scale per group (+ one zero point per group)."""
-    if fmt == FMT_MXFP4:
+    if fmt in MX_FORMATS:
         group = group or GROUP_MX
         scale_bits = 8
         zero_bits = 0
@@ -246,5 +281,5 @@ def storage_bytes(n, k, fmt, group=None, scale_bits=16, zero_bits=4):
 
 
 def bits_per_value(fmt, group=None, **kw):
-    g = group or (GROUP_MX if fmt == FMT_MXFP4 else GROUP_INT4)
+    g = group or (GROUP_MX if fmt in MX_FORMATS else GROUP_INT4)
     return storage_bytes(1, g, fmt, group=g, **kw) * 8.0 / g

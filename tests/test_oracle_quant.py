@@ -217,3 +217,70 @@ def test_bench_weight_bytes_match_storage():
     for n, k, name, fmt in [(14336, 4096, "uint4_zp", quant.FMT_UINT4_ZP), (7168, 2048, "mxfp4", quant.FMT_MXFP4),
                             (4096, 7168, "int4_sym", quant.FMT_INT4_SYM), (1792, 4096, "uint4_zp", quant.FMT_UINT4_ZP)]:
         assert b.weight_bytes(n, k, name) == quant.storage_bytes(n, k, fmt)
+
+
+# ------------------------------------------------------------------ MXINT4 (reading: 1.2 fixed-point INT4
+# elements under an E8M0 scale per 32, the MX rule X = floor(log2 amax))
+
+MXI4_VALUES = [0.0, 0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, -2.0, -1.75, -1.5, -1.25, -1.0, -0.75, -0.5, -0.25]
+
+
+def test_mxint4_dequant_all_codes():
+    """Nibble c is the two's complement q, value q/4 times 2^(b-127), written out."""
+    for b in (0, 1, 100, 127, 130, 253):
+        codes = quant.pack_nibbles(np.arange(32).reshape(1, 32) % 16)
+        got = quant.dequant(quant.FMT_MXINT4, codes, np.array([[b]], dtype=np.uint8))
+        want = np.array([MXI4_VALUES[c % 16] * 2.0 ** (b - 127) for c in range(32)], dtype=np.float32)
+        assert np.array_equal(got[0], want), b
+
+
+def test_mxint4_exact_round_trip():
+    """A block made of 2^X q / 4 with max |q| = 7 comes back exactly, scale byte X + 127."""
+    r = np.random.default_rng(3)
+    for x in (-20, -7, 0, 5):
+        q = r.integers(-7, 8, 32)
+        q[5] = 7 if r.integers(2) else -7
+        w = (q * 2.0 ** (x - 2)).astype(np.float32).reshape(1, 32)
+        c, e = quant.quant_mxint4(w)
+        assert int(e[0, 0]) == x + 127
+        assert np.array_equal(c[0], (q & 0xF).astype(np.uint8))
+
+
+def test_mxint4_brute_force():
+    """Pure-Python check on small random blocks: scale byte from the binary
+    exponent of amax, each code the nearest of the 16 (ties to even q), the
+    top end saturating at 7 and zero blocks all zero."""
+    import math
+    r = np.random.default_rng(4)
+    w = (r.standard_normal((6, 96)) * np.array([1e-3, 0.02, 1.0, 3.0, 1e5, 2.0 ** -120])[:, None]).astype(np.float32)
+    w[2, 32:64] = 0.0                                   # a zero block
+    w[3, 64] = 1.95 * 2.0 ** 3                          # saturating block: 4 w / 2^X rounds to 8 -> 7
+    w[3, 65:96] = np.clip(w[3, 65:96], -15.0, 15.0)
+    c, e = quant.quant_mxint4(w)
+    for n in range(w.shape[0]):
+        for blk in range(3):
+            vals = [float(v) for v in w[n, 32 * blk:32 * blk + 32]]
+            amax = max(abs(v) for v in vals)
+            if amax == 0.0:
+                assert e[n, blk] == 0 and all(c[n, 32 * blk + i] == 0 for i in range(32))
+                continue
+            x = math.frexp(amax)[1] - 1
+            assert e[n, blk] == x + 127
+            for i, v in enumerate(vals):
+                t = 4.0 * v / 2.0 ** x
+                best = min(range(-8, 8), key=lambda q: (abs(t - q), q % 2))
+                assert c[n, 32 * blk + i] == (best & 0xF), (n, blk, i, v, best)
+    assert c[3, 64] == 7
+
+
+def test_mxint4_storage_and_layout_match_mxfp4():
+    """Same standard-format sizes and the same device arrangement as MXFP4."""
+    from oracle import layout
+    assert quant.storage_bytes(7168, 2048, quant.FMT_MXINT4) == quant.storage_bytes(7168, 2048, quant.FMT_MXFP4)
+    assert layout.sizes(quant.FMT_MXINT4, 2, 40, 384) == layout.sizes(quant.FMT_MXFP4, 2, 40, 384)
+    r = np.random.default_rng(5)
+    codes = r.integers(0, 256, (2, 40, 192), dtype=np.uint8)
+    scales = r.integers(0, 255, (2, 40, 12), dtype=np.uint8)
+    a = layout.transform_ref(quant.FMT_MXINT4, codes, scales)
+    b = layout.transform_ref(quant.FMT_MXFP4, codes, scales)
+    assert np.array_equal(a, b)
