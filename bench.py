@@ -8,7 +8,7 @@ flops of the step / step time (TFLOP/s).  Weights rotate through enough
 distinct copies (>= 2 x 256 MB) that the 256 MB last-level cache cannot serve
 them; activations are resident in HBM before the timed region starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_w4a16|dense_w4a8|moe_w4a16|moe_w4a8|moe_w4a16_mxfp4|shards]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_w4a16|dense_w4a8|moe_w4a16|moe_w4a8|moe_w4a16_mxfp4|moe_w4a16_mxint4|shards]
 
 One JSON line is printed (rank 0).  Extra workloads exist for measurement; the
 default line is the dense W4A16 sweep.
@@ -38,7 +38,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="dense_w4a16",
-                   choices=["dense_w4a16", "dense_w4a8", "moe_w4a16", "moe_w4a8", "moe_w4a16_mxfp4", "shards"])
+                   choices=["dense_w4a16", "dense_w4a8", "moe_w4a16", "moe_w4a8", "moe_w4a16_mxfp4",
+                            "moe_w4a16_mxint4", "shards"])
     p.add_argument("--reps", type=int, default=30, help="launches per M for per-kernel timing")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle (cpu_baseline) leg")
     p.add_argument("--counters-run", action="store_true",
@@ -53,9 +54,9 @@ def parse():
 def weight_bytes(n, k, fmt):
     """Algorithmic bytes of one layer's weights in the standard format: 4-bit
     codes plus one scale per group (bf16 per 128 for the INT4 formats, one
-    E8M0 byte per 32 for MXFP4) and, for uint4, one 4-bit zero point per
+    E8M0 byte per 32 for MXFP4 and MXINT4) and, for uint4, one 4-bit zero point per
     group (the pages' 66 bytes per 128 weights, 66.5 with the zero point)."""
-    if fmt == "mxfp4":
+    if fmt in ("mxfp4", "mxint4"):
         return n * k / 2 + n * (k // 32)
     extra = 0.5 if fmt == "uint4_zp" else 0.0
     return n * k / 2 + n * (k // 128) * (2 + extra)
@@ -390,7 +391,7 @@ def run_moe(args, fmt, a8):
 
     def weights(n, k):
         codes = torch.randint(0, 256, (E, n, k // 2), dtype=torch.uint8, device=dev, generator=g)
-        if fmt == "mxfp4":
+        if fmt in ("mxfp4", "mxint4"):
             sc = torch.randint(118, 122, (E, n, k // 32), dtype=torch.uint8, device=dev, generator=g)
         else:
             sc = (0x3B00 + torch.randint(0, 0x100, (E, n, k // 128), device=dev, generator=g)).to(torch.int16)
@@ -497,8 +498,9 @@ def run_moe(args, fmt, a8):
                                        hbm_frac=round(comb_b / comb_ms / 1e6 / HBM_PEAK_GBS, 4))))
         step_ms += ms_t
         step_fl += fl
-    name = "W4A8-MXFP4" if a8 else ("W4A16-MXFP4 (E2M1 + E8M0/32, bf16 rows)" if fmt == "mxfp4"
-                                     else "W4A16 int4-sym G128")
+    name = "W4A8-MXFP4" if a8 else {"mxfp4": "W4A16-MXFP4 (E2M1 + E8M0/32, bf16 rows)",
+                                     "mxint4": "W4A16-MXINT4 (1.2 fixed-point INT4 + E8M0/32, bf16 rows)"}.get(
+                                         fmt, "W4A16 int4-sym G128")
     wl = (f"MoE {name} 256 experts top-8 "
           f"Zipf(1.1) router, gate_up N=4096 K=7168 + down N=7168 K=2048, T={ts}, sort included; "
           f"block_ms adds the SiLU product, the down GEMM on its output and the weighted combine")
@@ -506,7 +508,7 @@ def run_moe(args, fmt, a8):
                 n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=round(step_ms, 4),
                 higher_is_better=True, scaling="weak", vs_baseline=None,
                 dtype="fp8" if a8 else "bf16", data="synthetic",
-                config=dict(workload=wl), per_T=per_t, roofline=moe_roofline(per_t, a8, fmt == "mxfp4" and not a8),
+                config=dict(workload=wl), per_T=per_t, roofline=moe_roofline(per_t, a8, fmt in ("mxfp4", "mxint4") and not a8),
                 cpu_baseline=None)
 
 
@@ -516,8 +518,8 @@ def moe_roofline(per_t, a8, f4=False):
     GEMMs), its bound the binding one at that token count."""
     r = max(per_t, key=lambda e: e["ms"])
     peak = FP8_PEAK_TFLOPS if a8 else BF16_PEAK_TFLOPS
-    # MXFP4 weights with bf16 rows run grouped streaming and 128 x 128 units only
-    kern = ("hm_moe_gemm (grouped k_gemm_tile + k_gemm_stream)" if f4 else
+    # MX weights with bf16 rows run grouped streaming and 128-row units only
+    kern = ("hm_moe_gemm (grouped k_gemm_tile/mid + k_gemm_stream)" if f4 else
             "hm_moe_gemm (grouped k_gemm_big + k_gemm_mid/tile + k_gemm_stream)")
     if r["bound"] == "mfma":
         a = r["flops"] / (r["ms"] * 1e-3) / 1e12
@@ -637,8 +639,8 @@ def main():
     elif args.workload.startswith("dense"):
         out = run_dense(args, "mxfp4" if args.workload == "dense_w4a8" else "uint4_zp")
     else:
-        out = run_moe(args, "int4_sym" if args.workload == "moe_w4a16" else "mxfp4",
-                      args.workload == "moe_w4a8")
+        fmt = {"moe_w4a16": "int4_sym", "moe_w4a16_mxint4": "mxint4"}.get(args.workload, "mxfp4")
+        out = run_moe(args, fmt, args.workload == "moe_w4a8")
     print(json.dumps(out), flush=True)
 
 

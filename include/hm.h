@@ -71,7 +71,11 @@ typedef enum hm_status {
 typedef enum hm_wfmt {
   HM_W_INT4_SYM = 0, /* signed 4-bit two's complement q, bf16 scale per 128 along K: w = s*q */
   HM_W_UINT4_ZP = 1, /* unsigned 4-bit u, bf16 scale + 4-bit zero point per 128: w = s*(u-z) */
-  HM_W_MXFP4 = 2     /* E2M1 codes, E8M0 scale per 32 along K: w = e2m1(c) * 2^(b-127) */
+  HM_W_MXFP4 = 2,    /* E2M1 codes, E8M0 scale per 32 along K: w = e2m1(c) * 2^(b-127) */
+  HM_W_MXINT4 = 3    /* two's complement 4-bit q read as 1.2 fixed point, E8M0 scale per 32
+                        along K: w = (q/4) * 2^(b-127); the format is named in the pages' lists
+                        (cocoloop.cn item; aihaber.org article, hardware and format support)
+                        without a definition, this is the MX-family reading */
 } hm_wfmt;
 
 /* Activation format (the compute option choosing A16 or A8). */
@@ -81,12 +85,13 @@ typedef enum hm_afmt {
 } hm_afmt;
 
 /* Supported pairs: every weight format with HM_A_BF16 (W4A16: INT4_SYM,
- *                  UINT4_ZP, and MXFP4, whose E2M1 codes are scaled to bf16
- *                  in the kernel; the pages list MXFP4 W4A16 among the MoE
- *                  results, aihaber.org article, performance section);
+ *                  UINT4_ZP, and MXFP4 / MXINT4, whose codes are scaled to
+ *                  bf16 in the kernel; the pages list MXFP4 W4A16 among the
+ *                  MoE results, aihaber.org article, performance section);
  *                  MXFP4 with HM_A_FP8_ROWSCALE (W4A8-MXFP4).
  * MXFP4 with bf16 rows requires every |w| < 2^128 (E8M0 scale bytes up to
- * 252 always satisfy it; larger products become inf, and the row's sums NaN):
+ * 252 always satisfy it, up to 253 for MXINT4; larger products become inf,
+ * and the row's sums NaN):
  * the dequantized weights enter the bf16 MFMA.  Subnormal products (scale
  * bytes 0..3) are kept exactly. */
 

@@ -17,9 +17,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhm.so")
 
 HM_ABI_VERSION = 1
-HM_W_INT4_SYM, HM_W_UINT4_ZP, HM_W_MXFP4 = 0, 1, 2
+HM_W_INT4_SYM, HM_W_UINT4_ZP, HM_W_MXFP4, HM_W_MXINT4 = 0, 1, 2, 3
 HM_A_BF16, HM_A_FP8_ROWSCALE = 0, 1
-WFMT = {"int4_sym": HM_W_INT4_SYM, "uint4_zp": HM_W_UINT4_ZP, "mxfp4": HM_W_MXFP4}
+WFMT = {"int4_sym": HM_W_INT4_SYM, "uint4_zp": HM_W_UINT4_ZP, "mxfp4": HM_W_MXFP4, "mxint4": HM_W_MXINT4}
 STATUS = {0: "HM_OK", 1: "HM_ERR_NULL", 2: "HM_ERR_SHAPE", 3: "HM_ERR_ALIGN",
           4: "HM_ERR_UNSUPPORTED", 5: "HM_ERR_WORKSPACE", 6: "HM_ERR_HIP", 7: "HM_ERR_ABI"}
 
@@ -38,7 +38,7 @@ class hm_wdesc(ctypes.Structure):
 def wdesc(wfmt, n, k, num_experts=1):
     """Layer description; wfmt is an HM_W_* value or 'int4_sym' / 'uint4_zp' / 'mxfp4'."""
     f = WFMT.get(wfmt, wfmt)
-    return hm_wdesc(HM_ABI_VERSION, int(f), 32 if f == HM_W_MXFP4 else 128, int(num_experts),
+    return hm_wdesc(HM_ABI_VERSION, int(f), 32 if f in (HM_W_MXFP4, HM_W_MXINT4) else 128, int(num_experts),
                     int(n), int(k))
 
 

@@ -9,12 +9,12 @@
 //            sits in nibbles p and p+4, one per 16-bit half; the u32 j of a slot
 //            is the 8 K-values one lane feeds to the j-th 16x16x32 bf16 MFMA of
 //            the step.  INT4_SYM is stored offset-binary (q+8).
-//     mxfp4: byte b of slot L holds k = 128g + 32h + 2b (low), k+1 (high); the
-//            16 bytes are the 32 E2M1 values one lane feeds to a 16x16x128
-//            scaled MFMA.
+//     mxfp4, mxint4: byte b of slot L holds k = 128g + 32h + 2b (low), k+1
+//            (high); the 16 bytes are the 32 E2M1 (or two's complement)
+//            values one lane feeds to a 16x16x128 scaled MFMA (MXFP4).
 //     Columns >= N hold the value-zero code.
 //   Region B (scales, 256-aligned): int4: bf16 [E][NB][KG][16];
-//     mxfp4: bytes [E][NB][ceil(KG/4)][64 lanes][4], byte g%4 of lane L's u32
+//     mxfp4, mxint4: bytes [E][NB][ceil(KG/4)][64 lanes][4], byte g%4 of lane L's u32
 //     = E8M0 of (column 16nb + L%16, 32-block 4g + L/16).
 //   Region C (zero points, UINT4_ZP only, 256-aligned): [E][NB][KG] u64,
 //     nibble c = zero point of column 16nb + c.
@@ -26,7 +26,10 @@
 
 namespace hm {
 
-enum WFmt : int { W_INT4_SYM = 0, W_UINT4_ZP = 1, W_MXFP4 = 2 };
+enum WFmt : int { W_INT4_SYM = 0, W_UINT4_ZP = 1, W_MXFP4 = 2, W_MXINT4 = 3 };
+
+// formats with E8M0 scales per 32 values and the MX slot layout
+__host__ __device__ inline bool is_mx(int wfmt) { return wfmt == W_MXFP4 || wfmt == W_MXINT4; }
 
 struct Geom {
   int64_t E, N, K, NB, KG, KG4;
@@ -42,7 +45,7 @@ __host__ __device__ inline Geom make_geom(int wfmt, int64_t E, int64_t N, int64_
   g.KG = K / 128;
   g.KG4 = (g.KG + 3) / 4;
   size_t a = (size_t)E * g.NB * g.KG * 1024;
-  size_t b = (wfmt == W_MXFP4) ? (size_t)E * g.NB * g.KG4 * 256 : (size_t)E * g.NB * g.KG * 32;
+  size_t b = is_mx(wfmt) ? (size_t)E * g.NB * g.KG4 * 256 : (size_t)E * g.NB * g.KG * 32;
   size_t c = (wfmt == W_UINT4_ZP) ? (size_t)E * g.NB * g.KG * 8 : 0;
   g.off_scales = align256(a);
   g.off_zeros = align256(g.off_scales + b);
@@ -202,6 +205,19 @@ __device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t w, float s, int sel) {
     case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
     default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
   }
+}
+
+// MXINT4: eight two's complement codes of one word (value 2b in the low
+// nibble of byte b, 2b + 1 in its high nibble) times s -> eight bf16 in value
+// order; s carries the element's fixed-point factor 1/4.  Exact: q * s has at
+// most 4 significant bits.
+__device__ __forceinline__ uint32_t i4x2_bf16(uint32_t w, float s, int sel) {
+  const int lo = (int)(w << (28 - 8 * sel)) >> 28;       // sign-extended nibble 2 sel
+  const int hi = (int)(w << (24 - 8 * sel)) >> 28;       // and 2 sel + 1
+  return pack_bf16((float)lo * s, (float)hi * s);
+}
+__device__ __forceinline__ u32x4_t i4x8_bf16(uint32_t w, float s) {
+  return (u32x4_t){i4x2_bf16(w, s, 0), i4x2_bf16(w, s, 1), i4x2_bf16(w, s, 2), i4x2_bf16(w, s, 3)};
 }
 
 // 32x32x16 bf16 MFMA: lane L supplies A row L%32 and B column L%32 for K

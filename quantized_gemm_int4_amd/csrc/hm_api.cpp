@@ -46,9 +46,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 hm_status check_desc(const hm_wdesc* d) {
   if (!d) return HM_ERR_NULL;
   if (d->abi != HM_ABI_VERSION) return HM_ERR_ABI;
-  if (d->wfmt != HM_W_INT4_SYM && d->wfmt != HM_W_UINT4_ZP && d->wfmt != HM_W_MXFP4)
+  if (d->wfmt != HM_W_INT4_SYM && d->wfmt != HM_W_UINT4_ZP && d->wfmt != HM_W_MXFP4 && d->wfmt != HM_W_MXINT4)
     return HM_ERR_UNSUPPORTED;
-  const int want_group = (d->wfmt == HM_W_MXFP4) ? 32 : 128;
+  const int want_group = is_mx(d->wfmt) ? 32 : 128;
   if (d->group != want_group) return HM_ERR_SHAPE;
   if (d->num_experts < 1 || d->n < 1 || d->k < 128 || (d->k % 128) != 0) return HM_ERR_SHAPE;
   if (d->n > (1ll << 24) || d->k > (1ll << 24)) return HM_ERR_SHAPE;
@@ -62,11 +62,12 @@ hm_status check_pair(const hm_wdesc* d, int32_t afmt) {
   return HM_OK;
 }
 
-// MXFP4 weights with bf16 rows (E2M1 scaled to bf16 inside the kernels)
-bool mx_a16(const hm_wdesc* d, int32_t afmt) { return d->wfmt == HM_W_MXFP4 && afmt == HM_A_BF16; }
+// MX weights (MXFP4, MXINT4) with bf16 rows (codes scaled to bf16 inside the kernels)
+bool mx_a16(const hm_wdesc* d, int32_t afmt) { return is_mx(d->wfmt) && afmt == HM_A_BF16; }
 
 const char* pair_name(const hm_wdesc* d, int32_t afmt) {
   if (d->wfmt == HM_W_MXFP4) return afmt == HM_A_BF16 ? "w4a16-mxfp4" : "w4a8-mxfp4";
+  if (d->wfmt == HM_W_MXINT4) return "w4a16-mxint4";
   return d->wfmt == HM_W_UINT4_ZP ? "w4a16-uint4zp" : "w4a16-int4sym";
 }
 
@@ -107,7 +108,7 @@ DensePlan plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m) {
   // launch costs ~8 us + 0.8 ns per (chunk x column) and a round of 128 x 64
   // tiles 23-25 us, so chunks x N <= 16384 streams (N = 1792, M = 128: 14.9
   // against 23.4 us; N = 7168, M = 128 stays on tiles: 25.3 against 28.8 us)
-  const bool narrow = d->wfmt != HM_W_MXFP4 && m <= kStreamWideRows &&
+  const bool narrow = !is_mx(d->wfmt) && m <= kStreamWideRows &&
                       ((m + kStreamMaxRows - 1) / kStreamMaxRows) * d->n <= kStreamChunkCols;
   p.stream = (force == 1) || (force == 0 && (m <= kStreamMaxRows || narrow));
   if (force == 1 && m > kStreamWideRows) p.stream = false;  // forced streaming: up to 256 rows
@@ -119,7 +120,7 @@ DensePlan plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m) {
     // faster on the smaller tiles
     const int64_t big_rounds = (big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows) + 255) / 256;
     const int64_t mid_rounds = (mid_n_tiles(G, false) * ((m + kTileM - 1) / kTileM) + 255) / 256;
-    const bool mid_fewer = d->wfmt != HM_W_MXFP4 && mid_rounds * 10 < big_rounds * 38;
+    const bool mid_fewer = !is_mx(d->wfmt) && mid_rounds * 10 < big_rounds * 38;
     p.big = (force == 3) || (force == 0 && m >= kBigMinRows && !mid_fewer);
     p.mid = !p.big && force != 4;
     // MXFP4 with bf16 rows (no 256 x 256 kernel): 128 x 64 tiles, or 128 x
@@ -258,7 +259,7 @@ HM_API hm_status hm_transform(const hm_wdesc* d, const uint8_t* codes, const voi
   if (!codes || !scales || !w_dev) return HM_ERR_NULL;
   if (d->wfmt == HM_W_UINT4_ZP && !zeros) return HM_ERR_NULL;
   if (!aligned(codes, 16) || !aligned(w_dev, 256)) return HM_ERR_ALIGN;
-  if (!aligned(scales, d->wfmt == HM_W_MXFP4 ? 1 : 2)) return HM_ERR_ALIGN;
+  if (!aligned(scales, is_mx(d->wfmt) ? 1 : 2)) return HM_ERR_ALIGN;
   const Geom G = geom_of(d);
   if (w_bytes < G.total) return HM_ERR_WORKSPACE;
   if (launch_transform(d->wfmt, G, codes, scales, zeros, (uint8_t*)w_dev, stream) != hipSuccess)

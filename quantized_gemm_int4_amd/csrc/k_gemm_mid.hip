@@ -81,7 +81,7 @@ struct MxFrag {
 
 }  // namespace
 
-template <bool ZP, bool GROUPED, bool F4>
+template <bool ZP, bool GROUPED, bool F4, bool I4>
 __global__ void __launch_bounds__(256, 1)
 k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -231,7 +231,7 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
         if (F4) {
           // E8M0 of (column c16, K block w): byte g % 4 of scale word c16 + 16 w
           const uint32_t sw = *reinterpret_cast<const uint32_t*>(sz + 4 * (c16 + 16 * wave));
-          sv[nb2] = e8m0_f32((sw >> (8 * (g & 3))) & 0xFFu);
+          sv[nb2] = e8m0_f32((sw >> (8 * (g & 3))) & 0xFFu) * (I4 ? 0.25f : 1.0f);   // MXINT4: q / 4
           zs[nb2] = 0.f;
           continue;
         }
@@ -250,7 +250,8 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
       fetch(wso[0], 0, wq, csv, czs);
 #pragma unroll
       for (int nb2 = 0; nb2 < 2; ++nb2) {
-        af[nb2][0] = F4 ? fp4x8_bf16(wq[nb2][0], csv[nb2]) : dq8_bytes(wq[nb2][0], csv[nb2], czs[nb2]);
+        af[nb2][0] = I4 ? i4x8_bf16(wq[nb2][0], csv[nb2])
+                     : F4 ? fp4x8_bf16(wq[nb2][0], csv[nb2]) : dq8_bytes(wq[nb2][0], csv[nb2], czs[nb2]);
         af[nb2][1] = (u32x4_t){0u, 0u, 0u, 0u};
         c1[nb2] = wq[nb2][1];
       }
@@ -304,7 +305,7 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
           const uint32_t w = k2 == 0 ? c1[nb2] : nq[nb2][0];
           const float sv = k2 == 0 ? csv[nb2] : nsv[nb2], zs = k2 == 0 ? czs[nb2] : nzs[nb2];
           if (F4) {
-            af[nb2][k2 ^ 1][u] = fp4x2_bf16(w, sv, u);
+            af[nb2][k2 ^ 1][u] = I4 ? i4x2_bf16(w, sv, u) : fp4x2_bf16(w, sv, u);
             continue;
           }
           if (u == 0) {
@@ -612,9 +613,9 @@ static hipError_t go_mid_mx(const GemmArgs& a, int grid_items, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool ZP, bool GROUPED, bool F4 = false>
+template <bool ZP, bool GROUPED, bool F4 = false, bool I4 = false>
 static hipError_t go_mid(const GemmArgs& a, int grid_items, hipStream_t st) {
-  auto kern = &k_gemm_mid<ZP, GROUPED, F4>;
+  auto kern = &k_gemm_mid<ZP, GROUPED, F4, I4>;
   static const hipError_t attr_err = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kMidLds);
   if (attr_err != hipSuccess) return attr_err;
@@ -641,6 +642,8 @@ hipError_t launch_gemm_mid(const GemmArgs& a, bool grouped, int grid_items, hipS
   }
   if (kmode_of(a) == KM_MX_A16)
     return grouped ? go_mid<false, true, true>(a, grid_items, st) : go_mid<false, false, true>(a, 0, st);
+  if (kmode_of(a) == KM_MXI4_A16)
+    return grouped ? go_mid<false, true, true, true>(a, grid_items, st) : go_mid<false, false, true, true>(a, 0, st);
   if (a.wfmt == W_MXFP4) return grouped ? go_mid_mx<true>(a, grid_items, st) : go_mid_mx<false>(a, 0, st);
   if (a.wfmt == W_UINT4_ZP)
     return grouped ? go_mid<true, true>(a, grid_items, st) : go_mid<true, false>(a, 0, st);

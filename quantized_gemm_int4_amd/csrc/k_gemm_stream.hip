@@ -51,7 +51,8 @@ template <int MODE, bool ZP, int MB, int NBW, int KS, int DW, bool GROUPED>
 __global__ void __launch_bounds__(256)
 k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
   constexpr bool MX = MODE == KM_MX_A8;                 // FP8 rows, scaled fp4 x fp8 MFMA
-  constexpr bool F4 = MODE == KM_MX_A16;                // MXFP4 codes scaled to bf16
+  constexpr bool F4 = MODE == KM_MX_A16 || MODE == KM_MXI4_A16;   // MX codes scaled to bf16
+  constexpr bool I4 = MODE == KM_MXI4_A16;              // MXINT4: two's complement codes / 4
   constexpr bool MXW = MX || F4;                        // E8M0 scale words
   constexpr int ROWS = MB * 16;
   constexpr int GB = MX ? 128 : 256;                    // activation bytes per row per K group
@@ -244,7 +245,7 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
           // column; the activation fragment of MFMA kk covers the same K
           float sf[NBW];
 #pragma unroll
-          for (int j = 0; j < NBW; ++j) sf[j] = e8m0_f32((wsr[d][j] >> (8 * (g & 3))) & 0xFFu);
+          for (int j = 0; j < NBW; ++j) sf[j] = e8m0_f32((wsr[d][j] >> (8 * (g & 3))) & 0xFFu) * (I4 ? 0.25f : 1.0f);
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
             u32x4_t af[MB];
@@ -252,7 +253,7 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
             for (int rb = 0; rb < MB; ++rb) af[rb] = ld16(xg + lrow[rb] * xb + (32 * q_l + 8 * kk) * 2);
 #pragma unroll
             for (int j = 0; j < NBW; ++j) {
-              const u32x4_t bw = fp4x8_bf16(wq[d][j][kk], sf[j]);
+              const u32x4_t bw = I4 ? i4x8_bf16(wq[d][j][kk], sf[j]) : fp4x8_bf16(wq[d][j][kk], sf[j]);
 #pragma unroll
               for (int rb = 0; rb < MB; ++rb) acc[j][rb] = mfma_bf16(bw, af[rb], acc[j][rb]);
             }
@@ -494,6 +495,9 @@ hipError_t launch_gemm_stream(const GemmArgs& a, const StreamCfg& c, bool groupe
   if (mode == KM_MX_A16)
     return grouped ? go_stream_mb<KM_MX_A16, false, true>(a, c, grid_items, st)
                    : go_stream_mb<KM_MX_A16, false, false>(a, c, grid_items, st);
+  if (mode == KM_MXI4_A16)
+    return grouped ? go_stream_mb<KM_MXI4_A16, false, true>(a, c, grid_items, st)
+                   : go_stream_mb<KM_MXI4_A16, false, false>(a, c, grid_items, st);
   if (a.wfmt == W_UINT4_ZP)
     return grouped ? go_stream_mb<KM_INT4_A16, true, true>(a, c, grid_items, st)
                    : go_stream_mb<KM_INT4_A16, true, false>(a, c, grid_items, st);

@@ -26,7 +26,8 @@ template <int MODE, bool GROUPED>
 __global__ void __launch_bounds__(256)
 k_gemm_tile(GemmArgs a, int n_tiles) {
   constexpr bool MX = MODE == KM_MX_A8;                // FP8 rows, scaled fp4 x fp8 MFMA
-  constexpr bool F4 = MODE == KM_MX_A16;               // MXFP4 codes scaled to bf16
+  constexpr bool F4 = MODE == KM_MX_A16 || MODE == KM_MXI4_A16;  // MX codes scaled to bf16
+  constexpr bool I4 = MODE == KM_MXI4_A16;             // MXINT4: two's complement codes / 4
   constexpr int XB = MX ? (128 + 16) : (256 + 16);     // LDS activation row stride (bytes)
   constexpr int XPR = MX ? 8 : 16;                     // 16-byte pieces per activation row
   constexpr int XLD = kTileM * XPR / 256;              // pieces per thread
@@ -143,9 +144,10 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
           const int q = tid + 256 * i;
           const int nbl = q >> 6, L = q & 63;
           if (F4) {
-            const float sf = e8m0_f32(wsr[i]);
+            const float sf = e8m0_f32(wsr[i]) * (I4 ? 0.25f : 1.0f);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) st16(&ws_lds[((nbl * 4 + j) * 64 + L) * 16], fp4x8_bf16(wq[i][j], sf));
+            for (int j = 0; j < 4; ++j)
+              st16(&ws_lds[((nbl * 4 + j) * 64 + L) * 16], I4 ? i4x8_bf16(wq[i][j], sf) : fp4x8_bf16(wq[i][j], sf));
             continue;
           }
           const float sv = bf16_to_f32(wsr[i] & 0xFFFF);
@@ -248,6 +250,8 @@ hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hip
     return grouped ? go_tile<KM_MX_A8, true>(a, grid_items, st) : go_tile<KM_MX_A8, false>(a, grid_items, st);
   if (mode == KM_MX_A16)
     return grouped ? go_tile<KM_MX_A16, true>(a, grid_items, st) : go_tile<KM_MX_A16, false>(a, grid_items, st);
+  if (mode == KM_MXI4_A16)
+    return grouped ? go_tile<KM_MXI4_A16, true>(a, grid_items, st) : go_tile<KM_MXI4_A16, false>(a, grid_items, st);
   return grouped ? go_tile<KM_INT4_A16, true>(a, grid_items, st) : go_tile<KM_INT4_A16, false>(a, grid_items, st);
 }
 

@@ -31,7 +31,7 @@ k_transform_codes(int wfmt, Geom G, const uint8_t* __restrict__ codes, uint8_t* 
     u32x4_t v;
     if (n < G.N) {
       const uint8_t* row = codes + (e * G.N + n) * row_bytes;
-      if (wfmt == W_MXFP4) {
+      if (is_mx(wfmt)) {
         v = ld16(row + 64 * g + 16 * h);
       } else {
         const uint8_t* p = row + 64 * g + 4 * h;
@@ -142,14 +142,19 @@ k_dequant(int wfmt, Geom G, const uint8_t* __restrict__ w, int64_t e, float* __r
     const int64_t nb = n / 16, c = n % 16, g = k / 128, kk = k % 128;
     const int64_t tile = (e * G.NB + nb) * G.KG + g;
     float r[8];
-    if (wfmt == W_MXFP4) {
+    if (is_mx(wfmt)) {
       const int h = (int)(kk / 32);
       const int L = (int)c + 16 * h;
       const uint32_t word = *reinterpret_cast<const uint32_t*>(w + tile * 1024 + L * 16 + (kk % 32) / 2);
       const uint32_t* sc = reinterpret_cast<const uint32_t*>(w + G.off_scales);
       const uint32_t sb = (sc[((e * G.NB + nb) * G.KG4 + g / 4) * 64 + L] >> (8 * (g % 4))) & 0xFF;
       const float s = e8m0_value(sb);
-      for (int q = 0; q < 8; ++q) r[q] = e2m1_value((word >> (4 * q)) & 0xF) * s;
+      if (wfmt == W_MXINT4) {
+        // two's complement q, value q / 4 (exact)
+        for (int q = 0; q < 8; ++q) r[q] = (float)((int)(word << (28 - 4 * q)) >> 28) * 0.25f * s;
+      } else {
+        for (int q = 0; q < 8; ++q) r[q] = e2m1_value((word >> (4 * q)) & 0xF) * s;
+      }
     } else {
       const int j = (int)(kk / 32), h = (int)((kk % 32) / 8);
       const int L = (int)c + 16 * h;
@@ -184,7 +189,7 @@ hipError_t launch_transform(int wfmt, const Geom& G, const uint8_t* codes, const
                             const uint8_t* zeros, uint8_t* out, hipStream_t st) {
   hipLaunchKernelGGL(k_transform_codes, dim3(grid_for(G.E * G.NB * G.KG * 64)), dim3(256), 0, st,
                      wfmt, G, codes, out);
-  if (wfmt == W_MXFP4) {
+  if (is_mx(wfmt)) {
     hipLaunchKernelGGL(k_transform_scales_mx, dim3(grid_for(G.E * G.NB * G.KG4 * 64)), dim3(256), 0,
                        st, G, (const uint8_t*)scales, (uint32_t*)(out + G.off_scales));
   } else {
@@ -197,7 +202,7 @@ hipError_t launch_transform(int wfmt, const Geom& G, const uint8_t* codes, const
   }
   // gap ends: codes end .. scales start, scales end .. zeros start, zeros end .. total
   const size_t codes_end = (size_t)G.E * G.NB * G.KG * 1024;
-  const size_t scales_end = G.off_scales + ((wfmt == W_MXFP4) ? (size_t)G.E * G.NB * G.KG4 * 256
+  const size_t scales_end = G.off_scales + (is_mx(wfmt) ? (size_t)G.E * G.NB * G.KG4 * 256
                                                               : (size_t)G.E * G.NB * G.KG * 32);
   const size_t zeros_end = (wfmt == W_UINT4_ZP) ? G.off_zeros + (size_t)G.E * G.NB * G.KG * 8 : G.off_zeros;
   hipLaunchKernelGGL(k_zero_gaps, dim3(1), dim3(256), 0, st, out, codes_end, G.off_scales, scales_end,

@@ -11,13 +11,14 @@ constexpr int kBigRows = 256;   // rows of a 256 x 256 tile (and of a grouped 25
 // Kernel variants by (weight format, activation format): INT4 codes with
 // bf16 rows, MXFP4 with FP8 rows (scaled fp4 x fp8 MFMA), MXFP4 with bf16 rows
 // (E2M1 converted to bf16 with its E8M0 scale, bf16 MFMA).
-enum KMode : int { KM_INT4_A16 = 0, KM_MX_A8 = 1, KM_MX_A16 = 2 };
+// (MXINT4 weights with bf16 rows take the MXFP4 path with integer codes.)
+enum KMode : int { KM_INT4_A16 = 0, KM_MX_A8 = 1, KM_MX_A16 = 2, KM_MXI4_A16 = 3 };
 
 // Arguments shared by the GEMM kernels.
 struct GemmArgs {
   const uint8_t* w;        // device weight layout (all experts)
   Geom G;
-  int wfmt;                // W_INT4_SYM / W_UINT4_ZP / W_MXFP4
+  int wfmt;                // W_INT4_SYM / W_UINT4_ZP / W_MXFP4 / W_MXINT4
   int a8;                  // 1: x is E4M3 bytes with fp32 row scales (MXFP4 only); 0: bf16
   const void* x;           // activations: bf16 [rows][K] or E4M3 bytes [rows][K]
   const float* xs;         // fp32 row scales (A8) or null
@@ -92,6 +93,7 @@ int64_t big_n_tiles(const Geom& G);
 int64_t big_full_tiles(const Geom& G, int64_t M, bool mx);
 
 inline int kmode_of(const GemmArgs& a) {
+  if (a.wfmt == W_MXINT4) return KM_MXI4_A16;
   return a.wfmt != W_MXFP4 ? KM_INT4_A16 : (a.a8 ? KM_MX_A8 : KM_MX_A16);
 }
 

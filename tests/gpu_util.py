@@ -27,7 +27,7 @@ def bits_of(y):
 def std_to_dev(fmt, codes, scales, zeros):
     """Standard-format numpy arrays ([E,...]) -> device tensors for hm_transform."""
     c = to_dev(codes.astype(np.uint8))
-    if fmt == quant.FMT_MXFP4:
+    if fmt in quant.MX_FORMATS:
         s = to_dev(scales.astype(np.uint8))
     else:
         s = to_dev(scales.astype(np.uint16).view(np.int16))

@@ -38,7 +38,7 @@ def test_status_strings():
     assert hm.lib.hm_status_string(99).decode() == "unknown status"
 
 
-@pytest.mark.parametrize("fmt", ["int4_sym", "uint4_zp", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4_sym", "uint4_zp", "mxfp4", "mxint4"])
 @pytest.mark.parametrize("E,N,K", [(1, 256, 512), (1, 14336, 4096), (3, 37, 640), (256, 4096, 7168)])
 def test_transform_size_matches_layout_spec(fmt, E, N, K):
     d = hm.wdesc(fmt, N, K, E)
@@ -128,6 +128,24 @@ def test_mxfp4_bf16_rows_plans():
     moe = hm.wdesc("mxfp4", 4096, 7168, 256)
     assert _err("hm_moe_gemm_workspace_size", ctypes.byref(moe), 0, 64, 8, ctypes.byref(sz)) == 0
     assert sz.value > 0
+
+
+def test_mxint4_pairs_and_plans():
+    """MXINT4 (group 32) takes bf16 rows only, on the same kernels as MXFP4 with bf16 rows."""
+    import os
+    sz = ctypes.c_size_t()
+    d = hm.wdesc("mxint4", 7168, 2048)
+    bad = hm.wdesc("mxint4", 7168, 2048); bad.group = 128
+    assert _err("hm_transform_size", ctypes.byref(bad), ctypes.byref(sz)) == 2
+    assert _err("hm_gemm_workspace_size", ctypes.byref(d), 1, 16, ctypes.byref(sz)) == 4
+    assert hm.hm_gemm_plan(d, hm.HM_A_BF16, 16).startswith("w4a16-mxint4 stream")
+    assert hm.hm_gemm_plan(d, hm.HM_A_BF16, 256).startswith("w4a16-mxint4 tile 128x64")
+    assert hm.hm_gemm_plan(d, hm.HM_A_BF16, 4096).startswith("w4a16-mxint4 tile 128x128")
+    os.environ["HM_FORCE_PATH"] = "3"
+    try:
+        assert "128x64" in hm.hm_gemm_plan(d, hm.HM_A_BF16, 4096)
+    finally:
+        os.environ.pop("HM_FORCE_PATH", None)
 
 
 def test_moe_argument_checks():

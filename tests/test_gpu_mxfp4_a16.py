@@ -1,6 +1,7 @@
-"""GPU parity for MXFP4 weights with bf16 activation rows (the MXFP4 W4A16
-pair the pages report for MoE layers): the E2M1 codes are scaled by their
-E8M0 block scale to bf16 inside the kernels and multiplied on the bf16 MFMA.
+"""GPU parity for MX weights with bf16 activation rows: MXFP4 (the MXFP4
+W4A16 pair the pages report for MoE layers) and MXINT4 (1.2 fixed-point
+INT4 elements): the codes are scaled by their E8M0 block scale to bf16
+inside the kernels and multiplied on the bf16 MFMA.
 
 The oracle is the same fp64 GEMM of the exactly dequantized weights as for
 the other pairs, with the bf16 values of X; the dequantization itself is
@@ -19,6 +20,7 @@ from gpu_util import bf16_to_dev, bits_of, quantize_experts, std_to_dev, to_dev
 pytestmark = pytest.mark.gpu
 
 MX = quant.FMT_MXFP4
+MXS = [quant.FMT_MXFP4, quant.FMT_MXINT4]
 
 
 @pytest.fixture(autouse=True)
@@ -34,8 +36,9 @@ def _bf16_one_rows(k, cols):
     return x
 
 
+@pytest.mark.parametrize("fmt", MXS)
 @pytest.mark.parametrize("m,force", [(32, None), (7, None), (256, None), (256, 4), (200, 1)])
-def test_dequant_through_unit_rows(m, force):
+def test_dequant_through_unit_rows(fmt, m, force):
     """y[i, n] = w_hat[n, c_i] exactly: all 16 E2M1 codes under scale bytes
     from 0 (products down to 2^-128, subnormal in fp32 and bf16) to 252
     (largest 6 * 2^125, the last byte whose products stay below 2^128), on the
@@ -45,11 +48,13 @@ def test_dequant_through_unit_rows(m, force):
     n, k = 40, 256
     r = np.random.default_rng(11)
     codes = r.integers(0, 256, (n, k // 2), dtype=np.uint8)
-    ebytes = np.array([0, 1, 2, 3, 4, 60, 100, 119, 120, 126, 127, 128, 140, 200, 250, 252], dtype=np.uint8)
-    scales = r.choice(ebytes, (n, k // 32)).astype(np.uint8)
-    what = quant.dequant(MX, codes, scales, None).astype(np.float64)
-    d = hm.wdesc(MX, n, k)
-    w = hm.hm_transform(d, *std_to_dev(MX, codes[None], scales[None], None))
+    ebytes = [0, 1, 2, 3, 4, 60, 100, 119, 120, 126, 127, 128, 140, 200, 250, 252]
+    if fmt == quant.FMT_MXINT4:
+        ebytes.append(253)                       # |w| <= 2 * 2^126
+    scales = r.choice(np.array(ebytes, dtype=np.uint8), (n, k // 32)).astype(np.uint8)
+    what = quant.dequant(fmt, codes, scales, None).astype(np.float64)
+    d = hm.wdesc(fmt, n, k)
+    w = hm.hm_transform(d, *std_to_dev(fmt, codes[None], scales[None], None))
     cols = r.permutation(k)[:m] if m <= k else None
     xb = _bf16_one_rows(k, cols)
     if force is not None:
@@ -63,12 +68,12 @@ def test_dequant_through_unit_rows(m, force):
 
 
 class MxLayer:
-    def __init__(self, n, k, cfg=3, wseed=0):
+    def __init__(self, n, k, cfg=3, wseed=0, fmt=MX):
         import quantized_gemm_int4_amd as hm
-        codes, scales, _, what = quantize_experts(MX, [synthetic.weights(cfg, n, k, index=wseed)])
+        codes, scales, _, what = quantize_experts(fmt, [synthetic.weights(cfg, n, k, index=wseed)])
         self.what = what[0].astype(np.float64)
-        self.desc = hm.wdesc(MX, n, k)
-        self.w = hm.hm_transform(self.desc, *std_to_dev(MX, codes, scales, None))
+        self.desc = hm.wdesc(fmt, n, k)
+        self.w = hm.hm_transform(self.desc, *std_to_dev(fmt, codes, scales, None))
 
     def check(self, xb, rows=None):
         import quantized_gemm_int4_amd as hm
@@ -84,21 +89,23 @@ class MxLayer:
         return res
 
 
+@pytest.mark.parametrize("fmt", MXS)
 @pytest.mark.parametrize("n,k", [(200, 384), (37, 128), (1000, 1152)])
 @pytest.mark.parametrize("m", [1, 7, 16, 17, 32, 33, 100, 129, 257])
-def test_ragged_default_path(n, k, m):
-    MxLayer(n, k, cfg=7, wseed=n + k).check(synthetic.activations(7, m, k, index=m, outliers=0.01))
+def test_ragged_default_path(fmt, n, k, m):
+    MxLayer(n, k, cfg=7, wseed=n + k, fmt=fmt).check(synthetic.activations(7, m, k, index=m, outliers=0.01))
 
 
 @pytest.mark.parametrize("m,force", [(64, 1), (256, 1), (1, 4), (17, 4), (100, 4), (300, 4), (300, 3)])
-def test_forced_paths(m, force):
+@pytest.mark.parametrize("fmt", MXS)
+def test_forced_paths(fmt, m, force):
     os.environ["HM_FORCE_PATH"] = str(force)
-    MxLayer(264, 640, cfg=7, wseed=5).check(synthetic.activations(7, m, 640, index=m, outliers=0.01))
+    MxLayer(264, 640, cfg=7, wseed=5, fmt=fmt).check(synthetic.activations(7, m, 640, index=m, outliers=0.01))
 
 
-@pytest.fixture(scope="module")
-def wide():
-    return MxLayer(7168, 2048, cfg=3)
+@pytest.fixture(scope="module", params=MXS)
+def wide(request):
+    return MxLayer(7168, 2048, cfg=3, fmt=request.param)
 
 
 @pytest.mark.parametrize("m", [1, 16, 256])
@@ -120,29 +127,30 @@ def _skewed_ids(t, topk, E, seed):
     return np.stack([r.choice(E, topk, replace=False, p=p) for _ in range(t)]).astype(np.int32)
 
 
+@pytest.mark.parametrize("fmt", MXS)
 @pytest.mark.parametrize("rows_are_pairs", [0, 1])
 @pytest.mark.parametrize("mid", [1, 0])
-def test_moe_mixed_units(rows_are_pairs, mid):
+def test_moe_mixed_units(fmt, rows_are_pairs, mid):
     """Streaming units (small experts) and 128-row tile units in one grouped
     call; the tile units on the 128 x 64 kernel (mid=1, the default) or the
     128 x 128 one."""
     import quantized_gemm_int4_amd as hm
     os.environ["HM_MOE_MID"] = str(mid)
     try:
-        _moe_mixed(hm, rows_are_pairs)
+        _moe_mixed(hm, rows_are_pairs, fmt)
     finally:
         os.environ.pop("HM_MOE_MID", None)
 
 
-def _moe_mixed(hm, rows_are_pairs):
+def _moe_mixed(hm, rows_are_pairs, fmt):
     t, topk, E, n, k = 150, 2, 8, 208, 384
     ids = _skewed_ids(t, topk, E, 1)
     counts = np.bincount(ids.ravel(), minlength=E)
     assert counts.max() > 128 and (counts[counts > 0] <= 32).any()
     ws = [synthetic.weights(12, n, k, index=100 + e) for e in range(E)]
-    codes, scales, _, what = quantize_experts(MX, ws)
-    d = hm.wdesc(MX, n, k, E)
-    w = hm.hm_transform(d, *std_to_dev(MX, codes, scales, None))
+    codes, scales, _, what = quantize_experts(fmt, ws)
+    d = hm.wdesc(fmt, n, k, E)
+    w = hm.hm_transform(d, *std_to_dev(fmt, codes, scales, None))
     xb = synthetic.activations(12, t * topk if rows_are_pairs else t, k, index=1, outliers=0.01)
     _, off, sp = hm.hm_moe_sort(to_dev(ids), E)
     y = hm.hm_moe_gemm(d, w, bf16_to_dev(xb), off, sp, t, topk, rows_are_pairs)
@@ -153,8 +161,9 @@ def _moe_mixed(hm, rows_are_pairs):
     assert res["ok"], res
 
 
+@pytest.mark.parametrize("fmt", MXS)
 @pytest.mark.parametrize("t,proj", [(64, "gate_up"), (1024, "down")])
-def test_moe_workload_size_sampled(t, proj):
+def test_moe_workload_size_sampled(fmt, t, proj):
     """256 experts, top-8 routing, gate_up N=4096 K=7168 / down N=7168 K=2048,
     bf16 rows, checked on pairs of the largest and a few small experts."""
     import quantized_gemm_int4_amd as hm
@@ -165,7 +174,7 @@ def test_moe_workload_size_sampled(t, proj):
     g.manual_seed(9)
     codes = torch.randint(0, 256, (E, n, k // 2), dtype=torch.uint8, device="cuda", generator=g)
     scales = torch.randint(118, 122, (E, n, k // 32), dtype=torch.uint8, device="cuda", generator=g)
-    d = hm.wdesc(MX, n, k, E)
+    d = hm.wdesc(fmt, n, k, E)
     w = hm.hm_transform(d, codes, scales, None)
     ids, _ = synthetic.router_topk(6, t, E, topk)
     xb = synthetic.activations(14, t * topk if rows_are_pairs else t, k, outliers=0.01)
@@ -183,7 +192,7 @@ def test_moe_workload_size_sampled(t, proj):
 
     def what(e):
         if e not in cache:
-            cache[e] = quant.dequant(MX, codes[e].cpu().numpy(), scales[e].cpu().numpy(), None).astype(np.float64)
+            cache[e] = quant.dequant(fmt, codes[e].cpu().numpy(), scales[e].cpu().numpy(), None).astype(np.float64)
         return cache[e]
 
     yref, b, _ = moe.moe_gemm_ref(codecs.bf16_value(xb).astype(np.float64), bool(rows_are_pairs), topk, ids,

@@ -17,7 +17,7 @@ SHAPES = [(1, 16, 128), (2, 37, 256), (1, 5, 640), (3, 100, 384)]
 def _random_std(fmt, E, N, K, seed):
     r = np.random.default_rng(seed)
     codes = r.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
-    if fmt == quant.FMT_MXFP4:
+    if fmt in quant.MX_FORMATS:
         scales = r.integers(0, 255, size=(E, N, K // 32), dtype=np.uint8)   # every byte but NaN
     else:
         # finite bf16 patterns of both signs (|s| < 2^119 so s*15 stays finite),
@@ -28,7 +28,7 @@ def _random_std(fmt, E, N, K, seed):
     return codes, scales, zeros
 
 
-@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("fmt", quant.FORMATS + (quant.FMT_MXINT4,))
 @pytest.mark.parametrize("E,N,K", SHAPES)
 def test_transform_byte_exact(fmt, E, N, K):
     import quantized_gemm_int4_amd as hm
@@ -41,7 +41,7 @@ def test_transform_byte_exact(fmt, E, N, K):
     assert np.array_equal(w.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("fmt", quant.FORMATS + (quant.FMT_MXINT4,))
 @pytest.mark.parametrize("E,N,K", SHAPES)
 def test_dequant_bit_exact(fmt, E, N, K):
     import quantized_gemm_int4_amd as hm
@@ -54,11 +54,11 @@ def test_dequant_bit_exact(fmt, E, N, K):
         assert np.array_equal(out.view(np.uint32), ref.view(np.uint32)), f"expert {e}"
 
 
-@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("fmt", quant.FORMATS + (quant.FMT_MXINT4,))
 def test_dequant_full_size_quantized(fmt):
     """Quantized N(0,0.02) weights at the dense FFN up-projection size."""
     import quantized_gemm_int4_amd as hm
-    N, K = (7168, 2048) if fmt == quant.FMT_MXFP4 else (14336, 4096)
+    N, K = (7168, 2048) if fmt in quant.MX_FORMATS else (14336, 4096)
     wf = synthetic.weights(2, N, K)
     codes, scales, zeros, what = quantize_experts(fmt, [wf])
     d = hm.wdesc(fmt, N, K)
