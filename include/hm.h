@@ -116,9 +116,9 @@ hm_status hm_transform_size(const hm_wdesc* d, size_t* bytes);
  * one 1 KiB tile of 16 columns x 128 K per 16-byte-per-lane load).  Run once
  * per weight, before inference.
  *   codes  [E][N][K/2] bytes, element k=2j in the low nibble of byte j,
- *          k=2j+1 in the high nibble (two's complement for INT4_SYM, unsigned
- *          for UINT4_ZP, E2M1 bits for MXFP4).
- *   scales INT4 formats: bf16 [E][N][K/128]; MXFP4: E8M0 bytes [E][N][K/32].
+ *          k=2j+1 in the high nibble (two's complement for INT4_SYM and
+ *          MXINT4, unsigned for UINT4_ZP, E2M1 bits for MXFP4).
+ *   scales INT4 formats: bf16 [E][N][K/128]; MXFP4, MXINT4: E8M0 bytes [E][N][K/32].
  *   zeros  UINT4_ZP only: bytes [E][N][K/128], low nibble used; else NULL.
  *   w_dev  output, w_bytes >= hm_transform_size.  Opaque; valid only for the
  *          same descriptor. */
