@@ -88,7 +88,7 @@ struct DensePlan {
   size_t ws_bytes;
 };
 
-// MXFP4 with bf16 rows: rows that take the 128 x 128 kernel instead of the
+// MX weights with bf16 rows: rows that take the 128 x 128 kernel instead of the
 // 128 x 64 one (at least 8 rounds of 128 x 64 tiles on the 256 compute units)
 bool f4_wide_tiles(const Geom& G, int64_t rows) {
   const int64_t mt = (rows + kTileM - 1) / kTileM;
@@ -123,7 +123,7 @@ DensePlan plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m) {
     const bool mid_fewer = !is_mx(d->wfmt) && mid_rounds * 10 < big_rounds * 38;
     p.big = (force == 3) || (force == 0 && m >= kBigMinRows && !mid_fewer);
     p.mid = !p.big && force != 4;
-    // MXFP4 with bf16 rows (no 256 x 256 kernel): 128 x 64 tiles, or 128 x
+    // MX weights with bf16 rows (no 256 x 256 kernel): 128 x 64 tiles, or 128 x
     // 128 tiles once the 128 x 64 ones take many rounds of the chip.
     // Measured at N = 7168 K = 2048 / N = 14336 K = 4096: M = 256 / 128 on
     // 128 x 64 tiles 14.9 / 23.9 us against 30.1 / 63.2 (one round each),
@@ -475,7 +475,7 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   a.P = p.P;
   // 256-row units address activation rows with 32-bit byte offsets
   const int64_t a_bytes = (a_rows_are_pairs ? p.P : t) * d->k * (afmt == HM_A_FP8_ROWSCALE ? 1 : 2);
-  const bool f4 = mx_a16(d, afmt);   // MXFP4 with bf16 rows: streaming and 128-row units only
+  const bool f4 = mx_a16(d, afmt);   // MX weights with bf16 rows: streaming and 128-row units only
   const int big_min = (!f4 && a_bytes < (1ll << 32) && env_int("HM_MOE_BIG", 1)) ? p.big_min : 0;
   hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, p.s_rows, p.s_max, kTileM, big_min,
                                      p.max_s, p.max_t, p.max_b, hdr, su, tu, bu, stream);
@@ -491,7 +491,7 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
     // units of up to 128 rows: W4A16 on 128 x 64 tiles, W4A8 on 64 x 128
     // tiles (one block per compute unit, LDS-bound); HM_MOE_MID=0 keeps
     // them on the 128 x 128 kernel
-    // MXFP4 with bf16 rows: the 128 x 128 kernel when all pairs in 128-row
+    // MX weights with bf16 rows: the 128 x 128 kernel when all pairs in 128-row
     // units would take many rounds of 128 x 64 tiles (T = 8192: 7.92 against
     // 8.30 ms)
     const bool mid = env_int("HM_MOE_MID", 1) != 0 && !(f4 && f4_wide_tiles(a.G, p.P));

@@ -25,7 +25,8 @@
 // Operands of the next group's first K part are unpacked during the second
 // K part of the current one, so each group starts with ready operands.
 //
-// MXFP4 weights with bf16 rows (F4) run the same kernel: wave w's K values
+// MX weights with bf16 rows (F4: MXFP4, and MXINT4 with I4, whose two's
+// complement codes are converted on the vector ALU) run the same kernel: wave w's K values
 // 32 w .. 32 w + 31 are exactly the E2M1 codes of quarter w of each 16-byte
 // slot, whose words 2 kk' + hi the lanes read, with one E8M0 scale per lane
 // and column half; the gather copies the 256 bytes of scale words of the

@@ -5,7 +5,7 @@
 // registers: one 16-byte load per lane fetches one 1 KiB tile (16 columns x
 // 128 K) of the device layout, which is exactly the operand of four
 // 16x16x32 bf16 MFMAs (or of one 16x16x128 scaled fp4 x fp8 MFMA for MXFP4
-// with FP8 rows; with bf16 rows the E2M1 codes are scaled to bf16 first and fed
+// with FP8 rows; with bf16 rows the E2M1 (or MXINT4) codes are scaled to bf16 first and fed
 // to four bf16 MFMAs, the lane's 32 K values split into four runs of eight and
 // the activation fragments read in the same order).
 // The few activation rows are copied into LDS with direct global-to-LDS loads

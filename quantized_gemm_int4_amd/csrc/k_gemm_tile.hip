@@ -9,7 +9,7 @@
 //   * W4A16: the eight 1 KiB weight tiles are read once per block, unpacked and
 //     scaled to bf16 by the block's threads (once per block, not per wave) and
 //     written to LDS already in MFMA fragment order;
-//   * MXFP4 with bf16 rows: the same, each lane's eight E2M1 codes of a
+//   * MXFP4 / MXINT4 with bf16 rows: the same, each lane's eight codes of a
 //     fragment scaled to bf16 with their E8M0 scale (the fragment's K run is
 //     32 (L/16) + 8 ks + 0..7 instead of 32 ks + 8 (L/16) + 0..7, and the
 //     activation fragments follow it);

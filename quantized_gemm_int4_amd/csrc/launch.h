@@ -9,7 +9,7 @@ namespace hm {
 constexpr int kBigRows = 256;   // rows of a 256 x 256 tile (and of a grouped 256-row unit)
 
 // Kernel variants by (weight format, activation format): INT4 codes with
-// bf16 rows, MXFP4 with FP8 rows (scaled fp4 x fp8 MFMA), MXFP4 with bf16 rows
+// bf16 rows, MXFP4 with FP8 rows (scaled fp4 x fp8 MFMA), MXFP4 / MXINT4 with bf16 rows
 // (E2M1 converted to bf16 with its E8M0 scale, bf16 MFMA).
 // (MXINT4 weights with bf16 rows take the MXFP4 path with integer codes.)
 enum KMode : int { KM_INT4_A16 = 0, KM_MX_A8 = 1, KM_MX_A16 = 2, KM_MXI4_A16 = 3 };
@@ -76,7 +76,7 @@ constexpr int kTileN = 128;
 hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
 
 // Mid-M MFMA kernels: W4A16 128 x 64 output tiles (K groups split over the
-// four waves; INT4, and MXFP4 with bf16 rows), W4A8-MXFP4 64 x 128 tiles.  Dense: one block per tile.
+// four waves; INT4, and MXFP4 / MXINT4 with bf16 rows), W4A8-MXFP4 64 x 128 tiles.  Dense: one block per tile.
 // Grouped: persistent over items of hdr[1] units of up to 128 rows; items
 // per unit from mid_n_tiles (MXFP4: two 64-row halves per column tile).
 hipError_t launch_gemm_mid(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st);
