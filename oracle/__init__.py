@@ -11,8 +11,8 @@ title and section; the pages are the only specification):
 * ``codecs``  -- bit-level number formats: bf16, OCP E4M3 (fp8), E2M1 (fp4),
   E8M0 (power-of-two block scale).
 * ``quant``   -- the weight quantizers (symmetric INT4, asymmetric uint4 with a
-  zero point, MXFP4), nibble packing, exact dequantization, per-token FP8
-  activation quantization, storage accounting.
+  zero point, MXFP4, MXINT4), nibble packing, exact dequantization, per-token
+  FP8 activation quantization, storage accounting.
 * ``gemm``    -- Y = X_hat . W_hat^T in fp64, its error bound sum_k |x w|, the
   acceptance check, and the element-wise check of the MoE block steps.
 * ``moe``     -- expert sort/offsets, the per-expert (grouped) GEMM, and the
