@@ -29,6 +29,11 @@ constexpr int kMoeStreamRows = 16;   // rows per grouped streaming unit
 // -19% / -5% / -5% against 16 rows and one block); MXFP4 keeps 16 and one.
 constexpr int kMoeStreamMaxA16 = 64, kMoeStreamNbwA16 = 2;
 constexpr int kMoeStreamMaxMx = 16, kMoeStreamNbwMx = 1;
+// MXINT4 (bf16 rows): its streaming kernel is bound by the code conversion,
+// so 32-row units (each conversion serving twice the rows) with experts of
+// up to 128 rows streaming: T = 64 / 1024 / 8192 0.448 / 1.756 / 8.954 ms
+// against 0.463 / 1.826 / 9.018 with 16-row units up to 64 rows
+constexpr int kMoeStreamRowsMxi4 = 32, kMoeStreamMaxMxi4 = 128;
 constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles may be used
 // An expert remainder of at least this many rows gets a 256-row unit (a unit
 // of at most 128 rows runs four of the eight 32-row MFMA blocks) instead of
@@ -197,11 +202,13 @@ MoePlan plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk) {
   MoePlan p{};
   p.P = t * topk;
   const int64_t act = (p.P < d->num_experts) ? p.P : d->num_experts;
-  p.s_rows = env_int("HM_MOE_STREAM_ROWS", kMoeStreamRows);
-  if (p.s_rows != 16 && p.s_rows != 32) p.s_rows = kMoeStreamRows;
+  const bool mxi4 = d->wfmt == HM_W_MXINT4;
+  const int rows_dflt = mxi4 ? kMoeStreamRowsMxi4 : kMoeStreamRows;
+  p.s_rows = env_int("HM_MOE_STREAM_ROWS", rows_dflt);
+  if (p.s_rows != 16 && p.s_rows != 32) p.s_rows = rows_dflt;
   // experts with up to s_max rows stream, as ceil(rows / s_rows) units
   const bool mx = afmt == HM_A_FP8_ROWSCALE;
-  p.s_max = env_int("HM_MOE_STREAM_MAX", mx ? kMoeStreamMaxMx : kMoeStreamMaxA16);
+  p.s_max = env_int("HM_MOE_STREAM_MAX", mx ? kMoeStreamMaxMx : (mxi4 ? kMoeStreamMaxMxi4 : kMoeStreamMaxA16));
   if (p.s_max < p.s_rows) p.s_max = p.s_rows;
   p.max_s = p.P / p.s_rows + act;
   p.max_t = (p.P + kTileM - 1) / kTileM + act;
