@@ -434,9 +434,9 @@ def run_moe(args, fmt, a8):
             hm.hm_moe_sort(ids_d, E, cnt, off, sp)
             if a8:
                 hm.hm_quant_fp8_rows(x, x8, xs)
-                hm.hm_moe_gemm(d_gu, w_gu, x8, off, sp, t, topk, 0, a_row_scale=xs, y=y1, ws=ws1)
+                hm.hm_moe_gemm(d_gu, w_gu, x8, off, sp, t, topk, 0, a_scales=xs, y=y1, ws=ws1)
                 hm.hm_quant_fp8_rows(a2, a8b, as_)
-                hm.hm_moe_gemm(d_dn, w_dn, a8b, off, sp, t, topk, 1, a_row_scale=as_, y=y2, ws=ws2)
+                hm.hm_moe_gemm(d_dn, w_dn, a8b, off, sp, t, topk, 1, a_scales=as_, y=y2, ws=ws2)
             else:
                 hm.hm_moe_gemm(d_gu, w_gu, x, off, sp, t, topk, 0, y=y1, ws=ws1)
                 hm.hm_moe_gemm(d_dn, w_dn, a2, off, sp, t, topk, 1, y=y2, ws=ws2)
@@ -447,10 +447,10 @@ def run_moe(args, fmt, a8):
             hm.hm_moe_sort(ids_d, E, cnt, off, sp)
             if a8:
                 hm.hm_quant_fp8_rows(x, x8, xs)
-                hm.hm_moe_gemm(d_gu, w_gu, x8, off, sp, t, topk, 0, a_row_scale=xs, y=y1, ws=ws1)
+                hm.hm_moe_gemm(d_gu, w_gu, x8, off, sp, t, topk, 0, a_scales=xs, y=y1, ws=ws1)
                 hm.hm_silu_mul(y1, hbuf)
                 hm.hm_quant_fp8_rows(hbuf, a8b, as_)
-                hm.hm_moe_gemm(d_dn, w_dn, a8b, off, sp, t, topk, 1, a_row_scale=as_, y=y2, ws=ws2)
+                hm.hm_moe_gemm(d_dn, w_dn, a8b, off, sp, t, topk, 1, a_scales=as_, y=y2, ws=ws2)
             else:
                 hm.hm_moe_gemm(d_gu, w_gu, x, off, sp, t, topk, 0, y=y1, ws=ws1)
                 hm.hm_silu_mul(y1, hbuf)

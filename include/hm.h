@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define HM_ABI_VERSION 1
+#define HM_ABI_VERSION 2
 
 typedef enum hm_status {
   HM_OK = 0,
@@ -62,7 +62,8 @@ typedef enum hm_status {
   HM_ERR_UNSUPPORTED = 4, /* unknown weight format or format/activation pair */
   HM_ERR_WORKSPACE = 5,   /* buffer smaller than its size query */
   HM_ERR_HIP = 6,         /* a HIP launch failed */
-  HM_ERR_ABI = 7          /* descriptor abi field != HM_ABI_VERSION */
+  HM_ERR_ABI = 7,         /* descriptor abi field != HM_ABI_VERSION */
+  HM_ERR_TUNING = 8       /* a tuning field out of range, or a forced kernel that cannot run this call */
 } hm_status;
 
 /* Weight number format (the "number format / scale unit / zero point" of the
@@ -106,6 +107,34 @@ typedef struct hm_wdesc {
   int64_t k;           /* input features, multiple of 128, >= 128 */
 } hm_wdesc;
 
+/* Explicit choices of one GEMM call (the pages' "Tuning Config": tile
+ * shapes, launch shape and split of the work, chosen apart from the layer and
+ * compute description; aihaber.org article, Architecture; ywsung.com note,
+ * section on layout).  Pass NULL, or a zero-initialised struct with abi set,
+ * for the library's default heuristic choice; any nonzero field overrides the
+ * default for that one call (the library keeps no state).  Out-of-range
+ * values, or a forced kernel that cannot run the call, give HM_ERR_TUNING
+ * before any launch.  hm_gemm_plan / hm_moe_gemm_plan report what a given
+ * tuning selects.  Every field has a documented default (0). */
+typedef struct hm_tuning {
+  int32_t abi;             /* HM_ABI_VERSION */
+  int32_t path;            /* dense kernel: 0 default; 1 streaming (M <= 256); 2 128-row tiles
+                              (W4A16 128 x 64 split over K, W4A8 64 x 128); 3 256 x 256 tiles
+                              (not for MX weights with bf16 rows); 4 128 x 128 tiles */
+  int32_t stream_ks;       /* streaming: waves of a block splitting one column set's K: 0, 1, 2, 4 */
+  int32_t stream_nbw;      /* streaming: 16-column blocks per wave: 0, 1, 2 */
+  int32_t stream_splits;   /* dense streaming: K split over blocks (fp32 partials): 0, 1 .. K/128 */
+  int32_t moe_stream_rows; /* rows per grouped streaming unit: 0, 16, 32 */
+  int32_t moe_stream_max;  /* largest expert (rows) taking streaming units: 0, 1 .. 4096 */
+  int32_t moe_stream_nbw;  /* grouped streaming: 16-column blocks per wave: 0, 1, 2 */
+  int32_t moe_stream_ks;   /* grouped streaming: waves splitting K: 0, 1, 2, 4 */
+  int32_t moe_stream_lds_kb; /* grouped streaming: LDS per block in KiB: 0, 20 .. 159 */
+  int32_t moe_big_min;     /* smallest expert remainder that takes a 256-row unit: 0, 1 .. 256;
+                              -1: no 256-row units */
+  int32_t moe_tile;        /* kernel of the up-to-128-row units: 0 default; 1 the 128-row tile
+                              kernel of path 2; 2 the 128 x 128 kernel */
+} hm_tuning;
+
 /* ---------------------------------------------------------------- weights */
 
 /* Bytes of the device weight buffer for `d` (all experts). */
@@ -126,7 +155,10 @@ hm_status hm_transform(const hm_wdesc* d, const uint8_t* codes, const void* scal
                        const uint8_t* zeros, void* w_dev, size_t w_bytes, hipStream_t stream);
 
 /* Exact dequantization of one expert of a transformed buffer into fp32
- * out[N][K] (every restored weight is exactly representable in fp32). */
+ * out[N][K].  Every restored weight is exactly representable in fp32 for the
+ * INT4 formats, and for MXFP4 with E8M0 scale bytes up to 252 (MXINT4: up to
+ * 253); larger bytes give +-inf where the product leaves the fp32 range, and
+ * byte 255 (the E8M0 NaN) gives NaN. */
 hm_status hm_dequant(const hm_wdesc* d, const void* w_dev, size_t w_bytes, int32_t expert,
                      float* out, hipStream_t stream);
 
@@ -141,23 +173,26 @@ hm_status hm_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* x8
 
 /* ---------------------------------------------------------------- dense GEMM */
 
-/* Workspace bytes hm_gemm needs for this shape (may be 0). */
-hm_status hm_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t m, size_t* bytes);
+/* Workspace bytes hm_gemm needs for this shape and tuning (may be 0). */
+hm_status hm_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t m, const hm_tuning* tune,
+                                 size_t* bytes);
 
 /* y[m][n] = bf16( sum_k x_hat[m,k] * w_hat[n,k] ), fp32 accumulation.
  *   w_dev      transformed weights (num_experts must be 1).
  *   x          bf16 [m][k] (HM_A_BF16) or E4M3 bytes [m][k] (HM_A_FP8_ROWSCALE).
- *   x_row_scale fp32 [m] for HM_A_FP8_ROWSCALE, else ignored.
+ *   x_scales   fp32 [m] row scales for HM_A_FP8_ROWSCALE, else ignored.
  *   y          bf16 [m][n].
  *   ws         workspace of at least hm_gemm_workspace_size bytes (NULL if 0).
+ *   tune       NULL for the default choice, else explicit choices (hm_tuning).
  * m = 0 is a no-op. */
 hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* x,
-                  const float* x_row_scale, int64_t m, uint16_t* y, void* ws, size_t ws_bytes,
-                  hipStream_t stream);
+                  const void* x_scales, int64_t m, uint16_t* y, void* ws, size_t ws_bytes,
+                  const hm_tuning* tune, hipStream_t stream);
 
 /* A short text naming the kernel path and tile configuration hm_gemm selects
- * for this shape (so a caller can confirm what actually runs). */
-hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* buf, size_t buf_len);
+ * for this shape and tuning (so a caller can confirm what actually runs). */
+hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, const hm_tuning* tune, char* buf,
+                       size_t buf_len);
 
 /* ------------------------------------------------------------------- MoE */
 
@@ -176,9 +211,9 @@ hm_status hm_moe_sort(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t 
                       int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, void* ws,
                       size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes hm_moe_gemm needs for t tokens and topk. */
+/* Workspace bytes hm_moe_gemm needs for t tokens, topk and the tuning. */
 hm_status hm_moe_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
-                                     size_t* bytes);
+                                     const hm_tuning* tune, size_t* bytes);
 
 /* Grouped GEMM over all experts in one call:
  *   y[p][:] = bf16( A_row(p) . W_hat_{e(p)}^T ) for every routed pair p,
@@ -186,16 +221,26 @@ hm_status hm_moe_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t t,
  *   a            a_rows_are_pairs = 0: activations [t][k] and pair p uses row
  *                p / topk (gate/up projection);  = 1: [t*topk][k] and pair p
  *                uses row p (down projection).  bf16, or E4M3 bytes with
- *                a_row_scale (one fp32 per row of a) for HM_A_FP8_ROWSCALE.
+ *                a_scales (one fp32 per row of a) for HM_A_FP8_ROWSCALE.
  *   offsets, sorted_pairs  as produced by hm_moe_sort (device).
  *   y            bf16 [t*topk][n], rows in pair order; rows of dropped pairs
  *                are not written.
- *   ws           at least hm_moe_gemm_workspace_size bytes.
+ *   ws           at least hm_moe_gemm_workspace_size bytes (the work lists
+ *                of the schedule, written by the call).
+ *   tune         NULL for the default choice, else explicit choices.
+ * Activations of 4 GiB or more run their up-to-128-row units on the 128 x 128
+ * kernel (64-bit row addressing) and take no 256-row units.
  * t = 0 is a no-op. */
 hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* a,
-                      const float* a_row_scale, int32_t a_rows_are_pairs, int64_t t,
+                      const void* a_scales, int32_t a_rows_are_pairs, int64_t t,
                       int32_t topk, const int32_t* offsets, const int32_t* sorted_pairs,
-                      uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
+                      uint16_t* y, void* ws, size_t ws_bytes, const hm_tuning* tune,
+                      hipStream_t stream);
+
+/* A short text naming the unit kinds and kernels hm_moe_gemm schedules for
+ * this call shape and tuning (no device access). */
+hm_status hm_moe_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
+                           int32_t a_rows_are_pairs, const hm_tuning* tune, char* buf, size_t buf_len);
 
 /* ------------------------------------------------------- MoE block steps */
 

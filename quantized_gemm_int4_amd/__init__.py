@@ -16,12 +16,13 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhm.so")
 
-HM_ABI_VERSION = 1
+HM_ABI_VERSION = 2
 HM_W_INT4_SYM, HM_W_UINT4_ZP, HM_W_MXFP4, HM_W_MXINT4 = 0, 1, 2, 3
 HM_A_BF16, HM_A_FP8_ROWSCALE = 0, 1
 WFMT = {"int4_sym": HM_W_INT4_SYM, "uint4_zp": HM_W_UINT4_ZP, "mxfp4": HM_W_MXFP4, "mxint4": HM_W_MXINT4}
 STATUS = {0: "HM_OK", 1: "HM_ERR_NULL", 2: "HM_ERR_SHAPE", 3: "HM_ERR_ALIGN",
-          4: "HM_ERR_UNSUPPORTED", 5: "HM_ERR_WORKSPACE", 6: "HM_ERR_HIP", 7: "HM_ERR_ABI"}
+          4: "HM_ERR_UNSUPPORTED", 5: "HM_ERR_WORKSPACE", 6: "HM_ERR_HIP", 7: "HM_ERR_ABI", 8: "HM_ERR_TUNING"}
+HM_PATH_STREAM, HM_PATH_MID, HM_PATH_BIG, HM_PATH_TILE = 1, 2, 3, 4
 
 
 class HmError(RuntimeError):
@@ -33,6 +34,36 @@ class HmError(RuntimeError):
 class hm_wdesc(ctypes.Structure):
     _fields_ = [("abi", ctypes.c_int32), ("wfmt", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
+
+
+class hm_tuning(ctypes.Structure):
+    _fields_ = [("abi", ctypes.c_int32), ("path", ctypes.c_int32), ("stream_ks", ctypes.c_int32),
+                ("stream_nbw", ctypes.c_int32), ("stream_splits", ctypes.c_int32),
+                ("moe_stream_rows", ctypes.c_int32), ("moe_stream_max", ctypes.c_int32),
+                ("moe_stream_nbw", ctypes.c_int32), ("moe_stream_ks", ctypes.c_int32),
+                ("moe_stream_lds_kb", ctypes.c_int32), ("moe_big_min", ctypes.c_int32),
+                ("moe_tile", ctypes.c_int32)]
+
+
+TUNING_FIELDS = tuple(f for f, _ in hm_tuning._fields_ if f != "abi")
+
+
+def make_tuning(**fields):
+    """Explicit choices of one call (hm_tuning); unnamed fields keep the default."""
+    t = hm_tuning(HM_ABI_VERSION)
+    for k, v in fields.items():
+        if k not in TUNING_FIELDS:
+            raise ValueError(f"unknown tuning field {k}")
+        setattr(t, k, int(v))
+    return t
+
+
+def _tune(t):
+    if t is None:
+        return None
+    if isinstance(t, dict):
+        t = make_tuning(**t)
+    return ctypes.byref(t)
 
 
 def wdesc(wfmt, n, k, num_experts=1):
@@ -49,18 +80,20 @@ def _load():
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     D = ctypes.POINTER(hm_wdesc)
+    T = ctypes.POINTER(hm_tuning)
     sig = {
         "hm_transform_size": [D, ctypes.POINTER(SZ)],
         "hm_transform": [D, P, P, P, P, SZ, P],
         "hm_dequant": [D, P, SZ, I32, P, P],
         "hm_quant_fp8_rows": [P, I64, I64, P, P, P],
-        "hm_gemm_workspace_size": [D, I32, I64, ctypes.POINTER(SZ)],
-        "hm_gemm": [D, P, I32, P, P, I64, P, P, SZ, P],
-        "hm_gemm_plan": [D, I32, I64, ctypes.c_char_p, SZ],
+        "hm_gemm_workspace_size": [D, I32, I64, T, ctypes.POINTER(SZ)],
+        "hm_gemm": [D, P, I32, P, P, I64, P, P, SZ, T, P],
+        "hm_gemm_plan": [D, I32, I64, T, ctypes.c_char_p, SZ],
         "hm_moe_sort_workspace_size": [I64, I32, I32, ctypes.POINTER(SZ)],
         "hm_moe_sort": [P, I64, I32, I32, P, P, P, P, SZ, P],
-        "hm_moe_gemm_workspace_size": [D, I32, I64, I32, ctypes.POINTER(SZ)],
-        "hm_moe_gemm": [D, P, I32, P, P, I32, I64, I32, P, P, P, P, SZ, P],
+        "hm_moe_gemm_workspace_size": [D, I32, I64, I32, T, ctypes.POINTER(SZ)],
+        "hm_moe_gemm": [D, P, I32, P, P, I32, I64, I32, P, P, P, P, SZ, T, P],
+        "hm_moe_gemm_plan": [D, I32, I64, I32, I32, T, ctypes.c_char_p, SZ],
         "hm_silu_mul": [P, I64, I64, P, P],
         "hm_moe_combine": [P, P, I64, I32, I64, P, P],
     }
@@ -150,35 +183,38 @@ def _afmt(x):
     return HM_A_FP8_ROWSCALE if x.dtype == torch.uint8 else HM_A_BF16
 
 
-def hm_gemm_workspace_size(desc, afmt, m):
+def hm_gemm_workspace_size(desc, afmt, m, tuning=None):
     out = ctypes.c_size_t()
     _ok("hm_gemm_workspace_size", lib.hm_gemm_workspace_size(ctypes.byref(desc), int(afmt), int(m),
-                                                             ctypes.byref(out)))
+                                                             _tune(tuning), ctypes.byref(out)))
     return out.value
 
 
-def hm_gemm_plan(desc, afmt, m):
+def hm_gemm_plan(desc, afmt, m, tuning=None):
     buf = ctypes.create_string_buffer(256)
-    _ok("hm_gemm_plan", lib.hm_gemm_plan(ctypes.byref(desc), int(afmt), int(m), buf, 256))
+    _ok("hm_gemm_plan", lib.hm_gemm_plan(ctypes.byref(desc), int(afmt), int(m), _tune(tuning), buf, 256))
     return buf.value.decode()
 
 
-def hm_gemm(desc, w_dev, x, x_row_scale=None, y=None, ws=None, afmt=None, stream=None):
+def hm_gemm(desc, w_dev, x, x_scales=None, y=None, ws=None, afmt=None, tuning=None, stream=None):
     """y[m,n] = x_hat . w_hat^T in bf16.  x: bf16 [m,k] (W4A16, any weight
-    format) or uint8 E4M3 [m,k] with fp32 x_row_scale [m] (W4A8-MXFP4)."""
+    format) or uint8 E4M3 [m,k] with fp32 x_scales [m] (W4A8-MXFP4).
+    tuning: None (default choice), an hm_tuning, or a dict of its fields."""
     afmt = _afmt(x) if afmt is None else afmt
     m = x.shape[0]
     if y is None:
         y = torch.empty(m, desc.n, dtype=torch.bfloat16, device=x.device)
     _need(y, torch.bfloat16, m * desc.n, "y")
+    if isinstance(tuning, dict):
+        tuning = make_tuning(**tuning)
     if ws is None:
         # a caller-provided workspace is passed through as is (the library checks its size)
-        need = hm_gemm_workspace_size(desc, afmt, m)
+        need = hm_gemm_workspace_size(desc, afmt, m, tuning)
         if need:
             ws = torch.empty(need, dtype=torch.uint8, device=x.device)
-    _ok("hm_gemm", lib.hm_gemm(ctypes.byref(desc), _ptr(w_dev), int(afmt), _ptr(x), _ptr(x_row_scale),
+    _ok("hm_gemm", lib.hm_gemm(ctypes.byref(desc), _ptr(w_dev), int(afmt), _ptr(x), _ptr(x_scales),
                                m, _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0,
-                               _stream(stream)))
+                               _tune(tuning), _stream(stream)))
     return y
 
 
@@ -205,29 +241,39 @@ def hm_moe_sort(topk_ids, num_experts, counts=None, offsets=None, sorted_pairs=N
     return counts, offsets, sorted_pairs
 
 
-def hm_moe_gemm_workspace_size(desc, afmt, t, topk):
+def hm_moe_gemm_workspace_size(desc, afmt, t, topk, tuning=None):
     out = ctypes.c_size_t()
-    _ok("hm_moe_gemm_workspace_size", lib.hm_moe_gemm_workspace_size(ctypes.byref(desc), int(afmt),
-                                                                     int(t), int(topk), ctypes.byref(out)))
+    _ok("hm_moe_gemm_workspace_size", lib.hm_moe_gemm_workspace_size(ctypes.byref(desc), int(afmt), int(t),
+                                                                     int(topk), _tune(tuning), ctypes.byref(out)))
     return out.value
 
 
-def hm_moe_gemm(desc, w_dev, a, offsets, sorted_pairs, t, topk, a_rows_are_pairs, a_row_scale=None,
-                y=None, ws=None, afmt=None, stream=None):
+def hm_moe_gemm_plan(desc, afmt, t, topk, a_rows_are_pairs, tuning=None):
+    buf = ctypes.create_string_buffer(512)
+    _ok("hm_moe_gemm_plan", lib.hm_moe_gemm_plan(ctypes.byref(desc), int(afmt), int(t), int(topk),
+                                                 int(a_rows_are_pairs), _tune(tuning), buf, 512))
+    return buf.value.decode()
+
+
+def hm_moe_gemm(desc, w_dev, a, offsets, sorted_pairs, t, topk, a_rows_are_pairs, a_scales=None,
+                y=None, ws=None, afmt=None, tuning=None, stream=None):
     """Grouped GEMM; returns y bf16 [t*topk, n] in pair order.  a: bf16 rows,
-    or E4M3 bytes with fp32 a_row_scale (MXFP4 weights only)."""
+    or E4M3 bytes with fp32 a_scales (MXFP4 weights only).  tuning: None, an
+    hm_tuning, or a dict of its fields."""
     afmt = _afmt(a) if afmt is None else afmt
     P = t * topk
     if y is None:
         y = torch.empty(P, desc.n, dtype=torch.bfloat16, device=a.device)
     _need(y, torch.bfloat16, P * desc.n, "y")
+    if isinstance(tuning, dict):
+        tuning = make_tuning(**tuning)
     if ws is None:
-        need = hm_moe_gemm_workspace_size(desc, afmt, t, topk)
+        need = hm_moe_gemm_workspace_size(desc, afmt, t, topk, tuning)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=a.device)
     _ok("hm_moe_gemm", lib.hm_moe_gemm(ctypes.byref(desc), _ptr(w_dev), int(afmt), _ptr(a),
-                                       _ptr(a_row_scale), int(a_rows_are_pairs), int(t), int(topk),
+                                       _ptr(a_scales), int(a_rows_are_pairs), int(t), int(topk),
                                        _ptr(offsets), _ptr(sorted_pairs), _ptr(y), _ptr(ws),
-                                       ws.numel(), _stream(stream)))
+                                       ws.numel(), _tune(tuning), _stream(stream)))
     return y
 
 

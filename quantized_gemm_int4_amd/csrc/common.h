@@ -110,24 +110,40 @@ __device__ __forceinline__ u32x4_t dq8_u4(uint32_t w, float s, float zs) {
   return r;
 }
 
-// The same eight codes as bf16 values 1 + u/16, exact, in value order: each
-// code is OR-ed into the top four mantissa bits of bf16(1.0), so the constant
-// part of every value (1) is only 16 code steps, which keeps the cancellation
-// in a later subtraction of the zero-point product small.  mask must hold
-// 0x00780078 and bias 0x3F803F80; passing them in registers (not literals)
-// lets each pair compile to a shift and one v_and_or_b32.
-__device__ __forceinline__ u32x4_t raw8_u4(uint32_t w, uint32_t mask, uint32_t bias) {
-  u32x4_t r;
-  r[0] = ((w << 3) & mask) | bias;
-#pragma unroll
-  for (int j = 1; j < 4; ++j) r[j] = ((w >> (4 * j - 3)) & mask) | bias;
+// Eight unsigned codes of one device-layout word (value 2p in nibble p, 2p+1
+// in nibble p+4) minus their zero point z -> eight bf16 of u - z, exact (the
+// integers -15..15), in value order.  zc = 0x80808080 - z * 0x01010101: a
+// byte u + 128 - z lies in 113..143, so the 32-bit add carries across no byte,
+// and the xor with 0x80 leaves the two's complement byte u - z, which a
+// sign-extending byte conversion turns into fp32 (one instruction per value).
+__device__ __forceinline__ u32x4_t dz8_u4(uint32_t w, uint32_t zc) {
+  const uint32_t lo = ((w & 0x0F0F0F0Fu) + zc) ^ 0x80808080u;          // bytes: v0 v4 v1 v5
+  const uint32_t hi = (((w >> 4) & 0x0F0F0F0Fu) + zc) ^ 0x80808080u;   // bytes: v2 v6 v3 v7
+  auto sb = [](uint32_t x, int b) { return (float)(int8_t)(x >> (8 * b)); };
+  return (u32x4_t){pack_bf16(sb(lo, 0), sb(lo, 2)), pack_bf16(sb(hi, 0), sb(hi, 2)),
+                   pack_bf16(sb(lo, 1), sb(lo, 3)), pack_bf16(sb(hi, 1), sb(hi, 3))};
+}
+
+// Low nibble of byte B of x read as a two's complement 4-bit q -> q / 16 in
+// fp32, exactly (gfx9 v_cvt_off_f32_i4 with a byte select).
+template <int B>
+__device__ __forceinline__ float off_i4(uint32_t x) {
+  float r;
+  if (B == 0) __asm__("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(x));
+  if (B == 1) __asm__("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(x));
+  if (B == 2) __asm__("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(x));
+  if (B == 3) __asm__("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(x));
   return r;
 }
 
-// bf16 pair of -(1 + z/16) for a 4-bit zero point z: the A operand that
-// subtracts the zero-point product inside the same MFMA accumulation.
-__device__ __forceinline__ uint32_t neg_raw_u4_pair(uint32_t z) {
-  return (z * 0x00080008u) | 0xBF80BF80u;
+// Eight offset-binary codes q + 8 of one device-layout word (symmetric INT4)
+// -> eight bf16 of q / 16, exact, in value order: the xor with 0x8 per nibble
+// gives the two's complement q, converted nibble by nibble.
+__device__ __forceinline__ u32x4_t dq8_sym16(uint32_t w) {
+  const uint32_t lo = w ^ 0x88888888u;     // nibble p of byte b: value 2p of byte b's low nibble
+  const uint32_t hi = lo >> 4;             // low nibbles: nibbles 1, 3, 5, 7
+  return (u32x4_t){pack_bf16(off_i4<0>(lo), off_i4<2>(lo)), pack_bf16(off_i4<0>(hi), off_i4<2>(hi)),
+                   pack_bf16(off_i4<1>(lo), off_i4<3>(lo)), pack_bf16(off_i4<1>(hi), off_i4<3>(hi))};
 }
 
 // Opaque copies of constants, so the compiler keeps them in registers.

@@ -34,6 +34,7 @@ constexpr int kMoeStreamMaxMx = 16, kMoeStreamNbwMx = 1;
 // up to 128 rows streaming: T = 64 / 1024 / 8192 0.448 / 1.756 / 8.954 ms
 // against 0.463 / 1.826 / 9.018 with 16-row units up to 64 rows
 constexpr int kMoeStreamRowsMxi4 = 32, kMoeStreamMaxMxi4 = 128;
+constexpr int kMoeStreamLdsKb = 79;   // LDS per grouped streaming block (two blocks per CU)
 constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles may be used
 // An expert remainder of at least this many rows gets a 256-row unit (a unit
 // of at most 128 rows runs four of the eight 32-row MFMA blocks) instead of
@@ -45,6 +46,9 @@ constexpr int kGroupedGridStream = 2048;
 constexpr int kGroupedGridTile = 1024;
 constexpr int kGroupedGridMid = 256;     // one 128 x 64 tile block per compute unit (LDS-bound)
 constexpr int kGroupedGridBig = 256;     // one 256-tile block per compute unit (LDS-bound)
+constexpr uint64_t kAddr32 = 1ull << 32; // extent of one 32-bit buffer offset
+
+enum Path : int { P_AUTO = 0, P_STREAM = 1, P_MID = 2, P_BIG = 3, P_TILE = 4 };
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -55,8 +59,9 @@ hm_status check_desc(const hm_wdesc* d) {
     return HM_ERR_UNSUPPORTED;
   const int want_group = is_mx(d->wfmt) ? 32 : 128;
   if (d->group != want_group) return HM_ERR_SHAPE;
-  if (d->num_experts < 1 || d->n < 1 || d->k < 128 || (d->k % 128) != 0) return HM_ERR_SHAPE;
-  if (d->n > (1ll << 24) || d->k > (1ll << 24)) return HM_ERR_SHAPE;
+  if (d->num_experts < 1 || d->num_experts > 512 || d->n < 1 || d->k < 128 || (d->k % 128) != 0)
+    return HM_ERR_SHAPE;
+  if (d->n > (1ll << 24) || d->k > (1ll << 20)) return HM_ERR_SHAPE;
   return HM_OK;
 }
 
@@ -78,16 +83,41 @@ const char* pair_name(const hm_wdesc* d, int32_t afmt) {
 
 Geom geom_of(const hm_wdesc* d) { return make_geom(d->wfmt, d->num_experts, d->n, d->k); }
 
-int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  return (s && *s) ? atoi(s) : dflt;
+// The 128-row and 256-row tile kernels address the scale / zero-point region
+// with 32-bit offsets from its start.
+bool scales_addr32(const Geom& G) { return G.total - G.off_scales < kAddr32; }
+
+// ---------------------------------------------------------------- tuning
+struct Tune {
+  int path, sks, snbw, ssplits, mrows, mmax, mnbw, mks, mlds, mbig, mtile;
+};
+
+bool in_set(int v, std::initializer_list<int> ok) {
+  for (int x : ok)
+    if (v == x) return true;
+  return false;
+}
+
+hm_status read_tuning(const hm_tuning* t, Tune* out) {
+  *out = Tune{};
+  if (!t) return HM_OK;
+  if (t->abi != HM_ABI_VERSION) return HM_ERR_ABI;
+  const bool ok = in_set(t->path, {0, 1, 2, 3, 4}) && in_set(t->stream_ks, {0, 1, 2, 4}) &&
+                  in_set(t->stream_nbw, {0, 1, 2}) && t->stream_splits >= 0 &&
+                  in_set(t->moe_stream_rows, {0, 16, 32}) && t->moe_stream_max >= 0 &&
+                  t->moe_stream_max <= 4096 && in_set(t->moe_stream_nbw, {0, 1, 2}) &&
+                  in_set(t->moe_stream_ks, {0, 1, 2, 4}) &&
+                  (t->moe_stream_lds_kb == 0 || (t->moe_stream_lds_kb >= 20 && t->moe_stream_lds_kb <= 159)) &&
+                  t->moe_big_min >= -1 && t->moe_big_min <= kBigRows && in_set(t->moe_tile, {0, 1, 2});
+  if (!ok) return HM_ERR_TUNING;
+  *out = Tune{t->path, t->stream_ks, t->stream_nbw, t->stream_splits, t->moe_stream_rows, t->moe_stream_max,
+              t->moe_stream_nbw, t->moe_stream_ks, t->moe_stream_lds_kb, t->moe_big_min, t->moe_tile};
+  return HM_OK;
 }
 
 // ---------------------------------------------------------------- dense plan
 struct DensePlan {
-  bool stream;
-  bool big;          // 256 x 256 tiles (large M)
-  bool mid;          // W4A16 128 x 64 tiles with the K groups split over the waves
+  int path;          // P_STREAM, P_MID (128-row tiles), P_BIG (256 x 256), P_TILE (128 x 128)
   StreamCfg sc;
   int ksg;
   size_t ws_bytes;
@@ -102,12 +132,22 @@ bool f4_wide_tiles(const Geom& G, int64_t rows) {
   return mid_rounds >= 8 && tile_rounds < mid_rounds;
 }
 
-DensePlan plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m) {
+// one block per tile of the dense 128-row tile kernels (a 32-bit grid)
+bool mid_grid_fits(const Geom& G, bool a8, int64_t m) {
+  const int64_t tiles_m = a8 ? (m + 63) / 64 : (m + kTileM - 1) / kTileM;
+  const int64_t tiles_n = a8 ? (G.NB + 7) / 8 : mid_n_tiles(G, false);
+  return tiles_n * tiles_m <= 0x7FFFFFFFll;
+}
+
+hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu, DensePlan* out) {
   DensePlan p{};
   const Geom G = geom_of(d);
   const bool f4 = mx_a16(d, afmt);
-  // 1 = streaming, 2 = 128-row tiles, 3 = 256-row tiles, 4 = W4A16 128 x 128 tiles
-  const int force = env_int("HM_FORCE_PATH", 0);
+  const bool a8 = afmt == HM_A_FP8_ROWSCALE;
+  const bool tiles32 = scales_addr32(G);        // 128-row and 256-row kernels can address the scales
+  if (tu.path == P_STREAM && m > kStreamWideRows) return HM_ERR_TUNING;
+  if (tu.path == P_BIG && f4) return HM_ERR_TUNING;  // no 256 x 256 kernel for MX weights with bf16 rows
+  if ((tu.path == P_MID || tu.path == P_BIG) && (!tiles32 || !mid_grid_fits(G, a8, m))) return HM_ERR_TUNING;
   // W4A16 up to 256 rows also streams (in 32-row chunks, each re-reading the
   // weights from the L2) when N is narrow: measured at K = 4096, a streaming
   // launch costs ~8 us + 0.8 ns per (chunk x column) and a round of 128 x 64
@@ -115,51 +155,54 @@ DensePlan plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m) {
   // against 23.4 us; N = 7168, M = 128 stays on tiles: 25.3 against 28.8 us)
   const bool narrow = !is_mx(d->wfmt) && m <= kStreamWideRows &&
                       ((m + kStreamMaxRows - 1) / kStreamMaxRows) * d->n <= kStreamChunkCols;
-  p.stream = (force == 1) || (force == 0 && (m <= kStreamMaxRows || narrow));
-  if (force == 1 && m > kStreamWideRows) p.stream = false;  // forced streaming: up to 256 rows
-  if (!p.stream) {
-    // W4A16: 256 x 256 tiles unless 128 x 64 tiles take fewer rounds of the
-    // chip by the measured cost of a round (one of 256 x 256 tiles ~ 3.8 of
-    // 128 x 64 tiles, N = 1792 / 7168 / 14336, K = 4096): a narrow N (one
-    // rank's column shard, N = 1792, M = 1024: 28 large tiles) runs 3.5x
-    // faster on the smaller tiles
-    const int64_t big_rounds = (big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows) + 255) / 256;
-    const int64_t mid_rounds = (mid_n_tiles(G, false) * ((m + kTileM - 1) / kTileM) + 255) / 256;
-    const bool mid_fewer = !is_mx(d->wfmt) && mid_rounds * 10 < big_rounds * 38;
-    p.big = (force == 3) || (force == 0 && m >= kBigMinRows && !mid_fewer);
-    p.mid = !p.big && force != 4;
+  if (tu.path != P_AUTO) {
+    p.path = tu.path;
+  } else if (m <= kStreamMaxRows || narrow) {
+    p.path = P_STREAM;
+  } else if (f4) {
     // MX weights with bf16 rows (no 256 x 256 kernel): 128 x 64 tiles, or 128 x
     // 128 tiles once the 128 x 64 ones take many rounds of the chip.
     // Measured at N = 7168 K = 2048 / N = 14336 K = 4096: M = 256 / 128 on
     // 128 x 64 tiles 14.9 / 23.9 us against 30.1 / 63.2 (one round each),
     // M = 1024 even (4 / 7 rounds against 2 / 4), M = 4096 147 / 520 us on
     // 128 x 128 tiles against 273 / 1039 (14 / 28 rounds against 7 / 14)
-    if (f4) {
-      p.big = false;
-      p.mid = (force == 2 || force == 3) || (force == 0 && !f4_wide_tiles(G, m));
-    }
-    return p;
+    p.path = f4_wide_tiles(G, m) ? P_TILE : P_MID;
+  } else {
+    // 256 x 256 tiles unless 128 x 64 tiles take fewer rounds of the chip by
+    // the measured cost of a round (one of 256 x 256 tiles ~ 3.8 of 128 x 64
+    // tiles, N = 1792 / 7168 / 14336, K = 4096): a narrow N (one rank's
+    // column shard, N = 1792, M = 1024: 28 large tiles) runs 3.5x faster on
+    // the smaller tiles
+    const int64_t big_rounds = (big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows) + 255) / 256;
+    const int64_t mid_rounds = (mid_n_tiles(G, false) * ((m + kTileM - 1) / kTileM) + 255) / 256;
+    const bool mid_fewer = !is_mx(d->wfmt) && mid_rounds * 10 < big_rounds * 38;
+    p.path = (m >= kBigMinRows && !mid_fewer) ? P_BIG : P_MID;
+  }
+  // kernels with 32-bit offsets fall back to the 128 x 128 kernel (64-bit addressing)
+  if (tu.path == P_AUTO && (p.path == P_MID || p.path == P_BIG) && (!tiles32 || !mid_grid_fits(G, a8, m)))
+    p.path = P_TILE;
+  if (p.path != P_STREAM) {
+    *out = p;
+    return HM_OK;
   }
   p.sc.mb = (m <= 16) ? 1 : 2;
   const int64_t rows = (m < 16 * p.sc.mb) ? m : 16 * p.sc.mb;
   const int64_t m_chunks = (m + 16 * p.sc.mb - 1) / (16 * p.sc.mb);
-  const int64_t gb = (afmt == HM_A_FP8_ROWSCALE) ? 128 : 256;   // activation bytes per row per group
+  const int64_t gb = a8 ? 128 : 256;   // activation bytes per row per group
   // Launch shape: (ks, nbw) from the narrowest block (most waves, least work
   // per wave) to the widest, take the first whose blocks all fit on the chip
   // at once.  A block keeps its activation rows in LDS, so the LDS footprint
   // decides how many blocks share a compute unit (at most 5: the register
   // budget allows 5 waves per SIMD).
-  int ks = env_int("HM_STREAM_KS", 0), nbw = env_int("HM_STREAM_NBW", 0);
+  int ks = tu.sks, nbw = tu.snbw;
   static const int kShapes[6][2] = {{4, 1}, {2, 1}, {4, 2}, {2, 2}, {1, 1}, {1, 2}};
-  if (ks != 1 && ks != 2 && ks != 4) ks = 0;
-  if (nbw != 1 && nbw != 2) nbw = 0;
   if (!ks || !nbw) {
     const int64_t row_bytes = std::min<int64_t>(G.KG * gb + 16, kStreamLdsBytes / rows);
-    int pick = 5;
+    int pick = -1;
     for (int i = 0; i < 6; ++i) {
       const int cks = kShapes[i][0], cnbw = kShapes[i][1];
       if ((ks && cks != ks) || (nbw && cnbw != nbw)) continue;
-      if (G.KG < 2 * cks && cks > 1) continue;                  // >= 2 groups per wave
+      if (G.KG < 2 * cks && cks > 1 && !ks) continue;         // >= 2 groups per wave
       StreamCfg t = p.sc;
       t.ks = cks;
       t.nbw = cnbw;
@@ -169,13 +212,15 @@ DensePlan plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m) {
       pick = i;
       if (blocks <= 256 * per_cu) break;
     }
+    if (pick < 0) pick = 5;
     ks = kShapes[pick][0];
     nbw = kShapes[pick][1];
   }
   p.sc.ks = ks;
   p.sc.nbw = nbw;
   const int64_t n_tiles = stream_n_tiles(G, p.sc);
-  int64_t splits = env_int("HM_STREAM_SPLITS", 0);
+  int64_t splits = tu.ssplits;
+  if (splits > G.KG) return HM_ERR_TUNING;
   if (splits <= 0) {
     // enough waves to keep every SIMD streaming (1024 SIMDs); split K over
     // blocks only below that
@@ -185,51 +230,123 @@ DensePlan plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m) {
   }
   if (splits > G.KG) splits = G.KG;
   if (splits < 1) splits = 1;
+  if (splits > 65535 || n_tiles > 0x7FFFFFFFll) return HM_ERR_SHAPE;
   p.ksg = (int)((G.KG + splits - 1) / splits);
   p.sc.splits = (int)((G.KG + p.ksg - 1) / p.ksg);
   p.ws_bytes = (p.sc.splits > 1) ? (size_t)p.sc.splits * m * G.NB * 16 * sizeof(float) : 0;
-  return p;
+  *out = p;
+  return HM_OK;
 }
 
 // ---------------------------------------------------------------- MoE plan
 struct MoePlan {
   int64_t P, max_s, max_t, max_b;
   size_t off_su, off_tu, off_bu, ws_bytes;
-  int nbw, ks, lds_kb, s_rows, s_max, big_min;
+  int nbw, ks, lds_kb, s_rows, s_max;
+  int big_min;       // 0: no 256-row units
+  int tile;          // kernel of the up-to-128-row units: P_MID or P_TILE
+  bool a64;          // activations of 4 GiB or more (64-bit row addressing only)
 };
 
-MoePlan plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk) {
+// Work-list sizes and workspace layout (independent of the activation size);
+// kernel choices need rows_are_pairs (< 0: sizes only).
+hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int rows_are_pairs,
+                   const Tune& tu, MoePlan* out) {
   MoePlan p{};
   p.P = t * topk;
   const int64_t act = (p.P < d->num_experts) ? p.P : d->num_experts;
   const bool mxi4 = d->wfmt == HM_W_MXINT4;
-  const int rows_dflt = mxi4 ? kMoeStreamRowsMxi4 : kMoeStreamRows;
-  p.s_rows = env_int("HM_MOE_STREAM_ROWS", rows_dflt);
-  if (p.s_rows != 16 && p.s_rows != 32) p.s_rows = rows_dflt;
-  // experts with up to s_max rows stream, as ceil(rows / s_rows) units
-  const bool mx = afmt == HM_A_FP8_ROWSCALE;
-  p.s_max = env_int("HM_MOE_STREAM_MAX", mx ? kMoeStreamMaxMx : (mxi4 ? kMoeStreamMaxMxi4 : kMoeStreamMaxA16));
-  if (p.s_max < p.s_rows) p.s_max = p.s_rows;
+  const bool a8 = afmt == HM_A_FP8_ROWSCALE;
+  const bool f4 = mx_a16(d, afmt);
+  p.s_rows = tu.mrows ? tu.mrows : (mxi4 ? kMoeStreamRowsMxi4 : kMoeStreamRows);
+  p.s_max = tu.mmax ? tu.mmax : (a8 ? kMoeStreamMaxMx : (mxi4 ? kMoeStreamMaxMxi4 : kMoeStreamMaxA16));
+  p.nbw = tu.mnbw ? tu.mnbw : (a8 ? kMoeStreamNbwMx : kMoeStreamNbwA16);
+  p.ks = tu.mks ? tu.mks : 1;
+  p.lds_kb = tu.mlds ? tu.mlds : kMoeStreamLdsKb;
+  // an expert remainder of at least big_min rows takes a 256-row unit
+  const int big_min = tu.mbig > 0 ? tu.mbig : kMoeBigMinRows;
   p.max_s = p.P / p.s_rows + act;
   p.max_t = (p.P + kTileM - 1) / kTileM + act;
-  // an expert remainder of at least big_min rows takes a 256-row unit
-  p.big_min = env_int("HM_MOE_BIG_MIN", kMoeBigMinRows);
-  if (p.big_min < 1 || p.big_min > kBigRows) p.big_min = kMoeBigMinRows;
-  p.max_b = p.P / p.big_min + 1;              // every 256-row unit holds >= big_min rows
+  p.max_b = p.P / big_min + 1;              // every 256-row unit holds >= big_min rows
   p.off_su = 256;
   p.off_tu = align256(p.off_su + (size_t)p.max_s * 16);
   p.off_bu = align256(p.off_tu + (size_t)p.max_t * 16);
   p.ws_bytes = align256(p.off_bu + (size_t)p.max_b * 16);
-  p.nbw = env_int("HM_MOE_STREAM_NBW", mx ? kMoeStreamNbwMx : kMoeStreamNbwA16);
-  if (p.nbw != 1 && p.nbw != 2) p.nbw = mx ? kMoeStreamNbwMx : kMoeStreamNbwA16;
-  p.ks = env_int("HM_MOE_STREAM_KS", 1);
-  if (p.ks != 1 && p.ks != 2 && p.ks != 4) p.ks = 1;
-  // LDS per streaming block: a unit stages up to s_rows rows, so K is walked in
-  // pieces that fit this budget; a smaller budget lets more blocks share a
-  // compute unit
-  p.lds_kb = env_int("HM_MOE_STREAM_LDS_KB", 79);
-  if (p.lds_kb < 20 || p.lds_kb > 159) p.lds_kb = 79;
-  return p;
+  if (rows_are_pairs >= 0) {
+    const Geom G = geom_of(d);
+    const int64_t a_rows = rows_are_pairs ? p.P : t;
+    p.a64 = (uint64_t)a_rows * (uint64_t)d->k * (a8 ? 1u : 2u) >= kAddr32;
+    const bool tiles32 = scales_addr32(G);
+    // 256-row units: not for MX weights with bf16 rows; they address
+    // activation rows and scales with 32-bit offsets
+    const bool big_ok = !f4 && !p.a64 && tiles32;
+    if (tu.mbig > 0 && !big_ok) return HM_ERR_TUNING;
+    p.big_min = (tu.mbig == -1 || !big_ok) ? 0 : big_min;
+    // up-to-128-row units: the 128-row tile kernel (32-bit offsets), or the
+    // 128 x 128 kernel for MX weights with bf16 rows when all pairs in
+    // 128-row units would take many rounds of 128 x 64 tiles (T = 8192:
+    // 7.92 against 8.30 ms)
+    const bool mid_ok = !p.a64 && tiles32;
+    if (tu.mtile == 1 && !mid_ok) return HM_ERR_TUNING;
+    if (tu.mtile == 1) p.tile = P_MID;
+    else if (tu.mtile == 2) p.tile = P_TILE;
+    else p.tile = (mid_ok && !(f4 && f4_wide_tiles(G, p.P))) ? P_MID : P_TILE;
+  }
+  *out = p;
+  return HM_OK;
+}
+
+
+// The launches of one grouped GEMM: the schedule, then the grouped streaming,
+// 128-row and 256-row unit kernels (each a persistent grid over its units).
+hm_status launch_moe(const hm_wdesc* d, int32_t afmt, const void* w_dev, const void* a_in, const void* a_scales,
+                     int32_t a_rows_are_pairs, int64_t t, int32_t topk, const int32_t* offsets,
+                     const int32_t* sorted_pairs, uint16_t* y, uint8_t* w8, const MoePlan& p, hipStream_t stream) {
+  int32_t* hdr = (int32_t*)w8;
+  int32_t* su = (int32_t*)(w8 + p.off_su);
+  int32_t* tu = (int32_t*)(w8 + p.off_tu);
+  int32_t* bu = (int32_t*)(w8 + p.off_bu);
+  GemmArgs a{};
+  a.w = (const uint8_t*)w_dev;
+  a.G = geom_of(d);
+  a.wfmt = d->wfmt;
+  a.a8 = afmt == HM_A_FP8_ROWSCALE;
+  a.x = a_in;
+  a.xs = a.a8 ? (const float*)a_scales : nullptr;
+  a.M = 0;
+  a.y = y;
+  a.hdr = hdr;
+  a.sorted_pairs = sorted_pairs;
+  a.topk = topk;
+  a.rows_are_pairs = a_rows_are_pairs;
+  a.P = p.P;
+  (void)t;
+  hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, p.s_rows, p.s_max, kTileM, p.big_min,
+                                     p.max_s, p.max_t, p.max_b, hdr, su, tu, bu, stream);
+  if (e == hipSuccess) {
+    StreamCfg sc{p.s_rows / 16, p.nbw, 1, p.ks, p.lds_kb};
+    const int64_t nts = stream_n_tiles(a.G, sc);
+    int64_t gi = p.max_s * nts;
+    if (gi > kGroupedGridStream) gi = kGroupedGridStream;
+    a.units = su;
+    if (gi > 0) e = launch_gemm_stream(a, sc, true, (int)gi, stream);
+  }
+  if (e == hipSuccess) {
+    const bool mid = p.tile == P_MID;
+    const int64_t ntt = mid ? mid_n_tiles(a.G, a.a8) : (a.G.NB + 7) / 8;
+    int64_t gi = p.max_t * ntt;
+    const int64_t cap = mid ? kGroupedGridMid : kGroupedGridTile;
+    if (gi > cap) gi = cap;
+    a.units = tu;
+    if (gi > 0) e = mid ? launch_gemm_mid(a, true, (int)gi, stream) : launch_gemm_tile(a, true, (int)gi, stream);
+  }
+  if (e == hipSuccess && p.big_min > 0) {
+    int64_t gi = p.max_b * big_n_tiles(a.G);
+    if (gi > kGroupedGridBig) gi = kGroupedGridBig;
+    a.units = bu;
+    if (gi > 0) e = launch_gemm_big(a, true, (int)gi, stream);
+  }
+  return (e == hipSuccess) ? HM_OK : HM_ERR_HIP;
 }
 
 }  // namespace
@@ -246,6 +363,7 @@ HM_API const char* hm_status_string(hm_status s) {
     case HM_ERR_WORKSPACE: return "workspace too small";
     case HM_ERR_HIP: return "HIP launch failed";
     case HM_ERR_ABI: return "descriptor ABI version mismatch";
+    case HM_ERR_TUNING: return "tuning field out of range, or the forced kernel cannot run this call";
   }
   return "unknown status";
 }
@@ -320,30 +438,42 @@ HM_API hm_status hm_moe_combine(const uint16_t* y, const float* w, int64_t t, in
   return HM_OK;
 }
 
-HM_API hm_status hm_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t m, size_t* bytes) {
+HM_API hm_status hm_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t m, const hm_tuning* tune,
+                                        size_t* bytes) {
   hm_status s = check_desc(d);
   if (s) return s;
   if ((s = check_pair(d, afmt))) return s;
   if (!bytes) return HM_ERR_NULL;
   if (m < 0) return HM_ERR_SHAPE;
-  *bytes = (m == 0) ? 0 : plan_dense(d, afmt, m).ws_bytes;
+  Tune tu;
+  if ((s = read_tuning(tune, &tu))) return s;
+  if (m == 0) {
+    *bytes = 0;
+    return HM_OK;
+  }
+  DensePlan p;
+  if ((s = plan_dense(d, afmt, m, tu, &p))) return s;
+  *bytes = p.ws_bytes;
   return HM_OK;
 }
 
-HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* buf,
+HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, const hm_tuning* tune, char* buf,
                               size_t buf_len) {
   hm_status s = check_desc(d);
   if (s) return s;
   if ((s = check_pair(d, afmt))) return s;
   if (!buf || buf_len == 0) return HM_ERR_NULL;
   if (m < 0) return HM_ERR_SHAPE;
-  const DensePlan p = plan_dense(d, afmt, m);
+  Tune tu;
+  if ((s = read_tuning(tune, &tu))) return s;
+  DensePlan p;
+  if ((s = plan_dense(d, afmt, m > 0 ? m : 1, tu, &p))) return s;
   const char* w = pair_name(d, afmt);
   const bool a8 = afmt == HM_A_FP8_ROWSCALE;
-  if (p.stream)
+  if (p.path == P_STREAM)
     snprintf(buf, buf_len, "%s stream mb=%d nbw=%d ks=%d splits=%d ksg=%d mfma=%s", w, p.sc.mb,
              p.sc.nbw, p.sc.ks, p.sc.splits, p.ksg, a8 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
-  else if (p.big) {
+  else if (p.path == P_BIG) {
     const Geom G = make_geom(d->wfmt, 1, d->n, d->k);
     const int64_t tiles = big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows);
     const int64_t halves = 2 * (tiles - big_full_tiles(G, m, d->wfmt == HM_W_MXFP4));
@@ -351,9 +481,9 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* 
              d->wfmt == HM_W_MXFP4 ? "4x2" : "1x4", d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "32x32x16_bf16",
              (long long)halves);
   }
-  else if (p.mid && a8)
+  else if (p.path == P_MID && a8)
     snprintf(buf, buf_len, "%s tile 64x128 waves=2x2 mfma=scale_16x16x128_f8f6f4", w);
-  else if (p.mid)
+  else if (p.path == P_MID)
     snprintf(buf, buf_len, "%s tile 128x64 waves=4 (K split) mfma=32x32x16_bf16", w);
   else
     snprintf(buf, buf_len, "%s tile %dx%d waves=2x2 mfma=%s", w, kTileM, kTileN,
@@ -362,19 +492,22 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, char* 
 }
 
 HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* x,
-                         const float* x_row_scale, int64_t m, uint16_t* y, void* ws,
-                         size_t ws_bytes, hipStream_t stream) {
+                         const void* x_scales, int64_t m, uint16_t* y, void* ws, size_t ws_bytes,
+                         const hm_tuning* tune, hipStream_t stream) {
   hm_status s = check_desc(d);
   if (s) return s;
   if ((s = check_pair(d, afmt))) return s;
   if (d->num_experts != 1) return HM_ERR_SHAPE;
   if (m < 0 || m > 65535ll * kTileM) return HM_ERR_SHAPE;
+  Tune tu;
+  if ((s = read_tuning(tune, &tu))) return s;
   if (m == 0) return HM_OK;
   if (!w_dev || !x || !y) return HM_ERR_NULL;
-  if (afmt == HM_A_FP8_ROWSCALE && !x_row_scale) return HM_ERR_NULL;
+  if (afmt == HM_A_FP8_ROWSCALE && !x_scales) return HM_ERR_NULL;
   if (!aligned(w_dev, 256) || !aligned(x, 16) || !aligned(y, 16)) return HM_ERR_ALIGN;
-  if (x_row_scale && !aligned(x_row_scale, 4)) return HM_ERR_ALIGN;
-  const DensePlan p = plan_dense(d, afmt, m);
+  if (x_scales && !aligned(x_scales, 4)) return HM_ERR_ALIGN;
+  DensePlan p;
+  if ((s = plan_dense(d, afmt, m, tu, &p))) return s;
   if (p.ws_bytes) {
     if (!ws) return HM_ERR_NULL;
     if (ws_bytes < p.ws_bytes) return HM_ERR_WORKSPACE;
@@ -386,18 +519,18 @@ HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, con
   a.wfmt = d->wfmt;
   a.a8 = afmt == HM_A_FP8_ROWSCALE;
   a.x = x;
-  a.xs = (afmt == HM_A_FP8_ROWSCALE) ? x_row_scale : nullptr;
+  a.xs = (afmt == HM_A_FP8_ROWSCALE) ? (const float*)x_scales : nullptr;
   a.M = m;
   a.y = y;
   hipError_t e;
-  if (p.stream) {
+  if (p.path == P_STREAM) {
     a.part = (p.sc.splits > 1) ? (float*)ws : nullptr;
     a.ksg = p.ksg;
     e = launch_gemm_stream(a, p.sc, false, 0, stream);
     if (e == hipSuccess && p.sc.splits > 1) e = launch_splitk_reduce(a, p.sc.splits, stream);
   } else {
-    e = p.big ? launch_gemm_big(a, false, 0, stream)
-              : (p.mid ? launch_gemm_mid(a, false, 0, stream) : launch_gemm_tile(a, false, 0, stream));
+    e = p.path == P_BIG ? launch_gemm_big(a, false, 0, stream)
+        : (p.path == P_MID ? launch_gemm_mid(a, false, 0, stream) : launch_gemm_tile(a, false, 0, stream));
   }
   return (e == hipSuccess) ? HM_OK : HM_ERR_HIP;
 }
@@ -429,91 +562,71 @@ HM_API hm_status hm_moe_sort(const int32_t* topk_ids, int64_t t, int32_t topk, i
   return HM_OK;
 }
 
-HM_API hm_status hm_moe_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
-                                            size_t* bytes) {
+// Common checks of the grouped GEMM's size query, plan and call.
+static hm_status moe_common(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, const hm_tuning* tune,
+                            Tune* tu) {
   hm_status s = check_desc(d);
   if (s) return s;
   if ((s = check_pair(d, afmt))) return s;
+  if (t < 0 || topk < 1 || topk > d->num_experts) return HM_ERR_SHAPE;
+  if (t * (int64_t)topk >= (1ll << 31)) return HM_ERR_SHAPE;
+  return read_tuning(tune, tu);
+}
+
+HM_API hm_status hm_moe_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
+                                            const hm_tuning* tune, size_t* bytes) {
+  Tune tu;
+  hm_status s = moe_common(d, afmt, t, topk, tune, &tu);
+  if (s) return s;
   if (!bytes) return HM_ERR_NULL;
-  if (t < 0 || topk < 1 || topk > d->num_experts || d->num_experts > 512) return HM_ERR_SHAPE;
-  *bytes = plan_moe(d, afmt, t, topk).ws_bytes;
+  MoePlan p;
+  if ((s = plan_moe(d, afmt, t, topk, -1, tu, &p))) return s;
+  *bytes = p.ws_bytes;
+  return HM_OK;
+}
+
+HM_API hm_status hm_moe_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
+                                  int32_t a_rows_are_pairs, const hm_tuning* tune, char* buf, size_t buf_len) {
+  Tune tu;
+  hm_status s = moe_common(d, afmt, t, topk, tune, &tu);
+  if (s) return s;
+  if (a_rows_are_pairs != 0 && a_rows_are_pairs != 1) return HM_ERR_SHAPE;
+  if (!buf || buf_len == 0) return HM_ERR_NULL;
+  MoePlan p;
+  if ((s = plan_moe(d, afmt, t, topk, a_rows_are_pairs, tu, &p))) return s;
+  const bool a8 = afmt == HM_A_FP8_ROWSCALE;
+  const char* tile = p.tile == P_TILE ? "k_gemm_tile 128x128"
+                     : (a8 ? "k_gemm_mid_mx 64x128" : "k_gemm_mid 128x64");
+  char big[64];
+  if (p.big_min > 0) snprintf(big, sizeof big, "k_gemm_big from %d rows", p.big_min);
+  else snprintf(big, sizeof big, "none");
+  snprintf(buf, buf_len,
+           "%s moe stream(rows=%d max=%d nbw=%d ks=%d lds=%dKiB)=k_gemm_stream tile(<=128 rows)=%s "
+           "big(256 rows)=%s%s ws=%zu",
+           pair_name(d, afmt), p.s_rows, p.s_max, p.nbw, p.ks, p.lds_kb, tile, big,
+           p.a64 ? " activations>=4GiB" : "", p.ws_bytes);
   return HM_OK;
 }
 
 HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* a_in,
-                             const float* a_row_scale, int32_t a_rows_are_pairs, int64_t t,
+                             const void* a_scales, int32_t a_rows_are_pairs, int64_t t,
                              int32_t topk, const int32_t* offsets, const int32_t* sorted_pairs,
-                             uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
-  hm_status s = check_desc(d);
+                             uint16_t* y, void* ws, size_t ws_bytes, const hm_tuning* tune,
+                             hipStream_t stream) {
+  Tune tu;
+  hm_status s = moe_common(d, afmt, t, topk, tune, &tu);
   if (s) return s;
-  if ((s = check_pair(d, afmt))) return s;
-  if (t < 0 || topk < 1 || topk > d->num_experts || d->num_experts > 512) return HM_ERR_SHAPE;
-  if (t * (int64_t)topk >= (1ll << 31)) return HM_ERR_SHAPE;
   if (a_rows_are_pairs != 0 && a_rows_are_pairs != 1) return HM_ERR_SHAPE;
   if (t == 0) return HM_OK;
   if (!w_dev || !a_in || !offsets || !sorted_pairs || !y || !ws) return HM_ERR_NULL;
-  if (afmt == HM_A_FP8_ROWSCALE && !a_row_scale) return HM_ERR_NULL;
+  if (afmt == HM_A_FP8_ROWSCALE && !a_scales) return HM_ERR_NULL;
   if (!aligned(w_dev, 256) || !aligned(a_in, 16) || !aligned(y, 16) || !aligned(ws, 256) ||
       !aligned(offsets, 4) || !aligned(sorted_pairs, 4))
     return HM_ERR_ALIGN;
-  if (a_row_scale && !aligned(a_row_scale, 4)) return HM_ERR_ALIGN;
-  const MoePlan p = plan_moe(d, afmt, t, topk);
+  if (a_scales && !aligned(a_scales, 4)) return HM_ERR_ALIGN;
+  MoePlan p;
+  if ((s = plan_moe(d, afmt, t, topk, a_rows_are_pairs, tu, &p))) return s;
   if (ws_bytes < p.ws_bytes) return HM_ERR_WORKSPACE;
-
-  uint8_t* w8 = (uint8_t*)ws;
-  int32_t* hdr = (int32_t*)w8;
-  int32_t* su = (int32_t*)(w8 + p.off_su);
-  int32_t* tu = (int32_t*)(w8 + p.off_tu);
-  int32_t* bu = (int32_t*)(w8 + p.off_bu);
-  GemmArgs a{};
-  a.w = (const uint8_t*)w_dev;
-  a.G = geom_of(d);
-  a.wfmt = d->wfmt;
-  a.a8 = afmt == HM_A_FP8_ROWSCALE;
-  a.x = a_in;
-  a.xs = (afmt == HM_A_FP8_ROWSCALE) ? a_row_scale : nullptr;
-  a.M = 0;
-  a.y = y;
-  a.hdr = hdr;
-  a.sorted_pairs = sorted_pairs;
-  a.topk = topk;
-  a.rows_are_pairs = a_rows_are_pairs;
-
-  a.P = p.P;
-  // 256-row units address activation rows with 32-bit byte offsets
-  const int64_t a_bytes = (a_rows_are_pairs ? p.P : t) * d->k * (afmt == HM_A_FP8_ROWSCALE ? 1 : 2);
-  const bool f4 = mx_a16(d, afmt);   // MX weights with bf16 rows: streaming and 128-row units only
-  const int big_min = (!f4 && a_bytes < (1ll << 32) && env_int("HM_MOE_BIG", 1)) ? p.big_min : 0;
-  hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, p.s_rows, p.s_max, kTileM, big_min,
-                                     p.max_s, p.max_t, p.max_b, hdr, su, tu, bu, stream);
-  if (e == hipSuccess) {
-    StreamCfg sc{p.s_rows / 16, p.nbw, 1, p.ks, p.lds_kb};
-    const int64_t nts = stream_n_tiles(a.G, sc);
-    int64_t gi = p.max_s * nts;
-    if (gi > kGroupedGridStream) gi = kGroupedGridStream;
-    a.units = su;
-    if (gi > 0) e = launch_gemm_stream(a, sc, true, (int)gi, stream);
-  }
-  if (e == hipSuccess) {
-    // units of up to 128 rows: W4A16 on 128 x 64 tiles, W4A8 on 64 x 128
-    // tiles (one block per compute unit, LDS-bound); HM_MOE_MID=0 keeps
-    // them on the 128 x 128 kernel
-    // MX weights with bf16 rows: the 128 x 128 kernel when all pairs in 128-row
-    // units would take many rounds of 128 x 64 tiles (T = 8192: 7.92 against
-    // 8.30 ms)
-    const bool mid = env_int("HM_MOE_MID", 1) != 0 && !(f4 && f4_wide_tiles(a.G, p.P));
-    const int64_t ntt = mid ? mid_n_tiles(a.G, afmt == HM_A_FP8_ROWSCALE) : (a.G.NB + 7) / 8;
-    int64_t gi = p.max_t * ntt;
-    const int64_t cap = mid ? kGroupedGridMid : kGroupedGridTile;
-    if (gi > cap) gi = cap;
-    a.units = tu;
-    if (gi > 0) e = mid ? launch_gemm_mid(a, true, (int)gi, stream) : launch_gemm_tile(a, true, (int)gi, stream);
-  }
-  if (e == hipSuccess && big_min > 0) {
-    int64_t gi = p.max_b * big_n_tiles(a.G);
-    if (gi > kGroupedGridBig) gi = kGroupedGridBig;
-    a.units = bu;
-    if (gi > 0) e = launch_gemm_big(a, true, (int)gi, stream);
-  }
-  return (e == hipSuccess) ? HM_OK : HM_ERR_HIP;
+  return launch_moe(d, afmt, w_dev, a_in, a_scales, a_rows_are_pairs, t, topk, offsets, sorted_pairs, y,
+                    (uint8_t*)ws, p, stream);
 }

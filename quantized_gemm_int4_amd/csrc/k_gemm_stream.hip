@@ -76,8 +76,6 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
   const int64_t xrow_bytes = MX ? K : 2 * K;
   const uint8_t* sbase = a.w + G.off_scales;
   const uint8_t* zbase = a.w + G.off_zeros;
-  // register-held constants of the raw-code conversion (see raw8_u4)
-  const uint32_t cmask = in_vgpr(0x00780078u), cbias = in_sgpr(0x3F803F80u);
   const uint32_t zshift = 4u * (uint32_t)(n_l & 7);
 
   const int64_t n_items = GROUPED ? (int64_t)a.hdr[0] * n_tiles : 1;
@@ -259,16 +257,17 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
             }
           }
         } else {
-          // Raw codes: one MFMA chain adds x * (1 + u/16) and x * -(1 + z/16)
-          // per K step, i.e. x * (u - z) / 16, exactly 0 where every code
-          // equals the zero point; the group scale of each output row is
-          // applied once to the chain's result, the factor 16 at the end.
-          u32x4_t bz[ZP ? NBW : 1];
+          // INT4 codes enter the MFMA exactly: u - z (zero-point format) or
+          // q / 16 (symmetric), so the per-group chain holds sum x (u - z)
+          // (or sum x q / 16) with fp32 rounding relative to sum |x w|; the
+          // group scale of each of the lane's four output rows multiplies
+          // the chain's result once, and the symmetric factor 16 is applied
+          // in the epilogue (exact).
+          uint32_t zc[ZP ? NBW : 1];
 #pragma unroll
           for (int j = 0; j < (ZP ? NBW : 1); ++j) {
             const uint32_t z = ZP ? ((wzr[ZP ? d : 0][ZP ? j : 0] >> zshift) & 0xFu) : 8u;
-            const uint32_t pz = neg_raw_u4_pair(z);
-            bz[j] = (u32x4_t){pz, pz, pz, pz};
+            zc[j] = 0x80808080u - z * 0x01010101u;
           }
           f32x4_t t[NBW][MB];
 #pragma unroll
@@ -278,12 +277,10 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
             for (int rb = 0; rb < MB; ++rb) af[rb] = ld16(xg + lrow[rb] * xb + (32 * kk + 8 * q_l) * 2);
 #pragma unroll
             for (int j = 0; j < NBW; ++j) {
-              const u32x4_t bw = raw8_u4(wq[d][j][kk], cmask, cbias);
+              const u32x4_t bw = ZP ? dz8_u4(wq[d][j][kk], zc[ZP ? j : 0]) : dq8_sym16(wq[d][j][kk]);
 #pragma unroll
-              for (int rb = 0; rb < MB; ++rb) {
+              for (int rb = 0; rb < MB; ++rb)
                 t[j][rb] = mfma_bf16(bw, af[rb], kk == 0 ? (f32x4_t){0.f, 0.f, 0.f, 0.f} : t[j][rb]);
-                t[j][rb] = mfma_bf16(bz[ZP ? j : 0], af[rb], t[j][rb]);
-              }
             }
           }
 #pragma unroll
@@ -362,7 +359,7 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
           const int rl = rb * 16 + n_l;
           if (rl >= rcount || orow_s[rl] < 0) continue;
           f32x4_t v = acc[j][rb];
-          if (MODE == KM_INT4_A16) v = v * 16.f;   // raw-code sums carry a factor 1/16 (exact)
+          if (MODE == KM_INT4_A16 && !ZP) v = v * 16.f;   // symmetric sums carry a factor 1/16 (exact)
           if (partial) {
             float* dst = a.part + ((int64_t)split * a.M + m0 + rl) * Np + n;
             st16(dst, __builtin_bit_cast(u32x4_t, v));

@@ -127,8 +127,8 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
 }
 
 __device__ __forceinline__ float e8m0_value(uint32_t b) {
-  // 2^(b-127); b = 0 is the fp32 subnormal 2^-127; b = 255 (NaN) is passed through.
-  return (b == 0) ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
+  // 2^(b-127); b = 0 is the fp32 subnormal 2^-127; b = 255 is the format's NaN.
+  return (b == 0) ? __uint_as_float(0x00400000u) : (b == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(b << 23));
 }
 
 // Exact dequantization of expert `e`: one thread per 8 consecutive K-values.

@@ -77,3 +77,38 @@ def random_std_format(fmt, num_experts, n, k, seed=0):
         zeros = r.integers(0, 16, size=(num_experts, n, k // 128), dtype=np.uint8) \
             if fmt == "uint4_zp" else None
     return codes, scales, zeros
+
+
+def activations_dev(seed, m, k, device="cuda", outliers=0.0, outlier_scale=20.0):
+    """Device-side draw of bf16 [m, k] activations for large runs: N(0,1) from
+    torch's seeded generator on the device, optionally times `outlier_scale`
+    where a Bernoulli(`outliers`) mask fires, rounded to bf16 by torch.
+    Returns the device tensor; any row can be copied back to the host."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn((m, k), generator=g, device=device, dtype=torch.float32)
+    if outliers > 0:
+        mask = torch.rand((m, k), generator=g, device=device) < outliers
+        x = torch.where(mask, x * outlier_scale, x)
+    return x.to(torch.bfloat16)
+
+
+def random_std_format_dev(fmt, num_experts, n, k, seed, device="cuda"):
+    """Device-side random standard-format weights (codes, scales, zeros) with
+    the value ranges of random_std_format; MX formats take E8M0 bytes in
+    118..121.  Returns device tensors (scales of the INT4 formats as int16
+    bf16 patterns)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    codes = torch.randint(0, 256, (num_experts, n, k // 2), dtype=torch.uint8, device=device, generator=g)
+    if fmt in ("mxfp4", "mxint4"):
+        scales = torch.randint(118, 122, (num_experts, n, k // 32), dtype=torch.uint8, device=device, generator=g)
+        zeros = None
+    else:
+        scales = (0x3B00 + torch.randint(0, 0x100, (num_experts, n, k // 128), device=device,
+                                         generator=g)).to(torch.int16)
+        zeros = (torch.randint(0, 16, (num_experts, n, k // 128), dtype=torch.uint8, device=device, generator=g)
+                 if fmt == "uint4_zp" else None)
+    return codes, scales, zeros

@@ -54,22 +54,3 @@ def xhat_of(fmt, x_bits):
         return quant.fp8_rows_dequant(c, s)
     return codecs.bf16_value(x_bits).astype(np.float64)
 
-
-def raw_code_bound(x, scale_bits, group=128):
-    """Extra error bound of the streaming INT4 path, in units of the acceptance
-    rule's bound (which is multiplied by gemm.ELEM_TOL).
-
-    That path multiplies codes encoded as bf16 1 + u/16 (each below 2 in
-    magnitude) and, separately, 1 + z/16, in fp32 MFMA chains of 128 products per
-    group, then subtracts the two, scales by 16 (exact) and by the group scale.
-    With first-order fp32 summation error at most 128 * 2**-24 * sum|terms| per
-    chain, one group contributes at most 16 * 2 * 128 * 2**-24 * 2 * |s| * sum|x|
-    = 2**-11 * |s| * sum_{k in group} |x_k|.
-
-    x: fp64 [M, K] activation values; scale_bits: uint16 bf16 scales [N, K/group].
-    Returns [M, N] (already divided by ELEM_TOL)."""
-    from oracle import gemm
-    s = np.abs(codecs.bf16_value(np.asarray(scale_bits, dtype=np.uint16)).astype(np.float64))
-    m, k = x.shape
-    xa = np.abs(x).reshape(m, k // group, group).sum(axis=2)           # [M, K/group]
-    return (2.0 ** -11 / gemm.ELEM_TOL) * (xa @ s.T)

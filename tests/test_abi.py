@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         s = hm.lib.hm_status_string(code)
         assert s and s.decode() != "unknown status"
     assert hm.lib.hm_status_string(99).decode() == "unknown status"
@@ -72,21 +72,21 @@ def test_gemm_argument_checks():
     good = P(0x100000)          # aligned fake addresses: never dereferenced, calls return first
     odd = P(0x100008)
     # wrong activation format for the weight format
-    assert _err("hm_gemm", ctypes.byref(d), good, 1, good, good, 4, good, None, 0, None) == 4
+    assert _err("hm_gemm", ctypes.byref(d), good, 1, good, good, 4, good, None, 0, None, None) == 4
     # m = 0 is a no-op even with null pointers
-    assert _err("hm_gemm", ctypes.byref(d), None, 0, None, None, 0, None, None, 0, None) == 0
-    assert _err("hm_gemm", ctypes.byref(d), None, 0, good, None, 4, good, None, 0, None) == 1
-    assert _err("hm_gemm", ctypes.byref(d), good, 0, good, None, -1, good, None, 0, None) == 2
-    assert _err("hm_gemm", ctypes.byref(d), odd, 0, good, None, 4, good, None, 0, None) == 3
+    assert _err("hm_gemm", ctypes.byref(d), None, 0, None, None, 0, None, None, 0, None, None) == 0
+    assert _err("hm_gemm", ctypes.byref(d), None, 0, good, None, 4, good, None, 0, None, None) == 1
+    assert _err("hm_gemm", ctypes.byref(d), good, 0, good, None, -1, good, None, 0, None, None) == 2
+    assert _err("hm_gemm", ctypes.byref(d), odd, 0, good, None, 4, good, None, 0, None, None) == 3
     # the streaming path at M=1 needs a split-K workspace
     need = hm.hm_gemm_workspace_size(d, 0, 1)
     assert need > 0
-    assert _err("hm_gemm", ctypes.byref(d), good, 0, good, None, 1, good, None, 0, None) == 1
-    assert _err("hm_gemm", ctypes.byref(d), good, 0, good, None, 1, good, good, need - 1, None) == 5
+    assert _err("hm_gemm", ctypes.byref(d), good, 0, good, None, 1, good, None, 0, None, None) == 1
+    assert _err("hm_gemm", ctypes.byref(d), good, 0, good, None, 1, good, good, need - 1, None, None) == 5
     mx = hm.wdesc("mxfp4", 256, 512)
-    assert _err("hm_gemm", ctypes.byref(mx), good, 1, good, None, 4, good, None, 0, None) == 1
+    assert _err("hm_gemm", ctypes.byref(mx), good, 1, good, None, 4, good, None, 0, None, None) == 1
     moe = hm.wdesc("int4_sym", 256, 512, 4)
-    assert _err("hm_gemm", ctypes.byref(moe), good, 0, good, None, 4, good, None, 0, None) == 2
+    assert _err("hm_gemm", ctypes.byref(moe), good, 0, good, None, 4, good, None, 0, None, None) == 2
 
 
 def test_plan_strings():
@@ -101,7 +101,6 @@ def test_mxfp4_bf16_rows_plans():
     """MXFP4 weights take bf16 rows too: the streaming kernel for few rows,
     the 128 x 64 kernel above (128 x 128 when forced; bf16 MFMA); FP8 rows
     keep the W4A8 kernels; INT4 weights reject FP8 rows."""
-    import os
     mx = hm.wdesc("mxfp4", 7168, 2048)
     for m in (1, 16, 32):
         p = hm.hm_gemm_plan(mx, hm.HM_A_BF16, m)
@@ -112,40 +111,33 @@ def test_mxfp4_bf16_rows_plans():
     # 14 rounds of 128 x 64 tiles against 7 of 128 x 128
     p = hm.hm_gemm_plan(mx, hm.HM_A_BF16, 4096)
     assert p.startswith("w4a16-mxfp4 tile 128x128") and p.endswith("16x16x32_bf16"), p
-    os.environ["HM_FORCE_PATH"] = "4"
-    try:
-        p = hm.hm_gemm_plan(mx, hm.HM_A_BF16, 256)
-        assert p.startswith("w4a16-mxfp4 tile 128x128") and p.endswith("16x16x32_bf16"), p
-        os.environ["HM_FORCE_PATH"] = "3"      # no 256 x 256 kernel for this pair
-        assert "128x64" in hm.hm_gemm_plan(mx, hm.HM_A_BF16, 4096)
-    finally:
-        os.environ.pop("HM_FORCE_PATH", None)
+    p = hm.hm_gemm_plan(mx, hm.HM_A_BF16, 256, dict(path=4))
+    assert p.startswith("w4a16-mxfp4 tile 128x128") and p.endswith("16x16x32_bf16"), p
+    assert "128x64" in hm.hm_gemm_plan(mx, hm.HM_A_BF16, 4096, dict(path=2))
+    with pytest.raises(hm.HmError) as e:             # no 256 x 256 kernel for this pair
+        hm.hm_gemm_plan(mx, hm.HM_A_BF16, 4096, dict(path=3))
+    assert e.value.code == 8
     assert hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, 4096).startswith("w4a8-mxfp4 tile 256x256")
     assert hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, 1).startswith("w4a8-mxfp4 stream")
     sz = ctypes.c_size_t()
     i4 = hm.wdesc("int4_sym", 256, 512)
-    assert _err("hm_gemm_workspace_size", ctypes.byref(i4), 1, 4, ctypes.byref(sz)) == 4
+    assert _err("hm_gemm_workspace_size", ctypes.byref(i4), 1, 4, None, ctypes.byref(sz)) == 4
     moe = hm.wdesc("mxfp4", 4096, 7168, 256)
-    assert _err("hm_moe_gemm_workspace_size", ctypes.byref(moe), 0, 64, 8, ctypes.byref(sz)) == 0
+    assert _err("hm_moe_gemm_workspace_size", ctypes.byref(moe), 0, 64, 8, None, ctypes.byref(sz)) == 0
     assert sz.value > 0
 
 
 def test_mxint4_pairs_and_plans():
     """MXINT4 (group 32) takes bf16 rows only, on the same kernels as MXFP4 with bf16 rows."""
-    import os
     sz = ctypes.c_size_t()
     d = hm.wdesc("mxint4", 7168, 2048)
     bad = hm.wdesc("mxint4", 7168, 2048); bad.group = 128
     assert _err("hm_transform_size", ctypes.byref(bad), ctypes.byref(sz)) == 2
-    assert _err("hm_gemm_workspace_size", ctypes.byref(d), 1, 16, ctypes.byref(sz)) == 4
+    assert _err("hm_gemm_workspace_size", ctypes.byref(d), 1, 16, None, ctypes.byref(sz)) == 4
     assert hm.hm_gemm_plan(d, hm.HM_A_BF16, 16).startswith("w4a16-mxint4 stream")
     assert hm.hm_gemm_plan(d, hm.HM_A_BF16, 256).startswith("w4a16-mxint4 tile 128x64")
     assert hm.hm_gemm_plan(d, hm.HM_A_BF16, 4096).startswith("w4a16-mxint4 tile 128x128")
-    os.environ["HM_FORCE_PATH"] = "3"
-    try:
-        assert "128x64" in hm.hm_gemm_plan(d, hm.HM_A_BF16, 4096)
-    finally:
-        os.environ.pop("HM_FORCE_PATH", None)
+    assert "128x64" in hm.hm_gemm_plan(d, hm.HM_A_BF16, 4096, dict(path=2))
 
 
 def test_moe_argument_checks():
@@ -160,11 +152,11 @@ def test_moe_argument_checks():
     need = hm.hm_moe_gemm_workspace_size(d, 0, 64, 8)
     assert need > 0
     args = (ctypes.byref(d), good, 0, good, None, 0, 64, 8, good, good, good, good)
-    assert _err("hm_moe_gemm", *args, need - 1, None) == 5
+    assert _err("hm_moe_gemm", *args, need - 1, None, None) == 5
     assert _err("hm_moe_gemm", ctypes.byref(d), good, 0, good, None, 2, 64, 8, good, good, good,
-                good, need, None) == 2
+                good, need, None, None) == 2
     assert _err("hm_moe_gemm", ctypes.byref(d), good, 0, good, None, 0, 64, 8, None, good, good,
-                good, need, None) == 1
+                good, need, None, None) == 1
 
 
 def test_moe_block_argument_checks():
@@ -205,3 +197,69 @@ def test_tile_kernel_choice_by_rounds():
             assert "256x256" in hm.hm_gemm_plan(d, 0, m)
     assert "128x64" in hm.hm_gemm_plan(full, 0, 511)
     assert "half_tiles=256" in hm.hm_gemm_plan(full, 0, 4096)
+
+
+def test_tuning_validation():
+    """Explicit tuning: out-of-range fields and forced kernels that cannot run
+    the call give HM_ERR_TUNING (8) before any launch; a wrong abi gives
+    HM_ERR_ABI; the plan reports what a tuning selects."""
+    d = hm.wdesc("uint4_zp", 14336, 4096)
+    sz = ctypes.c_size_t()
+    for bad in (dict(path=5), dict(stream_ks=3), dict(stream_nbw=4), dict(stream_splits=-1),
+                dict(moe_stream_rows=8), dict(moe_stream_max=5000), dict(moe_stream_lds_kb=10),
+                dict(moe_big_min=300), dict(moe_tile=3)):
+        t = hm.make_tuning(**bad)
+        assert _err("hm_gemm_workspace_size", ctypes.byref(d), 0, 16, ctypes.byref(t), ctypes.byref(sz)) == 8, bad
+    t = hm.make_tuning()
+    t.abi = 1
+    assert _err("hm_gemm_workspace_size", ctypes.byref(d), 0, 16, ctypes.byref(t), ctypes.byref(sz)) == 7
+    # streaming is for at most 256 rows; K splits at most K / 128
+    assert _err("hm_gemm_workspace_size", ctypes.byref(d), 0, 257, ctypes.byref(hm.make_tuning(path=1)),
+                ctypes.byref(sz)) == 8
+    assert _err("hm_gemm_workspace_size", ctypes.byref(d), 0, 16, ctypes.byref(hm.make_tuning(stream_splits=33)),
+                ctypes.byref(sz)) == 8
+    p = hm.hm_gemm_plan(d, 0, 16, dict(stream_ks=4, stream_nbw=1, stream_splits=4))
+    assert "ks=4" in p and "nbw=1" in p and "splits=4" in p, p
+    assert hm.hm_gemm_workspace_size(d, 0, 16, dict(stream_splits=4)) == 4 * 16 * 14336 * 4
+    assert hm.hm_gemm_workspace_size(d, 0, 16, dict(stream_splits=1)) == 0
+    for path, tag in ((1, " stream "), (2, "128x64"), (3, "256x256"), (4, "128x128")):
+        assert tag in hm.hm_gemm_plan(d, 0, 200, dict(path=path))
+    # an all-zero tuning is the default choice
+    for m in (1, 16, 128, 1024, 4096):
+        assert hm.hm_gemm_plan(d, 0, m, hm.make_tuning()) == hm.hm_gemm_plan(d, 0, m)
+
+
+def test_moe_plan_and_large_activation_guard():
+    """The grouped GEMM's unit kinds, and the guard for activations of 4 GiB
+    or more: the 128-row tile kernels and the 256-row kernel address
+    activation rows with 32-bit offsets, so such calls schedule their
+    up-to-128-row units on the 128 x 128 kernel (64-bit row addressing) and
+    take no 256-row units; forcing either gives HM_ERR_TUNING."""
+    gu = hm.wdesc("int4_sym", 4096, 7168, 256)
+    dn = hm.wdesc("int4_sym", 7168, 2048, 256)
+    p = hm.hm_moe_gemm_plan(gu, 0, 8192, 8, 0)
+    assert "stream(rows=16 max=64 nbw=2" in p and "k_gemm_mid 128x64" in p and "k_gemm_big from 97 rows" in p, p
+    assert "activations>=4GiB" not in p
+    # down projection, bf16 rows: P = t * 8 pairs of 2048 * 2 bytes; 4 GiB at P = 2^20
+    small = hm.hm_moe_gemm_plan(dn, 0, (1 << 17) - 1, 8, 1)
+    assert "k_gemm_mid 128x64" in small and "k_gemm_big" in small and ">=4GiB" not in small, small
+    big = hm.hm_moe_gemm_plan(dn, 0, 1 << 17, 8, 1)
+    assert "k_gemm_tile 128x128" in big and "big(256 rows)=none" in big and "activations>=4GiB" in big, big
+    # the same token count with token-indexed rows (gate_up) stays below 4 GiB
+    assert ">=4GiB" not in hm.hm_moe_gemm_plan(hm.wdesc("int4_sym", 4096, 2048, 256), 0, 1 << 17, 8, 0)
+    for bad in (dict(moe_tile=1), dict(moe_big_min=97)):
+        with pytest.raises(hm.HmError) as e:
+            hm.hm_moe_gemm_plan(dn, 0, 1 << 17, 8, 1, bad)
+        assert e.value.code == 8
+    # FP8 rows take one byte per value: 4 GiB at P = 2^21 for K = 2048
+    mx = hm.wdesc("mxfp4", 7168, 2048, 256)
+    assert ">=4GiB" not in hm.hm_moe_gemm_plan(mx, 1, (1 << 18) - 1, 8, 1)
+    assert "k_gemm_tile 128x128" in hm.hm_moe_gemm_plan(mx, 1, 1 << 18, 8, 1)
+    # MX weights with bf16 rows never take 256-row units
+    mxa = hm.hm_moe_gemm_plan(mx, 0, 8192, 8, 1)
+    assert "big(256 rows)=none" in mxa, mxa
+    # explicit tuning shows up in the plan and in the workspace size
+    t = dict(moe_stream_rows=32, moe_stream_max=128, moe_stream_nbw=1, moe_big_min=-1, moe_tile=2)
+    p2 = hm.hm_moe_gemm_plan(gu, 0, 1024, 8, 0, t)
+    assert "stream(rows=32 max=128 nbw=1" in p2 and "k_gemm_tile" in p2 and "big(256 rows)=none" in p2, p2
+    assert hm.hm_moe_gemm_workspace_size(gu, 0, 1024, 8, t) > 0

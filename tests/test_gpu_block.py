@@ -110,13 +110,13 @@ def test_moe_block_chained(fmt):
     a8 = fmt == quant.FMT_MXFP4
     if a8:
         x8, xs = hm.hm_quant_fp8_rows(x)
-        y1 = hm.hm_moe_gemm(dg, w_g, x8, off, sp, t, topk, 0, a_row_scale=xs)
+        y1 = hm.hm_moe_gemm(dg, w_g, x8, off, sp, t, topk, 0, a_scales=xs)
     else:
         y1 = hm.hm_moe_gemm(dg, w_g, x, off, sp, t, topk, 0)
     h = hm.hm_silu_mul(y1)
     if a8:
         h8, hs = hm.hm_quant_fp8_rows(h)
-        y2 = hm.hm_moe_gemm(dd, w_d, h8, off, sp, t, topk, 1, a_row_scale=hs)
+        y2 = hm.hm_moe_gemm(dd, w_d, h8, off, sp, t, topk, 1, a_scales=hs)
     else:
         y2 = hm.hm_moe_gemm(dd, w_d, h, off, sp, t, topk, 1)
     out = hm.hm_moe_combine(y2, to_dev(w), topk)

@@ -2,15 +2,13 @@
 dequantized weights): the five acceptance shapes of the workloads at full
 size (large M on sampled rows), ragged shapes on both kernel paths, closed
 forms, degenerate inputs and run-to-run determinism."""
-import os
-
 import numpy as np
 import pytest
 import torch
 
 import synthetic
 from oracle import codecs, gemm, quant
-from gpu_util import bf16_to_dev, bits_of, quantize_experts, raw_code_bound, std_to_dev, xhat_of
+from gpu_util import bf16_to_dev, bits_of, quantize_experts, std_to_dev, xhat_of
 
 pytestmark = pytest.mark.gpu
 
@@ -27,19 +25,19 @@ class Layer:
         self.desc = hm.wdesc(fmt, n, k)
         self.w = hm.hm_transform(self.desc, *std_to_dev(fmt, codes, scales, zeros))
 
-    def run(self, x_bits):
+    def run(self, x_bits, tuning=None):
         import quantized_gemm_int4_amd as hm
         x = bf16_to_dev(x_bits)
         if self.fmt == quant.FMT_MXFP4:
             x8, s = hm.hm_quant_fp8_rows(x)
-            y = hm.hm_gemm(self.desc, self.w, x8, s)
+            y = hm.hm_gemm(self.desc, self.w, x8, s, tuning=tuning)
         else:
-            y = hm.hm_gemm(self.desc, self.w, x)
+            y = hm.hm_gemm(self.desc, self.w, x, tuning=tuning)
         torch.cuda.synchronize()
         return bits_of(y)
 
-    def check(self, x_bits, rows=None):
-        yb = self.run(x_bits)
+    def check(self, x_bits, rows=None, tuning=None):
+        yb = self.run(x_bits, tuning)
         xh = xhat_of(self.fmt, x_bits)
         if rows is not None:
             xh, yb = xh[rows], yb[rows]
@@ -47,19 +45,6 @@ class Layer:
         res = gemm.check(yb, yref, b)
         assert res["ok"], res
         return res
-
-
-def _force(path):
-    if path is None:
-        os.environ.pop("HM_FORCE_PATH", None)
-    else:
-        os.environ["HM_FORCE_PATH"] = str(path)
-
-
-@pytest.fixture(autouse=True)
-def _no_force():
-    yield
-    _force(None)
 
 
 def test_config1_symmetric_decode():
@@ -111,27 +96,21 @@ def test_ragged_default_path(fmt, n, k, m):
 @pytest.mark.parametrize("path", [1, 2, 4])
 def test_forced_paths_agree_with_oracle(fmt, m, path):
     L = Layer(fmt, 328, 640, cfg=8)
-    _force(path)
-    L.check(synthetic.activations(8, m, 640, index=m))
+    L.check(synthetic.activations(8, m, 640, index=m), tuning=dict(path=path))
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 5])
 def test_stream_split_counts(splits):
     L = Layer(quant.FMT_UINT4_ZP, 512, 640, cfg=9)
-    os.environ["HM_STREAM_SPLITS"] = str(splits)
-    try:
-        L.check(synthetic.activations(9, 5, 640))
-    finally:
-        os.environ.pop("HM_STREAM_SPLITS", None)
+    L.check(synthetic.activations(9, 5, 640), tuning=dict(stream_splits=splits))
 
 
 def test_one_hot_weights_exact():
     """Closed form: one nonzero code per row with a power-of-two scale makes Y a
-    scaled column gather of X.  The tile path (bf16 weights s*q, exact here)
-    reproduces it bit for bit.  The streaming path multiplies codes encoded as
-    1 + u/16 and subtracts the zero-point product, so its fp32 rounding scales
-    with sum|x| rather than with sum|x*w|: it must meet the acceptance rule
-    with the raw-code term of gpu_util.raw_code_bound added to the bound."""
+    scaled column gather of X.  Every path multiplies exact weights (the
+    streaming path feeds u - z, or q / 16, to the MFMA, the tile paths s * q),
+    and every other product is an exact zero, so both reproduce it bit for
+    bit, also with K split over the waves of a block or over blocks."""
     import quantized_gemm_int4_amd as hm
     n, k = 96, 512
     ks = np.random.default_rng(3).integers(0, k, size=n)
@@ -141,19 +120,52 @@ def test_one_hot_weights_exact():
     scales = np.full((1, n, k // 128), 0x3E00, dtype=np.uint16)     # bf16 0.125
     d = hm.wdesc("int4_sym", n, k)
     w = hm.hm_transform(d, *std_to_dev(quant.FMT_INT4_SYM, codes, scales, None))
-    for m, path in [(3, 1), (40, 2)]:
-        _force(path)
+    for m, path, extra in [(3, 1, {}), (40, 2, {}), (1, 1, {"stream_ks": 4}),
+                           (16, 1, {"stream_splits": 3}), (32, 1, {})]:
         xb = synthetic.activations(10, m, k, index=m)
-        y = bits_of(hm.hm_gemm(d, w, bf16_to_dev(xb)))
+        y = bits_of(hm.hm_gemm(d, w, bf16_to_dev(xb), tuning=dict(extra, path=path)))
         x = codecs.bf16_value(xb).astype(np.float64)
-        exact = x[:, ks] * 0.375
-        want = codecs.bf16_rne_bits(exact.astype(np.float32))
-        if path == 2:
-            assert np.array_equal(y, want)
-        else:
-            bound = np.abs(exact) + raw_code_bound(x, scales[0])
-            r = gemm.check(y, exact, bound)
-            assert r["ok"], r
+        want = codecs.bf16_rne_bits((x[:, ks] * 0.375).astype(np.float32))
+        assert np.array_equal(y, want), (m, path, extra)
+
+
+@pytest.mark.parametrize("fmt", [quant.FMT_UINT4_ZP, quant.FMT_INT4_SYM])
+@pytest.mark.parametrize("m", [1, 16, 32])
+def test_mostly_zero_point_codes(fmt, m):
+    """Groups in which 120 or more of the 128 codes equal the zero point
+    (pruned or outlier-dominated groups): sum |x w| is small against sum |x|,
+    and the decode path must still meet the acceptance rule element by
+    element with the plain bound."""
+    import quantized_gemm_int4_amd as hm
+    n, k = 2048, 4096
+    r = np.random.default_rng(40 + m)
+    kg = k // 128
+    if fmt == quant.FMT_UINT4_ZP:
+        zeros = r.integers(0, 16, size=(n, kg)).astype(np.uint8)
+    else:
+        zeros = np.full((n, kg), 8, dtype=np.uint8)             # q = u - 8 = 0
+    u = np.repeat(zeros, 128, axis=1).astype(np.int64).reshape(n, kg, 128)
+    pos = np.argsort(r.random((n, kg, 128)), axis=2)[:, :, :6]   # 6 codes per group may differ
+    np.put_along_axis(u, pos, r.integers(0, 16, size=pos.shape), axis=2)
+    per_group = (u == zeros[:, :, None]).sum(axis=2)
+    assert per_group.min() >= 122
+    u = u.reshape(n, k)
+    scales = (0x3B00 + r.integers(0, 0x100, size=(n, kg))).astype(np.uint16)
+    if fmt == quant.FMT_INT4_SYM:
+        codes = quant.pack_nibbles(u - 8)                       # two's complement q
+        zz = None
+    else:
+        codes = quant.pack_nibbles(u)
+        zz = zeros
+    what = quant.dequant(fmt, codes, scales, zz).astype(np.float64)
+    d = hm.wdesc(fmt, n, k)
+    w = hm.hm_transform(d, *std_to_dev(fmt, codes[None], scales[None], zz[None] if zz is not None else None))
+    assert " stream " in hm.hm_gemm_plan(d, hm.HM_A_BF16, m)
+    xb = synthetic.activations(19, m, k, index=m)
+    y = bits_of(hm.hm_gemm(d, w, bf16_to_dev(xb)))
+    yref, b = gemm.gemm_ref(codecs.bf16_value(xb).astype(np.float64), what)
+    res = gemm.check(y, yref, b)
+    assert res["ok"], res
 
 
 @pytest.mark.parametrize("fmt", quant.FORMATS)
@@ -195,19 +207,6 @@ def test_m_zero_is_noop(config2):
     assert y.shape == (0, 14336)
 
 
-def _with_env(env, fn):
-    old = {k: os.environ.get(k) for k in env}
-    os.environ.update({k: str(v) for k, v in env.items()})
-    try:
-        return fn()
-    finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
-
-
 @pytest.mark.parametrize("fmt", quant.FORMATS)
 @pytest.mark.parametrize("ks", [1, 2, 4])
 @pytest.mark.parametrize("nbw", [1, 2])
@@ -218,7 +217,7 @@ def test_stream_wave_splits(fmt, ks, nbw, m):
     blocks per wave, N ragged against the block's column sets."""
     L = Layer(fmt, 200, 896, cfg=10, wseed=ks + 3 * nbw)
     x = synthetic.activations(10, m, 896, index=m)
-    _with_env({"HM_FORCE_PATH": 1, "HM_STREAM_KS": ks, "HM_STREAM_NBW": nbw}, lambda: L.check(x))
+    L.check(x, tuning=dict(path=1, stream_ks=ks, stream_nbw=nbw))
 
 
 @pytest.mark.parametrize("fmt", quant.FORMATS)
@@ -231,8 +230,7 @@ def test_stream_multi_piece(fmt, ks, m, splits):
     k = 6144 if fmt == quant.FMT_MXFP4 else 3072
     L = Layer(fmt, 96, k, cfg=11, wseed=ks)
     x = synthetic.activations(11, m, k, index=m + splits)
-    env = {"HM_FORCE_PATH": 1, "HM_STREAM_KS": ks, "HM_STREAM_SPLITS": splits}
-    _with_env(env, lambda: L.check(x))
+    L.check(x, tuning=dict(path=1, stream_ks=ks, stream_splits=splits))
 
 
 @pytest.mark.parametrize("fmt", quant.FORMATS)
@@ -243,7 +241,7 @@ def test_big_tiles_ragged(fmt, m, n, k):
     256, one or an odd number of K groups, a single row, a single tile."""
     L = Layer(fmt, n, k, cfg=13, wseed=m)
     x = synthetic.activations(13, m, k, index=m, outliers=0.01 if fmt == quant.FMT_MXFP4 else 0)
-    _with_env({"HM_FORCE_PATH": 3}, lambda: L.check(x))
+    L.check(x, tuning=dict(path=3))
 
 
 @pytest.mark.parametrize("fmt", quant.FORMATS)
@@ -256,7 +254,7 @@ def test_mid_tiles_ragged(fmt, m, n, k):
     depths), a single row."""
     L = Layer(fmt, n, k, cfg=14, wseed=m + n)
     x = synthetic.activations(14, m, k, index=m, outliers=0.01 if fmt == quant.FMT_MXFP4 else 0)
-    _with_env({"HM_FORCE_PATH": 2}, lambda: L.check(x))
+    L.check(x, tuning=dict(path=2))
 
 
 @pytest.mark.parametrize("fmt", [quant.FMT_UINT4_ZP, quant.FMT_INT4_SYM])

@@ -3,8 +3,6 @@ the stable pair order), and the grouped GEMM matches the oracle's per-expert
 fp64 GEMM for every pair, on small shapes that mix streaming units (small
 experts, cut into 16- or 32-row units), 128-row and 256-row tile units, and
 at the workload sizes on sampled pairs."""
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -51,7 +49,7 @@ def _skewed_ids(t, topk, E, seed):
     return np.stack([r.choice(E, topk, replace=False, p=p) for _ in range(t)]).astype(np.int32)
 
 
-def _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, seed):
+def _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, seed, tuning=None):
     import quantized_gemm_int4_amd as hm
     ws = [synthetic.weights(12, n, k, index=seed * 100 + e) for e in range(E)]
     codes, scales, zeros, what = quantize_experts(fmt, ws)
@@ -64,9 +62,9 @@ def _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, seed):
     x = bf16_to_dev(xb)
     if fmt == quant.FMT_MXFP4:
         x8, s = hm.hm_quant_fp8_rows(x)
-        y = hm.hm_moe_gemm(d, w, x8, off, sp, t, topk, rows_are_pairs, a_row_scale=s)
+        y = hm.hm_moe_gemm(d, w, x8, off, sp, t, topk, rows_are_pairs, a_scales=s, tuning=tuning)
     else:
-        y = hm.hm_moe_gemm(d, w, x, off, sp, t, topk, rows_are_pairs)
+        y = hm.hm_moe_gemm(d, w, x, off, sp, t, topk, rows_are_pairs, tuning=tuning)
     torch.cuda.synchronize()
     xh = xhat_of(fmt, xb)
     yref, b, _ = moe.moe_gemm_ref(xh, bool(rows_are_pairs), topk, ids,
@@ -85,11 +83,7 @@ def test_moe_mixed_units(fmt, rows_are_pairs, mid):
     ids = _skewed_ids(t, topk, E, 1)
     counts = np.bincount(ids.ravel(), minlength=E)
     assert counts.max() > 128 and (counts[counts > 0] <= 32).any()   # both kernels used, multi-unit
-    os.environ["HM_MOE_MID"] = str(mid)
-    try:
-        _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, 1)
-    finally:
-        os.environ.pop("HM_MOE_MID", None)
+    _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, 1, tuning=dict(moe_tile=1 if mid else 2))
 
 
 @pytest.mark.parametrize("fmt", [quant.FMT_INT4_SYM, quant.FMT_MXFP4])
@@ -140,7 +134,7 @@ def test_moe_workload_size_sampled(fmt, t, proj):
     x = bf16_to_dev(xb)
     if fmt == quant.FMT_MXFP4:
         x8, s = hm.hm_quant_fp8_rows(x)
-        y = hm.hm_moe_gemm(d, w, x8, off, sp, t, topk, rows_are_pairs, a_row_scale=s)
+        y = hm.hm_moe_gemm(d, w, x8, off, sp, t, topk, rows_are_pairs, a_scales=s)
     else:
         y = hm.hm_moe_gemm(d, w, x, off, sp, t, topk, rows_are_pairs)
     torch.cuda.synchronize()
@@ -172,14 +166,9 @@ def test_moe_workload_size_sampled(fmt, t, proj):
 def test_moe_stream_wave_splits(fmt, ks):
     """Streaming units with K split over 2 or 4 waves of a block (K = 5 groups:
     uneven slices, and with 4 waves one wave holds a single group)."""
-    import os
     t, topk, E, n, k = 150, 2, 8, 208, 640
     ids = _skewed_ids(t, topk, E, 3)
-    os.environ["HM_MOE_STREAM_KS"] = str(ks)
-    try:
-        _run_moe(fmt, E, n, k, t, topk, ids, 0, 3)
-    finally:
-        os.environ.pop("HM_MOE_STREAM_KS", None)
+    _run_moe(fmt, E, n, k, t, topk, ids, 0, 3, tuning=dict(moe_stream_ks=ks))
 
 
 @pytest.mark.parametrize("fmt", quant.FORMATS)
@@ -191,7 +180,6 @@ def test_moe_big_units(fmt, rows_are_pairs, big):
     second 256-row unit), 100 rows (tile unit) and a few rows (streaming), on
     K = 5 groups and ragged N; with HM_MOE_BIG=0 the same call uses tile
     units only."""
-    import os
     t, topk, E, n, k = 600, 2, 6, 288, 640
     r = np.random.default_rng(7)
     ids = np.zeros((t, topk), dtype=np.int32)
@@ -199,11 +187,7 @@ def test_moe_big_units(fmt, rows_are_pairs, big):
     second = np.concatenate([np.full(450, 1), np.full(100, 2), np.full(30, 3), np.full(12, 4),
                              np.full(8, 5)])
     ids[:, 1] = r.permutation(second)
-    os.environ["HM_MOE_BIG"] = str(big)
-    try:
-        _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, 9)
-    finally:
-        os.environ.pop("HM_MOE_BIG", None)
+    _run_moe(fmt, E, n, k, t, topk, ids, rows_are_pairs, 9, tuning=None if big else dict(moe_big_min=-1))
 
 
 @pytest.mark.parametrize("fmt", quant.FORMATS)
@@ -217,10 +201,5 @@ def test_moe_stream_multi_unit(fmt, s_max, nbw, s_rows):
     r = np.random.default_rng(11)
     ids = r.permutation(np.concatenate([np.full(c, e) for e, c in enumerate([120, 64, 33, 17, 16, 5])]))
     ids = ids.reshape(t, topk).astype(np.int32)
-    env = {"HM_MOE_STREAM_MAX": s_max, "HM_MOE_STREAM_NBW": nbw, "HM_MOE_STREAM_ROWS": s_rows}
-    os.environ.update({kk: str(v) for kk, v in env.items()})
-    try:
-        _run_moe(fmt, E, n, k, t, topk, ids, 0, 13)
-    finally:
-        for kk in env:
-            os.environ.pop(kk, None)
+    _run_moe(fmt, E, n, k, t, topk, ids, 0, 13,
+             tuning=dict(moe_stream_max=s_max, moe_stream_nbw=nbw, moe_stream_rows=s_rows))

@@ -7,8 +7,6 @@ The oracle is the same fp64 GEMM of the exactly dequantized weights as for
 the other pairs, with the bf16 values of X; the dequantization itself is
 checked bit for bit through unit activation rows (every output is then one
 weight)."""
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -21,12 +19,6 @@ pytestmark = pytest.mark.gpu
 
 MX = quant.FMT_MXFP4
 MXS = [quant.FMT_MXFP4, quant.FMT_MXINT4]
-
-
-@pytest.fixture(autouse=True)
-def _no_force():
-    yield
-    os.environ.pop("HM_FORCE_PATH", None)
 
 
 def _bf16_one_rows(k, cols):
@@ -57,9 +49,7 @@ def test_dequant_through_unit_rows(fmt, m, force):
     w = hm.hm_transform(d, *std_to_dev(fmt, codes[None], scales[None], None))
     cols = r.permutation(k)[:m] if m <= k else None
     xb = _bf16_one_rows(k, cols)
-    if force is not None:
-        os.environ["HM_FORCE_PATH"] = str(force)
-    y = hm.hm_gemm(d, w, bf16_to_dev(xb))
+    y = hm.hm_gemm(d, w, bf16_to_dev(xb), tuning=None if force is None else dict(path=force))
     torch.cuda.synchronize()
     got = codecs.bf16_value(bits_of(y)).astype(np.float64)
     want = what[:, cols].T
@@ -75,9 +65,9 @@ class MxLayer:
         self.desc = hm.wdesc(fmt, n, k)
         self.w = hm.hm_transform(self.desc, *std_to_dev(fmt, codes, scales, None))
 
-    def check(self, xb, rows=None):
+    def check(self, xb, rows=None, tuning=None):
         import quantized_gemm_int4_amd as hm
-        y = hm.hm_gemm(self.desc, self.w, bf16_to_dev(xb))
+        y = hm.hm_gemm(self.desc, self.w, bf16_to_dev(xb), tuning=tuning)
         torch.cuda.synchronize()
         yb = bits_of(y)
         xh = codecs.bf16_value(xb).astype(np.float64)
@@ -96,11 +86,11 @@ def test_ragged_default_path(fmt, n, k, m):
     MxLayer(n, k, cfg=7, wseed=n + k, fmt=fmt).check(synthetic.activations(7, m, k, index=m, outliers=0.01))
 
 
-@pytest.mark.parametrize("m,force", [(64, 1), (256, 1), (1, 4), (17, 4), (100, 4), (300, 4), (300, 3)])
+@pytest.mark.parametrize("m,force", [(64, 1), (256, 1), (1, 4), (17, 4), (100, 4), (300, 4), (300, 2), (1, 2)])
 @pytest.mark.parametrize("fmt", MXS)
 def test_forced_paths(fmt, m, force):
-    os.environ["HM_FORCE_PATH"] = str(force)
-    MxLayer(264, 640, cfg=7, wseed=5, fmt=fmt).check(synthetic.activations(7, m, 640, index=m, outliers=0.01))
+    MxLayer(264, 640, cfg=7, wseed=5, fmt=fmt).check(synthetic.activations(7, m, 640, index=m, outliers=0.01),
+                                                     tuning=dict(path=force))
 
 
 @pytest.fixture(scope="module", params=MXS)
@@ -135,14 +125,10 @@ def test_moe_mixed_units(fmt, rows_are_pairs, mid):
     call; the tile units on the 128 x 64 kernel (mid=1, the default) or the
     128 x 128 one."""
     import quantized_gemm_int4_amd as hm
-    os.environ["HM_MOE_MID"] = str(mid)
-    try:
-        _moe_mixed(hm, rows_are_pairs, fmt)
-    finally:
-        os.environ.pop("HM_MOE_MID", None)
+    _moe_mixed(hm, rows_are_pairs, fmt, dict(moe_tile=1 if mid else 2))
 
 
-def _moe_mixed(hm, rows_are_pairs, fmt):
+def _moe_mixed(hm, rows_are_pairs, fmt, tuning):
     t, topk, E, n, k = 150, 2, 8, 208, 384
     ids = _skewed_ids(t, topk, E, 1)
     counts = np.bincount(ids.ravel(), minlength=E)
@@ -153,7 +139,7 @@ def _moe_mixed(hm, rows_are_pairs, fmt):
     w = hm.hm_transform(d, *std_to_dev(fmt, codes, scales, None))
     xb = synthetic.activations(12, t * topk if rows_are_pairs else t, k, index=1, outliers=0.01)
     _, off, sp = hm.hm_moe_sort(to_dev(ids), E)
-    y = hm.hm_moe_gemm(d, w, bf16_to_dev(xb), off, sp, t, topk, rows_are_pairs)
+    y = hm.hm_moe_gemm(d, w, bf16_to_dev(xb), off, sp, t, topk, rows_are_pairs, tuning=tuning)
     torch.cuda.synchronize()
     yref, b, _ = moe.moe_gemm_ref(codecs.bf16_value(xb).astype(np.float64), bool(rows_are_pairs), topk, ids,
                                   lambda e: what[e].astype(np.float64), n)

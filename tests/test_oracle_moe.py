@@ -120,3 +120,33 @@ def test_check_elementwise_rejects_two_ulps():
     off = bits.copy()
     off[1] += 2                                    # two bf16 ulps away
     assert not gemm.check_elementwise(off, ref)["ok"]
+
+
+def test_moe_pairs_subset_brute_force():
+    """The pairs= path (used by every workload-size parity test) returns the
+    rows of exactly the listed pairs, in the listed order, for both
+    projections: each row equals W_{ids[p]} @ a[row(p)] computed by an
+    explicit loop, and the subset equals the full result indexed by it
+    (unsorted pairs, a repeated pair, pairs of one expert and of several).
+    Rows taken by the subset index instead of the pair id fail."""
+    r = np.random.default_rng(9)
+    t, topk, E, k, n = 11, 3, 4, 128, 12
+    ids = np.stack([r.choice(E, topk, replace=False) for _ in range(t)]).astype(np.int32)
+    ws = [r.normal(size=(n, k)) for _ in range(E)]
+    flat = ids.ravel()
+    for rows_are_pairs in (False, True):
+        a = r.normal(size=(t * topk if rows_are_pairs else t, k))
+        pairs = np.array([31, 2, 17, 2, 0, 25, 9, 32])
+        y, b, pp = moe.moe_gemm_ref(a, rows_are_pairs, topk, ids, lambda e: ws[e], n, pairs=pairs)
+        assert np.array_equal(pp, pairs)
+        for i, p in enumerate(pairs):
+            row = a[p] if rows_are_pairs else a[p // topk]
+            w = ws[flat[p]]
+            ref = np.array([sum(w[c, kk] * row[kk] for kk in range(k)) for c in range(n)])
+            bnd = np.array([sum(abs(w[c, kk] * row[kk]) for kk in range(k)) for c in range(n)])
+            assert np.allclose(y[i], ref, rtol=0, atol=1e-12)
+            assert np.allclose(b[i], bnd, rtol=0, atol=1e-12)
+        yf, bf, _ = moe.moe_gemm_ref(a, rows_are_pairs, topk, ids, lambda e: ws[e], n)
+        # (BLAS may block a subset differently: equal up to fp64 rounding)
+        assert np.allclose(y, yf[pairs], rtol=1e-13, atol=1e-13)
+        assert np.allclose(b, bf[pairs], rtol=1e-13, atol=1e-13)

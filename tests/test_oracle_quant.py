@@ -284,3 +284,54 @@ def test_mxint4_storage_and_layout_match_mxfp4():
     a = layout.transform_ref(quant.FMT_MXINT4, codes, scales)
     b = layout.transform_ref(quant.FMT_MXFP4, codes, scales)
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ pins of the FP8 row restore and the
+# zero-point scale rule (per-token FP8: ywsung.com note, section on weight format / activation / backend;
+# zero points: aihaber.org article, Architecture, with the min-max reading of the oracle's header)
+
+def test_fp8_rows_dequant_power_of_two_scale():
+    """A row whose largest magnitude is 448 * 2^j has the exact scale s = 2^j,
+    and every element that is an E4M3 value times 2^j comes back exactly:
+    x_hat = E4M3(code) * s.  The expected values are written out (448, 1.75,
+    -0.5, the smallest subnormal 2^-9, 0 and -26 times 2^j), so a restore that
+    divided by s, dropped it or took the wrong row's scale fails."""
+    from synthetic import to_bf16_bits
+    base = np.array([448.0, 1.75, -0.5, 2.0 ** -9, 0.0, -26.0, 448.0, -448.0], dtype=np.float64)
+    rows = []
+    for j in (-20, -3, 0, 5):
+        rows.append(base * 2.0 ** j)
+    x = np.array(rows, dtype=np.float32)
+    xb = to_bf16_bits(x)
+    codes, s = quant.quant_fp8_rows(xb)
+    for i, j in enumerate((-20, -3, 0, 5)):
+        assert s[i] == np.float32(2.0 ** j)
+    xh = quant.fp8_rows_dequant(codes, s)
+    want = np.array(rows)
+    assert np.array_equal(xh, want)
+    # and the codes themselves: 448 -> 0x7E, 1.75 -> 0x3E, -0.5 -> 0xB0, 2^-9 -> 0x01, -26 = -1.625 * 2^4 -> 0xDD
+    assert list(codes[0][:6]) == [0x7E, 0x3E, 0xB0, 0x01, 0x00, 0xDD]
+    # a row of two rows' scales: the restore uses each row's own scale
+    both = quant.fp8_rows_dequant(np.array([[0x38], [0x38]], dtype=np.uint8), np.array([0.25, 8.0], np.float32))
+    assert both[0, 0] == 0.25 and both[1, 0] == 8.0
+
+
+def test_uint4_zp_scale_rule_against_torch():
+    """The zero-point format's scale is bf16(fp32((max - min) / 15)) per
+    128-group: recomputed here with torch's fp32 division and bf16
+    conversion, plus a written-out group (max 1.5, min 0: s = bf16(0.1) =
+    0x3DCD, z = 0, and w = 0.7 -> u = rne(0.7 / 0.10009765625) = 7).  A scale
+    over 14 or 16 steps, or from max alone, fails."""
+    r = np.random.default_rng(21)
+    w = r.normal(0, 0.02, size=(7, 384)).astype(np.float32)
+    w[4, :128] = np.linspace(0.0, 1.5, 128, dtype=np.float32)
+    w[4, 5] = 0.7
+    u, sbits, z = quant.quant_uint4_zp(w)
+    for n in range(7):
+        for g in range(3):
+            blk = torch.from_numpy(w[n, 128 * g:128 * (g + 1)].copy())
+            s32 = (blk.max() - blk.min()) / torch.tensor(15.0, dtype=torch.float32)
+            want = s32.to(torch.bfloat16).view(torch.int16).item() & 0xFFFF
+            assert sbits[n, g] == want, (n, g)
+    assert sbits[4, 0] == 0x3DCD and z[4, 0] == 0 and u[4, 5] == 7
+    assert u[4, 127] == 15 and u[4, 0] == 0
