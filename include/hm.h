@@ -274,6 +274,19 @@ hm_status hm_silu_mul(const uint16_t* gu, int64_t rows, int64_t d, uint16_t* h, 
 hm_status hm_moe_combine(const uint16_t* y, const float* w, int64_t t, int32_t topk, int64_t n,
                          uint16_t* out, hipStream_t stream);
 
+/* ------------------------------------------------------------ measurement */
+
+/* Plain-read reference: reads `bytes` bytes of `buf` once with the 16-byte
+ * loads the decode GEMM uses for its weights, `unroll` loads in flight per
+ * lane (1, 2, 4 or 8) over `blocks` blocks of 256 threads (1 .. 65535), and
+ * writes one xor-fold word per block to out[blocks] (so no load is skipped).
+ * Computes nothing of the GEMM: its time is the bandwidth floor the
+ * weight-streaming kernel is compared against.  bytes a positive multiple of
+ * 16; buf and out 16- and 4-byte aligned; HM_ERR_SHAPE / HM_ERR_NULL /
+ * HM_ERR_ALIGN before any launch. */
+hm_status hm_read_probe(const void* buf, int64_t bytes, int32_t blocks, int32_t unroll, uint32_t* out,
+                        hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* hm_status_string(hm_status s);
 

@@ -96,6 +96,7 @@ def _load():
         "hm_moe_gemm_plan": [D, I32, I64, I32, I32, T, ctypes.c_char_p, SZ],
         "hm_silu_mul": [P, I64, I64, P, P],
         "hm_moe_combine": [P, P, I64, I32, I64, P, P],
+        "hm_read_probe": [P, I64, I32, I32, P, P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -304,4 +305,17 @@ def hm_moe_combine(y, weights, topk, out=None, stream=None):
     _need(out, torch.bfloat16, t * n, "out")
     _ok("hm_moe_combine", lib.hm_moe_combine(_ptr(y), _ptr(weights), t, int(topk), n, _ptr(out),
                                              _stream(stream)))
+    return out
+
+
+# ----------------------------------------------------------------- measurement
+
+def hm_read_probe(buf, blocks=2048, unroll=4, out=None, stream=None):
+    """Plain-read reference over a device buffer (any dtype, byte size a
+    multiple of 16); returns the per-block words."""
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(blocks, dtype=torch.int32, device=buf.device)
+    _ok("hm_read_probe", lib.hm_read_probe(_ptr(buf), nbytes, int(blocks), int(unroll), _ptr(out),
+                                           _stream(stream)))
     return out

@@ -438,6 +438,15 @@ HM_API hm_status hm_moe_combine(const uint16_t* y, const float* w, int64_t t, in
   return HM_OK;
 }
 
+HM_API hm_status hm_read_probe(const void* buf, int64_t bytes, int32_t blocks, int32_t unroll, uint32_t* out,
+                               hipStream_t stream) {
+  if (bytes <= 0 || (bytes % 16) != 0 || blocks < 1 || blocks > 65535) return HM_ERR_SHAPE;
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) return HM_ERR_SHAPE;
+  if (!buf || !out) return HM_ERR_NULL;
+  if (!aligned(buf, 16) || !aligned(out, 4)) return HM_ERR_ALIGN;
+  return launch_read_probe(buf, bytes, blocks, unroll, out, stream) == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
 HM_API hm_status hm_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t m, const hm_tuning* tune,
                                         size_t* bytes) {
   hm_status s = check_desc(d);

@@ -118,3 +118,45 @@ hipError_t launch_combine(const uint16_t* y, const float* w, int64_t t, int topk
 }
 
 }  // namespace hm
+
+namespace hm {
+
+// Plain streaming read of `bytes` bytes (a multiple of 16): every lane loads
+// 16-byte chunks in a grid-stride loop, UNROLL loads in flight, xor-folds
+// them and each block writes one word (so no load can be dropped).  The
+// decode GEMM reads its weights with the same 16-byte loads; this is the
+// floor it is measured against.
+template <int UNROLL>
+__global__ void __launch_bounds__(256) k_read_probe(const u32x4_t* __restrict__ p, int64_t n16,
+                                                    uint32_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+    u32x4_t v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) acc ^= v[u];
+  }
+  for (; i < n16; i += stride) acc ^= p[i];
+  uint32_t r = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  for (int off = 32; off >= 1; off >>= 1) r ^= (uint32_t)__shfl_xor((int)r, off, 64);
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = r;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+hipError_t launch_read_probe(const void* buf, int64_t bytes, int blocks, int unroll, uint32_t* out,
+                             hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  const u32x4_t* p = reinterpret_cast<const u32x4_t*>(buf);
+  if (unroll == 8) hipLaunchKernelGGL(k_read_probe<8>, dim3(blocks), dim3(256), 0, st, p, n16, out);
+  else if (unroll == 2) hipLaunchKernelGGL(k_read_probe<2>, dim3(blocks), dim3(256), 0, st, p, n16, out);
+  else if (unroll == 1) hipLaunchKernelGGL(k_read_probe<1>, dim3(blocks), dim3(256), 0, st, p, n16, out);
+  else hipLaunchKernelGGL(k_read_probe<4>, dim3(blocks), dim3(256), 0, st, p, n16, out);
+  return hipGetLastError();
+}
+
+}  // namespace hm

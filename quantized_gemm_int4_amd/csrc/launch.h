@@ -53,6 +53,9 @@ hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_r
 hipError_t launch_silu_mul(const uint16_t* gu, int64_t rows, int64_t d, uint16_t* h, hipStream_t st);
 hipError_t launch_combine(const uint16_t* y, const float* w, int64_t t, int topk, int64_t n, uint16_t* out,
                           hipStream_t st);
+// plain streaming read of a buffer (16-byte loads), one word per block written
+hipError_t launch_read_probe(const void* buf, int64_t bytes, int blocks, int unroll, uint32_t* out,
+                             hipStream_t st);
 
 // Streaming (small-M) kernel.  Dense: grid (n_tiles, splits, m_chunks).
 // Grouped: persistent over (streaming unit x n tile) items.

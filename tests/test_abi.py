@@ -263,3 +263,52 @@ def test_moe_plan_and_large_activation_guard():
     p2 = hm.hm_moe_gemm_plan(gu, 0, 1024, 8, 0, t)
     assert "stream(rows=32 max=128 nbw=1" in p2 and "k_gemm_tile" in p2 and "big(256 rows)=none" in p2, p2
     assert hm.hm_moe_gemm_workspace_size(gu, 0, 1024, 8, t) > 0
+
+
+def test_read_probe_argument_checks():
+    P = ctypes.c_void_p
+    good = P(0x100000)
+    assert _err("hm_read_probe", good, 0, 64, 4, good, None) == 2          # no bytes
+    assert _err("hm_read_probe", good, 24, 64, 4, good, None) == 2         # not a multiple of 16
+    assert _err("hm_read_probe", good, 1024, 0, 4, good, None) == 2        # no blocks
+    assert _err("hm_read_probe", good, 1024, 64, 3, good, None) == 2       # unroll
+    assert _err("hm_read_probe", None, 1024, 64, 4, good, None) == 1
+    assert _err("hm_read_probe", P(0x100008), 1024, 64, 4, good, None) == 3
+
+
+def test_tuner_candidates_are_valid_and_distinct():
+    """The autotuner's search space: every candidate is accepted by the
+    planner, selects a distinct kernel configuration, and the default choice
+    comes first; grouped candidates likewise (no GPU needed: plans only)."""
+    from quantized_gemm_int4_amd import tune
+    d = hm.wdesc("uint4_zp", 14336, 4096)
+    for m in (1, 16, 128, 300, 4096):
+        cands = tune.dense_candidates(d, 0, m)
+        assert cands[0] == {}
+        plans = [hm.hm_gemm_plan(d, 0, m, c or None) for c in cands]
+        assert len(set(plans)) == len(plans)
+        assert any(" stream " in p for p in plans) == (m <= 256)
+        assert any("256x256" in p for p in plans) and any("128x128" in p for p in plans)
+    mx = hm.wdesc("mxfp4", 7168, 2048)
+    assert not any("256x256" in hm.hm_gemm_plan(mx, 0, 64, c or None) for c in tune.dense_candidates(mx, 0, 64))
+    moe = hm.wdesc("int4_sym", 4096, 7168, 256)
+    mc = tune.moe_candidates(moe, 0, 1024, 8, 0)
+    mplans = [hm.hm_moe_gemm_plan(moe, 0, 1024, 8, 0, c or None) for c in mc]
+    assert mc[0] == {} and len(set(mplans)) == len(mplans) > 10
+
+
+def test_tuning_table_lookup(tmp_path):
+    from quantized_gemm_int4_amd import tune
+    d = hm.wdesc("uint4_zp", 512, 1024)
+    t = tune.Table(meta=dict(device="test"))
+    t.put(tune._key(d, 0), 16, dict(path=1, stream_ks=2), 5.0, 6.0, "p16")
+    t.put(tune._key(d, 0), 128, {}, 9.0, 9.0, "p128")
+    f = tmp_path / "t.json"
+    t.save(str(f))
+    t2 = tune.Table.load(str(f))
+    assert t2.lookup(d, 0, 1) == dict(path=1, stream_ks=2)        # next tuned row count up
+    assert t2.lookup(d, 0, 16) == dict(path=1, stream_ks=2)
+    assert t2.lookup(d, 0, 17) is None                             # tuned default
+    assert t2.lookup(d, 0, 5000) is None                           # beyond: the largest
+    assert t2.lookup(hm.wdesc("uint4_zp", 512, 2048), 0, 16) is None
+    assert t2.meta["device"] == "test"

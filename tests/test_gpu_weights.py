@@ -19,6 +19,7 @@ def _random_std(fmt, E, N, K, seed):
     codes = r.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
     if fmt in quant.MX_FORMATS:
         scales = r.integers(0, 256, size=(E, N, K // 32), dtype=np.uint8)   # every byte, NaN (255) included
+        scales.reshape(-1)[:4] = [252, 253, 254, 255]          # the top bytes on every shape
     else:
         # finite bf16 patterns of both signs (|s| < 2^119 so s*15 stays finite),
         # including subnormals and zero
