@@ -121,9 +121,10 @@ typedef struct hm_tuning {
   int32_t path;            /* dense kernel: 0 default; 1 streaming (M <= 256); 2 128-row tiles
                               (W4A16 128 x 64 split over K, W4A8 64 x 128); 3 256 x 256 tiles
                               (not for MX weights with bf16 rows); 4 128 x 128 tiles */
-  int32_t stream_ks;       /* streaming: waves of a block splitting one column set's K: 0, 1, 2, 4 */
+  int32_t stream_ks;       /* streaming: waves of a block splitting one column set's K: 0, 1, 2, 4, 8 */
   int32_t stream_nbw;      /* streaming: 16-column blocks per wave: 0, 1, 2 */
   int32_t stream_splits;   /* dense streaming: K split over blocks (fp32 partials): 0, 1 .. K/128 */
+  int32_t stream_waves;    /* dense streaming: waves per block: 0, 4, 8 (8 needs stream_ks 2, 4 or 8) */
   int32_t moe_stream_rows; /* rows per grouped streaming unit: 0, 16, 32 */
   int32_t moe_stream_max;  /* largest expert (rows) taking streaming units: 0, 1 .. 4096 */
   int32_t moe_stream_nbw;  /* grouped streaming: 16-column blocks per wave: 0, 1, 2 */

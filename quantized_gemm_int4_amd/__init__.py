@@ -38,7 +38,7 @@ class hm_wdesc(ctypes.Structure):
 
 class hm_tuning(ctypes.Structure):
     _fields_ = [("abi", ctypes.c_int32), ("path", ctypes.c_int32), ("stream_ks", ctypes.c_int32),
-                ("stream_nbw", ctypes.c_int32), ("stream_splits", ctypes.c_int32),
+                ("stream_nbw", ctypes.c_int32), ("stream_splits", ctypes.c_int32), ("stream_waves", ctypes.c_int32),
                 ("moe_stream_rows", ctypes.c_int32), ("moe_stream_max", ctypes.c_int32),
                 ("moe_stream_nbw", ctypes.c_int32), ("moe_stream_ks", ctypes.c_int32),
                 ("moe_stream_lds_kb", ctypes.c_int32), ("moe_big_min", ctypes.c_int32),

@@ -89,7 +89,7 @@ bool scales_addr32(const Geom& G) { return G.total - G.off_scales < kAddr32; }
 
 // ---------------------------------------------------------------- tuning
 struct Tune {
-  int path, sks, snbw, ssplits, mrows, mmax, mnbw, mks, mlds, mbig, mtile;
+  int path, sks, snbw, ssplits, swaves, mrows, mmax, mnbw, mks, mlds, mbig, mtile;
 };
 
 bool in_set(int v, std::initializer_list<int> ok) {
@@ -102,15 +102,17 @@ hm_status read_tuning(const hm_tuning* t, Tune* out) {
   *out = Tune{};
   if (!t) return HM_OK;
   if (t->abi != HM_ABI_VERSION) return HM_ERR_ABI;
-  const bool ok = in_set(t->path, {0, 1, 2, 3, 4}) && in_set(t->stream_ks, {0, 1, 2, 4}) &&
+  const bool ok = in_set(t->path, {0, 1, 2, 3, 4}) && in_set(t->stream_ks, {0, 1, 2, 4, 8}) &&
                   in_set(t->stream_nbw, {0, 1, 2}) && t->stream_splits >= 0 &&
+                  in_set(t->stream_waves, {0, 4, 8}) && !(t->stream_ks == 8 && t->stream_waves != 8) &&
+                  !(t->stream_ks == 1 && t->stream_waves == 8) &&
                   in_set(t->moe_stream_rows, {0, 16, 32}) && t->moe_stream_max >= 0 &&
                   t->moe_stream_max <= 4096 && in_set(t->moe_stream_nbw, {0, 1, 2}) &&
                   in_set(t->moe_stream_ks, {0, 1, 2, 4}) &&
                   (t->moe_stream_lds_kb == 0 || (t->moe_stream_lds_kb >= 20 && t->moe_stream_lds_kb <= 159)) &&
                   t->moe_big_min >= -1 && t->moe_big_min <= kBigRows && in_set(t->moe_tile, {0, 1, 2});
   if (!ok) return HM_ERR_TUNING;
-  *out = Tune{t->path, t->stream_ks, t->stream_nbw, t->stream_splits, t->moe_stream_rows, t->moe_stream_max,
+  *out = Tune{t->path, t->stream_ks, t->stream_nbw, t->stream_splits, t->stream_waves, t->moe_stream_rows, t->moe_stream_max,
               t->moe_stream_nbw, t->moe_stream_ks, t->moe_stream_lds_kb, t->moe_big_min, t->moe_tile};
   return HM_OK;
 }
@@ -194,30 +196,57 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   // at once.  A block keeps its activation rows in LDS, so the LDS footprint
   // decides how many blocks share a compute unit (at most 5: the register
   // budget allows 5 waves per SIMD).
-  int ks = tu.sks, nbw = tu.snbw;
-  static const int kShapes[6][2] = {{4, 1}, {2, 1}, {4, 2}, {2, 2}, {1, 1}, {1, 2}};
-  if (!ks || !nbw) {
-    const int64_t row_bytes = std::min<int64_t>(G.KG * gb + 16, kStreamLdsBytes / rows);
-    int pick = -1;
+  // (ks, nbw) per block width, narrowest block first
+  static const int kShapes4[6][2] = {{4, 1}, {2, 1}, {4, 2}, {2, 2}, {1, 1}, {1, 2}};
+  static const int kShapes8[6][2] = {{8, 1}, {4, 1}, {8, 2}, {2, 1}, {4, 2}, {2, 2}};
+  const int64_t row_bytes = std::min<int64_t>(G.KG * gb + 16, kStreamLdsBytes / rows);
+  // the first shape (matching the forced fields) whose blocks all fit on the
+  // chip at once; per_cu returns the blocks one compute unit holds
+  auto search = [&](int nw, int ks, int nbw, int* pick, int64_t* per_cu) {
+    const int (*shapes)[2] = nw == 8 ? kShapes8 : kShapes4;
+    *pick = -1;
     for (int i = 0; i < 6; ++i) {
-      const int cks = kShapes[i][0], cnbw = kShapes[i][1];
+      const int cks = shapes[i][0], cnbw = shapes[i][1];
       if ((ks && cks != ks) || (nbw && cnbw != nbw)) continue;
       if (G.KG < 2 * cks && cks > 1 && !ks) continue;         // >= 2 groups per wave
       StreamCfg t = p.sc;
       t.ks = cks;
       t.nbw = cnbw;
-      const int64_t lds = rows * row_bytes + (cks > 1 ? 4 * cnbw * p.sc.mb * 1024 : 0);
-      const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(5, kStreamLdsBytes / lds));
-      const int64_t blocks = stream_n_tiles(G, t) * m_chunks;
-      pick = i;
-      if (blocks <= 256 * per_cu) break;
+      t.nw = nw;
+      const int64_t lds = rows * row_bytes + (cks > 1 ? nw * cnbw * p.sc.mb * 1024 : 0);
+      // blocks per compute unit: LDS, and at most 20 waves (the register budget)
+      *per_cu = std::max<int64_t>(1, std::min<int64_t>(20 / nw, kStreamLdsBytes / lds));
+      *pick = i;
+      if (stream_n_tiles(G, t) * m_chunks <= 256 * *per_cu) break;
     }
-    if (pick < 0) pick = 5;
-    ks = kShapes[pick][0];
-    nbw = kShapes[pick][1];
+    return shapes;
+  };
+  int ks = tu.sks, nbw = tu.snbw, nw = tu.swaves ? tu.swaves : (ks == 8 ? 8 : 4);
+  if (!ks || !nbw) {
+    int pick;
+    int64_t per_cu;
+    const int (*shapes)[2] = search(nw, ks, nbw, &pick, &per_cu);
+    // A block whose staged rows fill a compute unit's LDS runs alone on it:
+    // eight waves then share the rows (measured at N = 14336, K = 4096: M =
+    // 16 15.9 -> 15.4 us, M = 32 21.5 -> 18.4 us; M = 1, five blocks per
+    // compute unit, gains nothing)
+    if (!tu.swaves && ks != 1 && pick >= 0 && per_cu == 1) {
+      int pick8;
+      int64_t per_cu8;
+      const int (*shapes8)[2] = search(8, ks, nbw, &pick8, &per_cu8);
+      if (pick8 >= 0) {
+        shapes = shapes8;
+        pick = pick8;
+        nw = 8;
+      }
+    }
+    if (pick < 0) return HM_ERR_TUNING;                        // no shape matches the forced fields
+    ks = shapes[pick][0];
+    nbw = shapes[pick][1];
   }
   p.sc.ks = ks;
   p.sc.nbw = nbw;
+  p.sc.nw = nw;
   const int64_t n_tiles = stream_n_tiles(G, p.sc);
   int64_t splits = tu.ssplits;
   if (splits > G.KG) return HM_ERR_TUNING;
@@ -324,7 +353,7 @@ hm_status launch_moe(const hm_wdesc* d, int32_t afmt, const void* w_dev, const v
   hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, p.s_rows, p.s_max, kTileM, p.big_min,
                                      p.max_s, p.max_t, p.max_b, hdr, su, tu, bu, stream);
   if (e == hipSuccess) {
-    StreamCfg sc{p.s_rows / 16, p.nbw, 1, p.ks, p.lds_kb};
+    StreamCfg sc{p.s_rows / 16, p.nbw, 1, p.ks, p.lds_kb, 4};
     const int64_t nts = stream_n_tiles(a.G, sc);
     int64_t gi = p.max_s * nts;
     if (gi > kGroupedGridStream) gi = kGroupedGridStream;
@@ -480,8 +509,8 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, const 
   const char* w = pair_name(d, afmt);
   const bool a8 = afmt == HM_A_FP8_ROWSCALE;
   if (p.path == P_STREAM)
-    snprintf(buf, buf_len, "%s stream mb=%d nbw=%d ks=%d splits=%d ksg=%d mfma=%s", w, p.sc.mb,
-             p.sc.nbw, p.sc.ks, p.sc.splits, p.ksg, a8 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
+    snprintf(buf, buf_len, "%s stream mb=%d nbw=%d ks=%d waves=%d splits=%d ksg=%d mfma=%s", w, p.sc.mb,
+             p.sc.nbw, p.sc.ks, p.sc.nw, p.sc.splits, p.ksg, a8 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
   else if (p.path == P_BIG) {
     const Geom G = make_geom(d->wfmt, 1, d->n, d->k);
     const int64_t tiles = big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows);
@@ -639,3 +668,4 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   return launch_moe(d, afmt, w_dev, a_in, a_scales, a_rows_are_pairs, t, topk, offsets, sorted_pairs, y,
                     (uint8_t*)ws, p, stream);
 }
+

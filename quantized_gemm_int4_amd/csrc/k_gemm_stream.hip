@@ -14,9 +14,10 @@
 // output columns n) and the activations the "B" operand, so each lane ends
 // with four consecutive n of one row and stores them as one 8-byte write.
 //
-// Work split: a block has four waves; KS of them share one set of NBW
+// Work split: a block has NW waves (4, or 8 for dense calls, so that a
+// block's staged rows feed twice the waves); KS of them share one set of NBW
 // 16-column blocks and split its K range, adding their sums through LDS at
-// the end; 4/KS such sets make one block.  Dense calls may also split K over
+// the end; NW/KS such sets make one block.  Dense calls may also split K over
 // blocks and reduce fp32 partials in a second kernel.
 #include "common.h"
 #include "launch.h"
@@ -36,19 +37,19 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
-template <int KS, int NBW, int MB>
+template <int NW, int KS, int NBW, int MB>
 struct StreamShape {
-  static constexpr int kRedBytes = KS > 1 ? 4 * NBW * MB * 1024 : 0;  // K-split sums
+  static constexpr int kRedBytes = KS > 1 ? NW * NBW * MB * 1024 : 0;  // K-split sums
 };
 
 // Template parameters: MODE (KMode: INT4 / MXFP4 weights, bf16 / FP8 rows), ZP (zero points), MB (16-row
 // blocks per unit), NBW (16-column blocks per wave), KS (waves splitting one
 // column set's K range), DW (weight prefetch ring: K groups of 128 held in
-// registers ahead of use), GROUPED.
+// registers ahead of use), GROUPED, NW (waves per block).
 // Runtime: pg = K groups per activation piece staged in LDS, xb = LDS row
 // stride in bytes (a multiple of 1 KiB plus 16).
-template <int MODE, bool ZP, int MB, int NBW, int KS, int DW, bool GROUPED>
-__global__ void __launch_bounds__(256)
+template <int MODE, bool ZP, int MB, int NBW, int KS, int DW, bool GROUPED, int NW>
+__global__ void __launch_bounds__(64 * NW)
 k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
   constexpr bool MX = MODE == KM_MX_A8;                 // FP8 rows, scaled fp4 x fp8 MFMA
   constexpr bool F4 = MODE == KM_MX_A16 || MODE == KM_MXI4_A16;   // MX codes scaled to bf16
@@ -56,8 +57,8 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
   constexpr bool MXW = MX || F4;                        // E8M0 scale words
   constexpr int ROWS = MB * 16;
   constexpr int GB = MX ? 128 : 256;                    // activation bytes per row per K group
-  constexpr int CS = 4 / KS;                            // column sets per block
-  constexpr int RED = StreamShape<KS, NBW, MB>::kRedBytes;
+  constexpr int CS = NW / KS;                           // column sets per block
+  constexpr int RED = StreamShape<NW, KS, NBW, MB>::kRedBytes;
   // vector-memory loads per ring slot: per column block the 1 KiB tile and
   // its scale word(s), plus the zero-point word
   constexpr int kRingLoads = NBW * (MXW ? 2 : (ZP ? 3 : 2));
@@ -154,7 +155,7 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
       const int total = rcount * cpr;
       const int64_t off0 = (g_begin + gp) * GB;
 #pragma nounroll
-      for (int i = wave; i < total; i += 4) {
+      for (int i = wave; i < total; i += NW) {
         const int r = i / cpr, blk = i - (i / cpr) * cpr;
         const uint64_t ro = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xro_hi, r) << 32) |
                             (uint32_t)__builtin_amdgcn_readlane((int)xro_lo, r);
@@ -410,7 +411,7 @@ k_splitk_reduce(GemmArgs a, int splits) {
 }
 
 int64_t stream_n_tiles(const Geom& G, const StreamCfg& c) {
-  const int64_t cols = (int64_t)(4 / c.ks) * c.nbw;   // 16-column blocks per block
+  const int64_t cols = (int64_t)(c.nw / c.ks) * c.nbw;   // 16-column blocks per block
   return (G.NB + cols - 1) / cols;
 }
 
@@ -434,14 +435,14 @@ static void stream_lds_plan(const GemmArgs& a, const StreamCfg& c, bool grouped,
   *bytes_out = (size_t)(red_bytes + rows * xb);
 }
 
-template <int MODE, bool ZP, int MB, int NBW, int KS, bool GROUPED>
+template <int MODE, bool ZP, int MB, int NBW, int KS, bool GROUPED, int NW>
 static hipError_t go_stream(const GemmArgs& a, const StreamCfg& c, int grid_items, hipStream_t st) {
   // ring depth in K groups, within the 63 outstanding vector-memory operations
   // one wave can track (up to three loads per group and column block) and a
   // register budget that leaves room for four waves per SIMD at small M
   constexpr int DW = (NBW == 1 && MB == 1 && KS < 4) ? 16 : 8;
-  constexpr int RED = StreamShape<KS, NBW, MB>::kRedBytes;
-  auto kern = &k_gemm_stream<MODE, ZP, MB, NBW, KS, DW, GROUPED>;
+  constexpr int RED = StreamShape<NW, KS, NBW, MB>::kRedBytes;
+  auto kern = &k_gemm_stream<MODE, ZP, MB, NBW, KS, DW, GROUPED, NW>;
   int pg, xb;
   size_t lds;
   stream_lds_plan(a, c, GROUPED, RED, &pg, &xb, &lds);
@@ -458,16 +459,24 @@ static hipError_t go_stream(const GemmArgs& a, const StreamCfg& c, int grid_item
     const int64_t m_chunks = (a.M + MB * 16 - 1) / (MB * 16);
     grid = dim3((unsigned)n_tiles, (unsigned)c.splits, (unsigned)m_chunks);
   }
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, a, (int)n_tiles, pg, xb);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, st, a, (int)n_tiles, pg, xb);
   return hipGetLastError();
 }
 
 template <int MODE, bool ZP, int MB, int NBW, bool GROUPED>
 static hipError_t go_stream_ks(const GemmArgs& a, const StreamCfg& c, int gi, hipStream_t st) {
+  if (!GROUPED && c.nw == 8) {
+    // eight waves per block (dense only): K split over 2, 4 or 8 of them
+    switch (c.ks) {
+      case 8: return go_stream<MODE, ZP, MB, NBW, 8, GROUPED, 8>(a, c, gi, st);
+      case 4: return go_stream<MODE, ZP, MB, NBW, 4, GROUPED, 8>(a, c, gi, st);
+      default: return go_stream<MODE, ZP, MB, NBW, 2, GROUPED, 8>(a, c, gi, st);
+    }
+  }
   switch (c.ks) {
-    case 4: return go_stream<MODE, ZP, MB, NBW, 4, GROUPED>(a, c, gi, st);
-    case 2: return go_stream<MODE, ZP, MB, NBW, 2, GROUPED>(a, c, gi, st);
-    default: return go_stream<MODE, ZP, MB, NBW, 1, GROUPED>(a, c, gi, st);
+    case 4: return go_stream<MODE, ZP, MB, NBW, 4, GROUPED, 4>(a, c, gi, st);
+    case 2: return go_stream<MODE, ZP, MB, NBW, 2, GROUPED, 4>(a, c, gi, st);
+    default: return go_stream<MODE, ZP, MB, NBW, 1, GROUPED, 4>(a, c, gi, st);
   }
 }
 

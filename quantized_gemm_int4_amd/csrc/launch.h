@@ -63,8 +63,9 @@ struct StreamCfg {
   int mb;      // 16-row blocks per unit: 1 or 2
   int nbw;     // 16-column blocks per wave: 1 or 2
   int splits;  // dense split-K factor (over blocks, fp32 partials)
-  int ks;      // waves of a block splitting one column set's K range: 1, 2 or 4
+  int ks;      // waves of a block splitting one column set's K range: 1, 2 or 4 (8 with nw = 8)
   int lds_kb;  // dynamic LDS budget per block in KiB (0: the 159 KiB maximum)
+  int nw;      // waves per block: 4, or 8 (dense only, ks 2, 4 or 8)
 };
 // blocks along N (dense) or n tiles per unit (grouped) of a streaming launch
 int64_t stream_n_tiles(const Geom& G, const StreamCfg& c);

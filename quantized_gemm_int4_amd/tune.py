@@ -52,6 +52,8 @@ def dense_candidates(desc, afmt, m):
         if path == 1:
             combos = [dict(path=1, stream_ks=ks, stream_nbw=nbw, stream_splits=sp)
                       for ks, nbw, sp in itertools.product((1, 2, 4), (1, 2), (1, 2, 4, 8)) if sp <= kg]
+            combos += [dict(path=1, stream_waves=8, stream_ks=ks, stream_nbw=nbw, stream_splits=sp)
+                       for ks, nbw, sp in itertools.product((2, 4, 8), (1, 2), (1, 2, 4)) if sp <= kg]
         else:
             combos = [dict(path=path)]
         for c in combos:

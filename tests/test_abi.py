@@ -312,3 +312,4 @@ def test_tuning_table_lookup(tmp_path):
     assert t2.lookup(d, 0, 5000) is None                           # beyond: the largest
     assert t2.lookup(hm.wdesc("uint4_zp", 512, 2048), 0, 16) is None
     assert t2.meta["device"] == "test"
+

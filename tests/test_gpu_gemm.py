@@ -282,3 +282,17 @@ def test_tp8_shard_shapes(n, k, m):
     128-row and 256-row paths."""
     L = Layer(quant.FMT_UINT4_ZP, n, k, cfg=18, wseed=n + m)
     L.check(synthetic.activations(18, m, k, index=m))
+
+
+@pytest.mark.parametrize("fmt", quant.FORMATS)
+@pytest.mark.parametrize("ks", [2, 4, 8])
+@pytest.mark.parametrize("nbw", [1, 2])
+@pytest.mark.parametrize("m,splits", [(1, 1), (16, 2), (32, 1)])
+def test_stream_eight_wave_blocks(fmt, ks, nbw, m, splits):
+    """Dense streaming with eight waves per block: K split over 2, 4 or 8 of
+    them (9 groups: uneven slices, waves with one group or none), one or two
+    column blocks per wave, N ragged against the block's column sets, with
+    and without a K split over blocks."""
+    L = Layer(fmt, 216, 1152, cfg=21, wseed=ks + 5 * nbw)
+    x = synthetic.activations(21, m, 1152, index=m)
+    L.check(x, tuning=dict(path=1, stream_waves=8, stream_ks=ks, stream_nbw=nbw, stream_splits=splits))
