@@ -243,6 +243,25 @@ hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const 
 hm_status hm_moe_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
                            int32_t a_rows_are_pairs, const hm_tuning* tune, char* buf, size_t buf_len);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * grouped GEMM as hm_moe_gemm, with the schedule's work lists kept in a
+ * static device array of hm_moe_gemm_static_max_workspace() bytes (4 MiB)
+ * inside the library instead of a caller workspace.  Each GPU holds its own
+ * array until the process ends; its address is resolved once per device on
+ * the first call with that device current.  The call allocates nothing.
+ * Calls whose work lists exceed the array (hm_moe_gemm_workspace_size >
+ * the maximum, about three million routed pairs with the default tuning)
+ * return HM_ERR_WORKSPACE before any launch.  All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (different streams, or host
+ * threads) race and must be serialized by the caller.  Every other argument,
+ * check and result is as for hm_moe_gemm. */
+size_t hm_moe_gemm_static_max_workspace(void);
+hm_status hm_moe_gemm_static(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* a,
+                             const void* a_scales, int32_t a_rows_are_pairs, int64_t t, int32_t topk,
+                             const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* y,
+                             const hm_tuning* tune, hipStream_t stream);
+
 /* ------------------------------------------------------- MoE block steps */
 
 /* Gated activation between the gate_up and down grouped GEMMs of an MoE

@@ -97,11 +97,14 @@ def _load():
         "hm_silu_mul": [P, I64, I64, P, P],
         "hm_moe_combine": [P, P, I64, I32, I64, P, P],
         "hm_read_probe": [P, I64, I32, I32, P, P],
+        "hm_moe_gemm_static": [D, P, I32, P, P, I32, I64, I32, P, P, P, T, P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
         f.argtypes = args
         f.restype = ctypes.c_int
+    L.hm_moe_gemm_static_max_workspace.argtypes = []
+    L.hm_moe_gemm_static_max_workspace.restype = ctypes.c_size_t
     L.hm_status_string.argtypes = [ctypes.c_int]
     L.hm_status_string.restype = ctypes.c_char_p
     return L
@@ -276,6 +279,27 @@ def hm_moe_gemm(desc, w_dev, a, offsets, sorted_pairs, t, topk, a_rows_are_pairs
                                        _ptr(offsets), _ptr(sorted_pairs), _ptr(y), _ptr(ws),
                                        ws.numel(), _tune(tuning), _stream(stream)))
     return y
+
+
+def hm_moe_gemm_static(desc, w_dev, a, offsets, sorted_pairs, t, topk, a_rows_are_pairs, a_scales=None,
+                       y=None, afmt=None, tuning=None, stream=None):
+    """hm_moe_gemm with the library's static work-list array instead of a
+    workspace (no device allocation in the call; calls on one GPU must not
+    overlap).  y may be passed in so that nothing is allocated here either."""
+    afmt = _afmt(a) if afmt is None else afmt
+    P = t * topk
+    if y is None:
+        y = torch.empty(P, desc.n, dtype=torch.bfloat16, device=a.device)
+    _need(y, torch.bfloat16, P * desc.n, "y")
+    _ok("hm_moe_gemm_static", lib.hm_moe_gemm_static(ctypes.byref(desc), _ptr(w_dev), int(afmt), _ptr(a),
+                                                     _ptr(a_scales), int(a_rows_are_pairs), int(t), int(topk),
+                                                     _ptr(offsets), _ptr(sorted_pairs), _ptr(y), _tune(tuning),
+                                                     _stream(stream)))
+    return y
+
+
+def hm_moe_gemm_static_max_workspace():
+    return lib.hm_moe_gemm_static_max_workspace()
 
 
 # --------------------------------------------------------------- MoE block steps

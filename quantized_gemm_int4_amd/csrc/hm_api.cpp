@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/hm.h"
 #include "common.h"
@@ -669,3 +670,57 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
                     (uint8_t*)ws, p, stream);
 }
 
+// ------------------------------------------------ allocation-free grouped GEMM
+//
+// The work lists of hm_moe_gemm_static live in this file-scope device array
+// (each GPU the library runs on holds its own copy until the process ends).
+// In host code its name is only a stand-in: the device address comes from
+// hipGetSymbolAddress, resolved once per device with that device current.
+namespace {
+constexpr size_t kStaticScratchBytes = 4u << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hm_status scratch_of_current_device(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return HM_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (uint8_t*)g_scratch_ptr[dev];
+  return HM_OK;
+}
+}  // namespace
+
+HM_API size_t hm_moe_gemm_static_max_workspace(void) { return kStaticScratchBytes; }
+
+HM_API hm_status hm_moe_gemm_static(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* a_in,
+                                    const void* a_scales, int32_t a_rows_are_pairs, int64_t t, int32_t topk,
+                                    const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* y,
+                                    const hm_tuning* tune, hipStream_t stream) {
+  Tune tu;
+  hm_status s = moe_common(d, afmt, t, topk, tune, &tu);
+  if (s) return s;
+  if (a_rows_are_pairs != 0 && a_rows_are_pairs != 1) return HM_ERR_SHAPE;
+  if (t == 0) return HM_OK;
+  if (!w_dev || !a_in || !offsets || !sorted_pairs || !y) return HM_ERR_NULL;
+  if (afmt == HM_A_FP8_ROWSCALE && !a_scales) return HM_ERR_NULL;
+  if (!aligned(w_dev, 256) || !aligned(a_in, 16) || !aligned(y, 16) || !aligned(offsets, 4) ||
+      !aligned(sorted_pairs, 4))
+    return HM_ERR_ALIGN;
+  if (a_scales && !aligned(a_scales, 4)) return HM_ERR_ALIGN;
+  MoePlan p;
+  if ((s = plan_moe(d, afmt, t, topk, a_rows_are_pairs, tu, &p))) return s;
+  if (p.ws_bytes > kStaticScratchBytes) return HM_ERR_WORKSPACE;
+  uint8_t* ws = nullptr;
+  if ((s = scratch_of_current_device(&ws))) return s;
+  // the schedule writes the header and every unit it counts, so nothing of
+  // the previous call's contents is read
+  return launch_moe(d, afmt, w_dev, a_in, a_scales, a_rows_are_pairs, t, topk, offsets, sorted_pairs, y, ws, p,
+                    stream);
+}

@@ -313,3 +313,22 @@ def test_tuning_table_lookup(tmp_path):
     assert t2.lookup(hm.wdesc("uint4_zp", 512, 2048), 0, 16) is None
     assert t2.meta["device"] == "test"
 
+
+def test_static_moe_gemm_limits():
+    """The allocation-free grouped GEMM rejects calls whose work lists exceed
+    its static array (HM_ERR_WORKSPACE) and bad arguments before any launch."""
+    P = ctypes.c_void_p
+    good = P(0x100000)
+    cap = hm.hm_moe_gemm_static_max_workspace()
+    assert cap == 4 << 20
+    d = hm.wdesc("int4_sym", 4096, 7168, 256)
+    t_big = 500000                                              # 4 million pairs
+    assert hm.hm_moe_gemm_workspace_size(d, 0, t_big, 8) > cap
+    assert hm.hm_moe_gemm_workspace_size(d, 0, 200000, 8) <= cap
+    args = (ctypes.byref(d), good, 0, good, None, 0)
+    assert _err("hm_moe_gemm_static", *args, t_big, 8, good, good, good, None, None) == 5
+    assert _err("hm_moe_gemm_static", *args, 0, 8, None, None, None, None, None) == 0      # t = 0
+    assert _err("hm_moe_gemm_static", *args, 64, 8, None, good, good, None, None) == 1     # no offsets
+    assert _err("hm_moe_gemm_static", *args, 64, 8, good, good, P(0x100008), None, None) == 3
+    assert _err("hm_moe_gemm_static", ctypes.byref(d), good, 0, good, None, 2, 64, 8, good, good, good,
+                None, None) == 2
