@@ -8,10 +8,15 @@ flops of the step / step time (TFLOP/s).  Weights rotate through enough
 distinct copies (>= 2 x 256 MB) that the 256 MB last-level cache cannot serve
 them; activations are resident in HBM before the timed region starts.
 
+The same line carries the MoE half of the metric under "moe": the grouped
+GEMMs of the 256-expert top-8 MoE layer with symmetric INT4 weights and bf16
+rows at T = 64, 1024, 8192, and with MXFP4 weights and per-token FP8 rows at
+T = 16384 (TFLOP/s, weight GB/s and roofline fraction per T), each checked
+against the oracle on sampled pairs in its own cpu_baseline.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_w4a16|dense_w4a8|moe_w4a16|moe_w4a8|moe_w4a16_mxfp4|moe_w4a16_mxint4|shards]
 
-One JSON line is printed (rank 0).  Extra workloads exist for measurement; the
-default line is the dense W4A16 sweep.
+One JSON line is printed (rank 0).
 """
 import argparse
 import hashlib
@@ -41,7 +46,9 @@ def parse():
                    choices=["dense_w4a16", "dense_w4a8", "moe_w4a16", "moe_w4a8", "moe_w4a16_mxfp4",
                             "moe_w4a16_mxint4", "shards"])
     p.add_argument("--reps", type=int, default=30, help="launches per M for per-kernel timing")
-    p.add_argument("--no-cpu", action="store_true", help="skip the oracle (cpu_baseline) leg")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle (cpu_baseline) legs")
+    p.add_argument("--no-moe", action="store_true",
+                   help="default workload: skip the MoE half of the metric (grouped GEMM figures)")
     p.add_argument("--counters-run", action="store_true",
                    help="launches only, for rocprofv3 --pmc: each M of the dense sweep 3 times "
                         "between marker kernels, then a 512 MiB copy for calibration")
@@ -281,7 +288,39 @@ def run_dense(args, fmt):
                config=dict(workload=wl, weight_copies=S["copies"],
                            weight_bytes_per_copy=S["wbytes"], algorithmic_weight_bytes=alg_w),
                sweep=sweep, roofline=roof, cpu_baseline=cpu)
+    if fmt == "uint4_zp" and not args.no_moe:
+        # the MoE half of the metric: the grouped GEMMs of the W4A16 MoE layer
+        # at every token count and of the W4A8-MXFP4 layer at T = 16384
+        del S
+        torch.cuda.empty_cache()
+        out["moe"] = moe_half(args)
     return out
+
+
+def moe_half(args):
+    import torch
+    res = {}
+    cpus = []
+    for key, fmt, a8, ts in (("w4a16_int4sym", "int4_sym", False, [64, 1024, 8192]),
+                             ("w4a8_mxfp4", "mxfp4", True, [16384])):
+        per_t, state = moe_measure(args, fmt, a8, ts, cpu_sample=not args.no_cpu)
+        name = "W4A8-MXFP4 (E2M1 + E8M0/32, per-token FP8 E4M3)" if a8 else "W4A16 int4-sym G128 (bf16 scales)"
+        res[key] = dict(workload=f"MoE {name}, 256 experts top-8 Zipf(1.1) router, gate_up N=4096 K=7168 + "
+                                 f"down N=7168 K=2048, T={ts}; one call = expert sort + gate_up + down",
+                        **moe_summary(per_t, a8, False))
+        if not args.no_cpu:
+            cpus.append((key, cpu_moe(state, budget_s=10.0)))
+        del state
+        torch.cuda.empty_cache()
+    if cpus:
+        flops_s = [c["value"] for _, c in cpus]
+        res["cpu_baseline"] = dict(value=round(float(np.mean(flops_s)), 6), unit="TFLOP/s", cores=cpu_threads(),
+                                   kind="oracle", host_cpus=os.cpu_count(),
+                                   sample="; ".join(f"{k}: {c['sample']}" for k, c in cpus),
+                                   parity_ok=all(c["parity_ok"] for _, c in cpus),
+                                   parity_worst_ratio=max(c["parity_worst_ratio"] for _, c in cpus),
+                                   per_workload={k: c for k, c in cpus})
+    return res
 
 
 def cpu_dense(S, fmt, n, k, ms, hm, torch):
@@ -377,43 +416,41 @@ def run_shards(args):
                 shards=shapes, roofline=None, cpu_baseline=None)
 
 
-def run_moe(args, fmt, a8):
-    """a8: FP8 rows (W4A8-MXFP4); otherwise bf16 rows with any weight format."""
+MOE_E, MOE_TOPK, MOE_H, MOE_I = 256, 8, 7168, 2048
+
+
+def moe_measure(args, fmt, a8, ts, cpu_sample=False):
+    """The grouped GEMMs of one MoE layer (256 experts, top-8 Zipf(1.1)
+    routing, gate_up N=4096 K=7168, down N=7168 K=2048) at each token count
+    of ts.  One step = expert sort + gate_up + down grouped GEMMs (+ the
+    per-token FP8 quantization of both inputs for FP8 rows), timed as HIP
+    graph replays.  Weights are random standard-format codes drawn on the
+    device; activations N(0,1) bf16 (down: an independent [P, 2048] input).
+    Returns (per-T figures, state the oracle leg needs)."""
     import torch
     import quantized_gemm_int4_amd as hm
     import synthetic
 
     dev = torch.device("cuda:0")
-    E, topk, H, I = 256, 8, 7168, 2048
-    ts = [16384] if a8 else [64, 1024, 8192]
-    g = torch.Generator(device="cuda")
-    g.manual_seed(5)
+    E, topk, H, I = MOE_E, MOE_TOPK, MOE_H, MOE_I
 
-    def weights(n, k):
-        codes = torch.randint(0, 256, (E, n, k // 2), dtype=torch.uint8, device=dev, generator=g)
-        if fmt in ("mxfp4", "mxint4"):
-            sc = torch.randint(118, 122, (E, n, k // 32), dtype=torch.uint8, device=dev, generator=g)
-        else:
-            sc = (0x3B00 + torch.randint(0, 0x100, (E, n, k // 128), device=dev, generator=g)).to(torch.int16)
+    def weights(n, k, seed):
+        codes, sc, zeros = synthetic.random_std_format_dev(fmt, E, n, k, seed)
         d = hm.wdesc(fmt, n, k, E)
-        w = hm.hm_transform(d, codes, sc, None)
-        del codes, sc
-        return d, w
+        return d, hm.hm_transform(d, codes, sc, zeros), (codes, sc)
 
-    d_gu, w_gu = weights(2 * I, H)
-    d_dn, w_dn = weights(H, I)
+    d_gu, w_gu, std_gu = weights(2 * I, H, 5)
+    d_dn, w_dn, std_dn = weights(H, I, 6)
     afmt = 1 if a8 else 0
     per_t = []
+    keep = []
     tm = Timer(torch)
-    step_ms = 0.0
-    step_fl = 0.0
     for t in ts:
         ids, rw = synthetic.router_topk(5 if a8 else 4, t, E, topk)
         P = t * topk
         ids_d = torch.from_numpy(ids).to(dev)
-        x = torch.from_numpy(synthetic.activations(4, t, H, index=t).view(np.int16)).view(torch.bfloat16).to(dev)
-        a2 = torch.from_numpy(synthetic.activations(4, P, I, index=t, role=synthetic.ROLE_DOWN)
-                              .view(np.int16)).view(torch.bfloat16).to(dev)
+        x = synthetic.activations_dev(10 + t, t, H)
+        a2 = synthetic.activations_dev(20 + t, P, I)
         y1 = torch.empty(P, 2 * I, dtype=torch.bfloat16, device=dev)
         y2 = torch.empty(P, H, dtype=torch.bfloat16, device=dev)
         cnt = torch.empty(E, dtype=torch.int32, device=dev)
@@ -424,6 +461,7 @@ def run_moe(args, fmt, a8):
         rw_d = torch.from_numpy(rw).to(dev)
         hbuf = torch.empty(P, I, dtype=torch.bfloat16, device=dev)
         out = torch.empty(t, H, dtype=torch.bfloat16, device=dev)
+        x8 = xs = a8b = as_ = None
         if a8:
             x8 = torch.empty(t, H, dtype=torch.uint8, device=dev)
             xs = torch.empty(t, dtype=torch.float32, device=dev)
@@ -473,11 +511,12 @@ def run_moe(args, fmt, a8):
             ms = tm.stop_ms() / k
             del g_warm, g_steps
             return ms
-        ms_t = timed(step, args.steps)
-        block_ms = timed(block, args.steps)
+        msteps = max(2, min(args.steps, 10))
+        block_ms = timed(block, msteps)
         reps = max(args.reps, 1)
         silu_ms = timed(lambda: hm.hm_silu_mul(y1, hbuf), reps)
         comb_ms = timed(lambda: hm.hm_moe_combine(y2, rw_d, topk, out), reps)
+        ms_t = timed(step, msteps)          # last: y1, y2 of the step stay for the oracle leg
         silu_b = P * (2 * I) * 2 + P * I * 2               # read gate | up, write h
         comb_b = P * H * 2 + t * H * 2 + P * 4             # read pair rows and weights, write tokens
         counts = np.bincount(ids.ravel(), minlength=E)
@@ -486,30 +525,20 @@ def run_moe(args, fmt, a8):
         wb = act * (weight_bytes(2 * I, H, fmt) + weight_bytes(H, I, fmt))
         peak = FP8_PEAK_TFLOPS if a8 else BF16_PEAK_TFLOPS
         t_roof = max(wb / (HBM_PEAK_GBS * 1e9), fl / (peak * 1e12))
+        bound = "mfma" if fl / (peak * 1e12) >= wb / (HBM_PEAK_GBS * 1e9) else "hbm"
         per_t.append(dict(T=t, ms=round(ms_t, 4), tflops=round(fl / ms_t / 1e9, 3),
                           weight_GBps=round(wb / ms_t / 1e6, 1), active_experts=act,
                           max_rows=int(counts.max()), roofline_frac=round(t_roof / (ms_t * 1e-3), 4),
-                          bound="mfma" if fl / (peak * 1e12) >= wb / (HBM_PEAK_GBS * 1e9) else "hbm",
-                          flops=fl, weight_bytes=wb,
-                          block_ms=round(block_ms, 4),
+                          bound=bound, flops=fl, weight_bytes=wb, block_ms=round(block_ms, 4),
                           silu_mul=dict(us=round(silu_ms * 1e3, 2), GBps=round(silu_b / silu_ms / 1e6, 1),
                                         hbm_frac=round(silu_b / silu_ms / 1e6 / HBM_PEAK_GBS, 4)),
                           combine=dict(us=round(comb_ms * 1e3, 2), GBps=round(comb_b / comb_ms / 1e6, 1),
-                                       hbm_frac=round(comb_b / comb_ms / 1e6 / HBM_PEAK_GBS, 4))))
-        step_ms += ms_t
-        step_fl += fl
-    name = "W4A8-MXFP4" if a8 else {"mxfp4": "W4A16-MXFP4 (E2M1 + E8M0/32, bf16 rows)",
-                                     "mxint4": "W4A16-MXINT4 (1.2 fixed-point INT4 + E8M0/32, bf16 rows)"}.get(
-                                         fmt, "W4A16 int4-sym G128")
-    wl = (f"MoE {name} 256 experts top-8 "
-          f"Zipf(1.1) router, gate_up N=4096 K=7168 + down N=7168 K=2048, T={ts}, sort included; "
-          f"block_ms adds the SiLU product, the down GEMM on its output and the weighted combine")
-    return dict(metric=METRIC, value=round(step_fl / (step_ms * 1e-3) / 1e12, 3), unit="TFLOP/s",
-                n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=round(step_ms, 4),
-                higher_is_better=True, scaling="weak", vs_baseline=None,
-                dtype="fp8" if a8 else "bf16", data="synthetic",
-                config=dict(workload=wl), per_T=per_t, roofline=moe_roofline(per_t, a8, fmt in ("mxfp4", "mxint4") and not a8),
-                cpu_baseline=None)
+                                       hbm_frac=round(comb_b / comb_ms / 1e6 / HBM_PEAK_GBS, 4)),
+                          plan_gate_up=hm.hm_moe_gemm_plan(d_gu, afmt, t, topk, 0)))
+        if cpu_sample:
+            keep.append(dict(t=t, ids=ids, x=x, a2=a2, y1=y1, y2=y2))
+    state = dict(fmt=fmt, a8=a8, std_gu=std_gu, std_dn=std_dn, keep=keep)
+    return per_t, state
 
 
 def moe_roofline(per_t, a8, f4=False):
@@ -530,6 +559,115 @@ def moe_roofline(per_t, a8, f4=False):
     return dict(bound="hbm", kernel=kern,
                 achieved=round(a, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(a / HBM_PEAK_GBS, 4),
                 per_launch=f"weight bytes of the active experts at T={r['T']}", traffic=None)
+
+
+def moe_sample_pairs(ids, rng, per_chunk=2, experts_per_bucket=2):
+    """Pairs to check: some of every 256-row chunk of the largest expert
+    (including its last, partial chunk) and of a few experts in each
+    row-count bucket, so every unit kind of the schedule is sampled."""
+    flat = ids.ravel()
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=MOE_E)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    picks = []
+    big = int(np.argmax(counts))
+    seg = order[starts[big]:starts[big + 1]]
+    for c0 in range(0, seg.size, 256):
+        ch = seg[c0:c0 + 256]
+        picks += [ch[0], ch[-1]] + list(rng.choice(ch, min(per_chunk, ch.size), replace=False))
+    for lo, hi in [(1, 16), (17, 64), (65, 128), (129, 256), (257, 1 << 30)]:
+        es = [e for e in range(MOE_E) if lo <= counts[e] <= hi and e != big]
+        for e in (rng.choice(es, min(experts_per_bucket, len(es)), replace=False) if es else []):
+            seg = order[starts[e]:starts[e + 1]]
+            picks += [seg[0], seg[-1]]
+    return np.unique(np.array(picks, dtype=np.int64))
+
+
+def cpu_moe(state, budget_s=20.0):
+    """The oracle (plain NumPy fp64) on sampled pairs of the timed MoE calls:
+    exact dequantization of each sampled expert's weights, the fp64 GEMM of
+    its sampled rows and the |x||w| bound, for gate_up and down; checks the
+    GPU outputs of those pairs.  Stops adding token counts once `budget_s`
+    seconds of oracle time are used."""
+    import torch
+    from oracle import codecs, gemm, quant
+
+    fmt, a8 = state["fmt"], state["a8"]
+    t0 = time.perf_counter()
+    flops, worst, ok, npairs, nexp, desc = 0.0, 0.0, True, 0, 0, []
+    rng = np.random.default_rng(3)
+    for kp in state["keep"]:
+        if time.perf_counter() - t0 > budget_s:
+            break
+        ids = kp["ids"]
+        flat = ids.ravel()
+        pairs = moe_sample_pairs(ids, rng)
+        for proj, std, a, y, n, k, rows_are_pairs in (
+                ("gate_up", state["std_gu"], kp["x"], kp["y1"], 2 * MOE_I, MOE_H, False),
+                ("down", state["std_dn"], kp["a2"], kp["y2"], MOE_H, MOE_I, True)):
+            arows = pairs if rows_are_pairs else pairs // MOE_TOPK
+            ab = a[torch.from_numpy(arows).to(a.device)].view(torch.int16).cpu().numpy().view(np.uint16)
+            if a8:
+                c8, s8 = quant.quant_fp8_rows(ab)
+                xh = quant.fp8_rows_dequant(c8, s8)
+            else:
+                xh = codecs.bf16_value(ab).astype(np.float64)
+            yg = y[torch.from_numpy(pairs).to(y.device)].view(torch.int16).cpu().numpy().view(np.uint16)
+            yref = np.zeros((pairs.size, n))
+            bnd = np.zeros((pairs.size, n))
+            for e in np.unique(flat[pairs]):
+                sel = np.nonzero(flat[pairs] == e)[0]
+                c = std[0][int(e)].cpu().numpy()
+                sc = std[1][int(e)].cpu().numpy()
+                what = quant.dequant(fmt, c, sc if fmt in quant.MX_FORMATS else sc.view(np.uint16)).astype(np.float64)
+                yref[sel], bnd[sel] = gemm.gemm_ref(xh[sel], what, bound_dtype=np.float32)
+                flops += 2.0 * sel.size * n * k
+                nexp += 1
+            r = gemm.check(yg, yref, bnd)
+            ok = ok and r["ok"]
+            worst = max(worst, r["worst_ratio"])
+            npairs += pairs.size
+        desc.append(kp["t"])
+    dt = time.perf_counter() - t0
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", kind="oracle",
+                sample=f"{npairs} sampled (pair, projection) rows at T={desc} (every 256-row chunk of the "
+                       f"largest expert and experts of every row-count bucket), {nexp} expert dequantizations "
+                       f"+ fp64 GEMM and bound; {dt:.2f} s",
+                parity_ok=bool(ok), parity_worst_ratio=round(worst, 4))
+
+
+def moe_summary(per_t, a8, f4):
+    return dict(per_T=[{k: v for k, v in e.items() if k not in ("flops", "weight_bytes")} for e in per_t],
+                roofline=moe_roofline(per_t, a8, f4))
+
+
+def run_moe(args, fmt, a8):
+    """a8: FP8 rows (W4A8-MXFP4); otherwise bf16 rows with any weight format."""
+    ts = [16384] if a8 else [64, 1024, 8192]
+    per_t, state = moe_measure(args, fmt, a8, ts, cpu_sample=not args.no_cpu)
+    step_ms = sum(e["ms"] for e in per_t)
+    step_fl = sum(e["flops"] for e in per_t)
+    name = "W4A8-MXFP4" if a8 else {"mxfp4": "W4A16-MXFP4 (E2M1 + E8M0/32, bf16 rows)",
+                                     "mxint4": "W4A16-MXINT4 (1.2 fixed-point INT4 + E8M0/32, bf16 rows)"}.get(
+                                         fmt, "W4A16 int4-sym G128")
+    wl = (f"MoE {name} 256 experts top-8 "
+          f"Zipf(1.1) router, gate_up N=4096 K=7168 + down N=7168 K=2048, T={ts}, sort included; "
+          f"block_ms adds the SiLU product, the down GEMM on its output and the weighted combine")
+    cpu = None if args.no_cpu else cpu_moe(state)
+    if cpu:
+        cpu.update(cores=cpu_threads(), host_cpus=os.cpu_count())
+    return dict(metric=METRIC, value=round(step_fl / (step_ms * 1e-3) / 1e12, 3), unit="TFLOP/s",
+                n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=round(step_ms, 4),
+                higher_is_better=True, scaling="weak", vs_baseline=None,
+                dtype="fp8" if a8 else "bf16", data="synthetic",
+                config=dict(workload=wl), per_T=moe_summary(per_t, a8, fmt in ("mxfp4", "mxint4") and not a8)["per_T"],
+                roofline=moe_roofline(per_t, a8, fmt in ("mxfp4", "mxint4") and not a8),
+                cpu_baseline=cpu)
+
+
+def cpu_threads():
+    from threadpoolctl import threadpool_info
+    return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
 
 
 def counters_run(fmt):
