@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="dense_w4a16",
                    choices=["dense_w4a16", "dense_w4a8", "moe_w4a16", "moe_w4a8", "moe_w4a16_mxfp4",
-                            "moe_w4a16_mxint4", "shards"])
+                            "moe_w4a16_mxint4", "shards", "readfloor"])
     p.add_argument("--reps", type=int, default=30, help="launches per M for per-kernel timing")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle (cpu_baseline) legs")
     p.add_argument("--no-moe", action="store_true",
@@ -665,6 +665,42 @@ def run_moe(args, fmt, a8):
                 cpu_baseline=cpu)
 
 
+def run_readfloor(args):
+    """Plain-read floor of the decode shape: hm_read_probe reads the dense
+    layer's weight bytes (N=14336, K=4096, uint4 + zero point: 30.5 MB) once
+    per call with 16-byte loads, rotating over copies that exceed the
+    last-level cache, timed like the GEMM (graph of back-to-back calls)."""
+    import torch
+    import quantized_gemm_int4_amd as hm
+    nbytes = int(weight_bytes(14336, 4096, "uint4_zp"))
+    copies = int(np.ceil(2 * LLC_BYTES / nbytes)) + 1
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1) for _ in range(copies)]
+    tm = Timer(torch)
+    ctr = [0]
+    res = []
+    for blocks, unroll in ((1024, 2), (2048, 4), (2048, 8), (4096, 2)):
+        out = torch.empty(blocks, dtype=torch.int32, device="cuda:0")
+
+        def fn(blocks=blocks, unroll=unroll, out=out):
+            for _ in range(args.reps):
+                hm.hm_read_probe(bufs[ctr[0] % copies], blocks, unroll, out)
+                ctr[0] += 1
+        g = capture(torch, fn)
+        g.replay()
+        torch.cuda.synchronize()
+        tm.start()
+        g.replay()
+        us = tm.stop_ms() * 1e3 / args.reps
+        res.append(dict(blocks=blocks, unroll=unroll, us=round(us, 3), GBps=round(nbytes / us / 1e3, 1),
+                        hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)))
+    best = min(res, key=lambda r: r["us"])
+    return dict(metric="plain-read floor GB/s", value=best["GBps"], unit="GB/s", n_gpus=1, steps=args.reps,
+                warmup=1, ms_per_step=round(best["us"] / 1e3, 5), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="u8", data="synthetic",
+                config=dict(workload=f"hm_read_probe over {nbytes} bytes (the dense W4A16 layer's weights), "
+                                     f"{copies} rotating copies"), shapes=res, roofline=None, cpu_baseline=None)
+
+
 def cpu_threads():
     from threadpoolctl import threadpool_info
     return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
@@ -774,6 +810,8 @@ def main():
         sys.exit(2)
     if args.workload == "shards":
         out = run_shards(args)
+    elif args.workload == "readfloor":
+        out = run_readfloor(args)
     elif args.workload.startswith("dense"):
         out = run_dense(args, "mxfp4" if args.workload == "dense_w4a8" else "uint4_zp")
     else:
