@@ -79,17 +79,24 @@ typedef enum hm_wfmt {
                         without a definition, this is the MX-family reading */
 } hm_wfmt;
 
-/* Activation format (the compute option choosing A16 or A8). */
+/* Activation format (the compute option choosing A16, A8 or A4). */
 typedef enum hm_afmt {
-  HM_A_BF16 = 0,        /* X is bf16 [M,K]; x_row_scale unused (may be NULL) */
-  HM_A_FP8_ROWSCALE = 1 /* X is OCP E4M3 bytes [M,K] with one fp32 scale per row: x = e4m3(c)*s[m] */
+  HM_A_BF16 = 0,         /* X is bf16 [M,K]; x_scales unused (may be NULL) */
+  HM_A_FP8_ROWSCALE = 1, /* X is OCP E4M3 bytes [M,K] with one fp32 scale per row: x = e4m3(c)*s[m] */
+  HM_A_MXFP4 = 2         /* X is E2M1 codes [M][K/2] (value 2j in the low nibble of byte j) with E8M0
+                            scale bytes [M][K/32] in x_scales: x = e2m1(c) * 2^(b-127) (W4A4) */
 } hm_afmt;
 
 /* Supported pairs: every weight format with HM_A_BF16 (W4A16: INT4_SYM,
  *                  UINT4_ZP, and MXFP4 / MXINT4, whose codes are scaled to
  *                  bf16 in the kernel; the pages list MXFP4 W4A16 among the
  *                  MoE results, aihaber.org article, performance section);
- *                  MXFP4 with HM_A_FP8_ROWSCALE (W4A8-MXFP4).
+ *                  MXFP4 with HM_A_FP8_ROWSCALE (W4A8-MXFP4); MXFP4 with
+ *                  HM_A_MXFP4 (W4A4: both operands E2M1 with E8M0 scales on
+ *                  the scaled fp4 MFMA; the pages list W4A4 among the GEMM
+ *                  types, cocoloop.cn news item, format list).  W4A4 runs on
+ *                  the streaming kernel (path 1) and the 128 x 128 kernel
+ *                  (path 4) only.
  * MXFP4 with bf16 rows requires every |w| < 2^128 (E8M0 scale bytes up to
  * 252 always satisfy it, up to 253 for MXINT4; larger products become inf,
  * and the row's sums NaN):
@@ -172,6 +179,18 @@ hm_status hm_dequant(const hm_wdesc* d, const void* w_dev, size_t w_bytes, int32
 hm_status hm_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* x8,
                             float* row_scale, hipStream_t stream);
 
+/* MXFP4 activation rows (the W4A4 pair: 4-bit weights with 4-bit
+ * activations, cocoloop.cn news item, format list): per 32 consecutive values
+ * of each row, the OCP MX rule -- shared exponent X = floor(log2 amax) - 2
+ * clamped to [-127, 127], stored as the E8M0 byte X + 127 (0 for a zero
+ * block), elements E2M1(x / 2^X) rounded to nearest even and saturated at
+ * +-6 (negative values that round to zero keep the sign: code 8).
+ *   x bf16 [m][k]; codes [m][k/2] bytes, value 2j in the low nibble of byte
+ *   j; scales [m][k/32] E8M0 bytes.  k a multiple of 32; x and codes 16-byte
+ *   aligned.  m = 0 is a no-op. */
+hm_status hm_quant_mxfp4_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream);
+
 /* ---------------------------------------------------------------- dense GEMM */
 
 /* Workspace bytes hm_gemm needs for this shape and tuning (may be 0). */
@@ -180,8 +199,10 @@ hm_status hm_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t m, con
 
 /* y[m][n] = bf16( sum_k x_hat[m,k] * w_hat[n,k] ), fp32 accumulation.
  *   w_dev      transformed weights (num_experts must be 1).
- *   x          bf16 [m][k] (HM_A_BF16) or E4M3 bytes [m][k] (HM_A_FP8_ROWSCALE).
- *   x_scales   fp32 [m] row scales for HM_A_FP8_ROWSCALE, else ignored.
+ *   x          bf16 [m][k] (HM_A_BF16), E4M3 bytes [m][k] (HM_A_FP8_ROWSCALE) or
+ *              E2M1 codes [m][k/2] (HM_A_MXFP4).
+ *   x_scales   fp32 [m] row scales for HM_A_FP8_ROWSCALE, E8M0 bytes [m][k/32]
+ *              for HM_A_MXFP4 (4-byte aligned), else ignored.
  *   y          bf16 [m][n].
  *   ws         workspace of at least hm_gemm_workspace_size bytes (NULL if 0).
  *   tune       NULL for the default choice, else explicit choices (hm_tuning).
@@ -222,7 +243,9 @@ hm_status hm_moe_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t t,
  *   a            a_rows_are_pairs = 0: activations [t][k] and pair p uses row
  *                p / topk (gate/up projection);  = 1: [t*topk][k] and pair p
  *                uses row p (down projection).  bf16, or E4M3 bytes with
- *                a_scales (one fp32 per row of a) for HM_A_FP8_ROWSCALE.
+ *                a_scales (one fp32 per row of a) for HM_A_FP8_ROWSCALE, or
+ *                E2M1 codes [rows][k/2] with E8M0 a_scales [rows][k/32] for
+ *                HM_A_MXFP4.
  *   offsets, sorted_pairs  as produced by hm_moe_sort (device).
  *   y            bf16 [t*topk][n], rows in pair order; rows of dropped pairs
  *                are not written.

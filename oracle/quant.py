@@ -257,6 +257,23 @@ def quant_fp8_rows(x_bf16_bits):
     return codes, s
 
 
+def quant_mxfp4_rows(x_bf16_bits):
+    """MXFP4 activation rows (the W4A4 pair, cocoloop.cn news item, format
+    list): each row's bf16 values are quantized with the same OCP MX rule as
+    MXFP4 weights, one E8M0 scale per 32 values along K, E2M1 elements by
+    round-to-nearest-even with saturation.  The bf16 values are exact in
+    fp32, and the scaling by 2^-X is exact.
+    Returns (packed codes uint8 [M, K/2], e8m0 bytes uint8 [M, K/32])."""
+    x = codecs.bf16_value(np.asarray(x_bf16_bits, dtype=np.uint16)).astype(np.float32)
+    codes, e = quant_mxfp4(x)
+    return pack_nibbles(codes), e
+
+
+def mxfp4_rows_dequant(packed, scales):
+    """x_hat = E2M1(code) * 2^(b-127), float64 [M, K]."""
+    return dequant(FMT_MXFP4, packed, scales).astype(np.float64)
+
+
 def fp8_rows_dequant(codes, scales):
     """x_hat = E4M3(code) * s, float64 [M,K]."""
     return codecs.e4m3_value(codes) * np.asarray(scales, dtype=np.float64)[:, None]

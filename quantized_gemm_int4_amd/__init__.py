@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libhm.so")
 
 HM_ABI_VERSION = 2
 HM_W_INT4_SYM, HM_W_UINT4_ZP, HM_W_MXFP4, HM_W_MXINT4 = 0, 1, 2, 3
-HM_A_BF16, HM_A_FP8_ROWSCALE = 0, 1
+HM_A_BF16, HM_A_FP8_ROWSCALE, HM_A_MXFP4 = 0, 1, 2
 WFMT = {"int4_sym": HM_W_INT4_SYM, "uint4_zp": HM_W_UINT4_ZP, "mxfp4": HM_W_MXFP4, "mxint4": HM_W_MXINT4}
 STATUS = {0: "HM_OK", 1: "HM_ERR_NULL", 2: "HM_ERR_SHAPE", 3: "HM_ERR_ALIGN",
           4: "HM_ERR_UNSUPPORTED", 5: "HM_ERR_WORKSPACE", 6: "HM_ERR_HIP", 7: "HM_ERR_ABI", 8: "HM_ERR_TUNING"}
@@ -86,6 +86,7 @@ def _load():
         "hm_transform": [D, P, P, P, P, SZ, P],
         "hm_dequant": [D, P, SZ, I32, P, P],
         "hm_quant_fp8_rows": [P, I64, I64, P, P, P],
+        "hm_quant_mxfp4_rows": [P, I64, I64, P, P, P],
         "hm_gemm_workspace_size": [D, I32, I64, T, ctypes.POINTER(SZ)],
         "hm_gemm": [D, P, I32, P, P, I64, P, P, SZ, T, P],
         "hm_gemm_plan": [D, I32, I64, T, ctypes.c_char_p, SZ],
@@ -180,11 +181,27 @@ def hm_quant_fp8_rows(x, x8=None, row_scale=None, stream=None):
     return x8, row_scale
 
 
+def hm_quant_mxfp4_rows(x, codes=None, scales=None, stream=None):
+    """x bf16 [m,k] -> (E2M1 codes uint8 [m,k/2], E8M0 scales uint8 [m,k/32])."""
+    m, k = x.shape
+    _need(x, torch.bfloat16, m * k, "x")
+    if codes is None:
+        codes = torch.empty(m, k // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(m, k // 32, dtype=torch.uint8, device=x.device)
+    _ok("hm_quant_mxfp4_rows", lib.hm_quant_mxfp4_rows(_ptr(x), m, k, _ptr(codes), _ptr(scales),
+                                                       _stream(stream)))
+    return codes, scales
+
+
 # -------------------------------------------------------------------- dense GEMM
 
-def _afmt(x):
-    """Activation format from the activation tensor: bf16 rows or E4M3 bytes."""
-    return HM_A_FP8_ROWSCALE if x.dtype == torch.uint8 else HM_A_BF16
+def _afmt(x, x_scales=None):
+    """Activation format from the tensors: bf16 rows, E4M3 bytes with fp32
+    row scales, or E2M1 codes with E8M0 scale bytes (uint8 x_scales)."""
+    if x.dtype != torch.uint8:
+        return HM_A_BF16
+    return HM_A_MXFP4 if x_scales is not None and x_scales.dtype == torch.uint8 else HM_A_FP8_ROWSCALE
 
 
 def hm_gemm_workspace_size(desc, afmt, m, tuning=None):
@@ -204,7 +221,7 @@ def hm_gemm(desc, w_dev, x, x_scales=None, y=None, ws=None, afmt=None, tuning=No
     """y[m,n] = x_hat . w_hat^T in bf16.  x: bf16 [m,k] (W4A16, any weight
     format) or uint8 E4M3 [m,k] with fp32 x_scales [m] (W4A8-MXFP4).
     tuning: None (default choice), an hm_tuning, or a dict of its fields."""
-    afmt = _afmt(x) if afmt is None else afmt
+    afmt = _afmt(x, x_scales) if afmt is None else afmt
     m = x.shape[0]
     if y is None:
         y = torch.empty(m, desc.n, dtype=torch.bfloat16, device=x.device)
@@ -264,7 +281,7 @@ def hm_moe_gemm(desc, w_dev, a, offsets, sorted_pairs, t, topk, a_rows_are_pairs
     """Grouped GEMM; returns y bf16 [t*topk, n] in pair order.  a: bf16 rows,
     or E4M3 bytes with fp32 a_scales (MXFP4 weights only).  tuning: None, an
     hm_tuning, or a dict of its fields."""
-    afmt = _afmt(a) if afmt is None else afmt
+    afmt = _afmt(a, a_scales) if afmt is None else afmt
     P = t * topk
     if y is None:
         y = torch.empty(P, desc.n, dtype=torch.bfloat16, device=a.device)
@@ -286,7 +303,7 @@ def hm_moe_gemm_static(desc, w_dev, a, offsets, sorted_pairs, t, topk, a_rows_ar
     """hm_moe_gemm with the library's static work-list array instead of a
     workspace (no device allocation in the call; calls on one GPU must not
     overlap).  y may be passed in so that nothing is allocated here either."""
-    afmt = _afmt(a) if afmt is None else afmt
+    afmt = _afmt(a, a_scales) if afmt is None else afmt
     P = t * topk
     if y is None:
         y = torch.empty(P, desc.n, dtype=torch.bfloat16, device=a.device)

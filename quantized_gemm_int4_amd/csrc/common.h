@@ -268,4 +268,13 @@ __device__ __forceinline__ f32x4_t mfma_fp4_fp8(u32x4_t a, u32x4_t b0, u32x4_t b
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, 0, sa, 0, sb);
 }
 
+// 16x16x128 scaled MFMA with both operands E2M1 (W4A4): A as above; B lane L
+// supplies column L%16, K = 32*(L/16) + 0..31 (16 bytes, even K in the low
+// nibble), the same arrangement as A; the E8M0 scales as above.
+__device__ __forceinline__ f32x4_t mfma_fp4_fp4(u32x4_t a, u32x4_t b, f32x4_t c, int sa, int sb) {
+  i32x8_t av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  i32x8_t bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
+}
+
 }  // namespace hm

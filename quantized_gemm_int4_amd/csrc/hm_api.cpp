@@ -67,9 +67,9 @@ hm_status check_desc(const hm_wdesc* d) {
 }
 
 hm_status check_pair(const hm_wdesc* d, int32_t afmt) {
-  if (afmt != HM_A_BF16 && afmt != HM_A_FP8_ROWSCALE) return HM_ERR_UNSUPPORTED;
-  // FP8 rows pair with MXFP4 weights only; bf16 rows with every format
-  if (afmt == HM_A_FP8_ROWSCALE && d->wfmt != HM_W_MXFP4) return HM_ERR_UNSUPPORTED;
+  if (afmt != HM_A_BF16 && afmt != HM_A_FP8_ROWSCALE && afmt != HM_A_MXFP4) return HM_ERR_UNSUPPORTED;
+  // FP8 and MXFP4 rows pair with MXFP4 weights only; bf16 rows with every format
+  if (afmt != HM_A_BF16 && d->wfmt != HM_W_MXFP4) return HM_ERR_UNSUPPORTED;
   return HM_OK;
 }
 
@@ -77,7 +77,7 @@ hm_status check_pair(const hm_wdesc* d, int32_t afmt) {
 bool mx_a16(const hm_wdesc* d, int32_t afmt) { return is_mx(d->wfmt) && afmt == HM_A_BF16; }
 
 const char* pair_name(const hm_wdesc* d, int32_t afmt) {
-  if (d->wfmt == HM_W_MXFP4) return afmt == HM_A_BF16 ? "w4a16-mxfp4" : "w4a8-mxfp4";
+  if (d->wfmt == HM_W_MXFP4) return afmt == HM_A_BF16 ? "w4a16-mxfp4" : (afmt == HM_A_MXFP4 ? "w4a4-mxfp4" : "w4a8-mxfp4");
   if (d->wfmt == HM_W_MXINT4) return "w4a16-mxint4";
   return d->wfmt == HM_W_UINT4_ZP ? "w4a16-uint4zp" : "w4a16-int4sym";
 }
@@ -147,8 +147,11 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   const Geom G = geom_of(d);
   const bool f4 = mx_a16(d, afmt);
   const bool a8 = afmt == HM_A_FP8_ROWSCALE;
+  const bool a4 = afmt == HM_A_MXFP4;
   const bool tiles32 = scales_addr32(G);        // 128-row and 256-row kernels can address the scales
   if (tu.path == P_STREAM && m > kStreamWideRows) return HM_ERR_TUNING;
+  // W4A4: the streaming and 128 x 128 kernels only
+  if (a4 && (tu.path == P_MID || tu.path == P_BIG)) return HM_ERR_TUNING;
   if (tu.path == P_BIG && f4) return HM_ERR_TUNING;  // no 256 x 256 kernel for MX weights with bf16 rows
   if ((tu.path == P_MID || tu.path == P_BIG) && (!tiles32 || !mid_grid_fits(G, a8, m))) return HM_ERR_TUNING;
   // W4A16 up to 256 rows also streams (in 32-row chunks, each re-reading the
@@ -162,6 +165,8 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
     p.path = tu.path;
   } else if (m <= kStreamMaxRows || narrow) {
     p.path = P_STREAM;
+  } else if (a4) {
+    p.path = P_TILE;
   } else if (f4) {
     // MX weights with bf16 rows (no 256 x 256 kernel): 128 x 64 tiles, or 128 x
     // 128 tiles once the 128 x 64 ones take many rounds of the chip.
@@ -191,7 +196,7 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   p.sc.mb = (m <= 16) ? 1 : 2;
   const int64_t rows = (m < 16 * p.sc.mb) ? m : 16 * p.sc.mb;
   const int64_t m_chunks = (m + 16 * p.sc.mb - 1) / (16 * p.sc.mb);
-  const int64_t gb = a8 ? 128 : 256;   // activation bytes per row per group
+  const int64_t gb = a8 ? 128 : (a4 ? 68 : 256);   // activation bytes per row per group (A4: + scales)
   // Launch shape: (ks, nbw) from the narrowest block (most waves, least work
   // per wave) to the widest, take the first whose blocks all fit on the chip
   // at once.  A block keeps its activation rows in LDS, so the LDS footprint
@@ -286,7 +291,8 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
   p.P = t * topk;
   const int64_t act = (p.P < d->num_experts) ? p.P : d->num_experts;
   const bool mxi4 = d->wfmt == HM_W_MXINT4;
-  const bool a8 = afmt == HM_A_FP8_ROWSCALE;
+  const bool a8 = afmt != HM_A_BF16;          // FP8 or MXFP4 rows: the W4A8 streaming settings
+  const bool a4 = afmt == HM_A_MXFP4;
   const bool f4 = mx_a16(d, afmt);
   p.s_rows = tu.mrows ? tu.mrows : (mxi4 ? kMoeStreamRowsMxi4 : kMoeStreamRows);
   p.s_max = tu.mmax ? tu.mmax : (a8 ? kMoeStreamMaxMx : (mxi4 ? kMoeStreamMaxMxi4 : kMoeStreamMaxA16));
@@ -305,18 +311,18 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
   if (rows_are_pairs >= 0) {
     const Geom G = geom_of(d);
     const int64_t a_rows = rows_are_pairs ? p.P : t;
-    p.a64 = (uint64_t)a_rows * (uint64_t)d->k * (a8 ? 1u : 2u) >= kAddr32;
+    p.a64 = (uint64_t)a_rows * (uint64_t)d->k * (a4 ? 1u : (a8 ? 2u : 4u)) >= 2 * kAddr32;
     const bool tiles32 = scales_addr32(G);
     // 256-row units: not for MX weights with bf16 rows; they address
     // activation rows and scales with 32-bit offsets
-    const bool big_ok = !f4 && !p.a64 && tiles32;
+    const bool big_ok = !f4 && !a4 && !p.a64 && tiles32;
     if (tu.mbig > 0 && !big_ok) return HM_ERR_TUNING;
     p.big_min = (tu.mbig == -1 || !big_ok) ? 0 : big_min;
     // up-to-128-row units: the 128-row tile kernel (32-bit offsets), or the
     // 128 x 128 kernel for MX weights with bf16 rows when all pairs in
     // 128-row units would take many rounds of 128 x 64 tiles (T = 8192:
     // 7.92 against 8.30 ms)
-    const bool mid_ok = !p.a64 && tiles32;
+    const bool mid_ok = !a4 && !p.a64 && tiles32;
     if (tu.mtile == 1 && !mid_ok) return HM_ERR_TUNING;
     if (tu.mtile == 1) p.tile = P_MID;
     else if (tu.mtile == 2) p.tile = P_TILE;
@@ -341,8 +347,10 @@ hm_status launch_moe(const hm_wdesc* d, int32_t afmt, const void* w_dev, const v
   a.G = geom_of(d);
   a.wfmt = d->wfmt;
   a.a8 = afmt == HM_A_FP8_ROWSCALE;
+  a.a4 = afmt == HM_A_MXFP4;
   a.x = a_in;
   a.xs = a.a8 ? (const float*)a_scales : nullptr;
+  a.xsb = a.a4 ? (const uint8_t*)a_scales : nullptr;
   a.M = 0;
   a.y = y;
   a.hdr = hdr;
@@ -446,6 +454,16 @@ HM_API hm_status hm_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint
   return HM_OK;
 }
 
+HM_API hm_status hm_quant_mxfp4_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes, uint8_t* scales,
+                                     hipStream_t stream) {
+  if (m < 0 || k < 32 || (k % 32) != 0) return HM_ERR_SHAPE;
+  if (m == 0) return HM_OK;
+  if (!x || !codes || !scales) return HM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return HM_ERR_ALIGN;
+  if (launch_quant_mxfp4_rows(x, m, k, codes, scales, stream) != hipSuccess) return HM_ERR_HIP;
+  return HM_OK;
+}
+
 HM_API hm_status hm_silu_mul(const uint16_t* gu, int64_t rows, int64_t d, uint16_t* h, hipStream_t stream) {
   if (rows < 0 || d <= 0) return HM_ERR_SHAPE;
   if (rows == 0) return HM_OK;
@@ -508,10 +526,11 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, const 
   DensePlan p;
   if ((s = plan_dense(d, afmt, m > 0 ? m : 1, tu, &p))) return s;
   const char* w = pair_name(d, afmt);
-  const bool a8 = afmt == HM_A_FP8_ROWSCALE;
+  const bool a8 = afmt != HM_A_BF16;        // scaled f8f6f4 MFMA (FP8 or MXFP4 rows)
   if (p.path == P_STREAM)
     snprintf(buf, buf_len, "%s stream mb=%d nbw=%d ks=%d waves=%d splits=%d ksg=%d mfma=%s", w, p.sc.mb,
-             p.sc.nbw, p.sc.ks, p.sc.nw, p.sc.splits, p.ksg, a8 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
+             p.sc.nbw, p.sc.ks, p.sc.nw, p.sc.splits, p.ksg,
+             afmt == HM_A_MXFP4 ? "scale_16x16x128_f8f6f4_fp4xfp4" : (a8 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16"));
   else if (p.path == P_BIG) {
     const Geom G = make_geom(d->wfmt, 1, d->n, d->k);
     const int64_t tiles = big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows);
@@ -526,7 +545,7 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, const 
     snprintf(buf, buf_len, "%s tile 128x64 waves=4 (K split) mfma=32x32x16_bf16", w);
   else
     snprintf(buf, buf_len, "%s tile %dx%d waves=2x2 mfma=%s", w, kTileM, kTileN,
-             a8 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16");
+             afmt == HM_A_MXFP4 ? "scale_16x16x128_f8f6f4_fp4xfp4" : (a8 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16"));
   return HM_OK;
 }
 
@@ -542,7 +561,7 @@ HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, con
   if ((s = read_tuning(tune, &tu))) return s;
   if (m == 0) return HM_OK;
   if (!w_dev || !x || !y) return HM_ERR_NULL;
-  if (afmt == HM_A_FP8_ROWSCALE && !x_scales) return HM_ERR_NULL;
+  if (afmt != HM_A_BF16 && !x_scales) return HM_ERR_NULL;
   if (!aligned(w_dev, 256) || !aligned(x, 16) || !aligned(y, 16)) return HM_ERR_ALIGN;
   if (x_scales && !aligned(x_scales, 4)) return HM_ERR_ALIGN;
   DensePlan p;
@@ -557,8 +576,10 @@ HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, con
   a.G = geom_of(d);
   a.wfmt = d->wfmt;
   a.a8 = afmt == HM_A_FP8_ROWSCALE;
+  a.a4 = afmt == HM_A_MXFP4;
   a.x = x;
   a.xs = (afmt == HM_A_FP8_ROWSCALE) ? (const float*)x_scales : nullptr;
+  a.xsb = a.a4 ? (const uint8_t*)x_scales : nullptr;
   a.M = m;
   a.y = y;
   hipError_t e;
@@ -658,7 +679,7 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
   if (a_rows_are_pairs != 0 && a_rows_are_pairs != 1) return HM_ERR_SHAPE;
   if (t == 0) return HM_OK;
   if (!w_dev || !a_in || !offsets || !sorted_pairs || !y || !ws) return HM_ERR_NULL;
-  if (afmt == HM_A_FP8_ROWSCALE && !a_scales) return HM_ERR_NULL;
+  if (afmt != HM_A_BF16 && !a_scales) return HM_ERR_NULL;
   if (!aligned(w_dev, 256) || !aligned(a_in, 16) || !aligned(y, 16) || !aligned(ws, 256) ||
       !aligned(offsets, 4) || !aligned(sorted_pairs, 4))
     return HM_ERR_ALIGN;
@@ -709,7 +730,7 @@ HM_API hm_status hm_moe_gemm_static(const hm_wdesc* d, const void* w_dev, int32_
   if (a_rows_are_pairs != 0 && a_rows_are_pairs != 1) return HM_ERR_SHAPE;
   if (t == 0) return HM_OK;
   if (!w_dev || !a_in || !offsets || !sorted_pairs || !y) return HM_ERR_NULL;
-  if (afmt == HM_A_FP8_ROWSCALE && !a_scales) return HM_ERR_NULL;
+  if (afmt != HM_A_BF16 && !a_scales) return HM_ERR_NULL;
   if (!aligned(w_dev, 256) || !aligned(a_in, 16) || !aligned(y, 16) || !aligned(offsets, 4) ||
       !aligned(sorted_pairs, 4))
     return HM_ERR_ALIGN;

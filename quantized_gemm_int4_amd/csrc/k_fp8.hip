@@ -141,3 +141,74 @@ hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_
 }
 
 }  // namespace hm
+
+namespace hm {
+
+// MXFP4 activation rows (the W4A4 pair): per 32 consecutive values of a row,
+// the OCP MX rule -- shared exponent X = floor(log2 amax) - 2 clamped to
+// [-127, 127] (E8M0 byte X + 127; a zero block takes byte 0), elements
+// E2M1(x / 2^X) rounded to nearest even and saturated at 6.  The bf16 values
+// are exact in fp32 and the scaling by 2^-X is exact, so the codes are those
+// of the exact quotient.
+
+// |v| -> E2M1 magnitude code 0..7 (0, 0.5, 1, 1.5, 2, 3, 4, 6): count the
+// rounding boundaries below |v|; ties (0.25, 0.75, ..., 5) go to the even code
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+                     (a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);          // sign bit 3 (negative zero keeps it)
+}
+
+// One thread per 32-value block: four 16-byte loads, one 16-byte code store
+// (value 2i in the low nibble of byte i) and one scale byte.
+__global__ void __launch_bounds__(256)
+k_quant_mxfp4_rows(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint8_t* __restrict__ codes,
+                   uint8_t* __restrict__ scales) {
+  const int64_t per_row = k / 32;
+  const int64_t n = m * per_row;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = i / per_row, b = i - row * per_row;
+    const uint16_t* xp = x + row * k + b * 32;
+    u32x4_t v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = ld16(xp + 8 * c);
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        amax_bits = max(amax_bits, (v[c][j] << 16) & 0x7FFFFFFFu);
+        amax_bits = max(amax_bits, v[c][j] & 0x7FFF0000u);
+      }
+    // biased fp32 exponent of amax (0 for zero and subnormal); byte = max(e - 2, 0)
+    const int e = (int)(amax_bits >> 23);
+    const int byte = e > 2 ? e - 2 : 0;
+    const float inv = __uint_as_float((uint32_t)(254 - byte) << 23);   // 2^-(byte - 127)
+    uint32_t out[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = e2m1_code(bf16_to_f32(v[c][j] & 0xFFFFu) * inv);
+        const uint32_t hi = e2m1_code(bf16_to_f32(v[c][j] >> 16) * inv);
+        w |= (lo | (hi << 4)) << (8 * j);
+      }
+      out[c] = w;
+    }
+    st16(codes + row * (k / 2) + b * 16, (u32x4_t){out[0], out[1], out[2], out[3]});
+    scales[row * per_row + b] = (uint8_t)byte;
+  }
+}
+
+hipError_t launch_quant_mxfp4_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes, uint8_t* scales,
+                                   hipStream_t st) {
+  const int64_t n = m * (k / 32);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_quant_mxfp4_rows, dim3((unsigned)blocks), dim3(256), 0, st, x, m, k, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace hm

@@ -54,9 +54,10 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
   constexpr bool MX = MODE == KM_MX_A8;                 // FP8 rows, scaled fp4 x fp8 MFMA
   constexpr bool F4 = MODE == KM_MX_A16 || MODE == KM_MXI4_A16;   // MX codes scaled to bf16
   constexpr bool I4 = MODE == KM_MXI4_A16;              // MXINT4: two's complement codes / 4
-  constexpr bool MXW = MX || F4;                        // E8M0 scale words
+  constexpr bool A4 = MODE == KM_MX_A4;                 // MXFP4 rows, scaled fp4 x fp4 MFMA
+  constexpr bool MXW = MX || F4 || A4;                  // E8M0 scale words
   constexpr int ROWS = MB * 16;
-  constexpr int GB = MX ? 128 : 256;                    // activation bytes per row per K group
+  constexpr int GB = MX ? 128 : (A4 ? 64 : 256);        // activation bytes per row per K group
   constexpr int CS = NW / KS;                           // column sets per block
   constexpr int RED = StreamShape<NW, KS, NBW, MB>::kRedBytes;
   // vector-memory loads per ring slot: per column block the 1 KiB tile and
@@ -74,8 +75,12 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
   const int64_t K = G.K;
   const int n_l = lane & 15, q_l = lane >> 4;
   const uint8_t* xbase = reinterpret_cast<const uint8_t*>(a.x);
-  const int64_t xrow_bytes = MX ? K : 2 * K;
+  const int64_t xrow_bytes = MX ? K : (A4 ? K / 2 : 2 * K);
   const uint8_t* sbase = a.w + G.off_scales;
+  // MXFP4 rows: the E8M0 words of each row's groups (4 blocks of 32 per group)
+  // are staged after the rows' codes, `sb` bytes per row
+  const int sb = A4 ? ((pg + 63) / 64) * 256 : 0;
+  const uint8_t* xsbase = A4 ? a.xsb : nullptr;
   const uint8_t* zbase = a.w + G.off_zeros;
   const uint32_t zshift = 4u * (uint32_t)(n_l & 7);
 
@@ -142,6 +147,9 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
     // wait for the copies already in flight (they write LDS too).
     const int64_t xrow_off = arow_s[lane & (ROWS - 1)] * xrow_bytes;
     const uint32_t xro_lo = (uint32_t)xrow_off, xro_hi = (uint32_t)((uint64_t)xrow_off >> 32);
+    const int64_t srow_off = A4 ? arow_s[lane & (ROWS - 1)] * G.KG * 4 : 0;    // scale bytes of the row
+    const uint32_t sro_lo = (uint32_t)srow_off, sro_hi = (uint32_t)((uint64_t)srow_off >> 32);
+    uint8_t* const xsc_lds = xs_lds + rcount * xb;      // MXFP4 rows: staged scale words
 
     // Copy activation rows [0, rcount) x groups [gp, gp + plen) into LDS: one
     // wave instruction moves 1 KiB of one row (buffer over the row's piece,
@@ -161,6 +169,20 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
                             (uint32_t)__builtin_amdgcn_readlane((int)xro_lo, r);
         b2lds16(make_rsrc(xbase + ro + off0, (uint64_t)per_row * 16), lane16, (uint32_t)blk * 1024,
                 xs_lds + r * xb + blk * 1024);
+      }
+      if (A4) {
+        // the rows' scale words of groups [gp, gp + plen): 4-byte copies,
+        // 64 words per instruction, lanes past the piece read zeros
+        const int cps = (plen + 63) / 64;
+        const int tot = rcount * cps;
+#pragma nounroll
+        for (int i = wave; i < tot; i += NW) {
+          const int r = i / cps, blk = i - (i / cps) * cps;
+          const uint64_t ro = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sro_hi, r) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)sro_lo, r);
+          b2lds4(make_rsrc(xsbase + ro + (g_begin + gp) * 4, (uint64_t)plen * 4), (uint32_t)lane * 4,
+                 (uint32_t)blk * 256, xsc_lds + r * sb + blk * 256);
+        }
       }
     };
 
@@ -224,7 +246,23 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
       auto process = [&](int d, int lg) {
         const int64_t g = gw + lg;
         const uint8_t* xg = xs_lds + (lo + lg) * GB;
-        if (MX) {
+        if (A4) {
+          // lane L: row n_l of the row block, K block q_l of the group (16
+          // bytes of codes) and that block's scale byte
+          u32x4_t bq[MB];
+          int bs[MB];
+#pragma unroll
+          for (int rb = 0; rb < MB; ++rb) {
+            bq[rb] = ld16(xg + lrow[rb] * xb + 16 * q_l);
+            bs[rb] = xsc_lds[lrow[rb] * sb + (lo + lg) * 4 + q_l];
+          }
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            const int sc = (int)((wsr[d][j] >> (8 * (g & 3))) & 0xFF);
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) acc[j][rb] = mfma_fp4_fp4(wq[d][j], bq[rb], acc[j][rb], sc, bs[rb]);
+          }
+        } else if (MX) {
           u32x4_t a0[MB], a1[MB];
 #pragma unroll
           for (int rb = 0; rb < MB; ++rb) {
@@ -418,21 +456,24 @@ int64_t stream_n_tiles(const Geom& G, const StreamCfg& c) {
 // LDS plan of one launch: K groups per activation piece and the row stride.
 static void stream_lds_plan(const GemmArgs& a, const StreamCfg& c, bool grouped, int red_bytes,
                             int* pg_out, int* xb_out, size_t* bytes_out) {
-  const int64_t gb = (kmode_of(a) == KM_MX_A8) ? 128 : 256;
+  const bool a4 = kmode_of(a) == KM_MX_A4;
+  const int64_t gb = (kmode_of(a) == KM_MX_A8) ? 128 : (a4 ? 64 : 256);
   const int64_t rows = grouped ? 16 * c.mb : (a.M < 16 * c.mb ? a.M : 16 * c.mb);
   const int64_t ksl = grouped ? a.G.KG : a.ksg;         // groups one block walks
   const int64_t gq = 1024 / gb;                         // groups per 1 KiB of a row
   // largest piece (a multiple of gq groups) whose rows fit the budget
   const int64_t budget = (c.lds_kb > 0 && c.lds_kb * 1024 < kStreamLdsBudget) ? c.lds_kb * 1024 : kStreamLdsBudget;
   const int64_t avail = budget - red_bytes;
-  int64_t pg = ((avail / rows - 16) / 1024) * gq;
+  // MXFP4 rows add 4 scale bytes per group (staged in 256-byte pieces)
+  int64_t pg = a4 ? ((avail / rows - 16 - 256) / (1024 + 4 * gq)) * gq : ((avail / rows - 16) / 1024) * gq;
   if (pg < gq) pg = gq;
   const int64_t need = (ksl + gq - 1) / gq * gq;
   if (pg > need) pg = need;
   const int64_t xb = (pg * gb + 1023) / 1024 * 1024 + 16;
+  const int64_t sb = a4 ? (pg + 63) / 64 * 256 : 0;
   *pg_out = (int)pg;
   *xb_out = (int)xb;
-  *bytes_out = (size_t)(red_bytes + rows * xb);
+  *bytes_out = (size_t)(red_bytes + rows * (xb + sb));
 }
 
 template <int MODE, bool ZP, int MB, int NBW, int KS, bool GROUPED, int NW>
@@ -498,6 +539,9 @@ hipError_t launch_gemm_stream(const GemmArgs& a, const StreamCfg& c, bool groupe
   if (mode == KM_MX_A8)
     return grouped ? go_stream_mb<KM_MX_A8, false, true>(a, c, grid_items, st)
                    : go_stream_mb<KM_MX_A8, false, false>(a, c, grid_items, st);
+  if (mode == KM_MX_A4)
+    return grouped ? go_stream_mb<KM_MX_A4, false, true>(a, c, grid_items, st)
+                   : go_stream_mb<KM_MX_A4, false, false>(a, c, grid_items, st);
   if (mode == KM_MX_A16)
     return grouped ? go_stream_mb<KM_MX_A16, false, true>(a, c, grid_items, st)
                    : go_stream_mb<KM_MX_A16, false, false>(a, c, grid_items, st);

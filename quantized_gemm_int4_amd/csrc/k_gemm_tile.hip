@@ -25,14 +25,17 @@ namespace hm {
 template <int MODE, bool GROUPED>
 __global__ void __launch_bounds__(256)
 k_gemm_tile(GemmArgs a, int n_tiles) {
-  constexpr bool MX = MODE == KM_MX_A8;                // FP8 rows, scaled fp4 x fp8 MFMA
+  constexpr bool A4 = MODE == KM_MX_A4;                // MXFP4 rows, scaled fp4 x fp4 MFMA
+  constexpr bool MX = MODE == KM_MX_A8 || A4;          // E2M1 weight fragments fed as stored
   constexpr bool F4 = MODE == KM_MX_A16 || MODE == KM_MXI4_A16;  // MX codes scaled to bf16
   constexpr bool I4 = MODE == KM_MXI4_A16;             // MXINT4: two's complement codes / 4
-  constexpr int XB = MX ? (128 + 16) : (256 + 16);     // LDS activation row stride (bytes)
-  constexpr int XPR = MX ? 8 : 16;                     // 16-byte pieces per activation row
+  constexpr int GBX = A4 ? 64 : (MX ? 128 : 256);      // activation bytes per row per K step
+  constexpr int XB = GBX + 16;                         // LDS activation row stride (bytes)
+  constexpr int XPR = GBX / 16;                        // 16-byte pieces per activation row
   constexpr int XLD = kTileM * XPR / 256;              // pieces per thread
   constexpr int WLDS = MX ? 16 : 8 * 4 * 1024;         // dequantized weight fragments
   __shared__ __attribute__((aligned(16))) uint8_t xs_lds[kTileM * XB];
+  __shared__ uint32_t xsc_lds[A4 ? kTileM : 1];        // MXFP4 rows: E8M0 word of each row's step
   __shared__ __attribute__((aligned(16))) uint8_t ws_lds[WLDS];
   __shared__ int64_t arow_s[kTileM];
   __shared__ int64_t orow_s[kTileM];
@@ -44,7 +47,7 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
   const Geom G = a.G;
   const int64_t K = G.K;
   const uint8_t* xbase = reinterpret_cast<const uint8_t*>(a.x);
-  const int64_t xrow_bytes = MX ? K : 2 * K;
+  const int64_t xrow_bytes = A4 ? K / 2 : (MX ? K : 2 * K);
 
   const int64_t n_items = GROUPED ? (int64_t)a.hdr[1] * n_tiles : 1;
   for (int64_t item = GROUPED ? blockIdx.x : 0; item < n_items;
@@ -93,16 +96,19 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
     u32x4_t xr[XLD];
     u32x4_t wq[2];               // W4A16: two code slots per thread
     uint32_t wsr[2], wzr[2];
-    u32x4_t mq[4];               // W4A8: this wave's four fragments
+    u32x4_t mq[4];               // W4A8 / W4A4: this wave's four fragments
     uint32_t msr[4];
+    uint32_t xsr = 0;            // W4A4: this thread's row scale word (threads < 128)
 
     auto load_step = [&](int64_t g) {
 #pragma unroll
       for (int i = 0; i < XLD; ++i) {
         const int q = tid + 256 * i;
         const int row = q / XPR, pc = q % XPR;
-        xr[i] = ld16(xbase + arow_s[row] * xrow_bytes + g * (MX ? 128 : 256) + pc * 16);
+        xr[i] = ld16(xbase + arow_s[row] * xrow_bytes + g * GBX + pc * 16);
       }
+      if (A4 && tid < kTileM)
+        xsr = *reinterpret_cast<const uint32_t*>(a.xsb + arow_s[tid] * (G.KG * 4) + g * 4);
       if (MX) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -138,6 +144,7 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
         const int row = q / XPR, pc = q % XPR;
         st16(&xs_lds[row * XB + pc * 16], xr[i]);
       }
+      if (A4 && tid < kTileM) xsc_lds[tid] = xsr;
       if (!MX) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -178,7 +185,16 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
       }
       const bool more = (g + 1 < G.KG);
       if (more) load_step(g + 1);
-      if (MX) {
+      if (A4) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int r = wm * 64 + mb * 16 + n_l;
+          const u32x4_t b = ld16(xs_lds + r * XB + 16 * q_l);
+          const int bs = (int)((xsc_lds[r] >> (8 * q_l)) & 0xFFu);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j][mb] = mfma_fp4_fp4(cq[j], b, acc[j][mb], csc[j], bs);
+        }
+      } else if (MX) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           const uint8_t* p = xs_lds + (wm * 64 + mb * 16 + n_l) * XB + 16 * q_l;
@@ -219,7 +235,7 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
         const int rl = wm * 64 + mb * 16 + n_l;
         if (rl >= rcount || orow_s[rl] < 0) continue;
         f32x4_t v = acc[j][mb];
-        if (MX) v = v * a.xs[arow_s[rl]];
+        if (MX && !A4) v = v * a.xs[arow_s[rl]];
         uint16_t* dst = a.y + orow_s[rl] * G.N + n;
         if ((G.N & 3) == 0 && n + 3 < G.N) {
           *reinterpret_cast<u32x2_t*>(dst) = (u32x2_t){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
@@ -248,6 +264,8 @@ hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hip
   const int mode = kmode_of(a);
   if (mode == KM_MX_A8)
     return grouped ? go_tile<KM_MX_A8, true>(a, grid_items, st) : go_tile<KM_MX_A8, false>(a, grid_items, st);
+  if (mode == KM_MX_A4)
+    return grouped ? go_tile<KM_MX_A4, true>(a, grid_items, st) : go_tile<KM_MX_A4, false>(a, grid_items, st);
   if (mode == KM_MX_A16)
     return grouped ? go_tile<KM_MX_A16, true>(a, grid_items, st) : go_tile<KM_MX_A16, false>(a, grid_items, st);
   if (mode == KM_MXI4_A16)

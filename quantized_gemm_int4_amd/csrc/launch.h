@@ -12,7 +12,7 @@ constexpr int kBigRows = 256;   // rows of a 256 x 256 tile (and of a grouped 25
 // bf16 rows, MXFP4 with FP8 rows (scaled fp4 x fp8 MFMA), MXFP4 / MXINT4 with bf16 rows
 // (E2M1 converted to bf16 with its E8M0 scale, bf16 MFMA).
 // (MXINT4 weights with bf16 rows take the MXFP4 path with integer codes.)
-enum KMode : int { KM_INT4_A16 = 0, KM_MX_A8 = 1, KM_MX_A16 = 2, KM_MXI4_A16 = 3 };
+enum KMode : int { KM_INT4_A16 = 0, KM_MX_A8 = 1, KM_MX_A16 = 2, KM_MXI4_A16 = 3, KM_MX_A4 = 4 };
 
 // Arguments shared by the GEMM kernels.
 struct GemmArgs {
@@ -20,6 +20,8 @@ struct GemmArgs {
   Geom G;
   int wfmt;                // W_INT4_SYM / W_UINT4_ZP / W_MXFP4 / W_MXINT4
   int a8;                  // 1: x is E4M3 bytes with fp32 row scales (MXFP4 only); 0: bf16
+  int a4;                  // 1: x is E2M1 codes [rows][K/2] with E8M0 bytes xsb [rows][K/32] (MXFP4 only)
+  const uint8_t* xsb;      // E8M0 activation scales (a4) or null
   const void* x;           // activations: bf16 [rows][K] or E4M3 bytes [rows][K]
   const float* xs;         // fp32 row scales (A8) or null
   int64_t M;               // dense: rows of x and y
@@ -41,6 +43,8 @@ hipError_t launch_dequant(int wfmt, const Geom& G, const uint8_t* w, int64_t e, 
                           hipStream_t st);
 hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* x8, float* s,
                                  hipStream_t st);
+hipError_t launch_quant_mxfp4_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes, uint8_t* scales,
+                                   hipStream_t st);
 hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int E, int32_t* counts, int32_t* offsets,
                            int32_t* sorted_pairs, hipStream_t st);
 hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_rows, int s_max, int bm,
@@ -98,6 +102,7 @@ int64_t big_full_tiles(const Geom& G, int64_t M, bool mx);
 
 inline int kmode_of(const GemmArgs& a) {
   if (a.wfmt == W_MXINT4) return KM_MXI4_A16;
+  if (a.wfmt == W_MXFP4 && a.a4) return KM_MX_A4;
   return a.wfmt != W_MXFP4 ? KM_INT4_A16 : (a.a8 ? KM_MX_A8 : KM_MX_A16);
 }
 

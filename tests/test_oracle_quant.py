@@ -335,3 +335,31 @@ def test_uint4_zp_scale_rule_against_torch():
             assert sbits[n, g] == want, (n, g)
     assert sbits[4, 0] == 0x3DCD and z[4, 0] == 0 and u[4, 5] == 7
     assert u[4, 127] == 15 and u[4, 0] == 0
+
+
+# ------------------------------------------------------------------ MXFP4 activation rows (W4A4)
+
+def test_mxfp4_rows_worked_block():
+    """A bf16 block whose largest magnitude is 6 * 2^j takes the scale byte
+    j + 127 (X = floor(log2 amax) - 2 = j) and each value v / 2^X rounds to
+    the written-out E2M1 code: 6 -> 7, -6 -> 15, 0.25 -> 0 (tie to even),
+    0.75 -> 2 (tie to even), 1.25 -> 2, 1.75 -> 4, 2.5 -> 4, 3.5 -> 6, 5 -> 6,
+    -0.125 -> 8 (-0), 4.875 -> 6, 5.125 -> 7 (6 above the tie at 5), 0 -> 0."""
+    from synthetic import to_bf16_bits
+    vals = [6.0, -6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.125, 4.875, 5.125, 0.0, 0.5, 1.0, 1.5]
+    want = [7, 15, 0, 2, 2, 4, 4, 6, 6, 8, 6, 7, 0, 1, 2, 3]
+    for j in (-10, 0, 3):
+        blk = np.array(vals + vals, dtype=np.float32) * np.float32(2.0 ** j)
+        xb = to_bf16_bits(blk.reshape(1, 32))
+        assert np.array_equal(codecs.bf16_value(xb)[0], blk)          # exact in bf16
+        packed, e = quant.quant_mxfp4_rows(xb)
+        assert e[0, 0] == j + 127
+        codes = quant.unpack_nibbles(packed)[0]
+        assert list(codes[:16]) == want and list(codes[16:]) == want
+        xh = quant.mxfp4_rows_dequant(packed, e)[0]
+        mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+        assert xh[0] == 6.0 * 2.0 ** j and xh[8] == 4.0 * 2.0 ** j and np.signbit(xh[9]) and xh[9] == 0.0
+        assert all(abs(xh[i]) == mags[want[i] & 7] * 2.0 ** j for i in range(16))
+    # a zero row: scale byte 0, zero codes
+    packed, e = quant.quant_mxfp4_rows(np.zeros((1, 64), dtype=np.uint16))
+    assert (e == 0).all() and (packed == 0).all()
