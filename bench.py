@@ -34,6 +34,7 @@ METRIC = "W4A16 GEMM TFLOP/s & weight-HBM GB/s vs M; MoE grouped-GEMM TFLOP/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+FP4_PEAK_TFLOPS = 10100.0      # dense fp4 (and fp6) MFMA
 LLC_BYTES = 256 * 2 ** 20      # last-level (Infinity) cache
 
 
@@ -43,7 +44,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="dense_w4a16",
-                   choices=["dense_w4a16", "dense_w4a8", "moe_w4a16", "moe_w4a8", "moe_w4a16_mxfp4",
+                   choices=["dense_w4a16", "dense_w4a8", "dense_w4a4", "moe_w4a16", "moe_w4a8", "moe_w4a16_mxfp4",
                             "moe_w4a16_mxint4", "shards", "readfloor"])
     p.add_argument("--reps", type=int, default=30, help="launches per M for per-kernel timing")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle (cpu_baseline) legs")
@@ -143,32 +144,45 @@ class Timer:
 
 # ============================================================================ dense
 
+def wfmt_of(fmt):
+    """Weight format of a bench format ("mxfp4" = W4A8, "mxfp4_a4" = W4A4)."""
+    return "mxfp4" if fmt.startswith("mxfp4") else fmt
+
+
 def dense_setup(torch, hm, synthetic, fmt, n, k, ms):
-    codes, scales, zeros = synthetic.random_std_format(fmt, 1, n, k, seed=1)
+    wf = wfmt_of(fmt)
+    codes, scales, zeros = synthetic.random_std_format(wf, 1, n, k, seed=1)
     dev = torch.device("cuda:0")
-    d = hm.wdesc(fmt, n, k)
+    d = hm.wdesc(wf, n, k)
     c = torch.from_numpy(codes).to(dev)
-    s = torch.from_numpy(scales.view(np.int16) if fmt != "mxfp4" else scales).to(dev)
+    s = torch.from_numpy(scales.view(np.int16) if wf != "mxfp4" else scales).to(dev)
     z = torch.from_numpy(zeros).to(dev) if zeros is not None else None
     w0 = hm.hm_transform(d, c, s, z)
     copies = max(2, int(np.ceil(2 * LLC_BYTES / w0.numel())) + 1)
     ws = [w0] + [w0.clone() for _ in range(copies - 1)]
     xs = {}
     for m in ms:
-        xb = synthetic.activations(2 if fmt != "mxfp4" else 3, m, k, index=m,
-                                   outliers=0.01 if fmt == "mxfp4" else 0.0)
+        xb = synthetic.activations(2 if wf != "mxfp4" else 3, m, k, index=m,
+                                   outliers=0.01 if wf == "mxfp4" else 0.0)
         x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
         if fmt == "mxfp4":
             x8, sc = hm.hm_quant_fp8_rows(x)
             xs[m] = (x, x8, sc)
+        elif fmt == "mxfp4_a4":
+            x4, sc = hm.hm_quant_mxfp4_rows(x)
+            xs[m] = (x, x4, sc)
         else:
             xs[m] = (x, None, None)
     ys = {m: torch.empty(m, n, dtype=torch.bfloat16, device=dev) for m in ms}
-    wsz = max(hm.hm_gemm_workspace_size(d, 1 if fmt == "mxfp4" else 0, m) for m in ms)
+    wsz = max(hm.hm_gemm_workspace_size(d, afmt_of(fmt), m) for m in ms)
     work = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     return dict(desc=d, codes=codes, scales=scales, zeros=zeros, w=ws, x=xs, y=ys, work=work,
                 copies=copies, wbytes=w0.numel())
+
+
+def afmt_of(fmt):
+    return {"mxfp4": 1, "mxfp4_a4": 2}.get(fmt, 0)
 
 
 def dense_call(hm, S, m, i, fmt):
@@ -177,6 +191,10 @@ def dense_call(hm, S, m, i, fmt):
     if fmt == "mxfp4":
         # per-token FP8 quantization is part of the W4A8 step
         hm.hm_quant_fp8_rows(x, x8, sc)
+        hm.hm_gemm(S["desc"], w, x8, sc, y=S["y"][m], ws=S["work"])
+    elif fmt == "mxfp4_a4":
+        # and the MXFP4 quantization of the rows part of the W4A4 step
+        hm.hm_quant_mxfp4_rows(x, x8, sc)
         hm.hm_gemm(S["desc"], w, x8, sc, y=S["y"][m], ws=S["work"])
     else:
         hm.hm_gemm(S["desc"], w, x, y=S["y"][m], ws=S["work"])
@@ -192,6 +210,11 @@ def run_dense(args, fmt):
         peak = FP8_PEAK_TFLOPS
         afmt = 1
         wl = "dense W4A8-MXFP4 (E2M1 + E8M0/32, per-token FP8 E4M3) N=7168 K=2048 M={16,256,4096}"
+    elif fmt == "mxfp4_a4":
+        n, k, ms = 7168, 2048, [16, 256, 4096]
+        peak = FP4_PEAK_TFLOPS
+        afmt = 2
+        wl = "dense W4A4-MXFP4 (E2M1 + E8M0/32 weights and rows) N=7168 K=2048 M={16,256,4096}"
     else:
         n, k, ms = 14336, 4096, [1, 16, 128, 1024, 4096]
         peak = BF16_PEAK_TFLOPS
@@ -247,7 +270,7 @@ def run_dense(args, fmt):
         us = tm.stop_ms() * 1e3 / args.reps
         del g
         fl = 2.0 * m * n * k
-        xbytes = m * k * (1 if fmt == "mxfp4" else 2) + (4 * m if fmt == "mxfp4" else 0)
+        xbytes = {"mxfp4": m * k + 4 * m, "mxfp4_a4": m * k // 2 + m * k // 32}.get(fmt, m * k * 2)
         ybytes = m * n * 2
         t_roof = max((alg_w + xbytes + ybytes) / (HBM_PEAK_GBS * 1e9), fl / (peak * 1e12))
         sweep.append(dict(M=m, us=round(us, 3), tflops=round(fl / us / 1e6, 3),
@@ -282,7 +305,7 @@ def run_dense(args, fmt):
     cpu = None if args.no_cpu else cpu_dense(S, fmt, n, k, ms, hm, torch)
     out = dict(metric=METRIC, value=round(value, 3), unit="TFLOP/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms_step, 4), higher_is_better=True,
-               scaling="weak", vs_baseline=None, dtype="fp8" if fmt == "mxfp4" else "bf16",
+               scaling="weak", vs_baseline=None, dtype={"mxfp4": "fp8", "mxfp4_a4": "fp4"}.get(fmt, "bf16"),
                data="synthetic", timing="HIP graph replay of the K steps (eager launch: "
                f"{eager_ms_step:.4f} ms/step)",
                config=dict(workload=wl, weight_copies=S["copies"],
@@ -333,18 +356,21 @@ def cpu_dense(S, fmt, n, k, ms, hm, torch):
     import synthetic
 
     t0 = time.perf_counter()
-    what = quant.dequant(fmt, S["codes"][0], S["scales"][0],
+    what = quant.dequant(wfmt_of(fmt), S["codes"][0], S["scales"][0],
                          S["zeros"][0] if S["zeros"] is not None else None).astype(np.float64)
     flops = 0.0
     worst = 0.0
     ok = True
     for m in ms:
         rows = min(m, 512)
-        xb = synthetic.activations(2 if fmt != "mxfp4" else 3, m, k, index=m,
-                                   outliers=0.01 if fmt == "mxfp4" else 0.0)[:rows]
+        xb = synthetic.activations(2 if fmt == "uint4_zp" else 3, m, k, index=m,
+                                   outliers=0.01 if fmt != "uint4_zp" else 0.0)[:rows]
         if fmt == "mxfp4":
             c, s = quant.quant_fp8_rows(xb)
             xh = quant.fp8_rows_dequant(c, s)
+        elif fmt == "mxfp4_a4":
+            c, s = quant.quant_mxfp4_rows(xb)
+            xh = quant.mxfp4_rows_dequant(c, s)
         else:
             xh = codecs.bf16_value(xb).astype(np.float64)
         y, b = gemm.gemm_ref(xh, what)
@@ -813,7 +839,7 @@ def main():
     elif args.workload == "readfloor":
         out = run_readfloor(args)
     elif args.workload.startswith("dense"):
-        out = run_dense(args, "mxfp4" if args.workload == "dense_w4a8" else "uint4_zp")
+        out = run_dense(args, {"dense_w4a8": "mxfp4", "dense_w4a4": "mxfp4_a4"}.get(args.workload, "uint4_zp"))
     else:
         fmt = {"moe_w4a16": "int4_sym", "moe_w4a16_mxint4": "mxint4"}.get(args.workload, "mxfp4")
         out = run_moe(args, fmt, args.workload == "moe_w4a8")
