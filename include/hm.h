@@ -73,10 +73,16 @@ typedef enum hm_wfmt {
   HM_W_INT4_SYM = 0, /* signed 4-bit two's complement q, bf16 scale per 128 along K: w = s*q */
   HM_W_UINT4_ZP = 1, /* unsigned 4-bit u, bf16 scale + 4-bit zero point per 128: w = s*(u-z) */
   HM_W_MXFP4 = 2,    /* E2M1 codes, E8M0 scale per 32 along K: w = e2m1(c) * 2^(b-127) */
-  HM_W_MXINT4 = 3    /* two's complement 4-bit q read as 1.2 fixed point, E8M0 scale per 32
+  HM_W_MXINT4 = 3,   /* two's complement 4-bit q read as 1.2 fixed point, E8M0 scale per 32
                         along K: w = (q/4) * 2^(b-127); the format is named in the pages' lists
                         (cocoloop.cn item; aihaber.org article, hardware and format support)
                         without a definition, this is the MX-family reading */
+  HM_W_UINT3_ZP = 4, /* unsigned 3-bit u, bf16 scale + 3-bit zero point per 128: w = s*(u-z) */
+  HM_W_UINT2_ZP = 5  /* unsigned 2-bit u, bf16 scale + 2-bit zero point per 128: w = s*(u-z);
+                        the pages list INT1..INT8 weights and name GPTQ INT3 as a compatibility
+                        case (cocoloop.cn news item, format list and deployer section).  Both are
+                        widened to the 4-bit zero-point device layout by hm_transform (exact; no
+                        bandwidth saving over 4 bits) and run on every W4A16 kernel */
 } hm_wfmt;
 
 /* Activation format (the compute option choosing A16, A8 or A4). */
@@ -154,9 +160,13 @@ hm_status hm_transform_size(const hm_wdesc* d, size_t* bytes);
  * per weight, before inference.
  *   codes  [E][N][K/2] bytes, element k=2j in the low nibble of byte j,
  *          k=2j+1 in the high nibble (two's complement for INT4_SYM and
- *          MXINT4, unsigned for UINT4_ZP, E2M1 bits for MXFP4).
+ *          MXINT4, unsigned for UINT4_ZP, E2M1 bits for MXFP4);
+ *          UINT2_ZP: [E][N][K/4], element 4j+i at bits 2i..2i+1 of byte j;
+ *          UINT3_ZP: [E][N][3K/8], element 8j+i at bits 3i..3i+2 of the
+ *          little-endian 24-bit word of bytes 3j..3j+2.
  *   scales INT4 formats: bf16 [E][N][K/128]; MXFP4, MXINT4: E8M0 bytes [E][N][K/32].
- *   zeros  UINT4_ZP only: bytes [E][N][K/128], low nibble used; else NULL.
+ *   zeros  zero-point formats only: bytes [E][N][K/128], the code's low 4 / 3 / 2
+ *          bits used; else NULL.
  *   w_dev  output, w_bytes >= hm_transform_size.  Opaque; valid only for the
  *          same descriptor. */
 hm_status hm_transform(const hm_wdesc* d, const uint8_t* codes, const void* scales,

@@ -33,10 +33,15 @@ Region C, zero points (uint4_zp only, next 256-byte boundary): 8 bytes per
   point of column 16*nb + c, group g.  Padding 0.
 Total size: end of the last region rounded up to 256 bytes.  Every byte not
 named above (the alignment gaps between regions) is zero.
+
+uint3_zp and uint2_zp (3- and 2-bit codes with zero points) are widened: their
+device bytes are exactly those of uint4_zp built from the same code and zero
+point values (each below 8 or 4), with the same scales.
 """
 import numpy as np
 
-from .quant import FMT_INT4_SYM, FMT_UINT4_ZP, FMT_MXFP4, MX_FORMATS, unpack_nibbles
+from .quant import (FMT_INT4_SYM, FMT_UINT4_ZP, FMT_MXFP4, MX_FORMATS, NARROW_ZP, pack_nibbles, unpack_bits,
+                    unpack_nibbles)
 
 
 def _align(x, a=256):
@@ -45,6 +50,8 @@ def _align(x, a=256):
 
 def sizes(fmt, E, N, K):
     """(offset_B, offset_C, total) in bytes."""
+    if fmt in NARROW_ZP:
+        fmt = FMT_UINT4_ZP
     NB = (N + 15) // 16
     KG = K // 128
     a = E * NB * KG * 1024
@@ -65,6 +72,11 @@ def transform_ref(fmt, codes, scales, zeros=None):
     scales int4: uint16 bf16 bits [E,N,K/128]; mxfp4: uint8 [E,N,K/32]
     zeros  uint8 [E,N,K/128] (uint4_zp only)
     Returns a uint8 array of the total size."""
+    if fmt in NARROW_ZP:
+        bits = NARROW_ZP[fmt]
+        c = np.asarray(codes, dtype=np.uint8)
+        wide = np.stack([pack_nibbles(unpack_bits(c[e], bits)) for e in range(c.shape[0])])
+        return transform_ref(FMT_UINT4_ZP, wide, scales, np.asarray(zeros) & ((1 << bits) - 1))
     codes = np.asarray(codes, dtype=np.uint8)
     E, N, K2 = codes.shape
     K = 2 * K2

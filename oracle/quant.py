@@ -41,7 +41,12 @@ FMT_INT4_SYM = "int4_sym"
 FMT_UINT4_ZP = "uint4_zp"
 FMT_MXFP4 = "mxfp4"
 FMT_MXINT4 = "mxint4"
+FMT_UINT3_ZP = "uint3_zp"
+FMT_UINT2_ZP = "uint2_zp"
 FORMATS = (FMT_INT4_SYM, FMT_UINT4_ZP, FMT_MXFP4)
+# narrower unsigned formats with a zero point (INT1..INT8 are in the pages'
+# format list, cocoloop.cn news item; GPTQ INT3 is their compatibility case)
+NARROW_ZP = {FMT_UINT3_ZP: 3, FMT_UINT2_ZP: 2}
 # formats with one E8M0 scale per 32 values (the MX family)
 MX_FORMATS = (FMT_MXFP4, FMT_MXINT4)
 
@@ -105,6 +110,64 @@ def quant_uint4_zp(w):
     u[nz] = np.clip(np.rint(wg[nz] / s[nz][:, None]) + z[nz][:, None].astype(np.float64),
                     0, 15).astype(np.uint8)
     return u.reshape(n, k), sbits, z
+
+
+def quant_uint_zp(w, bits):
+    """The zero-point rule of quant_uint4_zp for b-bit codes (b = 2, 3, 4):
+    per 128-group s = bf16(fp32((max - min) / (2^b - 1)));
+    z = clamp(rne(-min / s), 0, 2^b - 1);  u = clamp(rne(w / s) + z, 0, 2^b - 1);
+    s = 0 gives u = z = 0.  Returns (u uint8 [N,K], scale bits, z uint8)."""
+    top = (1 << bits) - 1
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    wg = _groups(w, GROUP_INT4).astype(np.float64)
+    mx = wg.max(axis=2)
+    mn = wg.min(axis=2)
+    s32 = ((mx - mn) / float(top)).astype(np.float32)
+    sbits = codecs.bf16_rne_bits(s32)
+    s = codecs.bf16_value(sbits).astype(np.float64)
+    u = np.zeros(wg.shape, dtype=np.uint8)
+    z = np.zeros(s.shape, dtype=np.uint8)
+    nz = s > 0
+    z[nz] = np.clip(np.rint(-mn[nz] / s[nz]), 0, top).astype(np.uint8)
+    u[nz] = np.clip(np.rint(wg[nz] / s[nz][:, None]) + z[nz][:, None].astype(np.float64),
+                    0, top).astype(np.uint8)
+    return u.reshape(n, k), sbits, z
+
+
+def pack_bits(codes, bits):
+    """[N,K] b-bit codes -> the standard packing: b = 2: four per byte, value
+    4j + i at bits 2i..2i+1 of byte j; b = 3: eight per three bytes, value
+    8j + i at bits 3i..3i+2 of the little-endian 24-bit word of bytes 3j..3j+2."""
+    c = np.asarray(codes).astype(np.int64) & ((1 << bits) - 1)
+    n, k = c.shape
+    per = 4 if bits == 2 else 8
+    assert k % per == 0
+    g = c.reshape(n, k // per, per)
+    word = np.zeros((n, k // per), dtype=np.int64)
+    for i in range(per):
+        word |= g[:, :, i] << (bits * i)
+    nbytes = bits * per // 8
+    out = np.zeros((n, k // per, nbytes), dtype=np.uint8)
+    for b in range(nbytes):
+        out[:, :, b] = (word >> (8 * b)) & 0xFF
+    return out.reshape(n, k * bits // 8)
+
+
+def unpack_bits(packed, bits):
+    """Inverse of pack_bits: [N, K*b/8] bytes -> [N, K] codes (uint8)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    n, kb = p.shape
+    per = 4 if bits == 2 else 8
+    nbytes = bits * per // 8
+    g = p.reshape(n, kb // nbytes, nbytes).astype(np.int64)
+    word = np.zeros(g.shape[:2], dtype=np.int64)
+    for b in range(nbytes):
+        word |= g[:, :, b] << (8 * b)
+    out = np.zeros((n, kb // nbytes, per), dtype=np.uint8)
+    for i in range(per):
+        out[:, :, i] = (word >> (bits * i)) & ((1 << bits) - 1)
+    return out.reshape(n, kb // nbytes * per)
 
 
 # ----------------------------------------------------------------------------- MXFP4
@@ -194,8 +257,16 @@ def dequant(fmt, packed, scales, zeros=None):
     uint4_zp:  s * (u - z)     (z one byte per group, low nibble used)
     mxfp4:     E2M1(code) * 2^(b-127)
     mxint4:    (q / 4) * 2^(b-127)   (q two's complement nibble)
+    uint3_zp, uint2_zp: s * (u - z) with u, z 3- or 2-bit (packed as in pack_bits)
     Every product is exact in fp32 (at most 12 significant bits, and the MX
     products stay at or above 2^-129) while it stays below 2^128."""
+    if fmt in NARROW_ZP:
+        u = unpack_bits(packed, NARROW_ZP[fmt])
+        n, k = u.shape
+        s = codecs.bf16_value(scales).astype(np.float64)
+        z = (np.asarray(zeros, dtype=np.int64) & ((1 << NARROW_ZP[fmt]) - 1)).astype(np.float64)
+        d = u.astype(np.float64).reshape(n, k // GROUP_INT4, GROUP_INT4) - z[:, :, None]
+        return (d * s[:, :, None]).reshape(n, k).astype(np.float32)
     u = unpack_nibbles(packed)
     n, k = u.shape
     if fmt == FMT_INT4_SYM:
@@ -233,6 +304,9 @@ def quantize(fmt, w):
     if fmt == FMT_MXINT4:
         c, e = quant_mxint4(w)
         return dict(codes=pack_nibbles(c), scales=e, zeros=None)
+    if fmt in NARROW_ZP:
+        u, s, z = quant_uint_zp(w, NARROW_ZP[fmt])
+        return dict(codes=pack_bits(u, NARROW_ZP[fmt]), scales=s, zeros=z)
     raise ValueError(fmt)
 
 
@@ -284,6 +358,9 @@ def fp8_rows_dequant(codes, scales):
 def storage_bytes(n, k, fmt, group=None, scale_bits=16, zero_bits=4):
     """Bytes of the standard format excluding padding and alignment:
     n*k 4-bit codes + one scale per group (+ one zero point per group)."""
+    code_bits = NARROW_ZP.get(fmt, 4)
+    if fmt in NARROW_ZP:
+        zero_bits = code_bits
     if fmt in MX_FORMATS:
         group = group or GROUP_MX
         scale_bits = 8
@@ -293,7 +370,7 @@ def storage_bytes(n, k, fmt, group=None, scale_bits=16, zero_bits=4):
         if fmt == FMT_INT4_SYM:
             zero_bits = 0
     groups = n * (k // group)
-    bits = n * k * 4 + groups * (scale_bits + zero_bits)
+    bits = n * k * code_bits + groups * (scale_bits + zero_bits)
     return bits / 8.0
 
 

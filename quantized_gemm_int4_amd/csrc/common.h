@@ -26,7 +26,12 @@
 
 namespace hm {
 
-enum WFmt : int { W_INT4_SYM = 0, W_UINT4_ZP = 1, W_MXFP4 = 2, W_MXINT4 = 3 };
+enum WFmt : int { W_INT4_SYM = 0, W_UINT4_ZP = 1, W_MXFP4 = 2, W_MXINT4 = 3, W_UINT3_ZP = 4, W_UINT2_ZP = 5 };
+
+// 3- and 2-bit zero-point formats share the 4-bit zero-point device layout
+__host__ __device__ inline int device_fmt(int wfmt) {
+  return (wfmt == W_UINT3_ZP || wfmt == W_UINT2_ZP) ? W_UINT4_ZP : wfmt;
+}
 
 // formats with E8M0 scales per 32 values and the MX slot layout
 __host__ __device__ inline bool is_mx(int wfmt) { return wfmt == W_MXFP4 || wfmt == W_MXINT4; }

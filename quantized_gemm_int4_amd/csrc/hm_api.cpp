@@ -56,8 +56,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 hm_status check_desc(const hm_wdesc* d) {
   if (!d) return HM_ERR_NULL;
   if (d->abi != HM_ABI_VERSION) return HM_ERR_ABI;
-  if (d->wfmt != HM_W_INT4_SYM && d->wfmt != HM_W_UINT4_ZP && d->wfmt != HM_W_MXFP4 && d->wfmt != HM_W_MXINT4)
-    return HM_ERR_UNSUPPORTED;
+  if (d->wfmt < HM_W_INT4_SYM || d->wfmt > HM_W_UINT2_ZP) return HM_ERR_UNSUPPORTED;
   const int want_group = is_mx(d->wfmt) ? 32 : 128;
   if (d->group != want_group) return HM_ERR_SHAPE;
   if (d->num_experts < 1 || d->num_experts > 512 || d->n < 1 || d->k < 128 || (d->k % 128) != 0)
@@ -79,10 +78,13 @@ bool mx_a16(const hm_wdesc* d, int32_t afmt) { return is_mx(d->wfmt) && afmt == 
 const char* pair_name(const hm_wdesc* d, int32_t afmt) {
   if (d->wfmt == HM_W_MXFP4) return afmt == HM_A_BF16 ? "w4a16-mxfp4" : (afmt == HM_A_MXFP4 ? "w4a4-mxfp4" : "w4a8-mxfp4");
   if (d->wfmt == HM_W_MXINT4) return "w4a16-mxint4";
+  if (d->wfmt == HM_W_UINT3_ZP) return "w3a16-uint3zp";
+  if (d->wfmt == HM_W_UINT2_ZP) return "w2a16-uint2zp";
   return d->wfmt == HM_W_UINT4_ZP ? "w4a16-uint4zp" : "w4a16-int4sym";
 }
 
-Geom geom_of(const hm_wdesc* d) { return make_geom(d->wfmt, d->num_experts, d->n, d->k); }
+// the device layout's geometry (3- and 2-bit zero-point formats use the 4-bit one)
+Geom geom_of(const hm_wdesc* d) { return make_geom(device_fmt(d->wfmt), d->num_experts, d->n, d->k); }
 
 // The 128-row and 256-row tile kernels address the scale / zero-point region
 // with 32-bit offsets from its start.
@@ -345,7 +347,7 @@ hm_status launch_moe(const hm_wdesc* d, int32_t afmt, const void* w_dev, const v
   GemmArgs a{};
   a.w = (const uint8_t*)w_dev;
   a.G = geom_of(d);
-  a.wfmt = d->wfmt;
+  a.wfmt = device_fmt(d->wfmt);
   a.a8 = afmt == HM_A_FP8_ROWSCALE;
   a.a4 = afmt == HM_A_MXFP4;
   a.x = a_in;
@@ -420,7 +422,7 @@ HM_API hm_status hm_transform(const hm_wdesc* d, const uint8_t* codes, const voi
   hm_status s = check_desc(d);
   if (s) return s;
   if (!codes || !scales || !w_dev) return HM_ERR_NULL;
-  if (d->wfmt == HM_W_UINT4_ZP && !zeros) return HM_ERR_NULL;
+  if (device_fmt(d->wfmt) == HM_W_UINT4_ZP && !zeros) return HM_ERR_NULL;
   if (!aligned(codes, 16) || !aligned(w_dev, 256)) return HM_ERR_ALIGN;
   if (!aligned(scales, is_mx(d->wfmt) ? 1 : 2)) return HM_ERR_ALIGN;
   const Geom G = geom_of(d);
@@ -439,7 +441,7 @@ HM_API hm_status hm_dequant(const hm_wdesc* d, const void* w_dev, size_t w_bytes
   if (expert < 0 || expert >= d->num_experts) return HM_ERR_SHAPE;
   const Geom G = geom_of(d);
   if (w_bytes < G.total) return HM_ERR_WORKSPACE;
-  if (launch_dequant(d->wfmt, G, (const uint8_t*)w_dev, expert, out, stream) != hipSuccess)
+  if (launch_dequant(device_fmt(d->wfmt), G, (const uint8_t*)w_dev, expert, out, stream) != hipSuccess)
     return HM_ERR_HIP;
   return HM_OK;
 }
@@ -532,7 +534,7 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, const 
              p.sc.nbw, p.sc.ks, p.sc.nw, p.sc.splits, p.ksg,
              afmt == HM_A_MXFP4 ? "scale_16x16x128_f8f6f4_fp4xfp4" : (a8 ? "scale_16x16x128_f8f6f4" : "16x16x32_bf16"));
   else if (p.path == P_BIG) {
-    const Geom G = make_geom(d->wfmt, 1, d->n, d->k);
+    const Geom G = make_geom(device_fmt(d->wfmt), 1, d->n, d->k);
     const int64_t tiles = big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows);
     const int64_t halves = 2 * (tiles - big_full_tiles(G, m, d->wfmt == HM_W_MXFP4));
     snprintf(buf, buf_len, "%s tile 256x256 waves=%s mfma=%s half_tiles=%lld", w,
@@ -574,7 +576,7 @@ HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, con
   GemmArgs a{};
   a.w = (const uint8_t*)w_dev;
   a.G = geom_of(d);
-  a.wfmt = d->wfmt;
+  a.wfmt = device_fmt(d->wfmt);
   a.a8 = afmt == HM_A_FP8_ROWSCALE;
   a.a4 = afmt == HM_A_MXFP4;
   a.x = x;

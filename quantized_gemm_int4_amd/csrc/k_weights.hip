@@ -29,7 +29,25 @@ k_transform_codes(int wfmt, Geom G, const uint8_t* __restrict__ codes, uint8_t* 
     const int64_t n = nb * 16 + (L & 15);
     const int h = L >> 4;
     u32x4_t v;
-    if (n < G.N) {
+    if (n < G.N && (wfmt == W_UINT3_ZP || wfmt == W_UINT2_ZP)) {
+      // narrow codes widened to nibbles: word j of the slot holds values
+      // k = 128 g + 32 j + 8 h + i, i = 0..7, value 2p in nibble p, 2p+1 in p+4
+      const int bits = wfmt == W_UINT3_ZP ? 3 : 2;
+      const uint8_t* row = codes + (e * G.N + n) * (G.K * bits / 8);
+      for (int j = 0; j < 4; ++j) {
+        const int64_t k0 = 128 * g + 32 * j + 8 * h;       // multiple of 8
+        const uint8_t* p = row + k0 * bits / 8;
+        const uint32_t word = bits == 3 ? (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16)
+                                        : (uint32_t)p[0] | ((uint32_t)p[1] << 8);
+        uint32_t o = 0;
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t val = (word >> (bits * i)) & ((1u << bits) - 1u);
+          const int pos = (i & 1) ? 4 + (i >> 1) : (i >> 1);
+          o |= val << (4 * pos);
+        }
+        v[j] = o;
+      }
+    } else if (n < G.N) {
       const uint8_t* row = codes + (e * G.N + n) * row_bytes;
       if (is_mx(wfmt)) {
         v = ld16(row + 64 * g + 16 * h);
@@ -91,9 +109,10 @@ k_transform_scales_mx(Geom G, const uint8_t* __restrict__ scales, uint32_t* __re
   }
 }
 
-// Zero points (UINT4_ZP): one thread per (e, nb, g) u64 of 16 nibbles.
+// Zero points (zero-point formats): one thread per (e, nb, g) u64 of 16
+// nibbles; `mask` keeps the code width's bits of each zero-point byte.
 __global__ void __launch_bounds__(256)
-k_transform_zeros(Geom G, const uint8_t* __restrict__ zeros, uint64_t* __restrict__ out) {
+k_transform_zeros(Geom G, const uint8_t* __restrict__ zeros, uint64_t* __restrict__ out, uint32_t mask) {
   const int64_t cnt = G.E * G.NB * G.KG;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < cnt;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -104,7 +123,7 @@ k_transform_zeros(Geom G, const uint8_t* __restrict__ zeros, uint64_t* __restric
     uint64_t v = 0;
     for (int c = 0; c < 16; ++c) {
       const int64_t n = nb * 16 + c;
-      if (n < G.N) v |= (uint64_t)(zeros[(e * G.N + n) * G.KG + g] & 0xF) << (4 * c);
+      if (n < G.N) v |= (uint64_t)(zeros[(e * G.N + n) * G.KG + g] & mask) << (4 * c);
     }
     out[i] = v;
   }
@@ -196,15 +215,16 @@ hipError_t launch_transform(int wfmt, const Geom& G, const uint8_t* codes, const
     hipLaunchKernelGGL(k_transform_scales_int4, dim3(grid_for(G.E * G.NB * G.KG * 16)), dim3(256),
                        0, st, G, (const uint16_t*)scales, (uint16_t*)(out + G.off_scales));
   }
-  if (wfmt == W_UINT4_ZP) {
+  if (device_fmt(wfmt) == W_UINT4_ZP) {
+    const uint32_t mask = wfmt == W_UINT3_ZP ? 0x7u : (wfmt == W_UINT2_ZP ? 0x3u : 0xFu);
     hipLaunchKernelGGL(k_transform_zeros, dim3(grid_for(G.E * G.NB * G.KG)), dim3(256), 0, st, G,
-                       zeros, (uint64_t*)(out + G.off_zeros));
+                       zeros, (uint64_t*)(out + G.off_zeros), mask);
   }
   // gap ends: codes end .. scales start, scales end .. zeros start, zeros end .. total
   const size_t codes_end = (size_t)G.E * G.NB * G.KG * 1024;
   const size_t scales_end = G.off_scales + (is_mx(wfmt) ? (size_t)G.E * G.NB * G.KG4 * 256
                                                               : (size_t)G.E * G.NB * G.KG * 32);
-  const size_t zeros_end = (wfmt == W_UINT4_ZP) ? G.off_zeros + (size_t)G.E * G.NB * G.KG * 8 : G.off_zeros;
+  const size_t zeros_end = (device_fmt(wfmt) == W_UINT4_ZP) ? G.off_zeros + (size_t)G.E * G.NB * G.KG * 8 : G.off_zeros;
   hipLaunchKernelGGL(k_zero_gaps, dim3(1), dim3(256), 0, st, out, codes_end, G.off_scales, scales_end,
                      G.off_zeros, zeros_end, G.total);
   return hipGetLastError();

@@ -41,7 +41,7 @@ def quantize_experts(fmt, ws):
     sts = [quant.quantize(fmt, w) for w in ws]
     codes = np.stack([s["codes"] for s in sts])
     scales = np.stack([s["scales"] for s in sts])
-    zeros = np.stack([s["zeros"] for s in sts]) if fmt == quant.FMT_UINT4_ZP else None
+    zeros = np.stack([s["zeros"] for s in sts]) if sts[0]["zeros"] is not None else None
     what = np.stack([quant.dequant(fmt, s["codes"], s["scales"], s["zeros"]) for s in sts])
     return codes, scales, zeros, what
 

@@ -16,7 +16,8 @@ SHAPES = [(1, 16, 128), (2, 37, 256), (1, 5, 640), (3, 100, 384)]
 
 def _random_std(fmt, E, N, K, seed):
     r = np.random.default_rng(seed)
-    codes = r.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    bits = quant.NARROW_ZP.get(fmt, 4)
+    codes = r.integers(0, 256, size=(E, N, K * bits // 8), dtype=np.uint8)
     if fmt in quant.MX_FORMATS:
         scales = r.integers(0, 256, size=(E, N, K // 32), dtype=np.uint8)   # every byte, NaN (255) included
         scales.reshape(-1)[:4] = [252, 253, 254, 255]          # the top bytes on every shape
@@ -25,11 +26,16 @@ def _random_std(fmt, E, N, K, seed):
         # including subnormals and zero
         scales = r.integers(0, 0x7B00, size=(E, N, K // 128)).astype(np.uint16)
         scales |= (r.integers(0, 2, size=scales.shape) << 15).astype(np.uint16)
-    zeros = r.integers(0, 16, size=(E, N, K // 128), dtype=np.uint8) if fmt == quant.FMT_UINT4_ZP else None
+    # zero-point bytes: random high bits too (only the code width's low bits count)
+    zeros = (r.integers(0, 256, size=(E, N, K // 128), dtype=np.uint8)
+             if fmt in (quant.FMT_UINT4_ZP,) + tuple(quant.NARROW_ZP) else None)
     return codes, scales, zeros
 
 
-@pytest.mark.parametrize("fmt", quant.FORMATS + (quant.FMT_MXINT4,))
+ALL = quant.FORMATS + (quant.FMT_MXINT4, quant.FMT_UINT3_ZP, quant.FMT_UINT2_ZP)
+
+
+@pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("E,N,K", SHAPES)
 def test_transform_byte_exact(fmt, E, N, K):
     import quantized_gemm_int4_amd as hm
@@ -42,7 +48,7 @@ def test_transform_byte_exact(fmt, E, N, K):
     assert np.array_equal(w.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("fmt", quant.FORMATS + (quant.FMT_MXINT4,))
+@pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("E,N,K", SHAPES)
 def test_dequant_bit_exact(fmt, E, N, K):
     import quantized_gemm_int4_amd as hm
@@ -61,7 +67,7 @@ def test_dequant_bit_exact(fmt, E, N, K):
         assert (scales == 255).any() and (scales >= 253).any()
 
 
-@pytest.mark.parametrize("fmt", quant.FORMATS + (quant.FMT_MXINT4,))
+@pytest.mark.parametrize("fmt", ALL)
 def test_dequant_full_size_quantized(fmt):
     """Quantized N(0,0.02) weights at the dense FFN up-projection size."""
     import quantized_gemm_int4_amd as hm

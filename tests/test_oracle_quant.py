@@ -363,3 +363,71 @@ def test_mxfp4_rows_worked_block():
     # a zero row: scale byte 0, zero codes
     packed, e = quant.quant_mxfp4_rows(np.zeros((1, 64), dtype=np.uint16))
     assert (e == 0).all() and (packed == 0).all()
+
+
+# ------------------------------------------------------------------ 3- and 2-bit zero-point formats
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_uint_zp_narrow_brute_force(bits):
+    """The zero-point rule at 3 and 2 bits: scale bf16(fp32((max - min) /
+    (2^b - 1))) recomputed with torch, zero point and codes by nearest-value
+    search with ties to even, the clamp at 0 and 2^b - 1, s = 0 groups; at 4
+    bits the generic rule equals quant_uint4_zp."""
+    top = (1 << bits) - 1
+    r = np.random.default_rng(30 + bits)
+    w = r.normal(0, 0.02, size=(5, 256)).astype(np.float32)
+    w[2, 128:] = 0.01                                         # constant group -> s = 0
+    w[3, :128] = np.abs(w[3, :128]) + 0.05                    # one-signed -> z clamps at 0
+    u, sbits, z = quant.quant_uint_zp(w, bits)
+    s = codecs.bf16_value(sbits).astype(np.float64)
+    assert u.max() <= top and z.max() <= top
+    for n in range(5):
+        for g in range(2):
+            blk = w[n, g * 128:(g + 1) * 128]
+            tb = torch.from_numpy(blk.copy())
+            s32 = (tb.max() - tb.min()) / torch.tensor(float(top), dtype=torch.float32)
+            assert sbits[n, g] == s32.to(torch.bfloat16).view(torch.int16).item() & 0xFFFF
+            if s[n, g] == 0:
+                assert z[n, g] == 0 and (u[n, g * 128:(g + 1) * 128] == 0).all()
+                continue
+            zz = min(max(_brute_nearest(-float(blk.min()) / s[n, g], np.arange(-64, 64.0)), 0), top)
+            assert z[n, g] == zz
+            for i, wk in enumerate(blk.astype(np.float64)):
+                v = _brute_nearest(wk / s[n, g], np.arange(-64, 64.0)) + zz
+                assert u[n, g * 128 + i] == min(max(v, 0), top)
+    u4, s4, z4 = quant.quant_uint_zp(w, 4)
+    u4r, s4r, z4r = quant.quant_uint4_zp(w)
+    assert np.array_equal(u4, u4r) and np.array_equal(s4, s4r) and np.array_equal(z4, z4r)
+
+
+def test_pack_bits_layout_and_round_trips():
+    """2-bit: value 4j + i at bits 2i of byte j (every byte value decodes and
+    re-encodes); 3-bit: codes 0..7 pack to the 24-bit word 0o76543210 =
+    0xFAC688, i.e. bytes 0x88 0xC6 0xFA; random round trips at both widths."""
+    p = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    u = quant.unpack_bits(p, 2)
+    for i in range(4):
+        assert (u[0, i::4] == (np.arange(256) >> (2 * i)) & 3).all()
+    assert np.array_equal(quant.pack_bits(u, 2), p)
+    assert list(quant.pack_bits(np.arange(8).reshape(1, 8), 3)[0]) == [0x88, 0xC6, 0xFA]
+    r = np.random.default_rng(7)
+    for bits in (2, 3):
+        c = r.integers(0, 1 << bits, size=(9, 256))
+        assert np.array_equal(quant.unpack_bits(quant.pack_bits(c, bits), bits), c)
+
+
+def test_narrow_storage_and_dequant():
+    """Storage by the pages' formula (codes + 16-bit scale + zero point per
+    128): 3.1484375 and 2.140625 bits per value; dequant is s * (u - z) per
+    element, recomputed from the unpacked parts."""
+    assert quant.bits_per_value(quant.FMT_UINT3_ZP) == (128 * 3 + 16 + 3) / 128
+    assert quant.bits_per_value(quant.FMT_UINT2_ZP) == (128 * 2 + 16 + 2) / 128
+    r = np.random.default_rng(8)
+    w = r.normal(0, 0.02, size=(6, 384)).astype(np.float32)
+    for fmt, bits in quant.NARROW_ZP.items():
+        st = quant.quantize(fmt, w)
+        d = quant.dequant(fmt, st["codes"], st["scales"], st["zeros"]).astype(np.float64)
+        u = quant.unpack_bits(st["codes"], bits).astype(np.float64)
+        s = np.repeat(codecs.bf16_value(st["scales"]).astype(np.float64), 128, 1)
+        z = np.repeat(st["zeros"].astype(np.float64), 128, 1)
+        assert np.array_equal(d, (u - z) * s)
