@@ -78,11 +78,14 @@ typedef enum hm_wfmt {
                         (cocoloop.cn item; aihaber.org article, hardware and format support)
                         without a definition, this is the MX-family reading */
   HM_W_UINT3_ZP = 4, /* unsigned 3-bit u, bf16 scale + 3-bit zero point per 128: w = s*(u-z) */
-  HM_W_UINT2_ZP = 5  /* unsigned 2-bit u, bf16 scale + 2-bit zero point per 128: w = s*(u-z);
+  HM_W_UINT2_ZP = 5, /* unsigned 2-bit u, bf16 scale + 2-bit zero point per 128: w = s*(u-z);
                         the pages list INT1..INT8 weights and name GPTQ INT3 as a compatibility
                         case (cocoloop.cn news item, format list and deployer section).  Both are
                         widened to the 4-bit zero-point device layout by hm_transform (exact; no
                         bandwidth saving over 4 bits) and run on every W4A16 kernel */
+  HM_W_INT8_SYM = 6  /* signed 8-bit two's complement q, bf16 scale per 128 along K: w = s*q (own
+                        device layout of 2 KiB tiles; the streaming (path 1) and 128 x 128
+                        (path 4) kernels, and grouped streaming and 128-row units) */
 } hm_wfmt;
 
 /* Activation format (the compute option choosing A16, A8 or A4). */
@@ -163,7 +166,8 @@ hm_status hm_transform_size(const hm_wdesc* d, size_t* bytes);
  *          MXINT4, unsigned for UINT4_ZP, E2M1 bits for MXFP4);
  *          UINT2_ZP: [E][N][K/4], element 4j+i at bits 2i..2i+1 of byte j;
  *          UINT3_ZP: [E][N][3K/8], element 8j+i at bits 3i..3i+2 of the
- *          little-endian 24-bit word of bytes 3j..3j+2.
+ *          little-endian 24-bit word of bytes 3j..3j+2;
+ *          INT8_SYM: [E][N][K], one two's complement byte per element.
  *   scales INT4 formats: bf16 [E][N][K/128]; MXFP4, MXINT4: E8M0 bytes [E][N][K/32].
  *   zeros  zero-point formats only: bytes [E][N][K/128], the code's low 4 / 3 / 2
  *          bits used; else NULL.

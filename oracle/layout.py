@@ -37,11 +37,18 @@ named above (the alignment gaps between regions) is zero.
 uint3_zp and uint2_zp (3- and 2-bit codes with zero points) are widened: their
 device bytes are exactly those of uint4_zp built from the same code and zero
 point values (each below 8 or 4), with the same scales.
+
+int8_sym (one byte per value): Region A holds E*NB*KG tiles of 2048 bytes,
+tile index (e*NB + nb)*KG + g; a tile is two halves of 64 slots of 16 bytes;
+slot L of half p covers column 16*nb + L%16 and quarter h = L//16, and its
+byte 8*jj + i holds the value k = 128*g + 32*(2*p + jj) + 8*h + i (jj in 0..1,
+i in 0..7) as its two's complement byte.  Columns >= N hold 0.  Region B is
+the int4 one (bf16 scales); there is no Region C.
 """
 import numpy as np
 
-from .quant import (FMT_INT4_SYM, FMT_UINT4_ZP, FMT_MXFP4, MX_FORMATS, NARROW_ZP, pack_nibbles, unpack_bits,
-                    unpack_nibbles)
+from .quant import (FMT_INT4_SYM, FMT_INT8_SYM, FMT_UINT4_ZP, FMT_MXFP4, MX_FORMATS, NARROW_ZP, pack_nibbles,
+                    unpack_bits, unpack_nibbles)
 
 
 def _align(x, a=256):
@@ -54,7 +61,7 @@ def sizes(fmt, E, N, K):
         fmt = FMT_UINT4_ZP
     NB = (N + 15) // 16
     KG = K // 128
-    a = E * NB * KG * 1024
+    a = E * NB * KG * (2048 if fmt == FMT_INT8_SYM else 1024)
     if fmt in MX_FORMATS:
         b = E * NB * ((KG + 3) // 4) * 256
     else:
@@ -78,6 +85,8 @@ def transform_ref(fmt, codes, scales, zeros=None):
         wide = np.stack([pack_nibbles(unpack_bits(c[e], bits)) for e in range(c.shape[0])])
         return transform_ref(FMT_UINT4_ZP, wide, scales, np.asarray(zeros) & ((1 << bits) - 1))
     codes = np.asarray(codes, dtype=np.uint8)
+    if fmt == FMT_INT8_SYM:
+        return _transform_int8_ref(codes, scales)
     E, N, K2 = codes.shape
     K = 2 * K2
     NB = (N + 15) // 16
@@ -153,4 +162,35 @@ def transform_ref(fmt, codes, scales, zeros=None):
                 if n < N:
                     zb[:, nb, :, cc // 2] |= (zz[:, n, :] << (4 * (cc % 2))).astype(np.uint8)
         out[oc:oc + zb.size] = zb.ravel()
+    return out
+
+
+def _transform_int8_ref(codes, scales):
+    """int8_sym device bytes, element by element from the rule in the header."""
+    E, N, K = codes.shape
+    NB = (N + 15) // 16
+    KG = K // 128
+    ob, _, total = sizes(FMT_INT8_SYM, E, N, K)
+    out = np.zeros(total, dtype=np.uint8)
+    tiles = np.zeros((E, NB, KG, 2, 64, 16), dtype=np.uint8)
+    for p in range(2):
+        for L in range(64):
+            c, h = L % 16, L // 16
+            for jj in range(2):
+                for i in range(8):
+                    for g in range(KG):
+                        k = 128 * g + 32 * (2 * p + jj) + 8 * h + i
+                        for nb in range(NB):
+                            n = 16 * nb + c
+                            if n < N:
+                                tiles[:, nb, g, p, L, 8 * jj + i] = codes[:, n, k]
+    out[:tiles.size] = tiles.ravel()
+    sb = np.zeros((E, NB, KG, 16), dtype=np.uint16)
+    sc = np.asarray(scales, dtype=np.uint16)
+    for nb in range(NB):
+        for cc in range(16):
+            n = 16 * nb + cc
+            if n < N:
+                sb[:, nb, :, cc] = sc[:, n, :]
+    out[ob:ob + sb.size * 2] = sb.view(np.uint8).ravel()
     return out

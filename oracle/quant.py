@@ -43,6 +43,7 @@ FMT_MXFP4 = "mxfp4"
 FMT_MXINT4 = "mxint4"
 FMT_UINT3_ZP = "uint3_zp"
 FMT_UINT2_ZP = "uint2_zp"
+FMT_INT8_SYM = "int8_sym"
 FORMATS = (FMT_INT4_SYM, FMT_UINT4_ZP, FMT_MXFP4)
 # narrower unsigned formats with a zero point (INT1..INT8 are in the pages'
 # format list, cocoloop.cn news item; GPTQ INT3 is their compatibility case)
@@ -83,6 +84,25 @@ def quant_int4_sym(w):
     q = np.zeros(wg.shape, dtype=np.int8)
     nz = s > 0
     q[nz] = np.clip(np.rint(wg[nz] / s[nz][:, None]), -8, 7).astype(np.int8)
+    return q.reshape(n, k), sbits
+
+
+# ----------------------------------------------------------------------------- symmetric INT8
+
+def quant_int8_sym(w):
+    """Symmetric INT8 (in the pages' INT1..INT8 weight list, cocoloop.cn news
+    item, format list), the INT4 rule at 8 bits: per (row, 128-group)
+    s = bf16(fp32(amax / 127)), q = clamp(rne(w / s), -128, 127) against the
+    stored scale, s = 0 gives q = 0.  Returns (q int8 [N,K], scale bits)."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    wg = _groups(w, GROUP_INT4).astype(np.float64)
+    amax = np.abs(wg).max(axis=2)
+    sbits = codecs.bf16_rne_bits((amax / 127.0).astype(np.float32))
+    s = codecs.bf16_value(sbits).astype(np.float64)
+    q = np.zeros(wg.shape, dtype=np.int8)
+    nz = s > 0
+    q[nz] = np.clip(np.rint(wg[nz] / s[nz][:, None]), -128, 127).astype(np.int8)
     return q.reshape(n, k), sbits
 
 
@@ -258,8 +278,14 @@ def dequant(fmt, packed, scales, zeros=None):
     mxfp4:     E2M1(code) * 2^(b-127)
     mxint4:    (q / 4) * 2^(b-127)   (q two's complement nibble)
     uint3_zp, uint2_zp: s * (u - z) with u, z 3- or 2-bit (packed as in pack_bits)
+    int8_sym:  s * q           (q a two's complement byte, one per value)
     Every product is exact in fp32 (at most 12 significant bits, and the MX
     products stay at or above 2^-129) while it stays below 2^128."""
+    if fmt == FMT_INT8_SYM:
+        q = np.asarray(packed, dtype=np.uint8).view(np.int8).astype(np.float64)
+        n, k = q.shape
+        s = codecs.bf16_value(scales).astype(np.float64)
+        return (q.reshape(n, k // GROUP_INT4, GROUP_INT4) * s[:, :, None]).reshape(n, k).astype(np.float32)
     if fmt in NARROW_ZP:
         u = unpack_bits(packed, NARROW_ZP[fmt])
         n, k = u.shape
@@ -307,6 +333,9 @@ def quantize(fmt, w):
     if fmt in NARROW_ZP:
         u, s, z = quant_uint_zp(w, NARROW_ZP[fmt])
         return dict(codes=pack_bits(u, NARROW_ZP[fmt]), scales=s, zeros=z)
+    if fmt == FMT_INT8_SYM:
+        q, s = quant_int8_sym(w)
+        return dict(codes=q.view(np.uint8), scales=s, zeros=None)
     raise ValueError(fmt)
 
 
@@ -358,7 +387,7 @@ def fp8_rows_dequant(codes, scales):
 def storage_bytes(n, k, fmt, group=None, scale_bits=16, zero_bits=4):
     """Bytes of the standard format excluding padding and alignment:
     n*k 4-bit codes + one scale per group (+ one zero point per group)."""
-    code_bits = NARROW_ZP.get(fmt, 4)
+    code_bits = NARROW_ZP.get(fmt, 8 if fmt == FMT_INT8_SYM else 4)
     if fmt in NARROW_ZP:
         zero_bits = code_bits
     if fmt in MX_FORMATS:
@@ -367,7 +396,7 @@ def storage_bytes(n, k, fmt, group=None, scale_bits=16, zero_bits=4):
         zero_bits = 0
     else:
         group = group or GROUP_INT4
-        if fmt == FMT_INT4_SYM:
+        if fmt in (FMT_INT4_SYM, FMT_INT8_SYM):
             zero_bits = 0
     groups = n * (k // group)
     bits = n * k * code_bits + groups * (scale_bits + zero_bits)

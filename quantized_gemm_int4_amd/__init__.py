@@ -17,11 +17,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhm.so")
 
 HM_ABI_VERSION = 2
-HM_W_INT4_SYM, HM_W_UINT4_ZP, HM_W_MXFP4, HM_W_MXINT4, HM_W_UINT3_ZP, HM_W_UINT2_ZP = 0, 1, 2, 3, 4, 5
+HM_W_INT4_SYM, HM_W_UINT4_ZP, HM_W_MXFP4, HM_W_MXINT4, HM_W_UINT3_ZP, HM_W_UINT2_ZP, HM_W_INT8_SYM = range(7)
 HM_A_BF16, HM_A_FP8_ROWSCALE, HM_A_MXFP4 = 0, 1, 2
 WFMT = {"int4_sym": HM_W_INT4_SYM, "uint4_zp": HM_W_UINT4_ZP, "mxfp4": HM_W_MXFP4, "mxint4": HM_W_MXINT4,
-        "uint3_zp": HM_W_UINT3_ZP, "uint2_zp": HM_W_UINT2_ZP}
-CODE_BITS = {HM_W_UINT3_ZP: 3, HM_W_UINT2_ZP: 2}     # other formats: 4
+        "uint3_zp": HM_W_UINT3_ZP, "uint2_zp": HM_W_UINT2_ZP, "int8_sym": HM_W_INT8_SYM}
+CODE_BITS = {HM_W_UINT3_ZP: 3, HM_W_UINT2_ZP: 2, HM_W_INT8_SYM: 8}     # other formats: 4
 STATUS = {0: "HM_OK", 1: "HM_ERR_NULL", 2: "HM_ERR_SHAPE", 3: "HM_ERR_ALIGN",
           4: "HM_ERR_UNSUPPORTED", 5: "HM_ERR_WORKSPACE", 6: "HM_ERR_HIP", 7: "HM_ERR_ABI", 8: "HM_ERR_TUNING"}
 HM_PATH_STREAM, HM_PATH_MID, HM_PATH_BIG, HM_PATH_TILE = 1, 2, 3, 4

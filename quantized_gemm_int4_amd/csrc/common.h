@@ -26,7 +26,8 @@
 
 namespace hm {
 
-enum WFmt : int { W_INT4_SYM = 0, W_UINT4_ZP = 1, W_MXFP4 = 2, W_MXINT4 = 3, W_UINT3_ZP = 4, W_UINT2_ZP = 5 };
+enum WFmt : int { W_INT4_SYM = 0, W_UINT4_ZP = 1, W_MXFP4 = 2, W_MXINT4 = 3, W_UINT3_ZP = 4, W_UINT2_ZP = 5,
+                  W_INT8_SYM = 6 };
 
 // 3- and 2-bit zero-point formats share the 4-bit zero-point device layout
 __host__ __device__ inline int device_fmt(int wfmt) {
@@ -49,7 +50,8 @@ __host__ __device__ inline Geom make_geom(int wfmt, int64_t E, int64_t N, int64_
   g.NB = (N + 15) / 16;
   g.KG = K / 128;
   g.KG4 = (g.KG + 3) / 4;
-  size_t a = (size_t)E * g.NB * g.KG * 1024;
+  // INT8: 2048-byte tiles (two 1 KiB halves, MFMA operands 0-1 and 2-3)
+  size_t a = (size_t)E * g.NB * g.KG * (wfmt == W_INT8_SYM ? 2048 : 1024);
   size_t b = is_mx(wfmt) ? (size_t)E * g.NB * g.KG4 * 256 : (size_t)E * g.NB * g.KG * 32;
   size_t c = (wfmt == W_UINT4_ZP) ? (size_t)E * g.NB * g.KG * 8 : 0;
   g.off_scales = align256(a);
@@ -113,6 +115,20 @@ __device__ __forceinline__ u32x4_t dq8_u4(uint32_t w, float s, float zs) {
     r[j] = pack_bf16(__builtin_fmaf((float)(t & 0xFFu), s, zs), __builtin_fmaf((float)(t >> 16), s, zs));
   }
   return r;
+}
+
+// Eight two's complement bytes (value i in byte i of the two words) -> eight
+// bf16 of q, exact, in value order: one sign-extending conversion per value.
+__device__ __forceinline__ u32x4_t i8x8_bf16(uint32_t lo, uint32_t hi) {
+  auto sb = [](uint32_t x, int b) { return (float)(int8_t)(x >> (8 * b)); };
+  return (u32x4_t){pack_bf16(sb(lo, 0), sb(lo, 1)), pack_bf16(sb(lo, 2), sb(lo, 3)),
+                   pack_bf16(sb(hi, 0), sb(hi, 1)), pack_bf16(sb(hi, 2), sb(hi, 3))};
+}
+// The same times s, each product rounded once to bf16.
+__device__ __forceinline__ u32x4_t i8x8_bf16_scaled(uint32_t lo, uint32_t hi, float s) {
+  auto sb = [s](uint32_t x, int b) { return (float)(int8_t)(x >> (8 * b)) * s; };
+  return (u32x4_t){pack_bf16(sb(lo, 0), sb(lo, 1)), pack_bf16(sb(lo, 2), sb(lo, 3)),
+                   pack_bf16(sb(hi, 0), sb(hi, 1)), pack_bf16(sb(hi, 2), sb(hi, 3))};
 }
 
 // Eight unsigned codes of one device-layout word (value 2p in nibble p, 2p+1

@@ -56,7 +56,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 hm_status check_desc(const hm_wdesc* d) {
   if (!d) return HM_ERR_NULL;
   if (d->abi != HM_ABI_VERSION) return HM_ERR_ABI;
-  if (d->wfmt < HM_W_INT4_SYM || d->wfmt > HM_W_UINT2_ZP) return HM_ERR_UNSUPPORTED;
+  if (d->wfmt < HM_W_INT4_SYM || d->wfmt > HM_W_INT8_SYM) return HM_ERR_UNSUPPORTED;
   const int want_group = is_mx(d->wfmt) ? 32 : 128;
   if (d->group != want_group) return HM_ERR_SHAPE;
   if (d->num_experts < 1 || d->num_experts > 512 || d->n < 1 || d->k < 128 || (d->k % 128) != 0)
@@ -80,6 +80,7 @@ const char* pair_name(const hm_wdesc* d, int32_t afmt) {
   if (d->wfmt == HM_W_MXINT4) return "w4a16-mxint4";
   if (d->wfmt == HM_W_UINT3_ZP) return "w3a16-uint3zp";
   if (d->wfmt == HM_W_UINT2_ZP) return "w2a16-uint2zp";
+  if (d->wfmt == HM_W_INT8_SYM) return "w8a16-int8sym";
   return d->wfmt == HM_W_UINT4_ZP ? "w4a16-uint4zp" : "w4a16-int4sym";
 }
 
@@ -152,8 +153,9 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   const bool a4 = afmt == HM_A_MXFP4;
   const bool tiles32 = scales_addr32(G);        // 128-row and 256-row kernels can address the scales
   if (tu.path == P_STREAM && m > kStreamWideRows) return HM_ERR_TUNING;
-  // W4A4: the streaming and 128 x 128 kernels only
-  if (a4 && (tu.path == P_MID || tu.path == P_BIG)) return HM_ERR_TUNING;
+  // W4A4 and INT8 weights: the streaming and 128 x 128 kernels only
+  const bool tile_only = a4 || d->wfmt == HM_W_INT8_SYM;
+  if (tile_only && (tu.path == P_MID || tu.path == P_BIG)) return HM_ERR_TUNING;
   if (tu.path == P_BIG && f4) return HM_ERR_TUNING;  // no 256 x 256 kernel for MX weights with bf16 rows
   if ((tu.path == P_MID || tu.path == P_BIG) && (!tiles32 || !mid_grid_fits(G, a8, m))) return HM_ERR_TUNING;
   // W4A16 up to 256 rows also streams (in 32-row chunks, each re-reading the
@@ -167,7 +169,7 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
     p.path = tu.path;
   } else if (m <= kStreamMaxRows || narrow) {
     p.path = P_STREAM;
-  } else if (a4) {
+  } else if (tile_only) {
     p.path = P_TILE;
   } else if (f4) {
     // MX weights with bf16 rows (no 256 x 256 kernel): 128 x 64 tiles, or 128 x
@@ -317,14 +319,15 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
     const bool tiles32 = scales_addr32(G);
     // 256-row units: not for MX weights with bf16 rows; they address
     // activation rows and scales with 32-bit offsets
-    const bool big_ok = !f4 && !a4 && !p.a64 && tiles32;
+    const bool tile_only = a4 || d->wfmt == HM_W_INT8_SYM;   // no 128-row tile or 256-row kernel
+    const bool big_ok = !f4 && !tile_only && !p.a64 && tiles32;
     if (tu.mbig > 0 && !big_ok) return HM_ERR_TUNING;
     p.big_min = (tu.mbig == -1 || !big_ok) ? 0 : big_min;
     // up-to-128-row units: the 128-row tile kernel (32-bit offsets), or the
     // 128 x 128 kernel for MX weights with bf16 rows when all pairs in
     // 128-row units would take many rounds of 128 x 64 tiles (T = 8192:
     // 7.92 against 8.30 ms)
-    const bool mid_ok = !a4 && !p.a64 && tiles32;
+    const bool mid_ok = !tile_only && !p.a64 && tiles32;
     if (tu.mtile == 1 && !mid_ok) return HM_ERR_TUNING;
     if (tu.mtile == 1) p.tile = P_MID;
     else if (tu.mtile == 2) p.tile = P_TILE;

@@ -726,7 +726,8 @@ int64_t big_n_tiles(const Geom& G) { return (G.NB + kBigCB - 1) / kBigCB; }
 
 hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
   // MX weights with bf16 rows run on the streaming, 128 x 64 and 128 x 128 kernels only
-  if (kmode_of(a) == KM_MX_A16 || kmode_of(a) == KM_MXI4_A16 || kmode_of(a) == KM_MX_A4) return hipErrorInvalidValue;
+  if (kmode_of(a) == KM_MX_A16 || kmode_of(a) == KM_MXI4_A16 || kmode_of(a) == KM_MX_A4 || kmode_of(a) == KM_INT8_A16)
+    return hipErrorInvalidValue;
   // scale and zero-point copies use 32-bit offsets from the scale region
   if (a.G.total - a.G.off_scales > 0xFFFFFFFFull) return hipErrorInvalidValue;
   if (a.wfmt == W_MXFP4)

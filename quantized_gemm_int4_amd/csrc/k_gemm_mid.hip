@@ -634,7 +634,8 @@ int64_t mid_n_tiles(const Geom& G, bool mx) {
 }
 
 hipError_t launch_gemm_mid(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
-  if (kmode_of(a) == KM_MX_A4) return hipErrorInvalidValue;   // W4A4 has no 128-row tile kernel
+  // W4A4 and INT8 weights have no 128-row tile kernel
+  if (kmode_of(a) == KM_MX_A4 || kmode_of(a) == KM_INT8_A16) return hipErrorInvalidValue;
   // scale and zero-point copies use 32-bit offsets from the scale region
   if (a.G.total - a.G.off_scales > 0xFFFFFFFFull) return hipErrorInvalidValue;
   // grouped activation rows are addressed by 32-bit offsets from x

@@ -55,6 +55,7 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
   constexpr bool F4 = MODE == KM_MX_A16 || MODE == KM_MXI4_A16;   // MX codes scaled to bf16
   constexpr bool I4 = MODE == KM_MXI4_A16;              // MXINT4: two's complement codes / 4
   constexpr bool A4 = MODE == KM_MX_A4;                 // MXFP4 rows, scaled fp4 x fp4 MFMA
+  constexpr bool Q8 = MODE == KM_INT8_A16;              // INT8 weights: 2 KiB tiles, two halves
   constexpr bool MXW = MX || F4 || A4;                  // E8M0 scale words
   constexpr int ROWS = MB * 16;
   constexpr int GB = MX ? 128 : (A4 ? 64 : 256);        // activation bytes per row per K group
@@ -62,7 +63,7 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
   constexpr int RED = StreamShape<NW, KS, NBW, MB>::kRedBytes;
   // vector-memory loads per ring slot: per column block the 1 KiB tile and
   // its scale word(s), plus the zero-point word
-  constexpr int kRingLoads = NBW * (MXW ? 2 : (ZP ? 3 : 2));
+  constexpr int kRingLoads = NBW * (MXW ? 2 : (ZP || Q8 ? 3 : 2));
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   uint8_t* const xs_lds = lds + RED;                    // activations: [rows][xb]
   __shared__ int64_t arow_s[ROWS];
@@ -188,12 +189,18 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
 
     // ---- weight ring: DW groups ahead, raw scale / zero words kept until use
     u32x4_t wq[DW][NBW];
+    u32x4_t wq2[Q8 ? DW : 1][Q8 ? NBW : 1];            // INT8: the tile's second half
     uint32_t wsr[DW][NBW], wsh[MXW ? 1 : DW][MXW ? 1 : NBW], wzr[ZP ? DW : 1][ZP ? NBW : 1];
     auto load_w = [&](int d, int64_t g) {               // g: group index in [0, KG)
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
         const int64_t tile = wtile0[j] + g;
-        wq[d][j] = ld16(a.w + tile * 1024 + lane * 16);
+        if (Q8) {
+          wq[d][j] = ld16(a.w + tile * 2048 + lane * 16);
+          wq2[Q8 ? d : 0][Q8 ? j : 0] = ld16(a.w + tile * 2048 + 1024 + lane * 16);
+        } else {
+          wq[d][j] = ld16(a.w + tile * 1024 + lane * 16);
+        }
         if (MXW) {
           // four groups' E8M0 scales per lane word: [e][nb][g/4][64 lanes]
           wsr[d][j] = *reinterpret_cast<const uint32_t*>(sbase + ((stile0[j] + g / 4) * 64 + lane) * 4);
@@ -293,6 +300,37 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
               const u32x4_t bw = I4 ? i4x8_bf16(wq[d][j][kk], sf[j]) : fp4x8_bf16(wq[d][j][kk], sf[j]);
 #pragma unroll
               for (int rb = 0; rb < MB; ++rb) acc[j][rb] = mfma_bf16(bw, af[rb], acc[j][rb]);
+            }
+          }
+        } else if (Q8) {
+          // INT8 codes enter the MFMA exactly (bf16 holds every byte value);
+          // operand kk is bytes 8 (kk % 2) .. + 7 of half kk / 2
+          f32x4_t t[NBW][MB];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            u32x4_t af[MB];
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) af[rb] = ld16(xg + lrow[rb] * xb + (32 * kk + 8 * q_l) * 2);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+              const u32x4_t hv = kk < 2 ? wq[d][j] : wq2[Q8 ? d : 0][Q8 ? j : 0];
+              const u32x4_t bw = i8x8_bf16(hv[2 * (kk & 1)], hv[2 * (kk & 1) + 1]);
+#pragma unroll
+              for (int rb = 0; rb < MB; ++rb)
+                t[j][rb] = mfma_bf16(bw, af[rb], kk == 0 ? (f32x4_t){0.f, 0.f, 0.f, 0.f} : t[j][rb]);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            const uint32_t lo2 = wsr[d][j], hi2 = wsh[MXW ? 0 : d][MXW ? 0 : j];
+            const float s0 = bf16_to_f32(lo2 & 0xFFFFu), s1 = __uint_as_float(lo2 & 0xFFFF0000u);
+            const float s2 = bf16_to_f32(hi2 & 0xFFFFu), s3 = __uint_as_float(hi2 & 0xFFFF0000u);
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) {
+              acc[j][rb][0] = fmaf(s0, t[j][rb][0], acc[j][rb][0]);
+              acc[j][rb][1] = fmaf(s1, t[j][rb][1], acc[j][rb][1]);
+              acc[j][rb][2] = fmaf(s2, t[j][rb][2], acc[j][rb][2]);
+              acc[j][rb][3] = fmaf(s3, t[j][rb][3], acc[j][rb][3]);
             }
           }
         } else {
@@ -481,7 +519,7 @@ static hipError_t go_stream(const GemmArgs& a, const StreamCfg& c, int grid_item
   // ring depth in K groups, within the 63 outstanding vector-memory operations
   // one wave can track (up to three loads per group and column block) and a
   // register budget that leaves room for four waves per SIMD at small M
-  constexpr int DW = (NBW == 1 && MB == 1 && KS < 4) ? 16 : 8;
+  constexpr int DW = (NBW == 1 && MB == 1 && KS < 4 && MODE != KM_INT8_A16) ? 16 : 8;
   constexpr int RED = StreamShape<NW, KS, NBW, MB>::kRedBytes;
   auto kern = &k_gemm_stream<MODE, ZP, MB, NBW, KS, DW, GROUPED, NW>;
   int pg, xb;
@@ -542,6 +580,9 @@ hipError_t launch_gemm_stream(const GemmArgs& a, const StreamCfg& c, bool groupe
   if (mode == KM_MX_A4)
     return grouped ? go_stream_mb<KM_MX_A4, false, true>(a, c, grid_items, st)
                    : go_stream_mb<KM_MX_A4, false, false>(a, c, grid_items, st);
+  if (mode == KM_INT8_A16)
+    return grouped ? go_stream_mb<KM_INT8_A16, false, true>(a, c, grid_items, st)
+                   : go_stream_mb<KM_INT8_A16, false, false>(a, c, grid_items, st);
   if (mode == KM_MX_A16)
     return grouped ? go_stream_mb<KM_MX_A16, false, true>(a, c, grid_items, st)
                    : go_stream_mb<KM_MX_A16, false, false>(a, c, grid_items, st);

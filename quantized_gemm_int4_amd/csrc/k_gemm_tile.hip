@@ -29,6 +29,8 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
   constexpr bool MX = MODE == KM_MX_A8 || A4;          // E2M1 weight fragments fed as stored
   constexpr bool F4 = MODE == KM_MX_A16 || MODE == KM_MXI4_A16;  // MX codes scaled to bf16
   constexpr bool I4 = MODE == KM_MXI4_A16;             // MXINT4: two's complement codes / 4
+  constexpr bool Q8 = MODE == KM_INT8_A16;             // INT8 weights: 2 KiB tiles in two halves
+  constexpr int WLD = Q8 ? 4 : 2;                      // 16-byte weight loads per thread per step
   constexpr int GBX = A4 ? 64 : (MX ? 128 : 256);      // activation bytes per row per K step
   constexpr int XB = GBX + 16;                         // LDS activation row stride (bytes)
   constexpr int XPR = GBX / 16;                        // 16-byte pieces per activation row
@@ -94,8 +96,8 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
     const uint32_t* z32 = reinterpret_cast<const uint32_t*>(a.w + G.off_zeros);
     const bool zp = (a.wfmt == W_UINT4_ZP);
     u32x4_t xr[XLD];
-    u32x4_t wq[2];               // W4A16: two code slots per thread
-    uint32_t wsr[2], wzr[2];
+    u32x4_t wq[WLD];             // W4A16: two code slots per thread (INT8: four half slots)
+    uint32_t wsr[WLD], wzr[WLD];
     u32x4_t mq[4];               // W4A8 / W4A4: this wave's four fragments
     uint32_t msr[4];
     uint32_t xsr = 0;            // W4A4: this thread's row scale word (threads < 128)
@@ -117,6 +119,19 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
           const int64_t tile = (e * G.NB + nb) * G.KG + g;
           mq[j] = ld16(a.w + tile * 1024 + lane * 16);
           msr[j] = s32[((e * G.NB + nb) * G.KG4 + g / 4) * 64 + lane];
+        }
+      } else if (Q8) {
+        // load i: column block (q >> 6) & 7, half q >> 9, slot q & 63
+#pragma unroll
+        for (int i = 0; i < WLD; ++i) {
+          const int q = tid + 256 * i;
+          int64_t nb = nbt + ((q >> 6) & 7);
+          if (nb >= G.NB) nb = G.NB - 1;
+          const int L = q & 63;
+          const int64_t tile = (e * G.NB + nb) * G.KG + g;
+          wq[i] = ld16(a.w + tile * 2048 + (q >> 9) * 1024 + L * 16);
+          wsr[i] = s16[tile * 16 + (L & 15)];
+          wzr[i] = 0u;
         }
       } else {
 #pragma unroll
@@ -145,7 +160,18 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
         st16(&xs_lds[row * XB + pc * 16], xr[i]);
       }
       if (A4 && tid < kTileM) xsc_lds[tid] = xsr;
-      if (!MX) {
+      if (Q8) {
+        // half p holds the operands of MFMAs 2 p and 2 p + 1, each s * q rounded to bf16
+#pragma unroll
+        for (int i = 0; i < WLD; ++i) {
+          const int q = tid + 256 * i;
+          const int nbl = (q >> 6) & 7, p = q >> 9, L = q & 63;
+          const float sv = bf16_to_f32(wsr[i] & 0xFFFF);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            st16(&ws_lds[((nbl * 4 + 2 * p + jj) * 64 + L) * 16], i8x8_bf16_scaled(wq[i][2 * jj], wq[i][2 * jj + 1], sv));
+        }
+      } else if (!MX) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int q = tid + 256 * i;
@@ -266,6 +292,8 @@ hipError_t launch_gemm_tile(const GemmArgs& a, bool grouped, int grid_items, hip
     return grouped ? go_tile<KM_MX_A8, true>(a, grid_items, st) : go_tile<KM_MX_A8, false>(a, grid_items, st);
   if (mode == KM_MX_A4)
     return grouped ? go_tile<KM_MX_A4, true>(a, grid_items, st) : go_tile<KM_MX_A4, false>(a, grid_items, st);
+  if (mode == KM_INT8_A16)
+    return grouped ? go_tile<KM_INT8_A16, true>(a, grid_items, st) : go_tile<KM_INT8_A16, false>(a, grid_items, st);
   if (mode == KM_MX_A16)
     return grouped ? go_tile<KM_MX_A16, true>(a, grid_items, st) : go_tile<KM_MX_A16, false>(a, grid_items, st);
   if (mode == KM_MXI4_A16)

@@ -69,6 +69,37 @@ k_transform_codes(int wfmt, Geom G, const uint8_t* __restrict__ codes, uint8_t* 
   }
 }
 
+// INT8 codes: one thread per 16-byte output chunk (e, nb, g, half p, slot L):
+// bytes 8 jj + i = value k = 128 g + 32 (2 p + jj) + 8 h + i of column
+// 16 nb + L % 16, h = L / 16; columns past N hold 0.
+__global__ void __launch_bounds__(256)
+k_transform_codes_i8(Geom G, const uint8_t* __restrict__ codes, uint8_t* __restrict__ out) {
+  const int64_t chunks = G.E * G.NB * G.KG * 128;
+  for (int64_t s = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; s < chunks;
+       s += (int64_t)gridDim.x * blockDim.x) {
+    const int L = (int)(s & 63);
+    const int p = (int)((s >> 6) & 1);
+    int64_t t = s >> 7;
+    const int64_t g = t % G.KG; t /= G.KG;
+    const int64_t nb = t % G.NB;
+    const int64_t e = t / G.NB;
+    const int64_t n = nb * 16 + (L & 15);
+    const int h = L >> 4;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (n < G.N) {
+      const uint8_t* row = codes + (e * G.N + n) * G.K;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const uint8_t* q = row + 128 * g + 32 * (2 * p + jj) + 8 * h;   // 8-byte aligned
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(q);
+        v[2 * jj] = w[0];
+        v[2 * jj + 1] = w[1];
+      }
+    }
+    st16(out + s * 16, v);
+  }
+}
+
 // INT4 scales: one thread per (e, nb, g, c) bf16 entry.
 __global__ void __launch_bounds__(256)
 k_transform_scales_int4(Geom G, const uint16_t* __restrict__ scales, uint16_t* __restrict__ out) {
@@ -161,7 +192,14 @@ k_dequant(int wfmt, Geom G, const uint8_t* __restrict__ w, int64_t e, float* __r
     const int64_t nb = n / 16, c = n % 16, g = k / 128, kk = k % 128;
     const int64_t tile = (e * G.NB + nb) * G.KG + g;
     float r[8];
-    if (is_mx(wfmt)) {
+    if (wfmt == W_INT8_SYM) {
+      const int j = (int)(kk / 32), h = (int)((kk % 32) / 8);
+      const int L = (int)c + 16 * h;
+      const u32x2_t wv = *reinterpret_cast<const u32x2_t*>(w + tile * 2048 + (j >> 1) * 1024 + L * 16 + 8 * (j & 1));
+      const uint16_t* sc = reinterpret_cast<const uint16_t*>(w + G.off_scales);
+      const float s = bf16_to_f32(sc[tile * 16 + c]);
+      for (int q = 0; q < 8; ++q) r[q] = (float)(int8_t)(wv[q >> 2] >> (8 * (q & 3))) * s;
+    } else if (is_mx(wfmt)) {
       const int h = (int)(kk / 32);
       const int L = (int)c + 16 * h;
       const uint32_t word = *reinterpret_cast<const uint32_t*>(w + tile * 1024 + L * 16 + (kk % 32) / 2);
@@ -206,8 +244,12 @@ static inline unsigned grid_for(int64_t items) {
 
 hipError_t launch_transform(int wfmt, const Geom& G, const uint8_t* codes, const void* scales,
                             const uint8_t* zeros, uint8_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_transform_codes, dim3(grid_for(G.E * G.NB * G.KG * 64)), dim3(256), 0, st,
-                     wfmt, G, codes, out);
+  if (wfmt == W_INT8_SYM)
+    hipLaunchKernelGGL(k_transform_codes_i8, dim3(grid_for(G.E * G.NB * G.KG * 128)), dim3(256), 0, st, G, codes,
+                       out);
+  else
+    hipLaunchKernelGGL(k_transform_codes, dim3(grid_for(G.E * G.NB * G.KG * 64)), dim3(256), 0, st,
+                       wfmt, G, codes, out);
   if (is_mx(wfmt)) {
     hipLaunchKernelGGL(k_transform_scales_mx, dim3(grid_for(G.E * G.NB * G.KG4 * 64)), dim3(256), 0,
                        st, G, (const uint8_t*)scales, (uint32_t*)(out + G.off_scales));
@@ -221,7 +263,7 @@ hipError_t launch_transform(int wfmt, const Geom& G, const uint8_t* codes, const
                        zeros, (uint64_t*)(out + G.off_zeros), mask);
   }
   // gap ends: codes end .. scales start, scales end .. zeros start, zeros end .. total
-  const size_t codes_end = (size_t)G.E * G.NB * G.KG * 1024;
+  const size_t codes_end = (size_t)G.E * G.NB * G.KG * (wfmt == W_INT8_SYM ? 2048 : 1024);
   const size_t scales_end = G.off_scales + (is_mx(wfmt) ? (size_t)G.E * G.NB * G.KG4 * 256
                                                               : (size_t)G.E * G.NB * G.KG * 32);
   const size_t zeros_end = (device_fmt(wfmt) == W_UINT4_ZP) ? G.off_zeros + (size_t)G.E * G.NB * G.KG * 8 : G.off_zeros;

@@ -12,7 +12,7 @@ constexpr int kBigRows = 256;   // rows of a 256 x 256 tile (and of a grouped 25
 // bf16 rows, MXFP4 with FP8 rows (scaled fp4 x fp8 MFMA), MXFP4 / MXINT4 with bf16 rows
 // (E2M1 converted to bf16 with its E8M0 scale, bf16 MFMA).
 // (MXINT4 weights with bf16 rows take the MXFP4 path with integer codes.)
-enum KMode : int { KM_INT4_A16 = 0, KM_MX_A8 = 1, KM_MX_A16 = 2, KM_MXI4_A16 = 3, KM_MX_A4 = 4 };
+enum KMode : int { KM_INT4_A16 = 0, KM_MX_A8 = 1, KM_MX_A16 = 2, KM_MXI4_A16 = 3, KM_MX_A4 = 4, KM_INT8_A16 = 5 };
 
 // Arguments shared by the GEMM kernels.
 struct GemmArgs {
@@ -102,6 +102,7 @@ int64_t big_full_tiles(const Geom& G, int64_t M, bool mx);
 
 inline int kmode_of(const GemmArgs& a) {
   if (a.wfmt == W_MXINT4) return KM_MXI4_A16;
+  if (a.wfmt == W_INT8_SYM) return KM_INT8_A16;
   if (a.wfmt == W_MXFP4 && a.a4) return KM_MX_A4;
   return a.wfmt != W_MXFP4 ? KM_INT4_A16 : (a.a8 ? KM_MX_A8 : KM_MX_A16);
 }

@@ -38,7 +38,7 @@ def test_status_strings():
     assert hm.lib.hm_status_string(99).decode() == "unknown status"
 
 
-@pytest.mark.parametrize("fmt", ["int4_sym", "uint4_zp", "mxfp4", "mxint4", "uint3_zp", "uint2_zp"])
+@pytest.mark.parametrize("fmt", ["int4_sym", "uint4_zp", "mxfp4", "mxint4", "uint3_zp", "uint2_zp", "int8_sym"])
 @pytest.mark.parametrize("E,N,K", [(1, 256, 512), (1, 14336, 4096), (3, 37, 640), (256, 4096, 7168)])
 def test_transform_size_matches_layout_spec(fmt, E, N, K):
     d = hm.wdesc(fmt, N, K, E)

@@ -16,7 +16,7 @@ SHAPES = [(1, 16, 128), (2, 37, 256), (1, 5, 640), (3, 100, 384)]
 
 def _random_std(fmt, E, N, K, seed):
     r = np.random.default_rng(seed)
-    bits = quant.NARROW_ZP.get(fmt, 4)
+    bits = 8 if fmt == quant.FMT_INT8_SYM else quant.NARROW_ZP.get(fmt, 4)
     codes = r.integers(0, 256, size=(E, N, K * bits // 8), dtype=np.uint8)
     if fmt in quant.MX_FORMATS:
         scales = r.integers(0, 256, size=(E, N, K // 32), dtype=np.uint8)   # every byte, NaN (255) included
@@ -32,7 +32,7 @@ def _random_std(fmt, E, N, K, seed):
     return codes, scales, zeros
 
 
-ALL = quant.FORMATS + (quant.FMT_MXINT4, quant.FMT_UINT3_ZP, quant.FMT_UINT2_ZP)
+ALL = quant.FORMATS + (quant.FMT_MXINT4, quant.FMT_UINT3_ZP, quant.FMT_UINT2_ZP, quant.FMT_INT8_SYM)
 
 
 @pytest.mark.parametrize("fmt", ALL)

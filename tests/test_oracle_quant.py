@@ -431,3 +431,31 @@ def test_narrow_storage_and_dequant():
         s = np.repeat(codecs.bf16_value(st["scales"]).astype(np.float64), 128, 1)
         z = np.repeat(st["zeros"].astype(np.float64), 128, 1)
         assert np.array_equal(d, (u - z) * s)
+
+
+def test_int8_sym_brute_force_and_storage():
+    """Symmetric INT8 (the INT4 rule at 8 bits): s = bf16(fp32(amax / 127))
+    recomputed with torch, each code the nearest of -128..127 (ties to even),
+    the clamp, |w - w_hat| <= s / 2; 8.125 bits per value by the pages'
+    storage formula; dequant s * q from the signed bytes."""
+    r = np.random.default_rng(33)
+    w = r.normal(0, 0.02, size=(4, 256)).astype(np.float32)
+    w[1, :128] = 0.0
+    q, sbits = quant.quant_int8_sym(w)
+    s = codecs.bf16_value(sbits).astype(np.float64)
+    cands = np.arange(-128, 128, dtype=np.float64)
+    for n in range(4):
+        for g in range(2):
+            blk = w[n, 128 * g:128 * (g + 1)]
+            s32 = torch.tensor(float(np.abs(blk).max()), dtype=torch.float32) / 127.0
+            assert sbits[n, g] == s32.to(torch.bfloat16).view(torch.int16).item() & 0xFFFF
+            for i, wk in enumerate(blk.astype(np.float64)):
+                want = 0 if s[n, g] == 0 else _brute_nearest(wk / s[n, g], cands)
+                assert q[n, 128 * g + i] == want
+    assert quant.quant_int8_sym(np.full((1, 128), 1.0, np.float32))[0].max() == 127
+    assert quant.bits_per_value(quant.FMT_INT8_SYM) == 8.125
+    st = quant.quantize(quant.FMT_INT8_SYM, w)
+    d = quant.dequant(quant.FMT_INT8_SYM, st["codes"], st["scales"]).astype(np.float64)
+    assert np.array_equal(d, q.astype(np.float64) * np.repeat(s, 128, 1))
+    sr = np.repeat(s, 128, 1)
+    assert (np.abs(w - d) <= sr / 2 + 1e-12).all()
