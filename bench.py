@@ -512,8 +512,7 @@ def moe_measure(args, fmt, a8, ts, cpu_sample=False):
             if a8:
                 hm.hm_quant_fp8_rows(x, x8, xs)
                 hm.hm_moe_gemm(d_gu, w_gu, x8, off, sp, t, topk, 0, a_scales=xs, y=y1, ws=ws1)
-                hm.hm_silu_mul(y1, hbuf)
-                hm.hm_quant_fp8_rows(hbuf, a8b, as_)
+                hm.hm_silu_mul_fp8(y1, a8b, as_)      # bf16 h never written
                 hm.hm_moe_gemm(d_dn, w_dn, a8b, off, sp, t, topk, 1, a_scales=as_, y=y2, ws=ws2)
             else:
                 hm.hm_moe_gemm(d_gu, w_gu, x, off, sp, t, topk, 0, y=y1, ws=ws1)
@@ -540,10 +539,14 @@ def moe_measure(args, fmt, a8, ts, cpu_sample=False):
         msteps = max(2, min(args.steps, 10))
         block_ms = timed(block, msteps)
         reps = max(args.reps, 1)
-        silu_ms = timed(lambda: hm.hm_silu_mul(y1, hbuf), reps)
+        if a8:
+            silu_ms = timed(lambda: hm.hm_silu_mul_fp8(y1, a8b, as_), reps)
+        else:
+            silu_ms = timed(lambda: hm.hm_silu_mul(y1, hbuf), reps)
         comb_ms = timed(lambda: hm.hm_moe_combine(y2, rw_d, topk, out), reps)
         ms_t = timed(step, msteps)          # last: y1, y2 of the step stay for the oracle leg
-        silu_b = P * (2 * I) * 2 + P * I * 2               # read gate | up, write h
+        # read gate | up, write h (bf16; FP8 codes + a row scale for FP8 rows)
+        silu_b = P * (2 * I) * 2 + (P * I + 4 * P if a8 else P * I * 2)
         comb_b = P * H * 2 + t * H * 2 + P * 4             # read pair rows and weights, write tokens
         counts = np.bincount(ids.ravel(), minlength=E)
         act = int((counts > 0).sum())

@@ -317,6 +317,18 @@ hm_status hm_moe_gemm_static(const hm_wdesc* d, const void* w_dev, int32_t afmt,
  * HM_ERR_HIP if the launch fails. */
 hm_status hm_silu_mul(const uint16_t* gu, int64_t rows, int64_t d, uint16_t* h, hipStream_t stream);
 
+/* The gated activation and the per-token FP8 quantization of its rows in one
+ * pass, for an MoE block whose down projection takes FP8 rows (per-token FP8
+ * activations: ywsung.com note, section on weight format / activation /
+ * backend): h8 and h_scales are exactly what hm_silu_mul followed by
+ * hm_quant_fp8_rows on its bf16 output give (h rounded to bf16 first, then
+ * s = amax/448 and E4M3(h/s)), without writing or reading the bf16 h.
+ *   gu bf16 [rows][2d]; h8 E4M3 bytes [rows][d]; h_scales fp32 [rows].
+ * d a multiple of 8 and at most 8192 (HM_ERR_SHAPE otherwise); gu and h8
+ * 16-byte aligned, h_scales 4-byte aligned.  rows = 0 is a no-op. */
+hm_status hm_silu_mul_fp8(const uint16_t* gu, int64_t rows, int64_t d, uint8_t* h8, float* h_scales,
+                          hipStream_t stream);
+
 /* Top-k weighted combine of an MoE block (same pages; the reading: each
  * token's output is its routing-weighted sum of its experts' outputs):
  *   out[t][c] = bf16( sum_{j = 0..topk-1} w[t][j] * y[t*topk + j][c] ),

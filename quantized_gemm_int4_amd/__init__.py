@@ -98,6 +98,7 @@ def _load():
         "hm_moe_gemm": [D, P, I32, P, P, I32, I64, I32, P, P, P, P, SZ, T, P],
         "hm_moe_gemm_plan": [D, I32, I64, I32, I32, T, ctypes.c_char_p, SZ],
         "hm_silu_mul": [P, I64, I64, P, P],
+        "hm_silu_mul_fp8": [P, I64, I64, P, P, P],
         "hm_moe_combine": [P, P, I64, I32, I64, P, P],
         "hm_read_probe": [P, I64, I32, I32, P, P],
         "hm_moe_gemm_static": [D, P, I32, P, P, I32, I64, I32, P, P, P, T, P],
@@ -335,6 +336,20 @@ def hm_silu_mul(gu, h=None, stream=None):
     _need(h, torch.bfloat16, rows * d, "h")
     _ok("hm_silu_mul", lib.hm_silu_mul(_ptr(gu), rows, d, _ptr(h), _stream(stream)))
     return h
+
+
+def hm_silu_mul_fp8(gu, h8=None, h_scales=None, stream=None):
+    """gu bf16 [rows, 2d] -> (E4M3 bytes [rows, d], fp32 row scales [rows]) of
+    silu(gate) * up, in one pass."""
+    rows, two_d = gu.shape
+    d = two_d // 2
+    _need(gu, torch.bfloat16, rows * two_d, "gu")
+    if h8 is None:
+        h8 = torch.empty(rows, d, dtype=torch.uint8, device=gu.device)
+    if h_scales is None:
+        h_scales = torch.empty(rows, dtype=torch.float32, device=gu.device)
+    _ok("hm_silu_mul_fp8", lib.hm_silu_mul_fp8(_ptr(gu), rows, d, _ptr(h8), _ptr(h_scales), _stream(stream)))
+    return h8, h_scales
 
 
 def hm_moe_combine(y, weights, topk, out=None, stream=None):

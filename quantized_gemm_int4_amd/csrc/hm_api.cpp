@@ -480,6 +480,16 @@ HM_API hm_status hm_silu_mul(const uint16_t* gu, int64_t rows, int64_t d, uint16
   return HM_OK;
 }
 
+HM_API hm_status hm_silu_mul_fp8(const uint16_t* gu, int64_t rows, int64_t d, uint8_t* h8, float* h_scales,
+                                 hipStream_t stream) {
+  if (rows < 0 || d <= 0 || (d % 8) != 0 || d > 8192) return HM_ERR_SHAPE;
+  if (rows == 0) return HM_OK;
+  if (!gu || !h8 || !h_scales) return HM_ERR_NULL;
+  if (!aligned(gu, 16) || !aligned(h8, 16) || !aligned(h_scales, 4)) return HM_ERR_ALIGN;
+  if (launch_silu_mul_fp8(gu, rows, d, h8, h_scales, stream) != hipSuccess) return HM_ERR_HIP;
+  return HM_OK;
+}
+
 HM_API hm_status hm_moe_combine(const uint16_t* y, const float* w, int64_t t, int32_t topk, int64_t n,
                                 uint16_t* out, hipStream_t stream) {
   if (t < 0 || n <= 0 || topk < 1) return HM_ERR_SHAPE;

@@ -11,21 +11,6 @@
 
 namespace hm {
 
-// fp32 -> E4M3 bits, round to nearest even, saturating; sign kept on zero.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  const uint32_t b = __float_as_uint(x);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const uint32_t a = b & 0x7FFFFFFFu;
-  if (a >= 0x43E00000u) return sign | 0x7Eu;           // |x| >= 448: saturate
-  if (a < 0x3C800000u) {                                // |x| < 2^-6: subnormal range
-    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);  // units of 2^-9, 0..8
-    return sign | (uint32_t)m;                          // 8 -> 0x08 = 2^-6 (exact carry)
-  }
-  // normal: keep 3 mantissa bits with round-to-nearest-even, then rebias 127 -> 7
-  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-  return sign | ((r >> 20) - (120u << 3));
-}
-
 // One 256-thread block per row; rows of any length k (two passes over the row).
 __global__ void __launch_bounds__(256)
 k_quant_fp8_rows(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint8_t* __restrict__ x8,

@@ -55,6 +55,9 @@ hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_r
 // d (n) is a multiple of 8).  Grids of one thread per chunk: the caller keeps
 // rows * d (t * n) / 8 under 2^31 * 256.
 hipError_t launch_silu_mul(const uint16_t* gu, int64_t rows, int64_t d, uint16_t* h, hipStream_t st);
+// gated activation + per-token FP8 rows in one pass (d % 8 == 0, d <= 8192)
+hipError_t launch_silu_mul_fp8(const uint16_t* gu, int64_t rows, int64_t d, uint8_t* h8, float* hs,
+                               hipStream_t st);
 hipError_t launch_combine(const uint16_t* y, const float* w, int64_t t, int topk, int64_t n, uint16_t* out,
                           hipStream_t st);
 // plain streaming read of a buffer (16-byte loads), one word per block written

@@ -59,6 +59,42 @@ def test_silu_mul_rows_zero_and_workload_rows():
     assert res["ok"], res
 
 
+@pytest.mark.parametrize("rows,d", [(1, 8), (37, 2048), (300, 64), (3, 2056), (9, 4104), (2, 8192), (64, 1000)])
+def test_silu_mul_fp8_equals_two_steps(rows, d):
+    """The fused pass gives exactly the bytes and scales of the SiLU product
+    followed by the per-token FP8 quantization of its bf16 output, and both
+    match the oracle's quantization of the oracle's product where the bf16
+    product agrees (it is within one ulp of it by the parity above)."""
+    import quantized_gemm_int4_amd as hm
+    r = np.random.default_rng(rows * 13 + d)
+    gu = r.normal(0, 3, size=(rows, 2 * d))
+    flat = gu.reshape(-1)
+    special = [0.0, -0.0, 100.0, -100.0, -90.0, 88.5, 1e-30, -1e-38, 6.0, -87.5, -79.9, -150.0, -80.5]
+    flat[: min(flat.size, len(special))] = special[: min(flat.size, len(special))]
+    if rows > 2:
+        gu[1] = 0.0                                   # an all-zero row: scale 0, codes 0
+    bits = _bf16_bits(gu)
+    x = bf16_to_dev(bits)
+    h8, hs = hm.hm_silu_mul_fp8(x)
+    h = hm.hm_silu_mul(x)
+    c2, s2 = hm.hm_quant_fp8_rows(h)
+    torch.cuda.synchronize()
+    assert np.array_equal(h8.cpu().numpy(), c2.cpu().numpy())
+    assert np.array_equal(hs.cpu().numpy().view(np.uint32), s2.cpu().numpy().view(np.uint32))
+    c_ref, s_ref = quant.quant_fp8_rows(bits_of(h))
+    assert np.array_equal(h8.cpu().numpy(), c_ref)
+    assert np.array_equal(hs.cpu().numpy().view(np.uint32), np.asarray(s_ref, np.float32).view(np.uint32))
+
+
+def test_silu_mul_fp8_rows_zero_and_shape_errors():
+    import quantized_gemm_int4_amd as hm
+    h8, hs = hm.hm_silu_mul_fp8(torch.empty(0, 16, dtype=torch.bfloat16, device="cuda"))
+    assert h8.shape == (0, 8) and hs.shape == (0,)
+    for d in (12, 8200):
+        with pytest.raises(hm.HmError):
+            hm.hm_silu_mul_fp8(torch.zeros(2, 2 * d, dtype=torch.bfloat16, device="cuda"))
+
+
 @pytest.mark.parametrize("t,topk,n", [(1, 1, 8), (50, 8, 7168), (33, 2, 24), (7, 3, 13), (16, 8, 1001)])
 def test_combine_parity(t, topk, n):
     import quantized_gemm_int4_amd as hm
@@ -115,7 +151,7 @@ def test_moe_block_chained(fmt):
         y1 = hm.hm_moe_gemm(dg, w_g, x, off, sp, t, topk, 0)
     h = hm.hm_silu_mul(y1)
     if a8:
-        h8, hs = hm.hm_quant_fp8_rows(h)
+        h8, hs = hm.hm_silu_mul_fp8(y1)
         y2 = hm.hm_moe_gemm(dd, w_d, h8, off, sp, t, topk, 1, a_scales=hs)
     else:
         y2 = hm.hm_moe_gemm(dd, w_d, h, off, sp, t, topk, 1)
