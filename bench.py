@@ -482,6 +482,7 @@ def moe_measure(args, fmt, a8, ts, cpu_sample=False):
         cnt = torch.empty(E, dtype=torch.int32, device=dev)
         off = torch.empty(E + 1, dtype=torch.int32, device=dev)
         sp = torch.empty(P, dtype=torch.int32, device=dev)
+        sws = torch.empty(max(hm.hm_moe_sort_workspace_size(t, topk, E), 4), dtype=torch.uint8, device=dev)
         ws1 = torch.empty(hm.hm_moe_gemm_workspace_size(d_gu, afmt, t, topk), dtype=torch.uint8, device=dev)
         ws2 = torch.empty(hm.hm_moe_gemm_workspace_size(d_dn, afmt, t, topk), dtype=torch.uint8, device=dev)
         rw_d = torch.from_numpy(rw).to(dev)
@@ -495,7 +496,7 @@ def moe_measure(args, fmt, a8, ts, cpu_sample=False):
             as_ = torch.empty(P, dtype=torch.float32, device=dev)
 
         def step():
-            hm.hm_moe_sort(ids_d, E, cnt, off, sp)
+            hm.hm_moe_sort(ids_d, E, cnt, off, sp, ws=sws)
             if a8:
                 hm.hm_quant_fp8_rows(x, x8, xs)
                 hm.hm_moe_gemm(d_gu, w_gu, x8, off, sp, t, topk, 0, a_scales=xs, y=y1, ws=ws1)
@@ -508,7 +509,7 @@ def moe_measure(args, fmt, a8, ts, cpu_sample=False):
         def block():
             # the whole MoE feed-forward block: sort, gate_up, SiLU product,
             # down on its output, weighted combine back to token order
-            hm.hm_moe_sort(ids_d, E, cnt, off, sp)
+            hm.hm_moe_sort(ids_d, E, cnt, off, sp, ws=sws)
             if a8:
                 hm.hm_quant_fp8_rows(x, x8, xs)
                 hm.hm_moe_gemm(d_gu, w_gu, x8, off, sp, t, topk, 0, a_scales=xs, y=y1, ws=ws1)
@@ -544,6 +545,7 @@ def moe_measure(args, fmt, a8, ts, cpu_sample=False):
         else:
             silu_ms = timed(lambda: hm.hm_silu_mul(y1, hbuf), reps)
         comb_ms = timed(lambda: hm.hm_moe_combine(y2, rw_d, topk, out), reps)
+        sort_ms = timed(lambda: hm.hm_moe_sort(ids_d, E, cnt, off, sp, ws=sws), reps)
         ms_t = timed(step, msteps)          # last: y1, y2 of the step stay for the oracle leg
         # read gate | up, write h (bf16; FP8 codes + a row scale for FP8 rows)
         silu_b = P * (2 * I) * 2 + (P * I + 4 * P if a8 else P * I * 2)
@@ -563,6 +565,7 @@ def moe_measure(args, fmt, a8, ts, cpu_sample=False):
                                         hbm_frac=round(silu_b / silu_ms / 1e6 / HBM_PEAK_GBS, 4)),
                           combine=dict(us=round(comb_ms * 1e3, 2), GBps=round(comb_b / comb_ms / 1e6, 1),
                                        hbm_frac=round(comb_b / comb_ms / 1e6 / HBM_PEAK_GBS, 4)),
+                          sort_us=round(sort_ms * 1e3, 2),
                           plan_gate_up=hm.hm_moe_gemm_plan(d_gu, afmt, t, topk, 0)))
         if cpu_sample:
             keep.append(dict(t=t, ids=ids, x=x, a2=a2, y1=y1, y2=y2))

@@ -220,7 +220,8 @@ hm_status hm_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int64_t m, con
  *   y          bf16 [m][n].
  *   ws         workspace of at least hm_gemm_workspace_size bytes (NULL if 0).
  *   tune       NULL for the default choice, else explicit choices (hm_tuning).
- * m = 0 is a no-op. */
+ * m = 0 is a no-op; m above 8388480 (65535 x 128) gives HM_ERR_SHAPE, here
+ * and in the size and plan queries. */
 hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* x,
                   const void* x_scales, int64_t m, uint16_t* y, void* ws, size_t ws_bytes,
                   const hm_tuning* tune, hipStream_t stream);
@@ -232,17 +233,27 @@ hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, const hm_tuni
 
 /* ------------------------------------------------------------------- MoE */
 
-/* Workspace bytes hm_moe_sort needs (0 in this version; kept for the ABI). */
+/* Workspace bytes hm_moe_sort needs: 0 up to 4096 pairs (one workgroup),
+ * else chunks x E x 4 for the per-chunk expert counts of the GPU-wide sort
+ * (chunks of about 2048 pairs, at most 512 chunks: at most 1 MiB). */
 hm_status hm_moe_sort_workspace_size(int64_t t, int32_t topk, int32_t num_experts, size_t* bytes);
 
-/* Expert sort: pairs p = t*topk + j with ids topk_ids[t][j].
+/* Expert sort: pairs p = t*topk + j with ids topk_ids[t][j] (the expert
+ * grouping of the MoE path: ywsung.com note, section on one token vs many
+ * tokens; each expert's M follows its routing load).  Up to 4096 pairs one
+ * workgroup counts and places them; more are cut into consecutive chunks,
+ * one workgroup each: a counting pass writes every chunk's per-expert counts
+ * to ws, and a placing pass gives each chunk its base positions from the
+ * totals and the counts of the chunks before it.
  *   counts[e]        number of pairs routed to expert e        (int32 [E])
  *   offsets[e]       exclusive prefix sum, offsets[E] = pairs  (int32 [E+1])
  *   sorted_pairs[i]  pair ids grouped by expert, ascending within each
  *                    expert (stable)                           (int32 [t*topk])
  * Ids outside [0, E) are dropped (not counted, not placed); offsets[E] then
  * falls short of t*topk.  1 <= num_experts <= 512, topk <= num_experts,
- * t*topk < 2^31.  t = 0 is a no-op. */
+ * t*topk < 2^31.  t = 0 is a no-op.  ws: hm_moe_sort_workspace_size bytes
+ * (may be NULL when that is 0; HM_ERR_WORKSPACE when smaller), overwritten
+ * by the call. */
 hm_status hm_moe_sort(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t num_experts,
                       int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, void* ws,
                       size_t ws_bytes, hipStream_t stream);
@@ -357,7 +368,7 @@ hm_status hm_read_probe(const void* buf, int64_t bytes, int32_t blocks, int32_t 
                         hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
-const char* hm_status_string(hm_status s);
+const char* hm_status_string(int32_t status);  /* any value; unknown ones named so */
 
 #ifdef __cplusplus
 }

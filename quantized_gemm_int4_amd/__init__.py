@@ -251,8 +251,10 @@ def hm_moe_sort_workspace_size(t, topk, num_experts):
     return out.value
 
 
-def hm_moe_sort(topk_ids, num_experts, counts=None, offsets=None, sorted_pairs=None, stream=None):
-    """topk_ids int32 [t, topk] -> (counts [E], offsets [E+1], sorted_pairs [t*topk])."""
+def hm_moe_sort(topk_ids, num_experts, counts=None, offsets=None, sorted_pairs=None, ws=None, stream=None):
+    """topk_ids int32 [t, topk] -> (counts [E], offsets [E+1], sorted_pairs [t*topk]).
+    ws: a uint8 buffer of hm_moe_sort_workspace_size bytes (allocated here
+    when None and needed)."""
     t, topk = topk_ids.shape
     dev = topk_ids.device
     _need(topk_ids, torch.int32, t * topk, "topk_ids")
@@ -260,8 +262,12 @@ def hm_moe_sort(topk_ids, num_experts, counts=None, offsets=None, sorted_pairs=N
     offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
     sorted_pairs = (torch.empty(t * topk, dtype=torch.int32, device=dev)
                     if sorted_pairs is None else sorted_pairs)
+    need = hm_moe_sort_workspace_size(t, topk, num_experts)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsp, wsb = (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
     _ok("hm_moe_sort", lib.hm_moe_sort(_ptr(topk_ids), t, topk, int(num_experts), _ptr(counts),
-                                       _ptr(offsets), _ptr(sorted_pairs), None, 0, _stream(stream)))
+                                       _ptr(offsets), _ptr(sorted_pairs), wsp, wsb, _stream(stream)))
     return counts, offsets, sorted_pairs
 
 

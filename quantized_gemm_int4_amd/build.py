@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhm.so")
 SOURCES = ["k_weights.hip", "k_fp8.hip", "k_moe.hip", "k_gemm_stream.hip", "k_gemm_tile.hip",
-           "k_gemm_mid.hip", "k_gemm_big.hip", "k_block.hip", "hm_api.cpp"]
+           "k_gemm_mid.hip", "k_gemm_big.hip", "k_block.hip", "plan_host.cpp", "hm_api.cpp"]
 ARCH = "gfx950"
 
 

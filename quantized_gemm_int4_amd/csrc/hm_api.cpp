@@ -145,8 +145,12 @@ bool mid_grid_fits(const Geom& G, bool a8, int64_t m) {
   return tiles_n * tiles_m <= 0x7FFFFFFFll;
 }
 
+// Dense rows: the 128 x 128 kernel's grid has one block row per 128 rows.
+constexpr int64_t kMaxDenseRows = 65535ll * kTileM;
+
 hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu, DensePlan* out) {
   DensePlan p{};
+  if (m < 1 || m > kMaxDenseRows) return HM_ERR_SHAPE;
   const Geom G = geom_of(d);
   const bool f4 = mx_a16(d, afmt);
   const bool a8 = afmt == HM_A_FP8_ROWSCALE;
@@ -396,7 +400,7 @@ hm_status launch_moe(const hm_wdesc* d, int32_t afmt, const void* w_dev, const v
 
 // =====================================================================================
 
-HM_API const char* hm_status_string(hm_status s) {
+HM_API const char* hm_status_string(int32_t s) {
   switch (s) {
     case HM_OK: return "ok";
     case HM_ERR_NULL: return "null pointer";
@@ -571,7 +575,7 @@ HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, con
   if (s) return s;
   if ((s = check_pair(d, afmt))) return s;
   if (d->num_experts != 1) return HM_ERR_SHAPE;
-  if (m < 0 || m > 65535ll * kTileM) return HM_ERR_SHAPE;
+  if (m < 0 || m > kMaxDenseRows) return HM_ERR_SHAPE;
   Tune tu;
   if ((s = read_tuning(tune, &tu))) return s;
   if (m == 0) return HM_OK;
@@ -610,20 +614,25 @@ HM_API hm_status hm_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, con
   return (e == hipSuccess) ? HM_OK : HM_ERR_HIP;
 }
 
+// Per-chunk expert counts of the GPU-wide sort (none for one block).
+static size_t sort_ws_bytes(int64_t P, int E) {
+  const int nb = moe_sort_blocks(P, nullptr);
+  return nb > 1 ? (size_t)nb * (size_t)E * sizeof(int32_t) : 0;
+}
+
 HM_API hm_status hm_moe_sort_workspace_size(int64_t t, int32_t topk, int32_t num_experts,
                                             size_t* bytes) {
   if (!bytes) return HM_ERR_NULL;
   if (t < 0 || topk < 1 || num_experts < 1 || num_experts > 512 || topk > num_experts)
     return HM_ERR_SHAPE;
-  *bytes = 0;
+  if (t * (int64_t)topk >= (1ll << 31)) return HM_ERR_SHAPE;
+  *bytes = sort_ws_bytes(t * topk, num_experts);
   return HM_OK;
 }
 
 HM_API hm_status hm_moe_sort(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t num_experts,
                              int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, void* ws,
                              size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (t < 0 || topk < 1 || num_experts < 1 || num_experts > 512 || topk > num_experts)
     return HM_ERR_SHAPE;
   if (t * (int64_t)topk >= (1ll << 31)) return HM_ERR_SHAPE;
@@ -631,8 +640,14 @@ HM_API hm_status hm_moe_sort(const int32_t* topk_ids, int64_t t, int32_t topk, i
   if (!topk_ids || !counts || !offsets || !sorted_pairs) return HM_ERR_NULL;
   if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_pairs, 4))
     return HM_ERR_ALIGN;
-  if (launch_moe_sort(topk_ids, t * topk, num_experts, counts, offsets, sorted_pairs, stream) !=
-      hipSuccess)
+  const size_t need = sort_ws_bytes(t * topk, num_experts);
+  if (need) {
+    if (!ws) return HM_ERR_NULL;
+    if (ws_bytes < need) return HM_ERR_WORKSPACE;
+    if (!aligned(ws, 4)) return HM_ERR_ALIGN;
+  }
+  if (launch_moe_sort(topk_ids, t * topk, num_experts, counts, offsets, sorted_pairs,
+                      static_cast<int32_t*>(ws), stream) != hipSuccess)
     return HM_ERR_HIP;
   return HM_OK;
 }

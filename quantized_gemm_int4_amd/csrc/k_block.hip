@@ -48,59 +48,60 @@ k_silu_mul_v8(const uint16_t* __restrict__ gu, int64_t chunks, int64_t dc, uint1
 }
 
 // Gated activation and per-token FP8 quantization of its rows in one pass
-// (the input of an MoE block's down projection with FP8 rows): block r owns
-// row r; thread t holds outputs 8 (256 c + t) .. + 7 (c < CH) of h rounded to
-// bf16 exactly as k_silu_mul_v8 writes them, the row's amax is reduced over
-// the block, and the codes are those k_quant_fp8_rows_reg gives for the bf16
-// row: s = amax / 448, E4M3(h / s) by correctly rounded fp32 divisions.  The
-// bf16 h never reaches memory.  d % 8 == 0, d <= 2048 CH.
+// (the input of an MoE block's down projection with FP8 rows): one wave per
+// row; lane l holds outputs 8 (64 c + l) .. + 7 (c < CH) of h rounded to bf16
+// exactly as k_silu_mul_v8 writes them, the row's amax is a wave reduction,
+// and the codes are those k_quant_fp8_rows_reg gives for the bf16 row:
+// s = amax / 448, E4M3 of the correctly rounded fp32 quotient h / s.  The
+// bf16 h never reaches memory.  d % 8 == 0, d <= 512 CH.
 template <int CH>
 __global__ void __launch_bounds__(256)
 k_silu_mul_fp8(const uint16_t* __restrict__ gu, int64_t rows, int64_t d, uint8_t* __restrict__ h8,
                float* __restrict__ hs) {
-  __shared__ float red[4];
+  const int lane = threadIdx.x & 63;
   const int64_t dc = d / 8;
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += (int64_t)gridDim.x * 4) {
     const uint16_t* g = gu + r * 2 * d;
-    u32x4_t hv[CH];
+    u32x4_t gv[CH], uv[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t q = (int64_t)c * 64 + lane;
+      gv[c] = (u32x4_t){0u, 0u, 0u, 0u};
+      uv[c] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (q < dc) {
+        gv[c] = ld16(g + 8 * q);
+        uv[c] = ld16(g + d + 8 * q);
+      }
+    }
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int64_t q = (int64_t)c * 256 + threadIdx.x;
-      hv[c] = (u32x4_t){0u, 0u, 0u, 0u};
-      if (q < dc) {
-        const u32x4_t gv = ld16(g + 8 * q), uv = ld16(g + d + 8 * q);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          hv[c][j] = pack_bf16(silu_f(lo_bf16(gv[j])) * lo_bf16(uv[j]), silu_f(hi_bf16(gv[j])) * hi_bf16(uv[j]));
-          amax = fmaxf(amax, fabsf(lo_bf16(hv[c][j])));
-          amax = fmaxf(amax, fabsf(hi_bf16(hv[c][j])));
-        }
+      for (int j = 0; j < 4; ++j) {
+        gv[c][j] = pack_bf16(silu_f(lo_bf16(gv[c][j])) * lo_bf16(uv[c][j]),
+                             silu_f(hi_bf16(gv[c][j])) * hi_bf16(uv[c][j]));
+        amax = fmaxf(amax, fabsf(lo_bf16(gv[c][j])));
+        amax = fmaxf(amax, fabsf(hi_bf16(gv[c][j])));
       }
     }
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
     const float s = __fdiv_rn(amax, 448.0f);
-    if (threadIdx.x == 0) hs[r] = s;
+    if (lane == 0) hs[r] = s;
+    uint32_t cw[CH][2];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int64_t q = (int64_t)c * 256 + threadIdx.x;
-      if (q >= dc) continue;
-      uint32_t lo = 0, hi = 0;
+      cw[c][0] = cw[c][1] = 0;
+      if (s == 0.0f) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t c0 = 0, c1 = 0;
-        if (s != 0.0f) {
-          c0 = f32_to_e4m3(__fdiv_rn(lo_bf16(hv[c][j]), s));
-          c1 = f32_to_e4m3(__fdiv_rn(hi_bf16(hv[c][j]), s));
-        }
-        const uint32_t pair = c0 | (c1 << 8);
-        if (j < 2) lo |= pair << (16 * j); else hi |= pair << (16 * (j - 2));
+      for (int j = 0; j < 8; ++j) {
+        const float h = (j & 1) ? hi_bf16(gv[c][j >> 1]) : lo_bf16(gv[c][j >> 1]);
+        cw[c][j >> 2] |= f32_to_e4m3(__fdiv_rn(h, s)) << (8 * (j & 3));
       }
-      *reinterpret_cast<u32x2_t*>(h8 + r * d + 8 * q) = (u32x2_t){lo, hi};
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t q = (int64_t)c * 64 + lane;
+      if (q < dc) *reinterpret_cast<u32x2_t*>(h8 + r * d + 8 * q) = (u32x2_t){cw[c][0], cw[c][1]};
     }
   }
 }
@@ -151,10 +152,12 @@ k_combine_s(const uint16_t* __restrict__ y, const float* __restrict__ w, int64_t
 
 hipError_t launch_silu_mul_fp8(const uint16_t* gu, int64_t rows, int64_t d, uint8_t* h8, float* hs,
                                hipStream_t st) {
-  const unsigned blocks = (unsigned)(rows < 65536 ? rows : 65536);
-  if (d <= 2048) hipLaunchKernelGGL(k_silu_mul_fp8<1>, dim3(blocks), dim3(256), 0, st, gu, rows, d, h8, hs);
-  else if (d <= 4096) hipLaunchKernelGGL(k_silu_mul_fp8<2>, dim3(blocks), dim3(256), 0, st, gu, rows, d, h8, hs);
-  else hipLaunchKernelGGL(k_silu_mul_fp8<4>, dim3(blocks), dim3(256), 0, st, gu, rows, d, h8, hs);
+  const int64_t want = (rows + 3) / 4;
+  const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+  if (d <= 512) hipLaunchKernelGGL(k_silu_mul_fp8<1>, dim3(blocks), dim3(256), 0, st, gu, rows, d, h8, hs);
+  else if (d <= 2048) hipLaunchKernelGGL(k_silu_mul_fp8<4>, dim3(blocks), dim3(256), 0, st, gu, rows, d, h8, hs);
+  else if (d <= 4096) hipLaunchKernelGGL(k_silu_mul_fp8<8>, dim3(blocks), dim3(256), 0, st, gu, rows, d, h8, hs);
+  else hipLaunchKernelGGL(k_silu_mul_fp8<16>, dim3(blocks), dim3(256), 0, st, gu, rows, d, h8, hs);
   return hipGetLastError();
 }
 

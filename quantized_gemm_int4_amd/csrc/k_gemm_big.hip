@@ -50,10 +50,7 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* yrow, int64_t N, int64_t 
 // first column block of expert e
 __device__ __forceinline__ int64_t wbase_of(int64_t e, const Geom& G) { return e * G.NB; }
 
-constexpr int kBigM = 256;        // rows per block
-constexpr int kBigCB = 16;        // 16-column blocks per block (256 columns)
 constexpr int kBigStages = 3;     // LDS stages: loads run two K steps ahead
-constexpr int kBigGrid = 256;     // persistent dense grid: one block per CU
 
 // LDS bytes of one stage: activation fragments (32 x 1 KiB) and the block's
 // 16 weight tiles (16 KiB), plus MXFP4: their E8M0 scale words (16 x 256 B);
@@ -694,13 +691,6 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
 // CUs: 3.5), the last round's tiles are split so that every CU takes part in
 // it; W4A16 only (the half tiles compute four of the eight row blocks), and
 // not where the second half of a last tile row would be empty.
-int64_t big_full_tiles(const Geom& G, int64_t M, bool mx) {
-  const int64_t tiles_n = (G.NB + kBigCB - 1) / kBigCB, tiles_m = (M + kBigM - 1) / kBigM;
-  const int64_t tiles = tiles_n * tiles_m, rest = tiles % kBigGrid;
-  const bool tail_ok = (M % kBigM) == 0 || (M % kBigM) > kBigM / 2;
-  if (mx || tiles <= kBigGrid || rest == 0 || 2 * rest > kBigGrid || !tail_ok) return tiles;
-  return tiles - rest;
-}
 
 template <bool MX, bool ZP, bool GROUPED>
 static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
@@ -722,7 +712,6 @@ static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
   return hipGetLastError();
 }
 
-int64_t big_n_tiles(const Geom& G) { return (G.NB + kBigCB - 1) / kBigCB; }
 
 hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
   // MX weights with bf16 rows run on the streaming, 128 x 64 and 128 x 128 kernels only

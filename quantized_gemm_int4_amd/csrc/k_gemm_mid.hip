@@ -51,7 +51,6 @@ namespace hm {
 namespace {
 
 constexpr int kMidM = 128;                       // rows per tile
-constexpr int kMidCB = 4;                        // 16-column blocks per tile (64 columns)
 constexpr int kMidDX = 3;                        // activation groups copied ahead
 constexpr int kMidDW = 5;                        // weight groups copied ahead
 constexpr int kMidXS = kMidDX + 1;               // activation stages
@@ -66,7 +65,6 @@ struct MidTile {
 };
 
 constexpr int kMxM = 64;                         // rows per W4A8 tile
-constexpr int kMxCB = 8;                         // 16-column blocks per W4A8 tile (128 columns)
 constexpr int kMxStages = 6;                     // one K group each, copied five ahead
 constexpr int kMxSB = 8 * 1024 + kMxCB * 1024 + kMxCB * 256;   // activations, code tiles, scale words
 constexpr int kMxLds = kMxStages * kMxSB;        // 108 KiB
@@ -629,9 +627,6 @@ static hipError_t go_mid(const GemmArgs& a, int grid_items, hipStream_t st) {
   return hipGetLastError();
 }
 
-int64_t mid_n_tiles(const Geom& G, bool mx) {
-  return mx ? 2 * ((G.NB + kMxCB - 1) / kMxCB) : (G.NB + kMidCB - 1) / kMidCB;
-}
 
 hipError_t launch_gemm_mid(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
   // W4A4 and INT8 weights have no 128-row tile kernel

@@ -486,10 +486,6 @@ k_splitk_reduce(GemmArgs a, int splits) {
   }
 }
 
-int64_t stream_n_tiles(const Geom& G, const StreamCfg& c) {
-  const int64_t cols = (int64_t)(c.nw / c.ks) * c.nbw;   // 16-column blocks per block
-  return (G.NB + cols - 1) / cols;
-}
 
 // LDS plan of one launch: K groups per activation piece and the row stride.
 static void stream_lds_plan(const GemmArgs& a, const StreamCfg& c, bool grouped, int red_bytes,

@@ -31,21 +31,20 @@ __device__ int block_scan512(int v, int* wsum) {
   return v + pre;
 }
 
-// Deterministic, stable counting sort of pair ids by expert in one block.
-// Wave w owns the contiguous pair range [w*chunk, (w+1)*chunk); its per-expert
-// base positions come from the exclusive prefix over earlier waves, and inside
-// a wave each batch of 64 pairs is ranked in lane order with ballot matching.
-__global__ void __launch_bounds__(kSortThreads)
-k_moe_sort(const int32_t* __restrict__ ids, int64_t P, int E, int32_t* __restrict__ counts,
-           int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs) {
-  __shared__ int hist[kSortWaves][512];
-  __shared__ int wsum[8];
+// Places the pairs of [lo, hi) stably: wave w owns the contiguous subrange
+// [lo + w*chunk, ...), its per-expert base positions are base[e] plus the
+// counts of earlier waves, and inside a wave each batch of 64 pairs is ranked
+// in lane order with ballot matching.  hist is the block's [16][512] LDS
+// array (zeroed here); base[e] (LDS) is the first position of this range's
+// pairs of expert e.  Must be reached by every thread of the block.
+__device__ void sort_range(const int32_t* __restrict__ ids, int64_t lo, int64_t hi, int E, const int* base,
+                           int (*hist)[512], int32_t* __restrict__ sorted_pairs) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kSortWaves * 512; i += kSortThreads) (&hist[0][0])[i] = 0;
   __syncthreads();
-  const int64_t chunk = (P + kSortWaves - 1) / kSortWaves;
-  const int64_t beg = wave * chunk;
-  const int64_t end = (beg + chunk < P) ? beg + chunk : P;
+  const int64_t chunk = (hi - lo + kSortWaves - 1) / kSortWaves;
+  const int64_t beg = lo + wave * chunk;
+  const int64_t end = (beg + chunk < hi) ? beg + chunk : hi;
   for (int64_t b = beg; b < end; b += 64) {
     const int64_t p = b + lane;
     if (p < end) {
@@ -54,22 +53,13 @@ k_moe_sort(const int32_t* __restrict__ ids, int64_t P, int E, int32_t* __restric
     }
   }
   __syncthreads();
-  // per-expert totals and per-wave exclusive bases
-  int total = 0;
   if (tid < E) {
+    int run = base[tid];
     for (int w = 0; w < kSortWaves; ++w) {
       const int c = hist[w][tid];
-      hist[w][tid] = total;
-      total += c;
+      hist[w][tid] = run;
+      run += c;
     }
-  }
-  const int incl = block_scan512(tid < 512 ? total : 0, wsum);
-  const int excl = incl - total;
-  if (tid < E) {
-    counts[tid] = total;
-    offsets[tid] = excl;
-    if (tid == E - 1) offsets[E] = incl;
-    for (int w = 0; w < kSortWaves; ++w) hist[w][tid] += excl;
   }
   __syncthreads();
   int nbits = 0;
@@ -94,6 +84,94 @@ k_moe_sort(const int32_t* __restrict__ ids, int64_t P, int E, int32_t* __restric
     if (valid && __popcll(m & lt) == 0) hist[wave][e] += __popcll(m);
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// Exclusive scan of the per-expert totals tot[] (LDS) into base[] (LDS,
+// adding what base[] holds), and, when `out` is set, the counts and offsets.
+__device__ void expert_offsets(const int* tot, int* base, int E, int* wsum, bool out, int32_t* __restrict__ counts,
+                               int32_t* __restrict__ offsets) {
+  const int tid = threadIdx.x;
+  const int total = tid < E ? tot[tid] : 0;
+  const int incl = block_scan512(tid < 512 ? total : 0, wsum);
+  const int excl = incl - total;
+  if (tid < E) {
+    base[tid] += excl;
+    if (out) {
+      counts[tid] = total;
+      offsets[tid] = excl;
+      if (tid == E - 1) offsets[E] = incl;
+    }
+  }
+  __syncthreads();
+}
+
+// Deterministic, stable counting sort of pair ids by expert in one block
+// (few pairs).
+__global__ void __launch_bounds__(kSortThreads)
+k_moe_sort(const int32_t* __restrict__ ids, int64_t P, int E, int32_t* __restrict__ counts,
+           int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs) {
+  __shared__ int hist[kSortWaves][512];
+  __shared__ int tot[512], base[512];
+  __shared__ int wsum[8];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 512; i += kSortThreads) { tot[i] = 0; base[i] = 0; }
+  __syncthreads();
+  for (int64_t p = tid; p < P; p += kSortThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&tot[e], 1);
+  }
+  __syncthreads();
+  expert_offsets(tot, base, E, wsum, true, counts, offsets);
+  sort_range(ids, 0, P, E, base, hist, sorted_pairs);
+}
+
+// GPU-wide sort, pass 1: block b counts the pairs of its chunk
+// [b*C, min((b+1)*C, P)) per expert into cnt[b][e] (every e < E written).
+__global__ void __launch_bounds__(kSortThreads)
+k_moe_sort_count(const int32_t* __restrict__ ids, int64_t P, int E, int64_t C, int32_t* __restrict__ cnt) {
+  __shared__ int h[512];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 512; i += kSortThreads) h[i] = 0;
+  __syncthreads();
+  const int64_t lo = (int64_t)blockIdx.x * C;
+  const int64_t hi = (lo + C < P) ? lo + C : P;
+  for (int64_t p = lo + tid; p < hi; p += kSortThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kSortThreads) cnt[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// Pass 2: block b sums every chunk's counts per expert (the totals) and those
+// of the chunks before its own, scans the totals into the expert offsets
+// (block 0 writes counts and offsets), and places its chunk's pairs after
+// those of the earlier chunks: the order is stable over the whole input.
+__global__ void __launch_bounds__(kSortThreads)
+k_moe_sort_place(const int32_t* __restrict__ ids, int64_t P, int E, int64_t C, int nb,
+                 const int32_t* __restrict__ cnt, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                 int32_t* __restrict__ sorted_pairs) {
+  __shared__ int hist[kSortWaves][512];
+  __shared__ int tot[512], base[512];
+  __shared__ int wsum[8];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  for (int i = tid; i < 512; i += kSortThreads) { tot[i] = 0; base[i] = 0; }
+  __syncthreads();
+  const int64_t all = (int64_t)nb * E;
+  for (int64_t i = tid; i < all; i += kSortThreads) {
+    const int bb = (int)(i / E), e = (int)(i - (int64_t)bb * E);
+    const int c = cnt[i];
+    if (c) {
+      atomicAdd(&tot[e], c);
+      if (bb < b) atomicAdd(&base[e], c);
+    }
+  }
+  __syncthreads();
+  expert_offsets(tot, base, E, wsum, b == 0, counts, offsets);
+  const int64_t lo = (int64_t)b * C;
+  const int64_t hi = (lo + C < P) ? lo + C : P;
+  sort_range(ids, lo, hi, E, base, hist, sorted_pairs);
 }
 
 // Work units of a grouped GEMM from the expert offsets (one thread per
@@ -162,10 +240,21 @@ k_moe_schedule(const int32_t* __restrict__ offsets, int E, int64_t P, int s_rows
   }
 }
 
+
 hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int E, int32_t* counts, int32_t* offsets,
-                           int32_t* sorted_pairs, hipStream_t st) {
-  hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(kSortThreads), 0, st, ids, P, E, counts, offsets,
-                     sorted_pairs);
+                           int32_t* sorted_pairs, int32_t* cnt, hipStream_t st) {
+  int64_t C = 0;
+  const int nb = moe_sort_blocks(P, &C);
+  if (nb == 1) {
+    hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(kSortThreads), 0, st, ids, P, E, counts, offsets,
+                       sorted_pairs);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_moe_sort_count, dim3(nb), dim3(kSortThreads), 0, st, ids, P, E, C, cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_moe_sort_place, dim3(nb), dim3(kSortThreads), 0, st, ids, P, E, C, nb, cnt, counts,
+                     offsets, sorted_pairs);
   return hipGetLastError();
 }
 

@@ -8,6 +8,13 @@ namespace hm {
 
 constexpr int kBigRows = 256;   // rows of a 256 x 256 tile (and of a grouped 256-row unit)
 
+// Launch geometry the planner shares with the kernels.
+constexpr int kBigM = kBigRows;  // rows per 256 x 256 block
+constexpr int kBigCB = 16;       // 16-column blocks per 256 x 256 block (256 columns)
+constexpr int kBigGrid = 256;    // persistent dense 256 x 256 grid: one block per CU
+constexpr int kMidCB = 4;        // 16-column blocks per W4A16 128 x 64 tile (64 columns)
+constexpr int kMxCB = 8;         // 16-column blocks per W4A8 64 x 128 tile (128 columns)
+
 // Kernel variants by (weight format, activation format): INT4 codes with
 // bf16 rows, MXFP4 with FP8 rows (scaled fp4 x fp8 MFMA), MXFP4 / MXINT4 with bf16 rows
 // (E2M1 converted to bf16 with its E8M0 scale, bf16 MFMA).
@@ -45,8 +52,15 @@ hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_
                                  hipStream_t st);
 hipError_t launch_quant_mxfp4_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes, uint8_t* scales,
                                    hipStream_t st);
+// Expert sort: up to kSortOneBlock pairs in one block; more are cut into
+// moe_sort_blocks(P) chunks of *chunk pairs (about kSortChunk, at most
+// kSortMaxBlocks chunks) whose per-expert counts go to cnt [chunks][E].
+constexpr int64_t kSortOneBlock = 4096;
+constexpr int64_t kSortChunk = 2048;
+constexpr int kSortMaxBlocks = 512;
+int moe_sort_blocks(int64_t P, int64_t* chunk);
 hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int E, int32_t* counts, int32_t* offsets,
-                           int32_t* sorted_pairs, hipStream_t st);
+                           int32_t* sorted_pairs, int32_t* cnt, hipStream_t st);
 hipError_t launch_moe_schedule(const int32_t* offsets, int E, int64_t P, int s_rows, int s_max, int bm,
                                int big_min, int64_t max_s, int64_t max_t, int64_t max_b, int32_t* hdr,
                                int32_t* su, int32_t* tu, int32_t* bu, hipStream_t st);

@@ -148,6 +148,16 @@ def test_moe_argument_checks():
     assert _err("hm_moe_sort", None, 0, 2, 8, None, None, None, None, 0, None) == 0      # t = 0
     assert _err("hm_moe_sort", None, 4, 2, 8, good, good, good, None, 0, None) == 1
     assert _err("hm_moe_sort", P(0x100002), 4, 2, 8, good, good, good, None, 0, None) == 3
+    # one workgroup up to 4096 pairs (no workspace), then ~2048-pair chunks
+    # of E counts each, at most 512 chunks
+    assert hm.hm_moe_sort_workspace_size(512, 8, 256) == 0
+    assert hm.hm_moe_sort_workspace_size(4096, 1, 7) == 0
+    assert hm.hm_moe_sort_workspace_size(4097, 1, 7) == 3 * 7 * 4
+    assert hm.hm_moe_sort_workspace_size(16384, 8, 256) == 64 * 256 * 4
+    assert hm.hm_moe_sort_workspace_size(2 ** 28 - 1, 8, 512) == 512 * 512 * 4
+    assert _err("hm_moe_sort", good, 1024, 8, 256, good, good, good, None, 0, None) == 1     # ws needed
+    assert _err("hm_moe_sort", good, 1024, 8, 256, good, good, good, good, 4095, None) == 5
+    assert _err("hm_moe_sort", good, 1024, 8, 256, good, good, good, P(0x100002), 4096, None) == 3
     d = hm.wdesc("int4_sym", 4096, 7168, 256)
     need = hm.hm_moe_gemm_workspace_size(d, 0, 64, 8)
     assert need > 0

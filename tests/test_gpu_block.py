@@ -86,6 +86,43 @@ def test_silu_mul_fp8_equals_two_steps(rows, d):
     assert np.array_equal(hs.cpu().numpy().view(np.uint32), np.asarray(s_ref, np.float32).view(np.uint32))
 
 
+# (amax, h values) as bf16 bits where h * fl(1/s), s = fl(amax / 448), rounds
+# to another E4M3 code than the correctly rounded h / s (found by a search
+# over bf16 values with a float32 model of that product)
+_RECIP_CASES = [(0x3fc4, [0x3f2f, 0x3f4b, 0x3faf]), (0x3fcc, [0x3f19, 0x3f99]), (0x3fd0, [0x3f1c, 0x3f9c]),
+                (0x3ff8, [0x3f3a, 0x3fba]), (0x3f8a, [0x3ecf, 0x3f4f]), (0x3f98, [0x3f64]), (0x3fa6, [0x3f79])]
+
+
+def test_silu_mul_fp8_quotients_near_e4m3_midpoints():
+    """Rows where a multiply by the reciprocal of the row scale would give a
+    different code than the correctly rounded quotient: the fused pass must
+    give the quotient's code (that of the two-step path and the oracle).
+    gate = 64 gives silu = 64 exactly, so h = 64 u exactly."""
+    import quantized_gemm_int4_amd as hm
+    d = 64
+    h = np.zeros((len(_RECIP_CASES), d), dtype=np.float32)
+    for r, (amax, hv) in enumerate(_RECIP_CASES):
+        v = codecs.bf16_value(np.array([amax] + hv + hv, dtype=np.uint16)).astype(np.float32)
+        v[1 + len(hv):] *= -1.0
+        h[r, :v.size] = v
+        s = np.float32(v[0]) / np.float32(448.0)
+        fast = codecs.e4m3_rne_sat(v * (np.float32(1.0) / s))
+        exact = codecs.e4m3_rne_sat(v / s)
+        assert (fast != exact).any()                  # the case does separate the two
+    gu = np.concatenate([np.full_like(h, 64.0), h / np.float32(64.0)], axis=1)
+    bits = _bf16_bits(gu)
+    x = bf16_to_dev(bits)
+    h8, hs = hm.hm_silu_mul_fp8(x)
+    hh = hm.hm_silu_mul(x)
+    c2, s2 = hm.hm_quant_fp8_rows(hh)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(hh), _bf16_bits(h))          # h is what was planned
+    assert np.array_equal(h8.cpu().numpy(), c2.cpu().numpy())
+    assert np.array_equal(hs.cpu().numpy(), s2.cpu().numpy())
+    c_ref, s_ref = quant.quant_fp8_rows(bits_of(hh))
+    assert np.array_equal(h8.cpu().numpy(), c_ref)
+
+
 def test_silu_mul_fp8_rows_zero_and_shape_errors():
     import quantized_gemm_int4_amd as hm
     h8, hs = hm.hm_silu_mul_fp8(torch.empty(0, 16, dtype=torch.bfloat16, device="cuda"))

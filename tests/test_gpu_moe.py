@@ -15,8 +15,11 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("t,topk,E", [(1, 1, 1), (64, 8, 256), (1024, 8, 256), (333, 3, 17),
-                                      (5000, 6, 512), (16384, 8, 256)])
+                                      (5000, 6, 512), (16384, 8, 256), (4096, 1, 7), (4097, 1, 7),
+                                      (140000, 8, 256)])
 def test_sort_exact(t, topk, E):
+    """One workgroup up to 4096 pairs, chunks of ~2048 pairs above (4097
+    pairs: three ragged chunks; 1.12 M pairs: the 512-chunk cap)."""
     import quantized_gemm_int4_amd as hm
     if E == 256 and topk == 8:
         ids, _ = synthetic.router_topk(4, t, E, topk)
@@ -28,6 +31,27 @@ def test_sort_exact(t, topk, E):
     assert np.array_equal(c.cpu().numpy(), rc)
     assert np.array_equal(o.cpu().numpy(), ro)
     assert np.array_equal(sp.cpu().numpy(), rsp)
+
+
+def test_sort_chunks_drop_out_of_range_ids_and_reuse_workspace():
+    """Chunked sort with ids outside [0, E) in every chunk, into one caller
+    workspace used twice (the second call with fewer pairs)."""
+    import quantized_gemm_int4_amd as hm
+    E = 40
+    ws = torch.empty(hm.hm_moe_sort_workspace_size(9000, 4, E), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+    for t in (9000, 3000):
+        ids = np.random.default_rng(t).integers(-3, E + 3, size=(t, 4)).astype(np.int32)
+        c, o, sp = hm.hm_moe_sort(to_dev(ids), E, ws=ws)
+        torch.cuda.synchronize()
+        flat = ids.ravel()
+        keep = np.nonzero((flat >= 0) & (flat < E))[0]          # the pairs that are placed
+        rc, ro, rsub = moe.moe_sort_ref(flat[keep], E)
+        n = int(ro[-1])
+        assert n == keep.size < flat.size
+        assert np.array_equal(c.cpu().numpy(), rc)
+        assert np.array_equal(o.cpu().numpy(), ro)
+        assert np.array_equal(sp.cpu().numpy()[:n], keep[rsub])
 
 
 def test_sort_drops_out_of_range_ids():
