@@ -176,6 +176,16 @@ hm_status hm_transform_size(const hm_wdesc* d, size_t* bytes);
 hm_status hm_transform(const hm_wdesc* d, const uint8_t* codes, const void* scales,
                        const uint8_t* zeros, void* w_dev, size_t w_bytes, hipStream_t stream);
 
+/* hm_transform of a gate_up weight (n = 2d rows: gate rows 0..d-1, up rows
+ * d..2d-1, n a multiple of 32, else HM_ERR_SHAPE) into the gated device
+ * layout that hm_moe_gemm_gated reads: device row 32 i + c holds gate row
+ * 16 i + c and device row 32 i + 16 + c up row 16 i + c (c < 16), i.e. the
+ * buffer equals hm_transform of the standard format with its rows so
+ * permuted (hm_dequant of it returns the rows in that order).  Same size
+ * (hm_transform_size) and arguments as hm_transform. */
+hm_status hm_transform_gated(const hm_wdesc* d, const uint8_t* codes, const void* scales,
+                             const uint8_t* zeros, void* w_dev, size_t w_bytes, hipStream_t stream);
+
 /* Exact dequantization of one expert of a transformed buffer into fp32
  * out[N][K].  Every restored weight is exactly representable in fp32 for the
  * INT4 formats, and for MXFP4 with E8M0 scale bytes up to 252 (MXINT4: up to
@@ -290,6 +300,34 @@ hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const 
  * this call shape and tuning (no device access). */
 hm_status hm_moe_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
                            int32_t a_rows_are_pairs, const hm_tuning* tune, char* buf, size_t buf_len);
+
+/* The gate_up grouped GEMM with the gated activation in its epilogue (the
+ * MoE feed-forward block of the pages: aihaber.org article on Humming, "what
+ * problem does it solve"; ywsung.com note, section on one token vs many
+ * tokens; the fusion is this library's, the formula that of hm_silu_mul):
+ *   h[p][i] = bf16( silu(y[p][i]) * y[p][d + i] ),  y = hm_moe_gemm's bf16
+ *   output for the same call, d = n / 2,
+ * bit for bit what hm_moe_gemm followed by hm_silu_mul gives, without
+ * writing or reading y.
+ *   w_dev  from hm_transform_gated (same descriptor, n = 2d, n a multiple of
+ *          32; HM_ERR_SHAPE otherwise): gate rows 0..d-1 and up rows
+ *          d..2d-1 of the standard format, interleaved by 16-row blocks in
+ *          the device layout so that a wave holds both halves of an output.
+ *   h      bf16 [t*topk][n/2], rows in pair order; rows of dropped pairs are
+ *          not written.
+ *   ws     at least hm_moe_gemm_workspace_size bytes (the same schedule).
+ * Other arguments and errors as hm_moe_gemm; the grouped streaming units
+ * take two column blocks per wave (tune->moe_stream_nbw = 1 gives
+ * HM_ERR_TUNING). */
+hm_status hm_moe_gemm_gated(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* a,
+                            const void* a_scales, int32_t a_rows_are_pairs, int64_t t,
+                            int32_t topk, const int32_t* offsets, const int32_t* sorted_pairs,
+                            uint16_t* h, void* ws, size_t ws_bytes, const hm_tuning* tune,
+                            hipStream_t stream);
+
+/* The plan text of hm_moe_gemm_gated (as hm_moe_gemm_plan). */
+hm_status hm_moe_gemm_gated_plan(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
+                                 int32_t a_rows_are_pairs, const hm_tuning* tune, char* buf, size_t buf_len);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same

@@ -194,3 +194,19 @@ def _transform_int8_ref(codes, scales):
                 sb[:, nb, :, cc] = sc[:, n, :]
     out[ob:ob + sb.size * 2] = sb.view(np.uint8).ravel()
     return out
+
+
+def gated_rows(n):
+    """Source row of each device row of the gated layout of a gate_up weight
+    with n = 2d rows (gate rows 0..d-1, up rows d..2d-1, n a multiple of 32):
+    device 16-row block 2i holds gate rows 16i..16i+15 and block 2i+1 the up
+    rows d+16i..d+16i+15, so that one wave's pair of column blocks holds both
+    halves of 16 outputs.  The buffer of the gated layout equals transform_ref
+    of the weight with its rows taken in this order."""
+    assert n % 32 == 0
+    d = n // 2
+    src = []
+    for blk in range(n // 16):
+        base = (d if blk % 2 else 0) + 16 * (blk // 2)
+        src.extend(range(base, base + 16))
+    return np.array(src, dtype=np.int64)

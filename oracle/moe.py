@@ -72,6 +72,23 @@ def silu_mul_ref(gu_hat, d):
     return g * sig * u
 
 
+# |d silu(x) / dx| = |s (1 + x (1 - s))| with s the logistic function: at
+# most 1.0998 (near x = 2.40), so 1.1 bounds it everywhere
+SILU_SLOPE = 1.1
+
+
+def silu_mul_bound(g, u, eg, eu):
+    """Bound on |silu(g') u' - silu(g) u| over |g' - g| <= eg, |u' - u| <= eu
+    (the gated product of a gate_up output known to within eg, eu element by
+    element): |silu(g') - silu(g)| <= 1.1 eg and |silu(g')| <= |silu(g)| + 1.1 eg,
+    so the difference is at most 1.1 eg (|u| + eu) + |silu(g)| eu."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        sg = g / (1.0 + np.exp(-g))
+    return SILU_SLOPE * eg * (np.abs(u) + eu) + np.abs(sg) * eu
+
+
 def combine_ref(y_hat, weights, topk):
     """out[t] = sum_j w[t, j] * y[t*topk + j] in float64 over pair-order rows
     y_hat [T*topk, N], and the bound sum_j |w[t, j] * y[t*topk + j]|."""

@@ -86,6 +86,7 @@ def _load():
     sig = {
         "hm_transform_size": [D, ctypes.POINTER(SZ)],
         "hm_transform": [D, P, P, P, P, SZ, P],
+        "hm_transform_gated": [D, P, P, P, P, SZ, P],
         "hm_dequant": [D, P, SZ, I32, P, P],
         "hm_quant_fp8_rows": [P, I64, I64, P, P, P],
         "hm_quant_mxfp4_rows": [P, I64, I64, P, P, P],
@@ -96,7 +97,9 @@ def _load():
         "hm_moe_sort": [P, I64, I32, I32, P, P, P, P, SZ, P],
         "hm_moe_gemm_workspace_size": [D, I32, I64, I32, T, ctypes.POINTER(SZ)],
         "hm_moe_gemm": [D, P, I32, P, P, I32, I64, I32, P, P, P, P, SZ, T, P],
+        "hm_moe_gemm_gated": [D, P, I32, P, P, I32, I64, I32, P, P, P, P, SZ, T, P],
         "hm_moe_gemm_plan": [D, I32, I64, I32, I32, T, ctypes.c_char_p, SZ],
+        "hm_moe_gemm_gated_plan": [D, I32, I64, I32, I32, T, ctypes.c_char_p, SZ],
         "hm_silu_mul": [P, I64, I64, P, P],
         "hm_silu_mul_fp8": [P, I64, I64, P, P, P],
         "hm_moe_combine": [P, P, I64, I32, I64, P, P],
@@ -146,17 +149,20 @@ def hm_transform_size(desc):
     return out.value
 
 
-def hm_transform(desc, codes, scales, zeros=None, w_dev=None, stream=None):
+def hm_transform(desc, codes, scales, zeros=None, w_dev=None, stream=None, gated=False):
     """codes uint8 [E,N,K/2]; scales int16/uint16 bits [E,N,K/128] (INT4) or uint8
-    [E,N,K/32] (MXFP4); zeros uint8 [E,N,K/128] (UINT4_ZP).  Returns w_dev (uint8)."""
+    [E,N,K/32] (MXFP4); zeros uint8 [E,N,K/128] (UINT4_ZP).  Returns w_dev (uint8).
+    gated: a gate_up weight (gate rows, then up rows) into the gated layout
+    of hm_moe_gemm_gated (hm_transform_gated)."""
     nbytes = hm_transform_size(desc)
     if w_dev is None:
         w_dev = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
     E, n, k = desc.num_experts, desc.n, desc.k
     _need(codes, torch.uint8, E * n * k * CODE_BITS.get(desc.wfmt, 4) // 8, "codes")
     _need(w_dev, torch.uint8, nbytes, "w_dev")
-    _ok("hm_transform", lib.hm_transform(ctypes.byref(desc), _ptr(codes), _ptr(scales), _ptr(zeros),
-                                         _ptr(w_dev), w_dev.numel(), _stream(stream)))
+    fn = "hm_transform_gated" if gated else "hm_transform"
+    _ok(fn, getattr(lib, fn)(ctypes.byref(desc), _ptr(codes), _ptr(scales), _ptr(zeros),
+                             _ptr(w_dev), w_dev.numel(), _stream(stream)))
     return w_dev
 
 
@@ -278,32 +284,36 @@ def hm_moe_gemm_workspace_size(desc, afmt, t, topk, tuning=None):
     return out.value
 
 
-def hm_moe_gemm_plan(desc, afmt, t, topk, a_rows_are_pairs, tuning=None):
+def hm_moe_gemm_plan(desc, afmt, t, topk, a_rows_are_pairs, tuning=None, gated=False):
     buf = ctypes.create_string_buffer(512)
-    _ok("hm_moe_gemm_plan", lib.hm_moe_gemm_plan(ctypes.byref(desc), int(afmt), int(t), int(topk),
-                                                 int(a_rows_are_pairs), _tune(tuning), buf, 512))
+    fn = "hm_moe_gemm_gated_plan" if gated else "hm_moe_gemm_plan"
+    _ok(fn, getattr(lib, fn)(ctypes.byref(desc), int(afmt), int(t), int(topk),
+                             int(a_rows_are_pairs), _tune(tuning), buf, 512))
     return buf.value.decode()
 
 
 def hm_moe_gemm(desc, w_dev, a, offsets, sorted_pairs, t, topk, a_rows_are_pairs, a_scales=None,
-                y=None, ws=None, afmt=None, tuning=None, stream=None):
+                y=None, ws=None, afmt=None, tuning=None, stream=None, gated=False):
     """Grouped GEMM; returns y bf16 [t*topk, n] in pair order.  a: bf16 rows,
     or E4M3 bytes with fp32 a_scales (MXFP4 weights only).  tuning: None, an
-    hm_tuning, or a dict of its fields."""
+    hm_tuning, or a dict of its fields.  gated: hm_moe_gemm_gated on weights
+    from hm_transform(..., gated=True); returns h bf16 [t*topk, n/2]."""
     afmt = _afmt(a, a_scales) if afmt is None else afmt
     P = t * topk
+    ncols = desc.n // 2 if gated else desc.n
     if y is None:
-        y = torch.empty(P, desc.n, dtype=torch.bfloat16, device=a.device)
-    _need(y, torch.bfloat16, P * desc.n, "y")
+        y = torch.empty(P, ncols, dtype=torch.bfloat16, device=a.device)
+    _need(y, torch.bfloat16, P * ncols, "y")
     if isinstance(tuning, dict):
         tuning = make_tuning(**tuning)
     if ws is None:
         need = hm_moe_gemm_workspace_size(desc, afmt, t, topk, tuning)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=a.device)
-    _ok("hm_moe_gemm", lib.hm_moe_gemm(ctypes.byref(desc), _ptr(w_dev), int(afmt), _ptr(a),
-                                       _ptr(a_scales), int(a_rows_are_pairs), int(t), int(topk),
-                                       _ptr(offsets), _ptr(sorted_pairs), _ptr(y), _ptr(ws),
-                                       ws.numel(), _tune(tuning), _stream(stream)))
+    fn = "hm_moe_gemm_gated" if gated else "hm_moe_gemm"
+    _ok(fn, getattr(lib, fn)(ctypes.byref(desc), _ptr(w_dev), int(afmt), _ptr(a),
+                             _ptr(a_scales), int(a_rows_are_pairs), int(t), int(topk),
+                             _ptr(offsets), _ptr(sorted_pairs), _ptr(y), _ptr(ws),
+                             ws.numel(), _tune(tuning), _stream(stream)))
     return y
 
 

@@ -313,4 +313,41 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | ((r >> 20) - (120u << 3));
 }
 
+// silu(g) = g / (1 + e^-g) = g s with s = 1 / (1 + e), e = e^-|g|, for
+// g >= 0, and g e s for g < 0.  One exponential, taken as ee = e 2^64 =
+// e^(64 ln 2 - |g|), which stays normal for |g| up to about 131 (where e
+// alone would leave the normal range below |g| = 87); e = ee 2^-64 and the
+// negative branch's g ee s 2^-64 are exact rescalings (the latter rounds once
+// if it is subnormal).  The fast exponential (relative error about 3e-6 for
+// arguments near 44) and the hardware reciprocal (1 ulp) stay far below the
+// final bf16 rounding (2^-9).
+__device__ __forceinline__ float silu_f(float g) {
+  const float ee = __expf(44.3614195558365f - fabsf(g));
+  const float s = __builtin_amdgcn_rcpf(1.0f + ee * 5.421010862427522e-20f);
+  return g >= 0.0f ? g * s : ((g * ee) * s) * 5.421010862427522e-20f;
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+
+// The gated activation of two bf16 pairs: bf16(silu(g) * u) for the low and
+// high halves (g, u already rounded to bf16, as a bf16 gate_up output is).
+__device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g2, uint32_t u2) {
+  return pack_bf16(silu_f(lo_bf16(g2)) * lo_bf16(u2), silu_f(hi_bf16(g2)) * hi_bf16(u2));
+}
+
+// Gated (gate / up interleaved) weight layout: device 16-column block 2 i
+// holds gate columns 16 i .. 16 i + 15, block 2 i + 1 the matching up
+// columns (N a multiple of 32).  Source row of device row n:
+__host__ __device__ inline int64_t gated_src_row(int64_t n, int64_t N) {
+  const int64_t i = n >> 5, c = n & 15;
+  return ((n >> 4) & 1) ? N / 2 + 16 * i + c : 16 * i + c;
+}
+// Staged bf16 rows of a tile that starts on an even block: output chunk oc
+// (8 columns of the tile's output row, which starts at column 8 nb0 of the
+// [rows][N/2] output) is the gated product of staged chunk gated_gate_chunk(oc)
+// (gate) and that chunk + 2 (up).
+__device__ __forceinline__ int gated_gate_chunk(int oc) { return ((oc >> 1) << 2) | (oc & 1); }
+
 }  // namespace hm

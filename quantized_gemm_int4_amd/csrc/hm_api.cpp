@@ -294,7 +294,7 @@ struct MoePlan {
 // Work-list sizes and workspace layout (independent of the activation size);
 // kernel choices need rows_are_pairs (< 0: sizes only).
 hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int rows_are_pairs,
-                   const Tune& tu, MoePlan* out) {
+                   const Tune& tu, MoePlan* out, bool gated = false) {
   MoePlan p{};
   p.P = t * topk;
   const int64_t act = (p.P < d->num_experts) ? p.P : d->num_experts;
@@ -305,6 +305,12 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
   p.s_rows = tu.mrows ? tu.mrows : (mxi4 ? kMoeStreamRowsMxi4 : kMoeStreamRows);
   p.s_max = tu.mmax ? tu.mmax : (a8 ? kMoeStreamMaxMx : (mxi4 ? kMoeStreamMaxMxi4 : kMoeStreamMaxA16));
   p.nbw = tu.mnbw ? tu.mnbw : (a8 ? kMoeStreamNbwMx : kMoeStreamNbwA16);
+  if (gated) {
+    // the gated epilogue pairs a wave's two column blocks (gate, up)
+    if (d->n % 32 != 0) return HM_ERR_SHAPE;
+    if (tu.mnbw == 1) return HM_ERR_TUNING;
+    p.nbw = 2;
+  }
   p.ks = tu.mks ? tu.mks : 1;
   p.lds_kb = tu.mlds ? tu.mlds : kMoeStreamLdsKb;
   // an expert remainder of at least big_min rows takes a 256-row unit
@@ -346,7 +352,8 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
 // 128-row and 256-row unit kernels (each a persistent grid over its units).
 hm_status launch_moe(const hm_wdesc* d, int32_t afmt, const void* w_dev, const void* a_in, const void* a_scales,
                      int32_t a_rows_are_pairs, int64_t t, int32_t topk, const int32_t* offsets,
-                     const int32_t* sorted_pairs, uint16_t* y, uint8_t* w8, const MoePlan& p, hipStream_t stream) {
+                     const int32_t* sorted_pairs, uint16_t* y, uint8_t* w8, const MoePlan& p, hipStream_t stream,
+                     bool gated = false) {
   int32_t* hdr = (int32_t*)w8;
   int32_t* su = (int32_t*)(w8 + p.off_su);
   int32_t* tu = (int32_t*)(w8 + p.off_tu);
@@ -367,6 +374,7 @@ hm_status launch_moe(const hm_wdesc* d, int32_t afmt, const void* w_dev, const v
   a.topk = topk;
   a.rows_are_pairs = a_rows_are_pairs;
   a.P = p.P;
+  a.gated = gated ? 1 : 0;
   (void)t;
   hipError_t e = launch_moe_schedule(offsets, d->num_experts, p.P, p.s_rows, p.s_max, kTileM, p.big_min,
                                      p.max_s, p.max_t, p.max_b, hdr, su, tu, bu, stream);
@@ -423,20 +431,33 @@ HM_API hm_status hm_transform_size(const hm_wdesc* d, size_t* bytes) {
   return HM_OK;
 }
 
-HM_API hm_status hm_transform(const hm_wdesc* d, const uint8_t* codes, const void* scales,
-                              const uint8_t* zeros, void* w_dev, size_t w_bytes,
-                              hipStream_t stream) {
+static hm_status transform_impl(const hm_wdesc* d, const uint8_t* codes, const void* scales,
+                                const uint8_t* zeros, void* w_dev, size_t w_bytes, bool gated,
+                                hipStream_t stream) {
   hm_status s = check_desc(d);
   if (s) return s;
+  if (gated && d->n % 32 != 0) return HM_ERR_SHAPE;
   if (!codes || !scales || !w_dev) return HM_ERR_NULL;
   if (device_fmt(d->wfmt) == HM_W_UINT4_ZP && !zeros) return HM_ERR_NULL;
   if (!aligned(codes, 16) || !aligned(w_dev, 256)) return HM_ERR_ALIGN;
   if (!aligned(scales, is_mx(d->wfmt) ? 1 : 2)) return HM_ERR_ALIGN;
   const Geom G = geom_of(d);
   if (w_bytes < G.total) return HM_ERR_WORKSPACE;
-  if (launch_transform(d->wfmt, G, codes, scales, zeros, (uint8_t*)w_dev, stream) != hipSuccess)
+  if (launch_transform(d->wfmt, G, codes, scales, zeros, (uint8_t*)w_dev, gated ? 1 : 0, stream) != hipSuccess)
     return HM_ERR_HIP;
   return HM_OK;
+}
+
+HM_API hm_status hm_transform(const hm_wdesc* d, const uint8_t* codes, const void* scales,
+                              const uint8_t* zeros, void* w_dev, size_t w_bytes,
+                              hipStream_t stream) {
+  return transform_impl(d, codes, scales, zeros, w_dev, w_bytes, false, stream);
+}
+
+HM_API hm_status hm_transform_gated(const hm_wdesc* d, const uint8_t* codes, const void* scales,
+                                    const uint8_t* zeros, void* w_dev, size_t w_bytes,
+                                    hipStream_t stream) {
+  return transform_impl(d, codes, scales, zeros, w_dev, w_bytes, true, stream);
 }
 
 HM_API hm_status hm_dequant(const hm_wdesc* d, const void* w_dev, size_t w_bytes, int32_t expert,
@@ -675,15 +696,15 @@ HM_API hm_status hm_moe_gemm_workspace_size(const hm_wdesc* d, int32_t afmt, int
   return HM_OK;
 }
 
-HM_API hm_status hm_moe_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
-                                  int32_t a_rows_are_pairs, const hm_tuning* tune, char* buf, size_t buf_len) {
+static hm_status moe_plan_text(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int32_t a_rows_are_pairs,
+                               const hm_tuning* tune, char* buf, size_t buf_len, bool gated) {
   Tune tu;
   hm_status s = moe_common(d, afmt, t, topk, tune, &tu);
   if (s) return s;
   if (a_rows_are_pairs != 0 && a_rows_are_pairs != 1) return HM_ERR_SHAPE;
   if (!buf || buf_len == 0) return HM_ERR_NULL;
   MoePlan p;
-  if ((s = plan_moe(d, afmt, t, topk, a_rows_are_pairs, tu, &p))) return s;
+  if ((s = plan_moe(d, afmt, t, topk, a_rows_are_pairs, tu, &p, gated))) return s;
   const bool a8 = afmt == HM_A_FP8_ROWSCALE;
   const char* tile = p.tile == P_TILE ? "k_gemm_tile 128x128"
                      : (a8 ? "k_gemm_mid_mx 64x128" : "k_gemm_mid 128x64");
@@ -691,18 +712,28 @@ HM_API hm_status hm_moe_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t t, in
   if (p.big_min > 0) snprintf(big, sizeof big, "k_gemm_big from %d rows", p.big_min);
   else snprintf(big, sizeof big, "none");
   snprintf(buf, buf_len,
-           "%s moe stream(rows=%d max=%d nbw=%d ks=%d lds=%dKiB)=k_gemm_stream tile(<=128 rows)=%s "
+           "%s moe%s stream(rows=%d max=%d nbw=%d ks=%d lds=%dKiB)=k_gemm_stream tile(<=128 rows)=%s "
            "big(256 rows)=%s%s ws=%zu",
-           pair_name(d, afmt), p.s_rows, p.s_max, p.nbw, p.ks, p.lds_kb, tile, big,
-           p.a64 ? " activations>=4GiB" : "", p.ws_bytes);
+           pair_name(d, afmt), gated ? " gated(silu epilogue)" : "", p.s_rows, p.s_max, p.nbw, p.ks, p.lds_kb, tile,
+           big, p.a64 ? " activations>=4GiB" : "", p.ws_bytes);
   return HM_OK;
 }
 
-HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* a_in,
-                             const void* a_scales, int32_t a_rows_are_pairs, int64_t t,
-                             int32_t topk, const int32_t* offsets, const int32_t* sorted_pairs,
-                             uint16_t* y, void* ws, size_t ws_bytes, const hm_tuning* tune,
-                             hipStream_t stream) {
+HM_API hm_status hm_moe_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
+                                  int32_t a_rows_are_pairs, const hm_tuning* tune, char* buf, size_t buf_len) {
+  return moe_plan_text(d, afmt, t, topk, a_rows_are_pairs, tune, buf, buf_len, false);
+}
+
+HM_API hm_status hm_moe_gemm_gated_plan(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk,
+                                        int32_t a_rows_are_pairs, const hm_tuning* tune, char* buf,
+                                        size_t buf_len) {
+  return moe_plan_text(d, afmt, t, topk, a_rows_are_pairs, tune, buf, buf_len, true);
+}
+
+static hm_status moe_gemm_impl(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* a_in,
+                               const void* a_scales, int32_t a_rows_are_pairs, int64_t t, int32_t topk,
+                               const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* y, void* ws,
+                               size_t ws_bytes, const hm_tuning* tune, bool gated, hipStream_t stream) {
   Tune tu;
   hm_status s = moe_common(d, afmt, t, topk, tune, &tu);
   if (s) return s;
@@ -715,10 +746,28 @@ HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt,
     return HM_ERR_ALIGN;
   if (a_scales && !aligned(a_scales, 4)) return HM_ERR_ALIGN;
   MoePlan p;
-  if ((s = plan_moe(d, afmt, t, topk, a_rows_are_pairs, tu, &p))) return s;
+  if ((s = plan_moe(d, afmt, t, topk, a_rows_are_pairs, tu, &p, gated))) return s;
   if (ws_bytes < p.ws_bytes) return HM_ERR_WORKSPACE;
   return launch_moe(d, afmt, w_dev, a_in, a_scales, a_rows_are_pairs, t, topk, offsets, sorted_pairs, y,
-                    (uint8_t*)ws, p, stream);
+                    (uint8_t*)ws, p, stream, gated);
+}
+
+HM_API hm_status hm_moe_gemm(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* a_in,
+                             const void* a_scales, int32_t a_rows_are_pairs, int64_t t,
+                             int32_t topk, const int32_t* offsets, const int32_t* sorted_pairs,
+                             uint16_t* y, void* ws, size_t ws_bytes, const hm_tuning* tune,
+                             hipStream_t stream) {
+  return moe_gemm_impl(d, w_dev, afmt, a_in, a_scales, a_rows_are_pairs, t, topk, offsets, sorted_pairs, y, ws,
+                       ws_bytes, tune, false, stream);
+}
+
+HM_API hm_status hm_moe_gemm_gated(const hm_wdesc* d, const void* w_dev, int32_t afmt, const void* a_in,
+                                   const void* a_scales, int32_t a_rows_are_pairs, int64_t t,
+                                   int32_t topk, const int32_t* offsets, const int32_t* sorted_pairs,
+                                   uint16_t* h, void* ws, size_t ws_bytes, const hm_tuning* tune,
+                                   hipStream_t stream) {
+  return moe_gemm_impl(d, w_dev, afmt, a_in, a_scales, a_rows_are_pairs, t, topk, offsets, sorted_pairs, h, ws,
+                       ws_bytes, tune, true, stream);
 }
 
 // ------------------------------------------------ allocation-free grouped GEMM

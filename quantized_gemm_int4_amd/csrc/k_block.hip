@@ -14,23 +14,6 @@
 
 namespace hm {
 
-namespace {
-
-// silu(g) = g / (1 + e^-g) = g s with s = 1 / (1 + e) for g >= 0 and
-// e / (1 + e) for g < 0, e = e^-|g| (never overflows); below -80, where e
-// would leave the normal range, as (g e^(g + 64 ln 2)) 2^-64.  The fast
-// exponential (relative error about 1e-5 at |g| = 80) and the hardware
-// reciprocal (1 ulp) stay far below the final bf16 rounding (2^-9).
-__device__ __forceinline__ float silu_f(float g) {
-  if (g < -80.0f) return (g * __expf(g + 44.3614195558365f)) * 5.421010862427522e-20f;
-  const float e = __expf(-fabsf(g));
-  return g * ((g >= 0.0f ? 1.0f : e) * __builtin_amdgcn_rcpf(1.0f + e));
-}
-
-__device__ __forceinline__ float lo_bf16(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
-
-}  // namespace
 
 // d % 8 == 0: thread q handles outputs 8 (q % (d/8)) .. + 7 of row q / (d/8)
 __global__ void __launch_bounds__(256)

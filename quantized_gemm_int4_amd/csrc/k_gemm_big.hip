@@ -358,7 +358,18 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
       const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(ost + r * 512 + ((2 * c + 1) ^ g) * 8);
       int64_t row, arow;
       local_row(t, 64 * p + r, row, arow);
-      if (row >= 0) store_bf16x8(a.y + row * G.N, G.N, t.nb0 * 16 + 8 * c, (u32x4_t){v0[0], v0[1], v1[0], v1[1]});
+      if (GROUPED && a.gated) {
+        // gated layout: lane c takes half c & 1 (4 values) of output chunk
+        // c >> 1, from the same half of its gate and up chunks
+        const int oc = c >> 1, hf = c & 1, gc = gated_gate_chunk(oc);
+        const u32x2_t gv = *reinterpret_cast<const u32x2_t*>(ost + r * 512 + ((2 * gc + hf) ^ g) * 8);
+        const u32x2_t uv = *reinterpret_cast<const u32x2_t*>(ost + r * 512 + ((2 * gc + 4 + hf) ^ g) * 8);
+        if (row >= 0)
+          *reinterpret_cast<u32x2_t*>(a.y + row * (G.N / 2) + t.nb0 * 8 + 8 * oc + 4 * hf) =
+              (u32x2_t){silu_mul_pair(gv[0], uv[0]), silu_mul_pair(gv[1], uv[1])};
+      } else if (row >= 0) {
+        store_bf16x8(a.y + row * G.N, G.N, t.nb0 * 16 + 8 * c, (u32x4_t){v0[0], v0[1], v1[0], v1[1]});
+      }
     }
   };
 

@@ -397,7 +397,19 @@ k_gemm_mid(GemmArgs a, int tiles_n, int tiles_m) {
       const int r = 8 * k + (lane >> 3), cidx = lane & 7;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ost + r * 128 + ((cidx ^ (r & 7)) * 16));
       const int lr = 32 * wave + r;
-      if (lr < t.rows) {
+      if (GROUPED && a.gated) {
+        // gated layout: lane cidx takes half cidx & 1 (4 values) of output
+        // chunk cidx >> 1, from the same half of its gate and up chunks
+        const int oc = cidx >> 1, hf = cidx & 1, gc = gated_gate_chunk(oc);
+        const u32x2_t gv = *reinterpret_cast<const u32x2_t*>(ost + r * 128 + ((gc ^ (r & 7)) * 16) + 8 * hf);
+        const u32x2_t uv = *reinterpret_cast<const u32x2_t*>(ost + r * 128 + (((gc + 2) ^ (r & 7)) * 16) + 8 * hf);
+        if (lr < t.rows) {
+          const int64_t row = orow_s[lr];
+          if (row >= 0)
+            *reinterpret_cast<u32x2_t*>(a.y + row * (G.N / 2) + t.nb0 * 8 + 8 * oc + 4 * hf) =
+                (u32x2_t){silu_mul_pair(gv[0], uv[0]), silu_mul_pair(gv[1], uv[1])};
+        }
+      } else if (lr < t.rows) {
         const int64_t row = GROUPED ? (int64_t)orow_s[lr] : t.m0 + lr;
         if (row >= 0) store_bf16x8(a.y + row * G.N, G.N, t.nb0 * 16 + 8 * cidx, v);
       }
@@ -587,7 +599,20 @@ k_gemm_mid_mx(GemmArgs a, int tiles_n, int tiles_m) {
     for (int k = 0; k < 4; ++k) {
       const int r = 16 * k + (tid >> 4), c16 = tid & 15;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + r * 256 + ((2 * c16) ^ (2 * (r & 15))) * 8);
-      if (r < t.rows) {
+      if (GROUPED && a.gated) {
+        // gated layout: lane c16 takes half c16 & 1 (4 values) of output
+        // chunk c16 >> 1, from the same half of its gate and up chunks
+        const int oc = c16 >> 1, hf = c16 & 1, gc = gated_gate_chunk(oc);
+        const u32x2_t gv = *reinterpret_cast<const u32x2_t*>(lds + r * 256 + ((2 * gc + hf) ^ (2 * (r & 15))) * 8);
+        const u32x2_t uv =
+            *reinterpret_cast<const u32x2_t*>(lds + r * 256 + ((2 * gc + 4 + hf) ^ (2 * (r & 15))) * 8);
+        if (r < t.rows) {
+          const int64_t row = orow_s[r];
+          if (row >= 0)
+            *reinterpret_cast<u32x2_t*>(a.y + row * (G.N / 2) + t.nb0 * 8 + 8 * oc + 4 * hf) =
+                (u32x2_t){silu_mul_pair(gv[0], uv[0]), silu_mul_pair(gv[1], uv[1])};
+        }
+      } else if (r < t.rows) {
         const int64_t row = GROUPED ? (int64_t)orow_s[r] : t.m0 + r;
         if (row >= 0) store_bf16x8(a.y + row * G.N, G.N, t.nb0 * 16 + 8 * c16, v);
       }

@@ -423,7 +423,32 @@ k_gemm_stream(GemmArgs a, int n_tiles, int pg, int xb) {
     }
 
     // ---- epilogue: lane holds C[n = 16nb + 4*q_l + r][row = 16rb + n_l]
-    if (kq == 0) {
+    if (NBW == 2 && GROUPED && a.gated && kq == 0) {
+      // gated layout: the wave's blocks nb0 (even) and nb0 + 1 are the gate
+      // and up halves of output columns 8 nb0 + 4 q_l + r of [rows][N/2]
+      if (nb0 < G.NB) {
+        const int64_t n = nb0 * 8 + 4 * q_l;
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+          const int rl = rb * 16 + n_l;
+          if (rl >= rcount || orow_s[rl] < 0) continue;
+          f32x4_t vg = acc[0][rb], vu = acc[NBW - 1][rb];
+          if (MODE == KM_INT4_A16 && !ZP) {
+            vg = vg * 16.f;
+            vu = vu * 16.f;
+          }
+          if (MX) {
+            const float rs = a.xs[arow_s[rl]];
+            vg = vg * rs;
+            vu = vu * rs;
+          }
+          uint16_t* dst = a.y + orow_s[rl] * (G.N / 2) + n;
+          *reinterpret_cast<u32x2_t*>(dst) =
+              (u32x2_t){silu_mul_pair(pack_bf16(vg[0], vg[1]), pack_bf16(vu[0], vu[1])),
+                        silu_mul_pair(pack_bf16(vg[2], vg[3]), pack_bf16(vu[2], vu[3]))};
+        }
+      }
+    } else if (kq == 0) {
       const bool partial = (!GROUPED) && (a.part != nullptr);
       const int64_t Np = G.NB * 16;
 #pragma unroll

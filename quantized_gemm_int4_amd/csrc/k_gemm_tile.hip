@@ -251,6 +251,33 @@ k_gemm_tile(GemmArgs a, int n_tiles) {
     }
 
     // ---- epilogue: lane holds C[n = 16nb + 4*q_l + r][row = 16mb + n_l]
+    if (GROUPED && a.gated) {
+      // gated layout: blocks nb (even) and nb + 1 of the lane's j = 2 p and
+      // 2 p + 1 are the gate and up halves of output columns 8 nb + 4 q_l + r
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int64_t nb = nbt + wn * 4 + 2 * p;
+        if (nb >= G.NB) continue;
+        const int64_t n = nb * 8 + 4 * q_l;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int rl = wm * 64 + mb * 16 + n_l;
+          if (rl >= rcount || orow_s[rl] < 0) continue;
+          f32x4_t vg = acc[2 * p][mb], vu = acc[2 * p + 1][mb];
+          if (MX && !A4) {
+            const float rs = a.xs[arow_s[rl]];
+            vg = vg * rs;
+            vu = vu * rs;
+          }
+          uint16_t* dst = a.y + orow_s[rl] * (G.N / 2) + n;
+          *reinterpret_cast<u32x2_t*>(dst) =
+              (u32x2_t){silu_mul_pair(pack_bf16(vg[0], vg[1]), pack_bf16(vu[0], vu[1])),
+                        silu_mul_pair(pack_bf16(vg[2], vg[3]), pack_bf16(vu[2], vu[3]))};
+        }
+      }
+      __syncthreads();
+      continue;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t nb = nbt + wn * 4 + j;

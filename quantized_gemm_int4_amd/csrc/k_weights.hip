@@ -16,7 +16,7 @@ __device__ __forceinline__ uint32_t compact_nibbles(uint32_t x) {
 
 // One thread per 16-byte code slot (e, nb, g, L).
 __global__ void __launch_bounds__(256)
-k_transform_codes(int wfmt, Geom G, const uint8_t* __restrict__ codes, uint8_t* __restrict__ out) {
+k_transform_codes(int wfmt, Geom G, const uint8_t* __restrict__ codes, uint8_t* __restrict__ out, int gated) {
   const int64_t slots = G.E * G.NB * G.KG * 64;
   const int64_t row_bytes = G.K / 2;
   for (int64_t s = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; s < slots;
@@ -33,7 +33,7 @@ k_transform_codes(int wfmt, Geom G, const uint8_t* __restrict__ codes, uint8_t* 
       // narrow codes widened to nibbles: word j of the slot holds values
       // k = 128 g + 32 j + 8 h + i, i = 0..7, value 2p in nibble p, 2p+1 in p+4
       const int bits = wfmt == W_UINT3_ZP ? 3 : 2;
-      const uint8_t* row = codes + (e * G.N + n) * (G.K * bits / 8);
+      const uint8_t* row = codes + (e * G.N + (gated ? gated_src_row(n, G.N) : n)) * (G.K * bits / 8);
       for (int j = 0; j < 4; ++j) {
         const int64_t k0 = 128 * g + 32 * j + 8 * h;       // multiple of 8
         const uint8_t* p = row + k0 * bits / 8;
@@ -48,7 +48,7 @@ k_transform_codes(int wfmt, Geom G, const uint8_t* __restrict__ codes, uint8_t* 
         v[j] = o;
       }
     } else if (n < G.N) {
-      const uint8_t* row = codes + (e * G.N + n) * row_bytes;
+      const uint8_t* row = codes + (e * G.N + (gated ? gated_src_row(n, G.N) : n)) * row_bytes;
       if (is_mx(wfmt)) {
         v = ld16(row + 64 * g + 16 * h);
       } else {
@@ -73,7 +73,7 @@ k_transform_codes(int wfmt, Geom G, const uint8_t* __restrict__ codes, uint8_t* 
 // bytes 8 jj + i = value k = 128 g + 32 (2 p + jj) + 8 h + i of column
 // 16 nb + L % 16, h = L / 16; columns past N hold 0.
 __global__ void __launch_bounds__(256)
-k_transform_codes_i8(Geom G, const uint8_t* __restrict__ codes, uint8_t* __restrict__ out) {
+k_transform_codes_i8(Geom G, const uint8_t* __restrict__ codes, uint8_t* __restrict__ out, int gated) {
   const int64_t chunks = G.E * G.NB * G.KG * 128;
   for (int64_t s = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; s < chunks;
        s += (int64_t)gridDim.x * blockDim.x) {
@@ -87,7 +87,7 @@ k_transform_codes_i8(Geom G, const uint8_t* __restrict__ codes, uint8_t* __restr
     const int h = L >> 4;
     u32x4_t v = {0u, 0u, 0u, 0u};
     if (n < G.N) {
-      const uint8_t* row = codes + (e * G.N + n) * G.K;
+      const uint8_t* row = codes + (e * G.N + (gated ? gated_src_row(n, G.N) : n)) * G.K;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const uint8_t* q = row + 128 * g + 32 * (2 * p + jj) + 8 * h;   // 8-byte aligned
@@ -102,7 +102,7 @@ k_transform_codes_i8(Geom G, const uint8_t* __restrict__ codes, uint8_t* __restr
 
 // INT4 scales: one thread per (e, nb, g, c) bf16 entry.
 __global__ void __launch_bounds__(256)
-k_transform_scales_int4(Geom G, const uint16_t* __restrict__ scales, uint16_t* __restrict__ out) {
+k_transform_scales_int4(Geom G, const uint16_t* __restrict__ scales, uint16_t* __restrict__ out, int gated) {
   const int64_t cnt = G.E * G.NB * G.KG * 16;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < cnt;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -112,13 +112,13 @@ k_transform_scales_int4(Geom G, const uint16_t* __restrict__ scales, uint16_t* _
     const int64_t nb = t % G.NB;
     const int64_t e = t / G.NB;
     const int64_t n = nb * 16 + c;
-    out[i] = (n < G.N) ? scales[(e * G.N + n) * G.KG + g] : (uint16_t)0;
+    out[i] = (n < G.N) ? scales[(e * G.N + (gated ? gated_src_row(n, G.N) : n)) * G.KG + g] : (uint16_t)0;
   }
 }
 
 // MX scales: one thread per (e, nb, g4, L) u32 holding the E8M0 bytes of steps 4*g4 + 0..3.
 __global__ void __launch_bounds__(256)
-k_transform_scales_mx(Geom G, const uint8_t* __restrict__ scales, uint32_t* __restrict__ out) {
+k_transform_scales_mx(Geom G, const uint8_t* __restrict__ scales, uint32_t* __restrict__ out, int gated) {
   const int64_t cnt = G.E * G.NB * G.KG4 * 64;
   const int64_t blocks = G.K / 32;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < cnt;
@@ -133,7 +133,9 @@ k_transform_scales_mx(Geom G, const uint8_t* __restrict__ scales, uint32_t* __re
     if (n < G.N) {
       for (int gi = 0; gi < 4; ++gi) {
         const int64_t g = 4 * g4 + gi;
-        if (g < G.KG) v |= (uint32_t)scales[(e * G.N + n) * blocks + 4 * g + (L >> 4)] << (8 * gi);
+        if (g < G.KG)
+          v |= (uint32_t)scales[(e * G.N + (gated ? gated_src_row(n, G.N) : n)) * blocks + 4 * g + (L >> 4)]
+               << (8 * gi);
       }
     }
     out[i] = v;
@@ -143,7 +145,7 @@ k_transform_scales_mx(Geom G, const uint8_t* __restrict__ scales, uint32_t* __re
 // Zero points (zero-point formats): one thread per (e, nb, g) u64 of 16
 // nibbles; `mask` keeps the code width's bits of each zero-point byte.
 __global__ void __launch_bounds__(256)
-k_transform_zeros(Geom G, const uint8_t* __restrict__ zeros, uint64_t* __restrict__ out, uint32_t mask) {
+k_transform_zeros(Geom G, const uint8_t* __restrict__ zeros, uint64_t* __restrict__ out, uint32_t mask, int gated) {
   const int64_t cnt = G.E * G.NB * G.KG;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < cnt;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -154,7 +156,7 @@ k_transform_zeros(Geom G, const uint8_t* __restrict__ zeros, uint64_t* __restric
     uint64_t v = 0;
     for (int c = 0; c < 16; ++c) {
       const int64_t n = nb * 16 + c;
-      if (n < G.N) v |= (uint64_t)(zeros[(e * G.N + n) * G.KG + g] & mask) << (4 * c);
+      if (n < G.N) v |= (uint64_t)(zeros[(e * G.N + (gated ? gated_src_row(n, G.N) : n)) * G.KG + g] & mask) << (4 * c);
     }
     out[i] = v;
   }
@@ -243,24 +245,24 @@ static inline unsigned grid_for(int64_t items) {
 }
 
 hipError_t launch_transform(int wfmt, const Geom& G, const uint8_t* codes, const void* scales,
-                            const uint8_t* zeros, uint8_t* out, hipStream_t st) {
+                            const uint8_t* zeros, uint8_t* out, int gated, hipStream_t st) {
   if (wfmt == W_INT8_SYM)
     hipLaunchKernelGGL(k_transform_codes_i8, dim3(grid_for(G.E * G.NB * G.KG * 128)), dim3(256), 0, st, G, codes,
-                       out);
+                       out, gated);
   else
     hipLaunchKernelGGL(k_transform_codes, dim3(grid_for(G.E * G.NB * G.KG * 64)), dim3(256), 0, st,
-                       wfmt, G, codes, out);
+                       wfmt, G, codes, out, gated);
   if (is_mx(wfmt)) {
     hipLaunchKernelGGL(k_transform_scales_mx, dim3(grid_for(G.E * G.NB * G.KG4 * 64)), dim3(256), 0,
-                       st, G, (const uint8_t*)scales, (uint32_t*)(out + G.off_scales));
+                       st, G, (const uint8_t*)scales, (uint32_t*)(out + G.off_scales), gated);
   } else {
     hipLaunchKernelGGL(k_transform_scales_int4, dim3(grid_for(G.E * G.NB * G.KG * 16)), dim3(256),
-                       0, st, G, (const uint16_t*)scales, (uint16_t*)(out + G.off_scales));
+                       0, st, G, (const uint16_t*)scales, (uint16_t*)(out + G.off_scales), gated);
   }
   if (device_fmt(wfmt) == W_UINT4_ZP) {
     const uint32_t mask = wfmt == W_UINT3_ZP ? 0x7u : (wfmt == W_UINT2_ZP ? 0x3u : 0xFu);
     hipLaunchKernelGGL(k_transform_zeros, dim3(grid_for(G.E * G.NB * G.KG)), dim3(256), 0, st, G,
-                       zeros, (uint64_t*)(out + G.off_zeros), mask);
+                       zeros, (uint64_t*)(out + G.off_zeros), mask, gated);
   }
   // gap ends: codes end .. scales start, scales end .. zeros start, zeros end .. total
   const size_t codes_end = (size_t)G.E * G.NB * G.KG * (wfmt == W_INT8_SYM ? 2048 : 1024);

@@ -42,10 +42,14 @@ struct GemmArgs {
   int topk;
   int rows_are_pairs;
   int64_t P;               // routed pairs (row ids outside [0, P) are skipped)
+  // 1: weights in the gated layout (gate / up 16-column blocks interleaved,
+  // N % 32 == 0) and y is [rows][N/2] = bf16(silu(bf16 gate) * bf16 up)
+  int gated;
 };
 
+// gated: device row n takes source row gated_src_row(n, N) (N % 32 == 0)
 hipError_t launch_transform(int wfmt, const Geom& G, const uint8_t* codes, const void* scales,
-                            const uint8_t* zeros, uint8_t* out, hipStream_t st);
+                            const uint8_t* zeros, uint8_t* out, int gated, hipStream_t st);
 hipError_t launch_dequant(int wfmt, const Geom& G, const uint8_t* w, int64_t e, float* out,
                           hipStream_t st);
 hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* x8, float* s,

@@ -143,6 +143,21 @@ static void moe_sweep(const hm_wdesc& d) {
             } else {
               EXPECT(s != HM_OK || t == 0, "moe wfmt %d afmt %d t %lld topk %d rp %d: plan/size failed (%d/%d) but the call ran", d.wfmt, afmt, (long long)t, topk, rp, (int)s_plan, (int)s_ws);
             }
+            // the gated variant: same schedule, its own plan
+            {
+              const hm_status g_plan = hm_moe_gemm_gated_plan(&d, afmt, t, topk, rp, tn, buf, sizeof buf);
+              check_plan_text(g_plan, buf, sizeof buf);
+              const hm_status g = hm_moe_gemm_gated(&d, dev(1), afmt, dev(2), dev(3), rp, t, topk,
+                                                    (const int32_t*)dev(6), (const int32_t*)dev(7),
+                                                    (uint16_t*)dev(4), dev(5), ws, tn, nullptr);
+              if (s_ws == HM_OK && g_plan == HM_OK)
+                EXPECT(g == HM_OK, "gated moe wfmt %d n %lld t %lld: plan ok, call %d", d.wfmt, (long long)d.n,
+                       (long long)t, (int)g);
+              else
+                EXPECT(g != HM_OK || t == 0, "gated moe: plan/size failed (%d/%d) but the call ran", (int)g_plan,
+                       (int)s_ws);
+              if (g_plan == HM_OK) EXPECT(d.n % 32 == 0, "gated plan accepted n = %lld", (long long)d.n);
+            }
             // the allocation-free variant: its device lookup may fail here (no GPU)
             (void)hm_moe_gemm_static(&d, dev(1), afmt, dev(2), dev(3), rp, t, topk, (const int32_t*)dev(6),
                                      (const int32_t*)dev(7), (uint16_t*)dev(4), tn, nullptr);
@@ -177,10 +192,13 @@ int main() {
             const hm_status st = hm_transform_size(&d, &bytes);
             const hm_status tr = hm_transform(&d, (const uint8_t*)dev(1), dev(2), (const uint8_t*)dev(3), dev(4),
                                               bytes, nullptr);
+            const hm_status trg = hm_transform_gated(&d, (const uint8_t*)dev(1), dev(2), (const uint8_t*)dev(3),
+                                                     dev(4), bytes, nullptr);
             if (st != HM_OK) {
-              EXPECT(tr != HM_OK, "transform ran on a rejected descriptor");
+              EXPECT(tr != HM_OK && trg != HM_OK, "transform ran on a rejected descriptor");
               continue;
             }
+            EXPECT((trg == HM_OK) == (tr == HM_OK && n % 32 == 0), "gated transform status %d", (int)trg);
             ++descs;
             EXPECT(bytes > 0 && bytes % 256 == 0, "transform size %zu", bytes);
             if (bytes > 1) EXPECT(hm_transform(&d, (const uint8_t*)dev(1), dev(2), (const uint8_t*)dev(3), dev(4),

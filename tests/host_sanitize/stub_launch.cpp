@@ -26,6 +26,7 @@ static void check_gemm(const GemmArgs& a, bool grouped, int grid_items) {
   need(!a.a8 || a.xs != nullptr, "FP8 rows come with row scales");
   need(!a.a4 || a.xsb != nullptr, "MXFP4 rows come with block scales");
   need(!(a.a8 && a.a4), "one activation format");
+  need(!a.gated || (a.G.N % 32 == 0 && grouped), "gated output: grouped, N a multiple of 32");
   if (grouped) {
     need(grid_items >= 1, "grouped launches have items");
     need(a.units != nullptr && a.hdr != nullptr && a.sorted_pairs != nullptr, "grouped work lists");
@@ -37,8 +38,9 @@ static void check_gemm(const GemmArgs& a, bool grouped, int grid_items) {
 }
 
 hipError_t launch_transform(int wfmt, const Geom& G, const uint8_t* codes, const void* scales,
-                            const uint8_t* zeros, uint8_t* out, hipStream_t) {
+                            const uint8_t* zeros, uint8_t* out, int gated, hipStream_t) {
   need(wfmt >= 0 && wfmt <= 6 && codes && scales && out && G.total > 0, "transform arguments");
+  need(!gated || G.N % 32 == 0, "gated layout pairs whole 16-column blocks");
   (void)zeros;
   ++g_launches;
   return hipSuccess;

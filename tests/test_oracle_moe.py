@@ -150,3 +150,44 @@ def test_moe_pairs_subset_brute_force():
         # (BLAS may block a subset differently: equal up to fp64 rounding)
         assert np.allclose(y, yf[pairs], rtol=1e-13, atol=1e-13)
         assert np.allclose(b, bf[pairs], rtol=1e-13, atol=1e-13)
+
+
+def test_gated_rows_written_out():
+    """The gated layout's row order, written out for n = 64 and n = 96 from
+    the rule (device block 2i = gate rows 16i.., block 2i+1 = up rows
+    d + 16i..): a swapped gate/up or a wrong block stride fails it."""
+    from oracle import layout
+    r = lambda a, b: list(range(a, b))
+    assert list(layout.gated_rows(64)) == r(0, 16) + r(32, 48) + r(16, 32) + r(48, 64)
+    assert list(layout.gated_rows(96)) == (r(0, 16) + r(48, 64) + r(16, 32) + r(64, 80) + r(32, 48)
+                                           + r(80, 96))
+    p = layout.gated_rows(4096)
+    assert sorted(p) == list(range(4096))
+
+
+def test_silu_mul_bound_slope_and_corners():
+    """The slope constant bounds |silu'| (finite differences on a fine grid:
+    the maximum, about 1.0998, is within 1% of it), and the bound holds at
+    the worst corners of random error boxes (g +- eg, u +- eu), including
+    boxes around the slope maximum and wide ones; dropping either term of
+    the bound fails the corners."""
+    x = np.linspace(-30, 30, 600001)
+    f = x / (1 + np.exp(-x))
+    slope = np.abs(np.diff(f) / np.diff(x)).max()
+    assert 1.089 < slope <= moe.SILU_SLOPE
+    r = np.random.default_rng(11)
+    g = np.concatenate([r.normal(0, 4, 4000), np.full(200, 2.4)])
+    u = r.normal(0, 3, g.size)
+    eg = np.abs(r.normal(0, 0.5, g.size))
+    eu = np.abs(r.normal(0, 0.5, g.size))
+    b = moe.silu_mul_bound(g, u, eg, eu)
+    h0 = g / (1 + np.exp(-g)) * u
+    worst = np.zeros_like(g)
+    for sg in (-1, 0, 1):
+        for su in (-1, 1):
+            gp, up = g + sg * eg, u + su * eu
+            worst = np.maximum(worst, np.abs(gp / (1 + np.exp(-gp)) * up - h0))
+    assert np.all(worst <= b * (1 + 1e-12))
+    sgv = np.abs(g / (1 + np.exp(-g)))
+    assert np.any(worst > moe.SILU_SLOPE * eg * (np.abs(u) + eu))          # the eu term is needed
+    assert np.any(worst > sgv * eu)                                         # and the eg term
