@@ -157,10 +157,11 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   const bool a4 = afmt == HM_A_MXFP4;
   const bool tiles32 = scales_addr32(G);        // 128-row and 256-row kernels can address the scales
   if (tu.path == P_STREAM && m > kStreamWideRows) return HM_ERR_TUNING;
-  // W4A4 and INT8 weights: the streaming and 128 x 128 kernels only
-  const bool tile_only = a4 || d->wfmt == HM_W_INT8_SYM;
-  if (tile_only && (tu.path == P_MID || tu.path == P_BIG)) return HM_ERR_TUNING;
-  if (tu.path == P_BIG && f4) return HM_ERR_TUNING;  // no 256 x 256 kernel for MX weights with bf16 rows
+  // W4A4 and INT8 weights have no 128-row tile kernel; MX weights with bf16
+  // rows and INT8 weights no 256 x 256 kernel
+  const bool int8 = d->wfmt == HM_W_INT8_SYM;
+  const bool no_mid = a4 || int8, no_big = f4 || int8;
+  if ((no_mid && tu.path == P_MID) || (no_big && tu.path == P_BIG)) return HM_ERR_TUNING;
   if ((tu.path == P_MID || tu.path == P_BIG) && (!tiles32 || !mid_grid_fits(G, a8, m))) return HM_ERR_TUNING;
   // W4A16 up to 256 rows also streams (in 32-row chunks, each re-reading the
   // weights from the L2) when N is narrow: measured at K = 4096, a streaming
@@ -173,8 +174,11 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
     p.path = tu.path;
   } else if (m <= kStreamMaxRows || narrow) {
     p.path = P_STREAM;
-  } else if (tile_only) {
+  } else if (int8) {
     p.path = P_TILE;
+  } else if (a4) {
+    // W4A4: 256 x 256 tiles from kBigMinRows rows, else 128 x 128
+    p.path = m >= kBigMinRows ? P_BIG : P_TILE;
   } else if (f4) {
     // MX weights with bf16 rows (no 256 x 256 kernel): 128 x 64 tiles, or 128 x
     // 128 tiles once the 128 x 64 ones take many rounds of the chip.
@@ -329,8 +333,9 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
     const bool tiles32 = scales_addr32(G);
     // 256-row units: not for MX weights with bf16 rows; they address
     // activation rows and scales with 32-bit offsets
-    const bool tile_only = a4 || d->wfmt == HM_W_INT8_SYM;   // no 128-row tile or 256-row kernel
-    const bool big_ok = !f4 && !tile_only && !p.a64 && tiles32;
+    const bool int8 = d->wfmt == HM_W_INT8_SYM;
+    const bool tile_only = a4 || int8;                       // no 128-row tile kernel
+    const bool big_ok = !f4 && !int8 && !p.a64 && tiles32;   // W4A4 has 256-row units
     if (tu.mbig > 0 && !big_ok) return HM_ERR_TUNING;
     p.big_min = (tu.mbig == -1 || !big_ok) ? 0 : big_min;
     // up-to-128-row units: the 128-row tile kernel (32-bit offsets), or the
@@ -576,7 +581,9 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, const 
     const int64_t tiles = big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows);
     const int64_t halves = 2 * (tiles - big_full_tiles(G, m, d->wfmt == HM_W_MXFP4));
     snprintf(buf, buf_len, "%s tile 256x256 waves=%s mfma=%s half_tiles=%lld", w,
-             d->wfmt == HM_W_MXFP4 ? "4x2" : "1x4", d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "32x32x16_bf16",
+             d->wfmt == HM_W_MXFP4 ? "4x2" : "1x4",
+             afmt == HM_A_MXFP4 ? "scale_16x16x128_f8f6f4_fp4xfp4"
+                                : (d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "32x32x16_bf16"),
              (long long)halves);
   }
   else if (p.path == P_MID && a8)

@@ -52,11 +52,14 @@ __device__ __forceinline__ int64_t wbase_of(int64_t e, const Geom& G) { return e
 
 constexpr int kBigStages = 3;     // LDS stages: loads run two K steps ahead
 
-// LDS bytes of one stage: activation fragments (32 x 1 KiB) and the block's
-// 16 weight tiles (16 KiB), plus MXFP4: their E8M0 scale words (16 x 256 B);
-// INT4: per wave 256 B of bf16 scales and 256 B of zero-point words.
-__host__ __device__ constexpr int big_stage_bytes(bool mx) { return mx ? (32 + 16 + 4) * 1024 : (32 + 16 + 2) * 1024; }
-__host__ __device__ constexpr int big_lds_bytes(bool mx) { return kBigStages * big_stage_bytes(mx); }
+// LDS bytes of one stage: activation fragments (32 x 1 KiB; MXFP4 rows 16 x
+// 1 KiB) and the block's 16 weight tiles (16 KiB), plus MXFP4: their E8M0
+// scale words (16 x 256 B) and, with MXFP4 rows, the rows' E8M0 words (8 x
+// 256 B); INT4: per wave 256 B of bf16 scales and 256 B of zero-point words.
+__host__ __device__ constexpr int big_stage_bytes(bool mx, bool a4 = false) {
+  return a4 ? (16 + 16 + 4 + 2) * 1024 : (mx ? (32 + 16 + 4) * 1024 : (32 + 16 + 2) * 1024);
+}
+__host__ __device__ constexpr int big_lds_bytes(bool mx, bool a4 = false) { return kBigStages * big_stage_bytes(mx, a4); }
 // MXFP4: eight waves (two per SIMD); W4A16: four (one per SIMD, 256 accumulators each)
 __host__ __device__ constexpr int big_threads(bool mx) { return mx ? 512 : 256; }
 
@@ -85,6 +88,8 @@ struct BigCopy {
   uint32_t xoff[NX];  // activation copies (row offset + swizzled chunk)
   uint32_t wvo[NWT];  // weight tile copies
   uint32_t svo[2];    // MXFP4: scale words of the two tiles; INT4: scale / zero gather
+  rsrc_t rxs;         // MXFP4 rows: buffer over the rows' E8M0 bytes
+  uint32_t xso;       // MXFP4 rows: this lane's row of E8M0 bytes
 };
 
 // A persistent grid: block b takes tiles b, b + grid, b + 2 grid, ...  Dense
@@ -186,13 +191,16 @@ _Pragma("unroll")                                                               
         }                                                                                                           \
   } while (0)
 
-template <bool MX, bool ZP, bool GROUPED>
+template <bool MX, bool ZP, bool GROUPED, bool A4 = false>
 __global__ void __launch_bounds__(big_threads(MX), 1)
 k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
-  constexpr int SB = big_stage_bytes(MX);
+  static_assert(!A4 || MX, "MXFP4 rows go with MXFP4 weights");
+  constexpr int SB = big_stage_bytes(MX, A4);
   constexpr int NW = big_threads(MX) / 64;         // waves
-  constexpr int NX = 32 / NW;                      // activation copies per lane per step
+  constexpr int NX = A4 ? 2 : 32 / NW;             // activation copies per lane per step
+  constexpr int NPR = A4 ? NX + 1 : NX;            // grouped: pair rows a thread's copies read
   constexpr int NWT = 16 / NW;                     // weight tiles copied per wave per step
+  constexpr int XSTEP = A4 ? 64 : 128;             // activation bytes per row per K step
   typedef BigCopy<NX, NWT> Copy;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   __shared__ int32_t arow_s[GROUPED ? kBigM : 1];   // activation row of each local row
@@ -202,7 +210,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_l = lane & 15, q_l = lane >> 4, l32 = lane & 31, hi = lane >> 5;
   const Geom G = a.G;
-  const int64_t row_bytes = MX ? G.K : 2 * G.K;
+  const int64_t row_bytes = A4 ? G.K / 2 : (MX ? G.K : 2 * G.K);
   const int S = (int)(MX ? G.KG : 2 * G.KG);      // K steps per tile
   const bool chained = S >= 3;
   // dense: tiles n_full.. of the visiting order run as two 128-row halves
@@ -273,7 +281,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
   // (tile (L / 2) % 4, word L % 2)
   const bool zlane = !MX && ZP && lane >= 32 && lane < 40;
   const uint32_t szstride = zlane ? 8 : 32;
-  auto make_copy = [&](const BigTile& t, const int32_t (&pr)[NX]) __attribute__((always_inline)) -> Copy {
+  auto make_copy = [&](const BigTile& t, const int32_t (&pr)[NPR]) __attribute__((always_inline)) -> Copy {
     Copy c;
     c.rx = make_rsrc(reinterpret_cast<const uint8_t*>(a.x) + t.m0 * row_bytes,
                      GROUPED ? 0xFFFFFFFFull : (uint64_t)t.rows * row_bytes);
@@ -281,10 +289,22 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
     c.rw = make_rsrc(a.w + (wb + t.nb0) * G.KG * 1024, (uint64_t)kBigCB * G.KG * 1024);
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
-      const int r = 8 * (NX * wave + i) + (lane >> 3);
+      // MXFP4 rows (64 bytes a step): 16 rows a copy, lane L row 16 j + L / 4,
+      // chunk slot L % 4; else 8 rows a copy, lane L row 8 j + L / 8, slot L % 8
+      const int r = A4 ? 16 * (NX * wave + i) + (lane >> 2) : 8 * (NX * wave + i) + (lane >> 3);
       // dense rows past the tile's end lie outside the buffer: zeros, no memory traffic
       const int64_t src = GROUPED ? act_row(pr[i]) : (r < t.rows ? r : t.rows);
-      c.xoff[i] = (uint32_t)(src * row_bytes) + 16 * ((lane & 7) ^ ((r >> 1) & 7));
+      c.xoff[i] = (uint32_t)(src * row_bytes) +
+                  (A4 ? 16 * ((lane & 3) ^ ((r >> 2) & 3)) : 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+    }
+    if (A4) {
+      // the rows' E8M0 bytes (K / 32 per row, one 4-byte word per K step):
+      // lanes L and L + 32 of wave w copy the word of row 32 w + L % 32
+      const int64_t kb = G.K / 32;
+      c.rxs = make_rsrc(a.xsb + (GROUPED ? 0 : t.m0 * kb), GROUPED ? 0xFFFFFFFFull : (uint64_t)t.rows * kb);
+      const int r = 32 * wave + (lane & 31);
+      const int64_t src = GROUPED ? act_row(pr[NX]) : (r < t.rows ? r : t.rows);
+      c.xso = (uint32_t)(src * kb);
     }
 #pragma unroll
     for (int k = 0; k < NWT; ++k) {
@@ -303,9 +323,11 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
     return c;
   };
   // grouped: this thread's copy rows of tile t, and its row of the tables
-  auto load_rows = [&](const BigTile& t, int32_t (&pr)[NX], int32_t& tp) __attribute__((always_inline)) {
+  auto load_rows = [&](const BigTile& t, int32_t (&pr)[NPR], int32_t& tp) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NX; ++i) pr[i] = pair_of(t, 8 * (NX * wave + i) + (lane >> 3));
+    for (int i = 0; i < NX; ++i)
+      pr[i] = pair_of(t, A4 ? 16 * (NX * wave + i) + (lane >> 2) : 8 * (NX * wave + i) + (lane >> 3));
+    if (A4) pr[NPR - 1] = pair_of(t, 32 * wave + (lane & 31));
     tp = (tid < t.rows) ? a.sorted_pairs[t.first + tid] : -1;
   };
   auto write_table = [&](int32_t tp) __attribute__((always_inline)) {
@@ -326,7 +348,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
   };
   auto copy_x = [&](const Copy& c, int ls, uint8_t* stg) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NX; ++i) b2lds16(c.rx, c.xoff[i], (uint32_t)(ls * 128), stg + (NX * wave + i) * 1024);
+    for (int i = 0; i < NX; ++i) b2lds16(c.rx, c.xoff[i], (uint32_t)(ls * XSTEP), stg + (NX * wave + i) * 1024);
   };
   auto wait_barrier = [&](auto n_c) __attribute__((always_inline)) {
     // wait for this wave's copies except the n most recent vector-memory
@@ -374,7 +396,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
   };
 
   BigTile cur = decode(item);
-  int32_t pr[NX] = {}, tp = -1;
+  int32_t pr[NPR] = {}, tp = -1;
   if (GROUPED) load_rows(cur, pr, tp);
   Copy cc = make_copy(cur, pr);
   bool first = true;
@@ -385,26 +407,33 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
     // columns 128 (w >> 2) + 0..127 (4 x 8 blocks of 16 x 16, 128
     // accumulators per lane)
     const int wm = wave & 3, wn = wave >> 2;
-    // operand rows 16 rb + n_l: K chunks q_l and 4 + q_l (16 fp8 each)
+    // stage layout: activations (kXB bytes), weight tiles at kWO, their
+    // scale words at kSO, MXFP4 rows: the rows' E8M0 words at kAO (256 B per
+    // wave, rows 32 w + 0..31 twice)
+    constexpr int kXB = A4 ? 16 * 1024 : 32 * 1024, kWO = kXB, kSO = kXB + 16 * 1024, kAO = kSO + 4 * 1024;
+    // operand rows 16 rb + n_l: K chunks q_l and 4 + q_l (16 fp8 each); MXFP4
+    // rows: chunk q_l (32 E2M1 values), slot q_l ^ ((n_l >> 2) & 3)
     const int xsw = (n_l >> 1) & 7;
-    const uint32_t xo0 = n_l * 128 + 16 * (q_l ^ xsw), xo1 = n_l * 128 + 16 * ((4 + q_l) ^ xsw);
+    const uint32_t xo0 = A4 ? n_l * 64 + 16 * (q_l ^ ((n_l >> 2) & 3)) : n_l * 128 + 16 * (q_l ^ xsw);
+    const uint32_t xo1 = n_l * 128 + 16 * ((4 + q_l) ^ xsw);
     // copies of one stage: activations, weight tiles (column blocks w and
-    // w + 8) and their scale words
+    // w + 8) and their scale words, [the rows' scale words]
     auto copy_stage = [&](const Copy& c, int ls, uint8_t* st) __attribute__((always_inline)) {
       copy_x(c, ls, st);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int cb = wave + 8 * k;
-        b2lds16(c.rw, c.wvo[k], (uint32_t)(ls * 1024), st + 32 * 1024 + cb * 1024);
-        b2lds4(rsz, c.svo[k], (uint32_t)((ls / 4) * 256), st + 48 * 1024 + cb * 256);
+        b2lds16(c.rw, c.wvo[k], (uint32_t)(ls * 1024), st + kWO + cb * 1024);
+        b2lds4(rsz, c.svo[k], (uint32_t)((ls / 4) * 256), st + kSO + cb * 256);
       }
+      if (A4) b2lds4(c.rxs, c.xso, (uint32_t)(ls * 4), st + kAO + wave * 256);
     };
-    constexpr int kPer = 8;                         // copies per wave per stage
+    constexpr int kPer = A4 ? 7 : 8;                // copies per wave per stage
     while (true) {
       const int64_t nitem = item + gridDim.x;
       const bool has_next = nitem < n_items;
       const BigTile nxt = has_next ? decode(nitem) : cur;
-      int32_t prn[NX] = {}, tpn = -1;
+      int32_t prn[NPR] = {}, tpn = -1;
       if (!chained || first) {
         // stand-alone start: earlier copies and stores done, all waves past
         // the previous epilogue
@@ -451,21 +480,24 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
         uint8_t* d2 = lds + so[2];
         auto dma = [&](int q) __attribute__((always_inline)) {
           const Copy& c = xnext ? nc : cc;
-          if (q < 4) {
-            b2lds16(c.rx, c.xoff[q], (uint32_t)(ls * 128), d2 + (4 * wave + q) * 1024);
-          } else {
-            const int k = (q - 4) >> 1, cb = wave + 8 * k;
-            if ((q & 1) == 0) b2lds16(c.rw, c.wvo[k], (uint32_t)(ls * 1024), d2 + 32 * 1024 + cb * 1024);
-            else b2lds4(rsz, c.svo[k], (uint32_t)((ls / 4) * 256), d2 + 48 * 1024 + cb * 256);
+          if (q < NX) {
+            b2lds16(c.rx, c.xoff[q], (uint32_t)(ls * XSTEP), d2 + (NX * wave + q) * 1024);
+          } else if (q < NX + 4) {
+            const int k = (q - NX) >> 1, cb = wave + 8 * k;
+            if (((q - NX) & 1) == 0) b2lds16(c.rw, c.wvo[k], (uint32_t)(ls * 1024), d2 + kWO + cb * 1024);
+            else b2lds4(rsz, c.svo[k], (uint32_t)((ls / 4) * 256), d2 + kSO + cb * 256);
+          } else if (A4) {
+            b2lds4(c.rxs, c.xso, (uint32_t)(ls * 4), d2 + kAO + wave * 256);
           }
         };
         // operands: the wave's eight weight tiles and their scales (kept for
         // the step), activation halves of one row block at a time, read one
         // row block ahead
         const int sh = 8 * (s & 3);
-        const uint8_t* wbase = st + 32 * 1024 + wn * 8 * 1024 + lane * 16;
-        const uint8_t* sbase = st + 48 * 1024 + wn * 8 * 256 + lane * 4;
-        const uint8_t* xbase = st + wm * 4 * 2048;
+        const uint8_t* wbase = st + kWO + wn * 8 * 1024 + lane * 16;
+        const uint8_t* sbase = st + kSO + wn * 8 * 256 + lane * 4;
+        constexpr int XRB = A4 ? 1024 : 2048;         // bytes of one 16-row block of the stage
+        const uint8_t* xbase = st + wm * 4 * XRB;
         u32x4_t wq[8];
         int wsc[8];
 #pragma unroll
@@ -473,20 +505,31 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
           wq[j] = ld16(wbase + j * 1024);
           wsc[j] = (int)((*reinterpret_cast<const uint32_t*>(sbase + j * 256) >> sh) & 0xFF);
         }
+        // MXFP4 rows: the E8M0 byte of row 64 wm + 16 i + n_l and K block q_l
+        // (word of row r at kAO + (r / 32) 256 + (r % 32) 4)
+        int xsc[4] = {127, 127, 127, 127};
+        if (A4) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            xsc[i] = (int)((*reinterpret_cast<const uint32_t*>(st + kAO + (2 * wm + (i >> 1)) * 256 +
+                                                                 (16 * (i & 1) + n_l) * 4) >>
+                            (8 * q_l)) & 0xFF);
+        }
         u32x4_t b0[2], b1[2];
         b0[0] = ld16(xbase + xo0);
-        b1[0] = ld16(xbase + xo1);
+        if (!A4) b1[0] = ld16(xbase + xo1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (i + 1 < 4) {
-            b0[(i + 1) & 1] = ld16(xbase + (i + 1) * 2048 + xo0);
-            b1[(i + 1) & 1] = ld16(xbase + (i + 1) * 2048 + xo1);
+            b0[(i + 1) & 1] = ld16(xbase + (i + 1) * XRB + xo0);
+            if (!A4) b1[(i + 1) & 1] = ld16(xbase + (i + 1) * XRB + xo1);
           }
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            acc[j][i] = mfma_fp4_fp8(wq[j], b0[i & 1], b1[i & 1], acc[j][i], wsc[j], 127);
+            if (A4) acc[j][i] = mfma_fp4_fp4(wq[j], b0[i & 1], acc[j][i], wsc[j], xsc[i]);
+            else acc[j][i] = mfma_fp4_fp8(wq[j], b0[i & 1], b1[i & 1], acc[j][i], wsc[j], 127);
             if ((j & 3) == 3) {
-              dma(2 * i + (j >> 2));
+              if (2 * i + (j >> 2) < kPer) dma(2 * i + (j >> 2));
               __builtin_amdgcn_sched_barrier(0);
             }
           }
@@ -504,7 +547,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
       for (int i = 0; i < 4; ++i) {
         int64_t row, arow;
         local_row(cur, (wm * 4 + i) * 16 + n_l, row, arow);
-        rs[i] = a.xs[arow];
+        rs[i] = A4 ? 1.0f : a.xs[arow];              // MXFP4 rows: scaled inside the MFMA
       }
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       uint8_t* ost = lds + so[2];                    // the last step's stage
@@ -603,7 +646,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
       const int64_t nitem = item + gridDim.x;
       const bool has_next = nitem < n_items;
       const BigTile nxt = has_next ? decode(nitem) : cur;
-      int32_t prn[NX] = {}, tpn = -1;
+      int32_t prn[NPR] = {}, tpn = -1;
       if (!chained || first) {
         // stand-alone start: weights of steps 0, 1, 2 and activations of
         // steps 0, 1, then operands 0..2 of step 0
@@ -703,11 +746,11 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
 // it; W4A16 only (the half tiles compute four of the eight row blocks), and
 // not where the second half of a last tile row would be empty.
 
-template <bool MX, bool ZP, bool GROUPED>
+template <bool MX, bool ZP, bool GROUPED, bool A4 = false>
 static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
-  auto kern = &k_gemm_big<MX, ZP, GROUPED>;
+  auto kern = &k_gemm_big<MX, ZP, GROUPED, A4>;
   static const hipError_t attr_err = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, big_lds_bytes(MX));
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, big_lds_bytes(MX, A4));
   if (attr_err != hipSuccess) return attr_err;
   const int tiles_n = (int)((a.G.NB + kBigCB - 1) / kBigCB);
   const int tiles_m = GROUPED ? 0 : (int)((a.M + kBigM - 1) / kBigM);
@@ -718,18 +761,20 @@ static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
   const int64_t items = GROUPED ? 0 : 2 * tiles - n_full;
   const unsigned grid = GROUPED ? (unsigned)(grid_items > 0 ? grid_items : 1)
                                 : (unsigned)(items <= kBigGrid ? items : kBigGrid);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(big_threads(MX)), big_lds_bytes(MX), st, a, tiles_n, tiles_m,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(big_threads(MX)), big_lds_bytes(MX, A4), st, a, tiles_n, tiles_m,
                      n_full);
   return hipGetLastError();
 }
 
 
 hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
-  // MX weights with bf16 rows run on the streaming, 128 x 64 and 128 x 128 kernels only
-  if (kmode_of(a) == KM_MX_A16 || kmode_of(a) == KM_MXI4_A16 || kmode_of(a) == KM_MX_A4 || kmode_of(a) == KM_INT8_A16)
+  // MX weights with bf16 rows and INT8 weights run on the streaming, 128 x 64 and 128 x 128 kernels only
+  if (kmode_of(a) == KM_MX_A16 || kmode_of(a) == KM_MXI4_A16 || kmode_of(a) == KM_INT8_A16)
     return hipErrorInvalidValue;
   // scale and zero-point copies use 32-bit offsets from the scale region
   if (a.G.total - a.G.off_scales > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  if (kmode_of(a) == KM_MX_A4)
+    return grouped ? go_big<true, false, true, true>(a, grid_items, st) : go_big<true, false, false, true>(a, 0, st);
   if (a.wfmt == W_MXFP4)
     return grouped ? go_big<true, false, true>(a, grid_items, st) : go_big<true, false, false>(a, 0, st);
   if (a.wfmt == W_UINT4_ZP)

@@ -64,12 +64,12 @@ class Layer:
 
 
 @pytest.mark.parametrize("n,k", [(200, 384), (37, 128), (1000, 1152)])
-@pytest.mark.parametrize("m", [1, 7, 16, 17, 32, 33, 100, 129, 257])
+@pytest.mark.parametrize("m", [1, 7, 16, 17, 32, 33, 100, 129, 257, 513, 700])
 def test_w4a4_ragged_default_path(n, k, m):
     Layer(n, k, seed=n + k).check(_rows(m, k, m))
 
 
-@pytest.mark.parametrize("m,path", [(1, 4), (40, 4), (200, 1), (7, 1)])
+@pytest.mark.parametrize("m,path", [(1, 4), (40, 4), (200, 1), (7, 1), (1, 3), (300, 3), (600, 3)])
 def test_w4a4_forced_paths(m, path):
     Layer(264, 640, seed=3).check(_rows(m, 640, m), tuning=dict(path=path))
 
@@ -99,19 +99,23 @@ def test_w4a4_workload_shape_m4096_sampled(wide):
 def test_w4a4_rejects_other_kernels_and_weights():
     import quantized_gemm_int4_amd as hm
     d = hm.wdesc("mxfp4", 7168, 2048)
-    for path in (2, 3):
-        with pytest.raises(hm.HmError) as e:
-            hm.hm_gemm_plan(d, hm.HM_A_MXFP4, 256, dict(path=path))
-        assert e.value.code == 8
+    with pytest.raises(hm.HmError) as e:
+        hm.hm_gemm_plan(d, hm.HM_A_MXFP4, 256, dict(path=2))
+    assert e.value.code == 8
+    assert "256x256" in hm.hm_gemm_plan(d, hm.HM_A_MXFP4, 256, dict(path=3))
+    assert "256x256" in hm.hm_gemm_plan(d, hm.HM_A_MXFP4, 4096)
+    assert "fp4xfp4" in hm.hm_gemm_plan(d, hm.HM_A_MXFP4, 4096)
     with pytest.raises(hm.HmError) as e:
         hm.hm_gemm_plan(hm.wdesc("int4_sym", 256, 512), hm.HM_A_MXFP4, 16)
     assert e.value.code == 4
 
 
 @pytest.mark.parametrize("rows_are_pairs", [0, 1])
-def test_w4a4_grouped_mixed_units(rows_are_pairs):
+@pytest.mark.parametrize("big", [0, -1])
+def test_w4a4_grouped_mixed_units(rows_are_pairs, big):
     """A grouped W4A4 call: small experts on streaming units, large ones on
-    128-row units of the 128 x 128 kernel (no 256-row units for W4A4)."""
+    256-row units (big = 0, the default) and on 128-row units of the 128 x
+    128 kernel (big = -1: no 256-row units)."""
     import quantized_gemm_int4_amd as hm
     t, topk, E, n, k = 150, 2, 8, 208, 384
     r = np.random.default_rng(1)
@@ -124,9 +128,13 @@ def test_w4a4_grouped_mixed_units(rows_are_pairs):
     xb = _rows(t * topk if rows_are_pairs else t, k, 5)
     c, s = hm.hm_quant_mxfp4_rows(bf16_to_dev(xb))
     _, off, sp = hm.hm_moe_sort(to_dev(ids), E)
-    plan = hm.hm_moe_gemm_plan(d, hm.HM_A_MXFP4, t, topk, rows_are_pairs)
-    assert "k_gemm_tile" in plan and "big(256 rows)=none" in plan, plan
-    y = hm.hm_moe_gemm(d, w, c, off, sp, t, topk, rows_are_pairs, a_scales=s)
+    tuning = dict(moe_big_min=big) if big else None
+    plan = hm.hm_moe_gemm_plan(d, hm.HM_A_MXFP4, t, topk, rows_are_pairs, tuning)
+    assert "k_gemm_tile" in plan, plan
+    assert ("big(256 rows)=none" in plan) == (big == -1), plan
+    counts = np.bincount(ids.ravel(), minlength=E)
+    assert counts.max() >= 97                                # a 256-row unit by default
+    y = hm.hm_moe_gemm(d, w, c, off, sp, t, topk, rows_are_pairs, a_scales=s, tuning=tuning)
     torch.cuda.synchronize()
     rc, rs = quant.quant_mxfp4_rows(xb)
     yref, b, _ = moe.moe_gemm_ref(quant.mxfp4_rows_dequant(rc, rs), bool(rows_are_pairs), topk, ids,
