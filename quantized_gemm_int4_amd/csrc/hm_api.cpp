@@ -157,10 +157,11 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   const bool a4 = afmt == HM_A_MXFP4;
   const bool tiles32 = scales_addr32(G);        // 128-row and 256-row kernels can address the scales
   if (tu.path == P_STREAM && m > kStreamWideRows) return HM_ERR_TUNING;
-  // W4A4 and INT8 weights have no 128-row tile kernel; MX weights with bf16
+  // W4A4 and INT8 weights have no 128-row tile kernel; MXINT4 with bf16
   // rows and INT8 weights no 256 x 256 kernel
   const bool int8 = d->wfmt == HM_W_INT8_SYM;
-  const bool no_mid = a4 || int8, no_big = f4 || int8;
+  const bool mxi4 = d->wfmt == HM_W_MXINT4;
+  const bool no_mid = a4 || int8, no_big = mxi4 || int8;
   if ((no_mid && tu.path == P_MID) || (no_big && tu.path == P_BIG)) return HM_ERR_TUNING;
   if ((tu.path == P_MID || tu.path == P_BIG) && (!tiles32 || !mid_grid_fits(G, a8, m))) return HM_ERR_TUNING;
   // W4A16 up to 256 rows also streams (in 32-row chunks, each re-reading the
@@ -179,8 +180,21 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   } else if (a4) {
     // W4A4: 256 x 256 tiles from kBigMinRows rows, else 128 x 128
     p.path = m >= kBigMinRows ? P_BIG : P_TILE;
+  } else if (f4 && !mxi4) {
+    // MXFP4 with bf16 rows: the kernel with the least estimated time, from
+    // the measured cost of one round of the chip of each kernel's tiles in
+    // rounds of 128 x 64 tiles: 128 x 128 tiles 1.7, 256 x 256 tiles 4.4
+    // (N = 7168 K = 2048 and N = 14336 K = 4096, M = 256 .. 4096: M = 1024,
+    // N = 7168 45.8 us on 128 x 128 tiles against 53.5 / 57.3; N = 14336
+    // 114 us on 256 x 256 tiles against 162 / 154; M = 4096 410 us against
+    // 1038 / 516)
+    const int64_t mt = (m + kTileM - 1) / kTileM, bt = (m + kBigRows - 1) / kBigRows;
+    const int64_t c_mid = 10 * ((mid_n_tiles(G, false) * mt + 255) / 256);
+    const int64_t c_tile = 17 * ((((G.NB + 7) / 8) * mt + 255) / 256);
+    const int64_t c_big = 44 * ((big_n_tiles(G) * bt + 255) / 256);
+    p.path = (c_big < c_mid && c_big < c_tile) ? P_BIG : (c_tile < c_mid ? P_TILE : P_MID);
   } else if (f4) {
-    // MX weights with bf16 rows (no 256 x 256 kernel): 128 x 64 tiles, or 128 x
+    // MXINT4 with bf16 rows (no 256 x 256 kernel): 128 x 64 tiles, or 128 x
     // 128 tiles once the 128 x 64 ones take many rounds of the chip.
     // Measured at N = 7168 K = 2048 / N = 14336 K = 4096: M = 256 / 128 on
     // 128 x 64 tiles 14.9 / 23.9 us against 30.1 / 63.2 (one round each),
@@ -195,7 +209,7 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
     // the smaller tiles
     const int64_t big_rounds = (big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows) + 255) / 256;
     const int64_t mid_rounds = (mid_n_tiles(G, false) * ((m + kTileM - 1) / kTileM) + 255) / 256;
-    const bool mid_fewer = !is_mx(d->wfmt) && mid_rounds * 10 < big_rounds * 38;
+    const bool mid_fewer = (!is_mx(d->wfmt) || f4) && mid_rounds * 10 < big_rounds * 38;
     p.path = (m >= kBigMinRows && !mid_fewer) ? P_BIG : P_MID;
   }
   // kernels with 32-bit offsets fall back to the 128 x 128 kernel (64-bit addressing)
@@ -335,7 +349,7 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
     // activation rows and scales with 32-bit offsets
     const bool int8 = d->wfmt == HM_W_INT8_SYM;
     const bool tile_only = a4 || int8;                       // no 128-row tile kernel
-    const bool big_ok = !f4 && !int8 && !p.a64 && tiles32;   // W4A4 has 256-row units
+    const bool big_ok = !mxi4 && !int8 && !p.a64 && tiles32;   // W4A4 and MXFP4-bf16 have 256-row units
     if (tu.mbig > 0 && !big_ok) return HM_ERR_TUNING;
     p.big_min = (tu.mbig == -1 || !big_ok) ? 0 : big_min;
     // up-to-128-row units: the 128-row tile kernel (32-bit offsets), or the
@@ -346,7 +360,7 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
     if (tu.mtile == 1 && !mid_ok) return HM_ERR_TUNING;
     if (tu.mtile == 1) p.tile = P_MID;
     else if (tu.mtile == 2) p.tile = P_TILE;
-    else p.tile = (mid_ok && !(f4 && f4_wide_tiles(G, p.P))) ? P_MID : P_TILE;
+    else p.tile = (mid_ok && !(f4 && mxi4 && f4_wide_tiles(G, p.P))) ? P_MID : P_TILE;
   }
   *out = p;
   return HM_OK;
@@ -579,11 +593,11 @@ HM_API hm_status hm_gemm_plan(const hm_wdesc* d, int32_t afmt, int64_t m, const 
   else if (p.path == P_BIG) {
     const Geom G = make_geom(device_fmt(d->wfmt), 1, d->n, d->k);
     const int64_t tiles = big_n_tiles(G) * ((m + kBigRows - 1) / kBigRows);
-    const int64_t halves = 2 * (tiles - big_full_tiles(G, m, d->wfmt == HM_W_MXFP4));
-    snprintf(buf, buf_len, "%s tile 256x256 waves=%s mfma=%s half_tiles=%lld", w,
-             d->wfmt == HM_W_MXFP4 ? "4x2" : "1x4",
+    const bool mxk = afmt != HM_A_BF16;       // the scaled-MFMA path of the kernel
+    const int64_t halves = 2 * (tiles - big_full_tiles(G, m, mxk));
+    snprintf(buf, buf_len, "%s tile 256x256 waves=%s mfma=%s half_tiles=%lld", w, mxk ? "4x2" : "1x4",
              afmt == HM_A_MXFP4 ? "scale_16x16x128_f8f6f4_fp4xfp4"
-                                : (d->wfmt == HM_W_MXFP4 ? "scale_16x16x128_f8f6f4" : "32x32x16_bf16"),
+                                : (mxk ? "scale_16x16x128_f8f6f4" : "32x32x16_bf16"),
              (long long)halves);
   }
   else if (p.path == P_MID && a8)

@@ -140,14 +140,20 @@ _Pragma("nounroll")                                                             
               else                                                                                                  \
                 b2lds16(r, wnext ? nc.wvo[2 + k0] : cc.wvo[2 + k0], (uint32_t)(wg * 1024),                          \
                         dw + kWOff + (NWT * wave + 2 + k0) * 1024);                                                 \
+            } else if (F4) {                                                                                        \
+              b2lds16(rsz, (wnext ? nc.svo[0] : cc.svo[0]) + (uint32_t)(wg >> 2) * 256, 0u,                         \
+                      dw + kSOff + wave * 1024);                                                                    \
             } else {                                                                                                \
               b2lds4(rsz, (wnext ? nc.svo[0] : cc.svo[0]) + (uint32_t)wg * szstride, 0u, dw + kSOff + wave * 256);  \
             }                                                                                                       \
           };                                                                                                        \
           const uint8_t* xs = lds + so[0];                                                                          \
           uint32_t wv[2][4];                                                                                        \
-          float svn[2], zsn[2];                                                                                     \
-          fetch(lds + ((s & 1) ? wso[1] : wso[0]), (s + 1) & 1, wv, svn, zsn);                                      \
+          float svn[2], zsn[2], sfn[2][2];                                                                          \
+          if (F4)                                                                                                   \
+            fetch_f4(lds + ((s & 1) ? wso[1] : wso[0]), (s + 1) & 1, (s + 1 < S ? (s + 1) >> 1 : 0) & 3, wv, sfn); \
+          else                                                                                                      \
+            fetch(lds + ((s & 1) ? wso[1] : wso[0]), (s + 1) & 1, wv, svn, zsn);                                    \
           u32x4_t b[NI];                                                                                            \
 _Pragma("unroll")                                                                                                   \
           for (int i = 0; i < kD; ++i) b[i] = ld16(xs + (i % MB) * 4096 + xo[i / MB]);                              \
@@ -165,12 +171,17 @@ _Pragma("unroll")                                                               
             for (int e = 0; e < WPI; ++e) {                                                                         \
               const int wi = WPI * i + e, nb2 = (wi >> 2) & 1, u = wi & 3;                                          \
               const uint32_t w = kq == 0 ? w3c[nb2] : wv[nb2][kq - 1];                                              \
-              const float sv = kq == 0 ? sv3c[nb2] : svn[nb2], zs = kq == 0 ? zs3c[nb2] : zsn[nb2];                 \
-              if (u == 0) {                                                                                         \
-                lo = in_vgpr(w & 0x0F0F0F0Fu);                                                                      \
-                hi4 = in_vgpr((w >> 4) & 0x0F0F0F0Fu);                                                              \
+              if (F4) {                                                                                             \
+                const float sf = kq == 0 ? sv3c[nb2] : sfn[nb2][(kq - 1) >> 1];                                     \
+                af[nb2][(kq + 3) & 3][u] = fp4x2_bf16(w, sf, u);                                                    \
+              } else {                                                                                              \
+                const float sv = kq == 0 ? sv3c[nb2] : svn[nb2], zs = kq == 0 ? zs3c[nb2] : zsn[nb2];               \
+                if (u == 0) {                                                                                       \
+                  lo = in_vgpr(w & 0x0F0F0F0Fu);                                                                    \
+                  hi4 = in_vgpr((w >> 4) & 0x0F0F0F0Fu);                                                            \
+                }                                                                                                   \
+                af[nb2][(kq + 3) & 3][u] = dq8_word(lo, hi4, u, sv, zs);                                            \
               }                                                                                                     \
-              af[nb2][(kq + 3) & 3][u] = dq8_word(lo, hi4, u, sv, zs);                                              \
             }                                                                                                       \
             if (MB == 8) {                                                                                          \
               if ((i & 1) && (i >> 1) < kPer) dma(i >> 1);                                                          \
@@ -182,8 +193,8 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                                   \
           for (int nb2 = 0; nb2 < 2; ++nb2) {                                                                       \
             w3c[nb2] = wv[nb2][3];                                                                                  \
-            sv3c[nb2] = svn[nb2];                                                                                   \
-            zs3c[nb2] = zsn[nb2];                                                                                   \
+            sv3c[nb2] = F4 ? sfn[nb2][1] : svn[nb2];                                                                \
+            zs3c[nb2] = F4 ? 0.f : zsn[nb2];                                                                        \
           }                                                                                                         \
           wait_barrier(std::integral_constant<int, kPer>());                                                        \
           rotate();                                                                                                 \
@@ -191,11 +202,12 @@ _Pragma("unroll")                                                               
         }                                                                                                           \
   } while (0)
 
-template <bool MX, bool ZP, bool GROUPED, bool A4 = false>
+template <bool MX, bool ZP, bool GROUPED, bool A4 = false, bool F4 = false>
 __global__ void __launch_bounds__(big_threads(MX), 1)
 k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
   static_assert(!A4 || MX, "MXFP4 rows go with MXFP4 weights");
-  constexpr int SB = big_stage_bytes(MX, A4);
+  static_assert(!F4 || (!MX && !ZP), "MXFP4 weights with bf16 rows take the bf16 path");
+  constexpr int SB = big_stage_bytes(MX || F4, A4);
   constexpr int NW = big_threads(MX) / 64;         // waves
   constexpr int NX = A4 ? 2 : 32 / NW;             // activation copies per lane per step
   constexpr int NPR = A4 ? NX + 1 : NX;            // grouped: pair rows a thread's copies read
@@ -313,7 +325,14 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
       c.wvo[k] = (uint32_t)((nb - t.nb0) * G.KG * 1024 + lane * 16);
       if (MX) c.svo[k & 1] = (uint32_t)((wb + nb) * G.KG4 * 256 + lane * 4);
     }
-    if (!MX) {
+    if (F4) {
+      // MXFP4 with bf16 rows: lane L copies 16 bytes (four lanes' E8M0
+      // words) of the word array of column block 4 w + L / 16
+      c.svo[1] = 0u;
+      int64_t nbq = t.nb0 + NWT * wave + (lane >> 4);
+      if (nbq >= G.NB) nbq = G.NB - 1;
+      c.svo[0] = (uint32_t)((wb + nbq) * G.KG4 * 256 + (lane & 15) * 16);
+    } else if (!MX) {
       c.svo[1] = 0u;
       int64_t nbq = t.nb0 + NWT * wave + (zlane ? ((lane >> 1) & 3) : ((lane >> 3) & 3));
       if (nbq >= G.NB) nbq = G.NB - 1;
@@ -607,12 +626,15 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
       wso[1] = wso[2];
       wso[2] = t;
     };
-    // all four tiles of group g and the gather
+    // all four tiles of group g and the gather (MXFP4 weights: the E8M0 word
+    // arrays of the four column blocks for groups 4 (g / 4) .. + 3, 1 KiB per
+    // wave at kSOff + 1024 w)
     auto copy_w = [&](const Copy& c, int g, uint8_t* slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < NWT; ++k)
         b2lds16(c.rw, c.wvo[k], (uint32_t)(g * 1024), slot + kWOff + (NWT * wave + k) * 1024);
-      b2lds4(rsz, c.svo[0] + (uint32_t)g * szstride, 0u, slot + kSOff + wave * 256);
+      if (F4) b2lds16(rsz, c.svo[0] + (uint32_t)(g >> 2) * 256, 0u, slot + kSOff + wave * 1024);
+      else b2lds4(rsz, c.svo[0] + (uint32_t)g * szstride, 0u, slot + kSOff + wave * 256);
     };
     constexpr int kPer = NX + 2 + 1;                // copies per wave per step
     // A operands of one step: column half nb2, K part kq.  Lane row n =
@@ -639,6 +661,26 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
         zs[nb2] = -z * sv[nb2];
       }
     };
+    // MXFP4 weights with bf16 rows: K = 64 h + 16 kq + 8 hi (the same K run
+    // of the lane as for INT4, so the activation side is unchanged) is word
+    // 2 (kq % 2) + hi of slot (l32 % 16) + 16 (2 h + kq / 2), scaled by the
+    // E8M0 byte gsel of that slot's word (groups 4 (g / 4) + gsel)
+    auto fetch_f4 = [&](const uint8_t* stg, int h, int gsel, uint32_t (&wv)[2][4], float (&sf)[2][2])
+        __attribute__((always_inline)) {
+      const uint8_t* sz = stg + kSOff + wave * 1024;
+#pragma unroll
+      for (int nb2 = 0; nb2 < 2; ++nb2) {
+        const int t4 = 2 * nb2 + c_l;
+        const uint8_t* tile = stg + kWOff + (NWT * wave + t4) * 1024;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int slot = c16 + 16 * (2 * h + kh);
+          wv[nb2][2 * kh] = *reinterpret_cast<const uint32_t*>(tile + slot * 16 + 4 * hi);
+          wv[nb2][2 * kh + 1] = *reinterpret_cast<const uint32_t*>(tile + slot * 16 + 8 + 4 * hi);
+          sf[nb2][kh] = e8m0_f32((*reinterpret_cast<const uint32_t*>(sz + t4 * 256 + slot * 4) >> (8 * gsel)) & 0xFFu);
+        }
+      }
+    };
     u32x4_t af[2][4];
     uint32_t w3c[2] = {0u, 0u};                     // code words of operands (nb2, 3), their scales and offsets
     float sv3c[2] = {0.f, 0.f}, zs3c[2] = {0.f, 0.f};
@@ -663,13 +705,26 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
         copy_x(cc, std::min(1, S - 1), lds + so[1]);
         wait_barrier(std::integral_constant<int, 0>());
         uint32_t wv[2][4];
-        fetch(lds + wso[0], 0, wv, sv3c, zs3c);
+        if (F4) {
+          float sf[2][2];
+          fetch_f4(lds + wso[0], 0, 0, wv, sf);
 #pragma unroll
-        for (int nb2 = 0; nb2 < 2; ++nb2) {
+          for (int nb2 = 0; nb2 < 2; ++nb2) {
 #pragma unroll
-          for (int kq = 0; kq < 3; ++kq) af[nb2][kq] = dq8_bytes(wv[nb2][kq], sv3c[nb2], zs3c[nb2]);
-          af[nb2][3] = (u32x4_t){0u, 0u, 0u, 0u};
-          w3c[nb2] = wv[nb2][3];
+            for (int kq = 0; kq < 3; ++kq) af[nb2][kq] = fp4x8_bf16(wv[nb2][kq], sf[nb2][kq >> 1]);
+            af[nb2][3] = (u32x4_t){0u, 0u, 0u, 0u};
+            w3c[nb2] = wv[nb2][3];
+            sv3c[nb2] = sf[nb2][1];
+          }
+        } else {
+          fetch(lds + wso[0], 0, wv, sv3c, zs3c);
+#pragma unroll
+          for (int nb2 = 0; nb2 < 2; ++nb2) {
+#pragma unroll
+            for (int kq = 0; kq < 3; ++kq) af[nb2][kq] = dq8_bytes(wv[nb2][kq], sv3c[nb2], zs3c[nb2]);
+            af[nb2][3] = (u32x4_t){0u, 0u, 0u, 0u};
+            w3c[nb2] = wv[nb2][3];
+          }
         }
       }
       if (GROUPED && chained && has_next) load_rows(nxt, prn, tpn);
@@ -746,11 +801,11 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
 // it; W4A16 only (the half tiles compute four of the eight row blocks), and
 // not where the second half of a last tile row would be empty.
 
-template <bool MX, bool ZP, bool GROUPED, bool A4 = false>
+template <bool MX, bool ZP, bool GROUPED, bool A4 = false, bool F4 = false>
 static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
-  auto kern = &k_gemm_big<MX, ZP, GROUPED, A4>;
+  auto kern = &k_gemm_big<MX, ZP, GROUPED, A4, F4>;
   static const hipError_t attr_err = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, big_lds_bytes(MX, A4));
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, big_lds_bytes(MX || F4, A4));
   if (attr_err != hipSuccess) return attr_err;
   const int tiles_n = (int)((a.G.NB + kBigCB - 1) / kBigCB);
   const int tiles_m = GROUPED ? 0 : (int)((a.M + kBigM - 1) / kBigM);
@@ -761,20 +816,22 @@ static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
   const int64_t items = GROUPED ? 0 : 2 * tiles - n_full;
   const unsigned grid = GROUPED ? (unsigned)(grid_items > 0 ? grid_items : 1)
                                 : (unsigned)(items <= kBigGrid ? items : kBigGrid);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(big_threads(MX)), big_lds_bytes(MX, A4), st, a, tiles_n, tiles_m,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(big_threads(MX)), big_lds_bytes(MX || F4, A4), st, a, tiles_n, tiles_m,
                      n_full);
   return hipGetLastError();
 }
 
 
 hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
-  // MX weights with bf16 rows and INT8 weights run on the streaming, 128 x 64 and 128 x 128 kernels only
-  if (kmode_of(a) == KM_MX_A16 || kmode_of(a) == KM_MXI4_A16 || kmode_of(a) == KM_INT8_A16)
-    return hipErrorInvalidValue;
+  // MXINT4 and INT8 weights run on the streaming, 128 x 64 and 128 x 128 kernels only
+  if (kmode_of(a) == KM_MXI4_A16 || kmode_of(a) == KM_INT8_A16) return hipErrorInvalidValue;
   // scale and zero-point copies use 32-bit offsets from the scale region
   if (a.G.total - a.G.off_scales > 0xFFFFFFFFull) return hipErrorInvalidValue;
   if (kmode_of(a) == KM_MX_A4)
     return grouped ? go_big<true, false, true, true>(a, grid_items, st) : go_big<true, false, false, true>(a, 0, st);
+  if (kmode_of(a) == KM_MX_A16)
+    return grouped ? go_big<false, false, true, false, true>(a, grid_items, st)
+                   : go_big<false, false, false, false, true>(a, 0, st);
   if (a.wfmt == W_MXFP4)
     return grouped ? go_big<true, false, true>(a, grid_items, st) : go_big<true, false, false>(a, 0, st);
   if (a.wfmt == W_UINT4_ZP)
