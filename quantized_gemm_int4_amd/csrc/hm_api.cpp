@@ -129,15 +129,6 @@ struct DensePlan {
   size_t ws_bytes;
 };
 
-// MX weights with bf16 rows: rows that take the 128 x 128 kernel instead of the
-// 128 x 64 one (at least 8 rounds of 128 x 64 tiles on the 256 compute units)
-bool f4_wide_tiles(const Geom& G, int64_t rows) {
-  const int64_t mt = (rows + kTileM - 1) / kTileM;
-  const int64_t mid_rounds = (mid_n_tiles(G, false) * mt + 255) / 256;
-  const int64_t tile_rounds = (((G.NB + 7) / 8) * mt + 255) / 256;
-  return mid_rounds >= 8 && tile_rounds < mid_rounds;
-}
-
 // one block per tile of the dense 128-row tile kernels (a 32-bit grid)
 bool mid_grid_fits(const Geom& G, bool a8, int64_t m) {
   const int64_t tiles_m = a8 ? (m + 63) / 64 : (m + kTileM - 1) / kTileM;
@@ -157,11 +148,10 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   const bool a4 = afmt == HM_A_MXFP4;
   const bool tiles32 = scales_addr32(G);        // 128-row and 256-row kernels can address the scales
   if (tu.path == P_STREAM && m > kStreamWideRows) return HM_ERR_TUNING;
-  // W4A4 and INT8 weights have no 128-row tile kernel; MXINT4 with bf16
-  // rows and INT8 weights no 256 x 256 kernel
+  // W4A4 and INT8 weights have no 128-row tile kernel, INT8 weights no
+  // 256 x 256 kernel
   const bool int8 = d->wfmt == HM_W_INT8_SYM;
-  const bool mxi4 = d->wfmt == HM_W_MXINT4;
-  const bool no_mid = a4 || int8, no_big = mxi4 || int8;
+  const bool no_mid = a4 || int8, no_big = int8;
   if ((no_mid && tu.path == P_MID) || (no_big && tu.path == P_BIG)) return HM_ERR_TUNING;
   if ((tu.path == P_MID || tu.path == P_BIG) && (!tiles32 || !mid_grid_fits(G, a8, m))) return HM_ERR_TUNING;
   // W4A16 up to 256 rows also streams (in 32-row chunks, each re-reading the
@@ -180,27 +170,21 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   } else if (a4) {
     // W4A4: 256 x 256 tiles from kBigMinRows rows, else 128 x 128
     p.path = m >= kBigMinRows ? P_BIG : P_TILE;
-  } else if (f4 && !mxi4) {
-    // MXFP4 with bf16 rows: the kernel with the least estimated time, from
-    // the measured cost of one round of the chip of each kernel's tiles in
-    // rounds of 128 x 64 tiles: 128 x 128 tiles 1.7, 256 x 256 tiles 4.4
-    // (N = 7168 K = 2048 and N = 14336 K = 4096, M = 256 .. 4096: M = 1024,
-    // N = 7168 45.8 us on 128 x 128 tiles against 53.5 / 57.3; N = 14336
-    // 114 us on 256 x 256 tiles against 162 / 154; M = 4096 410 us against
-    // 1038 / 516)
-    const int64_t mt = (m + kTileM - 1) / kTileM, bt = (m + kBigRows - 1) / kBigRows;
-    const int64_t c_mid = 10 * ((mid_n_tiles(G, false) * mt + 255) / 256);
-    const int64_t c_tile = 17 * ((((G.NB + 7) / 8) * mt + 255) / 256);
-    const int64_t c_big = 44 * ((big_n_tiles(G) * bt + 255) / 256);
-    p.path = (c_big < c_mid && c_big < c_tile) ? P_BIG : (c_tile < c_mid ? P_TILE : P_MID);
   } else if (f4) {
-    // MXINT4 with bf16 rows (no 256 x 256 kernel): 128 x 64 tiles, or 128 x
-    // 128 tiles once the 128 x 64 ones take many rounds of the chip.
-    // Measured at N = 7168 K = 2048 / N = 14336 K = 4096: M = 256 / 128 on
-    // 128 x 64 tiles 14.9 / 23.9 us against 30.1 / 63.2 (one round each),
-    // M = 1024 even (4 / 7 rounds against 2 / 4), M = 4096 147 / 520 us on
-    // 128 x 128 tiles against 273 / 1039 (14 / 28 rounds against 7 / 14)
-    p.path = f4_wide_tiles(G, m) ? P_TILE : P_MID;
+    // MX weights with bf16 rows: the kernel with the least estimated time
+    // (0.1 us per 2048 of K), fitted to MXFP4 and MXINT4 at N = 7168 K = 2048
+    // and N = 14336 K = 4096, M = 256 .. 4096: 128 x 64 tiles 13.4 a round of
+    // the chip, 128 x 128 tiles 17 a round plus 12, 256 x 256 tiles 58 a round
+    // (fractional: the last round's half tiles) and at least one round.
+    // Picks: N = 7168, M = 512 128 x 64 (28.0 us against 34.4 / 55.4), M =
+    // 1024 128 x 128 (45.8 against 53.5 / 57.3), M = 4096 256 x 256 (116.8
+    // against 272.6 / 142.8); N = 14336, M = 512 128 x 128 (83.3 against
+    // 96.8 / 106.4), M = 1024 and 4096 256 x 256 (114.0, 409.8)
+    const int64_t mt = (m + kTileM - 1) / kTileM, bt = (m + kBigRows - 1) / kBigRows;
+    const int64_t c_mid = 134 * ((mid_n_tiles(G, false) * mt + 255) / 256) + 10;
+    const int64_t c_tile = 170 * ((((G.NB + 7) / 8) * mt + 255) / 256) + 120;
+    const int64_t c_big = 580 * std::max<int64_t>(big_n_tiles(G) * bt, 256) / 256;
+    p.path = (c_big < c_mid && c_big < c_tile) ? P_BIG : (c_tile < c_mid ? P_TILE : P_MID);
   } else {
     // 256 x 256 tiles unless 128 x 64 tiles take fewer rounds of the chip by
     // the measured cost of a round (one of 256 x 256 tiles ~ 3.8 of 128 x 64
@@ -349,7 +333,7 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
     // activation rows and scales with 32-bit offsets
     const bool int8 = d->wfmt == HM_W_INT8_SYM;
     const bool tile_only = a4 || int8;                       // no 128-row tile kernel
-    const bool big_ok = !mxi4 && !int8 && !p.a64 && tiles32;   // W4A4 and MXFP4-bf16 have 256-row units
+    const bool big_ok = !int8 && !p.a64 && tiles32;          // INT8 has no 256-row units
     if (tu.mbig > 0 && !big_ok) return HM_ERR_TUNING;
     p.big_min = (tu.mbig == -1 || !big_ok) ? 0 : big_min;
     // up-to-128-row units: the 128-row tile kernel (32-bit offsets), or the
@@ -360,7 +344,7 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
     if (tu.mtile == 1 && !mid_ok) return HM_ERR_TUNING;
     if (tu.mtile == 1) p.tile = P_MID;
     else if (tu.mtile == 2) p.tile = P_TILE;
-    else p.tile = (mid_ok && !(f4 && mxi4 && f4_wide_tiles(G, p.P))) ? P_MID : P_TILE;
+    else p.tile = mid_ok ? P_MID : P_TILE;
   }
   *out = p;
   return HM_OK;

@@ -173,7 +173,7 @@ _Pragma("unroll")                                                               
               const uint32_t w = kq == 0 ? w3c[nb2] : wv[nb2][kq - 1];                                              \
               if (F4) {                                                                                             \
                 const float sf = kq == 0 ? sv3c[nb2] : sfn[nb2][(kq - 1) >> 1];                                     \
-                af[nb2][(kq + 3) & 3][u] = fp4x2_bf16(w, sf, u);                                                    \
+                af[nb2][(kq + 3) & 3][u] = I4 ? i4x2_bf16(w, sf, u) : fp4x2_bf16(w, sf, u);                          \
               } else {                                                                                              \
                 const float sv = kq == 0 ? sv3c[nb2] : svn[nb2], zs = kq == 0 ? zs3c[nb2] : zsn[nb2];               \
                 if (u == 0) {                                                                                       \
@@ -202,11 +202,12 @@ _Pragma("unroll")                                                               
         }                                                                                                           \
   } while (0)
 
-template <bool MX, bool ZP, bool GROUPED, bool A4 = false, bool F4 = false>
+template <bool MX, bool ZP, bool GROUPED, bool A4 = false, bool F4 = false, bool I4 = false>
 __global__ void __launch_bounds__(big_threads(MX), 1)
 k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
   static_assert(!A4 || MX, "MXFP4 rows go with MXFP4 weights");
-  static_assert(!F4 || (!MX && !ZP), "MXFP4 weights with bf16 rows take the bf16 path");
+  static_assert(!F4 || (!MX && !ZP), "MX weights with bf16 rows take the bf16 path");
+  static_assert(!I4 || F4, "MXINT4 codes take the MX bf16-row path");
   constexpr int SB = big_stage_bytes(MX || F4, A4);
   constexpr int NW = big_threads(MX) / 64;         // waves
   constexpr int NX = A4 ? 2 : 32 / NW;             // activation copies per lane per step
@@ -677,7 +678,8 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
           const int slot = c16 + 16 * (2 * h + kh);
           wv[nb2][2 * kh] = *reinterpret_cast<const uint32_t*>(tile + slot * 16 + 4 * hi);
           wv[nb2][2 * kh + 1] = *reinterpret_cast<const uint32_t*>(tile + slot * 16 + 8 + 4 * hi);
-          sf[nb2][kh] = e8m0_f32((*reinterpret_cast<const uint32_t*>(sz + t4 * 256 + slot * 4) >> (8 * gsel)) & 0xFFu);
+          sf[nb2][kh] = e8m0_f32((*reinterpret_cast<const uint32_t*>(sz + t4 * 256 + slot * 4) >> (8 * gsel)) & 0xFFu) *
+                        (I4 ? 0.25f : 1.0f);                   // MXINT4: q / 4
         }
       }
     };
@@ -711,7 +713,8 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
 #pragma unroll
           for (int nb2 = 0; nb2 < 2; ++nb2) {
 #pragma unroll
-            for (int kq = 0; kq < 3; ++kq) af[nb2][kq] = fp4x8_bf16(wv[nb2][kq], sf[nb2][kq >> 1]);
+            for (int kq = 0; kq < 3; ++kq)
+              af[nb2][kq] = I4 ? i4x8_bf16(wv[nb2][kq], sf[nb2][kq >> 1]) : fp4x8_bf16(wv[nb2][kq], sf[nb2][kq >> 1]);
             af[nb2][3] = (u32x4_t){0u, 0u, 0u, 0u};
             w3c[nb2] = wv[nb2][3];
             sv3c[nb2] = sf[nb2][1];
@@ -801,9 +804,9 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
 // it; W4A16 only (the half tiles compute four of the eight row blocks), and
 // not where the second half of a last tile row would be empty.
 
-template <bool MX, bool ZP, bool GROUPED, bool A4 = false, bool F4 = false>
+template <bool MX, bool ZP, bool GROUPED, bool A4 = false, bool F4 = false, bool I4 = false>
 static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
-  auto kern = &k_gemm_big<MX, ZP, GROUPED, A4, F4>;
+  auto kern = &k_gemm_big<MX, ZP, GROUPED, A4, F4, I4>;
   static const hipError_t attr_err = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, big_lds_bytes(MX || F4, A4));
   if (attr_err != hipSuccess) return attr_err;
@@ -823,8 +826,8 @@ static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
 
 
 hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
-  // MXINT4 and INT8 weights run on the streaming, 128 x 64 and 128 x 128 kernels only
-  if (kmode_of(a) == KM_MXI4_A16 || kmode_of(a) == KM_INT8_A16) return hipErrorInvalidValue;
+  // INT8 weights run on the streaming and 128 x 128 kernels only
+  if (kmode_of(a) == KM_INT8_A16) return hipErrorInvalidValue;
   // scale and zero-point copies use 32-bit offsets from the scale region
   if (a.G.total - a.G.off_scales > 0xFFFFFFFFull) return hipErrorInvalidValue;
   if (kmode_of(a) == KM_MX_A4)
@@ -832,6 +835,9 @@ hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipS
   if (kmode_of(a) == KM_MX_A16)
     return grouped ? go_big<false, false, true, false, true>(a, grid_items, st)
                    : go_big<false, false, false, false, true>(a, 0, st);
+  if (kmode_of(a) == KM_MXI4_A16)
+    return grouped ? go_big<false, false, true, false, true, true>(a, grid_items, st)
+                   : go_big<false, false, false, false, true, true>(a, 0, st);
   if (a.wfmt == W_MXFP4)
     return grouped ? go_big<true, false, true>(a, grid_items, st) : go_big<true, false, false>(a, 0, st);
   if (a.wfmt == W_UINT4_ZP)

@@ -32,7 +32,7 @@ import math
 
 import torch
 
-from . import (HM_A_BF16, HM_A_FP8_ROWSCALE, HM_W_MXINT4, HmError, hm_gemm, hm_gemm_plan,
+from . import (HM_A_BF16, HM_A_FP8_ROWSCALE, HM_W_INT8_SYM, HmError, hm_gemm, hm_gemm_plan,
                hm_gemm_workspace_size, hm_moe_gemm, hm_moe_gemm_plan, hm_moe_gemm_workspace_size)
 
 LLC_BYTES = 256 * 2 ** 20
@@ -72,7 +72,7 @@ def moe_candidates(desc, afmt, t, topk, rows_are_pairs):
     """Valid explicit tunings of hm_moe_gemm (the default first)."""
     out = [dict()]
     seen = {hm_moe_gemm_plan(desc, afmt, t, topk, rows_are_pairs)}
-    no_big = int(desc.wfmt) == HM_W_MXINT4 and afmt == HM_A_BF16     # no 256-row units
+    no_big = int(desc.wfmt) == HM_W_INT8_SYM                         # no 256-row units
     for rows, smax, nbw, big, tile in itertools.product((16, 32), (16, 32, 64, 128), (1, 2),
                                                         (0, -1, 65, 129), (1, 2)):
         if smax < rows or (no_big and big > 0):

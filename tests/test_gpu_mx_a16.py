@@ -35,10 +35,8 @@ def test_dequant_through_unit_rows(fmt, m, force):
     from 0 (products down to 2^-128, subnormal in fp32 and bf16) to 252
     (largest 6 * 2^125, the last byte whose products stay below 2^128), on the
     streaming (m <= 32, or forced), 128 x 64 (default above 32 rows), 128 x
-    128 and 256 x 256 (forced; MXFP4 only) kernels."""
+    128 and 256 x 256 (forced) kernels."""
     import quantized_gemm_int4_amd as hm
-    if force == 3 and fmt == quant.FMT_MXINT4:
-        pytest.skip("no 256 x 256 kernel for MXINT4")
     n, k = 40, 256
     r = np.random.default_rng(11)
     codes = r.integers(0, 256, (n, k // 2), dtype=np.uint8)
@@ -92,8 +90,6 @@ def test_ragged_default_path(fmt, n, k, m):
                                      (1, 3), (300, 3), (600, 3)])
 @pytest.mark.parametrize("fmt", MXS)
 def test_forced_paths(fmt, m, force):
-    if force == 3 and fmt == quant.FMT_MXINT4:
-        pytest.skip("no 256 x 256 kernel for MXINT4")
     MxLayer(264, 640, cfg=7, wseed=5, fmt=fmt).check(synthetic.activations(7, m, 640, index=m, outliers=0.01),
                                                      tuning=dict(path=force))
 
@@ -126,8 +122,8 @@ def _skewed_ids(t, topk, E, seed):
 @pytest.mark.parametrize("rows_are_pairs", [0, 1])
 @pytest.mark.parametrize("mid", [1, 0])
 def test_moe_mixed_units(fmt, rows_are_pairs, mid):
-    """Streaming units (small experts), 128-row tile units and (MXFP4)
-    256-row units in one grouped call; the tile units on the 128 x 64 kernel
+    """Streaming units (small experts), 128-row tile units and 256-row units
+    in one grouped call; the tile units on the 128 x 64 kernel
     (mid=1, the default) or the 128 x 128 one."""
     import quantized_gemm_int4_amd as hm
     _moe_mixed(hm, rows_are_pairs, fmt, dict(moe_tile=1 if mid else 2))
