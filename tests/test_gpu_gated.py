@@ -150,3 +150,26 @@ def test_gated_moe_workload_shape_sampled():
         h = hm.hm_moe_gemm(d, w_gated, x, off, sp, t, topk, 0, tuning=tuning, gated=True)
         torch.cuda.synchronize()
         assert torch.equal(h.view(torch.int16), h2.view(torch.int16))
+
+
+def test_gated_moe_workload_w4a8_t1024():
+    """The W4A8 gate_up (MXFP4 weights, FP8 rows) at T = 1024: bit-exact
+    against the two-step path on every row (streaming, 64 x 128 and 256-row
+    units all take part)."""
+    import quantized_gemm_int4_amd as hm
+    E, topk, n, k, t = 256, 8, 4096, 7168, 1024
+    codes, sc, zeros = synthetic.random_std_format_dev(quant.FMT_MXFP4, E, n, k, 10)
+    d = hm.wdesc(quant.FMT_MXFP4, n, k, E)
+    w_plain = hm.hm_transform(d, codes, sc, zeros)
+    w_gated = hm.hm_transform(d, codes, sc, zeros, gated=True)
+    ids, _ = synthetic.router_topk(5, t, E, topk)
+    x8, xs = hm.hm_quant_fp8_rows(synthetic.activations_dev(40, t, k))
+    _, off, sp = hm.hm_moe_sort(to_dev(ids), E)
+    tuning = dict(moe_stream_nbw=2)
+    plan = hm.hm_moe_gemm_plan(d, 1, t, topk, 0, tuning, gated=True)
+    assert "k_gemm_big" in plan and "k_gemm_mid_mx" in plan, plan
+    y = hm.hm_moe_gemm(d, w_plain, x8, off, sp, t, topk, 0, a_scales=xs, tuning=tuning)
+    h2 = hm.hm_silu_mul(y)
+    h = hm.hm_moe_gemm(d, w_gated, x8, off, sp, t, topk, 0, a_scales=xs, tuning=tuning, gated=True)
+    torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int16), h2.view(torch.int16))

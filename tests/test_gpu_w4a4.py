@@ -141,3 +141,48 @@ def test_w4a4_grouped_mixed_units(rows_are_pairs, big):
                                   lambda e: what[e].astype(np.float64), n)
     res = gemm.check(bits_of(y), yref, b)
     assert res["ok"], res
+
+
+@pytest.mark.parametrize("t,proj", [(1024, "gate_up"), (1024, "down")])
+def test_w4a4_moe_workload_size_sampled(t, proj):
+    """256 experts, top-8 routing, gate_up N=4096 K=7168 / down N=7168 K=2048
+    with MXFP4 rows: the largest expert runs 256-row units; every 256-row
+    chunk of it (the partial last one included) and a few rows of the three
+    smallest experts (streaming units) are checked."""
+    import quantized_gemm_int4_amd as hm
+    E, topk = 256, 8
+    n, k = (4096, 7168) if proj == "gate_up" else (7168, 2048)
+    rows_are_pairs = 0 if proj == "gate_up" else 1
+    g = torch.Generator(device="cuda")
+    g.manual_seed(21)
+    codes = torch.randint(0, 256, (E, n, k // 2), dtype=torch.uint8, device="cuda", generator=g)
+    scales = torch.randint(118, 122, (E, n, k // 32), dtype=torch.uint8, device="cuda", generator=g)
+    d = hm.wdesc("mxfp4", n, k, E)
+    w = hm.hm_transform(d, codes, scales, None)
+    ids, _ = synthetic.router_topk(6, t, E, topk)
+    xb = _rows(t * topk if rows_are_pairs else t, k, 8)
+    c, s = hm.hm_quant_mxfp4_rows(bf16_to_dev(xb))
+    _, off, sp = hm.hm_moe_sort(to_dev(ids), E)
+    assert "k_gemm_big" in hm.hm_moe_gemm_plan(d, hm.HM_A_MXFP4, t, topk, rows_are_pairs)
+    y = hm.hm_moe_gemm(d, w, c, off, sp, t, topk, rows_are_pairs, a_scales=s)
+    torch.cuda.synchronize()
+    counts = np.bincount(ids.ravel(), minlength=E)
+    flat = ids.ravel()
+    big = int(np.argmax(counts))
+    assert counts[big] > 256
+    seg = np.nonzero(flat == big)[0]                  # the expert's pairs in sorted (stable) order
+    pick = [seg[i] for i in range(0, seg.size, 256)] + [seg[min(i + 255, seg.size - 1)] for i in range(0, seg.size, 256)]
+    small = [e for e in np.argsort(counts) if counts[e] > 0][:3]
+    pairs = np.unique(np.concatenate([np.array(pick)] + [np.nonzero(flat == e)[0][:4] for e in small]))
+    cache = {}
+
+    def what(e):
+        if e not in cache:
+            cache[e] = quant.dequant("mxfp4", codes[e].cpu().numpy(), scales[e].cpu().numpy(), None).astype(np.float64)
+        return cache[e]
+
+    rc, rs = quant.quant_mxfp4_rows(xb)
+    yref, b, _ = moe.moe_gemm_ref(quant.mxfp4_rows_dequant(rc, rs), bool(rows_are_pairs), topk, ids, what, n,
+                                  pairs=pairs)
+    res = gemm.check(bits_of(y)[pairs], yref, b)
+    assert res["ok"], res
