@@ -124,6 +124,11 @@ __device__ __forceinline__ u32x4_t i8x8_bf16(uint32_t lo, uint32_t hi) {
   return (u32x4_t){pack_bf16(sb(lo, 0), sb(lo, 1)), pack_bf16(sb(lo, 2), sb(lo, 3)),
                    pack_bf16(sb(hi, 0), sb(hi, 1)), pack_bf16(sb(hi, 2), sb(hi, 3))};
 }
+// Bytes 2 sel and 2 sel + 1 of x (two's complement) times s -> one bf16 pair
+// (sel = 0, 1 known at compile time after unrolling).
+__device__ __forceinline__ uint32_t i8x2_bf16_scaled(uint32_t x, int sel, float s) {
+  return pack_bf16((float)(int8_t)(x >> (16 * sel)) * s, (float)(int8_t)(x >> (16 * sel + 8)) * s);
+}
 // The same times s, each product rounded once to bf16.
 __device__ __forceinline__ u32x4_t i8x8_bf16_scaled(uint32_t lo, uint32_t hi, float s) {
   auto sb = [s](uint32_t x, int b) { return (float)(int8_t)(x >> (8 * b)) * s; };

@@ -148,11 +148,10 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   const bool a4 = afmt == HM_A_MXFP4;
   const bool tiles32 = scales_addr32(G);        // 128-row and 256-row kernels can address the scales
   if (tu.path == P_STREAM && m > kStreamWideRows) return HM_ERR_TUNING;
-  // W4A4 and INT8 weights have no 128-row tile kernel, INT8 weights no
-  // 256 x 256 kernel
+  // W4A4 and INT8 weights have no 128-row tile kernel
   const bool int8 = d->wfmt == HM_W_INT8_SYM;
-  const bool no_mid = a4 || int8, no_big = int8;
-  if ((no_mid && tu.path == P_MID) || (no_big && tu.path == P_BIG)) return HM_ERR_TUNING;
+  const bool no_mid = a4 || int8;
+  if (no_mid && tu.path == P_MID) return HM_ERR_TUNING;
   if ((tu.path == P_MID || tu.path == P_BIG) && (!tiles32 || !mid_grid_fits(G, a8, m))) return HM_ERR_TUNING;
   // W4A16 up to 256 rows also streams (in 32-row chunks, each re-reading the
   // weights from the L2) when N is narrow: measured at K = 4096, a streaming
@@ -166,7 +165,12 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   } else if (m <= kStreamMaxRows || narrow) {
     p.path = P_STREAM;
   } else if (int8) {
-    p.path = P_TILE;
+    // INT8: 128 x 128 or 256 x 256 tiles by the round costs of the MX
+    // bf16-row choice below (the same two kernels' step loops)
+    const int64_t mt = (m + kTileM - 1) / kTileM, bt = (m + kBigRows - 1) / kBigRows;
+    const int64_t c_tile = 170 * ((((G.NB + 7) / 8) * mt + 255) / 256) + 120;
+    const int64_t c_big = 580 * std::max<int64_t>(big_n_tiles(G) * bt, 256) / 256;
+    p.path = c_big < c_tile ? P_BIG : P_TILE;
   } else if (a4) {
     // W4A4: 256 x 256 tiles from kBigMinRows rows, else 128 x 128
     p.path = m >= kBigMinRows ? P_BIG : P_TILE;
@@ -333,7 +337,7 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
     // activation rows and scales with 32-bit offsets
     const bool int8 = d->wfmt == HM_W_INT8_SYM;
     const bool tile_only = a4 || int8;                       // no 128-row tile kernel
-    const bool big_ok = !int8 && !p.a64 && tiles32;          // INT8 has no 256-row units
+    const bool big_ok = !p.a64 && tiles32;
     if (tu.mbig > 0 && !big_ok) return HM_ERR_TUNING;
     p.big_min = (tu.mbig == -1 || !big_ok) ? 0 : big_min;
     // up-to-128-row units: the 128-row tile kernel (32-bit offsets), or the

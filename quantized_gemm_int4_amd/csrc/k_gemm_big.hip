@@ -127,10 +127,23 @@ _Pragma("nounroll")                                                             
           const int wg = tg < KGt ? tg : (wnext ? tg - KGt : KGt - 1);                                              \
           uint8_t* d2 = lds + so[2];                                                                                \
           uint8_t* dw = lds + wso[2];                                                                               \
+          /* INT8 weights travel per step, three steps ahead, through the ring of weight slots */                  \
+          const int t3 = s + 3;                                                                                     \
+          const bool w8next = chained && has_next && t3 >= S;                                                       \
+          const int w8s = t3 < S ? t3 : (w8next ? t3 - S : S - 1);                                                  \
+          uint8_t* dw8 = lds + wso[0];                                                                              \
           auto dma = [&](int q) __attribute__((always_inline)) {                                                    \
             if (q < NX) {                                                                                           \
               const rsrc_t r = xnext ? nc.rx : cc.rx;                                                               \
               b2lds16(r, xnext ? nc.xoff[q] : cc.xoff[q], (uint32_t)(xls * 128), d2 + (NX * wave + q) * 1024);      \
+            } else if (Q8 && q < NX + 4) {                                                                          \
+              /* INT8: step s + 3's half (1 KiB) of each 2 KiB tile into the free weight slot */                    \
+              const int k0 = q - NX;                                                                                \
+              b2lds16(w8next ? nc.rw : cc.rw, w8next ? nc.wvo[k0] : cc.wvo[k0],                                     \
+                      (uint32_t)((w8s >> 1) * 2048 + (w8s & 1) * 1024), dw8 + kWOff + (NWT * wave + k0) * 1024);    \
+            } else if (Q8) {                                                                                        \
+              b2lds4(rsz, (w8next ? nc.svo[0] : cc.svo[0]) + (uint32_t)(w8s >> 1) * szstride, 0u,                   \
+                     dw8 + kSOff + wave * 256);                                                                     \
             } else if (q < NX + 2) {                                                                                \
               const rsrc_t r = wnext ? nc.rw : cc.rw;                                                               \
               const int k0 = q - NX;                                                                                \
@@ -150,7 +163,10 @@ _Pragma("nounroll")                                                             
           const uint8_t* xs = lds + so[0];                                                                          \
           uint32_t wv[2][4];                                                                                        \
           float svn[2], zsn[2], sfn[2][2];                                                                          \
-          if (F4)                                                                                                   \
+          u32x2_t wv8[2][4];                                                                                        \
+          if (Q8)                                                                                                   \
+            fetch8(lds + wso[1], wv8, svn);                                                                         \
+          else if (F4)                                                                                              \
             fetch_f4(lds + ((s & 1) ? wso[1] : wso[0]), (s + 1) & 1, (s + 1 < S ? (s + 1) >> 1 : 0) & 3, wv, sfn); \
           else                                                                                                      \
             fetch(lds + ((s & 1) ? wso[1] : wso[0]), (s + 1) & 1, wv, svn, zsn);                                    \
@@ -171,7 +187,11 @@ _Pragma("unroll")                                                               
             for (int e = 0; e < WPI; ++e) {                                                                         \
               const int wi = WPI * i + e, nb2 = (wi >> 2) & 1, u = wi & 3;                                          \
               const uint32_t w = kq == 0 ? w3c[nb2] : wv[nb2][kq - 1];                                              \
-              if (F4) {                                                                                             \
+              if (Q8) {                                                                                             \
+                const u32x2_t w8 = kq == 0 ? w3c8[nb2] : wv8[nb2][kq - 1];                                          \
+                const float sv = kq == 0 ? sv3c[nb2] : svn[nb2];                                                    \
+                af[nb2][(kq + 3) & 3][u] = i8x2_bf16_scaled(w8[u >> 1], u & 1, sv);                                \
+              } else if (F4) {                                                                                      \
                 const float sf = kq == 0 ? sv3c[nb2] : sfn[nb2][(kq - 1) >> 1];                                     \
                 af[nb2][(kq + 3) & 3][u] = I4 ? i4x2_bf16(w, sf, u) : fp4x2_bf16(w, sf, u);                          \
               } else {                                                                                              \
@@ -193,21 +213,23 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                                   \
           for (int nb2 = 0; nb2 < 2; ++nb2) {                                                                       \
             w3c[nb2] = wv[nb2][3];                                                                                  \
+            if (Q8) w3c8[nb2] = wv8[nb2][3];                                                                        \
             sv3c[nb2] = F4 ? sfn[nb2][1] : svn[nb2];                                                                \
             zs3c[nb2] = F4 ? 0.f : zsn[nb2];                                                                        \
           }                                                                                                         \
           wait_barrier(std::integral_constant<int, kPer>());                                                        \
           rotate();                                                                                                 \
-          if (s & 1) rotate_w();                                                                                    \
+          if (Q8 || (s & 1)) rotate_w();                                                                            \
         }                                                                                                           \
   } while (0)
 
-template <bool MX, bool ZP, bool GROUPED, bool A4 = false, bool F4 = false, bool I4 = false>
+template <bool MX, bool ZP, bool GROUPED, bool A4 = false, bool F4 = false, bool I4 = false, bool Q8 = false>
 __global__ void __launch_bounds__(big_threads(MX), 1)
 k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
   static_assert(!A4 || MX, "MXFP4 rows go with MXFP4 weights");
   static_assert(!F4 || (!MX && !ZP), "MX weights with bf16 rows take the bf16 path");
   static_assert(!I4 || F4, "MXINT4 codes take the MX bf16-row path");
+  static_assert(!Q8 || (!MX && !ZP && !F4), "INT8 weights take the bf16 path");
   constexpr int SB = big_stage_bytes(MX || F4, A4);
   constexpr int NW = big_threads(MX) / 64;         // waves
   constexpr int NX = A4 ? 2 : 32 / NW;             // activation copies per lane per step
@@ -299,7 +321,8 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
     c.rx = make_rsrc(reinterpret_cast<const uint8_t*>(a.x) + t.m0 * row_bytes,
                      GROUPED ? 0xFFFFFFFFull : (uint64_t)t.rows * row_bytes);
     const int64_t wb = wbase_of(t.e, G);
-    c.rw = make_rsrc(a.w + (wb + t.nb0) * G.KG * 1024, (uint64_t)kBigCB * G.KG * 1024);
+    constexpr int TB = Q8 ? 2048 : 1024;             // bytes of one (column block, group) tile
+    c.rw = make_rsrc(a.w + (wb + t.nb0) * G.KG * TB, (uint64_t)kBigCB * G.KG * TB);
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       // MXFP4 rows (64 bytes a step): 16 rows a copy, lane L row 16 j + L / 4,
@@ -323,7 +346,7 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
     for (int k = 0; k < NWT; ++k) {
       int64_t nb = MX ? t.nb0 + wave + 8 * k : t.nb0 + NWT * wave + k;
       if (nb >= G.NB) nb = G.NB - 1;
-      c.wvo[k] = (uint32_t)((nb - t.nb0) * G.KG * 1024 + lane * 16);
+      c.wvo[k] = (uint32_t)((nb - t.nb0) * G.KG * TB + lane * 16);
       if (MX) c.svo[k & 1] = (uint32_t)((wb + nb) * G.KG4 * 256 + lane * 4);
     }
     if (F4) {
@@ -637,7 +660,9 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
       if (F4) b2lds16(rsz, c.svo[0] + (uint32_t)(g >> 2) * 256, 0u, slot + kSOff + wave * 1024);
       else b2lds4(rsz, c.svo[0] + (uint32_t)g * szstride, 0u, slot + kSOff + wave * 256);
     };
-    constexpr int kPer = NX + 2 + 1;                // copies per wave per step
+    // copies per wave per step: activations, half of the wave's code tiles
+    // (INT8: the step's half of all four) and the scale / zero-point gather
+    constexpr int kPer = Q8 ? NX + 4 + 1 : NX + 2 + 1;
     // A operands of one step: column half nb2, K part kq.  Lane row n =
     // 64 w + 32 nb2 + l32 lies in tile 4 w + 2 nb2 + l32 / 16 at column
     // l32 % 16; K = 64 h + 16 kq + 8 hi is word 2 h + kq / 2 of slot
@@ -683,7 +708,35 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
         }
       }
     };
+    // INT8 weights (the step's half of a 2 KiB tile; per step, through the
+    // ring of weight slots: at step s slot wso[1] holds step s + 1, wso[2]
+    // step s + 2, and step s + 3 is copied into wso[0], free since step s's
+    // operands were read during step s - 1):
+    // K = 16 kq + 8 hi of the step is bytes 8 (kq / 2) .. + 7 of slot
+    // (l32 % 16) + 16 (2 (kq % 2) + hi); one bf16 scale per column and group
+    auto fetch8 = [&](const uint8_t* stg, u32x2_t (&wv8)[2][4], float (&sv)[2]) __attribute__((always_inline)) {
+      const uint8_t* sz = stg + kSOff + wave * 256;
+#pragma unroll
+      for (int nb2 = 0; nb2 < 2; ++nb2) {
+        const int t4 = 2 * nb2 + c_l;
+        const uint8_t* tile = stg + kWOff + (NWT * wave + t4) * 1024;
+        const u32x4_t va = ld16(tile + (c16 + 16 * hi) * 16), vb = ld16(tile + (c16 + 16 * (2 + hi)) * 16);
+        wv8[nb2][0] = (u32x2_t){va[0], va[1]};
+        wv8[nb2][1] = (u32x2_t){vb[0], vb[1]};
+        wv8[nb2][2] = (u32x2_t){va[2], va[3]};
+        wv8[nb2][3] = (u32x2_t){vb[2], vb[3]};
+        sv[nb2] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sz + t4 * 32 + c16 * 2));
+      }
+    };
+    // INT8: all four tiles' halves of step st and the scale gather of its group
+    auto copy_w8 = [&](const Copy& c, int st, uint8_t* stage) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < NWT; ++k)
+        b2lds16(c.rw, c.wvo[k], (uint32_t)((st >> 1) * 2048 + (st & 1) * 1024), stage + kWOff + (NWT * wave + k) * 1024);
+      b2lds4(rsz, c.svo[0] + (uint32_t)(st >> 1) * szstride, 0u, stage + kSOff + wave * 256);
+    };
     u32x4_t af[2][4];
+    u32x2_t w3c8[2] = {};                           // INT8: code bytes of operands (nb2, 3)
     uint32_t w3c[2] = {0u, 0u};                     // code words of operands (nb2, 3), their scales and offsets
     float sv3c[2] = {0.f, 0.f}, zs3c[2] = {0.f, 0.f};
     while (true) {
@@ -701,13 +754,29 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
         }
         write_table(tp);
         const int KGt = S >> 1;
-        copy_w(cc, 0, lds + wso[0]);
-        copy_w(cc, std::min(1, KGt - 1), lds + wso[1]);
+        if (Q8) {
+          copy_w8(cc, 0, lds + wso[0]);
+          copy_w8(cc, std::min(1, S - 1), lds + wso[1]);
+          copy_w8(cc, std::min(2, S - 1), lds + wso[2]);
+        } else {
+          copy_w(cc, 0, lds + wso[0]);
+          copy_w(cc, std::min(1, KGt - 1), lds + wso[1]);
+        }
         copy_x(cc, 0, lds + so[0]);
         copy_x(cc, std::min(1, S - 1), lds + so[1]);
         wait_barrier(std::integral_constant<int, 0>());
         uint32_t wv[2][4];
-        if (F4) {
+        if (Q8) {
+          u32x2_t w8[2][4];
+          fetch8(lds + wso[0], w8, sv3c);
+#pragma unroll
+          for (int nb2 = 0; nb2 < 2; ++nb2) {
+#pragma unroll
+            for (int kq = 0; kq < 3; ++kq) af[nb2][kq] = i8x8_bf16_scaled(w8[nb2][kq][0], w8[nb2][kq][1], sv3c[nb2]);
+            af[nb2][3] = (u32x4_t){0u, 0u, 0u, 0u};
+            w3c8[nb2] = w8[nb2][3];
+          }
+        } else if (F4) {
           float sf[2][2];
           fetch_f4(lds + wso[0], 0, 0, wv, sf);
 #pragma unroll
@@ -804,9 +873,9 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
 // it; W4A16 only (the half tiles compute four of the eight row blocks), and
 // not where the second half of a last tile row would be empty.
 
-template <bool MX, bool ZP, bool GROUPED, bool A4 = false, bool F4 = false, bool I4 = false>
+template <bool MX, bool ZP, bool GROUPED, bool A4 = false, bool F4 = false, bool I4 = false, bool Q8 = false>
 static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
-  auto kern = &k_gemm_big<MX, ZP, GROUPED, A4, F4, I4>;
+  auto kern = &k_gemm_big<MX, ZP, GROUPED, A4, F4, I4, Q8>;
   static const hipError_t attr_err = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, big_lds_bytes(MX || F4, A4));
   if (attr_err != hipSuccess) return attr_err;
@@ -826,8 +895,9 @@ static hipError_t go_big(const GemmArgs& a, int grid_items, hipStream_t st) {
 
 
 hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipStream_t st) {
-  // INT8 weights run on the streaming and 128 x 128 kernels only
-  if (kmode_of(a) == KM_INT8_A16) return hipErrorInvalidValue;
+  if (kmode_of(a) == KM_INT8_A16)
+    return grouped ? go_big<false, false, true, false, false, false, true>(a, grid_items, st)
+                   : go_big<false, false, false, false, false, false, true>(a, 0, st);
   // scale and zero-point copies use 32-bit offsets from the scale region
   if (a.G.total - a.G.off_scales > 0xFFFFFFFFull) return hipErrorInvalidValue;
   if (kmode_of(a) == KM_MX_A4)

@@ -144,7 +144,7 @@ hipError_t launch_gemm_mid(const GemmArgs& a, bool grouped, int grid_items, hipS
 hipError_t launch_gemm_big(const GemmArgs& a, bool grouped, int grid_items, hipStream_t) {
   check_gemm(a, grouped, grid_items);
   const int km = kmode_of(a);
-  need(km != KM_INT8_A16, "256 x 256 kernel formats");
+  need(km >= KM_INT4_A16 && km <= KM_INT8_A16, "256 x 256 kernel formats");
   need(a.G.total - a.G.off_scales <= 0xFFFFFFFFull, "scale region addressed in 32 bits");
   return hipSuccess;
 }

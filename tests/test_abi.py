@@ -124,8 +124,11 @@ def test_mxfp4_bf16_rows_plans():
     assert "128x64" in hm.hm_gemm_plan(mx, hm.HM_A_BF16, 4096, dict(path=2))
     assert "256x256" in hm.hm_gemm_plan(mx, hm.HM_A_BF16, 256, dict(path=3))
     assert "256x256" in hm.hm_gemm_plan(hm.wdesc("mxint4", 7168, 2048), hm.HM_A_BF16, 4096, dict(path=3))
-    with pytest.raises(hm.HmError) as e:             # no 256 x 256 kernel for INT8
-        hm.hm_gemm_plan(hm.wdesc("int8_sym", 7168, 2048), hm.HM_A_BF16, 4096, dict(path=3))
+    i8 = hm.wdesc("int8_sym", 7168, 2048)
+    assert "256x256" in hm.hm_gemm_plan(i8, hm.HM_A_BF16, 4096)
+    assert "128x128" in hm.hm_gemm_plan(i8, hm.HM_A_BF16, 1024)
+    with pytest.raises(hm.HmError) as e:             # no 128-row tile kernel for INT8
+        hm.hm_gemm_plan(i8, hm.HM_A_BF16, 4096, dict(path=2))
     assert e.value.code == 8
     assert hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, 4096).startswith("w4a8-mxfp4 tile 256x256")
     assert hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, 1).startswith("w4a8-mxfp4 stream")
@@ -281,7 +284,7 @@ def test_moe_plan_and_large_activation_guard():
     mxi = hm.hm_moe_gemm_plan(hm.wdesc("mxint4", 7168, 2048, 256), 0, 8192, 8, 1)
     assert "k_gemm_big from 97 rows" in mxi, mxi
     i8p = hm.hm_moe_gemm_plan(hm.wdesc("int8_sym", 7168, 2048, 256), 0, 8192, 8, 1)
-    assert "big(256 rows)=none" in i8p, i8p
+    assert "k_gemm_big from 97 rows" in i8p and "k_gemm_tile" in i8p, i8p
     # explicit tuning shows up in the plan and in the workspace size
     t = dict(moe_stream_rows=32, moe_stream_max=128, moe_stream_nbw=1, moe_big_min=-1, moe_tile=2)
     p2 = hm.hm_moe_gemm_plan(gu, 0, 1024, 8, 0, t)
@@ -314,7 +317,7 @@ def test_tuner_candidates_are_valid_and_distinct():
         assert any(" stream " in p for p in plans) == (m <= 256)
         assert any("256x256" in p for p in plans) and any("128x128" in p for p in plans)
     i8 = hm.wdesc("int8_sym", 7168, 2048)
-    assert not any("256x256" in hm.hm_gemm_plan(i8, 0, 64, c or None) for c in tune.dense_candidates(i8, 0, 64))
+    assert not any("128x64" in hm.hm_gemm_plan(i8, 0, 64, c or None) for c in tune.dense_candidates(i8, 0, 64))
     mx = hm.wdesc("mxfp4", 7168, 2048)
     assert any("256x256" in hm.hm_gemm_plan(mx, 0, 64, c or None) for c in tune.dense_candidates(mx, 0, 64))
     moe = hm.wdesc("int4_sym", 4096, 7168, 256)

@@ -37,7 +37,7 @@ def _check(d, w, what, xb, tuning=None, rows=None):
 
 
 @pytest.mark.parametrize("n,k", [(200, 384), (37, 128), (1000, 1152)])
-@pytest.mark.parametrize("m", [1, 7, 16, 17, 32, 33, 100, 257])
+@pytest.mark.parametrize("m", [1, 7, 16, 17, 32, 33, 100, 257, 700])
 def test_int8_ragged_default_path(n, k, m):
     d, w, what = _layer(n, k, n + k)
     _check(d, w, what, synthetic.activations(60, m, k, index=m))
@@ -46,7 +46,8 @@ def test_int8_ragged_default_path(n, k, m):
 @pytest.mark.parametrize("m,tuning", [(1, dict(path=4)), (40, dict(path=4)), (200, dict(path=1)),
                                       (16, dict(path=1, stream_ks=1, stream_nbw=2, stream_splits=3)),
                                       (16, dict(path=1, stream_waves=8, stream_ks=8, stream_nbw=1)),
-                                      (32, dict(path=1, stream_ks=4, stream_nbw=1))])
+                                      (32, dict(path=1, stream_ks=4, stream_nbw=1)),
+                                      (1, dict(path=3)), (300, dict(path=3)), (600, dict(path=3))])
 def test_int8_forced_paths(m, tuning):
     d, w, what = _layer(264, 1152, 4)
     _check(d, w, what, synthetic.activations(60, m, 1152, index=m), tuning)
@@ -63,7 +64,7 @@ def test_int8_one_hot_exact():
     scales = np.full((1, n, k // 128), 0x3E00, dtype=np.uint16)     # bf16 0.125
     d = hm.wdesc(F, n, k)
     w = hm.hm_transform(d, *std_to_dev(F, q.view(np.uint8)[None], scales, None))
-    for m, path in [(3, 1), (40, 4), (1, 1)]:
+    for m, path in [(3, 1), (40, 4), (1, 1), (40, 3), (300, 3)]:
         xb = synthetic.activations(61, m, k, index=m)
         y = bits_of(hm.hm_gemm(d, w, bf16_to_dev(xb), tuning=dict(path=path)))
         x = codecs.bf16_value(xb).astype(np.float64)
@@ -73,12 +74,13 @@ def test_int8_one_hot_exact():
 
 def test_int8_full_layer():
     """The dense FFN up-projection shape (N = 14336, K = 4096): M = 1, 16, and
-    sampled rows of M = 1024."""
+    sampled rows of M = 1024 and of M = 4096 (256 x 256 tiles)."""
     d, w, what = _layer(14336, 4096, 9)
     for m in (1, 16):
         _check(d, w, what, synthetic.activations(62, m, 4096, index=m))
-    rows = np.concatenate([np.random.default_rng(1).choice(1024, 40, replace=False), [0, 1023]])
-    _check(d, w, what, synthetic.activations(62, 1024, 4096, index=1024), rows=rows)
+    for m in (1024, 4096):
+        rows = np.concatenate([np.random.default_rng(m).choice(m, 40, replace=False), [0, m - 1]])
+        _check(d, w, what, synthetic.activations(62, m, 4096, index=m), rows=rows)
 
 
 def test_int8_grouped():
@@ -92,7 +94,7 @@ def test_int8_grouped():
     d = hm.wdesc(F, n, k, E)
     w = hm.hm_transform(d, *std_to_dev(F, codes, scales, None))
     plan = hm.hm_moe_gemm_plan(d, 0, t, topk, 0)
-    assert "k_gemm_tile" in plan and "big(256 rows)=none" in plan, plan
+    assert "k_gemm_tile" in plan and "k_gemm_big" in plan, plan
     xb = synthetic.activations(63, t, k)
     _, off, sp = hm.hm_moe_sort(to_dev(ids), E)
     y = hm.hm_moe_gemm(d, w, bf16_to_dev(xb), off, sp, t, topk, 0)
