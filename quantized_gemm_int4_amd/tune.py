@@ -15,7 +15,10 @@ explicit choices of hm_tuning for given call shapes:
   * timing: a HIP graph of `reps` back-to-back calls on the current stream,
     rotating over weight copies that together exceed the last-level cache,
     replayed once to warm up and once under HIP events; the per-call time is
-    the event time / reps.
+    the event time / reps.  The default choice is timed once before the
+    search and discarded (the first timed graph of a process runs slow), and
+    the fastest candidate is re-timed against the default, alternating, at
+    the end: it replaces the default only if it is faster there too.
   * check: each candidate's output is compared with the default choice's
     (normwise relative difference at most 1e-2 and finite), which catches a
     misconfigured launch; the parity tests cover every path against the
@@ -112,6 +115,16 @@ def _graph_us(fn, reps):
     return a.elapsed_time(b) * 1e3 / reps
 
 
+def _confirm(fn_default, fn_best, reps, rounds=2):
+    """Alternating re-timing of the default and the best candidate; returns
+    (default us, best us) as the minimum over the rounds."""
+    d, b = [], []
+    for _ in range(rounds):
+        d.append(_graph_us(fn_default, reps))
+        b.append(_graph_us(fn_best, reps))
+    return min(d), min(b)
+
+
 def _close(y, y0):
     d = (y.float() - y0.float()).norm().item()
     n = y0.float().norm().item()
@@ -166,6 +179,8 @@ def tune_dense(desc, w_copies, x, ms, x_scales=None, reps=30, table=None, log=No
         y = torch.empty_like(y0)
         best = None
         default_us = None
+        warm_ws = torch.empty(max(hm_gemm_workspace_size(desc, afmt, m, None), 256), dtype=torch.uint8, device=dev)
+        _graph_us(lambda i: hm_gemm(desc, w_copies[i % len(w_copies)], xm, xs, y=y0, ws=warm_ws), reps)
         for c in dense_candidates(desc, afmt, m):
             need = hm_gemm_workspace_size(desc, afmt, m, c or None)
             ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -184,6 +199,15 @@ def tune_dense(desc, w_copies, x, ms, x_scales=None, reps=30, table=None, log=No
                 log(f"m={m} {hm_gemm_plan(desc, afmt, m, c or None)}: {us:.2f} us")
             if best is None or us < best[1]:
                 best = (c, us)
+        if best[0]:
+            bws = torch.empty(max(hm_gemm_workspace_size(desc, afmt, m, best[0]), 256), dtype=torch.uint8, device=dev)
+            d_us, b_us = _confirm(
+                lambda i: hm_gemm(desc, w_copies[i % len(w_copies)], xm, xs, y=y0, ws=warm_ws),
+                lambda i: hm_gemm(desc, w_copies[i % len(w_copies)], xm, xs, y=y, ws=bws, tuning=best[0]), reps)
+            default_us = d_us
+            best = (best[0], b_us) if b_us < d_us else ({}, d_us)
+            if log:
+                log(f"m={m} confirm: default {d_us:.2f} us, best {b_us:.2f} us")
         table.put(_key(desc, afmt), m, best[0], best[1], default_us, hm_gemm_plan(desc, afmt, m, best[0] or None))
     return table
 
@@ -198,6 +222,10 @@ def tune_moe(desc, w, a, offsets, sorted_pairs, t, topk, rows_are_pairs, a_scale
     y0 = torch.empty(P, desc.n, dtype=torch.bfloat16, device=dev)
     y = torch.empty_like(y0)
     best, default_us = None, None
+    warm_ws = torch.empty(max(hm_moe_gemm_workspace_size(desc, afmt, t, topk, None), 256), dtype=torch.uint8,
+                          device=dev)
+    _graph_us(lambda i: hm_moe_gemm(desc, w, a, offsets, sorted_pairs, t, topk, rows_are_pairs, a_scales, y=y0,
+                                    ws=warm_ws), reps)
     for c in moe_candidates(desc, afmt, t, topk, rows_are_pairs):
         need = hm_moe_gemm_workspace_size(desc, afmt, t, topk, c or None)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -217,6 +245,18 @@ def tune_moe(desc, w, a, offsets, sorted_pairs, t, topk, rows_are_pairs, a_scale
             log(f"t={t} {c}: {us:.1f} us")
         if best is None or us < best[1]:
             best = (c, us)
+    if best[0]:
+        bws = torch.empty(max(hm_moe_gemm_workspace_size(desc, afmt, t, topk, best[0]), 256), dtype=torch.uint8,
+                          device=dev)
+        d_us, b_us = _confirm(
+            lambda i: hm_moe_gemm(desc, w, a, offsets, sorted_pairs, t, topk, rows_are_pairs, a_scales, y=y0,
+                                  ws=warm_ws),
+            lambda i: hm_moe_gemm(desc, w, a, offsets, sorted_pairs, t, topk, rows_are_pairs, a_scales, y=y,
+                                  ws=bws, tuning=best[0]), reps)
+        default_us = d_us
+        best = (best[0], b_us) if b_us < d_us else ({}, d_us)
+        if log:
+            log(f"t={t} confirm: default {d_us:.1f} us, best {b_us:.1f} us")
     key = _key(desc, afmt) + f"_moe_topk{topk}_rp{rows_are_pairs}"
     table.put(key, t, best[0], best[1], default_us,
               hm_moe_gemm_plan(desc, afmt, t, topk, rows_are_pairs, best[0] or None))
