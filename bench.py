@@ -14,7 +14,8 @@ rows at T = 64, 1024, 8192, and with MXFP4 weights and per-token FP8 rows at
 T = 16384 (TFLOP/s, weight GB/s and roofline fraction per T), each checked
 against the oracle on sampled pairs in its own cpu_baseline.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_w4a16|dense_w4a8|moe_w4a16|moe_w4a8|moe_w4a16_mxfp4|moe_w4a16_mxint4|shards]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+        [--workload dense_w4a16|dense_w4a8|dense_w4a4|moe_w4a16|moe_w4a8|moe_w4a16_mxfp4|moe_w4a16_mxint4|shards|readfloor]
 
 One JSON line is printed (rank 0).
 """

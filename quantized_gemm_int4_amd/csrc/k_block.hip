@@ -73,13 +73,14 @@ k_silu_mul_fp8(const uint16_t* __restrict__ gu, int64_t rows, int64_t d, uint8_t
     uint32_t cw[CH][2];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      cw[c][0] = cw[c][1] = 0;
-      if (s == 0.0f) continue;
+      float q[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float h = (j & 1) ? hi_bf16(gv[c][j >> 1]) : lo_bf16(gv[c][j >> 1]);
-        cw[c][j >> 2] |= f32_to_e4m3(__fdiv_rn(h, s)) << (8 * (j & 3));
+        q[j] = s != 0.0f ? __fdiv_rn(h, s) : 0.0f;
       }
+      cw[c][0] = e4m3x4(q[0], q[1], q[2], q[3]);
+      cw[c][1] = e4m3x4(q[4], q[5], q[6], q[7]);
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {

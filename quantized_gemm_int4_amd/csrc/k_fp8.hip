@@ -42,21 +42,16 @@ k_quant_fp8_rows(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint8_t* 
     if (vec) {
       for (int64_t i = threadIdx.x * 8; i < k; i += 256 * 8) {
         const u32x4_t v = ld16(xr + i);
-        uint32_t lo = 0, hi = 0;
+        float q[8];
         for (int j = 0; j < 4; ++j) {
-          uint32_t c0 = 0, c1 = 0;
-          if (s != 0.0f) {
-            c0 = f32_to_e4m3(__fdiv_rn(bf16_to_f32(v[j] & 0xFFFF), s));
-            c1 = f32_to_e4m3(__fdiv_rn(bf16_to_f32(v[j] >> 16), s));
-          }
-          const uint32_t pair = c0 | (c1 << 8);
-          if (j < 2) lo |= pair << (16 * j); else hi |= pair << (16 * (j - 2));
+          q[2 * j] = s != 0.0f ? __fdiv_rn(bf16_to_f32(v[j] & 0xFFFF), s) : 0.0f;
+          q[2 * j + 1] = s != 0.0f ? __fdiv_rn(bf16_to_f32(v[j] >> 16), s) : 0.0f;
         }
-        *reinterpret_cast<u32x2_t*>(qr + i) = (u32x2_t){lo, hi};
+        *reinterpret_cast<u32x2_t*>(qr + i) = (u32x2_t){e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
       }
     } else {
       for (int64_t i = threadIdx.x; i < k; i += 256)
-        qr[i] = (s != 0.0f) ? (uint8_t)f32_to_e4m3(__fdiv_rn(bf16_to_f32(xr[i]), s)) : (uint8_t)0;
+        qr[i] = (s != 0.0f) ? (uint8_t)(e4m3x4(__fdiv_rn(bf16_to_f32(xr[i]), s), 0.0f, 0.0f, 0.0f) & 0xFFu) : (uint8_t)0;
     }
   }
 }
@@ -95,18 +90,13 @@ k_quant_fp8_rows_reg(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint8
     for (int c = 0; c < CH; ++c) {
       const int64_t i = ((int64_t)c * 256 + threadIdx.x) * 8;
       if (i >= k) continue;
-      uint32_t lo = 0, hi = 0;
+      float q[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t c0 = 0, c1 = 0;
-        if (s != 0.0f) {
-          c0 = f32_to_e4m3(__fdiv_rn(bf16_to_f32(v[c][j] & 0xFFFF), s));
-          c1 = f32_to_e4m3(__fdiv_rn(bf16_to_f32(v[c][j] >> 16), s));
-        }
-        const uint32_t pair = c0 | (c1 << 8);
-        if (j < 2) lo |= pair << (16 * j); else hi |= pair << (16 * (j - 2));
+        q[2 * j] = s != 0.0f ? __fdiv_rn(bf16_to_f32(v[c][j] & 0xFFFF), s) : 0.0f;
+        q[2 * j + 1] = s != 0.0f ? __fdiv_rn(bf16_to_f32(v[c][j] >> 16), s) : 0.0f;
       }
-      *reinterpret_cast<u32x2_t*>(qr + i) = (u32x2_t){lo, hi};
+      *reinterpret_cast<u32x2_t*>(qr + i) = (u32x2_t){e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
     }
   }
 }
