@@ -162,7 +162,10 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
                       ((m + kStreamMaxRows - 1) / kStreamMaxRows) * d->n <= kStreamChunkCols;
   if (tu.path != P_AUTO) {
     p.path = tu.path;
-  } else if (m <= kStreamMaxRows || narrow) {
+  } else if (m <= kStreamMaxRows || narrow || (a4 && m <= kStreamWideRows)) {
+    // (W4A4 rows are 1/4 of bf16 bytes: streaming 32-row chunks beats the
+    // 128 x 128 tiles up to 256 rows, N = 7168 K = 2048: M = 64 7.0 against
+    // 15.5 us, M = 256 12.4 against 18.1)
     p.path = P_STREAM;
   } else if (int8) {
     // INT8: 128 x 128 or 256 x 256 tiles by the round costs of the MX
@@ -172,8 +175,13 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
     const int64_t c_big = 580 * std::max<int64_t>(big_n_tiles(G) * bt, 256) / 256;
     p.path = c_big < c_tile ? P_BIG : P_TILE;
   } else if (a4) {
-    // W4A4: 256 x 256 tiles from kBigMinRows rows, else 128 x 128
-    p.path = m >= kBigMinRows ? P_BIG : P_TILE;
+    // W4A4: 128 x 128 or 256 x 256 tiles by the round costs of the MX bf16-row
+    // choice below (M = 512, N = 7168: 16.9 against 23.5 us; M = 4096 on
+    // 256 x 256 tiles)
+    const int64_t mt = (m + kTileM - 1) / kTileM, bt = (m + kBigRows - 1) / kBigRows;
+    const int64_t c_tile = 170 * ((((G.NB + 7) / 8) * mt + 255) / 256) + 120;
+    const int64_t c_big = 580 * std::max<int64_t>(big_n_tiles(G) * bt, 256) / 256;
+    p.path = c_big < c_tile ? P_BIG : P_TILE;
   } else if (f4) {
     // MX weights with bf16 rows: the kernel with the least estimated time
     // (0.1 us per 2048 of K), fitted to MXFP4 and MXINT4 at N = 7168 K = 2048
@@ -242,6 +250,10 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
     return shapes;
   };
   int ks = tu.sks, nbw = tu.snbw, nw = tu.swaves ? tu.swaves : (ks == 8 ? 8 : 4);
+  // W4A4 in several 32-row chunks: two column blocks per wave, so each
+  // block stages its rows for twice the columns (N = 7168 K = 2048, M = 256:
+  // 12.4 against 16.6 us with one)
+  if (a4 && m_chunks > 1 && !nbw) nbw = 2;
   if (!ks || !nbw) {
     int pick;
     int64_t per_cu;
