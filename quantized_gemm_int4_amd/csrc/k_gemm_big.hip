@@ -145,14 +145,12 @@ _Pragma("nounroll")                                                             
               b2lds4(rsz, (w8next ? nc.svo[0] : cc.svo[0]) + (uint32_t)(w8s >> 1) * szstride, 0u,                   \
                      dw8 + kSOff + wave * 256);                                                                     \
             } else if (q < NX + 2) {                                                                                \
+              /* tile k0 + 2 wh of the wave: selected operands, no branch (a branch here splits */                  \
+              /* the step into blocks and the compiler then bunches the unpacking of later K parts) */             \
               const rsrc_t r = wnext ? nc.rw : cc.rw;                                                               \
               const int k0 = q - NX;                                                                                \
-              if (wh == 0)                                                                                          \
-                b2lds16(r, wnext ? nc.wvo[k0] : cc.wvo[k0], (uint32_t)(wg * 1024),                                  \
-                        dw + kWOff + (NWT * wave + k0) * 1024);                                                     \
-              else                                                                                                  \
-                b2lds16(r, wnext ? nc.wvo[2 + k0] : cc.wvo[2 + k0], (uint32_t)(wg * 1024),                          \
-                        dw + kWOff + (NWT * wave + 2 + k0) * 1024);                                                 \
+              const uint32_t vlo = wnext ? nc.wvo[k0] : cc.wvo[k0], vhi = wnext ? nc.wvo[2 + k0] : cc.wvo[2 + k0];  \
+              b2lds16(r, wh ? vhi : vlo, (uint32_t)(wg * 1024), dw + kWOff + (NWT * wave + k0 + 2 * wh) * 1024);    \
             } else if (F4) {                                                                                        \
               b2lds16(rsz, (wnext ? nc.svo[0] : cc.svo[0]) + (uint32_t)(wg >> 2) * 256, 0u,                         \
                       dw + kSOff + wave * 1024);                                                                    \
