@@ -21,6 +21,7 @@ using namespace hm;
 constexpr int kStreamMaxRows = 32;   // dense rows of one streaming block (two 16-row blocks)
 constexpr int64_t kStreamWideRows = 256;      // narrow-N dense calls stream up to this many rows ...
 constexpr int64_t kStreamChunkCols = 16384;   // ... while 32-row chunks x N stays within this
+constexpr int64_t kA8StreamChunkCols = 28672;  // W4A8 (FP8 rows, half the bytes): the same rule's limit
 constexpr int64_t kStreamLdsBytes = 159 * 1024;  // dynamic LDS one streaming block may use
 constexpr int kMoeStreamRows = 16;   // rows per grouped streaming unit
 // Experts with at most this many rows use the streaming kernel (as units of
@@ -160,12 +161,24 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   // against 23.4 us; N = 7168, M = 128 stays on tiles: 25.3 against 28.8 us)
   const bool narrow = !is_mx(d->wfmt) && m <= kStreamWideRows &&
                       ((m + kStreamMaxRows - 1) / kStreamMaxRows) * d->n <= kStreamChunkCols;
+  // W4A8 chunks: eight-wave blocks of four column sets (K split over two
+  // waves), one column block per wave for two chunks and two for more; taken
+  // where that grid has at least 128 blocks without a K split (measured up to
+  // four chunks)
+  const int64_t a8_nchunks = (m + kStreamMaxRows - 1) / kStreamMaxRows;
+  const int a8_nbw = a8_nchunks <= 2 ? 1 : 2;
+  const bool a8_chunks = a8 && m > kStreamMaxRows && m <= 4 * kStreamMaxRows &&
+                         a8_nchunks * d->n <= kA8StreamChunkCols &&
+                         (G.NB + 4 * a8_nbw - 1) / (4 * a8_nbw) * a8_nchunks >= 128;
   if (tu.path != P_AUTO) {
     p.path = tu.path;
-  } else if (m <= kStreamMaxRows || narrow || (a4 && m <= kStreamWideRows)) {
+  } else if (m <= kStreamMaxRows || narrow || (a4 && m <= kStreamWideRows) || a8_chunks) {
     // (W4A4 rows are 1/4 of bf16 bytes: streaming 32-row chunks beats the
     // 128 x 128 tiles up to 256 rows, N = 7168 K = 2048: M = 64 7.0 against
-    // 15.5 us, M = 256 12.4 against 18.1)
+    // 15.5 us, M = 256 12.4 against 18.1.  W4A8 likewise while chunks x N
+    // <= 28672, N = 7168 K = 2048: M = 64 6.1 against 9.3 us on 64 x 128
+    // tiles, M = 128 7.6 against 9.6; M = 256 stays on tiles, 10.1 against
+    // 10.8)
     p.path = P_STREAM;
   } else if (int8) {
     // INT8: 128 x 128 or 256 x 256 tiles by the round costs of the MX
@@ -254,6 +267,15 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   // block stages its rows for twice the columns (N = 7168 K = 2048, M = 256:
   // 12.4 against 16.6 us with one)
   if (a4 && m_chunks > 1 && !nbw) nbw = 2;
+  // W4A8 in several 32-row chunks (N = 7168 K = 2048: M = 64 6.1 us against
+  // 7.2 for the first shape that fits, M = 128 7.6 against 8.3; a K split
+  // over two blocks doubled the time)
+  const bool a8_shape = a8_chunks && tu.path == P_AUTO && !ks && !nbw && !tu.swaves;
+  if (a8_shape) {
+    nw = 8;
+    ks = 2;
+    nbw = a8_nbw;
+  }
   if (!ks || !nbw) {
     int pick;
     int64_t per_cu;
@@ -282,6 +304,7 @@ hm_status plan_dense(const hm_wdesc* d, int32_t afmt, int64_t m, const Tune& tu,
   const int64_t n_tiles = stream_n_tiles(G, p.sc);
   int64_t splits = tu.ssplits;
   if (splits > G.KG) return HM_ERR_TUNING;
+  if (splits <= 0 && a8_shape) splits = 1;
   if (splits <= 0) {
     // enough waves to keep every SIMD streaming (1024 SIMDs); split K over
     // blocks only below that

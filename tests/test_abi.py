@@ -132,6 +132,15 @@ def test_mxfp4_bf16_rows_plans():
     assert e.value.code == 8
     assert hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, 4096).startswith("w4a8-mxfp4 tile 256x256")
     assert hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, 1).startswith("w4a8-mxfp4 stream")
+    # W4A8 streams up to four 32-row chunks in eight-wave blocks without a K split
+    for m, nbw in ((33, 1), (64, 1), (96, 2), (128, 2)):
+        p = hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, m)
+        assert p.startswith(f"w4a8-mxfp4 stream mb=2 nbw={nbw} ks=2 waves=8 splits=1"), (m, p)
+    for m in (129, 256):
+        assert hm.hm_gemm_plan(mx, hm.HM_A_FP8_ROWSCALE, m).startswith("w4a8-mxfp4 tile 64x128")
+    # a narrow N whose chunk grid would be under 128 blocks stays on tiles
+    narrow = hm.wdesc("mxfp4", 2048, 7168)
+    assert hm.hm_gemm_plan(narrow, hm.HM_A_FP8_ROWSCALE, 64).startswith("w4a8-mxfp4 tile 64x128")
     sz = ctypes.c_size_t()
     i4 = hm.wdesc("int4_sym", 256, 512)
     assert _err("hm_gemm_workspace_size", ctypes.byref(i4), 1, 4, None, ctypes.byref(sz)) == 4

@@ -73,8 +73,10 @@ def config3():
     return Layer(quant.FMT_MXFP4, 7168, 2048, cfg=3)
 
 
-@pytest.mark.parametrize("m", [16, 256])
+@pytest.mark.parametrize("m", [16, 64, 100, 128, 256])
 def test_config3_mxfp4_full(config3, m):
+    """W4A8 at the full layer shape: M = 64..128 stream 32-row chunks in
+    eight-wave blocks (100: a ragged last chunk), 256 runs 64 x 128 tiles."""
     config3.check(synthetic.activations(3, m, 2048, index=m, outliers=0.01))
 
 
