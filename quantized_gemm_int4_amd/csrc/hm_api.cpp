@@ -36,7 +36,13 @@ constexpr int kMoeStreamMaxMx = 16, kMoeStreamNbwMx = 1;
 // up to 128 rows streaming: T = 64 / 1024 / 8192 0.448 / 1.756 / 8.954 ms
 // against 0.463 / 1.826 / 9.018 with 16-row units up to 64 rows
 constexpr int kMoeStreamRowsMxi4 = 32, kMoeStreamMaxMxi4 = 128;
-constexpr int kMoeStreamLdsKb = 79;   // LDS per grouped streaming block (two blocks per CU)
+// LDS per grouped streaming block: 48 KiB (three blocks per CU; rows longer
+// than that are staged in K pieces).  Measured against 79 KiB (two blocks),
+// 256 experts top-8: INT4 T = 64 / 1024 / 8192 gate_up 250 / 905 / 4087 ->
+// 205 / 835 / 4026 us, down 127 / 558 / 2347 -> 112 / 506 / 2318; MXFP4 bf16
+// rows and FP8 rows 1-8% faster; 20-32 KiB (four or more blocks) no better
+// than 79.  MXINT4 (32-row units) keeps 79 KiB: 48 was within +-3%.
+constexpr int kMoeStreamLdsKb = 48, kMoeStreamLdsKbMxi4 = 79;
 constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles may be used
 // An expert remainder of at least this many rows gets a 256-row unit (a unit
 // of at most 128 rows runs four of the eight 32-row MFMA blocks) instead of
@@ -353,7 +359,7 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
     p.nbw = 2;
   }
   p.ks = tu.mks ? tu.mks : 1;
-  p.lds_kb = tu.mlds ? tu.mlds : kMoeStreamLdsKb;
+  p.lds_kb = tu.mlds ? tu.mlds : (mxi4 ? kMoeStreamLdsKbMxi4 : kMoeStreamLdsKb);
   // an expert remainder of at least big_min rows takes a 256-row unit
   const int big_min = tu.mbig > 0 ? tu.mbig : kMoeBigMinRows;
   p.max_s = p.P / p.s_rows + act;
