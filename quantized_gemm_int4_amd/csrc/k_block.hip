@@ -34,7 +34,7 @@ k_silu_mul_v8(const uint16_t* __restrict__ gu, int64_t chunks, int64_t dc, uint1
 // (the input of an MoE block's down projection with FP8 rows): one wave per
 // row; lane l holds outputs 8 (64 c + l) .. + 7 (c < CH) of h rounded to bf16
 // exactly as k_silu_mul_v8 writes them, the row's amax is a wave reduction,
-// and the codes are those k_quant_fp8_rows_reg gives for the bf16 row:
+// and the codes are those k_quant_fp8_rows_wave gives for the bf16 row:
 // s = amax / 448, E4M3 of the correctly rounded fp32 quotient h / s.  The
 // bf16 h never reaches memory.  d % 8 == 0, d <= 512 CH.
 template <int CH>

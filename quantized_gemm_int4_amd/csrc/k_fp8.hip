@@ -56,60 +56,65 @@ k_quant_fp8_rows(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint8_t* 
   }
 }
 
-// Rows with k % 8 == 0 and k <= 2048 CH: each thread keeps its CH 16-byte
-// chunks of the row (thread t: values 8 (256 c + t) .. + 7) in registers, so
-// the row is read once and the amax pass and the quantizing pass share it.
+// Rows with k % 8 == 0 and k <= 512 CH: one wave per row (four rows per
+// block), lane L keeping 16-byte chunks c * 64 + L of the row in registers, so
+// the row is read once, the amax is a wave reduction (no block barrier) and
+// all of a wave's loads are in flight together.
 template <int CH>
 __global__ void __launch_bounds__(256)
-k_quant_fp8_rows_reg(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint8_t* __restrict__ x8,
-                     float* __restrict__ row_scale) {
-  __shared__ float red[4];
-  for (int64_t row = blockIdx.x; row < m; row += gridDim.x) {
+k_quant_fp8_rows_wave(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint8_t* __restrict__ x8,
+                      float* __restrict__ row_scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t kc = k / 8;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < m; row += (int64_t)gridDim.x * 4) {
     const uint16_t* xr = x + row * k;
-    uint8_t* qr = x8 + row * k;
     u32x4_t v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t q = (int64_t)c * 64 + lane;
+      v[c] = q < kc ? ld16(xr + 8 * q) : (u32x4_t){0u, 0u, 0u, 0u};
+    }
     float amax = 0.0f;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int64_t i = ((int64_t)c * 256 + threadIdx.x) * 8;
-      v[c] = i < k ? ld16(xr + i) : (u32x4_t){0u, 0u, 0u, 0u};
+    for (int c = 0; c < CH; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        amax = fmaxf(amax, fabsf(bf16_to_f32(v[c][j] & 0xFFFF)));
-        amax = fmaxf(amax, fabsf(bf16_to_f32(v[c][j] >> 16)));
+        amax = fmaxf(amax, fabsf(lo_bf16(v[c][j])));
+        amax = fmaxf(amax, fabsf(hi_bf16(v[c][j])));
       }
-    }
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
     const float s = __fdiv_rn(amax, 448.0f);
-    if (threadIdx.x == 0) row_scale[row] = s;
+    if (lane == 0) row_scale[row] = s;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int64_t i = ((int64_t)c * 256 + threadIdx.x) * 8;
-      if (i >= k) continue;
-      float q[8];
+      const int64_t q = (int64_t)c * 64 + lane;
+      float f[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        q[2 * j] = s != 0.0f ? __fdiv_rn(bf16_to_f32(v[c][j] & 0xFFFF), s) : 0.0f;
-        q[2 * j + 1] = s != 0.0f ? __fdiv_rn(bf16_to_f32(v[c][j] >> 16), s) : 0.0f;
+      for (int j = 0; j < 8; ++j) {
+        const float h = (j & 1) ? hi_bf16(v[c][j >> 1]) : lo_bf16(v[c][j >> 1]);
+        f[j] = s != 0.0f ? __fdiv_rn(h, s) : 0.0f;
       }
-      *reinterpret_cast<u32x2_t*>(qr + i) = (u32x2_t){e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
+      if (q < kc)
+        *reinterpret_cast<u32x2_t*>(x8 + row * k + 8 * q) =
+            (u32x2_t){e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7])};
     }
   }
 }
 
 hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* x8, float* s,
                                  hipStream_t st) {
-  const int64_t blocks = m < 65536 ? m : 65536;
-  if ((k & 7) == 0 && k <= 2048 * 4) {
-    // one row per block, held in registers
-    if (k <= 2048) hipLaunchKernelGGL(k_quant_fp8_rows_reg<1>, dim3((unsigned)blocks), dim3(256), 0, st, x, m, k, x8, s);
-    else if (k <= 4096) hipLaunchKernelGGL(k_quant_fp8_rows_reg<2>, dim3((unsigned)blocks), dim3(256), 0, st, x, m, k, x8, s);
-    else hipLaunchKernelGGL(k_quant_fp8_rows_reg<4>, dim3((unsigned)blocks), dim3(256), 0, st, x, m, k, x8, s);
+  if ((k & 7) == 0 && k <= 512 * 16) {
+    // one row per wave, held in registers
+    const int64_t want = (m + 3) / 4;
+    const dim3 g((unsigned)(want < 65536 ? want : 65536));
+    if (k <= 512) hipLaunchKernelGGL(k_quant_fp8_rows_wave<1>, g, dim3(256), 0, st, x, m, k, x8, s);
+    else if (k <= 1024) hipLaunchKernelGGL(k_quant_fp8_rows_wave<2>, g, dim3(256), 0, st, x, m, k, x8, s);
+    else if (k <= 2048) hipLaunchKernelGGL(k_quant_fp8_rows_wave<4>, g, dim3(256), 0, st, x, m, k, x8, s);
+    else if (k <= 4096) hipLaunchKernelGGL(k_quant_fp8_rows_wave<8>, g, dim3(256), 0, st, x, m, k, x8, s);
+    else hipLaunchKernelGGL(k_quant_fp8_rows_wave<16>, g, dim3(256), 0, st, x, m, k, x8, s);
   } else {
+    // one row per block, two passes over the row
+    const int64_t blocks = m < 65536 ? m : 65536;
     hipLaunchKernelGGL(k_quant_fp8_rows, dim3((unsigned)blocks), dim3(256), 0, st, x, m, k, x8, s);
   }
   return hipGetLastError();

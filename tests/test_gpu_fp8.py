@@ -35,6 +35,22 @@ def test_fp8_rows_bit_exact(m, k):
     assert np.array_equal(x8.cpu().numpy(), rc)
 
 
+@pytest.mark.parametrize("m,k", [(5, 8), (9, 512), (6, 520), (4, 1032), (3, 4096), (2, 4104), (2, 8192),
+                                 (3, 8200), (262149, 8)])
+def test_fp8_rows_every_row_length_class(m, k):
+    """Each register-chunk count of the wave-per-row kernel (k up to 512,
+    1024, 2048, 4096, 8192, full and ragged), the two-pass kernel above 8192,
+    row counts that leave a block's waves idle, and more rows than the grid
+    holds (grid-stride loop)."""
+    import quantized_gemm_int4_amd as hm
+    xb = _rows(m, k, m + 7 * k)
+    x8, s = hm.hm_quant_fp8_rows(bf16_to_dev(xb))
+    torch.cuda.synchronize()
+    rc, rs = quant.quant_fp8_rows(xb)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(x8.cpu().numpy(), rc)
+
+
 def test_fp8_rows_workload_outliers():
     import quantized_gemm_int4_amd as hm
     xb = synthetic.activations(3, 256, 2048, outliers=0.01)
