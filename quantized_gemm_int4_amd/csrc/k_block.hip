@@ -70,22 +70,25 @@ k_silu_mul_fp8(const uint16_t* __restrict__ gu, int64_t rows, int64_t d, uint8_t
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     const float s = __fdiv_rn(amax, 448.0f);
     if (lane == 0) hs[r] = s;
-    uint32_t cw[CH][2];
+    // quotients h / s by the reciprocal and one correction step when s
+    // allows it (uniform over the wave's row), else by the IEEE division
+    auto put = [&](auto div) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      float q[8];
+      for (int c = 0; c < CH; ++c) {
+        float q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float h = (j & 1) ? hi_bf16(gv[c][j >> 1]) : lo_bf16(gv[c][j >> 1]);
-        q[j] = s != 0.0f ? __fdiv_rn(h, s) : 0.0f;
+        for (int j = 0; j < 8; ++j) q[j] = div((j & 1) ? hi_bf16(gv[c][j >> 1]) : lo_bf16(gv[c][j >> 1]));
+        const int64_t qc = (int64_t)c * 64 + lane;
+        if (qc < dc)
+          *reinterpret_cast<u32x2_t*>(h8 + r * d + 8 * qc) =
+              (u32x2_t){e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
       }
-      cw[c][0] = e4m3x4(q[0], q[1], q[2], q[3]);
-      cw[c][1] = e4m3x4(q[4], q[5], q[6], q[7]);
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int64_t q = (int64_t)c * 64 + lane;
-      if (q < dc) *reinterpret_cast<u32x2_t*>(h8 + r * d + 8 * q) = (u32x2_t){cw[c][0], cw[c][1]};
+    };
+    if (__builtin_amdgcn_readfirstlane(recip_div_ok(s) ? 1 : 0)) {
+      const float rs = __fdiv_rn(1.0f, s);
+      put([&](float h) { return div_by_recip(h, s, rs); });
+    } else {
+      put([&](float h) { return s != 0.0f ? __fdiv_rn(h, s) : 0.0f; });
     }
   }
 }

@@ -85,18 +85,26 @@ k_quant_fp8_rows_wave(const uint16_t* __restrict__ x, int64_t m, int64_t k, uint
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     const float s = __fdiv_rn(amax, 448.0f);
     if (lane == 0) row_scale[row] = s;
+    // codes of the rounded quotients x / s: by the reciprocal and one
+    // correction step when s allows it (the row's s is the same on every
+    // lane, so the branch is uniform), else by the IEEE division
+    auto put = [&](auto div) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int64_t q = (int64_t)c * 64 + lane;
-      float f[8];
+      for (int c = 0; c < CH; ++c) {
+        const int64_t q = (int64_t)c * 64 + lane;
+        float f[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float h = (j & 1) ? hi_bf16(v[c][j >> 1]) : lo_bf16(v[c][j >> 1]);
-        f[j] = s != 0.0f ? __fdiv_rn(h, s) : 0.0f;
+        for (int j = 0; j < 8; ++j) f[j] = div((j & 1) ? hi_bf16(v[c][j >> 1]) : lo_bf16(v[c][j >> 1]));
+        if (q < kc)
+          *reinterpret_cast<u32x2_t*>(x8 + row * k + 8 * q) =
+              (u32x2_t){e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7])};
       }
-      if (q < kc)
-        *reinterpret_cast<u32x2_t*>(x8 + row * k + 8 * q) =
-            (u32x2_t){e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7])};
+    };
+    if (__builtin_amdgcn_readfirstlane(recip_div_ok(s) ? 1 : 0)) {
+      const float r = __fdiv_rn(1.0f, s);
+      put([&](float h) { return div_by_recip(h, s, r); });
+    } else {
+      put([&](float h) { return s != 0.0f ? __fdiv_rn(h, s) : 0.0f; });
     }
   }
 }

@@ -51,6 +51,31 @@ def test_fp8_rows_every_row_length_class(m, k):
     assert np.array_equal(x8.cpu().numpy(), rc)
 
 
+def test_fp8_rows_extreme_scales():
+    """Rows whose scale falls outside the reciprocal path's range (amax about
+    2^-100 and 2^115: the IEEE division) next to rows inside it, with bf16
+    subnormal elements and -0 in a normal row, all bit-exact."""
+    import quantized_gemm_int4_amd as hm
+    r = np.random.default_rng(5)
+    x = r.normal(0, 1, size=(8, 1024)).astype(np.float32)
+    x[0] *= np.float32(2.0 ** -100)
+    x[1] *= np.float32(2.0 ** -92)
+    x[2] *= np.float32(2.0 ** 100)
+    x[3] *= np.float32(2.0 ** 115)
+    x[4, :64] = np.float32(2.0 ** -130) * r.integers(-64, 64, size=64)     # bf16 subnormals
+    x[4, 64:70] = -0.0
+    x[5] = 0.0
+    x[5, 17] = -1.0                                                          # one nonzero, negative
+    x[6] = np.float32(2.0 ** -20) * r.normal(0, 1, size=1024)
+    x[6, 3] = 1.0                                                            # others far below the amax
+    xb = synthetic.to_bf16_bits(x)
+    x8, s = hm.hm_quant_fp8_rows(bf16_to_dev(xb))
+    torch.cuda.synchronize()
+    rc, rs = quant.quant_fp8_rows(xb)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(x8.cpu().numpy(), rc)
+
+
 def test_fp8_rows_workload_outliers():
     import quantized_gemm_int4_amd as hm
     xb = synthetic.activations(3, 256, 2048, outliers=0.01)
