@@ -541,11 +541,15 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
         const uint8_t* xbase = st + wm * 4 * XRB;
         u32x4_t wq[8];
         int wsc[8];
+        uint32_t swd[8];
+        // all eight scale words first, then the tiles, then the bytes: the
+        // reads go out together instead of one scale pair per LDS round trip
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          wq[j] = ld16(wbase + j * 1024);
-          wsc[j] = (int)((*reinterpret_cast<const uint32_t*>(sbase + j * 256) >> sh) & 0xFF);
-        }
+        for (int j = 0; j < 8; ++j) swd[j] = *reinterpret_cast<const uint32_t*>(sbase + j * 256);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wq[j] = ld16(wbase + j * 1024);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wsc[j] = (int)((swd[j] >> sh) & 0xFF);
         // MXFP4 rows: the E8M0 byte of row 64 wm + 16 i + n_l and K block q_l
         // (word of row r at kAO + (r / 32) 256 + (r % 32) 4)
         int xsc[4] = {127, 127, 127, 127};
