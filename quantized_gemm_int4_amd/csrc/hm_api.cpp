@@ -31,6 +31,10 @@ constexpr int kMoeStreamRows = 16;   // rows per grouped streaming unit
 // -19% / -5% / -5% against 16 rows and one block); MXFP4 keeps 16 and one.
 constexpr int kMoeStreamMaxA16 = 64, kMoeStreamNbwA16 = 2;
 constexpr int kMoeStreamMaxMx = 16, kMoeStreamNbwMx = 1;
+// FP8 rows (W4A8): 32-row units, experts of up to 128 rows streaming, two
+// blocks per wave (T = 1024 gate_up / down 583 / 334 -> 504 / 313 us; T =
+// 16384 0.3 / 1.2% faster), as dense W4A8 streams up to 128 rows
+constexpr int kMoeStreamRowsA8 = 32, kMoeStreamMaxA8 = 128, kMoeStreamNbwA8 = 2;
 // MXINT4 (bf16 rows): its streaming kernel is bound by the code conversion,
 // so 32-row units (each conversion serving twice the rows) with experts of
 // up to 128 rows streaming: T = 64 / 1024 / 8192 0.448 / 1.756 / 8.954 ms
@@ -349,9 +353,11 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
   const bool a8 = afmt != HM_A_BF16;          // FP8 or MXFP4 rows: the W4A8 streaming settings
   const bool a4 = afmt == HM_A_MXFP4;
   const bool f4 = mx_a16(d, afmt);
-  p.s_rows = tu.mrows ? tu.mrows : (mxi4 ? kMoeStreamRowsMxi4 : kMoeStreamRows);
-  p.s_max = tu.mmax ? tu.mmax : (a8 ? kMoeStreamMaxMx : (mxi4 ? kMoeStreamMaxMxi4 : kMoeStreamMaxA16));
-  p.nbw = tu.mnbw ? tu.mnbw : (a8 ? kMoeStreamNbwMx : kMoeStreamNbwA16);
+  const bool fp8 = afmt == HM_A_FP8_ROWSCALE;
+  p.s_rows = tu.mrows ? tu.mrows : (fp8 ? kMoeStreamRowsA8 : (mxi4 ? kMoeStreamRowsMxi4 : kMoeStreamRows));
+  p.s_max = tu.mmax ? tu.mmax
+                    : (fp8 ? kMoeStreamMaxA8 : (a8 ? kMoeStreamMaxMx : (mxi4 ? kMoeStreamMaxMxi4 : kMoeStreamMaxA16)));
+  p.nbw = tu.mnbw ? tu.mnbw : (fp8 ? kMoeStreamNbwA8 : (a8 ? kMoeStreamNbwMx : kMoeStreamNbwA16));
   if (gated) {
     // the gated epilogue pairs a wave's two column blocks (gate, up)
     if (d->n % 32 != 0) return HM_ERR_SHAPE;
