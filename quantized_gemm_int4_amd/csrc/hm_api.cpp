@@ -28,7 +28,7 @@ constexpr int kMoeStreamRows = 16;   // rows per grouped streaming unit
 // kMoeStreamRows rows that share the expert's weights through the L2), with
 // this many 16-column blocks per wave.  Measured on the 256-expert top-8
 // workloads: W4A16 64 rows and two blocks per wave (T = 64 / 1024 / 8192:
-// -19% / -5% / -5% against 16 rows and one block); MXFP4 keeps 16 and one.
+// -19% / -5% / -5% against 16 rows and one block); MXFP4 rows keep 16 and one.
 constexpr int kMoeStreamMaxA16 = 64, kMoeStreamNbwA16 = 2;
 constexpr int kMoeStreamMaxMx = 16, kMoeStreamNbwMx = 1;
 // FP8 rows (W4A8): 32-row units, experts of up to 128 rows streaming, two
@@ -350,7 +350,7 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
   p.P = t * topk;
   const int64_t act = (p.P < d->num_experts) ? p.P : d->num_experts;
   const bool mxi4 = d->wfmt == HM_W_MXINT4;
-  const bool a8 = afmt != HM_A_BF16;          // FP8 or MXFP4 rows: the W4A8 streaming settings
+  const bool a8 = afmt != HM_A_BF16;          // FP8 or MXFP4 rows
   const bool a4 = afmt == HM_A_MXFP4;
   const bool f4 = mx_a16(d, afmt);
   const bool fp8 = afmt == HM_A_FP8_ROWSCALE;
