@@ -80,6 +80,17 @@ def test_config3_mxfp4_full(config3, m):
     config3.check(synthetic.activations(3, m, 2048, index=m, outliers=0.01))
 
 
+@pytest.mark.parametrize("m", [33, 100, 128])
+def test_w4a8_chunked_streaming_ragged(m):
+    """W4A8 rows streamed in 32-row chunks on eight-wave blocks (the default
+    for 33..128 rows when the grid holds enough blocks) with N ragged against
+    the block's column sets and K not a multiple of the K slices."""
+    import quantized_gemm_int4_amd as hm
+    L = Layer(quant.FMT_MXFP4, 7000, 2304, cfg=3, wseed=17)
+    assert "stream" in hm.hm_gemm_plan(L.desc, hm.HM_A_FP8_ROWSCALE, m)
+    L.check(synthetic.activations(3, m, 2304, index=m + 1, outliers=0.01))
+
+
 def test_config3_m4096_sampled_rows(config3):
     rows = np.random.default_rng(1).choice(4096, 96, replace=False)
     config3.check(synthetic.activations(3, 4096, 2048, index=4096, outliers=0.01), rows=rows)
