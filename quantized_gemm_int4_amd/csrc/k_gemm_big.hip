@@ -541,28 +541,34 @@ k_gemm_big(GemmArgs a, int tiles_n, int tiles_m, int n_full) {
         const uint8_t* xbase = st + wm * 4 * XRB;
         u32x4_t wq[8];
         int wsc[8];
-        uint32_t swd[8];
-        // all eight scale words first, then the tiles, then the bytes: the
-        // reads go out together instead of one scale pair per LDS round trip
+        uint32_t swd[8], xsw4[4];
+        u32x4_t b0[2], b1[2];
+        // every read of the step's first MFMAs goes out before any of them is
+        // used, in the order they are needed (LDS returns in order): the
+        // scale words, row block 0's activations, then the tiles one by one,
+        // so the first MFMA waits for a fifth of the step's reads and each
+        // later one for its own tile
 #pragma unroll
         for (int j = 0; j < 8; ++j) swd[j] = *reinterpret_cast<const uint32_t*>(sbase + j * 256);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) wq[j] = ld16(wbase + j * 1024);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) wsc[j] = (int)((swd[j] >> sh) & 0xFF);
         // MXFP4 rows: the E8M0 byte of row 64 wm + 16 i + n_l and K block q_l
         // (word of row r at kAO + (r / 32) 256 + (r % 32) 4)
-        int xsc[4] = {127, 127, 127, 127};
         if (A4) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            xsc[i] = (int)((*reinterpret_cast<const uint32_t*>(st + kAO + (2 * wm + (i >> 1)) * 256 +
-                                                                 (16 * (i & 1) + n_l) * 4) >>
-                            (8 * q_l)) & 0xFF);
+            xsw4[i] = *reinterpret_cast<const uint32_t*>(st + kAO + (2 * wm + (i >> 1)) * 256 + (16 * (i & 1) + n_l) * 4);
         }
-        u32x4_t b0[2], b1[2];
         b0[0] = ld16(xbase + xo0);
         if (!A4) b1[0] = ld16(xbase + xo1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wq[j] = ld16(wbase + j * 1024);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wsc[j] = (int)((swd[j] >> sh) & 0xFF);
+        int xsc[4] = {127, 127, 127, 127};
+        if (A4) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xsc[i] = (int)((xsw4[i] >> (8 * q_l)) & 0xFF);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (i + 1 < 4) {
