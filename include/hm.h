@@ -135,8 +135,8 @@ typedef struct hm_wdesc {
 typedef struct hm_tuning {
   int32_t abi;             /* HM_ABI_VERSION */
   int32_t path;            /* dense kernel: 0 default; 1 streaming (M <= 256); 2 128-row tiles
-                              (W4A16 128 x 64 split over K, W4A8 64 x 128); 3 256 x 256 tiles
-                              (not for MX weights with bf16 rows); 4 128 x 128 tiles */
+                              (W4A16 128 x 64 split over K, W4A8 64 x 128); 3 256 x 256 tiles;
+                              4 128 x 128 tiles */
   int32_t stream_ks;       /* streaming: waves of a block splitting one column set's K: 0, 1, 2, 4, 8 */
   int32_t stream_nbw;      /* streaming: 16-column blocks per wave: 0, 1, 2 */
   int32_t stream_splits;   /* dense streaming: K split over blocks (fp32 partials): 0, 1 .. K/128 */

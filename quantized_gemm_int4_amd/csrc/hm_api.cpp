@@ -380,8 +380,7 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
     const int64_t a_rows = rows_are_pairs ? p.P : t;
     p.a64 = (uint64_t)a_rows * (uint64_t)d->k * (a4 ? 1u : (a8 ? 2u : 4u)) >= 2 * kAddr32;
     const bool tiles32 = scales_addr32(G);
-    // 256-row units: not for MX weights with bf16 rows; they address
-    // activation rows and scales with 32-bit offsets
+    // 256-row units address activation rows and scales with 32-bit offsets
     const bool int8 = d->wfmt == HM_W_INT8_SYM;
     const bool tile_only = a4 || int8;                       // no 128-row tile kernel
     const bool big_ok = !p.a64 && tiles32;
