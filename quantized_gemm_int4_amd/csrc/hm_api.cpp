@@ -52,8 +52,13 @@ constexpr int64_t kBigMinRows = 512;  // dense rows from which 256 x 256 tiles m
 // of at most 128 rows runs four of the eight 32-row MFMA blocks) instead of
 // 128 x 64 tile units, which copy the unit's activation rows once per 64
 // columns.  Measured against 192: W4A16 T = 1024 -12%, T = 8192 -2%; W4A8
-// T = 16384 -3..4% (65 and 129 rows).
+// T = 16384 -3..4% (65 and 129 rows).  With K <= 2048 (a down projection:
+// short K loops, so a 128 x 64 tile's staging weighs more) from 49 rows:
+// N = 7168 K = 2048, T = 1024 -5..7% for bf16 rows (INT4, MXFP4), -2% for
+// FP8 rows, T = 8192 within +-1%; with K = 7168 49 rows was 3-7% slower.
 constexpr int kMoeBigMinRows = 97;
+constexpr int kMoeBigMinRowsShortK = 49;
+constexpr int64_t kMoeShortK = 2048;
 constexpr int kGroupedGridStream = 2048;
 constexpr int kGroupedGridTile = 1024;
 constexpr int kGroupedGridMid = 256;     // one 128 x 64 tile block per compute unit (LDS-bound)
@@ -367,7 +372,7 @@ hm_status plan_moe(const hm_wdesc* d, int32_t afmt, int64_t t, int32_t topk, int
   p.ks = tu.mks ? tu.mks : 1;
   p.lds_kb = tu.mlds ? tu.mlds : (mxi4 ? kMoeStreamLdsKbMxi4 : kMoeStreamLdsKb);
   // an expert remainder of at least big_min rows takes a 256-row unit
-  const int big_min = tu.mbig > 0 ? tu.mbig : kMoeBigMinRows;
+  const int big_min = tu.mbig > 0 ? tu.mbig : (d->k <= kMoeShortK ? kMoeBigMinRowsShortK : kMoeBigMinRows);
   p.max_s = p.P / p.s_rows + act;
   p.max_t = (p.P + kTileM - 1) / kTileM + act;
   p.max_b = p.P / big_min + 1;              // every 256-row unit holds >= big_min rows

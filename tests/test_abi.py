@@ -289,11 +289,11 @@ def test_moe_plan_and_large_activation_guard():
     assert "k_gemm_tile 128x128" in hm.hm_moe_gemm_plan(mx, 1, 1 << 18, 8, 1)
     # MX weights with bf16 rows take 256-row units, INT8 ones never
     mxa = hm.hm_moe_gemm_plan(mx, 0, 8192, 8, 1)
-    assert "k_gemm_big from 97 rows" in mxa, mxa
+    assert "k_gemm_big from 49 rows" in mxa, mxa
     mxi = hm.hm_moe_gemm_plan(hm.wdesc("mxint4", 7168, 2048, 256), 0, 8192, 8, 1)
-    assert "k_gemm_big from 97 rows" in mxi, mxi
+    assert "k_gemm_big from 49 rows" in mxi, mxi
     i8p = hm.hm_moe_gemm_plan(hm.wdesc("int8_sym", 7168, 2048, 256), 0, 8192, 8, 1)
-    assert "k_gemm_big from 97 rows" in i8p and "k_gemm_tile" in i8p, i8p
+    assert "k_gemm_big from 49 rows" in i8p and "k_gemm_tile" in i8p, i8p
     # explicit tuning shows up in the plan and in the workspace size
     t = dict(moe_stream_rows=32, moe_stream_max=128, moe_stream_nbw=1, moe_big_min=-1, moe_tile=2)
     p2 = hm.hm_moe_gemm_plan(gu, 0, 1024, 8, 0, t)
