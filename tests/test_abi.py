@@ -261,6 +261,20 @@ def test_tuning_validation():
         assert hm.hm_gemm_plan(d, 0, m, hm.make_tuning()) == hm.hm_gemm_plan(d, 0, m)
 
 
+def test_moe_big_unit_threshold_by_k():
+    """Expert remainders take 256-row units from 49 rows when K <= 2048 (short
+    K loops: the down projection) and from 97 rows otherwise; an explicit
+    moe_big_min overrides both."""
+    for k, rows in ((2048, 49), (1024, 49), (2176, 97), (7168, 97)):
+        for fmt in ("int4_sym", "uint4_zp", "mxfp4"):
+            d = hm.wdesc(fmt, 4096, k, 64)
+            p = hm.hm_moe_gemm_plan(d, 0, 1024, 8, 1)
+            assert f"k_gemm_big from {rows} rows" in p, (fmt, k, p)
+    d = hm.wdesc("int4_sym", 4096, 2048, 64)
+    assert "k_gemm_big from 97 rows" in hm.hm_moe_gemm_plan(d, 0, 1024, 8, 1, dict(moe_big_min=97))
+    assert "k_gemm_big from 129 rows" in hm.hm_moe_gemm_plan(d, 0, 1024, 8, 1, dict(moe_big_min=129))
+
+
 def test_moe_plan_and_large_activation_guard():
     """The grouped GEMM's unit kinds, and the guard for activations of 4 GiB
     or more: the 128-row tile kernels and the 256-row kernel address
